@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = the whole prefill path over the Kimi K3 KDA layer workload (B=1, T=8192,
+H=96, K=V=128, bf16 q/k/v, fp32 gate/beta/state): the bounded-decay gate kernel on
+the raw logits, then the chunkwise prefill kernel (zero initial state, fp32 final
+state, bf16 output).  Inputs are resident in HBM before timing starts.  Reported:
+
+* value: prefill tokens/s over K timed steps (ms_per_step = wall time per step);
+* roofline: the chunk kernel's algorithmic HBM traffic (1,540 B per token-head) and
+  algorithmic flops (6KV + 64(3K+2V) per token-head) per launch divided by its average
+  launch time (HIP events on the launch stream), against 8 TB/s and 2.5 PFLOP/s bf16;
+* decode: 256 successive single-token steps over a kept [64,96,128,128] fp32 state
+  (gate kernel + fused step kernel per step), with the step kernel's algorithmic
+  bytes (state read + write plus the token vectors) per launch over its launch time;
+* cpu_baseline: the fp64 oracle (gate + token scan) on half the heads of the same
+  prefill workload, timed on the host cores and scaled to the whole workload.
+
+Prints ONE JSON line.  Only N=1 is meaningful: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "gated_delta_rule_31_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, workload: str):
+    """Counter-measured HBM bytes per launch (profiles/traffic.json), if they were taken
+    on the kernel source as it is now; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d.get(workload)
+        if not e or e.get("source_sha256_16") != kernel_source_hash(kernel_file):
+            return None
+        return float(e["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=32)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=48)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_31_amd as kda
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- prefill ---------------------------------------------------------
+    B, T, H, K, V = 1, 8192, 96, 128, 128
+    log("generating prefill inputs")
+    inp = synth.k3_prefill(device="cuda")
+    q, k, v, z, ls, beta = inp.q, inp.k, inp.v, inp.z, inp.log_scale, inp.beta
+    g = torch.empty(B, T, H, K, dtype=torch.float32, device=dev)
+    out = torch.empty(B, T, H, V, dtype=torch.bfloat16, device=dev)
+    fin = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev_pair=None):
+        kda.bounded_decay(z, ls, lower_bound=-5.0, out_log=True, out=g)
+        if ev_pair is not None:
+            ev_pair[0].record(stream)
+        kda.chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=args.chunk, gate_is_log=True,
+                      out=out, final_state=fin)
+        if ev_pair is not None:
+            ev_pair[1].record(stream)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    chunk_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = B * T / (wall / args.steps)
+
+    th = B * T * H
+    alg_bytes = th * (3 * 2 * K + 4 * K + 4 + 2 * V)       # q,k,v bf16 + gate fp32 + beta + out bf16
+    alg_flops = th * (6 * K * V + 64 * (3 * K + 2 * V))
+    achieved_gbs = alg_bytes / (chunk_ms * 1e-3) / 1e9
+    achieved_tflops = alg_flops / (chunk_ms * 1e-3) / 1e12
+    traffic = load_traffic("kda_chunk.hip", "k3_prefill_chunk_fwd")
+    log("prefill: %.3f ms/step, chunk kernel %.3f ms, %.1f GB/s, %.1f TFLOP/s" %
+        (ms_per_step, chunk_ms, achieved_gbs, achieved_tflops))
+
+    result = {
+        "metric": "KDA prefill tokens/s (H=96,D=128) + % MFMA peak; decode state HBM GB/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "k3_prefill_B1_T8192_H96_K128_V128", "global_batch": B, "seq_len": T,
+                   "heads": H, "key_dim": K, "value_dim": V, "chunk_size": args.chunk,
+                   "step": "bounded_decay + chunk_fwd", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": "chunk_fwd_kernel",
+                     "launch_ms": chunk_ms, "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
+    }
+    del g, out
+
+    # ---------------- decode ------------------------------------------------------------
+    if not args.no_decode:
+        nd = args.decode_steps
+        log("generating decode inputs (%d steps)" % nd)
+        dec = synth.decode(device="cuda", steps=nd)
+        Bd, Hd = dec.q.shape[1], dec.q.shape[2]
+        state = dec.state.clone()
+        al = torch.empty(Bd, Hd, K, dtype=torch.float32, device=dev)
+        od = torch.empty(Bd, Hd, V, dtype=torch.bfloat16, device=dev)
+
+        def dstep(t, ev_pair=None):
+            kda.bounded_decay(dec.z[t], dec.log_scale, out=al)
+            if ev_pair is not None:
+                ev_pair[0].record(stream)
+            kda.recurrent_step(dec.q[t], dec.k[t], dec.v[t], al, dec.beta[t], state, out=od)
+            if ev_pair is not None:
+                ev_pair[1].record(stream)
+
+        for t in range(min(8, nd)):
+            dstep(t)
+        state.copy_(dec.state)
+        torch.cuda.synchronize()
+        devs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nd)]
+        t0 = time.perf_counter()
+        for t in range(nd):
+            dstep(t, devs[t])
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t0
+        step_ms = sorted(a.elapsed_time(b) for a, b in devs)
+        step_med = step_ms[len(step_ms) // 2]
+        step_avg = sum(step_ms) / len(step_ms)
+        pair_bytes = 2 * K * V * 4 + 2 * 2 * K + 2 * V + 4 * K + 4 + 2 * V
+        d_bytes = Bd * Hd * pair_bytes
+        d_gbs = d_bytes / (step_avg * 1e-3) / 1e9
+        dtraffic = load_traffic("kda_step.hip", "decode_recurrent_step")
+        log("decode: %.3f ms/step wall, step kernel avg %.1f us (median %.1f), %.0f GB/s" %
+            (dwall * 1e3 / nd, step_avg * 1e3, step_med * 1e3, d_gbs))
+        result["decode"] = {
+            "workload": "decode_B64_H96_K128_V128_steps%d" % nd,
+            "tokens_per_s": Bd * nd / dwall,
+            "ms_per_step": dwall * 1e3 / nd,
+            "step": "bounded_decay + recurrent_step",
+            "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": d_gbs / HBM_PEAK_GBS, "traffic": dtraffic, "kernel": "recurrent_step_kernel",
+                         "launch_us_avg": step_avg * 1e3, "launch_us_median": step_med * 1e3,
+                         "algorithmic_bytes_per_launch": d_bytes},
+        }
+        del dec, state
+
+    # ---------------- CPU baseline: the oracle on a head sample -------------------------
+    if not args.no_cpu_baseline:
+        import oracle
+        from tests.helpers import f64
+        hs = list(range(0, H, max(1, H // args.cpu_heads)))[:args.cpu_heads]
+        log("cpu baseline: oracle on %d of %d heads" % (len(hs), H))
+        qs, ks, vs, zs = (f64(x[:, :, hs]) for x in (q, k, v, z))
+        bs = f64(beta[:, :, hs])
+        lss = f64(ls)[hs]
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        alpha = oracle.bounded_decay(zs, lss, g_min=-5.0)
+        oracle.scan(qs, ks, vs, alpha, bs)
+        cpu_s = time.perf_counter() - t0
+        cpu_tps = B * T / (cpu_s * H / len(hs))
+        result["cpu_baseline"] = {"value": cpu_tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                  "sample": "fp64 gate + token scan of %d of the %d heads (T=8192), %.1f s wall, "
+                                            "scaled by %d/%d" % (len(hs), H, cpu_s, H, len(hs))}
+        log("cpu baseline %.1f tokens/s (%.1f s on %d threads)" % (cpu_tps, cpu_s, threads))
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

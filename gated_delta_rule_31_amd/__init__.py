@@ -1,0 +1,234 @@
+"""MI355X (gfx950) Kimi Delta Attention (KDA) state recurrence.
+
+A thin Python binding over the C ABI of ``include/kda.h`` (``libkda.so``, built
+in-tree by ``gated_delta_rule_31_amd/build.py``).  PyTorch supplies device memory
+and the current stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing, or the tensors are not
+on a GPU, these functions raise.
+
+Entry points (same names as the C ABI, minus the ``kda_`` prefix where noted):
+
+* ``bounded_decay(logits, log_scale, lower_bound=-5, bias=None, out_log=False)``
+  -- the K3 gate alpha = exp(g_min * sigmoid(e^A (z + bias))) (or g itself).
+* ``chunk_fwd(q, k, v, gate, beta, ...)`` -- chunkwise prefill with optional
+  initial / final state and packed sequences (``cu_seqlens``).
+* ``recurrent_step(q, k, v, gate, beta, state, ...)`` -- one decode token, state
+  updated in place.
+* ``recurrent_kda(q, k, v, alpha, beta, initial_state=None)`` -- the functional
+  (output, final_state) form of the pages' operator contract, on ``chunk_fwd``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["bounded_decay", "chunk_fwd", "recurrent_step", "recurrent_kda", "KDAError",
+           "library_path", "abi_version", "GATE_ALPHA", "GATE_LOG"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+GATE_ALPHA, GATE_LOG = 0, 1
+_STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "bad dtype", 4: "unsupported",
+           5: "bad argument", 6: "alias", 7: "hip error"}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)%s" % (fn, _STATUS.get(status, "?"), status,
+                                                         (": " + detail) if detail else ""))
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libkda.so is not built (%s); run gated_delta_rule_31_amd/build.py" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.kda_bounded_decay.argtypes = [vp, i32, vp, vp, f32, i64, i32, i32, i32, vp, vp]
+    lib.kda_bounded_decay.restype = i32
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i64, i32, i32,
+                                  i32, i32, f32, vp, i32, vp]
+    lib.kda_chunk_fwd.restype = i32
+    lib.kda_recurrent_step.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, f32, vp,
+                                       i32, vp]
+    lib.kda_recurrent_step.restype = i32
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = i32
+    lib.kda_last_hip_error.argtypes = []
+    lib.kda_last_hip_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(_load().kda_abi_version())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        detail = _load().kda_last_hip_error().decode() if status == 7 else ""
+        if status in (2, 3, 4, 5, 6):
+            raise ValueError(str(KDAError(fn, status, detail)))
+        raise KDAError(fn, status, detail)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KDA_F32
+    if t == torch.bfloat16:
+        return KDA_BF16
+    raise ValueError("unsupported dtype %s (float32 or bfloat16)" % t)
+
+
+def _dev(x: Optional[torch.Tensor], name: str, dtype=None) -> Optional[torch.Tensor]:
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, x.device))
+    if x.requires_grad:
+        raise ValueError("%s requires grad: the library provides no backward" % name)
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, x.dtype))
+    return x.contiguous()
+
+
+def _ptr(x: Optional[torch.Tensor]):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(x: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)
+
+
+def bounded_decay(logits: torch.Tensor, log_scale: torch.Tensor, lower_bound: float = -5.0,
+                  bias: Optional[torch.Tensor] = None, out_log: bool = False,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Retention factors alpha [..., H, K] (float32) from logits [..., H, K]
+    (float32 or bfloat16); with ``out_log`` the log-decay g instead."""
+    logits = _dev(logits, "logits")
+    log_scale = _dev(log_scale, "log_scale", torch.float32)
+    bias = _dev(bias, "bias", torch.float32)
+    if logits.dim() < 2:
+        raise ValueError("logits must be [..., H, K]")
+    H, K = logits.shape[-2], logits.shape[-1]
+    if log_scale.numel() != H or (bias is not None and bias.numel() != H * K):
+        raise ValueError("log_scale must be [H] and bias [H, K]")
+    rows = logits.numel() // (H * K) if H * K else 0
+    if out is None:
+        out = torch.empty(logits.shape, dtype=torch.float32, device=logits.device)
+    elif out.shape != logits.shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like logits")
+    with torch.cuda.device(logits.device):
+        st = _load().kda_bounded_decay(_ptr(logits), _dtype_code(logits.dtype), _ptr(log_scale),
+                                       _ptr(bias), float(lower_bound), rows, H, K,
+                                       GATE_LOG if out_log else GATE_ALPHA, _ptr(out), _stream(logits))
+    _check("kda_bounded_decay", st)
+    return out
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
+              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+              chunk_size: int = 32, scale: float = 1.0, gate_is_log: bool = False,
+              out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise prefill.  q, k [B,T,H,K]; v [B,T,H,V] (one dtype, float32 or
+    bfloat16); gate [B,T,H,K] float32 (alpha, or ln alpha with ``gate_is_log``);
+    beta [B,T,H] float32; initial_state [N,H,K,V] float32 or None; cu_seqlens
+    int32 [N+1] (B == 1) or None.  Returns (out [B,T,H,V], final_state [N,H,K,V]
+    or None).  ``final_state`` may be passed in (it may be ``initial_state``)."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    gate = _dev(gate, "gate", torch.float32)
+    beta = _dev(beta, "beta", torch.float32)
+    initial_state = _dev(initial_state, "initial_state", torch.float32)
+    cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, D]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or gate.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes: q %s k %s v %s gate %s beta %s" % (
+            tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(gate.shape), tuple(beta.shape)))
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if initial_state is not None and initial_state.shape != (N, H, K, V):
+        raise ValueError("initial_state must be [%d, %d, %d, %d]" % (N, H, K, V))
+    od = out_dtype or v.dtype
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=od, device=q.device)
+    elif out.shape != (B, T, H, V) or out.dtype != od or not out.is_contiguous():
+        raise ValueError("out must be contiguous [B,T,H,V] of the output dtype")
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+    if final_state is not None and (final_state.shape != (N, H, K, V) or final_state.dtype != torch.float32
+                                    or not final_state.is_contiguous()):
+        raise ValueError("final_state must be contiguous float32 [N,H,K,V]")
+    with torch.cuda.device(q.device):
+        st = _load().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(gate),
+                                   GATE_LOG if gate_is_log else GATE_ALPHA, _ptr(beta),
+                                   _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, B, T,
+                                   H, K, V, int(chunk_size), float(scale), _ptr(out), _dtype_code(od),
+                                   _stream(q))
+    _check("kda_chunk_fwd", st)
+    return out, final_state
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
+                   beta: torch.Tensor, state: torch.Tensor, scale: float = 1.0,
+                   gate_is_log: bool = False, out_dtype: Optional[torch.dtype] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode token.  q, k [B,H,K]; v [B,H,V]; gate [B,H,K] float32; beta [B,H]
+    float32; state [B,H,K,V] float32 contiguous, updated in place.  Returns out [B,H,V]."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    gate = _dev(gate, "gate", torch.float32)
+    beta = _dev(beta, "beta", torch.float32)
+    if not isinstance(state, torch.Tensor) or state.device.type != "cuda" or state.dtype != torch.float32 \
+            or not state.is_contiguous():
+        raise ValueError("state must be a contiguous float32 GPU tensor (it is updated in place)")
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, K]")
+    B, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or gate.shape != q.shape or v.shape != (B, H, V) or beta.shape != (B, H) \
+            or state.shape != (B, H, K, V):
+        raise ValueError("inconsistent shapes")
+    od = out_dtype or v.dtype
+    if out is None:
+        out = torch.empty((B, H, V), dtype=od, device=q.device)
+    with torch.cuda.device(q.device):
+        st = _load().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(gate),
+                                        GATE_LOG if gate_is_log else GATE_ALPHA, _ptr(beta), _ptr(state),
+                                        B, H, K, V, float(scale), _ptr(out), _dtype_code(od), _stream(q))
+    _check("kda_recurrent_step", st)
+    return out
+
+
+def recurrent_kda(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 32):
+    """PaperLeet ``recurrent_kda`` contract: (output [B,T,H,V], final_state [B,H,K,V]),
+    output in the inputs' dtype, every output read after its token's update, inputs
+    untouched; T == 0 returns the supplied state (or zeros)."""
+    return chunk_fwd(q, k, v, alpha, beta, initial_state=initial_state, output_final_state=True,
+                     chunk_size=chunk_size)

@@ -1,0 +1,156 @@
+// kda_api.hip -- the C ABI (include/kda.h): argument validation, the empty-sequence
+// path, and dispatch onto the kernels.  Nothing here allocates, synchronises or
+// prints; every launch goes onto the caller's stream.
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+kda_status hip_fail(hipError_t e) {
+    const char *msg = hipGetErrorString(e);
+    strncpy(g_last_hip_error, msg ? msg : "unknown HIP error", sizeof(g_last_hip_error) - 1);
+    g_last_hip_error[sizeof(g_last_hip_error) - 1] = 0;
+    return e == hipErrorNotSupported ? KDA_ERR_UNSUPPORTED : KDA_ERR_HIP;
+}
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
+bool gate_ok(kda_gate_kind g) { return g == KDA_GATE_ALPHA || g == KDA_GATE_LOG; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case KDA_ERR_BAD_SHAPE: return "bad shape";
+        case KDA_ERR_BAD_DTYPE: return "bad dtype or gate kind";
+        case KDA_ERR_UNSUPPORTED: return "unsupported size combination";
+        case KDA_ERR_BAD_ARGUMENT: return "bad argument";
+        case KDA_ERR_ALIAS: return "an output aliases an input";
+        case KDA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_last_hip_error(void) { return g_last_hip_error; }
+
+kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const float *log_scale,
+                             const float *bias, float lower_bound, int64_t rows, int H, int K,
+                             kda_gate_kind out_kind, float *out, hipStream_t stream) {
+    if (rows < 0 || H <= 0 || K <= 0) return KDA_ERR_BAD_SHAPE;
+    if (!dtype_ok(logits_dtype) || !gate_ok(out_kind)) return KDA_ERR_BAD_DTYPE;
+    if (!(lower_bound < 0.f)) return KDA_ERR_BAD_ARGUMENT;
+    if (rows == 0) return KDA_OK;
+    if (!logits || !log_scale || !out) return KDA_ERR_NULL_POINTER;
+    if ((const void *)out == logits || (const void *)out == (const void *)log_scale ||
+        (bias && (const void *)out == (const void *)bias))
+        return KDA_ERR_ALIAS;
+    kda::GateArgs a;
+    a.logits = logits;
+    a.log_scale = log_scale;
+    a.bias = bias;
+    a.out = out;
+    a.n = rows * (int64_t)H * K;
+    a.H = H;
+    a.K = K;
+    a.lower_bound = lower_bound;
+    a.out_log = out_kind == KDA_GATE_LOG;
+    a.vec8 = (K % 8 == 0) && ((uintptr_t)logits % 16 == 0) && ((uintptr_t)out % 16 == 0);
+    hipError_t e = kda::launch_bounded_decay(a, logits_dtype == KDA_F32, stream);
+    return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                         const float *gate, kda_gate_kind gate_kind, const float *beta,
+                         const float *initial_state, float *final_state,
+                         const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H, int K,
+                         int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
+                         hipStream_t stream) {
+    if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype) || !gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
+    if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+    if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_BAD_ARGUMENT;
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    const size_t state_bytes = (size_t)N * H * K * V * sizeof(float);
+
+    if (B == 0 || T == 0 || N == 0) {
+        // Empty sequence (PaperLeet contract, "Empty sequence"): nothing to scan;
+        // the final state is the supplied state, or zeros.
+        if (final_state && N > 0 && initial_state != final_state) {
+            hipError_t e = kda::launch_fill_copy(final_state, initial_state, (int64_t)(state_bytes / 4), stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        return KDA_OK;
+    }
+    if (!q || !k || !v || !gate || !beta || !out) return KDA_ERR_NULL_POINTER;
+    const void *ins[] = {q, k, v, gate, beta, initial_state, cu_seqlens};
+    for (const void *p : ins) {
+        if (p && (p == out || p == (const void *)final_state)) {
+            if (p == (const void *)initial_state && p == (const void *)final_state) continue;
+            return KDA_ERR_ALIAS;
+        }
+    }
+    if ((const void *)out == (const void *)final_state) return KDA_ERR_ALIAS;
+    if (N > (int64_t)(1 << 30) / H) return KDA_ERR_UNSUPPORTED;
+
+    kda::ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.gate = gate;
+    a.beta = beta;
+    a.initial_state = initial_state;
+    a.final_state = final_state;
+    a.cu_seqlens = cu_seqlens;
+    a.out = out;
+    a.T = T;
+    a.H = H;
+    a.gate_is_log = gate_kind == KDA_GATE_LOG;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    a.scale = scale;
+    int bv = 0;
+    hipError_t e = kda::launch_chunk_fwd(a, in_dtype == KDA_F32, K, V, chunk_size, (int)(N * H), stream, &bv);
+    return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
+kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                              const float *gate, kda_gate_kind gate_kind, const float *beta,
+                              float *state, int B, int H, int K, int V, float scale, void *out,
+                              kda_dtype out_dtype, hipStream_t stream) {
+    if (B < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype) || !gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
+    if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
+    if (B == 0) return KDA_OK;
+    if (!q || !k || !v || !gate || !beta || !state || !out) return KDA_ERR_NULL_POINTER;
+    const void *ins[] = {q, k, v, gate, beta};
+    for (const void *p : ins)
+        if (p == out || p == (const void *)state) return KDA_ERR_ALIAS;
+    if ((const void *)out == (const void *)state) return KDA_ERR_ALIAS;
+    if ((uintptr_t)state % 16 != 0) return KDA_ERR_BAD_ARGUMENT;
+    if ((int64_t)B * H > (int64_t)0x7fffffff) return KDA_ERR_UNSUPPORTED;
+    kda::StepArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.gate = gate;
+    a.beta = beta;
+    a.state = state;
+    a.out = out;
+    a.gate_is_log = gate_kind == KDA_GATE_LOG;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    a.scale = scale;
+    hipError_t e = kda::launch_recurrent_step(a, in_dtype == KDA_F32, K, V, B * H, stream);
+    return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
+}  // extern "C"

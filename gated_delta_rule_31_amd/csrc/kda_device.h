@@ -1,0 +1,96 @@
+// Device-side helpers shared by the KDA kernels (gfx950 only).
+//
+// Matrix-core wrappers: every product in the chunk kernel is a 16x16 output
+// tile accumulated in float32 from two operands staged in LDS with the
+// reduction index contiguous ("A rows x k" and "B columns x k").  Lane layouts
+// (wave64) of the instructions used:
+//   16x16x32 (bf16 / f16): lane l holds A[l%16][8*(l/16) .. +8] and B^T likewise;
+//   16x16x16 (bf16 / f16): lane l holds A[l%16][4*(l/16) .. +4];
+//   16x16x4  (f32):        lane l holds A[l%16][l/16];
+//   result: lane l holds D[4*(l/16) + e][l%16], e = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __attribute__((ext_vector_type(4))) float f4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+
+// acc += A[16 x kdim] * B[kdim x 16], A stored row-major with stride lda (k contiguous),
+// B stored as B^T: 16 rows (output columns) with stride ldb (k contiguous).
+// kdim is a multiple of 16 (of 4 for float).  Every lane of the wave must call it.
+template <typename T>
+__device__ __forceinline__ void mma_tile(f4 &acc, const T *A, int lda, const T *B, int ldb, int kdim,
+                                         int lane);
+
+template <>
+__device__ __forceinline__ void mma_tile<__bf16>(f4 &acc, const __bf16 *A, int lda, const __bf16 *B,
+                                                 int ldb, int kdim, int lane) {
+    const __bf16 *a = A + (lane & 15) * lda;
+    const __bf16 *b = B + (lane & 15) * ldb;
+    int k0 = 0;
+    for (; k0 + 32 <= kdim; k0 += 32) {
+        bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + k0 + 8 * (lane >> 4));
+        bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + k0 + 8 * (lane >> 4));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+    }
+    if (k0 < kdim) {
+        s16x4 av = *reinterpret_cast<const s16x4 *>(a + k0 + 4 * (lane >> 4));
+        s16x4 bv = *reinterpret_cast<const s16x4 *>(b + k0 + 4 * (lane >> 4));
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+    }
+}
+
+template <>
+__device__ __forceinline__ void mma_tile<_Float16>(f4 &acc, const _Float16 *A, int lda,
+                                                   const _Float16 *B, int ldb, int kdim, int lane) {
+    const _Float16 *a = A + (lane & 15) * lda;
+    const _Float16 *b = B + (lane & 15) * ldb;
+    int k0 = 0;
+    for (; k0 + 32 <= kdim; k0 += 32) {
+        f16x8 av = *reinterpret_cast<const f16x8 *>(a + k0 + 8 * (lane >> 4));
+        f16x8 bv = *reinterpret_cast<const f16x8 *>(b + k0 + 8 * (lane >> 4));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+    }
+    if (k0 < kdim) {
+        f16x4 av = *reinterpret_cast<const f16x4 *>(a + k0 + 4 * (lane >> 4));
+        f16x4 bv = *reinterpret_cast<const f16x4 *>(b + k0 + 4 * (lane >> 4));
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, acc, 0, 0, 0);
+    }
+}
+
+template <>
+__device__ __forceinline__ void mma_tile<float>(f4 &acc, const float *A, int lda, const float *B,
+                                                int ldb, int kdim, int lane) {
+    const float *a = A + (lane & 15) * lda + (lane >> 4);
+    const float *b = B + (lane & 15) * ldb + (lane >> 4);
+    for (int k0 = 0; k0 < kdim; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k0], b[k0], acc, 0, 0, 0);
+}
+
+// Load one element of an input tensor as float.
+__device__ __forceinline__ float ld_f32(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_f32(const __bf16 *p, int64_t i) { return (float)p[i]; }
+
+__device__ __forceinline__ void st_out(void *out, int is_bf16, int64_t i, float x) {
+    if (is_bf16)
+        static_cast<__bf16 *>(out)[i] = (__bf16)x;
+    else
+        static_cast<float *>(out)[i] = x;
+}
+
+}  // namespace kda

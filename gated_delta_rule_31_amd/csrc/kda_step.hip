@@ -1,0 +1,138 @@
+// kda_step.hip -- fused single-token KDA decode step over a kept state (gfx950).
+//
+// Per (batch row, head), with the float32 state S [K x V] kept in HBM and
+// updated in place ("Kept memory": the call starts from the kept memory,
+// updates it with the one new token and keeps the result; PaperLeet
+// "Formula and conventions" for the recurrence):
+//   Sbar  = Diag(alpha) S
+//   p     = Sbar^T k,  r = Sbar^T q                    (two reductions over K, one pass)
+//   delta = beta (v - p)
+//   S_t   = Sbar + k delta^T
+//   o     = scale S_t^T q = scale (r + (k . q) delta)  (no second pass over the state)
+// The step is bound by the state stream: 2*K*V*4 bytes per head against ~7*K*V
+// flops.  Each workgroup owns one state: it reads it once with 16-byte coalesced
+// loads into registers, reduces across threads through LDS, and writes it back
+// once.  No atomics: every output element has one writer.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+template <int K, int V>
+struct StepCfg {
+    static constexpr int CQ = V / 4;                              // float4 column groups
+    static constexpr int RPT = (K * CQ) / 256 > 0 ? (K * CQ) / 256 : 1;  // rows per thread
+    static constexpr int NRG = K / RPT;                           // row groups
+    static constexpr int NT = CQ * NRG;                           // threads
+    static_assert(NT <= 256 && NRG * RPT == K, "step mapping");
+};
+
+template <typename TIn, int K, int V>
+__global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(StepArgs a) {
+    using Cf = StepCfg<K, V>;
+    constexpr int CQ = Cf::CQ, RPT = Cf::RPT, NRG = Cf::NRG;
+    __shared__ float red_p[NRG][V];
+    __shared__ float red_r[NRG][V];
+    __shared__ float red_kq[NRG];
+    __shared__ float dlt[V];
+    __shared__ float kq_s;
+
+    const int pair = blockIdx.x;  // b * H + h
+    const int tid = threadIdx.x;
+    const int cq = tid % CQ;  // this thread's 4 value columns: 4*cq .. 4*cq+3
+    const int rg = tid / CQ;  // this thread's key rows: rg + NRG * i
+    const TIn *q = static_cast<const TIn *>(a.q) + (int64_t)pair * K;
+    const TIn *k = static_cast<const TIn *>(a.k) + (int64_t)pair * K;
+    const TIn *v = static_cast<const TIn *>(a.v) + (int64_t)pair * V;
+    const float *gate = a.gate + (int64_t)pair * K;
+    float4 *S = reinterpret_cast<float4 *>(a.state + (int64_t)pair * K * V);
+
+    float4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = S[(rg + NRG * i) * CQ + cq];
+
+    float4 pp = {0.f, 0.f, 0.f, 0.f}, rr = {0.f, 0.f, 0.f, 0.f};
+    float kq = 0.f;
+    float kr[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + NRG * i;
+        const float g = gate[row];
+        const float al = a.gate_is_log ? expf(g) : g;
+        const float kv = ld_f32(k, row), qv = ld_f32(q, row);
+        kr[i] = kv;
+        kq += kv * qv;
+        s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
+        pp.x += s[i].x * kv; pp.y += s[i].y * kv; pp.z += s[i].z * kv; pp.w += s[i].w * kv;
+        rr.x += s[i].x * qv; rr.y += s[i].y * qv; rr.z += s[i].z * qv; rr.w += s[i].w * qv;
+    }
+    red_p[rg][4 * cq + 0] = pp.x; red_p[rg][4 * cq + 1] = pp.y;
+    red_p[rg][4 * cq + 2] = pp.z; red_p[rg][4 * cq + 3] = pp.w;
+    red_r[rg][4 * cq + 0] = rr.x; red_r[rg][4 * cq + 1] = rr.y;
+    red_r[rg][4 * cq + 2] = rr.z; red_r[rg][4 * cq + 3] = rr.w;
+    if (cq == 0) red_kq[rg] = kq;
+    __syncthreads();
+    if (tid == 0) {
+        float x = 0.f;
+        for (int g2 = 0; g2 < NRG; ++g2) x += red_kq[g2];
+        kq_s = x;
+    }
+    __syncthreads();
+    if (tid < V) {
+        float p = 0.f, r = 0.f;
+        for (int g2 = 0; g2 < NRG; ++g2) {
+            p += red_p[g2][tid];
+            r += red_r[g2][tid];
+        }
+        const float d = a.beta[pair] * (ld_f32(v, tid) - p);
+        dlt[tid] = d;
+        st_out(a.out, a.out_bf16, (int64_t)pair * V + tid, a.scale * (r + kq_s * d));
+    }
+    __syncthreads();
+    const float4 d4 = {dlt[4 * cq], dlt[4 * cq + 1], dlt[4 * cq + 2], dlt[4 * cq + 3]};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        float4 x = s[i];
+        x.x += kr[i] * d4.x; x.y += kr[i] * d4.y; x.z += kr[i] * d4.z; x.w += kr[i] * d4.w;
+        S[(rg + NRG * i) * CQ + cq] = x;
+    }
+}
+
+template <typename TIn, int K>
+hipError_t launch_k(const StepArgs &a, int V, int pairs, hipStream_t stream) {
+    switch (V) {
+#define KDA_STEP_CASE(VV)                                                                         \
+    case VV:                                                                                      \
+        hipLaunchKernelGGL((recurrent_step_kernel<TIn, K, VV>), dim3(pairs), dim3(StepCfg<K, VV>::NT), \
+                           0, stream, a);                                                        \
+        return hipGetLastError();
+        KDA_STEP_CASE(16)
+        KDA_STEP_CASE(32)
+        KDA_STEP_CASE(64)
+        KDA_STEP_CASE(128)
+#undef KDA_STEP_CASE
+        default: return hipErrorNotSupported;
+    }
+}
+
+template <typename TIn>
+hipError_t launch_t(const StepArgs &a, int K, int V, int pairs, hipStream_t stream) {
+    switch (K) {
+        case 16: return launch_k<TIn, 16>(a, V, pairs, stream);
+        case 32: return launch_k<TIn, 32>(a, V, pairs, stream);
+        case 64: return launch_k<TIn, 64>(a, V, pairs, stream);
+        case 128: return launch_k<TIn, 128>(a, V, pairs, stream);
+        default: return hipErrorNotSupported;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent_step(const StepArgs &a, bool fp32_inputs, int K, int V, int pairs,
+                                 hipStream_t stream) {
+    return fp32_inputs ? launch_t<float>(a, K, V, pairs, stream) : launch_t<__bf16>(a, K, V, pairs, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,153 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * What is computed (definitions from the pages):
+ *  - "Kimi K3: Bounded Decay and Delta Memory" (PaperLeet), section "Formula
+ *    and conventions": the bounded per-channel gate
+ *        g = g_min * sigmoid(e^A * z),   alpha = e^g   (alpha in [e^g_min, 1]),
+ *    and the per-token recurrence
+ *        Sbar_t = Diag(alpha_t) S_{t-1}
+ *        S_t    = Sbar_t + beta_t k_t (v_t - k_t^T Sbar_t)^T
+ *        o_t    = scale * S_t^T q_t          (scale = 1: the scan does no query scaling).
+ *  - KDA cheat sheet, "Chunkwise parallel form": the same recurrence evaluated
+ *    chunk by chunk (recurrent across chunks, parallel within a chunk); and the
+ *    gate table: g >= -5 bounds the cumulative log-decay of a 16-token tile by
+ *    -80, which keeps every rescale factor of the chunk kernel finite.
+ *  - "Kept memory" page: the per-head state is kept between calls and a decode
+ *    call updates it with one new token.
+ *
+ * Conventions for every entry point:
+ *  - Every pointer argument is a DEVICE pointer, except where stated.  The caller
+ *    owns every buffer; the library never allocates, never synchronises and never
+ *    prints.  Work is enqueued on `stream` (NULL = the default stream) and the
+ *    call returns as soon as it is enqueued.
+ *  - Tensors are dense, row-major, innermost dimension last.  Token tensors are
+ *    [B, T, H, D] (q, k, gate: D = K; v, out: D = V); beta is [B, T, H]; states
+ *    are [N, H, K, V] (key rows, value columns: the pages' key-by-value
+ *    orientation).  Element types are given by the kda_dtype arguments; gate,
+ *    beta and states are always float32.
+ *  - Inputs are never written.  Outputs must not overlap any input (checked for
+ *    the obvious cases: equal base pointers -> KDA_ERR_ALIAS).
+ *  - Errors are returned synchronously from host-side validation, before anything
+ *    is enqueued; KDA_ERR_HIP means the launch itself failed.  Faults inside a
+ *    kernel surface, as usual for HIP, at the caller's next synchronisation.
+ *  - Preconditions not checked on the device: finite inputs.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+    KDA_ERR_BAD_SHAPE = 2,    /* a size is negative/zero where it must be positive */
+    KDA_ERR_BAD_DTYPE = 3,    /* unknown dtype or gate kind */
+    KDA_ERR_UNSUPPORTED = 4,  /* sizes outside the compiled set (see each call) */
+    KDA_ERR_BAD_ARGUMENT = 5, /* e.g. lower_bound >= 0, cu_seqlens with B != 1 */
+    KDA_ERR_ALIAS = 6,        /* an output buffer is also an input buffer */
+    KDA_ERR_HIP = 7           /* the kernel launch failed */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* How a gate tensor is given: retention factors alpha in [0, 1], or their natural
+ * logarithm g = ln(alpha) <= 0. */
+typedef enum { KDA_GATE_ALPHA = 0, KDA_GATE_LOG = 1 } kda_gate_kind;
+
+/*
+ * kda_bounded_decay -- the bounded per-channel decay gate (PaperLeet "Formula and
+ * conventions", operator bounded_decay; cheat sheet gate table, Kimi K3 column).
+ *
+ *   out[r,h,c] = alpha   = exp(g)                     if out_kind == KDA_GATE_ALPHA
+ *              = g       = lower_bound * sigmoid(exp(log_scale[h]) * (logits[r,h,c] + bias[h*K+c]))
+ *                                                     if out_kind == KDA_GATE_LOG
+ *   logits    [rows, H, K] in logits_dtype (rows = B*T)
+ *   log_scale [H] float32 (the per-head A; the applied scale is e^A)
+ *   bias      [H*K] float32 or NULL (a featurewise offset added before the scale)
+ *   lower_bound  g_min, must be < 0 (the pages use -5)
+ *   out       [rows, H, K] float32
+ * Arithmetic is float32 with a sign-split sigmoid that never overflows.
+ * rows == 0 enqueues nothing.  Any H, K >= 1 is supported.
+ */
+kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const float *log_scale,
+                             const float *bias, float lower_bound, int64_t rows, int H, int K,
+                             kda_gate_kind out_kind, float *out, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd -- chunkwise-parallel prefill of the recurrence (cheat sheet
+ * "Chunkwise parallel form"; PaperLeet recurrent_kda contract for shapes, the
+ * read-after-write output and the empty-sequence rule).
+ *
+ *   q, k   [B, T, H, K] in in_dtype;  v [B, T, H, V] in in_dtype
+ *   gate   [B, T, H, K] float32, retention (KDA_GATE_ALPHA) or log-retention (KDA_GATE_LOG)
+ *   beta   [B, T, H] float32 write strengths
+ *   initial_state [N, H, K, V] float32, or NULL for zeros
+ *   final_state   [N, H, K, V] float32, or NULL (not written).  It may equal
+ *                 initial_state (in-place resume); no other overlap is allowed.
+ *   cu_seqlens    NULL: N = B sequences of length T (one per batch row).
+ *                 Otherwise int32 [num_seqs + 1] device array of packed offsets
+ *                 (B must be 1, cu_seqlens[0] = 0, cu_seqlens[num_seqs] = T,
+ *                 non-decreasing; zero-length sequences are allowed and get
+ *                 final = initial).  N = num_seqs; the state restarts at every
+ *                 sequence.  The offsets are read only on the device.
+ *   chunk_size    16, 32 or 64: tokens per chunk (results differ only by rounding)
+ *   scale         multiplies every output (1.0 = no query scaling)
+ *   out    [B, T, H, V] in out_dtype
+ * Supported: K, V in {16, 32, 64, 128}.  in_dtype KDA_F32 computes in float32
+ * (matrix cores in fp32); KDA_BF16 uses bf16/fp16 matrix-core operands with
+ * float32 accumulation and a float32 master state.
+ * Preconditions: every log-decay ln(alpha) >= -5 (the K3 bound; it is what keeps
+ * the chunk's rescale factors inside float range; alpha = 0 is not allowed here);
+ * on the bf16 path the state, the values and the per-chunk pseudo-values stay
+ * below 6.5e4 in magnitude (they pass through fp16 matrix-core operands).
+ * T == 0 (or B == 0): nothing is launched for the scan; final_state is set to
+ * initial_state (copied unless the pointers are equal) or zeros.
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                         const float *gate, kda_gate_kind gate_kind, const float *beta,
+                         const float *initial_state, float *final_state,
+                         const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H, int K,
+                         int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
+                         hipStream_t stream);
+
+/*
+ * kda_recurrent_step -- one decode token over a kept state, updated IN PLACE
+ * ("Kept memory": the call starts from the kept memory, updates it with the one
+ * new token and keeps the result; PaperLeet recurrence with T = 1).
+ *
+ *   q, k  [B, H, K] in in_dtype;  v [B, H, V] in in_dtype
+ *   gate  [B, H, K] float32 (alpha or ln alpha, per gate_kind; any alpha in [0, 1])
+ *   beta  [B, H] float32
+ *   state [B, H, K, V] float32, read and overwritten with S_t
+ *   out   [B, H, V] in out_dtype: o = scale * S_t^T q
+ * Supported: K, V in {16, 32, 64, 128}.  All arithmetic is float32.  B == 0
+ * enqueues nothing.
+ */
+kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                              const float *gate, kda_gate_kind gate_kind, const float *beta,
+                              float *state, int B, int H, int K, int V, float scale, void *out,
+                              kda_dtype out_dtype, hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char *kda_status_string(kda_status s);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Text of the last HIP launch error seen by this thread (empty if none). */
+const char *kda_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

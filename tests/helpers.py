@@ -1,0 +1,81 @@
+"""Shared test helpers: tolerance rules, oracle pipelines, tensor conversion."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+# Tolerances stated with the workload: float32 inputs -- max relative error 1e-4,
+# element error relative to max(|y|, rms(y)); bfloat16 inputs -- max error 2e-2 of the
+# oracle's RMS, for the output and the state separately.
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+def f64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def err_fp32(got, ref) -> float:
+    got, ref = f64(got), f64(ref)
+    if ref.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(ref ** 2))
+    den = np.maximum(np.abs(ref), rms)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(got - ref) / den))
+
+
+def err_bf16(got, ref) -> float:
+    got, ref = f64(got), f64(ref)
+    if ref.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(ref ** 2))
+    return float(np.max(np.abs(got - ref)) / (rms if rms > 0 else 1.0))
+
+
+def assert_close(got, ref, fp32: bool, what: str = ""):
+    e = err_fp32(got, ref) if fp32 else err_bf16(got, ref)
+    tol = FP32_TOL if fp32 else BF16_TOL
+    assert np.all(np.isfinite(f64(got))), "%s: non-finite values" % what
+    assert e <= tol, "%s: error %.3e > %.1e" % (what, e, tol)
+    return e
+
+
+def oracle_prefill(inp, heads=None, seqs=None):
+    """fp64 oracle of the whole prefill path: z -> gate -> scan.  Optional subsets of
+    heads / sequences (their outputs only) for sampled checks at full size."""
+    H = inp.q.shape[2]
+    hs = list(range(H)) if heads is None else list(heads)
+    q, k, v, z = (f64(x[:, :, hs]) for x in (inp.q, inp.k, inp.v, inp.z))
+    beta = f64(inp.beta[:, :, hs])
+    ls = f64(inp.log_scale)[hs]
+    alpha = oracle.bounded_decay(z, ls, g_min=inp.g_min)
+    s0 = None if inp.initial_state is None else f64(inp.initial_state[:, hs])
+    cu = None if inp.cu_seqlens is None else f64(inp.cu_seqlens).astype(np.int64)
+    if seqs is not None:
+        assert cu is not None
+        outs, fins, rows = [], [], []
+        for s in seqs:
+            a0, a1 = int(cu[s]), int(cu[s + 1])
+            sl = slice(a0, a1)
+            o, f = oracle.scan(q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl],
+                               None if s0 is None else s0[s:s + 1])
+            outs.append(o); fins.append(f); rows.append((a0, a1))
+        return outs, fins, rows
+    return oracle.scan(q, k, v, alpha, beta, s0, cu_seqlens=cu)
+
+
+def gpu_prefill(inp, chunk_size=32, out_dtype=torch.float32, device="cuda"):
+    """GPU path z -> gate -> chunk prefill.  Parity is judged on float32 outputs: a
+    bfloat16 output is that float32 value rounded once more (checked separately), and
+    that last rounding alone can exceed 2e-2 of the RMS on heavy-tailed outputs."""
+    import gated_delta_rule_31_amd as kda
+    d = lambda x: None if x is None else x.to(device)
+    g = kda.bounded_decay(d(inp.z), d(inp.log_scale), lower_bound=inp.g_min, out_log=True)
+    return kda.chunk_fwd(d(inp.q), d(inp.k), d(inp.v), g, d(inp.beta), initial_state=d(inp.initial_state),
+                         cu_seqlens=d(inp.cu_seqlens), chunk_size=chunk_size, gate_is_log=True,
+                         out_dtype=out_dtype)

@@ -1,0 +1,101 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and its
+host-side validation returns the documented status codes without launching."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+LIB = os.path.join(ROOT, "gated_delta_rule_31_amd", "libkda.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libkda.so is not built; run __graft_entry__.build()")
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kda_bounded_decay", "kda_chunk_fwd", "kda_recurrent_step"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "missing export %s" % n
+
+
+def test_status_strings_and_version(lib):
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    assert lib.kda_status_string(0) == b"ok"
+    for s in range(1, 8):
+        assert lib.kda_status_string(s) not in (b"", b"unknown status")
+    assert lib.kda_abi_version() == 1
+
+
+def _chunk(lib, **kw):
+    vp = ctypes.c_void_p
+    args = dict(q=1, k=2, v=3, in_dtype=1, gate=4, gate_kind=1, beta=5, s0=None, sf=None, cu=None,
+                num_seqs=0, B=1, T=64, H=2, K=16, V=16, C=16, scale=1.0, out=6, out_dtype=1)
+    args.update(kw)
+    f = lib.kda_chunk_fwd
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                  vp, ctypes.c_int, vp]
+    a = args
+    return f(a["q"], a["k"], a["v"], a["in_dtype"], a["gate"], a["gate_kind"], a["beta"], a["s0"], a["sf"],
+             a["cu"], a["num_seqs"], a["B"], a["T"], a["H"], a["K"], a["V"], a["C"], a["scale"], a["out"],
+             a["out_dtype"], None)
+
+
+# Each case is rejected on the host before any HIP call (the pointers are fake).
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=17), 4), (dict(V=256), 4), (dict(C=48), 4), (dict(H=0), 2), (dict(T=-1), 2),
+    (dict(in_dtype=7), 3), (dict(gate_kind=5), 3), (dict(q=None), 1), (dict(out=None), 1),
+    (dict(cu=9, B=2, num_seqs=1), 5), (dict(out=3), 6), (dict(sf=4), 6), (dict(sf=6), 6),
+])
+def test_chunk_validation(lib, kw, status):
+    assert _chunk(lib, **kw) == status
+
+
+def test_gate_validation(lib):
+    vp = ctypes.c_void_p
+    f = lib.kda_bounded_decay
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_float, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, vp, vp]
+    assert f(1, 1, 2, None, 0.0, 4, 2, 8, 0, 3, None) == 5      # lower_bound must be < 0
+    assert f(1, 1, 2, None, -5.0, 4, 0, 8, 0, 3, None) == 2     # H = 0
+    assert f(1, 9, 2, None, -5.0, 4, 2, 8, 0, 3, None) == 3     # bad dtype
+    assert f(None, 1, 2, None, -5.0, 4, 2, 8, 0, 3, None) == 1  # NULL logits
+    assert f(1, 1, 2, None, -5.0, 4, 2, 8, 0, 1, None) == 6     # out aliases logits
+    assert f(None, 1, None, None, -5.0, 0, 2, 8, 0, None, None) == 0  # rows = 0: nothing to do
+
+
+def test_step_validation(lib):
+    vp = ctypes.c_void_p
+    f = lib.kda_recurrent_step
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp]
+    assert f(1, 2, 3, 1, 4, 0, 5, 16, 2, 2, 24, 16, 1.0, 7, 1, None) == 4     # K = 24
+    assert f(1, 2, 3, 1, 4, 0, 5, None, 2, 2, 16, 16, 1.0, 7, 1, None) == 1   # NULL state
+    assert f(1, 2, 3, 1, 4, 0, 5, 16, 2, 2, 16, 16, 1.0, 3, 1, None) == 6     # out aliases v
+    assert f(1, 2, 3, 1, 4, 0, 5, 18, 2, 2, 16, 16, 1.0, 7, 1, None) == 5     # misaligned state
+    assert f(None, None, None, 1, None, 0, None, None, 0, 2, 16, 16, 1.0, None, 1, None) == 0  # B = 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import gated_delta_rule_31_amd as kda
+    z = torch.zeros(2, 3, 16)
+    with pytest.raises(ValueError):
+        kda.bounded_decay(z, torch.zeros(3))
