@@ -95,10 +95,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(ev_pair=None):
-        kda.bounded_decay(z, ls, lower_bound=-5.0, out_log=True, out=g)
+        kda.bounded_decay(z, ls, lower_bound=-5.0, out_log=False, out=g)
         if ev_pair is not None:
             ev_pair[0].record(stream)
-        kda.chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=args.chunk, gate_is_log=True,
+        kda.chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=args.chunk, gate_is_log=False,
                       out=out, final_state=fin)
         if ev_pair is not None:
             ev_pair[1].record(stream)

@@ -25,7 +25,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["bounded_decay", "chunk_fwd", "recurrent_step", "recurrent_kda", "KDAError",
+__all__ = ["bounded_decay", "chunk_fwd", "recurrent_step", "recurrent_kda", "KDAError", "chunk_fwd_supported",
            "library_path", "abi_version", "GATE_ALPHA", "GATE_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,8 @@ def _load():
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
     lib.kda_abi_version.restype = i32
+    lib.kda_chunk_fwd_supported.argtypes = [i32, i32, i32, i32]
+    lib.kda_chunk_fwd_supported.restype = i32
     lib.kda_last_hip_error.argtypes = []
     lib.kda_last_hip_error.restype = ctypes.c_char_p
     _lib = lib
@@ -79,6 +81,11 @@ def _load():
 
 def abi_version() -> int:
     return int(_load().kda_abi_version())
+
+
+def chunk_fwd_supported(dtype: torch.dtype, K: int, V: int, chunk_size: int) -> int:
+    """Value columns per workgroup kda_chunk_fwd uses for this shape, 0 if unsupported."""
+    return int(_load().kda_chunk_fwd_supported(_dtype_code(dtype), int(K), int(V), int(chunk_size)))
 
 
 def _check(fn: str, status: int):

@@ -41,6 +41,12 @@ const char *kda_status_string(kda_status s) {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
+int kda_chunk_fwd_supported(kda_dtype in_dtype, int K, int V, int chunk_size) {
+    if (!dtype_ok(in_dtype) || !dim_ok(K) || !dim_ok(V)) return 0;
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return 0;
+    return kda::chunk_fwd_value_block(in_dtype == KDA_F32, K, V, chunk_size);
+}
+
 const char *kda_last_hip_error(void) { return g_last_hip_error; }
 
 kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const float *log_scale,

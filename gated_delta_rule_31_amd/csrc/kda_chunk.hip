@@ -1,40 +1,44 @@
 // kda_chunk.hip -- chunkwise-parallel KDA prefill on gfx950 matrix cores.
 //
 // Method (KDA cheat sheet, "Chunkwise parallel form", with the UT transform the
-// page names written out): for a chunk of C tokens with start state S and
-// in-chunk inclusive cumulative log-decay Gamma_i = sum_{r<=i} g_r (per key
-// channel),
-//   A_kk[i,j] = beta_i sum_c k_ic k_jc e^{Gamma_ic - Gamma_jc}  (j < i),  T = (I + A_kk)^-1
-//   W = T (beta e^Gamma K),  U = T (beta V),  Vt = U - W S          (pseudo-values)
-//   A_qk[i,j] = sum_c q_ic k_jc e^{Gamma_ic - Gamma_jc}           (j <= i: the read
-//               follows the write, so the diagonal is kept)
-//   O  = (e^Gamma Q) S + A_qk Vt                                    (inter + intra chunk)
-//   S' = e^{Gamma_C} S + (K e^{Gamma_C - Gamma})^T Vt
-// This equals the token recurrence exactly in real arithmetic.
+// page names written out): for a chunk of C tokens with start state S and in-chunk
+// cumulative decay gamma_i = prod_{r<=i} alpha_r (per key channel),
+//   A_kk[i,j] = beta_i sum_c k_ic k_jc gamma_ic / gamma_jc   (j < i),  T = (I + A_kk)^-1
+//   Vt = T (beta V - (beta gamma K) S)                     (= U - W S, the pseudo-values)
+//   A_qk[i,j] = sum_c q_ic k_jc gamma_ic / gamma_jc         (j <= i: each read follows
+//                                                          its own write, so the diagonal stays)
+//   O  = (gamma Q) S + A_qk Vt                              (inter + intra chunk)
+//   S' = gamma_C S + (K gamma_C / gamma)^T Vt
+// which equals the token recurrence exactly in real arithmetic.
 //
-// Rescaling (cheat sheet gate table): with every g >= -5 the log-decay across a
-// 16-token tile stays above -80, so the split e^{Gamma_i - Gamma_j} =
-// e^{Gamma_i - R} e^{R - Gamma_j} with a per-tile reference R keeps both factors
-// within [e^-80, e^80] -- inside float and bf16 range -- and every tile of A_kk
-// and A_qk is a dense matrix-core product:
-//   diagonal tile p:      R = Gamma at the row before tile p,
-//   off-diagonal (p, q):  left e^{Gamma_i - R_p} (<= 1), right e^{R_p - Gamma_j} (<= 1),
-//                         built as k_j e^{E_q - Gamma_j} times e^{R_p - E_q} (E_q = Gamma at
-//                         the last row of tile q) so that nothing underflows early.
-// Gamma is carried in log2 units so each factor is one exp2.
+// Rescaling (cheat sheet gate table): with every log-decay >= -5, a 16-token tile
+// decays by at most e^-80, so each ratio gamma_i / gamma_j is split at a per-tile
+// reference into two factors inside [e^-80, e^80] -- within float and bf16 range --
+// and every tile of A_kk and A_qk is a dense matrix-core product.  With R_p / E_p
+// the cumulative decay before / at the end of 16-row tile p:
+//   diagonal tile p:         (gamma_i / R_p) * (R_p / gamma_j)
+//   off-diagonal tile (p,q): (gamma_i / R_p) * (R_p / gamma_j), the right factor built
+//                            as (E_q / gamma_j) * (R_p / E_q) so nothing underflows early.
+// All factors are products of retention factors (in-tile prefix and suffix
+// products), so no per-element exponential is needed.
 //
-// Work decomposition: one workgroup (4 waves) per (sequence, head, block of BV
-// value columns).  Value columns of the state evolve independently, so the
-// split is exact; the key-side work of a chunk is recomputed per value block.
-// The float32 master state lives in the accumulator registers across chunks; an
-// operand copy sits in LDS.
+// Work decomposition: one workgroup of 8 waves per (sequence, head, block of BV
+// value columns); value columns evolve independently, so the split is exact.
+//  * 4 state waves own the float32 state S[K x BV] in registers (one 16-column tile
+//    each) and run the serial part for chunk n: Y = beta V - Bw S, Vt = T Y,
+//    O = Qt S + A_qk Vt, S = gamma_C S + Kt^T Vt.  Their matrix-core operands come
+//    straight from the accumulators of the previous product (the k order of each
+//    product is permuted to match the accumulator layout), so the state never
+//    round-trips through LDS.
+//  * 4 prep waves build chunk n+1's package (Qt, -Bw, Kt, T, A_qk, beta V, gamma_C)
+//    in the other half of a double-buffered LDS area, and prefetch chunk n+2's raw
+//    inputs into registers.  Three workgroup barriers per chunk.
 //
-// Precision (bf16 inputs): the A-matrix operands carry factors up to e^80 and
-// use bf16; A_qk, which feeds each token's own value straight to its output, is
-// formed from hi+lo bf16 splits of both operands.  Every other product has
-// operands bounded by ~1 or by the state/value magnitude and uses fp16, which
-// has 3 more mantissa bits than bf16.  fp32 inputs use fp32 matrix cores
-// throughout.
+// Precision (bf16 inputs): the A-matrix operands carry factors up to e^80 and use
+// bf16; A_qk, which carries each token's own value to its output, is formed from
+// hi+lo bf16 splits of both operands.  Every other product has operands bounded by
+// ~1 or by the state/value magnitude and uses fp16 (3 more mantissa bits than
+// bf16).  fp32 inputs use fp32 matrix cores throughout.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -42,11 +46,11 @@ namespace kda {
 
 namespace {
 
-constexpr int NT = 256;  // threads per workgroup
-constexpr int NW = NT / 64;
+constexpr int NT = 512;   // threads per workgroup
+constexpr int NSW = 4;    // state waves: 0..3
+constexpr int NPT = 256;  // prep threads: waves 4..7
 
 constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
-constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 struct PrecMixed {
     using TA = __bf16;    // operands of the decay-rescaled key/query products
@@ -65,58 +69,207 @@ struct Layout {
     using TM = typename P::TM;
     static constexpr int NP = C / 16;                                  // 16-row tiles per chunk
     static constexpr int NX = NP >= 3 ? (NP - 1) * (NP - 2) / 2 : 0;  // tiles (p,q) with q <= p-2
-    static constexpr int NSPL = P::kSplit ? 2 : 1;
     static constexpr int LKA = K + 16 / (int)sizeof(TA);  // padded row strides (elements)
     static constexpr int LKM = K + 16 / (int)sizeof(TM);
     static constexpr int LCM = C + 16 / (int)sizeof(TM);
     static constexpr int LCF = C + 4;
-    static constexpr int NSEG = NT / K;      // threads sharing one key channel in the prep
-    static constexpr int RPS = C / NSEG;     // rows per prep thread
-    static_assert(NSEG >= 1 && RPS >= 1 && C % NSEG == 0, "prep mapping");
+    static constexpr int LKF = K + 4;                           // fp32 staging rows
+    static constexpr int NTC = NP * K;                          // prep tile-columns
+    static constexpr int TCPT = (NTC + NPT - 1) / NPT;          // tile-columns per prep thread
+    static constexpr int NJT = BV / 16;                         // value column tiles
+    static constexpr int MJ = (NJT + NSW - 1) / NSW;            // column tiles per state wave
 
-    static constexpr size_t szA = al16((size_t)C * LKA * sizeof(TA));
-    // region 1: A-phase operands; after the A phase it holds Tm, W and Vt
+    // prep-private
+    // Lk in the A-operand type; Lq, Rd, Ro and the extra versions X staged in fp32 (the
+    // matrix-core tasks round them to bf16, or split them into hi + lo bf16, as they load)
     static constexpr size_t oLk = 0;
-    static constexpr size_t oLq = oLk + szA;
-    static constexpr size_t oRd = oLq + NSPL * szA;
-    static constexpr size_t oRo = oRd + NSPL * szA;
-    static constexpr size_t szRo = al16((size_t)(C - 16) * LKA * sizeof(TA));
-    static constexpr size_t oX = oRo + NSPL * szRo;
-    static constexpr size_t szX = al16((size_t)16 * LKA * sizeof(TA));
-    static constexpr size_t r1a = oX + (size_t)NSPL * NX * szX;
-    static constexpr size_t oTm = 0;
-    static constexpr size_t oW = oTm + al16((size_t)C * LCM * sizeof(TM));
-    static constexpr size_t oVt = oW + al16((size_t)C * LKM * sizeof(TM));
-    static constexpr size_t r1b = oVt + al16((size_t)BV * LCM * sizeof(TM));
-    static constexpr size_t r1 = cmax(r1a, r1b);
-    // region 2: the other per-chunk operands
-    static constexpr size_t oQt = r1;
-    static constexpr size_t oBw = oQt + al16((size_t)C * LKM * sizeof(TM));
-    static constexpr size_t oKt = oBw + al16((size_t)K * LCM * sizeof(TM));
-    static constexpr size_t obV = oKt + al16((size_t)K * LCM * sizeof(TM));
-    // region 3: A_kk, T (fp32 while it is built), A_qk, scratch for T's off-diagonal blocks
-    static constexpr size_t oAkk = obV + al16((size_t)BV * LCM * sizeof(TM));
+    static constexpr size_t oLq = oLk + al16((size_t)C * LKA * sizeof(TA));
+    static constexpr size_t oRd = oLq + al16((size_t)C * LKF * 4);
+    static constexpr size_t oRo = oRd + al16((size_t)C * LKF * 4);
+    static constexpr size_t oX = oRo + al16((size_t)(C > 16 ? C - 16 : 0) * LKF * 4);
+    static constexpr size_t oAkk = oX + al16((size_t)NX * 16 * LKF * 4);
     static constexpr size_t oTf = oAkk + al16((size_t)C * LCF * 4);
-    static constexpr size_t oAqk = oTf + al16((size_t)C * LCF * 4);
-    static constexpr size_t oM = oAqk + al16((size_t)C * LCM * sizeof(TM));
-    // persistent: operand copy of the state (S^T: value rows, key contiguous)
-    static constexpr size_t oSt = oM + al16((size_t)3 * 256 * 4);
-    // per-chunk vectors (float): references R[NP][K], E[NP][K], e^{Gamma_C}[K],
-    // segment totals [NSEG][K], beta [C]
-    static constexpr size_t oR = oSt + al16((size_t)BV * LKM * sizeof(TM));
-    static constexpr size_t oE = oR + (size_t)NP * K * 4;
-    static constexpr size_t oGC = oE + (size_t)NP * K * 4;
-    static constexpr size_t oEGC = oGC + (size_t)K * 4;
-    static constexpr size_t oSeg = oEGC + (size_t)K * 4;
-    static constexpr size_t oBeta = oSeg + (size_t)NSEG * K * 4;
-    static constexpr size_t total = al16(oBeta + (size_t)C * 4);
+    static constexpr size_t oTP = oTf + al16((size_t)C * LCF * 4);
+    static constexpr size_t oBt = oTP + al16((size_t)NP * K * 4);
+    static constexpr size_t oPkg = oBt + al16((size_t)C * 4);
+    // package (two copies)
+    static constexpr size_t pQt = 0;
+    static constexpr size_t pBw = pQt + al16((size_t)C * LKM * sizeof(TM));
+    static constexpr size_t pKt = pBw + al16((size_t)C * LKM * sizeof(TM));
+    static constexpr size_t pTm = pKt + al16((size_t)K * LCM * sizeof(TM));
+    static constexpr size_t pAqk = pTm + al16((size_t)C * LCM * sizeof(TM));
+    static constexpr size_t pbV = pAqk + al16((size_t)C * LCM * sizeof(TM));
+    static constexpr size_t pGC = pbV + al16((size_t)BV * LCM * sizeof(TM));
+    static constexpr size_t szPkg = al16(pGC + (size_t)K * 4);
+    static constexpr size_t total = oPkg + 2 * szPkg;
     static constexpr bool fits = total <= 160 * 1024;
-
-    static constexpr int NTO = NP * (BV / 16);         // [C x BV] output / pseudo-value tiles
-    static constexpr int NTS = (K / 16) * (BV / 16);   // [K x BV] state tiles
-    static constexpr int MO = (NTO + NW - 1) / NW;     // tiles owned per wave
-    static constexpr int MS = (NTS + NW - 1) / NW;
 };
+
+// ---- matrix-core products whose B operand comes from accumulator tiles ----------------
+//
+// A D-layout accumulator tile (lane l holds rows 4*(l/16)+e, column l%16) is, after
+// conversion, directly a B operand when the k order is permuted: a 16x16x32 step over
+// k tiles (2m, 2m+1) takes k = 32m + 4g + i (i < 4) and 32m + 16 + 4g + (i-4) (i >= 4)
+// for lane group g = l/16; an odd last tile takes k = 16t + 4g + i in the lower half of
+// the same instruction (upper half zero); an fp32 16x16x4 step s over tile t takes
+// k = 16t + 4g + s.  The A operand is read from LDS
+// (k contiguous) in the same order.
+template <typename TM, int NKT>
+struct BFrag;  // packed B operands for NKT consecutive 16-k tiles
+
+template <int NKT>
+struct BFrag<_Float16, NKT> {
+    f16x8 pair[NKT / 2 > 0 ? NKT / 2 : 1];
+    f16x4 tail;
+    __device__ __forceinline__ void set(const f4 *t) {
+#pragma unroll
+        for (int m = 0; m < NKT / 2; ++m) {
+            f16x8 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = (_Float16)t[2 * m][e];
+                x[4 + e] = (_Float16)t[2 * m + 1][e];
+            }
+            pair[m] = x;
+        }
+        if constexpr (NKT % 2 == 1) {
+            f16x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = (_Float16)t[NKT - 1][e];
+            tail = y;
+        }
+    }
+};
+
+template <int NKT>
+struct BFrag<float, NKT> {
+    f4 t[NKT];
+    __device__ __forceinline__ void set(const f4 *x) {
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) t[i] = x[i];
+    }
+};
+
+// acc += A[16 x 16*nkt] * B, A rows in LDS (arow = this lane's row, k contiguous), over
+// the first nkt (<= NKT) k tiles of b.  Callers pass nkt rounded up to even on the
+// 16-bit path only when the extra tile of A is zero.
+template <int NKT>
+__device__ __forceinline__ void mma_bfrag(f4 &acc, const _Float16 *arow, const BFrag<_Float16, NKT> &b,
+                                          int nkt, int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < NKT / 2; ++m) {
+        if (2 * m < nkt) {
+            const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 32 * m + 4 * g);
+            const f16x4 hi = *reinterpret_cast<const f16x4 *>(arow + 32 * m + 16 + 4 * g);
+            const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b.pair[m], acc, 0, 0, 0);
+        }
+    }
+    if constexpr (NKT % 2 == 1) {
+        // an odd last tile goes through the same 16x16x32 instruction with its upper half
+        // zero, so one accumulation chain never mixes instruction shapes
+        if (NKT - 1 < nkt) {
+            const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 16 * (NKT - 1) + 4 * g);
+            const f16x8 a = {lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+            const f16x8 bb = {b.tail[0], b.tail[1], b.tail[2], b.tail[3], 0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bb, acc, 0, 0, 0);
+        }
+    }
+}
+
+template <int NKT>
+__device__ __forceinline__ void mma_bfrag(f4 &acc, const float *arow, const BFrag<float, NKT> &b, int nkt,
+                                          int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+        if (t < nkt) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[16 * t + 4 * g + s], b.t[t][s], acc, 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for LDS traffic only.  The waves exchange data through LDS alone,
+// so global loads may stay in flight across it (the prep waves' prefetch of the next
+// chunk does); __syncthreads() would drain them at every barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// acc += A[16 x kdim] * B[kdim x 16] for the A-matrix tiles: A rows in `A` (the Lk operand
+// type, or fp32 staging), B^T rows in fp32 staging.  On the bf16 path the fp32 values are
+// rounded to bf16 as they are loaded; with SPLIT both operands are split into hi + lo
+// bf16 and the product is hi*hi + hi*lo + lo*hi (about 16 mantissa bits).
+__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
+    const float4 u = *reinterpret_cast<const float4 *>(p), w = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+}
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        hi[i] = (__bf16)x[i];
+        lo[i] = (__bf16)(x[i] - (float)hi[i]);
+    }
+}
+template <class P, bool SPLIT, typename TAr>
+__device__ __forceinline__ void mma_rowsrc(f4 &acc, const TAr *A, int lda, const float *B, int ldb, int kdim,
+                                           int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    if constexpr (std::is_same<typename P::TA, float>::value) {
+        for (int k0 = 0; k0 < kdim; k0 += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + g], B[r * ldb + k0 + g], acc, 0, 0, 0);
+    } else {
+        for (int k0 = 0; k0 < kdim; k0 += 32) {
+            // a 16-wide tail (kdim % 32 == 16) fills the lower half of each operand and
+            // zeroes the upper half
+            const bool tail = k0 + 32 > kdim;
+            float xb[8];
+            if (tail) {
+                const float4 u = *reinterpret_cast<const float4 *>(B + r * ldb + k0 + 4 * g);
+                xb[0] = u.x; xb[1] = u.y; xb[2] = u.z; xb[3] = u.w; xb[4] = xb[5] = xb[6] = xb[7] = 0.f;
+            } else {
+                ld8(B + r * ldb + k0 + 8 * g, xb);
+            }
+            bf16x8 bh, bl;
+            bf16x8 ah, al;
+            if constexpr (SPLIT) split8(xb, bh, bl);
+            else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bh[i] = (__bf16)xb[i];
+            }
+            if constexpr (std::is_same<TAr, float>::value) {
+                float xa[8];
+                if (tail) {
+                    const float4 u = *reinterpret_cast<const float4 *>(A + r * lda + k0 + 4 * g);
+                    xa[0] = u.x; xa[1] = u.y; xa[2] = u.z; xa[3] = u.w; xa[4] = xa[5] = xa[6] = xa[7] = 0.f;
+                } else {
+                    ld8(A + r * lda + k0 + 8 * g, xa);
+                }
+                if constexpr (SPLIT) split8(xa, ah, al);
+                else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ah[i] = (__bf16)xa[i];
+                }
+            } else {
+                if (tail) {
+                    const TAr *pa = A + r * lda + k0 + 4 * g;
+                    const __bf16 z = (__bf16)0.f;
+                    ah = bf16x8{pa[0], pa[1], pa[2], pa[3], z, z, z, z};
+                } else {
+                    ah = *reinterpret_cast<const bf16x8 *>(A + r * lda + k0 + 8 * g);
+                }
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+            if constexpr (SPLIT) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+            }
+        }
+    }
+}
 
 template <class P, int K, int V, int C, int BV>
 __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
@@ -125,46 +278,24 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     using TM = typename P::TM;
     using TIn = typename std::conditional<std::is_same<P, PrecF32>::value, float, __bf16>::type;
     constexpr int NP = L::NP;
-    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr int NKT_K = K / 16;  // 16-channel tiles
 
     extern __shared__ __align__(16) unsigned char smem[];
-    TA *Lk = reinterpret_cast<TA *>(smem + L::oLk);
-    TA *Lq = reinterpret_cast<TA *>(smem + L::oLq);  // [NSPL][C][LKA]
-    TA *Rd = reinterpret_cast<TA *>(smem + L::oRd);
-    TA *Ro = reinterpret_cast<TA *>(smem + L::oRo);  // [NSPL][C-16][LKA]
-    TA *Xv = reinterpret_cast<TA *>(smem + L::oX);   // [NSPL][NX][16][LKA]
-    TM *Tm = reinterpret_cast<TM *>(smem + L::oTm);
-    TM *Wn = reinterpret_cast<TM *>(smem + L::oW);   // holds -W
-    TM *Vt = reinterpret_cast<TM *>(smem + L::oVt);  // [BV][LCM]
-    TM *Qt = reinterpret_cast<TM *>(smem + L::oQt);
-    TM *Bw = reinterpret_cast<TM *>(smem + L::oBw);  // [K][LCM]
-    TM *Kt = reinterpret_cast<TM *>(smem + L::oKt);  // [K][LCM]
-    TM *bV = reinterpret_cast<TM *>(smem + L::obV);  // [BV][LCM]
-    float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
-    float *Tf = reinterpret_cast<float *>(smem + L::oTf);
-    TM *Aqk = reinterpret_cast<TM *>(smem + L::oAqk);
-    float *Msc = reinterpret_cast<float *>(smem + L::oM);
-    TM *St = reinterpret_cast<TM *>(smem + L::oSt);  // [BV][LKM]
-    float *Rv = reinterpret_cast<float *>(smem + L::oR);
-    float *Ev = reinterpret_cast<float *>(smem + L::oE);
-    float *GCv = reinterpret_cast<float *>(smem + L::oGC);
-    float *eGC = reinterpret_cast<float *>(smem + L::oEGC);
-    float *Seg = reinterpret_cast<float *>(smem + L::oSeg);
-    float *Bt = reinterpret_cast<float *>(smem + L::oBeta);
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int g = lane >> 4;
 
-    // ---- which (sequence, head, value block) this workgroup owns -------------------
+    // ---- which (sequence, head, value block) this workgroup owns ----------------------
     constexpr int NVB = V / BV;
     const int G = gridDim.x;
     int lin = blockIdx.x;
-    if ((G & 7) == 0) lin = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // keep a head's value
-    const int vb = lin % NVB;                                                   // blocks on one XCD
+    if ((G & 7) == 0) lin = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // a head's value blocks
+    const int vb = lin % NVB;                                                   // share one XCD
     const int pair = lin / NVB;
-    const int h = pair % a.H;
-    const int s = pair / a.H;
+    const int H = a.H;
+    const int h = pair % H;
+    const int s = pair / H;
     int64_t bos, eos;
     if (a.cu_seqlens) {
         bos = a.cu_seqlens[s];
@@ -173,340 +304,406 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
         bos = (int64_t)s * a.T;
         eos = bos + a.T;
     }
-    const int H = a.H;
+    const int nchunks = (int)((eos - bos + C - 1) / C);
     const TIn *q = static_cast<const TIn *>(a.q);
     const TIn *k = static_cast<const TIn *>(a.k);
     const TIn *v = static_cast<const TIn *>(a.v);
 
-    // ---- master state in registers (wave-owned [16 x 16] tiles of S[K x BV]) -------
-    f4 accS[L::MS];
-    const float *s0 = a.initial_state ? a.initial_state + ((int64_t)s * H + h) * K * V : nullptr;
+    auto pkg = [&](int buf) { return smem + L::oPkg + (size_t)buf * L::szPkg; };
+
+    if (wave < NSW) {
+        // =================================== state waves ===================================
+        f4 S[L::MJ][NKT_K];
+        const float *s0 = a.initial_state ? a.initial_state + ((int64_t)s * H + h) * K * V : nullptr;
 #pragma unroll
-    for (int m = 0; m < L::MS; ++m) {
-        const int ts = wave + NW * m;
-        f4 x = {0.f, 0.f, 0.f, 0.f};
-        if (ts < L::NTS && s0) {
-            const int kr = (ts / (BV / 16)) * 16 + 4 * (lane >> 4);
-            const int vc = vb * BV + (ts % (BV / 16)) * 16 + (lane & 15);
+        for (int mj = 0; mj < L::MJ; ++mj) {
+            const int jt = wave + NSW * mj;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = s0[(int64_t)(kr + e) * V + vc];
+            for (int t = 0; t < NKT_K; ++t) {
+                f4 x = {0.f, 0.f, 0.f, 0.f};
+                if (jt < L::NJT && s0) {
+                    const int vc = vb * BV + jt * 16 + (lane & 15);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = s0[(int64_t)(16 * t + 4 * g + e) * V + vc];
+                }
+                S[mj][t] = x;
+            }
         }
-        accS[m] = x;
+        BFrag<TM, NKT_K> Sh[L::MJ];
+#pragma unroll
+        for (int mj = 0; mj < L::MJ; ++mj) Sh[mj].set(S[mj]);
+
+        for (int it = 0; it <= nchunks; ++it) {
+            lds_barrier();  // B1: prep waves have produced their tile products
+            f4 Vt[L::MJ][NP];
+            BFrag<TM, NP> Vh[L::MJ];
+            const int cn = it - 1;  // chunk handled by the state waves in this iteration
+            if (cn >= 0) {
+                const unsigned char *pk = pkg(cn & 1);
+                const TM *Qt = reinterpret_cast<const TM *>(pk + L::pQt);
+                const TM *Bw = reinterpret_cast<const TM *>(pk + L::pBw);
+                const TM *Tm = reinterpret_cast<const TM *>(pk + L::pTm);
+                const TM *Aqk = reinterpret_cast<const TM *>(pk + L::pAqk);
+                const TM *bV = reinterpret_cast<const TM *>(pk + L::pbV);
+                const int64_t t0 = bos + (int64_t)cn * C;
+                const int n = (int)((eos - t0) < C ? (eos - t0) : C);
+#pragma unroll
+                for (int mj = 0; mj < L::MJ; ++mj) {
+                    const int jt = wave + NSW * mj;
+                    if (jt >= L::NJT) continue;
+                    // Y = beta V - Bw S   (rows: tokens of the chunk; this wave's 16 columns)
+                    f4 Y[NP];
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        f4 y;
+                        const TM *bvr = bV + (jt * 16 + (lane & 15)) * L::LCM + 16 * p + 4 * g;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = to_f32(bvr[e]);
+                        mma_bfrag<NKT_K>(y, Bw + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
+                        Y[p] = y;
+                    }
+                    BFrag<TM, NP> Yh;
+                    Yh.set(Y);
+                    // Vt = T Y (T lower triangular: row tile p needs token tiles 0..p)
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        f4 x = {0.f, 0.f, 0.f, 0.f};
+                        mma_bfrag<NP>(x, Tm + (16 * p + (lane & 15)) * L::LCM, Yh, p + 1, lane);
+                        Vt[mj][p] = x;
+                    }
+                    Vh[mj].set(Vt[mj]);
+                    // O = Qt S + A_qk Vt
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        f4 o = {0.f, 0.f, 0.f, 0.f};
+                        mma_bfrag<NKT_K>(o, Qt + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
+                        mma_bfrag<NP>(o, Aqk + (16 * p + (lane & 15)) * L::LCM, Vh[mj], p + 1, lane);
+                        const int j = vb * BV + jt * 16 + (lane & 15);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = 16 * p + 4 * g + e;
+                            if (i < n) st_out(a.out, a.out_bf16, ((t0 + i) * H + h) * V + j, a.scale * o[e]);
+                        }
+                    }
+                }
+            }
+            lds_barrier();  // B2: prep waves have written the A-matrix operands
+            if (cn >= 0) {
+                const unsigned char *pk = pkg(cn & 1);
+                const TM *Kt = reinterpret_cast<const TM *>(pk + L::pKt);
+                const float *eGC = reinterpret_cast<const float *>(pk + L::pGC);
+#pragma unroll
+                for (int mj = 0; mj < L::MJ; ++mj) {
+                    const int jt = wave + NSW * mj;
+                    if (jt >= L::NJT) continue;
+                    // S = gamma_C S + Kt^T Vt
+#pragma unroll
+                    for (int t = 0; t < NKT_K; ++t) {
+                        f4 x = S[mj][t];
+                        const float4 d = *reinterpret_cast<const float4 *>(eGC + 16 * t + 4 * g);
+                        x[0] *= d.x; x[1] *= d.y; x[2] *= d.z; x[3] *= d.w;
+                        mma_bfrag<NP>(x, Kt + (16 * t + (lane & 15)) * L::LCM, Vh[mj], NP, lane);
+                        S[mj][t] = x;
+                    }
+                    Sh[mj].set(S[mj]);
+                }
+            }
+            lds_barrier();  // B3: the next package is complete
+        }
+        if (a.final_state) {
+            float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
+#pragma unroll
+            for (int mj = 0; mj < L::MJ; ++mj) {
+                const int jt = wave + NSW * mj;
+                if (jt >= L::NJT) continue;
+                const int vc = vb * BV + jt * 16 + (lane & 15);
+#pragma unroll
+                for (int t = 0; t < NKT_K; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sf[(int64_t)(16 * t + 4 * g + e) * V + vc] = S[mj][t][e];
+            }
+        }
+        return;
     }
-    auto write_state_copy = [&]() {
-#pragma unroll
-        for (int m = 0; m < L::MS; ++m) {
-            const int ts = wave + NW * m;
-            if (ts < L::NTS) {
-                const int kr = (ts / (BV / 16)) * 16 + 4 * (lane >> 4);
-                const int vc = (ts % (BV / 16)) * 16 + (lane & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) St[vc * L::LKM + kr + e] = from_f32<TM>(accS[m][e]);
+
+    // ====================================== prep waves =======================================
+    const int tp = tid - NSW * 64;  // 0 .. NPT-1
+    const int pw = wave - NSW;      // prep wave 0..3
+    TA *Lk = reinterpret_cast<TA *>(smem + L::oLk);         // [C][LKA]
+    float *Lq = reinterpret_cast<float *>(smem + L::oLq);   // [C][LKF]
+    float *Rd = reinterpret_cast<float *>(smem + L::oRd);   // [C][LKF]
+    float *Ro = reinterpret_cast<float *>(smem + L::oRo);   // [C-16][LKF]
+    float *Xv = reinterpret_cast<float *>(smem + L::oX);    // [NX][16][LKF]
+    float *Akk = reinterpret_cast<float *>(smem + L::oAkk); // [C][LCF]
+    float *Tf = reinterpret_cast<float *>(smem + L::oTf);   // [C][LCF]
+    float *TPv = reinterpret_cast<float *>(smem + L::oTP);  // [NP][K] tile decay products
+    float *Btv = reinterpret_cast<float *>(smem + L::oBt);  // [C] beta of the chunk
+
+    // The strictly upper 16x16 blocks of T and A_qk are zero in every chunk: write them
+    // once, in both package buffers.  (The state waves first read a package after the
+    // first iteration's last barrier.)
+    for (int buf = 0; buf < 2; ++buf) {
+        TM *Tm = reinterpret_cast<TM *>(pkg(buf) + L::pTm);
+        TM *Aq = reinterpret_cast<TM *>(pkg(buf) + L::pAqk);
+        for (int e = tp; e < C * C; e += NPT) {
+            const int i = e / C, j = e % C;
+            if ((j >> 4) > (i >> 4)) {
+                Tm[i * L::LCM + j] = from_f32<TM>(0.f);
+                Aq[i * L::LCM + j] = from_f32<TM>(0.f);
             }
         }
-    };
-    write_state_copy();
+    }
 
-    // prep mapping: thread -> (key channel c, segment of RPS consecutive rows)
-    const int pc = tid % K;
-    const int pseg = tid / K;
-
-    for (int64_t t0 = bos; t0 < eos; t0 += C) {
-        const int n = (int)((eos - t0) < C ? (eos - t0) : C);
-
-        // ---- 1. cumulative log2-decay Gamma of the chunk ----------------------------
-        if (tid < C) Bt[tid] = tid < n ? a.beta[(t0 + tid) * H + h] : 0.f;
-        float G2[L::RPS];
-        {
-            float run = 0.f;
+    // Raw inputs of one chunk, per tile-column (channel c, tile p): 16 rows of the gate,
+    // q and k, beta of row tp, and this thread's share of the value block.  The loads
+    // are unconditional (rows past the sequence end read its last row) and nothing is
+    // computed from them until they are used in the next iteration, so they stay in
+    // flight while the current chunk is processed; the padding rows are masked at use.
+    using RawIn = typename std::conditional<std::is_same<TIn, float>::value, float, unsigned short>::type;
+    float ral[L::TCPT][16];
+    RawIn rq[L::TCPT][16], rk[L::TCPT][16];
+    float rbeta = 0.f;
+    constexpr int NVE = (BV * C + NPT - 1) / NPT;  // beta*V elements per prep thread
+    RawIn rv[NVE];
+    auto load_raw = [&](int cn) {
+        const int64_t t0 = bos + (int64_t)cn * C;
+        const int last = (int)((eos - t0) < C ? (eos - t0) : C) - 1;  // last valid row (>= 0)
+        const int64_t rs = (int64_t)H * K;                          // row stride of q, k, gate
+        const RawIn *qr = reinterpret_cast<const RawIn *>(q);
+        const RawIn *kr = reinterpret_cast<const RawIn *>(k);
+        const RawIn *vr = reinterpret_cast<const RawIn *>(v);
 #pragma unroll
-            for (int i = 0; i < L::RPS; ++i) {
-                const int r = pseg * L::RPS + i;
-                float g = 0.f;
-                if (r < n) {
-                    const float x = a.gate[((t0 + r) * H + h) * K + pc];
-                    g = a.gate_is_log ? x * LOG2E : __log2f(x);
-                }
-                run += g;
-                G2[i] = run;
-            }
-            Seg[pseg * K + pc] = run;
-        }
-        __syncthreads();
-        {
-            float off = 0.f;
-            for (int sg = 0; sg < pseg; ++sg) off += Seg[sg * K + pc];
-#pragma unroll
-            for (int i = 0; i < L::RPS; ++i) {
-                G2[i] += off;
-                const int r = pseg * L::RPS + i;
-                if ((r & 15) == 15) {
-                    Ev[(r >> 4) * K + pc] = G2[i];
-                    if ((r >> 4) + 1 < NP) Rv[((r >> 4) + 1) * K + pc] = G2[i];
-                }
-                if (r == C - 1) {
-                    GCv[pc] = G2[i];
-                    eGC[pc] = exp2f(G2[i]);
-                }
-            }
-            if (pseg == 0) Rv[pc] = 0.f;
-        }
-        __syncthreads();
-
-        // ---- 2. rescaled operands ----------------------------------------------------
-        {
-            const float gC = GCv[pc];
-#pragma unroll
-            for (int i = 0; i < L::RPS; ++i) {
-                const int r = pseg * L::RPS + i;
-                const int p = r >> 4;
-                const float Rp = Rv[p * K + pc];
-                const float Ep = Ev[p * K + pc];
-                float qv = 0.f, kv = 0.f;
-                if (r < n) {
-                    qv = ld_f32(q, ((t0 + r) * H + h) * K + pc);
-                    kv = ld_f32(k, ((t0 + r) * H + h) * K + pc);
-                }
-                const float be = Bt[r];
-                const float ea = exp2f(G2[i] - Rp);  // <= 1
-                const float eb = exp2f(Rp - G2[i]);  // in [1, e^80]
-                const float lq = qv * ea;
-                const float lk = be * kv * ea;
-                const float rd = kv * eb;
-                const float ro = rd * exp2f(Ep - Rp);  // k e^{E_p - Gamma} <= 1
-                const float eR = exp2f(Rp);
-                Lk[r * L::LKA + pc] = from_f32<TA>(lk);
-                {
-                    const TA hq = from_f32<TA>(lq), hr = from_f32<TA>(rd);
-                    Lq[r * L::LKA + pc] = hq;
-                    Rd[r * L::LKA + pc] = hr;
-                    if constexpr (P::kSplit) {
-                        Lq[C * L::LKA + r * L::LKA + pc] = from_f32<TA>(lq - to_f32(hq));
-                        Rd[C * L::LKA + r * L::LKA + pc] = from_f32<TA>(rd - to_f32(hr));
-                    }
-                }
-                if (p < NP - 1) {
-                    const TA ho = from_f32<TA>(ro);
-                    Ro[r * L::LKA + pc] = ho;
-                    if constexpr (P::kSplit)
-                        Ro[(C - 16) * L::LKA + r * L::LKA + pc] = from_f32<TA>(ro - to_f32(ho));
-                }
-                if constexpr (L::NX > 0) {
-                    // versions of tile q = p for row tiles pp >= p + 2
-                    int xi = 0;
-                    for (int pp = 2; pp < NP; ++pp)
-                        for (int qq = 0; qq + 2 <= pp; ++qq, ++xi) {
-                            if (qq != p) continue;
-                            const float xv = ro * exp2f(Rv[pp * K + pc] - Ep);
-                            const TA hx = from_f32<TA>(xv);
-                            const int row = r - 16 * p;
-                            Xv[(size_t)xi * 16 * L::LKA + row * L::LKA + pc] = hx;
-                            if constexpr (P::kSplit)
-                                Xv[(size_t)(L::NX + xi) * 16 * L::LKA + row * L::LKA + pc] =
-                                    from_f32<TA>(xv - to_f32(hx));
-                        }
-                }
-                Qt[r * L::LKM + pc] = from_f32<TM>(lq * eR);
-                Bw[pc * L::LCM + r] = from_f32<TM>(lk * eR);
-                Kt[pc * L::LCM + r] = from_f32<TM>(ro * exp2f(gC - Ep));
-            }
-            // beta * V for this value block, transposed (token contiguous)
-            for (int e = tid; e < BV * C; e += NT) {
-                const int j = e % BV, r = e / BV;
-                float x = 0.f;
-                if (r < n) x = Bt[r] * ld_f32(v, ((t0 + r) * H + h) * V + vb * BV + j);
-                bV[j * L::LCM + r] = from_f32<TM>(x);
-            }
-        }
-        __syncthreads();
-
-        // ---- 3. A_kk (strictly lower, fp32), A_qk (lower incl. diagonal), O = Qt S ----
-        {
-            constexpr int NTA = NP * NP;  // all tiles; the upper ones are zero
-            for (int task = wave; task < 2 * NTA; task += NW) {
-                const bool isq = task >= NTA;
-                const int tt = isq ? task - NTA : task;
-                const int p = tt / NP, qt = tt % NP;
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
-                if (qt <= p) {
-                    const TA *right;
-                    int rstride_lo;  // offset of the lo copy of `right`
-                    if (qt == p) {
-                        right = Rd + qt * 16 * L::LKA;
-                        rstride_lo = C * L::LKA;
-                    } else if (qt == p - 1) {
-                        right = Ro + qt * 16 * L::LKA;
-                        rstride_lo = (C - 16) * L::LKA;
-                    } else {
-                        int xi = 0;
-                        for (int pp = 2; pp < p; ++pp) xi += pp - 1;
-                        xi += qt;
-                        right = Xv + (size_t)xi * 16 * L::LKA;
-                        rstride_lo = L::NX * 16 * L::LKA;
-                    }
-                    if (!isq) {
-                        mma_tile<TA>(acc, Lk + p * 16 * L::LKA, L::LKA, right, L::LKA, K, lane);
-                    } else {
-                        const TA *left = Lq + p * 16 * L::LKA;
-                        mma_tile<TA>(acc, left, L::LKA, right, L::LKA, K, lane);
-                        if constexpr (P::kSplit) {
-                            mma_tile<TA>(acc, left, L::LKA, right + rstride_lo, L::LKA, K, lane);
-                            mma_tile<TA>(acc, left + C * L::LKA, L::LKA, right, L::LKA, K, lane);
-                        }
-                    }
-                }
-                const int i0 = p * 16 + 4 * (lane >> 4), j = qt * 16 + (lane & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = i0 + e;
-                    if (!isq)
-                        Akk[i * L::LCF + j] = (j < i) ? acc[e] : 0.f;
-                    else
-                        Aqk[i * L::LCM + j] = from_f32<TM>((j <= i) ? acc[e] : 0.f);
-                }
-            }
-        }
-        f4 accO[L::MO];
-#pragma unroll
-        for (int m = 0; m < L::MO; ++m) {
-            accO[m] = f4{0.f, 0.f, 0.f, 0.f};
-            const int to = wave + NW * m;
-            if (to < L::NTO) {
-                const int p = to / (BV / 16), jt = to % (BV / 16);
-                mma_tile<TM>(accO[m], Qt + p * 16 * L::LKM, L::LKM, St + jt * 16 * L::LKM, L::LKM, K,
-                             lane);
-            }
-        }
-        __syncthreads();
-
-        // ---- 4. T = (I + A_kk)^-1 -------------------------------------------------------
-        if (tid < 16 * NP) {
-            // diagonal 16x16 blocks by forward substitution, one column per thread
-            const int p = tid >> 4, c = tid & 15;
-            const float *A = Akk + (p * 16) * L::LCF + p * 16;
-            float x[16];
+        for (int u = 0; u < L::TCPT; ++u) {
+            const int tc = tp + NPT * u < L::NTC ? tp + NPT * u : 0;
+            const int c = tc % K, p = tc / K;
+            const int64_t base = (t0 * H + h) * K + c;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float acc = (i == c) ? 1.f : 0.f;
-#pragma unroll
-                for (int jj = 0; jj < i; ++jj) acc -= A[i * L::LCF + jj] * x[jj];
-                x[i] = (i < c) ? 0.f : acc;
+                const int64_t o = base + (int64_t)(16 * p + i < last ? 16 * p + i : last) * rs;
+                ral[u][i] = a.gate[o];
+                rq[u][i] = qr[o];
+                rk[u][i] = kr[o];
             }
-            float *Td = Tf + (p * 16) * L::LCF + p * 16;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) Td[i * L::LCF + c] = x[i];
         }
-        __syncthreads();
-        for (int d = 1; d < NP; ++d) {
-            // blocks (p, p-d): M = sum_{r=q}^{p-1} A_pr T_rq ; T_pq = -T_pp M
-            for (int e = tid; e < (NP - d) * 256; e += NT) {
-                const int b = e >> 8, i = (e >> 4) & 15, jj = e & 15;
-                const int p = d + b, qb = b;
-                float acc = 0.f;
-                for (int r = qb; r < p; ++r)
+        rbeta = a.beta[(t0 + (tp < last ? tp : last)) * H + h];
 #pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        acc += Akk[(p * 16 + i) * L::LCF + r * 16 + m] * Tf[(r * 16 + m) * L::LCF + qb * 16 + jj];
-                Msc[b * 256 + i * 16 + jj] = acc;
-            }
-            __syncthreads();
-            for (int e = tid; e < (NP - d) * 256; e += NT) {
-                const int b = e >> 8, i = (e >> 4) & 15, jj = e & 15;
-                const int p = d + b, qb = b;
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m) acc += Tf[(p * 16 + i) * L::LCF + p * 16 + m] * Msc[b * 256 + m * 16 + jj];
-                Tf[(p * 16 + i) * L::LCF + qb * 16 + jj] = -acc;
-            }
-            __syncthreads();
+        for (int w = 0; w < NVE; ++w) {
+            const int e = (tp + NPT * w) % (BV * C);
+            const int j = e % BV, r = e / BV;
+            rv[w] = vr[((t0 + (r < last ? r : last)) * H + h) * V + vb * BV + j];
         }
-        // operand copy of T with an explicit zero upper triangle (region 1 is free now)
-        for (int e = tid; e < C * C; e += NT) {
-            const int i = e / C, jj = e % C;
-            Tm[i * L::LCM + jj] = from_f32<TM>(jj <= i ? Tf[i * L::LCF + jj] : 0.f);
-        }
-        __syncthreads();
+    };
+    auto raw_f32 = [&](RawIn x) -> float {
+        if constexpr (std::is_same<RawIn, float>::value) return x;
+        else return __builtin_bit_cast(float, (uint32_t)x << 16);
+    };
+    // right operand of A-matrix tile (p, qt), fp32 staging
+    auto right_of = [&](int p, int qt) -> const float * {
+        if (qt == p) return Rd + qt * 16 * L::LKF;
+        if (qt == p - 1) return Ro + qt * 16 * L::LKF;
+        int xi = 0;
+        for (int pp = 2; pp < p; ++pp) xi += pp - 1;
+        return Xv + (size_t)(xi + qt) * 16 * L::LKF;
+    };
+    if (nchunks > 0) load_raw(0);
 
-        // ---- 5. -W = -T (beta e^Gamma K) into LDS, U = T (beta V) into registers -------
-        for (int task = wave; task < NP * (K / 16); task += NW) {
-            const int p = task / (K / 16), ct = task % (K / 16);
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-            mma_tile<TM>(acc, Tm + p * 16 * L::LCM, L::LCM, Bw + ct * 16 * L::LCM, L::LCM, 16 * (p + 1),
-                         lane);
-            const int i0 = p * 16 + 4 * (lane >> 4), c = ct * 16 + (lane & 15);
+    for (int it = 0; it <= nchunks; ++it) {
+        const bool work = it < nchunks;
+        const int n_it = work ? (int)((eos - (bos + (int64_t)it * C)) < C ? (eos - (bos + (int64_t)it * C)) : C) : 0;
+        // ---- phase 1a: retention factors (1 on padding rows), tile totals, beta --------
+        if (work) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Wn[(i0 + e) * L::LKM + c] = from_f32<TM>(-acc[e]);
+            for (int u = 0; u < L::TCPT; ++u) {
+                const int tc = tp + NPT * u;
+                const int p = tc / K;
+                float run = 1.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float al = a.gate_is_log ? __expf(ral[u][i]) : ral[u][i];
+                    al = (16 * p + i < n_it) ? al : 1.f;
+                    ral[u][i] = al;
+                    run *= al;
+                }
+                if (tc < L::NTC) TPv[p * K + tc % K] = run;
+            }
+            if (tp < C) Btv[tp] = tp < n_it ? rbeta : 0.f;
         }
-        f4 accU[L::MO];
+        lds_barrier();  // B1
+        // ---- phase 1b: operands of chunk `it` -------------------------------------------
+        if (work) {
+            unsigned char *pk = pkg(it & 1);
+            TM *Qt = reinterpret_cast<TM *>(pk + L::pQt);
+            TM *Bw = reinterpret_cast<TM *>(pk + L::pBw);
+            TM *Kt = reinterpret_cast<TM *>(pk + L::pKt);
+            TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
+            float *eGC = reinterpret_cast<float *>(pk + L::pGC);
 #pragma unroll
-        for (int m = 0; m < L::MO; ++m) {
-            accU[m] = f4{0.f, 0.f, 0.f, 0.f};
-            const int to = wave + NW * m;
-            if (to < L::NTO) {
-                const int p = to / (BV / 16), jt = to % (BV / 16);
-                mma_tile<TM>(accU[m], Tm + p * 16 * L::LCM, L::LCM, bV + jt * 16 * L::LCM, L::LCM,
-                             16 * (p + 1), lane);
+            for (int u = 0; u < L::TCPT; ++u) {
+                const int tc = tp + NPT * u;
+                if (tc >= L::NTC) continue;
+                const int c = tc % K, p = tc / K;
+                float tpr[NP];
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) tpr[pp] = TPv[pp * K + c];
+                float eR = 1.f, eCE = 1.f, eAll = 1.f;
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    if (pp < p) eR *= tpr[pp];
+                    if (pp > p) eCE *= tpr[pp];
+                    eAll *= tpr[pp];
+                }
+                if (p == 0) eGC[c] = eAll;
+                const float rT = 1.f / tpr[p];
+                // extra right-operand versions for tiles (pp, p) with pp >= p + 2
+                float xf[NP];
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    float f = 1.f;
+#pragma unroll
+                    for (int r2 = 0; r2 < NP; ++r2)
+                        if (r2 > p && r2 < pp) f *= tpr[r2];
+                    xf[pp] = f;
+                }
+                float bet[16];
+#pragma unroll
+                for (int i = 0; i < 16; i += 4) {
+                    const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + i);
+                    bet[i] = b4.x; bet[i + 1] = b4.y; bet[i + 2] = b4.z; bet[i + 3] = b4.w;
+                }
+                float suf[16];  // E_p / gamma_i: product of the tile's later factors
+                {
+                    float run = 1.f;
+#pragma unroll
+                    for (int i = 15; i >= 0; --i) {
+                        suf[i] = run;
+                        run *= ral[u][i];
+                    }
+                }
+                float pre = 1.f;  // gamma_i / R_p
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = 16 * p + i;
+                    pre *= ral[u][i];
+                    const bool ok = r < n_it;
+                    const float qv = ok ? raw_f32(rq[u][i]) : 0.f, kv = ok ? raw_f32(rk[u][i]) : 0.f;
+                    const float lq = qv * pre;
+                    const float lk = bet[i] * kv * pre;
+                    const float ro = kv * suf[i];  // k E_p / gamma <= |k|
+                    const float rd = ro * rT;      // k R_p / gamma <= e^80 |k|
+                    Lk[r * L::LKA + c] = from_f32<TA>(lk);
+                    Lq[r * L::LKF + c] = lq;
+                    Rd[r * L::LKF + c] = rd;
+                    if (p < NP - 1) Ro[r * L::LKF + c] = ro;
+                    if constexpr (L::NX > 0) {
+                        int xi = 0;
+#pragma unroll
+                        for (int pp = 2; pp < NP; ++pp)
+#pragma unroll
+                            for (int qq = 0; qq + 2 <= pp; ++qq, ++xi)
+                                if (qq == p) Xv[(size_t)xi * 16 * L::LKF + i * L::LKF + c] = ro * xf[pp];
+                    }
+                    Qt[r * L::LKM + c] = from_f32<TM>(lq * eR);
+                    Bw[r * L::LKM + c] = from_f32<TM>(-lk * eR);
+                    Kt[c * L::LCM + r] = from_f32<TM>(ro * eCE);
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < NVE; ++w) {
+                const int e = tp + NPT * w;
+                if (e < BV * C) bV[(e % BV) * L::LCM + e / BV] = from_f32<TM>(raw_f32(rv[w]) * Btv[e / BV]);
+            }
+            if (it + 1 < nchunks) load_raw(it + 1);  // prefetch; consumed next iteration
+        }
+        lds_barrier();  // B2
+        // ---- phase 2: A_kk and T (prep wave 0), A_qk (prep waves 1..3) -----------------
+        if (work) {
+            unsigned char *pk = pkg(it & 1);
+            TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
+            TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
+            if (pw == 0) {
+                // A_kk (strictly lower) in fp32
+                for (int p = 0; p < NP; ++p)
+                    for (int qt = 0; qt <= p; ++qt) {
+                        f4 acc = {0.f, 0.f, 0.f, 0.f};
+                        mma_rowsrc<P, false>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKF, K, lane);
+                        const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Akk[(i0 + e) * L::LCF + j] = (j < i0 + e) ? acc[e] : 0.f;
+                    }
+                lds_fence();
+                // diagonal blocks of T = (I + A_kk)^-1 by forward substitution, one column
+                // per lane (lane = 16 * block + column)
+                if (lane < 16 * NP) {
+                    const int p = lane >> 4, cc = lane & 15;
+                    const float *A = Akk + (p * 16) * L::LCF + p * 16;
+                    float x[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float row[16];
+#pragma unroll
+                        for (int j4 = 0; j4 < 16; j4 += 4) {
+                            if (j4 < i) {
+                                const float4 r4 = *reinterpret_cast<const float4 *>(A + i * L::LCF + j4);
+                                row[j4] = r4.x; row[j4 + 1] = r4.y; row[j4 + 2] = r4.z; row[j4 + 3] = r4.w;
+                            }
+                        }
+                        float acc0 = (i == cc) ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+                        for (int jj = 0; jj < i; ++jj) {
+                            if (jj & 1) acc1 -= row[jj] * x[jj];
+                            else acc0 -= row[jj] * x[jj];
+                        }
+                        x[i] = (i < cc) ? 0.f : acc0 + acc1;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        Tf[(p * 16 + i) * L::LCF + p * 16 + cc] = x[i];
+                        Tm[(p * 16 + i) * L::LCM + p * 16 + cc] = from_f32<TM>(x[i]);
+                    }
+                }
+                lds_fence();
+                // off-diagonal blocks, one block distance at a time, on fp32 matrix cores:
+                //   M = sum_{r=q}^{p-1} A_pr T_rq,   T_pq = -T_pp M
+                for (int d = 1; d < NP; ++d) {
+                    for (int qb = 0; qb + d < NP; ++qb) {
+                        const int p = qb + d;
+                        f4 m = {0.f, 0.f, 0.f, 0.f};
+                        for (int r = qb; r < p; ++r)
+#pragma unroll
+                            for (int s4 = 0; s4 < 4; ++s4)
+                                m = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    Akk[(p * 16 + (lane & 15)) * L::LCF + r * 16 + 4 * s4 + g],
+                                    Tf[(r * 16 + 4 * s4 + g) * L::LCF + qb * 16 + (lane & 15)], m, 0, 0, 0);
+                        // M's accumulator layout is the B operand with k = 4g + s4
+                        f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4)
+                            t = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                Tf[(p * 16 + (lane & 15)) * L::LCF + p * 16 + 4 * g + s4], m[s4], t, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = p * 16 + 4 * g + e, j = qb * 16 + (lane & 15);
+                            Tf[i * L::LCF + j] = -t[e];
+                            Tm[i * L::LCM + j] = from_f32<TM>(-t[e]);
+                        }
+                    }
+                    lds_fence();
+                }
+            } else {
+                // A_qk, lower tiles only (the upper ones stay zero)
+                int task = 0;
+                for (int p = 0; p < NP; ++p)
+                    for (int qt = 0; qt <= p; ++qt, ++task) {
+                        if (task % 3 != pw - 1) continue;
+                        f4 acc = {0.f, 0.f, 0.f, 0.f};
+                        mma_rowsrc<P, P::kSplit>(acc, Lq + p * 16 * L::LKF, L::LKF, right_of(p, qt), L::LKF, K, lane);
+                        const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Aqk[(i0 + e) * L::LCM + j] = from_f32<TM>((j <= i0 + e) ? acc[e] : 0.f);
+                    }
             }
         }
-        __syncthreads();
-
-        // ---- 6. Vt = U - W S  (stored transposed: value rows, token contiguous) ----------
-#pragma unroll
-        for (int m = 0; m < L::MO; ++m) {
-            const int to = wave + NW * m;
-            if (to < L::NTO) {
-                const int p = to / (BV / 16), jt = to % (BV / 16);
-                mma_tile<TM>(accU[m], Wn + p * 16 * L::LKM, L::LKM, St + jt * 16 * L::LKM, L::LKM, K, lane);
-                const int i0 = p * 16 + 4 * (lane >> 4), j = jt * 16 + (lane & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Vt[j * L::LCM + i0 + e] = from_f32<TM>(accU[m][e]);
-            }
-        }
-        __syncthreads();
-
-        // ---- 7. O += A_qk Vt -> out ;  S = e^{Gamma_C} S + K~^T Vt ----------------------
-#pragma unroll
-        for (int m = 0; m < L::MO; ++m) {
-            const int to = wave + NW * m;
-            if (to < L::NTO) {
-                const int p = to / (BV / 16), jt = to % (BV / 16);
-                mma_tile<TM>(accO[m], Aqk + p * 16 * L::LCM, L::LCM, Vt + jt * 16 * L::LCM, L::LCM,
-                             16 * (p + 1), lane);
-                const int i0 = p * 16 + 4 * (lane >> 4);
-                const int j = vb * BV + jt * 16 + (lane & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (i0 + e < n) st_out(a.out, a.out_bf16, ((t0 + i0 + e) * H + h) * V + j, a.scale * accO[m][e]);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < L::MS; ++m) {
-            const int ts = wave + NW * m;
-            if (ts < L::NTS) {
-                const int kt = ts / (BV / 16), jt = ts % (BV / 16);
-                const int kr = kt * 16 + 4 * (lane >> 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) accS[m][e] *= eGC[kr + e];
-                mma_tile<TM>(accS[m], Kt + kt * 16 * L::LCM, L::LCM, Vt + jt * 16 * L::LCM, L::LCM, C, lane);
-            }
-        }
-        write_state_copy();
-        __syncthreads();
-    }
-
-    // ---- final state ------------------------------------------------------------------
-    if (a.final_state) {
-        float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
-#pragma unroll
-        for (int m = 0; m < L::MS; ++m) {
-            const int ts = wave + NW * m;
-            if (ts < L::NTS) {
-                const int kr = (ts / (BV / 16)) * 16 + 4 * (lane >> 4);
-                const int vc = vb * BV + (ts % (BV / 16)) * 16 + (lane & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sf[(int64_t)(kr + e) * V + vc] = accS[m][e];
-            }
-        }
+        lds_barrier();  // B3
     }
 }
 
@@ -527,7 +724,7 @@ hipError_t launch_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream, int
     } else {
         using L = Layout<P, K, V, C, BV>;
         auto kern = chunk_fwd_kernel<P, K, V, C, BV>;
-        static bool attr_set = false;  // per-instantiation, set once per process
+        static bool attr_set = false;  // per instantiation, once per process
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::total);
@@ -543,6 +740,12 @@ hipError_t launch_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream, int
 
 template <class P, int K, int V>
 hipError_t launch_kv(const ChunkArgs &a, int C, int num_pairs, hipStream_t stream, int *bv) {
+    if (!a.q) {  // query only: report the value block, launch nothing
+        const int b = C == 16 ? pick_bv<P, K, V, 16>() : C == 32 ? pick_bv<P, K, V, 32>()
+                    : C == 64 ? pick_bv<P, K, V, 64>() : 0;
+        if (bv) *bv = b;
+        return b ? hipSuccess : hipErrorNotSupported;
+    }
     switch (C) {
         case 16: return launch_kvc<P, K, V, 16>(a, num_pairs, stream, bv);
         case 32: return launch_kvc<P, K, V, 32>(a, num_pairs, stream, bv);
@@ -574,6 +777,16 @@ hipError_t launch_p(const ChunkArgs &a, int K, int V, int C, int num_pairs, hipS
 }
 
 }  // namespace
+
+int chunk_fwd_value_block(bool fp32_inputs, int K, int V, int C) {
+    ChunkArgs q{};  // q == nullptr: query
+    int bv = 0;
+    if (fp32_inputs)
+        launch_p<PrecF32>(q, K, V, C, 0, nullptr, &bv);
+    else
+        launch_p<PrecMixed>(q, K, V, C, 0, nullptr, &bv);
+    return bv;
+}
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                             hipStream_t stream, int *bv) {

@@ -4,8 +4,9 @@
 // tile accumulated in float32 from two operands staged in LDS with the
 // reduction index contiguous ("A rows x k" and "B columns x k").  Lane layouts
 // (wave64) of the instructions used:
-//   16x16x32 (bf16 / f16): lane l holds A[l%16][8*(l/16) .. +8] and B^T likewise;
-//   16x16x16 (bf16 / f16): lane l holds A[l%16][4*(l/16) .. +4];
+//   16x16x32 (bf16 / f16): lane l holds A[l%16][8*(l/16) .. +8] and B^T likewise
+//                          (a 16-wide reduction uses it with the upper four zero, so
+//                          accumulation chains never mix instruction shapes);
 //   16x16x4  (f32):        lane l holds A[l%16][l/16];
 //   result: lane l holds D[4*(l/16) + e][l%16], e = 0..3.
 #pragma once
@@ -49,9 +50,12 @@ __device__ __forceinline__ void mma_tile<__bf16>(f4 &acc, const __bf16 *A, int l
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
     }
     if (k0 < kdim) {
-        s16x4 av = *reinterpret_cast<const s16x4 *>(a + k0 + 4 * (lane >> 4));
-        s16x4 bv = *reinterpret_cast<const s16x4 *>(b + k0 + 4 * (lane >> 4));
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+        // a 16-wide tail uses the same instruction with the upper half of each operand zero
+        const __bf16 *pa = a + k0 + 4 * (lane >> 4), *pb = b + k0 + 4 * (lane >> 4);
+        const __bf16 z = (__bf16)0.f;
+        bf16x8 av = {pa[0], pa[1], pa[2], pa[3], z, z, z, z};
+        bf16x8 bv = {pb[0], pb[1], pb[2], pb[3], z, z, z, z};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
     }
 }
 
@@ -67,9 +71,11 @@ __device__ __forceinline__ void mma_tile<_Float16>(f4 &acc, const _Float16 *A, i
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
     }
     if (k0 < kdim) {
-        f16x4 av = *reinterpret_cast<const f16x4 *>(a + k0 + 4 * (lane >> 4));
-        f16x4 bv = *reinterpret_cast<const f16x4 *>(b + k0 + 4 * (lane >> 4));
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, acc, 0, 0, 0);
+        const f16x4 pa = *reinterpret_cast<const f16x4 *>(a + k0 + 4 * (lane >> 4));
+        const f16x4 pb = *reinterpret_cast<const f16x4 *>(b + k0 + 4 * (lane >> 4));
+        f16x8 av = {pa[0], pa[1], pa[2], pa[3], 0, 0, 0, 0};
+        f16x8 bv = {pb[0], pb[1], pb[2], pb[3], 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
     }
 }
 

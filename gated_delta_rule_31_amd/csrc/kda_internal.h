@@ -48,6 +48,9 @@ struct GateArgs {
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                             hipStream_t stream, int *bv);
+// value-block width the chunk kernel uses for this shape, 0 if the shape is not compiled
+// (its LDS layout would exceed 160 KB)
+int chunk_fwd_value_block(bool fp32_inputs, int K, int V, int C);
 hipError_t launch_recurrent_step(const StepArgs &a, bool fp32_inputs, int K, int V, int pairs,
                                  hipStream_t stream);
 hipError_t launch_bounded_decay(const GateArgs &a, bool fp32_logits, hipStream_t stream);

@@ -102,9 +102,12 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
  *   chunk_size    16, 32 or 64: tokens per chunk (results differ only by rounding)
  *   scale         multiplies every output (1.0 = no query scaling)
  *   out    [B, T, H, V] in out_dtype
- * Supported: K, V in {16, 32, 64, 128}.  in_dtype KDA_F32 computes in float32
- * (matrix cores in fp32); KDA_BF16 uses bf16/fp16 matrix-core operands with
- * float32 accumulation and a float32 master state.
+ * Supported: K, V in {16, 32, 64, 128} and chunk sizes whose per-workgroup LDS
+ * layout fits 160 KB; kda_chunk_fwd_supported() tells which (chunk size 16 and 32 are
+ * available for every K, V; 64 only for small widths).  Anything else returns
+ * KDA_ERR_UNSUPPORTED.  in_dtype KDA_F32 computes in float32 (matrix cores in fp32);
+ * KDA_BF16 uses bf16/fp16 matrix-core operands with float32 accumulation and a
+ * float32 master state.
  * Preconditions: every log-decay ln(alpha) >= -5 (the K3 bound; it is what keeps
  * the chunk's rescale factors inside float range; alpha = 0 is not allowed here);
  * on the bf16 path the state, the values and the per-chunk pseudo-values stay
@@ -136,6 +139,13 @@ kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_d
                               const float *gate, kda_gate_kind gate_kind, const float *beta,
                               float *state, int B, int H, int K, int V, float scale, void *out,
                               kda_dtype out_dtype, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_supported -- host-only query (no device work): the number of value
+ * columns one workgroup of kda_chunk_fwd handles for this shape (16, 32 or 64), or 0
+ * if kda_chunk_fwd would return KDA_ERR_UNSUPPORTED for it.
+ */
+int kda_chunk_fwd_supported(kda_dtype in_dtype, int K, int V, int chunk_size);
 
 /* A static, human-readable name for a status code. */
 const char *kda_status_string(kda_status s);

@@ -61,6 +61,10 @@ def test_bounded_decay_odd_width_scalar_path():
 def test_tiny_fp32_all_chunk_sizes(C):
     inp = synth.tiny_fp32()
     _case("tiny fp32 C=%d" % C)
+    if not kda.chunk_fwd_supported(torch.float32, 16, 16, C):
+        with pytest.raises(ValueError, match="unsupported"):
+            gpu_prefill(inp, chunk_size=C)
+        pytest.skip("chunk size %d not compiled for fp32 K=V=16 (LDS budget)" % C)
     o, f = gpu_prefill(inp, chunk_size=C)
     eo, ef = oracle_prefill(inp)
     assert_close(o, eo, True, "out")
