@@ -59,6 +59,51 @@ def load_traffic(kernel_file: str, workload: str):
         return None
 
 
+COPY_BYTES = 1 << 30
+
+
+def _counter_means(path, counter):
+    """Mean counter value per kernel (rocprofv3 counter_collection.csv, KiB per dispatch)."""
+    import csv
+    import collections
+    acc = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per launch of the chunk and step kernels: FETCH_SIZE and WRITE_SIZE (KiB)
+    each scaled by what the same counter reads for a plain copy of known size (a copy of
+    N bytes reads N and writes N)."""
+    def copy_kib(path, counter):
+        m = _counter_means(path, counter)
+        big = max(m.items(), key=lambda kv: kv[1])  # the 1 GiB copy kernel
+        return big[1], big[0]
+    cf, cname = copy_kib(copy_fetch_csv, "FETCH_SIZE")
+    cw, _ = copy_kib(copy_write_csv, "WRITE_SIZE")
+    f_scale = COPY_BYTES / cf
+    w_scale = COPY_BYTES / cw
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    out = {"_calibration": {"copy_kernel": cname[:120], "copy_bytes": COPY_BYTES, "fetch_kib": cf,
+                            "write_kib": cw, "bytes_per_fetch_kib": f_scale, "bytes_per_write_kib": w_scale}}
+    for key, pat, src in (("k3_prefill_chunk_fwd", "chunk_fwd_kernel", "kda_chunk.hip"),
+                          ("decode_recurrent_step", "recurrent_step_kernel", "kda_step.hip")):
+        fk = [v for k, v in fetch.items() if pat in k]
+        wk = [v for k, v in write.items() if pat in k]
+        if not fk or not wk:
+            continue
+        out[key] = {"fetch_kib": fk[0], "write_kib": wk[0],
+                    "bytes_per_launch": fk[0] * f_scale + wk[0] * w_scale,
+                    "source_sha256_16": kernel_source_hash(src)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,7 +114,15 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                                "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE results into profiles/traffic.json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -83,6 +136,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d bytes 4 times" % n)
+        return
 
     # ---------------- prefill ---------------------------------------------------------
     B, T, H, K, V = 1, 8192, 96, 128, 128
