@@ -1,8 +1,8 @@
 // kda_step.hip -- fused single-token KDA decode step over a kept state (gfx950).
 //
 // Per (batch row, head), with the float32 state S [K x V] kept in HBM and
-// updated in place ("Kept memory": the call starts from the kept memory,
-// updates it with the one new token and keeps the result; PaperLeet
+// updated in place (Kept-memory page: a decode call updates the kept per-head state
+// with one token and leaves the result for the next call; PaperLeet
 // "Formula and conventions" for the recurrence):
 //   Sbar  = Diag(alpha) S
 //   p     = Sbar^T k,  r = Sbar^T q                    (two reductions over K, one pass)

@@ -8,9 +8,9 @@
  *    and the per-token recurrence
  *        Sbar_t = Diag(alpha_t) S_{t-1}
  *        S_t    = Sbar_t + beta_t k_t (v_t - k_t^T Sbar_t)^T
- *        o_t    = scale * S_t^T q_t          (scale = 1: the scan does no query scaling).
+ *        o_t    = scale * S_t^T q_t          (scale = 1 leaves q unscaled, as the contract has it).
  *  - KDA cheat sheet, "Chunkwise parallel form": the same recurrence evaluated
- *    chunk by chunk (recurrent across chunks, parallel within a chunk); and the
+ *    chunk by chunk (serial from one chunk to the next, parallel inside a chunk); and the
  *    gate table: g >= -5 bounds the cumulative log-decay of a 16-token tile by
  *    -80, which keeps every rescale factor of the chunk kernel finite.
  *  - "Kept memory" page: the per-head state is kept between calls and a decode
@@ -100,7 +100,7 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
  *                 final = initial).  N = num_seqs; the state restarts at every
  *                 sequence.  The offsets are read only on the device.
  *   chunk_size    16, 32 or 64: tokens per chunk (results differ only by rounding)
- *   scale         multiplies every output (1.0 = no query scaling)
+ *   scale         multiplies every output (1.0 leaves q unscaled)
  *   out    [B, T, H, V] in out_dtype
  * Supported: K, V in {16, 32, 64, 128} and chunk sizes whose per-workgroup LDS
  * layout fits 160 KB; kda_chunk_fwd_supported() tells which (chunk size 16 and 32 are
@@ -124,8 +124,8 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
 
 /*
  * kda_recurrent_step -- one decode token over a kept state, updated IN PLACE
- * ("Kept memory": the call starts from the kept memory, updates it with the one
- * new token and keeps the result; PaperLeet recurrence with T = 1).
+ * (Kept-memory page: a decode call advances the kept per-head state by one token and
+ * leaves the result for the next call; PaperLeet recurrence with T = 1).
  *
  *   q, k  [B, H, K] in in_dtype;  v [B, H, V] in in_dtype
  *   gate  [B, H, K] float32 (alpha or ln alpha, per gate_kind; any alpha in [0, 1])

@@ -8,7 +8,7 @@ IEEE double, libm ``exp``), written from the definitions on the pages:
 * "Kimi K3: Bounded Decay and Delta Memory", section "Formula and
   conventions": the bounded gate g = g_min * sigmoid(e^A z), alpha = e^g,
   and the fade / correct / read recurrence; its contract table fixes the
-  shapes, the empty-sequence rule and "no query scaling".
+  shapes, the empty-sequence rule and the absence of a query scale.
 * "KDARecurrent", section "The state recurrence in source order": the same
   loop order.
 

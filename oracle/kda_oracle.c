@@ -15,7 +15,7 @@
  *        S_t    = Sbar_t + beta_t k_t (v_t - k_t^T Sbar_t)^T
  *        o_t    = S_t^T q_t,
  *    plus its argument-contract table (shapes, empty sequence, initial
- *    state omitted means zeros, no query scaling inside the scan).
+ *    state omitted means zeros, the scan itself applies no scale to q).
  *  - "KDARecurrent" page, section "The state recurrence in source order":
  *    the same loop order (decay rows indexed by key features, predict with
  *    the decayed state, rank-one correction scaled by beta, read after write)
@@ -125,7 +125,7 @@ static void scan_pair(const double *q, const double *k, const double *v, const d
  *   cu_seqlens [num_seqs + 1] (B must be 1): sequence s is rows
  *              cu_seqlens[s] .. cu_seqlens[s+1]-1 of the single batch row, and
  *              its state restarts from initial_state[s] (or zeros).
- *   out [B, T, H, V]; scale multiplies the read (1.0 = no query scaling).
+ *   out [B, T, H, V]; scale multiplies the read (1.0 leaves q unscaled).
  * Returns 0, or -1 on an inconsistent argument (nothing is written then).
  */
 int kda_oracle_scan(const double *q, const double *k, const double *v, const double *alpha,

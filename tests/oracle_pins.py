@@ -80,8 +80,8 @@ def pin_exact_recall(orc):
 
 
 def pin_overwrite(orc):
-    """Cheat sheet lineage table, DeltaNet row: with the delta rule writes replace rather
-    than accumulate; the same unit key written twice returns the second value."""
+    """Cheat sheet lineage table, DeltaNet row: under the delta rule a second write to the
+    same unit key overwrites the first; reading that key returns the second value."""
     K, V = 4, 3
     key = np.array([0.5, 0.5, 0.5, 0.5])
     k = np.tile(key, (1, 3, 1, 1)); q = k.copy()
@@ -160,7 +160,7 @@ def pin_gated_deltanet(orc):
 
 
 def pin_segmented_continuation(orc):
-    """Contract: 'final_state can resume the scan'.  Splitting at an unaligned point and
+    """Contract: the returned state continues the scan.  Splitting at an unaligned point and
     resuming from the returned state gives the one-call result."""
     rs = np.random.default_rng(15)
     q, k, v, alpha, beta, s0 = _rand_inputs(rs, 2, 23, 2, 6, 5)
@@ -208,7 +208,7 @@ def pin_varlen_equals_separate(orc):
 
 def pin_scale_is_linear(orc):
     """The read is o_t = scale * S_t^T q_t: the state does not depend on scale and the
-    output is linear in it (scale 1 = the contract's 'no query scaling')."""
+    output is linear in it (scale 1 = the contract's unscaled read)."""
     rs = np.random.default_rng(18)
     q, k, v, alpha, beta, s0 = _rand_inputs(rs, 1, 6, 1, 4, 3)
     o1, f1 = orc.scan(q, k, v, alpha, beta, s0, scale=1.0)
