@@ -74,8 +74,6 @@ struct Layout {
     static constexpr int LCM = C + 16 / (int)sizeof(TM);
     static constexpr int LCF = C + 4;
     static constexpr int LKF = K + 4;                           // fp32 staging rows
-    static constexpr int NTC = NP * K;                          // prep tile-columns
-    static constexpr int TCPT = (NTC + NPT - 1) / NPT;          // tile-columns per prep thread
     static constexpr int NJT = BV / 16;                         // value column tiles
     static constexpr int MJ = (NJT + NSW - 1) / NSW;            // column tiles per state wave
 
@@ -89,7 +87,8 @@ struct Layout {
     static constexpr size_t oX = oRo + al16((size_t)(C > 16 ? C - 16 : 0) * LKF * 4);
     static constexpr size_t oAkk = oX + al16((size_t)NX * 16 * LKF * 4);
     static constexpr size_t oTf = oAkk + al16((size_t)C * LCF * 4);
-    static constexpr size_t oTP = oTf + al16((size_t)C * LCF * 4);
+    static constexpr size_t oAdt = oTf + al16((size_t)C * LCF * 4);   // [NP][16][20] diag blocks, transposed
+    static constexpr size_t oTP = oAdt + al16((size_t)NP * 16 * 20 * 4);
     static constexpr size_t oBt = oTP + al16((size_t)NP * K * 4);
     static constexpr size_t oPkg = oBt + al16((size_t)C * 4);
     // package (two copies)
@@ -192,6 +191,24 @@ __device__ __forceinline__ void mma_bfrag(f4 &acc, const float *arow, const BFra
     }
 }
 
+// store two consecutive elements (a at p[0], b at p[1]) as one packed write
+template <typename T>
+__device__ __forceinline__ void st2(T *p, float a, float b);
+template <>
+__device__ __forceinline__ void st2<float>(float *p, float a, float b) {
+    *reinterpret_cast<float2 *>(p) = float2{a, b};
+}
+template <>
+__device__ __forceinline__ void st2<__bf16>(__bf16 *p, float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 v2;
+    *reinterpret_cast<v2 *>(p) = v2{(__bf16)a, (__bf16)b};
+}
+template <>
+__device__ __forceinline__ void st2<_Float16>(_Float16 *p, float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) _Float16 v2;
+    *reinterpret_cast<v2 *>(p) = v2{(_Float16)a, (_Float16)b};
+}
+
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier for LDS traffic only.  The waves exchange data through LDS alone,
@@ -214,14 +231,15 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &
         lo[i] = (__bf16)(x[i] - (float)hi[i]);
     }
 }
-template <class P, bool SPLIT, typename TAr>
-__device__ __forceinline__ void mma_rowsrc(f4 &acc, const TAr *A, int lda, const float *B, int ldb, int kdim,
-                                           int lane) {
+template <class P, bool SPLIT, int kdim, typename TAr>
+__device__ __forceinline__ void mma_rowsrc(f4 &acc, const TAr *A, int lda, const float *B, int ldb, int lane) {
     const int r = lane & 15, g = lane >> 4;
     if constexpr (std::is_same<typename P::TA, float>::value) {
+#pragma unroll
         for (int k0 = 0; k0 < kdim; k0 += 4)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + g], B[r * ldb + k0 + g], acc, 0, 0, 0);
     } else {
+#pragma unroll
         for (int k0 = 0; k0 < kdim; k0 += 32) {
             // a 16-wide tail (kdim % 32 == 16) fills the lower half of each operand and
             // zeroes the upper half
@@ -436,6 +454,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     float *Xv = reinterpret_cast<float *>(smem + L::oX);    // [NX][16][LKF]
     float *Akk = reinterpret_cast<float *>(smem + L::oAkk); // [C][LCF]
     float *Tf = reinterpret_cast<float *>(smem + L::oTf);   // [C][LCF]
+    float *Adt = reinterpret_cast<float *>(smem + L::oAdt); // [NP][16][20]: A_kk diagonal blocks, transposed
     float *TPv = reinterpret_cast<float *>(smem + L::oTP);  // [NP][K] tile decay products
     float *Btv = reinterpret_cast<float *>(smem + L::oBt);  // [C] beta of the chunk
 
@@ -454,48 +473,71 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
         }
     }
 
-    // Raw inputs of one chunk, per tile-column (channel c, tile p): 16 rows of the gate,
-    // q and k, beta of row tp, and this thread's share of the value block.  The loads
-    // are unconditional (rows past the sequence end read its last row) and nothing is
+    // Prep mapping: a "combo" is a (channel pair, 16-row tile); each combo is handled by
+    // two lanes of one wave, lane l (rows 0..7 of the tile) and lane l ^ 32 (rows 8..15),
+    // so in-tile prefix and suffix decay products need one exchange between them.
+    constexpr int NCP = K / 2;                   // channel pairs
+    constexpr int NCOMBO = NCP * NP;
+    constexpr int CPT = (NCOMBO + 127) / 128;    // combos per lane pair (4 prep waves x 32)
+    const int hf = lane >> 5;                    // which half of the tile
+    auto combo_of = [&](int u) { return 128 * u + 32 * pw + (lane & 31); };
+
+    // Raw inputs of one chunk: for each combo, 8 rows x 2 channels of the gate, q and k;
+    // beta of row tp; this thread's share of the value block.  The loads are
+    // unconditional (rows past the sequence end read its last row) and nothing is
     // computed from them until they are used in the next iteration, so they stay in
     // flight while the current chunk is processed; the padding rows are masked at use.
     using RawIn = typename std::conditional<std::is_same<TIn, float>::value, float, unsigned short>::type;
-    float ral[L::TCPT][16];
-    RawIn rq[L::TCPT][16], rk[L::TCPT][16];
+    using RawPair = typename std::conditional<std::is_same<TIn, float>::value, float2, uint32_t>::type;
+    float2 ral[CPT][8];
+    RawPair rq[CPT][8], rk[CPT][8];
     float rbeta = 0.f;
     constexpr int NVE = (BV * C + NPT - 1) / NPT;  // beta*V elements per prep thread
     RawIn rv[NVE];
     auto load_raw = [&](int cn) {
         const int64_t t0 = bos + (int64_t)cn * C;
         const int last = (int)((eos - t0) < C ? (eos - t0) : C) - 1;  // last valid row (>= 0)
-        const int64_t rs = (int64_t)H * K;                          // row stride of q, k, gate
-        const RawIn *qr = reinterpret_cast<const RawIn *>(q);
-        const RawIn *kr = reinterpret_cast<const RawIn *>(k);
-        const RawIn *vr = reinterpret_cast<const RawIn *>(v);
+        const int rs = H * K;                                        // row stride of q, k, gate
+        const int64_t cb = (t0 * H + h) * K;                         // chunk base (uniform)
+        const float *gb = a.gate + cb;
+        const RawIn *qb = reinterpret_cast<const RawIn *>(q) + cb;
+        const RawIn *kb = reinterpret_cast<const RawIn *>(k) + cb;
 #pragma unroll
-        for (int u = 0; u < L::TCPT; ++u) {
-            const int tc = tp + NPT * u < L::NTC ? tp + NPT * u : 0;
-            const int c = tc % K, p = tc / K;
-            const int64_t base = (t0 * H + h) * K + c;
+        for (int u = 0; u < CPT; ++u) {
+            const int cm = combo_of(u) < NCOMBO ? combo_of(u) : 0;
+            const int c0 = 2 * (cm % NCP);
+            int p = cm / NCP;
+            if constexpr (NCP % 32 == 0) p = __builtin_amdgcn_readfirstlane(p);  // one tile per wave
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t o = base + (int64_t)(16 * p + i < last ? 16 * p + i : last) * rs;
-                ral[u][i] = a.gate[o];
-                rq[u][i] = qr[o];
-                rk[u][i] = kr[o];
+            for (int i = 0; i < 8; ++i) {
+                const int r = 16 * p + 8 * hf + i;
+                const uint32_t o = (uint32_t)((r < last ? r : last) * rs + c0);
+                ral[u][i] = *reinterpret_cast<const float2 *>(gb + o);
+                rq[u][i] = *reinterpret_cast<const RawPair *>(qb + o);
+                rk[u][i] = *reinterpret_cast<const RawPair *>(kb + o);
             }
         }
         rbeta = a.beta[(t0 + (tp < last ? tp : last)) * H + h];
+        const RawIn *vbp = reinterpret_cast<const RawIn *>(v) + (t0 * H + h) * V + vb * BV;
 #pragma unroll
         for (int w = 0; w < NVE; ++w) {
             const int e = (tp + NPT * w) % (BV * C);
             const int j = e % BV, r = e / BV;
-            rv[w] = vr[((t0 + (r < last ? r : last)) * H + h) * V + vb * BV + j];
+            rv[w] = vbp[(uint32_t)((r < last ? r : last) * H * V + j)];
         }
     };
     auto raw_f32 = [&](RawIn x) -> float {
         if constexpr (std::is_same<RawIn, float>::value) return x;
         else return __builtin_bit_cast(float, (uint32_t)x << 16);
+    };
+    auto pair_f32 = [&](RawPair x, float &lo, float &hi) {
+        if constexpr (std::is_same<RawPair, float2>::value) {
+            lo = x.x;
+            hi = x.y;
+        } else {
+            lo = __builtin_bit_cast(float, x << 16);
+            hi = __builtin_bit_cast(float, x & 0xffff0000u);
+        }
     };
     // right operand of A-matrix tile (p, qt), fp32 staging
     auto right_of = [&](int p, int qt) -> const float * {
@@ -507,24 +549,41 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     };
     if (nchunks > 0) load_raw(0);
 
+    // per combo: decay factor entering this half from the other one (prefix: product of
+    // rows 0..7 for the second half; suffix: product of rows 8..15 for the first half)
+    float2 pin[CPT], sin[CPT];
     for (int it = 0; it <= nchunks; ++it) {
         const bool work = it < nchunks;
         const int n_it = work ? (int)((eos - (bos + (int64_t)it * C)) < C ? (eos - (bos + (int64_t)it * C)) : C) : 0;
         // ---- phase 1a: retention factors (1 on padding rows), tile totals, beta --------
         if (work) {
 #pragma unroll
-            for (int u = 0; u < L::TCPT; ++u) {
-                const int tc = tp + NPT * u;
-                const int p = tc / K;
-                float run = 1.f;
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u);
+                const int p = cm / NCP;
+                float2 run = {1.f, 1.f};
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float al = a.gate_is_log ? __expf(ral[u][i]) : ral[u][i];
-                    al = (16 * p + i < n_it) ? al : 1.f;
+                for (int i = 0; i < 8; ++i) {
+                    float2 al = ral[u][i];
+                    if (a.gate_is_log) {
+                        al.x = __expf(al.x);
+                        al.y = __expf(al.y);
+                    }
+                    if (16 * p + 8 * hf + i >= n_it) al = float2{1.f, 1.f};
                     ral[u][i] = al;
-                    run *= al;
+                    run.x *= al.x;
+                    run.y *= al.y;
                 }
-                if (tc < L::NTC) TPv[p * K + tc % K] = run;
+                // the other half's product
+                float2 oth;
+                oth.x = __shfl_xor(run.x, 32);
+                oth.y = __shfl_xor(run.y, 32);
+                pin[u] = hf ? oth : float2{1.f, 1.f};
+                sin[u] = hf ? float2{1.f, 1.f} : oth;
+                if (hf == 0 && cm < NCOMBO) {
+                    const int c0 = 2 * (cm % NCP);
+                    *reinterpret_cast<float2 *>(TPv + p * K + c0) = float2{run.x * oth.x, run.y * oth.y};
+                }
             }
             if (tp < C) Btv[tp] = tp < n_it ? rbeta : 0.f;
         }
@@ -538,73 +597,89 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
             TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
             float *eGC = reinterpret_cast<float *>(pk + L::pGC);
 #pragma unroll
-            for (int u = 0; u < L::TCPT; ++u) {
-                const int tc = tp + NPT * u;
-                if (tc >= L::NTC) continue;
-                const int c = tc % K, p = tc / K;
-                float tpr[NP];
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u);
+                if (cm >= NCOMBO) continue;
+                const int c0 = 2 * (cm % NCP), p = cm / NCP;
+                float2 tpr[NP];
 #pragma unroll
-                for (int pp = 0; pp < NP; ++pp) tpr[pp] = TPv[pp * K + c];
-                float eR = 1.f, eCE = 1.f, eAll = 1.f;
+                for (int pp = 0; pp < NP; ++pp) tpr[pp] = *reinterpret_cast<const float2 *>(TPv + pp * K + c0);
+                float2 eR = {1.f, 1.f}, eCE = {1.f, 1.f}, eAll = {1.f, 1.f}, own = {1.f, 1.f};
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp) {
-                    if (pp < p) eR *= tpr[pp];
-                    if (pp > p) eCE *= tpr[pp];
-                    eAll *= tpr[pp];
+                    if (pp < p) { eR.x *= tpr[pp].x; eR.y *= tpr[pp].y; }
+                    if (pp > p) { eCE.x *= tpr[pp].x; eCE.y *= tpr[pp].y; }
+                    if (pp == p) own = tpr[pp];
+                    eAll.x *= tpr[pp].x;
+                    eAll.y *= tpr[pp].y;
                 }
-                if (p == 0) eGC[c] = eAll;
-                const float rT = 1.f / tpr[p];
+                if (p == 0 && hf == 0) *reinterpret_cast<float2 *>(eGC + c0) = eAll;
+                const float2 rT = {1.f / own.x, 1.f / own.y};
                 // extra right-operand versions for tiles (pp, p) with pp >= p + 2
-                float xf[NP];
+                float2 xf[NP];
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp) {
-                    float f = 1.f;
+                    float2 f = {1.f, 1.f};
 #pragma unroll
                     for (int r2 = 0; r2 < NP; ++r2)
-                        if (r2 > p && r2 < pp) f *= tpr[r2];
+                        if (r2 > p && r2 < pp) { f.x *= tpr[r2].x; f.y *= tpr[r2].y; }
                     xf[pp] = f;
                 }
-                float bet[16];
+                float bet[8];
 #pragma unroll
-                for (int i = 0; i < 16; i += 4) {
-                    const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + i);
+                for (int i = 0; i < 8; i += 4) {
+                    const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + 8 * hf + i);
                     bet[i] = b4.x; bet[i + 1] = b4.y; bet[i + 2] = b4.z; bet[i + 3] = b4.w;
                 }
-                float suf[16];  // E_p / gamma_i: product of the tile's later factors
+                float2 suf[8];  // E_p / gamma_i: product of the tile's later factors
                 {
-                    float run = 1.f;
+                    float2 run = sin[u];
 #pragma unroll
-                    for (int i = 15; i >= 0; --i) {
+                    for (int i = 7; i >= 0; --i) {
                         suf[i] = run;
-                        run *= ral[u][i];
+                        run.x *= ral[u][i].x;
+                        run.y *= ral[u][i].y;
                     }
                 }
-                float pre = 1.f;  // gamma_i / R_p
+                float2 pre = pin[u];  // gamma_i / R_p
+                float2 kk_prev = {0.f, 0.f};  // k E_p / gamma of the previous row (token pairs of Kt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = 16 * p + i;
-                    pre *= ral[u][i];
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 16 * p + 8 * hf + i;
+                    pre.x *= ral[u][i].x;
+                    pre.y *= ral[u][i].y;
                     const bool ok = r < n_it;
-                    const float qv = ok ? raw_f32(rq[u][i]) : 0.f, kv = ok ? raw_f32(rk[u][i]) : 0.f;
-                    const float lq = qv * pre;
-                    const float lk = bet[i] * kv * pre;
-                    const float ro = kv * suf[i];  // k E_p / gamma <= |k|
-                    const float rd = ro * rT;      // k R_p / gamma <= e^80 |k|
-                    Lk[r * L::LKA + c] = from_f32<TA>(lk);
-                    Lq[r * L::LKF + c] = lq;
-                    Rd[r * L::LKF + c] = rd;
-                    if (p < NP - 1) Ro[r * L::LKF + c] = ro;
+                    float q0, q1, k0, k1;
+                    pair_f32(rq[u][i], q0, q1);
+                    pair_f32(rk[u][i], k0, k1);
+                    if (!ok) q0 = q1 = k0 = k1 = 0.f;
+                    const float2 lq = {q0 * pre.x, q1 * pre.y};
+                    const float2 lk = {bet[i] * k0 * pre.x, bet[i] * k1 * pre.y};
+                    const float2 ro = {k0 * suf[i].x, k1 * suf[i].y};  // k E_p / gamma <= |k|
+                    const float2 rd = {ro.x * rT.x, ro.y * rT.y};        // k R_p / gamma <= e^80 |k|
+                    st2<TA>(Lk + r * L::LKA + c0, lk.x, lk.y);
+                    *reinterpret_cast<float2 *>(Lq + r * L::LKF + c0) = lq;
+                    *reinterpret_cast<float2 *>(Rd + r * L::LKF + c0) = rd;
+                    if (p < NP - 1) *reinterpret_cast<float2 *>(Ro + r * L::LKF + c0) = ro;
                     if constexpr (L::NX > 0) {
                         int xi = 0;
 #pragma unroll
                         for (int pp = 2; pp < NP; ++pp)
 #pragma unroll
                             for (int qq = 0; qq + 2 <= pp; ++qq, ++xi)
-                                if (qq == p) Xv[(size_t)xi * 16 * L::LKF + i * L::LKF + c] = ro * xf[pp];
+                                if (qq == p)
+                                    *reinterpret_cast<float2 *>(Xv + (size_t)xi * 16 * L::LKF + (8 * hf + i) * L::LKF + c0) =
+                                        float2{ro.x * xf[pp].x, ro.y * xf[pp].y};
                     }
-                    Qt[r * L::LKM + c] = from_f32<TM>(lq * eR);
-                    Bw[r * L::LKM + c] = from_f32<TM>(-lk * eR);
-                    Kt[c * L::LCM + r] = from_f32<TM>(ro * eCE);
+                    st2<TM>(Qt + r * L::LKM + c0, lq.x * eR.x, lq.y * eR.y);
+                    st2<TM>(Bw + r * L::LKM + c0, -lk.x * eR.x, -lk.y * eR.y);
+                    const float2 kt = {ro.x * eCE.x, ro.y * eCE.y};
+                    if (i & 1) {
+                        // two consecutive tokens per channel row of Kt
+                        st2<TM>(Kt + c0 * L::LCM + r - 1, kk_prev.x, kt.x);
+                        st2<TM>(Kt + (c0 + 1) * L::LCM + r - 1, kk_prev.y, kt.y);
+                    }
+                    kk_prev = kt;
                 }
             }
 #pragma unroll
@@ -625,40 +700,60 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 for (int p = 0; p < NP; ++p)
                     for (int qt = 0; qt <= p; ++qt) {
                         f4 acc = {0.f, 0.f, 0.f, 0.f};
-                        mma_rowsrc<P, false>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKF, K, lane);
+                        mma_rowsrc<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKF, lane);
                         const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) Akk[(i0 + e) * L::LCF + j] = (j < i0 + e) ? acc[e] : 0.f;
+                        if (qt == p) {
+                            // column j of the diagonal block as a row: Adt[p][j][i] = A[i][j]
+                            float4 t4;
+                            t4.x = (j < i0) ? acc[0] : 0.f;
+                            t4.y = (j < i0 + 1) ? acc[1] : 0.f;
+                            t4.z = (j < i0 + 2) ? acc[2] : 0.f;
+                            t4.w = (j < i0 + 3) ? acc[3] : 0.f;
+                            *reinterpret_cast<float4 *>(Adt + (p * 16 + (lane & 15)) * 20 + 4 * g) = t4;
+                        }
                     }
                 lds_fence();
                 // diagonal blocks of T = (I + A_kk)^-1 by forward substitution, one column
-                // per lane (lane = 16 * block + column)
+                // per lane (lane = 16 * block + column), column-oriented: once x_j is final
+                // it is folded into every later row at once, so the dependent chain is one
+                // multiply-add per row
                 if (lane < 16 * NP) {
                     const int p = lane >> 4, cc = lane & 15;
-                    const float *A = Akk + (p * 16) * L::LCF + p * 16;
-                    float x[16];
+                    const float *At = Adt + p * 16 * 20;  // At[j][i] = A[i][j]
+                    float acc[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float row[16];
+                    for (int i = 0; i < 16; ++i) acc[i] = (i == cc) ? 1.f : 0.f;
+                    float4 col[4];
 #pragma unroll
-                        for (int j4 = 0; j4 < 16; j4 += 4) {
-                            if (j4 < i) {
-                                const float4 r4 = *reinterpret_cast<const float4 *>(A + i * L::LCF + j4);
-                                row[j4] = r4.x; row[j4 + 1] = r4.y; row[j4 + 2] = r4.z; row[j4 + 3] = r4.w;
-                            }
+                    for (int q4 = 0; q4 < 4; ++q4) col[q4] = *reinterpret_cast<const float4 *>(At + 4 * q4);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        float4 nxt[4];
+                        if (j + 1 < 16) {
+#pragma unroll
+                            for (int q4 = 0; q4 < 4; ++q4)
+                                nxt[q4] = *reinterpret_cast<const float4 *>(At + (j + 1) * 20 + 4 * q4);
                         }
-                        float acc0 = (i == cc) ? 1.f : 0.f, acc1 = 0.f;
+                        const float xj = acc[j];
+                        float cv[16];
 #pragma unroll
-                        for (int jj = 0; jj < i; ++jj) {
-                            if (jj & 1) acc1 -= row[jj] * x[jj];
-                            else acc0 -= row[jj] * x[jj];
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            cv[4 * q4] = col[q4].x; cv[4 * q4 + 1] = col[q4].y;
+                            cv[4 * q4 + 2] = col[q4].z; cv[4 * q4 + 3] = col[q4].w;
                         }
-                        x[i] = (i < cc) ? 0.f : acc0 + acc1;
+#pragma unroll
+                        for (int i = j + 1; i < 16; ++i) acc[i] -= cv[i] * xj;
+                        if (j + 1 < 16) {
+#pragma unroll
+                            for (int q4 = 0; q4 < 4; ++q4) col[q4] = nxt[q4];
+                        }
                     }
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        Tf[(p * 16 + i) * L::LCF + p * 16 + cc] = x[i];
-                        Tm[(p * 16 + i) * L::LCM + p * 16 + cc] = from_f32<TM>(x[i]);
+                        Tf[(p * 16 + i) * L::LCF + p * 16 + cc] = acc[i];
+                        Tm[(p * 16 + i) * L::LCM + p * 16 + cc] = from_f32<TM>(acc[i]);
                     }
                 }
                 lds_fence();
@@ -696,7 +791,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     for (int qt = 0; qt <= p; ++qt, ++task) {
                         if (task % 3 != pw - 1) continue;
                         f4 acc = {0.f, 0.f, 0.f, 0.f};
-                        mma_rowsrc<P, P::kSplit>(acc, Lq + p * 16 * L::LKF, L::LKF, right_of(p, qt), L::LKF, K, lane);
+                        mma_rowsrc<P, P::kSplit, K>(acc, Lq + p * 16 * L::LKF, L::LKF, right_of(p, qt), L::LKF, lane);
                         const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) Aqk[(i0 + e) * L::LCM + j] = from_f32<TM>((j <= i0 + e) ? acc[e] : 0.f);
