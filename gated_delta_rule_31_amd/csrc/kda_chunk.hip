@@ -492,8 +492,8 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     float2 ral[CPT][8];
     RawPair rq[CPT][8], rk[CPT][8];
     float rbeta = 0.f;
-    constexpr int NVE = (BV * C + NPT - 1) / NPT;  // beta*V elements per prep thread
-    RawIn rv[NVE];
+    constexpr int NVE = (BV * C / 2 + NPT - 1) / NPT;  // (column, token pair) items per prep thread
+    RawIn rv[NVE][2];
     auto load_raw = [&](int cn) {
         const int64_t t0 = bos + (int64_t)cn * C;
         const int last = (int)((eos - t0) < C ? (eos - t0) : C) - 1;  // last valid row (>= 0)
@@ -521,9 +521,10 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
         const RawIn *vbp = reinterpret_cast<const RawIn *>(v) + (t0 * H + h) * V + vb * BV;
 #pragma unroll
         for (int w = 0; w < NVE; ++w) {
-            const int e = (tp + NPT * w) % (BV * C);
-            const int j = e % BV, r = e / BV;
-            rv[w] = vbp[(uint32_t)((r < last ? r : last) * H * V + j)];
+            const int e = (tp + NPT * w) % (BV * C / 2);
+            const int j = e % BV, r = 2 * (e / BV);
+            rv[w][0] = vbp[(uint32_t)((r < last ? r : last) * H * V + j)];
+            rv[w][1] = vbp[(uint32_t)((r + 1 < last ? r + 1 : last) * H * V + j)];
         }
     };
     auto raw_f32 = [&](RawIn x) -> float {
@@ -685,9 +686,12 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int w = 0; w < NVE; ++w) {
                 const int e = tp + NPT * w;
-                if (e < BV * C) bV[(e % BV) * L::LCM + e / BV] = from_f32<TM>(raw_f32(rv[w]) * Btv[e / BV]);
+                if (e < BV * C / 2) {
+                    const int j = e % BV, r = 2 * (e / BV);
+                    st2<TM>(bV + j * L::LCM + r, raw_f32(rv[w][0]) * Btv[r], raw_f32(rv[w][1]) * Btv[r + 1]);
+                }
             }
-            if (it + 1 < nchunks) load_raw(it + 1);  // prefetch; consumed next iteration
+            if (pw == 0 && it + 1 < nchunks) load_raw(it + 1);  // prefetch; consumed next iteration
         }
         lds_barrier();  // B2
         // ---- phase 2: A_kk and T (prep wave 0), A_qk (prep waves 1..3) -----------------
@@ -697,7 +701,9 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
             TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
             if (pw == 0) {
                 // A_kk (strictly lower) in fp32
+#pragma unroll
                 for (int p = 0; p < NP; ++p)
+#pragma unroll
                     for (int qt = 0; qt <= p; ++qt) {
                         f4 acc = {0.f, 0.f, 0.f, 0.f};
                         mma_rowsrc<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKF, lane);
@@ -725,30 +731,28 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     float acc[16];
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[i] = (i == cc) ? 1.f : 0.f;
-                    float4 col[4];
+                    // columns j, j+1 and j+2 of the block in flight at once
+                    float4 col[3][4];
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) col[q4] = *reinterpret_cast<const float4 *>(At + 4 * q4);
+                    for (int d = 0; d < 2; ++d)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) col[d][q4] = *reinterpret_cast<const float4 *>(At + d * 20 + 4 * q4);
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        float4 nxt[4];
-                        if (j + 1 < 16) {
+                        if (j + 2 < 16) {
 #pragma unroll
                             for (int q4 = 0; q4 < 4; ++q4)
-                                nxt[q4] = *reinterpret_cast<const float4 *>(At + (j + 1) * 20 + 4 * q4);
+                                col[(j + 2) % 3][q4] = *reinterpret_cast<const float4 *>(At + (j + 2) * 20 + 4 * q4);
                         }
                         const float xj = acc[j];
                         float cv[16];
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4) {
-                            cv[4 * q4] = col[q4].x; cv[4 * q4 + 1] = col[q4].y;
-                            cv[4 * q4 + 2] = col[q4].z; cv[4 * q4 + 3] = col[q4].w;
+                            cv[4 * q4] = col[j % 3][q4].x; cv[4 * q4 + 1] = col[j % 3][q4].y;
+                            cv[4 * q4 + 2] = col[j % 3][q4].z; cv[4 * q4 + 3] = col[j % 3][q4].w;
                         }
 #pragma unroll
                         for (int i = j + 1; i < 16; ++i) acc[i] -= cv[i] * xj;
-                        if (j + 1 < 16) {
-#pragma unroll
-                            for (int q4 = 0; q4 < 4; ++q4) col[q4] = nxt[q4];
-                        }
                     }
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
@@ -785,10 +789,14 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     lds_fence();
                 }
             } else {
-                // A_qk, lower tiles only (the upper ones stay zero)
-                int task = 0;
+                // A_qk, lower tiles only (the upper ones stay zero); this wave's prefetch of
+                // the next chunk goes out first (wave 0's went out at the end of phase 1b)
+                if (it + 1 < nchunks) load_raw(it + 1);
+#pragma unroll
                 for (int p = 0; p < NP; ++p)
-                    for (int qt = 0; qt <= p; ++qt, ++task) {
+#pragma unroll
+                    for (int qt = 0; qt <= p; ++qt) {
+                        const int task = p * (p + 1) / 2 + qt;
                         if (task % 3 != pw - 1) continue;
                         f4 acc = {0.f, 0.f, 0.f, 0.f};
                         mma_rowsrc<P, P::kSplit, K>(acc, Lq + p * 16 * L::LKF, L::LKF, right_of(p, qt), L::LKF, lane);
