@@ -264,7 +264,21 @@ def main():
                          "launch_us_avg": step_avg * 1e3, "launch_us_median": step_med * 1e3,
                          "algorithmic_bytes_per_launch": d_bytes},
         }
-        del dec, state
+        # a plain device copy of the same byte count, timed the same way, as a practical
+        # reference for what read+write streaming reaches on this GPU (context only)
+        half = d_bytes // 2
+        src = torch.empty(half, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a_, b_ in cev:
+            a_.record(stream)
+            dst.copy_(src)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = sum(a_.elapsed_time(b_) for a_, b_ in cev) / len(cev)
+        result["decode"]["device_copy_GBps_same_bytes"] = 2 * half / (copy_ms * 1e-3) / 1e9
+        del dec, state, src, dst
 
     # ---------------- CPU baseline: the oracle on a head sample -------------------------
     if not args.no_cpu_baseline:

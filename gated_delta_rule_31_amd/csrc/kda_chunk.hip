@@ -405,8 +405,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     }
                 }
             }
-            lds_barrier();  // B2: prep waves have written the A-matrix operands
-            if (cn >= 0) {
+            if (cn >= 0) {  // S = gamma_C S + Kt^T Vt, still before B2
                 const unsigned char *pk = pkg(cn & 1);
                 const TM *Kt = reinterpret_cast<const TM *>(pk + L::pKt);
                 const float *eGC = reinterpret_cast<const float *>(pk + L::pGC);
@@ -426,6 +425,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     Sh[mj].set(S[mj]);
                 }
             }
+            lds_barrier();  // B2: prep waves have written the A-matrix operands
             lds_barrier();  // B3: the next package is complete
         }
         if (a.final_state) {

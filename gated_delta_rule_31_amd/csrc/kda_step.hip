@@ -49,9 +49,14 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
     const float *gate = a.gate + (int64_t)pair * K;
     float4 *S = reinterpret_cast<float4 *>(a.state + (int64_t)pair * K * V);
 
+    // the state is streamed: read once and written once per step, so both use
+    // non-temporal accesses that do not displace other data from the caches
     float4 s[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) s[i] = S[(rg + NRG * i) * CQ + cq];
+    for (int i = 0; i < RPT; ++i) {
+        const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * CQ + cq]));
+        s[i] = float4{x[0], x[1], x[2], x[3]};
+    }
 
     float4 pp = {0.f, 0.f, 0.f, 0.f}, rr = {0.f, 0.f, 0.f, 0.f};
     float kq = 0.f;
@@ -96,7 +101,7 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
     for (int i = 0; i < RPT; ++i) {
         float4 x = s[i];
         x.x += kr[i] * d4.x; x.y += kr[i] * d4.y; x.z += kr[i] * d4.z; x.w += kr[i] * d4.w;
-        S[(rg + NRG * i) * CQ + cq] = x;
+        __builtin_nontemporal_store(f4{x.x, x.y, x.z, x.w}, reinterpret_cast<f4 *>(&S[(rg + NRG * i) * CQ + cq]));
     }
 }
 
