@@ -73,19 +73,22 @@ struct Layout {
     static constexpr int LKM = K + 16 / (int)sizeof(TM);
     static constexpr int LCM = C + 16 / (int)sizeof(TM);
     static constexpr int LCF = C + 4;
-    static constexpr int LKF = K + 4;                           // fp32 staging rows
+    static constexpr int LKS = K + 16 / (int)sizeof(TA);        // staging rows
     static constexpr int NJT = BV / 16;                         // value column tiles
     static constexpr int MJ = (NJT + NSW - 1) / NSW;            // column tiles per state wave
 
-    // prep-private
-    // Lk in the A-operand type; Lq, Rd, Ro and the extra versions X staged in fp32 (the
-    // matrix-core tasks round them to bf16, or split them into hi + lo bf16, as they load)
+    // operand staging of the A-matrix products, in the A-operand type: Lk, then one block
+    // holding Lq, Rd, Ro and the extra right-operand versions X (element offsets sLq..sX).
+    // With a split precision the block is followed by a copy of the same shape holding
+    // the low parts (x - hi), NST elements further on.
     static constexpr size_t oLk = 0;
-    static constexpr size_t oLq = oLk + al16((size_t)C * LKA * sizeof(TA));
-    static constexpr size_t oRd = oLq + al16((size_t)C * LKF * 4);
-    static constexpr size_t oRo = oRd + al16((size_t)C * LKF * 4);
-    static constexpr size_t oX = oRo + al16((size_t)(C > 16 ? C - 16 : 0) * LKF * 4);
-    static constexpr size_t oAkk = oX + al16((size_t)NX * 16 * LKF * 4);
+    static constexpr size_t oSt = oLk + al16((size_t)C * LKA * sizeof(TA));
+    static constexpr int sLq = 0;
+    static constexpr int sRd = sLq + C * LKS;
+    static constexpr int sRo = sRd + C * LKS;
+    static constexpr int sX = sRo + (C > 16 ? C - 16 : 0) * LKS;
+    static constexpr int NST = sX + NX * 16 * LKS;
+    static constexpr size_t oAkk = oSt + al16((size_t)NST * sizeof(TA) * (P::kSplit ? 2 : 1));
     static constexpr size_t oTf = oAkk + al16((size_t)C * LCF * 4);
     static constexpr size_t oAdt = oTf + al16((size_t)C * LCF * 4);   // [NP][16][20] diag blocks, transposed
     static constexpr size_t oTP = oAdt + al16((size_t)NP * 16 * 20 * 4);
@@ -216,77 +219,162 @@ __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)
 // chunk does); __syncthreads() would drain them at every barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// acc += A[16 x kdim] * B[kdim x 16] for the A-matrix tiles: A rows in `A` (the Lk operand
-// type, or fp32 staging), B^T rows in fp32 staging.  On the bf16 path the fp32 values are
-// rounded to bf16 as they are loaded; with SPLIT both operands are split into hi + lo
-// bf16 and the product is hi*hi + hi*lo + lo*hi (about 16 mantissa bits).
-__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
-    const float4 u = *reinterpret_cast<const float4 *>(p), w = *reinterpret_cast<const float4 *>(p + 4);
-    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
-}
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        hi[i] = (__bf16)x[i];
-        lo[i] = (__bf16)(x[i] - (float)hi[i]);
-    }
-}
-template <class P, bool SPLIT, int kdim, typename TAr>
-__device__ __forceinline__ void mma_rowsrc(f4 &acc, const TAr *A, int lda, const float *B, int ldb, int lane) {
+// acc += A[16 x kdim] * B[kdim x 16] for the A-matrix tiles: A rows and B^T rows staged
+// in the A-operand type (k contiguous).  With SPLIT both operands also have low parts
+// (x - hi) `lo` elements further on, and the product is hi*hi + hi*lo + lo*hi (about 16
+// mantissa bits).
+template <class P, bool SPLIT, int kdim>
+__device__ __forceinline__ void mma_stage(f4 &acc, const typename P::TA *A, int lda, const typename P::TA *B,
+                                          int ldb, int lo, int lane) {
     const int r = lane & 15, g = lane >> 4;
     if constexpr (std::is_same<typename P::TA, float>::value) {
 #pragma unroll
         for (int k0 = 0; k0 < kdim; k0 += 4)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + g], B[r * ldb + k0 + g], acc, 0, 0, 0);
     } else {
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+        const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+        auto ld = [&](const __bf16 *p, int k0) -> bf16x8 {
+            if (k0 + 32 > kdim) {
+                // a 16-wide tail fills the lower half of the operand, the upper half is zero
+                const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p + k0 + 4 * g);
+                return __builtin_shufflevector(x, z4, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            return *reinterpret_cast<const bf16x8 *>(p + k0 + 8 * g);
+        };
 #pragma unroll
         for (int k0 = 0; k0 < kdim; k0 += 32) {
-            // a 16-wide tail (kdim % 32 == 16) fills the lower half of each operand and
-            // zeroes the upper half
-            const bool tail = k0 + 32 > kdim;
-            float xb[8];
-            if (tail) {
-                const float4 u = *reinterpret_cast<const float4 *>(B + r * ldb + k0 + 4 * g);
-                xb[0] = u.x; xb[1] = u.y; xb[2] = u.z; xb[3] = u.w; xb[4] = xb[5] = xb[6] = xb[7] = 0.f;
-            } else {
-                ld8(B + r * ldb + k0 + 8 * g, xb);
-            }
-            bf16x8 bh, bl;
-            bf16x8 ah, al;
-            if constexpr (SPLIT) split8(xb, bh, bl);
-            else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) bh[i] = (__bf16)xb[i];
-            }
-            if constexpr (std::is_same<TAr, float>::value) {
-                float xa[8];
-                if (tail) {
-                    const float4 u = *reinterpret_cast<const float4 *>(A + r * lda + k0 + 4 * g);
-                    xa[0] = u.x; xa[1] = u.y; xa[2] = u.z; xa[3] = u.w; xa[4] = xa[5] = xa[6] = xa[7] = 0.f;
-                } else {
-                    ld8(A + r * lda + k0 + 8 * g, xa);
-                }
-                if constexpr (SPLIT) split8(xa, ah, al);
-                else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) ah[i] = (__bf16)xa[i];
-                }
-            } else {
-                if (tail) {
-                    const TAr *pa = A + r * lda + k0 + 4 * g;
-                    const __bf16 z = (__bf16)0.f;
-                    ah = bf16x8{pa[0], pa[1], pa[2], pa[3], z, z, z, z};
-                } else {
-                    ah = *reinterpret_cast<const bf16x8 *>(A + r * lda + k0 + 8 * g);
-                }
-            }
+            const bf16x8 ah = ld(A + r * lda, k0), bh = ld(B + r * ldb, k0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
             if constexpr (SPLIT) {
+                const bf16x8 al = ld(A + lo + r * lda, k0), bl = ld(B + lo + r * ldb, k0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
             }
         }
     }
+}
+
+// Store two staged values in the A-operand type; with a split precision also their low
+// parts (x - hi), `lo` elements further on.
+template <class P>
+__device__ __forceinline__ void st2_stage(typename P::TA *p, int lo, float a, float b) {
+    if constexpr (std::is_same<typename P::TA, float>::value) {
+        *reinterpret_cast<float2 *>(p) = float2{a, b};
+    } else {
+        typedef __attribute__((ext_vector_type(2))) __bf16 v2;
+        const v2 h = {(__bf16)a, (__bf16)b};
+        *reinterpret_cast<v2 *>(p) = h;
+        if constexpr (P::kSplit) *reinterpret_cast<v2 *>(p + lo) = v2{(__bf16)(a - (float)h[0]), (__bf16)(b - (float)h[1])};
+    }
+}
+
+// The A-matrix work of one chunk, shared out over four waves (w = 0..3).  Wave p % 4
+// computes A_kk's diagonal tile p and inverts I + A_pp by forward substitution, giving
+// T's diagonal block p; the off-diagonal A_kk tiles (kept in fp32 for T's off-diagonal
+// blocks) and the lower A_qk tiles are dealt round-robin after them.  Reads the operand
+// staging of the chunk; writes Akk, Tf and the Tm / Aqk tiles of package `pk`.
+template <class P, int K, int V, int C, int BV>
+__device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char *pk, int w, int lane) {
+    using L = Layout<P, K, V, C, BV>;
+    using TA = typename P::TA;
+    using TM = typename P::TM;
+    constexpr int NP = L::NP;
+    const int g = lane >> 4;
+    const TA *Lk = reinterpret_cast<const TA *>(smem + L::oLk);
+    const TA *St = reinterpret_cast<const TA *>(smem + L::oSt);
+    float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
+    float *Tf = reinterpret_cast<float *>(smem + L::oTf);
+    float *Adt = reinterpret_cast<float *>(smem + L::oAdt);
+    TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
+    TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
+    // right operand of tile (p, qt)
+    auto right_of = [&](int p, int qt) -> const TA * {
+        if (qt == p) return St + L::sRd + qt * 16 * L::LKS;
+        if (qt == p - 1) return St + L::sRo + qt * 16 * L::LKS;
+        int xi = 0;
+        for (int pp = 2; pp < p; ++pp) xi += pp - 1;
+        return St + L::sX + (xi + qt) * 16 * L::LKS;
+    };
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        if ((p & 3) != w) continue;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, p), L::LKS, 0, lane);
+        {
+            // column j of the diagonal block as a row: Adt[p][j][i] = A[i][j], strictly lower
+            const int i0 = 4 * g, j = lane & 15;
+            float4 t4;
+            t4.x = (j < i0) ? acc[0] : 0.f;
+            t4.y = (j < i0 + 1) ? acc[1] : 0.f;
+            t4.z = (j < i0 + 2) ? acc[2] : 0.f;
+            t4.w = (j < i0 + 3) ? acc[3] : 0.f;
+            *reinterpret_cast<float4 *>(Adt + (p * 16 + j) * 20 + 4 * g) = t4;
+        }
+        lds_fence();
+        // T_pp = (I + A_pp)^-1, one column per lane, column-oriented: once x_j is final it
+        // is folded into every later row at once, so the dependent chain is one
+        // multiply-add per row
+        if (lane < 16) {
+            const int cc = lane;
+            const float *At = Adt + p * 16 * 20;  // At[j][i] = A[i][j]
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
+            float4 col[3][4];  // columns j, j+1 and j+2 in flight at once
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) col[d][q4] = *reinterpret_cast<const float4 *>(At + d * 20 + 4 * q4);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j + 2 < 16) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        col[(j + 2) % 3][q4] = *reinterpret_cast<const float4 *>(At + (j + 2) * 20 + 4 * q4);
+                }
+                const float xj = x[j];
+                float cv[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    cv[4 * q4] = col[j % 3][q4].x; cv[4 * q4 + 1] = col[j % 3][q4].y;
+                    cv[4 * q4 + 2] = col[j % 3][q4].z; cv[4 * q4 + 3] = col[j % 3][q4].w;
+                }
+#pragma unroll
+                for (int i = j + 1; i < 16; ++i) x[i] -= cv[i] * xj;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                Tf[(p * 16 + i) * L::LCF + p * 16 + cc] = x[i];
+                Tm[(p * 16 + i) * L::LCM + p * 16 + cc] = from_f32<TM>(x[i]);
+            }
+        }
+    }
+    constexpr int NOFF = NP * (NP - 1) / 2;
+    int t = 0;
+#pragma unroll
+    for (int p = 1; p < NP; ++p)
+#pragma unroll
+        for (int qt = 0; qt < p; ++qt, ++t) {
+            if (((t + NP) & 3) != w) continue;
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKS, 0, lane);
+            const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Akk[(i0 + e) * L::LCF + j] = acc[e];
+        }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int qt = 0; qt <= p; ++qt) {
+            const int tq = NOFF + p * (p + 1) / 2 + qt;
+            if (((tq + NP) & 3) != w) continue;
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_stage<P, P::kSplit, K>(acc, St + L::sLq + p * 16 * L::LKS, L::LKS, right_of(p, qt), L::LKS, L::NST, lane);
+            const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Aqk[(i0 + e) * L::LCM + j] = from_f32<TM>((j <= i0 + e) ? acc[e] : 0.f);
+        }
 }
 
 template <class P, int K, int V, int C, int BV>
@@ -351,7 +439,40 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int mj = 0; mj < L::MJ; ++mj) Sh[mj].set(S[mj]);
 
+        float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
+        float *Tf = reinterpret_cast<float *>(smem + L::oTf);
         for (int it = 0; it <= nchunks; ++it) {
+            if (NP > 1 && wave == 0 && it >= 1) {
+                // T's off-diagonal blocks of the chunk about to be consumed, one block
+                // distance at a time on fp32 matrix cores:
+                //   M = sum_{r=q}^{p-1} A_pr T_rq,   T_pq = -T_pp M
+                TM *Tm = reinterpret_cast<TM *>(pkg((it - 1) & 1) + L::pTm);
+                for (int d = 1; d < NP; ++d) {
+                    for (int qb = 0; qb + d < NP; ++qb) {
+                        const int p = qb + d;
+                        f4 m = {0.f, 0.f, 0.f, 0.f};
+                        for (int r = qb; r < p; ++r)
+#pragma unroll
+                            for (int s4 = 0; s4 < 4; ++s4)
+                                m = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    Akk[(p * 16 + (lane & 15)) * L::LCF + r * 16 + 4 * s4 + g],
+                                    Tf[(r * 16 + 4 * s4 + g) * L::LCF + qb * 16 + (lane & 15)], m, 0, 0, 0);
+                        // M's accumulator layout is the B operand with k = 4g + s4
+                        f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4)
+                            t = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                Tf[(p * 16 + (lane & 15)) * L::LCF + p * 16 + 4 * g + s4], m[s4], t, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = p * 16 + 4 * g + e, j = qb * 16 + (lane & 15);
+                            Tf[i * L::LCF + j] = -t[e];
+                            Tm[i * L::LCM + j] = from_f32<TM>(-t[e]);
+                        }
+                    }
+                    lds_fence();
+                }
+            }
             lds_barrier();  // B1: prep waves have produced their tile products
             f4 Vt[L::MJ][NP];
             BFrag<TM, NP> Vh[L::MJ];
@@ -426,6 +547,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 }
             }
             lds_barrier();  // B2: prep waves have written the A-matrix operands
+            if (it < nchunks) a_matrix_work<P, K, V, C, BV>(smem, pkg(it & 1), wave, lane);
             lds_barrier();  // B3: the next package is complete
         }
         if (a.final_state) {
@@ -448,13 +570,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     const int tp = tid - NSW * 64;  // 0 .. NPT-1
     const int pw = wave - NSW;      // prep wave 0..3
     TA *Lk = reinterpret_cast<TA *>(smem + L::oLk);         // [C][LKA]
-    float *Lq = reinterpret_cast<float *>(smem + L::oLq);   // [C][LKF]
-    float *Rd = reinterpret_cast<float *>(smem + L::oRd);   // [C][LKF]
-    float *Ro = reinterpret_cast<float *>(smem + L::oRo);   // [C-16][LKF]
-    float *Xv = reinterpret_cast<float *>(smem + L::oX);    // [NX][16][LKF]
-    float *Akk = reinterpret_cast<float *>(smem + L::oAkk); // [C][LCF]
-    float *Tf = reinterpret_cast<float *>(smem + L::oTf);   // [C][LCF]
-    float *Adt = reinterpret_cast<float *>(smem + L::oAdt); // [NP][16][20]: A_kk diagonal blocks, transposed
+    TA *St = reinterpret_cast<TA *>(smem + L::oSt);         // Lq, Rd, Ro, X (+ low parts)
     float *TPv = reinterpret_cast<float *>(smem + L::oTP);  // [NP][K] tile decay products
     float *Btv = reinterpret_cast<float *>(smem + L::oBt);  // [C] beta of the chunk
 
@@ -540,14 +656,6 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
             hi = __builtin_bit_cast(float, x & 0xffff0000u);
         }
     };
-    // right operand of A-matrix tile (p, qt), fp32 staging
-    auto right_of = [&](int p, int qt) -> const float * {
-        if (qt == p) return Rd + qt * 16 * L::LKF;
-        if (qt == p - 1) return Ro + qt * 16 * L::LKF;
-        int xi = 0;
-        for (int pp = 2; pp < p; ++pp) xi += pp - 1;
-        return Xv + (size_t)(xi + qt) * 16 * L::LKF;
-    };
     if (nchunks > 0) load_raw(0);
 
     // per combo: decay factor entering this half from the other one (prefix: product of
@@ -589,13 +697,14 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
             if (tp < C) Btv[tp] = tp < n_it ? rbeta : 0.f;
         }
         lds_barrier();  // B1
-        // ---- phase 1b: operands of chunk `it` -------------------------------------------
+        // ---- phase 1b: A-matrix operand staging of chunk `it` ---------------------------
+        // The package operands are computed here too but kept in registers and stored in
+        // phase 2, after the prefetch has gone out.
+        float2 kq[CPT][8], kk[CPT][8], kr[CPT][8];  // q gamma/R, beta k gamma/R, k E/gamma per row
+        float2 keR[CPT], keCE[CPT];                 // R_p and E_C / E_p of the combo's tile
+        float2 bvv[NVE];                            // beta v pairs of this thread's value items
         if (work) {
             unsigned char *pk = pkg(it & 1);
-            TM *Qt = reinterpret_cast<TM *>(pk + L::pQt);
-            TM *Bw = reinterpret_cast<TM *>(pk + L::pBw);
-            TM *Kt = reinterpret_cast<TM *>(pk + L::pKt);
-            TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
             float *eGC = reinterpret_cast<float *>(pk + L::pGC);
 #pragma unroll
             for (int u = 0; u < CPT; ++u) {
@@ -643,7 +752,8 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     }
                 }
                 float2 pre = pin[u];  // gamma_i / R_p
-                float2 kk_prev = {0.f, 0.f};  // k E_p / gamma of the previous row (token pairs of Kt)
+                keR[u] = eR;
+                keCE[u] = eCE;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int r = 16 * p + 8 * hf + i;
@@ -659,9 +769,9 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     const float2 ro = {k0 * suf[i].x, k1 * suf[i].y};  // k E_p / gamma <= |k|
                     const float2 rd = {ro.x * rT.x, ro.y * rT.y};        // k R_p / gamma <= e^80 |k|
                     st2<TA>(Lk + r * L::LKA + c0, lk.x, lk.y);
-                    *reinterpret_cast<float2 *>(Lq + r * L::LKF + c0) = lq;
-                    *reinterpret_cast<float2 *>(Rd + r * L::LKF + c0) = rd;
-                    if (p < NP - 1) *reinterpret_cast<float2 *>(Ro + r * L::LKF + c0) = ro;
+                    st2_stage<P>(St + L::sLq + r * L::LKS + c0, L::NST, lq.x, lq.y);
+                    st2_stage<P>(St + L::sRd + r * L::LKS + c0, L::NST, rd.x, rd.y);
+                    if (p < NP - 1) st2_stage<P>(St + L::sRo + r * L::LKS + c0, L::NST, ro.x, ro.y);
                     if constexpr (L::NX > 0) {
                         int xi = 0;
 #pragma unroll
@@ -669,18 +779,49 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                             for (int qq = 0; qq + 2 <= pp; ++qq, ++xi)
                                 if (qq == p)
-                                    *reinterpret_cast<float2 *>(Xv + (size_t)xi * 16 * L::LKF + (8 * hf + i) * L::LKF + c0) =
-                                        float2{ro.x * xf[pp].x, ro.y * xf[pp].y};
+                                    st2_stage<P>(St + L::sX + (xi * 16 + 8 * hf + i) * L::LKS + c0, L::NST,
+                                                 ro.x * xf[pp].x, ro.y * xf[pp].y);
                     }
-                    st2<TM>(Qt + r * L::LKM + c0, lq.x * eR.x, lq.y * eR.y);
-                    st2<TM>(Bw + r * L::LKM + c0, -lk.x * eR.x, -lk.y * eR.y);
-                    const float2 kt = {ro.x * eCE.x, ro.y * eCE.y};
+                    kq[u][i] = lq;
+                    kk[u][i] = lk;
+                    kr[u][i] = ro;
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < NVE; ++w) {
+                const int e = tp + NPT * w;
+                if (e < BV * C / 2) {
+                    const int r = 2 * (e / BV);
+                    bvv[w] = float2{raw_f32(rv[w][0]) * Btv[r], raw_f32(rv[w][1]) * Btv[r + 1]};
+                }
+            }
+        }
+        lds_barrier();  // B2
+        // ---- phase 2: the state waves compute the A-matrix tiles; the prep waves send the
+        // prefetch of the next chunk, then store the package operands of this one
+        if (work) {
+            if (it + 1 < nchunks) load_raw(it + 1);  // consumed next iteration
+            unsigned char *pk = pkg(it & 1);
+            TM *Qt = reinterpret_cast<TM *>(pk + L::pQt);
+            TM *Bw = reinterpret_cast<TM *>(pk + L::pBw);
+            TM *Kt = reinterpret_cast<TM *>(pk + L::pKt);
+            TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u);
+                if (cm >= NCOMBO) continue;
+                const int c0 = 2 * (cm % NCP), p = cm / NCP;
+                const float2 eR = keR[u], eCE = keCE[u];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 16 * p + 8 * hf + i;
+                    st2<TM>(Qt + r * L::LKM + c0, kq[u][i].x * eR.x, kq[u][i].y * eR.y);
+                    st2<TM>(Bw + r * L::LKM + c0, -kk[u][i].x * eR.x, -kk[u][i].y * eR.y);
                     if (i & 1) {
                         // two consecutive tokens per channel row of Kt
-                        st2<TM>(Kt + c0 * L::LCM + r - 1, kk_prev.x, kt.x);
-                        st2<TM>(Kt + (c0 + 1) * L::LCM + r - 1, kk_prev.y, kt.y);
+                        st2<TM>(Kt + c0 * L::LCM + r - 1, kr[u][i - 1].x * eCE.x, kr[u][i].x * eCE.x);
+                        st2<TM>(Kt + (c0 + 1) * L::LCM + r - 1, kr[u][i - 1].y * eCE.y, kr[u][i].y * eCE.y);
                     }
-                    kk_prev = kt;
                 }
             }
 #pragma unroll
@@ -688,122 +829,8 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 const int e = tp + NPT * w;
                 if (e < BV * C / 2) {
                     const int j = e % BV, r = 2 * (e / BV);
-                    st2<TM>(bV + j * L::LCM + r, raw_f32(rv[w][0]) * Btv[r], raw_f32(rv[w][1]) * Btv[r + 1]);
+                    st2<TM>(bV + j * L::LCM + r, bvv[w].x, bvv[w].y);
                 }
-            }
-            if (pw == 0 && it + 1 < nchunks) load_raw(it + 1);  // prefetch; consumed next iteration
-        }
-        lds_barrier();  // B2
-        // ---- phase 2: A_kk and T (prep wave 0), A_qk (prep waves 1..3) -----------------
-        if (work) {
-            unsigned char *pk = pkg(it & 1);
-            TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
-            TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
-            if (pw == 0) {
-                // A_kk (strictly lower) in fp32
-#pragma unroll
-                for (int p = 0; p < NP; ++p)
-#pragma unroll
-                    for (int qt = 0; qt <= p; ++qt) {
-                        f4 acc = {0.f, 0.f, 0.f, 0.f};
-                        mma_rowsrc<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKF, lane);
-                        const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Akk[(i0 + e) * L::LCF + j] = (j < i0 + e) ? acc[e] : 0.f;
-                        if (qt == p) {
-                            // column j of the diagonal block as a row: Adt[p][j][i] = A[i][j]
-                            float4 t4;
-                            t4.x = (j < i0) ? acc[0] : 0.f;
-                            t4.y = (j < i0 + 1) ? acc[1] : 0.f;
-                            t4.z = (j < i0 + 2) ? acc[2] : 0.f;
-                            t4.w = (j < i0 + 3) ? acc[3] : 0.f;
-                            *reinterpret_cast<float4 *>(Adt + (p * 16 + (lane & 15)) * 20 + 4 * g) = t4;
-                        }
-                    }
-                lds_fence();
-                // diagonal blocks of T = (I + A_kk)^-1 by forward substitution, one column
-                // per lane (lane = 16 * block + column), column-oriented: once x_j is final
-                // it is folded into every later row at once, so the dependent chain is one
-                // multiply-add per row
-                if (lane < 16 * NP) {
-                    const int p = lane >> 4, cc = lane & 15;
-                    const float *At = Adt + p * 16 * 20;  // At[j][i] = A[i][j]
-                    float acc[16];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[i] = (i == cc) ? 1.f : 0.f;
-                    // columns j, j+1 and j+2 of the block in flight at once
-                    float4 col[3][4];
-#pragma unroll
-                    for (int d = 0; d < 2; ++d)
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) col[d][q4] = *reinterpret_cast<const float4 *>(At + d * 20 + 4 * q4);
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        if (j + 2 < 16) {
-#pragma unroll
-                            for (int q4 = 0; q4 < 4; ++q4)
-                                col[(j + 2) % 3][q4] = *reinterpret_cast<const float4 *>(At + (j + 2) * 20 + 4 * q4);
-                        }
-                        const float xj = acc[j];
-                        float cv[16];
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            cv[4 * q4] = col[j % 3][q4].x; cv[4 * q4 + 1] = col[j % 3][q4].y;
-                            cv[4 * q4 + 2] = col[j % 3][q4].z; cv[4 * q4 + 3] = col[j % 3][q4].w;
-                        }
-#pragma unroll
-                        for (int i = j + 1; i < 16; ++i) acc[i] -= cv[i] * xj;
-                    }
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        Tf[(p * 16 + i) * L::LCF + p * 16 + cc] = acc[i];
-                        Tm[(p * 16 + i) * L::LCM + p * 16 + cc] = from_f32<TM>(acc[i]);
-                    }
-                }
-                lds_fence();
-                // off-diagonal blocks, one block distance at a time, on fp32 matrix cores:
-                //   M = sum_{r=q}^{p-1} A_pr T_rq,   T_pq = -T_pp M
-                for (int d = 1; d < NP; ++d) {
-                    for (int qb = 0; qb + d < NP; ++qb) {
-                        const int p = qb + d;
-                        f4 m = {0.f, 0.f, 0.f, 0.f};
-                        for (int r = qb; r < p; ++r)
-#pragma unroll
-                            for (int s4 = 0; s4 < 4; ++s4)
-                                m = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                    Akk[(p * 16 + (lane & 15)) * L::LCF + r * 16 + 4 * s4 + g],
-                                    Tf[(r * 16 + 4 * s4 + g) * L::LCF + qb * 16 + (lane & 15)], m, 0, 0, 0);
-                        // M's accumulator layout is the B operand with k = 4g + s4
-                        f4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s4 = 0; s4 < 4; ++s4)
-                            t = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                Tf[(p * 16 + (lane & 15)) * L::LCF + p * 16 + 4 * g + s4], m[s4], t, 0, 0, 0);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int i = p * 16 + 4 * g + e, j = qb * 16 + (lane & 15);
-                            Tf[i * L::LCF + j] = -t[e];
-                            Tm[i * L::LCM + j] = from_f32<TM>(-t[e]);
-                        }
-                    }
-                    lds_fence();
-                }
-            } else {
-                // A_qk, lower tiles only (the upper ones stay zero); this wave's prefetch of
-                // the next chunk goes out first (wave 0's went out at the end of phase 1b)
-                if (it + 1 < nchunks) load_raw(it + 1);
-#pragma unroll
-                for (int p = 0; p < NP; ++p)
-#pragma unroll
-                    for (int qt = 0; qt <= p; ++qt) {
-                        const int task = p * (p + 1) / 2 + qt;
-                        if (task % 3 != pw - 1) continue;
-                        f4 acc = {0.f, 0.f, 0.f, 0.f};
-                        mma_rowsrc<P, P::kSplit, K>(acc, Lq + p * 16 * L::LKF, L::LKF, right_of(p, qt), L::LKF, lane);
-                        const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Aqk[(i0 + e) * L::LCM + j] = from_f32<TM>((j <= i0 + e) ? acc[e] : 0.f);
-                    }
             }
         }
         lds_barrier();  // B3
