@@ -90,8 +90,7 @@ struct Layout {
     static constexpr int NST = sX + NX * 16 * LKS;
     static constexpr size_t oAkk = oSt + al16((size_t)NST * sizeof(TA) * (P::kSplit ? 2 : 1));
     static constexpr size_t oTf = oAkk + al16((size_t)C * LCF * 4);
-    static constexpr size_t oAdt = oTf + al16((size_t)C * LCF * 4);   // [NP][16][20] diag blocks, transposed
-    static constexpr size_t oTP = oAdt + al16((size_t)NP * 16 * 20 * 4);
+    static constexpr size_t oTP = oTf + al16((size_t)C * LCF * 4);
     static constexpr size_t oBt = oTP + al16((size_t)NP * K * 4);
     static constexpr size_t oPkg = oBt + al16((size_t)C * 4);
     // package (two copies)
@@ -269,9 +268,79 @@ __device__ __forceinline__ void st2_stage(typename P::TA *p, int lo, float a, fl
     }
 }
 
+// acc = X Y for 16x16 X, Y whose 16-wide reduction is held in registers: lane (g, r) gives
+// xr[s] = X[r][4g+s] and lane (g, n) gives yc[s] = Y[4g+s][n] (k = 4g + s on both sides;
+// the result is in the accumulator layout).  T is the operand type: float runs four fp32
+// steps, _Float16 one 16x16x32 step with the upper half of each operand zero.
+template <typename T>
+__device__ __forceinline__ f4 mma16_reg(f4 xr, f4 yc);
+template <>
+__device__ __forceinline__ f4 mma16_reg<float>(f4 xr, f4 yc) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[s], yc[s], acc, 0, 0, 0);
+    return acc;
+}
+template <>
+__device__ __forceinline__ f4 mma16_reg<_Float16>(f4 xr, f4 yc) {
+    const f16x8 a = {(_Float16)xr[0], (_Float16)xr[1], (_Float16)xr[2], (_Float16)xr[3], 0, 0, 0, 0};
+    const f16x8 b = {(_Float16)yc[0], (_Float16)yc[1], (_Float16)yc[2], (_Float16)yc[3], 0, 0, 0, 0};
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, z, 0, 0, 0);
+}
+
+// Value of `v` in lane J of this lane's group of four.
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), J * 0x55, 0xf, 0xf, false));
+}
+
+// (I + A)^-1 for a 16x16 strictly lower triangular A given as an accumulator tile (lane
+// (g, n) holds A[4g+e][n]; entries on and above the diagonal are ignored).  Returns the
+// inverse in the same layout.  Blocked: with Ad the 4x4 diagonal blocks of A and Ao the
+// rest, I + A = (I + Ad)(I + N), N = D Ao, D = (I + Ad)^-1; N is strictly lower at
+// 4x4-block level, so N^4 = 0 and (I + A)^-1 = (I - N + N^2 - N^3) D.  The four 4x4
+// inverses come from forward and backward substitution inside groups of four lanes; the
+// rest is six 16x16 products on the matrix cores in operand type T.
+template <typename T>
+__device__ __forceinline__ f4 unit_lower_inverse16(const f4 a, int lane) {
+    const int g = lane >> 4, n = lane & 15, c = n & 3;
+    const bool diag = (n >> 2) == g;  // lanes holding column c of diagonal block g
+    // entries a_ej = A[4g+e][4g+j] (e > j) of the diagonal block, from quad lane j
+    const float a10 = quad_bcast<0>(a[1]), a20 = quad_bcast<0>(a[2]), a30 = quad_bcast<0>(a[3]);
+    const float a21 = quad_bcast<1>(a[2]), a31 = quad_bcast<1>(a[3]);
+    const float a32 = quad_bcast<2>(a[3]);
+    // column c of the block inverse: x = e_c, then eliminate column by column
+    float x0 = c == 0 ? 1.f : 0.f, x1 = c == 1 ? 1.f : 0.f, x2 = c == 2 ? 1.f : 0.f, x3 = c == 3 ? 1.f : 0.f;
+    x1 -= a10 * x0;
+    x2 -= a20 * x0 + a21 * x1;
+    x3 -= a30 * x0 + a31 * x1 + a32 * x2;
+    // row c of the block inverse: y = e_c^T, then eliminate from the right
+    float y0 = c == 0 ? 1.f : 0.f, y1 = c == 1 ? 1.f : 0.f, y2 = c == 2 ? 1.f : 0.f, y3 = c == 3 ? 1.f : 0.f;
+    y2 -= y3 * a32;
+    y1 -= y2 * a21 + y3 * a31;
+    y0 -= y1 * a10 + y2 * a20 + y3 * a30;
+    // "c" = accumulator layout of a matrix, "r" = accumulator layout of its transpose
+    // (lane (g, n) holds M[n][4g+e]), which is its row-operand form
+    const f4 Dc = diag ? f4{x0, x1, x2, x3} : f4{0.f, 0.f, 0.f, 0.f};
+    const f4 Dr = diag ? f4{y0, y1, y2, y3} : f4{0.f, 0.f, 0.f, 0.f};
+    f4 Aoc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Aoc[e] = (n >> 2) < g ? a[e] : 0.f;
+    // P = X Y: Pc = mma(Xr, Yc) and Pr = mma(Yc, Xr)
+    const f4 Nc = mma16_reg<T>(Dr, Aoc);
+    const f4 Nr = mma16_reg<T>(Aoc, Dr);
+    const f4 N2c = mma16_reg<T>(Nr, Nc);
+    const f4 N2r = mma16_reg<T>(Nc, Nr);
+    const f4 N3r = mma16_reg<T>(N2c, Nr);
+    f4 Mr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Mr[e] = (4 * g + e == n ? 1.f : 0.f) - Nr[e] + N2r[e] - N3r[e];
+    return mma16_reg<T>(Mr, Dc);
+}
+
 // The A-matrix work of one chunk, shared out over four waves (w = 0..3).  Wave p % 4
-// computes A_kk's diagonal tile p and inverts I + A_pp by forward substitution, giving
-// T's diagonal block p; the off-diagonal A_kk tiles (kept in fp32 for T's off-diagonal
+// computes A_kk's diagonal tile p and inverts I + A_pp, giving T's diagonal block p; the off-diagonal A_kk tiles (kept in fp32 for T's off-diagonal
 // blocks) and the lower A_qk tiles are dealt round-robin after them.  Reads the operand
 // staging of the chunk; writes Akk, Tf and the Tm / Aqk tiles of package `pk`.
 template <class P, int K, int V, int C, int BV>
@@ -285,7 +354,6 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
     const TA *St = reinterpret_cast<const TA *>(smem + L::oSt);
     float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
     float *Tf = reinterpret_cast<float *>(smem + L::oTf);
-    float *Adt = reinterpret_cast<float *>(smem + L::oAdt);
     TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
     TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
     // right operand of tile (p, qt)
@@ -301,53 +369,14 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
         if ((p & 3) != w) continue;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
         mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, p), L::LKS, 0, lane);
-        {
-            // column j of the diagonal block as a row: Adt[p][j][i] = A[i][j], strictly lower
-            const int i0 = 4 * g, j = lane & 15;
-            float4 t4;
-            t4.x = (j < i0) ? acc[0] : 0.f;
-            t4.y = (j < i0 + 1) ? acc[1] : 0.f;
-            t4.z = (j < i0 + 2) ? acc[2] : 0.f;
-            t4.w = (j < i0 + 3) ? acc[3] : 0.f;
-            *reinterpret_cast<float4 *>(Adt + (p * 16 + j) * 20 + 4 * g) = t4;
-        }
-        lds_fence();
-        // T_pp = (I + A_pp)^-1, one column per lane, column-oriented: once x_j is final it
-        // is folded into every later row at once, so the dependent chain is one
-        // multiply-add per row
-        if (lane < 16) {
-            const int cc = lane;
-            const float *At = Adt + p * 16 * 20;  // At[j][i] = A[i][j]
-            float x[16];
+        const f4 t = unit_lower_inverse16<TM>(acc, lane);
+        const int j = lane & 15;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
-            float4 col[3][4];  // columns j, j+1 and j+2 in flight at once
-#pragma unroll
-            for (int d = 0; d < 2; ++d)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) col[d][q4] = *reinterpret_cast<const float4 *>(At + d * 20 + 4 * q4);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                if (j + 2 < 16) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        col[(j + 2) % 3][q4] = *reinterpret_cast<const float4 *>(At + (j + 2) * 20 + 4 * q4);
-                }
-                const float xj = x[j];
-                float cv[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    cv[4 * q4] = col[j % 3][q4].x; cv[4 * q4 + 1] = col[j % 3][q4].y;
-                    cv[4 * q4 + 2] = col[j % 3][q4].z; cv[4 * q4 + 3] = col[j % 3][q4].w;
-                }
-#pragma unroll
-                for (int i = j + 1; i < 16; ++i) x[i] -= cv[i] * xj;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                Tf[(p * 16 + i) * L::LCF + p * 16 + cc] = x[i];
-                Tm[(p * 16 + i) * L::LCM + p * 16 + cc] = from_f32<TM>(x[i]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g + e;
+            const float x = (j <= i) ? t[e] : 0.f;
+            Tf[(p * 16 + i) * L::LCF + p * 16 + j] = x;
+            Tm[(p * 16 + i) * L::LCM + p * 16 + j] = from_f32<TM>(x);
         }
     }
     constexpr int NOFF = NP * (NP - 1) / 2;
