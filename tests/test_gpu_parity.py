@@ -128,6 +128,23 @@ def test_decay_regimes_bf16(regime):
     assert_close(f, ef, False, "final state")
 
 
+@pytest.mark.parametrize("dtype,K,C", [(torch.float32, 64, 32), (torch.float32, 128, 16),
+                                     (torch.bfloat16, 128, 32), (torch.bfloat16, 32, 64)])
+def test_repeated_key_full_overwrite(dtype, K, C):
+    """Every token writes the same key with beta = 1 and no decay.  The strictly lower part
+    of each chunk's key-key matrix is then all ones: the in-chunk inverse sees its largest
+    intermediate terms."""
+    _case("repeated key K=%d C=%d %s" % (K, C, dtype))
+    inp = synth.make_prefill(1, 150, 2, K, 64, dtype=dtype, seed=57, z_mean=-200.0, state_std=0.1)
+    inp.k = inp.k[:, :1].expand_as(inp.k).contiguous()
+    inp.beta = torch.ones_like(inp.beta)
+    o, f = gpu_prefill(inp, chunk_size=C)
+    eo, ef = oracle_prefill(inp)
+    fp32 = dtype == torch.float32
+    assert_close(o, eo, fp32, "out")
+    assert_close(f, ef, fp32, "final state")
+
+
 def test_chunk_size_invariance_bf16():
     _case("chunk size 16 vs 32, bf16 K=V=128")
     inp = synth.make_prefill(1, 200, 2, 128, 128, seed=41, qk="silu", v_kind="silu", z_std=1.5)
