@@ -73,7 +73,7 @@ def _counter_means(path, counter):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gate="fused"):
     """HBM bytes per launch of the chunk and step kernels: FETCH_SIZE and WRITE_SIZE (KiB)
     each scaled by what the same counter reads for a plain copy of known size (a copy of
     N bytes reads N and writes N)."""
@@ -89,8 +89,8 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     write = _counter_means(write_csv, "WRITE_SIZE")
     out = {"_calibration": {"copy_kernel": cname[:120], "copy_bytes": COPY_BYTES, "fetch_kib": cf,
                             "write_kib": cw, "bytes_per_fetch_kib": f_scale, "bytes_per_write_kib": w_scale}}
-    for key, pat, src in (("k3_prefill_chunk_fwd", "chunk_fwd_kernel", "kda_chunk.hip"),
-                          ("decode_recurrent_step", "recurrent_step_kernel", "kda_step.hip")):
+    for key, pat, src in (("k3_prefill_chunk_fwd_" + gate, "chunk_fwd_kernel", "kda_chunk_kernel.h"),
+                          ("decode_recurrent_step_" + gate, "recurrent_step_kernel", "kda_step.hip")):
         fk = [v for k, v in fetch.items() if pat in k]
         wk = [v for k, v in write.items() if pat in k]
         if not fk or not wk:
@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=32)
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--gate", choices=("fused", "separate"), default="fused",
+                    help="fused: the kernels take the gate logits; separate: bounded_decay writes a "
+                         "float32 gate that the kernels read")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48)
@@ -121,7 +124,7 @@ def main():
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE results into profiles/traffic.json")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, gate=args.gate)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -157,12 +160,19 @@ def main():
     fin = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    fused = args.gate == "fused"
+
     def step(ev_pair=None):
-        kda.bounded_decay(z, ls, lower_bound=-5.0, out_log=False, out=g)
+        if not fused:
+            kda.bounded_decay(z, ls, lower_bound=-5.0, out_log=False, out=g)
         if ev_pair is not None:
             ev_pair[0].record(stream)
-        kda.chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=args.chunk, gate_is_log=False,
-                      out=out, final_state=fin)
+        if fused:
+            kda.chunk_fwd_fused_gate(q, k, v, z, ls, beta, lower_bound=-5.0, initial_state=None,
+                                     chunk_size=args.chunk, out=out, final_state=fin)
+        else:
+            kda.chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=args.chunk, gate_is_log=False,
+                          out=out, final_state=fin)
         if ev_pair is not None:
             ev_pair[1].record(stream)
 
@@ -184,11 +194,12 @@ def main():
     tokens_per_s = B * T / (wall / args.steps)
 
     th = B * T * H
-    alg_bytes = th * (3 * 2 * K + 4 * K + 4 + 2 * V)       # q,k,v bf16 + gate fp32 + beta + out bf16
+    gate_bytes = 2 * K if fused else 4 * K                  # bf16 logits, or the fp32 gate tensor
+    alg_bytes = th * (3 * 2 * K + gate_bytes + 4 + 2 * V)   # q,k,v bf16 + gate + beta + out bf16
     alg_flops = th * (6 * K * V + 64 * (3 * K + 2 * V))
     achieved_gbs = alg_bytes / (chunk_ms * 1e-3) / 1e9
     achieved_tflops = alg_flops / (chunk_ms * 1e-3) / 1e12
-    traffic = load_traffic("kda_chunk.hip", "k3_prefill_chunk_fwd")
+    traffic = load_traffic("kda_chunk_kernel.h", "k3_prefill_chunk_fwd_" + args.gate)
     log("prefill: %.3f ms/step, chunk kernel %.3f ms, %.1f GB/s, %.1f TFLOP/s" %
         (ms_per_step, chunk_ms, achieved_gbs, achieved_tflops))
 
@@ -207,7 +218,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "k3_prefill_B1_T8192_H96_K128_V128", "global_batch": B, "seq_len": T,
                    "heads": H, "key_dim": K, "value_dim": V, "chunk_size": args.chunk,
-                   "step": "bounded_decay + chunk_fwd", "parallelism": "single GPU"},
+                   "step": "chunk_fwd_fused_gate" if fused else "bounded_decay + chunk_fwd",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel": "chunk_fwd_kernel",
@@ -228,10 +240,15 @@ def main():
         od = torch.empty(Bd, Hd, V, dtype=torch.bfloat16, device=dev)
 
         def dstep(t, ev_pair=None):
-            kda.bounded_decay(dec.z[t], dec.log_scale, out=al)
+            if not fused:
+                kda.bounded_decay(dec.z[t], dec.log_scale, out=al)
             if ev_pair is not None:
                 ev_pair[0].record(stream)
-            kda.recurrent_step(dec.q[t], dec.k[t], dec.v[t], al, dec.beta[t], state, out=od)
+            if fused:
+                kda.recurrent_step_fused_gate(dec.q[t], dec.k[t], dec.v[t], dec.z[t], dec.log_scale, dec.beta[t],
+                                              state, out=od)
+            else:
+                kda.recurrent_step(dec.q[t], dec.k[t], dec.v[t], al, dec.beta[t], state, out=od)
             if ev_pair is not None:
                 ev_pair[1].record(stream)
 
@@ -248,17 +265,18 @@ def main():
         step_ms = sorted(a.elapsed_time(b) for a, b in devs)
         step_med = step_ms[len(step_ms) // 2]
         step_avg = sum(step_ms) / len(step_ms)
-        pair_bytes = 2 * K * V * 4 + 2 * 2 * K + 2 * V + 4 * K + 4 + 2 * V
+        # state read + write, q, k, v bf16, gate (bf16 logits or fp32), beta, out bf16
+        pair_bytes = 2 * K * V * 4 + 2 * 2 * K + 2 * V + gate_bytes + 4 + 2 * V
         d_bytes = Bd * Hd * pair_bytes
         d_gbs = d_bytes / (step_avg * 1e-3) / 1e9
-        dtraffic = load_traffic("kda_step.hip", "decode_recurrent_step")
+        dtraffic = load_traffic("kda_step.hip", "decode_recurrent_step_" + args.gate)
         log("decode: %.3f ms/step wall, step kernel avg %.1f us (median %.1f), %.0f GB/s" %
             (dwall * 1e3 / nd, step_avg * 1e3, step_med * 1e3, d_gbs))
         result["decode"] = {
             "workload": "decode_B64_H96_K128_V128_steps%d" % nd,
             "tokens_per_s": Bd * nd / dwall,
             "ms_per_step": dwall * 1e3 / nd,
-            "step": "bounded_decay + recurrent_step",
+            "step": "recurrent_step_fused_gate" if fused else "bounded_decay + recurrent_step",
             "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": d_gbs / HBM_PEAK_GBS, "traffic": dtraffic, "kernel": "recurrent_step_kernel",
                          "launch_us_avg": step_avg * 1e3, "launch_us_median": step_med * 1e3,

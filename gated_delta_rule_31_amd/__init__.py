@@ -14,6 +14,9 @@ Entry points (same names as the C ABI, minus the ``kda_`` prefix where noted):
   initial / final state and packed sequences (``cu_seqlens``).
 * ``recurrent_step(q, k, v, gate, beta, state, ...)`` -- one decode token, state
   updated in place.
+* ``chunk_fwd_fused_gate`` / ``recurrent_step_fused_gate`` -- the same two calls with
+  the gate applied inside the kernel from its logits (``log_scale``, ``bias``,
+  ``lower_bound``), so no float32 gate tensor is made.
 * ``recurrent_kda(q, k, v, alpha, beta, initial_state=None)`` -- the functional
   (output, final_state) form of the pages' operator contract, on ``chunk_fwd``.
 """
@@ -26,6 +29,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["bounded_decay", "chunk_fwd", "recurrent_step", "recurrent_kda", "KDAError", "chunk_fwd_supported",
+           "chunk_fwd_fused_gate", "recurrent_step_fused_gate",
            "library_path", "abi_version", "GATE_ALPHA", "GATE_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +71,12 @@ def _load():
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, f32, vp,
                                        i32, vp]
     lib.kda_recurrent_step.restype = i32
+    lib.kda_chunk_fwd_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, i32, i32, i64,
+                                             i32, i32, i32, i32, f32, vp, i32, vp]
+    lib.kda_chunk_fwd_fused_gate.restype = i32
+    lib.kda_recurrent_step_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32,
+                                                  f32, vp, i32, vp]
+    lib.kda_recurrent_step_fused_gate.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
@@ -152,22 +162,10 @@ def bounded_decay(logits: torch.Tensor, log_scale: torch.Tensor, lower_bound: fl
     return out
 
 
-def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
-              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
-              output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
-              chunk_size: int = 32, scale: float = 1.0, gate_is_log: bool = False,
-              out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-              final_state: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunkwise prefill.  q, k [B,T,H,K]; v [B,T,H,V] (one dtype, float32 or
-    bfloat16); gate [B,T,H,K] float32 (alpha, or ln alpha with ``gate_is_log``);
-    beta [B,T,H] float32; initial_state [N,H,K,V] float32 or None; cu_seqlens
-    int32 [N+1] (B == 1) or None.  Returns (out [B,T,H,V], final_state [N,H,K,V]
-    or None).  ``final_state`` may be passed in (it may be ``initial_state``)."""
+def _chunk_common(q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state):
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k and v must share one dtype")
-    gate = _dev(gate, "gate", torch.float32)
     beta = _dev(beta, "beta", torch.float32)
     initial_state = _dev(initial_state, "initial_state", torch.float32)
     cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32)
@@ -175,9 +173,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Ten
         raise ValueError("q, k, v must be [B, T, H, D]")
     B, T, H, K = q.shape
     V = v.shape[-1]
-    if k.shape != q.shape or gate.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
-        raise ValueError("inconsistent shapes: q %s k %s v %s gate %s beta %s" % (
-            tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(gate.shape), tuple(beta.shape)))
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes: q %s k %s v %s beta %s" % (
+            tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(beta.shape)))
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     if initial_state is not None and initial_state.shape != (N, H, K, V):
         raise ValueError("initial_state must be [%d, %d, %d, %d]" % (N, H, K, V))
@@ -191,6 +189,28 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Ten
     if final_state is not None and (final_state.shape != (N, H, K, V) or final_state.dtype != torch.float32
                                     or not final_state.is_contiguous()):
         raise ValueError("final_state must be contiguous float32 [N,H,K,V]")
+    return q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
+              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+              chunk_size: int = 32, scale: float = 1.0, gate_is_log: bool = False,
+              out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise prefill.  q, k [B,T,H,K]; v [B,T,H,V] (one dtype, float32 or
+    bfloat16); gate [B,T,H,K] float32 (alpha, or ln alpha with ``gate_is_log``);
+    beta [B,T,H] float32; initial_state [N,H,K,V] float32 or None; cu_seqlens
+    int32 [N+1] (B == 1) or None.  Returns (out [B,T,H,V], final_state [N,H,K,V]
+    or None).  ``final_state`` may be passed in (it may be ``initial_state``)."""
+    q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
+        q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state)
+    gate = _dev(gate, "gate", torch.float32)
+    if gate.shape != q.shape:
+        raise ValueError("gate must be shaped like q")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
     with torch.cuda.device(q.device):
         st = _load().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(gate),
                                    GATE_LOG if gate_is_log else GATE_ALPHA, _ptr(beta),
@@ -201,16 +221,47 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Ten
     return out, final_state
 
 
-def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
-                   beta: torch.Tensor, state: torch.Tensor, scale: float = 1.0,
-                   gate_is_log: bool = False, out_dtype: Optional[torch.dtype] = None,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One decode token.  q, k [B,H,K]; v [B,H,V]; gate [B,H,K] float32; beta [B,H]
-    float32; state [B,H,K,V] float32 contiguous, updated in place.  Returns out [B,H,V]."""
+def _gate_params(logits, log_scale, bias, like: torch.Tensor):
+    logits = _dev(logits, "logits", like.dtype)
+    log_scale = _dev(log_scale, "log_scale", torch.float32)
+    bias = _dev(bias, "bias", torch.float32)
+    H, K = like.shape[-2], like.shape[-1]
+    if logits.shape != like.shape:
+        raise ValueError("logits must be shaped like q")
+    if log_scale.numel() != H or (bias is not None and bias.numel() != H * K):
+        raise ValueError("log_scale must be [H] and bias [H, K]")
+    return logits, log_scale, bias
+
+
+def chunk_fwd_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: torch.Tensor,
+                         log_scale: torch.Tensor, beta: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                         lower_bound: float = -5.0, initial_state: Optional[torch.Tensor] = None,
+                         output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+                         chunk_size: int = 32, scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
+                         out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd`` with alpha = exp(lower_bound * sigmoid(e^log_scale (logits + bias)))
+    computed inside the kernel.  logits [B,T,H,K] in the dtype of q; log_scale [H] and
+    bias [H,K] float32; lower_bound in [-5, 0)."""
+    q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
+        q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state)
+    logits, log_scale, bias = _gate_params(logits, log_scale, bias, q)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    with torch.cuda.device(q.device):
+        st = _load().kda_chunk_fwd_fused_gate(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(logits),
+                                              _ptr(log_scale), _ptr(bias), float(lower_bound), _ptr(beta),
+                                              _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, B,
+                                              T, H, K, V, int(chunk_size), float(scale), _ptr(out),
+                                              _dtype_code(od), _stream(q))
+    _check("kda_chunk_fwd_fused_gate", st)
+    return out, final_state
+
+
+def _step_common(q, k, v, beta, state, out_dtype, out):
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k and v must share one dtype")
-    gate = _dev(gate, "gate", torch.float32)
     beta = _dev(beta, "beta", torch.float32)
     if not isinstance(state, torch.Tensor) or state.device.type != "cuda" or state.dtype != torch.float32 \
             or not state.is_contiguous():
@@ -219,17 +270,53 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torc
         raise ValueError("q must be [B, H, K]")
     B, H, K = q.shape
     V = v.shape[-1]
-    if k.shape != q.shape or gate.shape != q.shape or v.shape != (B, H, V) or beta.shape != (B, H) \
-            or state.shape != (B, H, K, V):
+    if k.shape != q.shape or v.shape != (B, H, V) or beta.shape != (B, H) or state.shape != (B, H, K, V):
         raise ValueError("inconsistent shapes")
     od = out_dtype or v.dtype
     if out is None:
         out = torch.empty((B, H, V), dtype=od, device=q.device)
+    elif out.shape != (B, H, V) or out.dtype != od or not out.is_contiguous():
+        raise ValueError("out must be contiguous [B,H,V] of the output dtype")
+    return q, k, v, beta, od, out
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
+                   beta: torch.Tensor, state: torch.Tensor, scale: float = 1.0,
+                   gate_is_log: bool = False, out_dtype: Optional[torch.dtype] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode token.  q, k [B,H,K]; v [B,H,V]; gate [B,H,K] float32; beta [B,H]
+    float32; state [B,H,K,V] float32 contiguous, updated in place.  Returns out [B,H,V]."""
+    q, k, v, beta, od, out = _step_common(q, k, v, beta, state, out_dtype, out)
+    gate = _dev(gate, "gate", torch.float32)
+    if gate.shape != q.shape:
+        raise ValueError("gate must be shaped like q")
+    B, H, K = q.shape
+    V = v.shape[-1]
     with torch.cuda.device(q.device):
         st = _load().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(gate),
                                         GATE_LOG if gate_is_log else GATE_ALPHA, _ptr(beta), _ptr(state),
                                         B, H, K, V, float(scale), _ptr(out), _dtype_code(od), _stream(q))
     _check("kda_recurrent_step", st)
+    return out
+
+
+def recurrent_step_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: torch.Tensor,
+                              log_scale: torch.Tensor, beta: torch.Tensor, state: torch.Tensor,
+                              bias: Optional[torch.Tensor] = None, lower_bound: float = -5.0,
+                              scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
+                              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``recurrent_step`` with the gate computed inside the kernel from logits [B,H,K]
+    (dtype of q), log_scale [H], bias [H,K] or None and lower_bound < 0."""
+    q, k, v, beta, od, out = _step_common(q, k, v, beta, state, out_dtype, out)
+    logits, log_scale, bias = _gate_params(logits, log_scale, bias, q)
+    B, H, K = q.shape
+    V = v.shape[-1]
+    with torch.cuda.device(q.device):
+        st = _load().kda_recurrent_step_fused_gate(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(logits),
+                                                   _ptr(log_scale), _ptr(bias), float(lower_bound), _ptr(beta),
+                                                   _ptr(state), B, H, K, V, float(scale), _ptr(out),
+                                                   _dtype_code(od), _stream(q))
+    _check("kda_recurrent_step_fused_gate", st)
     return out
 
 

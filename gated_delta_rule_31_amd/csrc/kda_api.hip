@@ -75,14 +75,18 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
     return e == hipSuccess ? KDA_OK : hip_fail(e);
 }
 
-kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,
-                         const float *gate, kda_gate_kind gate_kind, const float *beta,
-                         const float *initial_state, float *final_state,
-                         const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H, int K,
-                         int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
-                         hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the chunk entry points; `gate` says how the retention arrives.
+kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                          const kda::GateIn &gate, const float *beta, const float *initial_state,
+                          float *final_state, const int32_t *cu_seqlens, int num_seqs, int B, int64_t T,
+                          int H, int K, int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
+                          hipStream_t stream) {
     if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
-    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype) || !gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_BAD_DTYPE;
     if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
     if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_BAD_ARGUMENT;
@@ -98,8 +102,10 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
         }
         return KDA_OK;
     }
-    if (!q || !k || !v || !gate || !beta || !out) return KDA_ERR_NULL_POINTER;
-    const void *ins[] = {q, k, v, gate, beta, initial_state, cu_seqlens};
+    const void *gin = gate.mode == kda::GATE_LOGITS ? gate.logits : (const void *)gate.gate;
+    if (!q || !k || !v || !gin || !beta || !out) return KDA_ERR_NULL_POINTER;
+    if (gate.mode == kda::GATE_LOGITS && !gate.log_scale) return KDA_ERR_NULL_POINTER;
+    const void *ins[] = {q, k, v, gin, beta, initial_state, cu_seqlens, gate.log_scale, gate.bias};
     for (const void *p : ins) {
         if (p && (p == out || p == (const void *)final_state)) {
             if (p == (const void *)initial_state && p == (const void *)final_state) continue;
@@ -121,7 +127,6 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
     a.out = out;
     a.T = T;
     a.H = H;
-    a.gate_is_log = gate_kind == KDA_GATE_LOG;
     a.out_bf16 = out_dtype == KDA_BF16;
     a.scale = scale;
     int bv = 0;
@@ -129,18 +134,20 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
     return e == hipSuccess ? KDA_OK : hip_fail(e);
 }
 
-kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_dtype in_dtype,
-                              const float *gate, kda_gate_kind gate_kind, const float *beta,
-                              float *state, int B, int H, int K, int V, float scale, void *out,
-                              kda_dtype out_dtype, hipStream_t stream) {
+kda_status recurrent_step_impl(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                               const kda::GateIn &gate, const float *beta, float *state, int B, int H,
+                               int K, int V, float scale, void *out, kda_dtype out_dtype,
+                               hipStream_t stream) {
     if (B < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
-    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype) || !gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_BAD_DTYPE;
     if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
     if (B == 0) return KDA_OK;
-    if (!q || !k || !v || !gate || !beta || !state || !out) return KDA_ERR_NULL_POINTER;
-    const void *ins[] = {q, k, v, gate, beta};
+    const void *gin = gate.mode == kda::GATE_LOGITS ? gate.logits : (const void *)gate.gate;
+    if (!q || !k || !v || !gin || !beta || !state || !out) return KDA_ERR_NULL_POINTER;
+    if (gate.mode == kda::GATE_LOGITS && !gate.log_scale) return KDA_ERR_NULL_POINTER;
+    const void *ins[] = {q, k, v, gin, beta, gate.log_scale, gate.bias};
     for (const void *p : ins)
-        if (p == out || p == (const void *)state) return KDA_ERR_ALIAS;
+        if (p && (p == out || p == (const void *)state)) return KDA_ERR_ALIAS;
     if ((const void *)out == (const void *)state) return KDA_ERR_ALIAS;
     if ((uintptr_t)state % 16 != 0) return KDA_ERR_BAD_ARGUMENT;
     if ((int64_t)B * H > (int64_t)0x7fffffff) return KDA_ERR_UNSUPPORTED;
@@ -152,11 +159,76 @@ kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_d
     a.beta = beta;
     a.state = state;
     a.out = out;
-    a.gate_is_log = gate_kind == KDA_GATE_LOG;
+    a.H = H;
     a.out_bf16 = out_dtype == KDA_BF16;
     a.scale = scale;
     hipError_t e = kda::launch_recurrent_step(a, in_dtype == KDA_F32, K, V, B * H, stream);
     return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
+kda::GateIn gate_given(const float *gate, kda_gate_kind kind) {
+    kda::GateIn g{};
+    g.mode = kind == KDA_GATE_LOG ? kda::GATE_LOG : kda::GATE_ALPHA;
+    g.gate = gate;
+    return g;
+}
+
+kda::GateIn gate_logits(const void *logits, const float *log_scale, const float *bias, float lower_bound) {
+    kda::GateIn g{};
+    g.mode = kda::GATE_LOGITS;
+    g.logits = logits;
+    g.log_scale = log_scale;
+    g.bias = bias;
+    g.lower_bound = lower_bound;
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                         const float *gate, kda_gate_kind gate_kind, const float *beta,
+                         const float *initial_state, float *final_state,
+                         const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H, int K,
+                         int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
+                         hipStream_t stream) {
+    if (!gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
+    return chunk_fwd_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), beta, initial_state, final_state,
+                          cu_seqlens, num_seqs, B, T, H, K, V, chunk_size, scale, out, out_dtype, stream);
+}
+
+kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                                    const void *logits, const float *log_scale, const float *bias,
+                                    float lower_bound, const float *beta, const float *initial_state,
+                                    float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
+                                    int64_t T, int H, int K, int V, int chunk_size, float scale, void *out,
+                                    kda_dtype out_dtype, hipStream_t stream) {
+    // the chunk path needs every log-decay >= -5, which the bound guarantees when
+    // lower_bound >= -5
+    if (!(lower_bound < 0.f) || lower_bound < -5.f) return KDA_ERR_BAD_ARGUMENT;
+    return chunk_fwd_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), beta,
+                          initial_state, final_state, cu_seqlens, num_seqs, B, T, H, K, V, chunk_size, scale,
+                          out, out_dtype, stream);
+}
+
+kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                              const float *gate, kda_gate_kind gate_kind, const float *beta,
+                              float *state, int B, int H, int K, int V, float scale, void *out,
+                              kda_dtype out_dtype, hipStream_t stream) {
+    if (!gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
+    return recurrent_step_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), beta, state, B, H, K, V, scale,
+                               out, out_dtype, stream);
+}
+
+kda_status kda_recurrent_step_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                                         const void *logits, const float *log_scale, const float *bias,
+                                         float lower_bound, const float *beta, float *state, int B, int H,
+                                         int K, int V, float scale, void *out, kda_dtype out_dtype,
+                                         hipStream_t stream) {
+    if (!(lower_bound < 0.f)) return KDA_ERR_BAD_ARGUMENT;
+    return recurrent_step_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), beta, state,
+                               B, H, K, V, scale, out, out_dtype, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,986 @@
+// kda_chunk_kernel.h -- chunkwise-parallel KDA prefill on gfx950 matrix cores: the
+// kernel template and its launch helpers, instantiated by kda_chunk.hip (gate given as
+// a float32 tensor) and kda_chunk_logits.hip (gate computed from its logits in the
+// kernel), two translation units so the two sets compile in parallel.
+//
+// Method (KDA cheat sheet, "Chunkwise parallel form", with the UT transform the
+// page names written out): for a chunk of C tokens with start state S and in-chunk
+// cumulative decay gamma_i = prod_{r<=i} alpha_r (per key channel),
+//   A_kk[i,j] = beta_i sum_c k_ic k_jc gamma_ic / gamma_jc   (j < i),  T = (I + A_kk)^-1
+//   Vt = T (beta V - (beta gamma K) S)                     (= U - W S, the pseudo-values)
+//   A_qk[i,j] = sum_c q_ic k_jc gamma_ic / gamma_jc         (j <= i: each read follows
+//                                                          its own write, so the diagonal stays)
+//   O  = (gamma Q) S + A_qk Vt                              (inter + intra chunk)
+//   S' = gamma_C S + (K gamma_C / gamma)^T Vt
+// which equals the token recurrence exactly in real arithmetic.
+//
+// Rescaling (cheat sheet gate table): with every log-decay >= -5, a 16-token tile
+// decays by at most e^-80, so each ratio gamma_i / gamma_j is split at a per-tile
+// reference into two factors inside [e^-80, e^80] -- within float and bf16 range --
+// and every tile of A_kk and A_qk is a dense matrix-core product.  With R_p / E_p
+// the cumulative decay before / at the end of 16-row tile p:
+//   diagonal tile p:         (gamma_i / R_p) * (R_p / gamma_j)
+//   off-diagonal tile (p,q): (gamma_i / R_p) * (R_p / gamma_j), the right factor built
+//                            as (E_q / gamma_j) * (R_p / E_q) so nothing underflows early.
+// All factors are products of retention factors (in-tile prefix and suffix
+// products), so no per-element exponential is needed.
+//
+// Work decomposition: one workgroup of 8 waves per (sequence, head, block of BV
+// value columns); value columns evolve independently, so the split is exact.
+//  * 4 state waves own the float32 state S[K x BV] in registers (one 16-column tile
+//    each) and run the serial part for chunk n: Y = beta V - Bw S, Vt = T Y,
+//    O = Qt S + A_qk Vt, S = gamma_C S + Kt^T Vt.  Their matrix-core operands come
+//    straight from the accumulators of the previous product (the k order of each
+//    product is permuted to match the accumulator layout), so the state never
+//    round-trips through LDS.  In the rest of the chunk period they compute chunk
+//    n+1's A-matrix tiles and T from the operands the prep waves staged.
+//  * 4 prep waves turn chunk n+1's raw inputs into the staged A-matrix operands and
+//    the package (Qt, -Bw, Kt, beta V, gamma_C) in the other half of a
+//    double-buffered LDS area, and prefetch chunk n+2's raw inputs into registers.
+//    Three workgroup barriers per chunk.
+//
+// Precision (bf16 inputs): the A-matrix operands carry factors up to e^80 and use
+// bf16; A_qk, which carries each token's own value to its output, is formed from
+// hi+lo bf16 splits of both operands.  Every other product has operands bounded by
+// ~1 or by the state/value magnitude and uses fp16 (3 more mantissa bits than
+// bf16).  fp32 inputs use fp32 matrix cores throughout.
+#pragma once
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int NT = 512;   // threads per workgroup
+constexpr int NSW = 4;    // state waves: 0..3
+constexpr int NPT = 256;  // prep threads: waves 4..7
+
+constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
+
+struct PrecMixed {
+    using TA = __bf16;    // operands of the decay-rescaled key/query products
+    using TM = _Float16;  // every other matrix-core operand
+    static constexpr bool kSplit = true;
+};
+struct PrecF32 {
+    using TA = float;
+    using TM = float;
+    static constexpr bool kSplit = false;
+};
+
+template <class P, int K, int V, int C, int BV>
+struct Layout {
+    using TA = typename P::TA;
+    using TM = typename P::TM;
+    static constexpr int NP = C / 16;                                  // 16-row tiles per chunk
+    static constexpr int NX = NP >= 3 ? (NP - 1) * (NP - 2) / 2 : 0;  // tiles (p,q) with q <= p-2
+    static constexpr int LKA = K + 16 / (int)sizeof(TA);  // padded row strides (elements)
+    static constexpr int LKM = K + 16 / (int)sizeof(TM);
+    static constexpr int LCM = C + 16 / (int)sizeof(TM);
+    static constexpr int LCF = C + 4;
+    static constexpr int LKS = K + 16 / (int)sizeof(TA);        // staging rows
+    static constexpr int NJT = BV / 16;                         // value column tiles
+    static constexpr int MJ = (NJT + NSW - 1) / NSW;            // column tiles per state wave
+
+    // operand staging of the A-matrix products, in the A-operand type: Lk, then one block
+    // holding Lq, Rd, Ro and the extra right-operand versions X (element offsets sLq..sX).
+    // With a split precision the block is followed by a copy of the same shape holding
+    // the low parts (x - hi), NST elements further on.
+    static constexpr size_t oLk = 0;
+    static constexpr size_t oSt = oLk + al16((size_t)C * LKA * sizeof(TA));
+    static constexpr int sLq = 0;
+    static constexpr int sRd = sLq + C * LKS;
+    static constexpr int sRo = sRd + C * LKS;
+    static constexpr int sX = sRo + (C > 16 ? C - 16 : 0) * LKS;
+    static constexpr int NST = sX + NX * 16 * LKS;
+    static constexpr size_t oAkk = oSt + al16((size_t)NST * sizeof(TA) * (P::kSplit ? 2 : 1));
+    static constexpr size_t oTf = oAkk + al16((size_t)C * LCF * 4);
+    static constexpr size_t oTP = oTf + al16((size_t)C * LCF * 4);
+    static constexpr size_t oBt = oTP + al16((size_t)NP * K * 4);
+    static constexpr size_t oPkg = oBt + al16((size_t)C * 4);
+    // package (two copies)
+    static constexpr size_t pQt = 0;
+    static constexpr size_t pBw = pQt + al16((size_t)C * LKM * sizeof(TM));
+    static constexpr size_t pKt = pBw + al16((size_t)C * LKM * sizeof(TM));
+    static constexpr size_t pTm = pKt + al16((size_t)K * LCM * sizeof(TM));
+    static constexpr size_t pAqk = pTm + al16((size_t)C * LCM * sizeof(TM));
+    static constexpr size_t pbV = pAqk + al16((size_t)C * LCM * sizeof(TM));
+    static constexpr size_t pGC = pbV + al16((size_t)BV * LCM * sizeof(TM));
+    static constexpr size_t szPkg = al16(pGC + (size_t)K * 4);
+    static constexpr size_t total = oPkg + 2 * szPkg;
+    static constexpr bool fits = total <= 160 * 1024;
+};
+
+// ---- matrix-core products whose B operand comes from accumulator tiles ----------------
+//
+// A D-layout accumulator tile (lane l holds rows 4*(l/16)+e, column l%16) is, after
+// conversion, directly a B operand when the k order is permuted: a 16x16x32 step over
+// k tiles (2m, 2m+1) takes k = 32m + 4g + i (i < 4) and 32m + 16 + 4g + (i-4) (i >= 4)
+// for lane group g = l/16; an odd last tile takes k = 16t + 4g + i in the lower half of
+// the same instruction (upper half zero); an fp32 16x16x4 step s over tile t takes
+// k = 16t + 4g + s.  The A operand is read from LDS
+// (k contiguous) in the same order.
+template <typename TM, int NKT>
+struct BFrag;  // packed B operands for NKT consecutive 16-k tiles
+
+template <int NKT>
+struct BFrag<_Float16, NKT> {
+    f16x8 pair[NKT / 2 > 0 ? NKT / 2 : 1];
+    f16x4 tail;
+    __device__ __forceinline__ void set(const f4 *t) {
+#pragma unroll
+        for (int m = 0; m < NKT / 2; ++m) {
+            f16x8 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = (_Float16)t[2 * m][e];
+                x[4 + e] = (_Float16)t[2 * m + 1][e];
+            }
+            pair[m] = x;
+        }
+        if constexpr (NKT % 2 == 1) {
+            f16x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = (_Float16)t[NKT - 1][e];
+            tail = y;
+        }
+    }
+};
+
+template <int NKT>
+struct BFrag<float, NKT> {
+    f4 t[NKT];
+    __device__ __forceinline__ void set(const f4 *x) {
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) t[i] = x[i];
+    }
+};
+
+// acc += A[16 x 16*nkt] * B, A rows in LDS (arow = this lane's row, k contiguous), over
+// the first nkt (<= NKT) k tiles of b.  Callers pass nkt rounded up to even on the
+// 16-bit path only when the extra tile of A is zero.
+template <int NKT>
+__device__ __forceinline__ void mma_bfrag(f4 &acc, const _Float16 *arow, const BFrag<_Float16, NKT> &b,
+                                          int nkt, int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < NKT / 2; ++m) {
+        if (2 * m < nkt) {
+            const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 32 * m + 4 * g);
+            const f16x4 hi = *reinterpret_cast<const f16x4 *>(arow + 32 * m + 16 + 4 * g);
+            const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b.pair[m], acc, 0, 0, 0);
+        }
+    }
+    if constexpr (NKT % 2 == 1) {
+        // an odd last tile goes through the same 16x16x32 instruction with its upper half
+        // zero, so one accumulation chain never mixes instruction shapes
+        if (NKT - 1 < nkt) {
+            const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 16 * (NKT - 1) + 4 * g);
+            const f16x8 a = {lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+            const f16x8 bb = {b.tail[0], b.tail[1], b.tail[2], b.tail[3], 0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bb, acc, 0, 0, 0);
+        }
+    }
+}
+
+template <int NKT>
+__device__ __forceinline__ void mma_bfrag(f4 &acc, const float *arow, const BFrag<float, NKT> &b, int nkt,
+                                          int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+        if (t < nkt) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[16 * t + 4 * g + s], b.t[t][s], acc, 0, 0, 0);
+        }
+    }
+}
+
+// store two consecutive elements (a at p[0], b at p[1]) as one packed write
+template <typename T>
+__device__ __forceinline__ void st2(T *p, float a, float b);
+template <>
+__device__ __forceinline__ void st2<float>(float *p, float a, float b) {
+    *reinterpret_cast<float2 *>(p) = float2{a, b};
+}
+template <>
+__device__ __forceinline__ void st2<__bf16>(__bf16 *p, float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 v2;
+    *reinterpret_cast<v2 *>(p) = v2{(__bf16)a, (__bf16)b};
+}
+template <>
+__device__ __forceinline__ void st2<_Float16>(_Float16 *p, float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) _Float16 v2;
+    *reinterpret_cast<v2 *>(p) = v2{(_Float16)a, (_Float16)b};
+}
+
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for LDS traffic only.  The waves exchange data through LDS alone,
+// so global loads may stay in flight across it (the prep waves' prefetch of the next
+// chunk does); __syncthreads() would drain them at every barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// acc += A[16 x kdim] * B[kdim x 16] for the A-matrix tiles: A rows and B^T rows staged
+// in the A-operand type (k contiguous).  With SPLIT both operands also have low parts
+// (x - hi) `lo` elements further on, and the product is hi*hi + hi*lo + lo*hi (about 16
+// mantissa bits).
+template <class P, bool SPLIT, int kdim>
+__device__ __forceinline__ void mma_stage(f4 &acc, const typename P::TA *A, int lda, const typename P::TA *B,
+                                          int ldb, int lo, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    if constexpr (std::is_same<typename P::TA, float>::value) {
+#pragma unroll
+        for (int k0 = 0; k0 < kdim; k0 += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + g], B[r * ldb + k0 + g], acc, 0, 0, 0);
+    } else {
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+        const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+        auto ld = [&](const __bf16 *p, int k0) -> bf16x8 {
+            if (k0 + 32 > kdim) {
+                // a 16-wide tail fills the lower half of the operand, the upper half is zero
+                const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p + k0 + 4 * g);
+                return __builtin_shufflevector(x, z4, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            return *reinterpret_cast<const bf16x8 *>(p + k0 + 8 * g);
+        };
+#pragma unroll
+        for (int k0 = 0; k0 < kdim; k0 += 32) {
+            const bf16x8 ah = ld(A + r * lda, k0), bh = ld(B + r * ldb, k0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+            if constexpr (SPLIT) {
+                const bf16x8 al = ld(A + lo + r * lda, k0), bl = ld(B + lo + r * ldb, k0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Store two staged values in the A-operand type; with a split precision also their low
+// parts (x - hi), `lo` elements further on.
+template <class P>
+__device__ __forceinline__ void st2_stage(typename P::TA *p, int lo, float a, float b) {
+    if constexpr (std::is_same<typename P::TA, float>::value) {
+        *reinterpret_cast<float2 *>(p) = float2{a, b};
+    } else {
+        typedef __attribute__((ext_vector_type(2))) __bf16 v2;
+        const v2 h = {(__bf16)a, (__bf16)b};
+        *reinterpret_cast<v2 *>(p) = h;
+        if constexpr (P::kSplit) *reinterpret_cast<v2 *>(p + lo) = v2{(__bf16)(a - (float)h[0]), (__bf16)(b - (float)h[1])};
+    }
+}
+
+// acc = X Y for 16x16 X, Y whose 16-wide reduction is held in registers: lane (g, r) gives
+// xr[s] = X[r][4g+s] and lane (g, n) gives yc[s] = Y[4g+s][n] (k = 4g + s on both sides;
+// the result is in the accumulator layout).  T is the operand type: float runs four fp32
+// steps, _Float16 one 16x16x32 step with the upper half of each operand zero.
+template <typename T>
+__device__ __forceinline__ f4 mma16_reg(f4 xr, f4 yc);
+template <>
+__device__ __forceinline__ f4 mma16_reg<float>(f4 xr, f4 yc) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[s], yc[s], acc, 0, 0, 0);
+    return acc;
+}
+template <>
+__device__ __forceinline__ f4 mma16_reg<_Float16>(f4 xr, f4 yc) {
+    const f16x8 a = {(_Float16)xr[0], (_Float16)xr[1], (_Float16)xr[2], (_Float16)xr[3], 0, 0, 0, 0};
+    const f16x8 b = {(_Float16)yc[0], (_Float16)yc[1], (_Float16)yc[2], (_Float16)yc[3], 0, 0, 0, 0};
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, z, 0, 0, 0);
+}
+
+// Value of `v` in lane J of this lane's group of four.
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), J * 0x55, 0xf, 0xf, false));
+}
+
+// (I + A)^-1 for a 16x16 strictly lower triangular A given as an accumulator tile (lane
+// (g, n) holds A[4g+e][n]; entries on and above the diagonal are ignored).  Returns the
+// inverse in the same layout.  Blocked: with Ad the 4x4 diagonal blocks of A and Ao the
+// rest, I + A = (I + Ad)(I + N), N = D Ao, D = (I + Ad)^-1; N is strictly lower at
+// 4x4-block level, so N^4 = 0 and (I + A)^-1 = (I - N + N^2 - N^3) D.  The four 4x4
+// inverses come from forward and backward substitution inside groups of four lanes; the
+// rest is six 16x16 products on the matrix cores in operand type T.
+template <typename T>
+__device__ __forceinline__ f4 unit_lower_inverse16(const f4 a, int lane) {
+    const int g = lane >> 4, n = lane & 15, c = n & 3;
+    const bool diag = (n >> 2) == g;  // lanes holding column c of diagonal block g
+    // entries a_ej = A[4g+e][4g+j] (e > j) of the diagonal block, from quad lane j
+    const float a10 = quad_bcast<0>(a[1]), a20 = quad_bcast<0>(a[2]), a30 = quad_bcast<0>(a[3]);
+    const float a21 = quad_bcast<1>(a[2]), a31 = quad_bcast<1>(a[3]);
+    const float a32 = quad_bcast<2>(a[3]);
+    // column c of the block inverse: x = e_c, then eliminate column by column
+    float x0 = c == 0 ? 1.f : 0.f, x1 = c == 1 ? 1.f : 0.f, x2 = c == 2 ? 1.f : 0.f, x3 = c == 3 ? 1.f : 0.f;
+    x1 -= a10 * x0;
+    x2 -= a20 * x0 + a21 * x1;
+    x3 -= a30 * x0 + a31 * x1 + a32 * x2;
+    // row c of the block inverse: y = e_c^T, then eliminate from the right
+    float y0 = c == 0 ? 1.f : 0.f, y1 = c == 1 ? 1.f : 0.f, y2 = c == 2 ? 1.f : 0.f, y3 = c == 3 ? 1.f : 0.f;
+    y2 -= y3 * a32;
+    y1 -= y2 * a21 + y3 * a31;
+    y0 -= y1 * a10 + y2 * a20 + y3 * a30;
+    // "c" = accumulator layout of a matrix, "r" = accumulator layout of its transpose
+    // (lane (g, n) holds M[n][4g+e]), which is its row-operand form
+    const f4 Dc = diag ? f4{x0, x1, x2, x3} : f4{0.f, 0.f, 0.f, 0.f};
+    const f4 Dr = diag ? f4{y0, y1, y2, y3} : f4{0.f, 0.f, 0.f, 0.f};
+    f4 Aoc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Aoc[e] = (n >> 2) < g ? a[e] : 0.f;
+    // P = X Y: Pc = mma(Xr, Yc) and Pr = mma(Yc, Xr)
+    const f4 Nc = mma16_reg<T>(Dr, Aoc);
+    const f4 Nr = mma16_reg<T>(Aoc, Dr);
+    const f4 N2c = mma16_reg<T>(Nr, Nc);
+    const f4 N2r = mma16_reg<T>(Nc, Nr);
+    const f4 N3r = mma16_reg<T>(N2c, Nr);
+    f4 Mr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Mr[e] = (4 * g + e == n ? 1.f : 0.f) - Nr[e] + N2r[e] - N3r[e];
+    return mma16_reg<T>(Mr, Dc);
+}
+
+// The A-matrix work of one chunk, shared out over four waves (w = 0..3).  Wave p % 4
+// computes A_kk's diagonal tile p and inverts I + A_pp, giving T's diagonal block p; the off-diagonal A_kk tiles (kept in fp32 for T's off-diagonal
+// blocks) and the lower A_qk tiles are dealt round-robin after them.  Reads the operand
+// staging of the chunk; writes Akk, Tf and the Tm / Aqk tiles of package `pk`.
+template <class P, int K, int V, int C, int BV>
+__device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char *pk, int w, int lane) {
+    using L = Layout<P, K, V, C, BV>;
+    using TA = typename P::TA;
+    using TM = typename P::TM;
+    constexpr int NP = L::NP;
+    const int g = lane >> 4;
+    const TA *Lk = reinterpret_cast<const TA *>(smem + L::oLk);
+    const TA *St = reinterpret_cast<const TA *>(smem + L::oSt);
+    float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
+    float *Tf = reinterpret_cast<float *>(smem + L::oTf);
+    TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
+    TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
+    // right operand of tile (p, qt)
+    auto right_of = [&](int p, int qt) -> const TA * {
+        if (qt == p) return St + L::sRd + qt * 16 * L::LKS;
+        if (qt == p - 1) return St + L::sRo + qt * 16 * L::LKS;
+        int xi = 0;
+        for (int pp = 2; pp < p; ++pp) xi += pp - 1;
+        return St + L::sX + (xi + qt) * 16 * L::LKS;
+    };
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        if ((p & 3) != w) continue;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, p), L::LKS, 0, lane);
+        const f4 t = unit_lower_inverse16<TM>(acc, lane);
+        const int j = lane & 15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g + e;
+            const float x = (j <= i) ? t[e] : 0.f;
+            Tf[(p * 16 + i) * L::LCF + p * 16 + j] = x;
+            Tm[(p * 16 + i) * L::LCM + p * 16 + j] = from_f32<TM>(x);
+        }
+    }
+    constexpr int NOFF = NP * (NP - 1) / 2;
+    int t = 0;
+#pragma unroll
+    for (int p = 1; p < NP; ++p)
+#pragma unroll
+        for (int qt = 0; qt < p; ++qt, ++t) {
+            if (((t + NP) & 3) != w) continue;
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKS, 0, lane);
+            const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Akk[(i0 + e) * L::LCF + j] = acc[e];
+        }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int qt = 0; qt <= p; ++qt) {
+            const int tq = NOFF + p * (p + 1) / 2 + qt;
+            if (((tq + NP) & 3) != w) continue;
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_stage<P, P::kSplit, K>(acc, St + L::sLq + p * 16 * L::LKS, L::LKS, right_of(p, qt), L::LKS, L::NST, lane);
+            const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Aqk[(i0 + e) * L::LCM + j] = from_f32<TM>((j <= i0 + e) ? acc[e] : 0.f);
+        }
+}
+
+// ZG: the gate arrives as logits (GATE_LOGITS) and is evaluated in the prep waves;
+// otherwise it is a float32 tensor of alpha or ln alpha (a.gate.mode).
+template <class P, int K, int V, int C, int BV, bool ZG>
+__global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
+    using L = Layout<P, K, V, C, BV>;
+    using TA = typename P::TA;
+    using TM = typename P::TM;
+    using TIn = typename std::conditional<std::is_same<P, PrecF32>::value, float, __bf16>::type;
+    constexpr int NP = L::NP;
+    constexpr int NKT_K = K / 16;  // 16-channel tiles
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;
+
+    // ---- which (sequence, head, value block) this workgroup owns ----------------------
+    constexpr int NVB = V / BV;
+    const int G = gridDim.x;
+    int lin = blockIdx.x;
+    if ((G & 7) == 0) lin = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // a head's value blocks
+    const int vb = lin % NVB;                                                   // share one XCD
+    const int pair = lin / NVB;
+    const int H = a.H;
+    const int h = pair % H;
+    const int s = pair / H;
+    int64_t bos, eos;
+    if (a.cu_seqlens) {
+        bos = a.cu_seqlens[s];
+        eos = a.cu_seqlens[s + 1];
+    } else {
+        bos = (int64_t)s * a.T;
+        eos = bos + a.T;
+    }
+    const int nchunks = (int)((eos - bos + C - 1) / C);
+    const TIn *q = static_cast<const TIn *>(a.q);
+    const TIn *k = static_cast<const TIn *>(a.k);
+    const TIn *v = static_cast<const TIn *>(a.v);
+
+    auto pkg = [&](int buf) { return smem + L::oPkg + (size_t)buf * L::szPkg; };
+
+    if (wave < NSW) {
+        // =================================== state waves ===================================
+        f4 S[L::MJ][NKT_K];
+        const float *s0 = a.initial_state ? a.initial_state + ((int64_t)s * H + h) * K * V : nullptr;
+#pragma unroll
+        for (int mj = 0; mj < L::MJ; ++mj) {
+            const int jt = wave + NSW * mj;
+#pragma unroll
+            for (int t = 0; t < NKT_K; ++t) {
+                f4 x = {0.f, 0.f, 0.f, 0.f};
+                if (jt < L::NJT && s0) {
+                    const int vc = vb * BV + jt * 16 + (lane & 15);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = s0[(int64_t)(16 * t + 4 * g + e) * V + vc];
+                }
+                S[mj][t] = x;
+            }
+        }
+        BFrag<TM, NKT_K> Sh[L::MJ];
+#pragma unroll
+        for (int mj = 0; mj < L::MJ; ++mj) Sh[mj].set(S[mj]);
+
+        float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
+        float *Tf = reinterpret_cast<float *>(smem + L::oTf);
+        for (int it = 0; it <= nchunks; ++it) {
+            if (NP > 1 && wave == 0 && it >= 1) {
+                // T's off-diagonal blocks of the chunk about to be consumed, one block
+                // distance at a time on fp32 matrix cores:
+                //   M = sum_{r=q}^{p-1} A_pr T_rq,   T_pq = -T_pp M
+                TM *Tm = reinterpret_cast<TM *>(pkg((it - 1) & 1) + L::pTm);
+                for (int d = 1; d < NP; ++d) {
+                    for (int qb = 0; qb + d < NP; ++qb) {
+                        const int p = qb + d;
+                        f4 m = {0.f, 0.f, 0.f, 0.f};
+                        for (int r = qb; r < p; ++r)
+#pragma unroll
+                            for (int s4 = 0; s4 < 4; ++s4)
+                                m = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    Akk[(p * 16 + (lane & 15)) * L::LCF + r * 16 + 4 * s4 + g],
+                                    Tf[(r * 16 + 4 * s4 + g) * L::LCF + qb * 16 + (lane & 15)], m, 0, 0, 0);
+                        // M's accumulator layout is the B operand with k = 4g + s4
+                        f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4)
+                            t = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                Tf[(p * 16 + (lane & 15)) * L::LCF + p * 16 + 4 * g + s4], m[s4], t, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = p * 16 + 4 * g + e, j = qb * 16 + (lane & 15);
+                            Tf[i * L::LCF + j] = -t[e];
+                            Tm[i * L::LCM + j] = from_f32<TM>(-t[e]);
+                        }
+                    }
+                    lds_fence();
+                }
+            }
+            lds_barrier();  // B1: prep waves have produced their tile products
+            f4 Vt[L::MJ][NP];
+            BFrag<TM, NP> Vh[L::MJ];
+            const int cn = it - 1;  // chunk handled by the state waves in this iteration
+            if (cn >= 0) {
+                const unsigned char *pk = pkg(cn & 1);
+                const TM *Qt = reinterpret_cast<const TM *>(pk + L::pQt);
+                const TM *Bw = reinterpret_cast<const TM *>(pk + L::pBw);
+                const TM *Tm = reinterpret_cast<const TM *>(pk + L::pTm);
+                const TM *Aqk = reinterpret_cast<const TM *>(pk + L::pAqk);
+                const TM *bV = reinterpret_cast<const TM *>(pk + L::pbV);
+                const int64_t t0 = bos + (int64_t)cn * C;
+                const int n = (int)((eos - t0) < C ? (eos - t0) : C);
+#pragma unroll
+                for (int mj = 0; mj < L::MJ; ++mj) {
+                    const int jt = wave + NSW * mj;
+                    if (jt >= L::NJT) continue;
+                    // Y = beta V - Bw S   (rows: tokens of the chunk; this wave's 16 columns)
+                    f4 Y[NP];
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        f4 y;
+                        const TM *bvr = bV + (jt * 16 + (lane & 15)) * L::LCM + 16 * p + 4 * g;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = to_f32(bvr[e]);
+                        mma_bfrag<NKT_K>(y, Bw + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
+                        Y[p] = y;
+                    }
+                    BFrag<TM, NP> Yh;
+                    Yh.set(Y);
+                    // Vt = T Y (T lower triangular: row tile p needs token tiles 0..p)
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        f4 x = {0.f, 0.f, 0.f, 0.f};
+                        mma_bfrag<NP>(x, Tm + (16 * p + (lane & 15)) * L::LCM, Yh, p + 1, lane);
+                        Vt[mj][p] = x;
+                    }
+                    Vh[mj].set(Vt[mj]);
+                    // O = Qt S + A_qk Vt
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        f4 o = {0.f, 0.f, 0.f, 0.f};
+                        mma_bfrag<NKT_K>(o, Qt + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
+                        mma_bfrag<NP>(o, Aqk + (16 * p + (lane & 15)) * L::LCM, Vh[mj], p + 1, lane);
+                        const int j = vb * BV + jt * 16 + (lane & 15);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = 16 * p + 4 * g + e;
+                            if (i < n) st_out(a.out, a.out_bf16, ((t0 + i) * H + h) * V + j, a.scale * o[e]);
+                        }
+                    }
+                }
+            }
+            if (cn >= 0) {  // S = gamma_C S + Kt^T Vt, still before B2
+                const unsigned char *pk = pkg(cn & 1);
+                const TM *Kt = reinterpret_cast<const TM *>(pk + L::pKt);
+                const float *eGC = reinterpret_cast<const float *>(pk + L::pGC);
+#pragma unroll
+                for (int mj = 0; mj < L::MJ; ++mj) {
+                    const int jt = wave + NSW * mj;
+                    if (jt >= L::NJT) continue;
+                    // S = gamma_C S + Kt^T Vt
+#pragma unroll
+                    for (int t = 0; t < NKT_K; ++t) {
+                        f4 x = S[mj][t];
+                        const float4 d = *reinterpret_cast<const float4 *>(eGC + 16 * t + 4 * g);
+                        x[0] *= d.x; x[1] *= d.y; x[2] *= d.z; x[3] *= d.w;
+                        mma_bfrag<NP>(x, Kt + (16 * t + (lane & 15)) * L::LCM, Vh[mj], NP, lane);
+                        S[mj][t] = x;
+                    }
+                    Sh[mj].set(S[mj]);
+                }
+            }
+            lds_barrier();  // B2: prep waves have written the A-matrix operands
+            if (it < nchunks) a_matrix_work<P, K, V, C, BV>(smem, pkg(it & 1), wave, lane);
+            lds_barrier();  // B3: the next package is complete
+        }
+        if (a.final_state) {
+            float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
+#pragma unroll
+            for (int mj = 0; mj < L::MJ; ++mj) {
+                const int jt = wave + NSW * mj;
+                if (jt >= L::NJT) continue;
+                const int vc = vb * BV + jt * 16 + (lane & 15);
+#pragma unroll
+                for (int t = 0; t < NKT_K; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sf[(int64_t)(16 * t + 4 * g + e) * V + vc] = S[mj][t][e];
+            }
+        }
+        return;
+    }
+
+    // ====================================== prep waves =======================================
+    const int tp = tid - NSW * 64;  // 0 .. NPT-1
+    const int pw = wave - NSW;      // prep wave 0..3
+    TA *Lk = reinterpret_cast<TA *>(smem + L::oLk);         // [C][LKA]
+    TA *St = reinterpret_cast<TA *>(smem + L::oSt);         // Lq, Rd, Ro, X (+ low parts)
+    float *TPv = reinterpret_cast<float *>(smem + L::oTP);  // [NP][K] tile decay products
+    float *Btv = reinterpret_cast<float *>(smem + L::oBt);  // [C] beta of the chunk
+
+    // The strictly upper 16x16 blocks of T and A_qk are zero in every chunk: write them
+    // once, in both package buffers.  (The state waves first read a package after the
+    // first iteration's last barrier.)
+    for (int buf = 0; buf < 2; ++buf) {
+        TM *Tm = reinterpret_cast<TM *>(pkg(buf) + L::pTm);
+        TM *Aq = reinterpret_cast<TM *>(pkg(buf) + L::pAqk);
+        for (int e = tp; e < C * C; e += NPT) {
+            const int i = e / C, j = e % C;
+            if ((j >> 4) > (i >> 4)) {
+                Tm[i * L::LCM + j] = from_f32<TM>(0.f);
+                Aq[i * L::LCM + j] = from_f32<TM>(0.f);
+            }
+        }
+    }
+
+    // Prep mapping: a "combo" is a (channel pair, 16-row tile); each combo is handled by
+    // two lanes of one wave, lane l (rows 0..7 of the tile) and lane l ^ 32 (rows 8..15),
+    // so in-tile prefix and suffix decay products need one exchange between them.
+    constexpr int NCP = K / 2;                   // channel pairs
+    constexpr int NCOMBO = NCP * NP;
+    constexpr int CPT = (NCOMBO + 127) / 128;    // combos per lane pair (4 prep waves x 32)
+    const int hf = lane >> 5;                    // which half of the tile
+    auto combo_of = [&](int u) { return 128 * u + 32 * pw + (lane & 31); };
+
+    // Raw inputs of one chunk: for each combo, 8 rows x 2 channels of the gate, q and k;
+    // beta of row tp; this thread's share of the value block.  The loads are
+    // unconditional (rows past the sequence end read its last row) and nothing is
+    // computed from them until they are used in the next iteration, so they stay in
+    // flight while the current chunk is processed; the padding rows are masked at use.
+    using RawIn = typename std::conditional<std::is_same<TIn, float>::value, float, unsigned short>::type;
+    using RawPair = typename std::conditional<std::is_same<TIn, float>::value, float2, uint32_t>::type;
+    float2 ral[CPT][8];
+    RawPair rq[CPT][8], rk[CPT][8];
+    float rbeta = 0.f;
+    constexpr int NVE = (BV * C / 2 + NPT - 1) / NPT;  // (column, token pair) items per prep thread
+    RawIn rv[NVE][2];
+    // a gate given as logits: the per-head scale and this thread's channel biases
+    const bool glog = a.gate.mode == GATE_LOG;
+    float gs2 = 0.f, gl2 = 0.f;
+    float2 zbias[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) zbias[u] = float2{0.f, 0.f};
+    if constexpr (ZG) {
+        gs2 = expf(a.gate.log_scale[h]) * 1.44269504088896341f;  // e^A log2(e)
+        gl2 = a.gate.lower_bound * 1.44269504088896341f;
+        if (a.gate.bias) {
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u) < NCOMBO ? combo_of(u) : 0;
+                const float *bp = a.gate.bias + h * K + 2 * (cm % NCP);
+                zbias[u] = float2{bp[0], bp[1]};
+            }
+        }
+    }
+    auto load_raw = [&](int cn) {
+        const int64_t t0 = bos + (int64_t)cn * C;
+        const int last = (int)((eos - t0) < C ? (eos - t0) : C) - 1;  // last valid row (>= 0)
+        const int rs = H * K;                                        // row stride of q, k, gate
+        const int64_t cb = (t0 * H + h) * K;                         // chunk base (uniform)
+        const float *gb = a.gate.gate + cb;
+        const RawIn *zb = reinterpret_cast<const RawIn *>(a.gate.logits) + cb;
+        const RawIn *qb = reinterpret_cast<const RawIn *>(q) + cb;
+        const RawIn *kb = reinterpret_cast<const RawIn *>(k) + cb;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int cm = combo_of(u) < NCOMBO ? combo_of(u) : 0;
+            const int c0 = 2 * (cm % NCP);
+            int p = cm / NCP;
+            if constexpr (NCP % 32 == 0) p = __builtin_amdgcn_readfirstlane(p);  // one tile per wave
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 16 * p + 8 * hf + i;
+                const uint32_t o = (uint32_t)((r < last ? r : last) * rs + c0);
+                if constexpr (!ZG) {
+                    ral[u][i] = *reinterpret_cast<const float2 *>(gb + o);
+                } else if constexpr (std::is_same<RawPair, float2>::value) {
+                    ral[u][i] = *reinterpret_cast<const float2 *>(zb + o);
+                } else {
+                    ral[u][i].x = __builtin_bit_cast(float, *reinterpret_cast<const RawPair *>(zb + o));
+                }
+                rq[u][i] = *reinterpret_cast<const RawPair *>(qb + o);
+                rk[u][i] = *reinterpret_cast<const RawPair *>(kb + o);
+            }
+        }
+        rbeta = a.beta[(t0 + (tp < last ? tp : last)) * H + h];
+        const RawIn *vbp = reinterpret_cast<const RawIn *>(v) + (t0 * H + h) * V + vb * BV;
+#pragma unroll
+        for (int w = 0; w < NVE; ++w) {
+            const int e = (tp + NPT * w) % (BV * C / 2);
+            const int j = e % BV, r = 2 * (e / BV);
+            rv[w][0] = vbp[(uint32_t)((r < last ? r : last) * H * V + j)];
+            rv[w][1] = vbp[(uint32_t)((r + 1 < last ? r + 1 : last) * H * V + j)];
+        }
+    };
+    auto raw_f32 = [&](RawIn x) -> float {
+        if constexpr (std::is_same<RawIn, float>::value) return x;
+        else return __builtin_bit_cast(float, (uint32_t)x << 16);
+    };
+    auto pair_f32 = [&](RawPair x, float &lo, float &hi) {
+        if constexpr (std::is_same<RawPair, float2>::value) {
+            lo = x.x;
+            hi = x.y;
+        } else {
+            lo = __builtin_bit_cast(float, x << 16);
+            hi = __builtin_bit_cast(float, x & 0xffff0000u);
+        }
+    };
+    if (nchunks > 0) load_raw(0);
+
+    // per combo: decay factor entering this half from the other one (prefix: product of
+    // rows 0..7 for the second half; suffix: product of rows 8..15 for the first half)
+    float2 pin[CPT], sin[CPT];
+    for (int it = 0; it <= nchunks; ++it) {
+        const bool work = it < nchunks;
+        const int n_it = work ? (int)((eos - (bos + (int64_t)it * C)) < C ? (eos - (bos + (int64_t)it * C)) : C) : 0;
+        // ---- phase 1a: retention factors (1 on padding rows), tile totals, beta --------
+        if (work) {
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u);
+                const int p = cm / NCP;
+                float2 run = {1.f, 1.f};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float2 al = ral[u][i];
+                    if constexpr (!ZG) {
+                        if (glog) {
+                            al.x = __expf(al.x);
+                            al.y = __expf(al.y);
+                        }
+                    } else {
+                        float z0, z1;
+                        if constexpr (std::is_same<RawPair, float2>::value) {
+                            z0 = al.x;
+                            z1 = al.y;
+                        } else {
+                            pair_f32(__builtin_bit_cast(RawPair, al.x), z0, z1);
+                        }
+                        al.x = fast_bounded_alpha(z0 + zbias[u].x, gs2, gl2);
+                        al.y = fast_bounded_alpha(z1 + zbias[u].y, gs2, gl2);
+                    }
+                    if (16 * p + 8 * hf + i >= n_it) al = float2{1.f, 1.f};
+                    ral[u][i] = al;
+                    run.x *= al.x;
+                    run.y *= al.y;
+                }
+                // the other half's product
+                float2 oth;
+                oth.x = __shfl_xor(run.x, 32);
+                oth.y = __shfl_xor(run.y, 32);
+                pin[u] = hf ? oth : float2{1.f, 1.f};
+                sin[u] = hf ? float2{1.f, 1.f} : oth;
+                if (hf == 0 && cm < NCOMBO) {
+                    const int c0 = 2 * (cm % NCP);
+                    *reinterpret_cast<float2 *>(TPv + p * K + c0) = float2{run.x * oth.x, run.y * oth.y};
+                }
+            }
+            if (tp < C) Btv[tp] = tp < n_it ? rbeta : 0.f;
+        }
+        lds_barrier();  // B1
+        // ---- phase 1b: A-matrix operand staging of chunk `it` ---------------------------
+        // The package operands are computed here too but kept in registers and stored in
+        // phase 2, after the prefetch has gone out.
+        float2 kq[CPT][8], kk[CPT][8], kr[CPT][8];  // q gamma/R, beta k gamma/R, k E/gamma per row
+        float2 keR[CPT], keCE[CPT];                 // R_p and E_C / E_p of the combo's tile
+        float2 bvv[NVE];                            // beta v pairs of this thread's value items
+        if (work) {
+            unsigned char *pk = pkg(it & 1);
+            float *eGC = reinterpret_cast<float *>(pk + L::pGC);
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u);
+                if (cm >= NCOMBO) continue;
+                const int c0 = 2 * (cm % NCP), p = cm / NCP;
+                float2 tpr[NP];
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) tpr[pp] = *reinterpret_cast<const float2 *>(TPv + pp * K + c0);
+                float2 eR = {1.f, 1.f}, eCE = {1.f, 1.f}, eAll = {1.f, 1.f}, own = {1.f, 1.f};
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    if (pp < p) { eR.x *= tpr[pp].x; eR.y *= tpr[pp].y; }
+                    if (pp > p) { eCE.x *= tpr[pp].x; eCE.y *= tpr[pp].y; }
+                    if (pp == p) own = tpr[pp];
+                    eAll.x *= tpr[pp].x;
+                    eAll.y *= tpr[pp].y;
+                }
+                if (p == 0 && hf == 0) *reinterpret_cast<float2 *>(eGC + c0) = eAll;
+                const float2 rT = {1.f / own.x, 1.f / own.y};
+                // extra right-operand versions for tiles (pp, p) with pp >= p + 2
+                float2 xf[NP];
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    float2 f = {1.f, 1.f};
+#pragma unroll
+                    for (int r2 = 0; r2 < NP; ++r2)
+                        if (r2 > p && r2 < pp) { f.x *= tpr[r2].x; f.y *= tpr[r2].y; }
+                    xf[pp] = f;
+                }
+                float bet[8];
+#pragma unroll
+                for (int i = 0; i < 8; i += 4) {
+                    const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + 8 * hf + i);
+                    bet[i] = b4.x; bet[i + 1] = b4.y; bet[i + 2] = b4.z; bet[i + 3] = b4.w;
+                }
+                float2 suf[8];  // E_p / gamma_i: product of the tile's later factors
+                {
+                    float2 run = sin[u];
+#pragma unroll
+                    for (int i = 7; i >= 0; --i) {
+                        suf[i] = run;
+                        run.x *= ral[u][i].x;
+                        run.y *= ral[u][i].y;
+                    }
+                }
+                float2 pre = pin[u];  // gamma_i / R_p
+                keR[u] = eR;
+                keCE[u] = eCE;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 16 * p + 8 * hf + i;
+                    pre.x *= ral[u][i].x;
+                    pre.y *= ral[u][i].y;
+                    const bool ok = r < n_it;
+                    float q0, q1, k0, k1;
+                    pair_f32(rq[u][i], q0, q1);
+                    pair_f32(rk[u][i], k0, k1);
+                    if (!ok) q0 = q1 = k0 = k1 = 0.f;
+                    const float2 lq = {q0 * pre.x, q1 * pre.y};
+                    const float2 lk = {bet[i] * k0 * pre.x, bet[i] * k1 * pre.y};
+                    const float2 ro = {k0 * suf[i].x, k1 * suf[i].y};  // k E_p / gamma <= |k|
+                    const float2 rd = {ro.x * rT.x, ro.y * rT.y};        // k R_p / gamma <= e^80 |k|
+                    st2<TA>(Lk + r * L::LKA + c0, lk.x, lk.y);
+                    st2_stage<P>(St + L::sLq + r * L::LKS + c0, L::NST, lq.x, lq.y);
+                    st2_stage<P>(St + L::sRd + r * L::LKS + c0, L::NST, rd.x, rd.y);
+                    if (p < NP - 1) st2_stage<P>(St + L::sRo + r * L::LKS + c0, L::NST, ro.x, ro.y);
+                    if constexpr (L::NX > 0) {
+                        int xi = 0;
+#pragma unroll
+                        for (int pp = 2; pp < NP; ++pp)
+#pragma unroll
+                            for (int qq = 0; qq + 2 <= pp; ++qq, ++xi)
+                                if (qq == p)
+                                    st2_stage<P>(St + L::sX + (xi * 16 + 8 * hf + i) * L::LKS + c0, L::NST,
+                                                 ro.x * xf[pp].x, ro.y * xf[pp].y);
+                    }
+                    kq[u][i] = lq;
+                    kk[u][i] = lk;
+                    kr[u][i] = ro;
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < NVE; ++w) {
+                const int e = tp + NPT * w;
+                if (e < BV * C / 2) {
+                    const int r = 2 * (e / BV);
+                    bvv[w] = float2{raw_f32(rv[w][0]) * Btv[r], raw_f32(rv[w][1]) * Btv[r + 1]};
+                }
+            }
+        }
+        lds_barrier();  // B2
+        // ---- phase 2: the state waves compute the A-matrix tiles; the prep waves send the
+        // prefetch of the next chunk, then store the package operands of this one
+        if (work) {
+            if (it + 1 < nchunks) load_raw(it + 1);  // consumed next iteration
+            unsigned char *pk = pkg(it & 1);
+            TM *Qt = reinterpret_cast<TM *>(pk + L::pQt);
+            TM *Bw = reinterpret_cast<TM *>(pk + L::pBw);
+            TM *Kt = reinterpret_cast<TM *>(pk + L::pKt);
+            TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u);
+                if (cm >= NCOMBO) continue;
+                const int c0 = 2 * (cm % NCP), p = cm / NCP;
+                const float2 eR = keR[u], eCE = keCE[u];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 16 * p + 8 * hf + i;
+                    st2<TM>(Qt + r * L::LKM + c0, kq[u][i].x * eR.x, kq[u][i].y * eR.y);
+                    st2<TM>(Bw + r * L::LKM + c0, -kk[u][i].x * eR.x, -kk[u][i].y * eR.y);
+                    if (i & 1) {
+                        // two consecutive tokens per channel row of Kt
+                        st2<TM>(Kt + c0 * L::LCM + r - 1, kr[u][i - 1].x * eCE.x, kr[u][i].x * eCE.x);
+                        st2<TM>(Kt + (c0 + 1) * L::LCM + r - 1, kr[u][i - 1].y * eCE.y, kr[u][i].y * eCE.y);
+                    }
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < NVE; ++w) {
+                const int e = tp + NPT * w;
+                if (e < BV * C / 2) {
+                    const int j = e % BV, r = 2 * (e / BV);
+                    st2<TM>(bV + j * L::LCM + r, bvv[w].x, bvv[w].y);
+                }
+            }
+        }
+        lds_barrier();  // B3
+    }
+}
+
+// Largest value block (64, 32, 16; not above V) whose LDS layout fits; 0 if none does.
+template <class P, int K, int V, int C>
+constexpr int pick_bv() {
+    if constexpr (V >= 64 && Layout<P, K, V, C, 64>::fits) return 64;
+    else if constexpr (V >= 32 && Layout<P, K, V, C, 32>::fits) return 32;
+    else if constexpr (Layout<P, K, V, C, 16>::fits) return 16;
+    else return 0;
+}
+
+template <class P, bool ZG, int K, int V, int C>
+hipError_t launch_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream, int *bv_out) {
+    constexpr int BV = pick_bv<P, K, V, C>();
+    if constexpr (BV == 0) {
+        return hipErrorNotSupported;
+    } else {
+        using L = Layout<P, K, V, C, BV>;
+        auto kern = chunk_fwd_kernel<P, K, V, C, BV, ZG>;
+        static bool attr_set = false;  // per instantiation, once per process
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::total);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        if (bv_out) *bv_out = BV;
+        const int grid = num_pairs * (V / BV);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), L::total, stream, a);
+        return hipGetLastError();
+    }
+}
+
+template <class P, bool ZG, int K, int V>
+hipError_t launch_kv(const ChunkArgs &a, int C, int num_pairs, hipStream_t stream, int *bv) {
+    if (!a.q) {  // query only: report the value block, launch nothing
+        const int b = C == 16 ? pick_bv<P, K, V, 16>() : C == 32 ? pick_bv<P, K, V, 32>()
+                    : C == 64 ? pick_bv<P, K, V, 64>() : 0;
+        if (bv) *bv = b;
+        return b ? hipSuccess : hipErrorNotSupported;
+    }
+    switch (C) {
+        case 16: return launch_kvc<P, ZG, K, V, 16>(a, num_pairs, stream, bv);
+        case 32: return launch_kvc<P, ZG, K, V, 32>(a, num_pairs, stream, bv);
+        case 64: return launch_kvc<P, ZG, K, V, 64>(a, num_pairs, stream, bv);
+        default: return hipErrorNotSupported;
+    }
+}
+
+template <class P, bool ZG, int K>
+hipError_t launch_k(const ChunkArgs &a, int V, int C, int num_pairs, hipStream_t stream, int *bv) {
+    switch (V) {
+        case 16: return launch_kv<P, ZG, K, 16>(a, C, num_pairs, stream, bv);
+        case 32: return launch_kv<P, ZG, K, 32>(a, C, num_pairs, stream, bv);
+        case 64: return launch_kv<P, ZG, K, 64>(a, C, num_pairs, stream, bv);
+        case 128: return launch_kv<P, ZG, K, 128>(a, C, num_pairs, stream, bv);
+        default: return hipErrorNotSupported;
+    }
+}
+
+template <class P, bool ZG>
+hipError_t launch_p(const ChunkArgs &a, int K, int V, int C, int num_pairs, hipStream_t stream, int *bv) {
+    switch (K) {
+        case 16: return launch_k<P, ZG, 16>(a, V, C, num_pairs, stream, bv);
+        case 32: return launch_k<P, ZG, 32>(a, V, C, num_pairs, stream, bv);
+        case 64: return launch_k<P, ZG, 64>(a, V, C, num_pairs, stream, bv);
+        case 128: return launch_k<P, ZG, 128>(a, V, C, num_pairs, stream, bv);
+        default: return hipErrorNotSupported;
+    }
+}
+
+}  // namespace
+
+}  // namespace kda

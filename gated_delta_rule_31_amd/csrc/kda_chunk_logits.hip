@@ -1,0 +1,13 @@
+// kda_chunk_logits.hip -- the chunk kernels of kda_chunk_kernel.h that evaluate the
+// bounded gate from its logits while staging each chunk (no float32 gate tensor).
+#include "kda_chunk_kernel.h"
+
+namespace kda {
+
+hipError_t launch_chunk_fwd_logits(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
+                                   hipStream_t stream, int *bv) {
+    return fp32_inputs ? launch_p<PrecF32, true>(a, K, V, C, num_pairs, stream, bv)
+                       : launch_p<PrecMixed, true>(a, K, V, C, num_pairs, stream, bv);
+}
+
+}  // namespace kda

@@ -88,6 +88,18 @@ __device__ __forceinline__ void mma_tile<float>(f4 &acc, const float *A, int lda
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k0], b[k0], acc, 0, 0, 0);
 }
 
+// The bounded gate applied on the fly: alpha = exp(lower * sigmoid(scale * x)), with
+// s2 = scale * log2(e) and l2 = lower * log2(e), on the hardware base-2 exponential and
+// reciprocal (a few ulp).  The sigmoid takes exp only of a non-positive argument, so it
+// never overflows, and alpha stays in [e^lower, 1].
+__device__ __forceinline__ float fast_bounded_alpha(float x, float s2, float l2) {
+    const float u = s2 * x;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(u));
+    const float r = __builtin_amdgcn_rcpf(1.f + e);
+    const float sg = u >= 0.f ? r : e * r;
+    return __builtin_amdgcn_exp2f(l2 * sg);
+}
+
 // Load one element of an input tensor as float.
 __device__ __forceinline__ float ld_f32(const float *p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld_f32(const __bf16 *p, int64_t i) { return (float)p[i]; }

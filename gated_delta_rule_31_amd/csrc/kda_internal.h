@@ -8,9 +8,22 @@
 
 namespace kda {
 
+// How the per-channel retention reaches a kernel: alpha itself, its log, or the raw gate
+// logits z, turned into alpha = exp(lower * sigmoid(e^A (z + bias))) on the fly.
+enum GateMode { GATE_ALPHA = 0, GATE_LOG = 1, GATE_LOGITS = 2 };
+
+struct GateIn {
+    int mode;                       // GateMode
+    const float *gate;              // ALPHA / LOG: [rows, H, K] float32
+    const void *logits;             // LOGITS: [rows, H, K], same dtype as q, k, v
+    const float *log_scale;         // LOGITS: [H] (A; the applied scale is e^A)
+    const float *bias;              // LOGITS: [H*K] or null
+    float lower_bound;              // LOGITS: g_min < 0
+};
+
 struct ChunkArgs {
     const void *q, *k, *v;          // [B*T, H, K] / [B*T, H, V], bf16 or fp32
-    const float *gate;              // [B*T, H, K]
+    GateIn gate;
     const float *beta;              // [B*T, H]
     const float *initial_state;     // [N, H, K, V] or null
     float *final_state;             // [N, H, K, V] or null
@@ -18,18 +31,17 @@ struct ChunkArgs {
     void *out;                      // [B*T, H, V]
     int64_t T;                      // tokens per batch row (unused with cu_seqlens)
     int H;
-    int gate_is_log;
     int out_bf16;
     float scale;
 };
 
 struct StepArgs {
     const void *q, *k, *v;          // [B, H, K] / [B, H, V]
-    const float *gate;              // [B, H, K]
+    GateIn gate;                    // rows = B
     const float *beta;              // [B, H]
     float *state;                   // [B, H, K, V], in place
     void *out;                      // [B, H, V]
-    int gate_is_log;
+    int H;
     int out_bf16;
     float scale;
 };
@@ -48,6 +60,9 @@ struct GateArgs {
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                             hipStream_t stream, int *bv);
+// the same for a.gate.mode == GATE_LOGITS (kernels that evaluate the gate themselves)
+hipError_t launch_chunk_fwd_logits(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
+                                   hipStream_t stream, int *bv);
 // value-block width the chunk kernel uses for this shape, 0 if the shape is not compiled
 // (its LDS layout would exceed 160 KB)
 int chunk_fwd_value_block(bool fp32_inputs, int K, int V, int C);

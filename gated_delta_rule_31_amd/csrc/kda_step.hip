@@ -29,7 +29,8 @@ struct StepCfg {
     static_assert(NT <= 256 && NRG * RPT == K, "step mapping");
 };
 
-template <typename TIn, int K, int V>
+// ZG: the gate arrives as logits and is evaluated here; otherwise as alpha or ln alpha.
+template <typename TIn, int K, int V, bool ZG>
 __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(StepArgs a) {
     using Cf = StepCfg<K, V>;
     constexpr int CQ = Cf::CQ, RPT = Cf::RPT, NRG = Cf::NRG;
@@ -46,7 +47,15 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
     const TIn *q = static_cast<const TIn *>(a.q) + (int64_t)pair * K;
     const TIn *k = static_cast<const TIn *>(a.k) + (int64_t)pair * K;
     const TIn *v = static_cast<const TIn *>(a.v) + (int64_t)pair * V;
-    const float *gate = a.gate + (int64_t)pair * K;
+    const int h = pair % a.H;
+    const bool glog = a.gate.mode == GATE_LOG;
+    const float *gate = a.gate.gate + (int64_t)pair * K;
+    const TIn *zl = static_cast<const TIn *>(a.gate.logits) + (int64_t)pair * K;
+    float s2 = 0.f, l2 = 0.f;
+    if constexpr (ZG) {
+        s2 = expf(a.gate.log_scale[h]) * 1.44269504088896341f;
+        l2 = a.gate.lower_bound * 1.44269504088896341f;
+    }
     float4 *S = reinterpret_cast<float4 *>(a.state + (int64_t)pair * K * V);
 
     // the state is streamed: read once and written once per step, so both use
@@ -64,8 +73,14 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + NRG * i;
-        const float g = gate[row];
-        const float al = a.gate_is_log ? expf(g) : g;
+        float al;
+        if constexpr (ZG) {
+            const float z = ld_f32(zl, row) + (a.gate.bias ? a.gate.bias[h * K + row] : 0.f);
+            al = fast_bounded_alpha(z, s2, l2);
+        } else {
+            const float g = gate[row];
+            al = glog ? expf(g) : g;
+        }
         const float kv = ld_f32(k, row), qv = ld_f32(q, row);
         kr[i] = kv;
         kq += kv * qv;
@@ -110,8 +125,12 @@ hipError_t launch_k(const StepArgs &a, int V, int pairs, hipStream_t stream) {
     switch (V) {
 #define KDA_STEP_CASE(VV)                                                                         \
     case VV:                                                                                      \
-        hipLaunchKernelGGL((recurrent_step_kernel<TIn, K, VV>), dim3(pairs), dim3(StepCfg<K, VV>::NT), \
-                           0, stream, a);                                                        \
+        if (a.gate.mode == GATE_LOGITS)                                                           \
+            hipLaunchKernelGGL((recurrent_step_kernel<TIn, K, VV, true>), dim3(pairs),            \
+                               dim3(StepCfg<K, VV>::NT), 0, stream, a);                           \
+        else                                                                                      \
+            hipLaunchKernelGGL((recurrent_step_kernel<TIn, K, VV, false>), dim3(pairs),           \
+                               dim3(StepCfg<K, VV>::NT), 0, stream, a);                           \
         return hipGetLastError();
         KDA_STEP_CASE(16)
         KDA_STEP_CASE(32)

@@ -44,7 +44,8 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+/* 1: gate, chunk and step entry points; 2: adds the fused-gate variants */
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -104,7 +105,8 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
  *   out    [B, T, H, V] in out_dtype
  * Supported: K, V in {16, 32, 64, 128} and chunk sizes whose per-workgroup LDS
  * layout fits 160 KB; kda_chunk_fwd_supported() tells which (chunk size 16 and 32 are
- * available for every K, V; 64 only for small widths).  Anything else returns
+ * available for every K, V on the bf16 path and up to K = 64 on the float32 path; 64 only
+ * for small widths).  Anything else returns
  * KDA_ERR_UNSUPPORTED.  in_dtype KDA_F32 computes in float32 (matrix cores in fp32);
  * KDA_BF16 uses bf16/fp16 matrix-core operands with float32 accumulation and a
  * float32 master state.
@@ -123,6 +125,31 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
                          hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_fused_gate -- kda_chunk_fwd with the gate applied inside the kernel
+ * (PaperLeet "Formula and conventions", operator bounded_decay; the KDARecurrent page
+ * passes the raw gate logits, the per-head scale A, the featurewise bias and the lower
+ * bound to its kernels rather than a precomputed retention):
+ *
+ *   alpha[t,h,c] = exp(lower_bound * sigmoid(exp(log_scale[h]) * (logits[t,h,c] + bias[h*K+c])))
+ *
+ *   logits    [B, T, H, K] in in_dtype (the dtype of q, k and v)
+ *   log_scale [H] float32;  bias [H*K] float32 or NULL
+ *   lower_bound  in [-5, 0): the bound itself is the chunk path's precondition
+ *                (every log-decay >= -5), so it is checked here (KDA_ERR_BAD_ARGUMENT)
+ * Every other argument, the supported set and the empty-sequence rule are those of
+ * kda_chunk_fwd.  The gate is evaluated in float32 on the hardware exp2/reciprocal
+ * (a few ulp from kda_bounded_decay's value), never written to memory, and needs no
+ * float32 gate tensor: the HBM stream drops from 4 to 2 bytes per gate element with
+ * bf16 logits.
+ */
+kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                                    const void *logits, const float *log_scale, const float *bias,
+                                    float lower_bound, const float *beta, const float *initial_state,
+                                    float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
+                                    int64_t T, int H, int K, int V, int chunk_size, float scale, void *out,
+                                    kda_dtype out_dtype, hipStream_t stream);
+
+/*
  * kda_recurrent_step -- one decode token over a kept state, updated IN PLACE
  * (Kept-memory page: a decode call advances the kept per-head state by one token and
  * leaves the result for the next call; PaperLeet recurrence with T = 1).
@@ -139,6 +166,19 @@ kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_d
                               const float *gate, kda_gate_kind gate_kind, const float *beta,
                               float *state, int B, int H, int K, int V, float scale, void *out,
                               kda_dtype out_dtype, hipStream_t stream);
+
+/*
+ * kda_recurrent_step_fused_gate -- kda_recurrent_step with the gate applied inside the
+ * kernel from logits [B, H, K] (in in_dtype), log_scale [H], bias [H*K] or NULL and
+ * lower_bound < 0 (any value: the step accepts every alpha in [0, 1]); the formula is
+ * that of kda_chunk_fwd_fused_gate.  The state is updated in place as in
+ * kda_recurrent_step.
+ */
+kda_status kda_recurrent_step_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                                         const void *logits, const float *log_scale, const float *bias,
+                                         float lower_bound, const float *beta, float *state, int B, int H,
+                                         int K, int V, float scale, void *out, kda_dtype out_dtype,
+                                         hipStream_t stream);
 
 /*
  * kda_chunk_fwd_supported -- host-only query (no device work): the number of value

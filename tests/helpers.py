@@ -79,3 +79,12 @@ def gpu_prefill(inp, chunk_size=32, out_dtype=torch.float32, device="cuda"):
     return kda.chunk_fwd(d(inp.q), d(inp.k), d(inp.v), g, d(inp.beta), initial_state=d(inp.initial_state),
                          cu_seqlens=d(inp.cu_seqlens), chunk_size=chunk_size, gate_is_log=True,
                          out_dtype=out_dtype)
+
+
+def gpu_prefill_fused(inp, chunk_size=32, out_dtype=torch.float32, bias=None, device="cuda"):
+    """GPU path with the gate applied inside the chunk kernel (logits in, no gate tensor)."""
+    import gated_delta_rule_31_amd as kda
+    d = lambda x: None if x is None else x.to(device)
+    return kda.chunk_fwd_fused_gate(d(inp.q), d(inp.k), d(inp.v), d(inp.z), d(inp.log_scale), d(inp.beta),
+                                    bias=d(bias), lower_bound=inp.g_min, initial_state=d(inp.initial_state),
+                                    cu_seqlens=d(inp.cu_seqlens), chunk_size=chunk_size, out_dtype=out_dtype)

@@ -37,7 +37,7 @@ def test_status_strings_and_version(lib):
     assert lib.kda_status_string(0) == b"ok"
     for s in range(1, 8):
         assert lib.kda_status_string(s) not in (b"", b"unknown status")
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
 
 
 def _chunk(lib, **kw):
@@ -99,3 +99,28 @@ def test_python_binding_refuses_cpu_tensors():
     z = torch.zeros(2, 3, 16)
     with pytest.raises(ValueError):
         kda.bounded_decay(z, torch.zeros(3))
+
+
+def test_fused_gate_validation(lib):
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    f = lib.kda_chunk_fwd_fused_gate
+    f.restype = i32
+    f.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32, i32, i32, i32,
+                  f32, vp, i32, vp]
+
+    def chunk(z=4, ls=8, bias=None, lb=-5.0, out=6, K=16):
+        return f(1, 2, 3, 1, z, ls, bias, lb, 5, None, None, None, 0, 1, 64, 2, K, 16, 16, 1.0, out, 1, None)
+    assert chunk(lb=0.0) == 5        # lower bound must be negative
+    assert chunk(lb=-6.0) == 5       # and >= -5 on the chunk path (the tile rescale bound)
+    assert chunk(z=None) == 1        # NULL logits
+    assert chunk(ls=None) == 1       # NULL log_scale
+    assert chunk(out=4) == 6         # out aliases the logits
+    assert chunk(out=8) == 6         # out aliases log_scale
+    assert chunk(K=24) == 4          # unsupported width
+    g = lib.kda_recurrent_step_fused_gate
+    g.restype = i32
+    g.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp]
+    assert g(1, 2, 3, 1, 4, 8, None, 0.0, 5, 16, 2, 2, 16, 16, 1.0, 7, 1, None) == 5   # lower bound >= 0
+    assert g(1, 2, 3, 1, 4, 8, None, -9.0, 5, None, 2, 2, 16, 16, 1.0, 7, 1, None) == 1  # any bound; NULL state
+    assert g(1, 2, 3, 1, None, 8, None, -5.0, 5, 16, 2, 2, 16, 16, 1.0, 7, 1, None) == 1  # NULL logits
+    assert g(1, 2, 3, 1, 4, 8, None, -5.0, 5, 16, 2, 2, 16, 16, 1.0, 4, 1, None) == 6   # out aliases logits

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 from tests.helpers import (BF16_TOL, FP32_TOL, assert_close, err_bf16, err_fp32, f64, gpu_prefill,
-                           oracle_prefill)
+                           gpu_prefill_fused, oracle_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -315,6 +315,84 @@ def test_recurrent_step_equals_chunk_path_fp32():
     assert err_fp32(state, f) < 2 * FP32_TOL
 
 
+# ---- gate applied inside the kernels ---------------------------------------------------
+
+def _oracle_prefill_bias(inp, bias):
+    """fp64 oracle with a featurewise gate bias (added to the logits before the scale)."""
+    q, k, v, z = (f64(x) for x in (inp.q, inp.k, inp.v, inp.z))
+    alpha = oracle.bounded_decay(z, f64(inp.log_scale), g_min=inp.g_min, bias=f64(bias))
+    s0 = None if inp.initial_state is None else f64(inp.initial_state)
+    return oracle.scan(q, k, v, alpha, f64(inp.beta), initial_state=s0)
+
+
+@pytest.mark.parametrize("dtype,K,V,C", [(torch.float32, 16, 16, 16), (torch.float32, 64, 32, 32),
+                                         (torch.bfloat16, 128, 128, 32), (torch.bfloat16, 32, 64, 64)])
+def test_fused_gate_prefill_matches_oracle(dtype, K, V, C):
+    _case("fused gate prefill %s K=%d V=%d C=%d" % (dtype, K, V, C))
+    inp = synth.make_prefill(2, 77, 3, K, V, dtype=dtype, seed=7 * K + V, alog_std=0.5, state_std=0.1)
+    o, f = gpu_prefill_fused(inp, chunk_size=C)
+    eo, ef = oracle_prefill(inp)
+    fp32 = dtype == torch.float32
+    assert_close(o, eo, fp32, "out")
+    assert_close(f, ef, fp32, "final state")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_fused_gate_with_bias(dtype):
+    _case("fused gate with bias %s" % dtype)
+    K = 64 if dtype == torch.float32 else 128
+    inp = synth.make_prefill(1, 100, 2, K, 64, dtype=dtype, seed=77, alog_std=0.5, state_std=0.1)
+    bias = torch.linspace(-2.0, 2.0, 2 * K, dtype=torch.float32).reshape(2, K)
+    o, f = gpu_prefill_fused(inp, chunk_size=32, bias=bias)
+    eo, ef = _oracle_prefill_bias(inp, bias)
+    fp32 = dtype == torch.float32
+    assert_close(o, eo, fp32, "out")
+    assert_close(f, ef, fp32, "final state")
+
+
+def test_fused_gate_equals_separate_gate_fp32():
+    """The in-kernel gate agrees with the gate kernel feeding the plain chunk call to
+    float32 rounding (the two evaluate the same formula on different hardware paths)."""
+    _case("fused == separate gate, fp32")
+    inp = synth.make_prefill(1, 150, 3, 64, 64, dtype=torch.float32, seed=91, alog_std=0.5, state_std=0.1)
+    o1, f1 = gpu_prefill_fused(inp, chunk_size=32)
+    o2, f2 = gpu_prefill(inp, chunk_size=32)
+    assert err_fp32(o1, o2) < 1e-5 and err_fp32(f1, f2) < 1e-5
+
+
+def test_fused_gate_varlen():
+    _case("fused gate varlen")
+    lens = [37, 0, 64, 5, 100]
+    inp = synth.make_prefill(1, sum(lens), 2, 128, 128, seed=93, seqlens=lens, state_std=0.1)
+    o, f = gpu_prefill_fused(inp, chunk_size=32)
+    eo, ef = oracle_prefill(inp)
+    assert_close(o, eo, False, "out")
+    assert_close(f, ef, False, "final states")
+
+
+def test_fused_gate_lower_bound_checked():
+    inp = synth.make_prefill(1, 16, 1, 16, 16, dtype=torch.float32, seed=5)
+    inp.g_min = -6.0
+    with pytest.raises(ValueError):
+        gpu_prefill_fused(inp, chunk_size=16)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_fused_gate_step_sequence(dtype):
+    _case("fused gate decode %s" % dtype)
+    dec = synth.decode(B=3, H=4, K=128, V=64, steps=12, dtype=dtype, seed=103)
+    state = dec.state.cuda().clone()
+    outs = [kda.recurrent_step_fused_gate(dec.q[t].cuda(), dec.k[t].cuda(), dec.v[t].cuda(), dec.z[t].cuda(),
+                                          dec.log_scale.cuda(), dec.beta[t].cuda(), state,
+                                          out_dtype=torch.float32)
+            for t in range(12)]
+    eo, es = _oracle_steps(dec, dec.state, 12)
+    fp32 = dtype == torch.float32
+    for t in range(12):
+        assert_close(outs[t], eo[t], fp32, "step %d out" % t)
+    assert_close(state, es, fp32, "state")
+
+
 # ---- full-size workloads, sampled ------------------------------------------------------
 
 def test_k3_prefill_full_size_sampled_heads():
@@ -326,6 +404,20 @@ def test_k3_prefill_full_size_sampled_heads():
     ob, fb = gpu_prefill(inp, chunk_size=32, out_dtype=torch.bfloat16)
     assert torch.equal(ob, o.to(torch.bfloat16)) and torch.equal(fb, f)
     heads = [0, 47, 95]
+    eo, ef = oracle_prefill(inp, heads=heads)
+    assert_close(o[:, :, heads], eo, False, "out (heads %s)" % heads)
+    assert_close(f[:, heads], ef, False, "final state (heads %s)" % heads)
+    assert torch.isfinite(o).all() and torch.isfinite(f).all()
+
+
+def test_k3_prefill_fused_gate_full_size_sampled_heads():
+    """The same layer through the fused-gate entry point, as the benchmark times it."""
+    _case("k3 prefill fused gate full size, sampled heads")
+    inp = synth.k3_prefill(device="cuda")
+    o, f = gpu_prefill_fused(inp, chunk_size=32)
+    ob, fb = gpu_prefill_fused(inp, chunk_size=32, out_dtype=torch.bfloat16)
+    assert torch.equal(ob, o.to(torch.bfloat16)) and torch.equal(fb, f)
+    heads = [1, 50, 94]
     eo, ef = oracle_prefill(inp, heads=heads)
     assert_close(o[:, :, heads], eo, False, "out (heads %s)" % heads)
     assert_close(f[:, heads], ef, False, "final state (heads %s)" % heads)
