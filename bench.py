@@ -115,6 +115,7 @@ def main():
                     help="fused: the kernels take the gate logits; separate: bounded_decay writes a "
                          "float32 gate that the kernels read")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-short", action="store_true", help="skip the short-continuation (token-recurrent) block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -298,6 +299,49 @@ def main():
         result["decode"]["device_copy_GBps_same_bytes"] = 2 * half / (copy_ms * 1e-3) / 1e9
         del dec, state, src, dst
 
+    # ---------------- short continuations: the token-recurrent prefill ------------------
+    if not args.no_short:
+        log("generating short-continuation inputs")
+        sp = synth.short_prompts(device="cuda")
+        Bs, Ts, Hs = sp.q.shape[0], sp.q.shape[1], sp.q.shape[2]
+        so = torch.empty(Bs, Ts, Hs, V, dtype=torch.bfloat16, device=dev)
+        sf = torch.empty(Bs, Hs, K, V, dtype=torch.float32, device=dev)
+
+        def rcall():
+            if fused:
+                kda.recurrent_fwd_fused_gate(sp.q, sp.k, sp.v, sp.z, sp.log_scale, sp.beta, lower_bound=-5.0,
+                                             initial_state=sp.initial_state, out=so, final_state=sf)
+            else:
+                kda.recurrent_fwd(sp.q, sp.k, sp.v, sg, sp.beta, initial_state=sp.initial_state, out=so,
+                                  final_state=sf)
+
+        if not fused:
+            sg = kda.bounded_decay(sp.z, sp.log_scale, lower_bound=-5.0)
+        for _ in range(3):
+            rcall()
+        torch.cuda.synchronize()
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        t0 = time.perf_counter()
+        for a_, b_ in rev:
+            a_.record(stream)
+            rcall()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        rwall = time.perf_counter() - t0
+        r_ms = sum(a_.elapsed_time(b_) for a_, b_ in rev) / len(rev)
+        # per (sequence, head): state read + write, and per token q, k, v, gate, beta, out
+        r_bytes = Bs * Hs * (2 * K * V * 4 + Ts * (3 * 2 * K + gate_bytes + 4 + 2 * V))
+        r_gbs = r_bytes / (r_ms * 1e-3) / 1e9
+        log("short continuations: %.1f us per call, %.0f GB/s" % (r_ms * 1e3, r_gbs))
+        result["short_continuations"] = {
+            "workload": sp.name, "call": "recurrent_fwd_fused_gate" if fused else "recurrent_fwd",
+            "tokens_per_s": Bs * Ts / (r_ms * 1e-3), "us_per_call": r_ms * 1e3,
+            "roofline": {"bound": "hbm", "achieved": r_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": r_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "recurrent_fwd_kernel",
+                         "algorithmic_bytes_per_launch": r_bytes},
+        }
+        del so, sf
+
     # ---------------- CPU baseline: the oracle on a head sample -------------------------
     if not args.no_cpu_baseline:
         import oracle
@@ -316,6 +360,20 @@ def main():
         result["cpu_baseline"] = {"value": cpu_tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                   "sample": "fp64 gate + token scan of %d of the %d heads (T=8192), %.1f s wall, "
                                             "scaled by %d/%d" % (len(hs), H, cpu_s, H, len(hs))}
+        if not args.no_short:
+            # the same oracle on a sample of the short-continuation (sequence, head) pairs
+            npairs = 48
+            t0 = time.perf_counter()
+            for i in range(npairs):
+                b_i, h_i = (i * 37) % Bs, (i * 53) % Hs
+                sl = lambda x: f64(x[b_i:b_i + 1, :, h_i:h_i + 1])
+                al = oracle.bounded_decay(sl(sp.z), f64(sp.log_scale[h_i:h_i + 1]), g_min=-5.0)
+                oracle.scan(sl(sp.q), sl(sp.k), sl(sp.v), al, sl(sp.beta),
+                            f64(sp.initial_state[b_i:b_i + 1, h_i:h_i + 1]))
+            r_cpu = (time.perf_counter() - t0) * (Bs * Hs) / npairs
+            result["short_continuations"]["cpu_baseline"] = {
+                "value": Bs * Ts / r_cpu, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": "%d of the %d (sequence, head) pairs, scaled" % (npairs, Bs * Hs)}
         log("cpu baseline %.1f tokens/s (%.1f s on %d threads)" % (cpu_tps, cpu_s, threads))
 
     print(json.dumps(result), flush=True)

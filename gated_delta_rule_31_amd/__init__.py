@@ -14,7 +14,10 @@ Entry points (same names as the C ABI, minus the ``kda_`` prefix where noted):
   initial / final state and packed sequences (``cu_seqlens``).
 * ``recurrent_step(q, k, v, gate, beta, state, ...)`` -- one decode token, state
   updated in place.
-* ``chunk_fwd_fused_gate`` / ``recurrent_step_fused_gate`` -- the same two calls with
+* ``recurrent_fwd(q, k, v, gate, beta, ...)`` -- the prefill contract of ``chunk_fwd``
+  evaluated token by token (short sequences; no chunk size, any alpha in [0, 1]).
+* ``chunk_fwd_fused_gate`` / ``recurrent_fwd_fused_gate`` / ``recurrent_step_fused_gate``
+  -- the same calls with
   the gate applied inside the kernel from its logits (``log_scale``, ``bias``,
   ``lower_bound``), so no float32 gate tensor is made.
 * ``recurrent_kda(q, k, v, alpha, beta, initial_state=None)`` -- the functional
@@ -29,7 +32,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["bounded_decay", "chunk_fwd", "recurrent_step", "recurrent_kda", "KDAError", "chunk_fwd_supported",
-           "chunk_fwd_fused_gate", "recurrent_step_fused_gate",
+           "chunk_fwd_fused_gate", "recurrent_step_fused_gate", "recurrent_fwd", "recurrent_fwd_fused_gate",
            "library_path", "abi_version", "GATE_ALPHA", "GATE_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +80,12 @@ def _load():
     lib.kda_recurrent_step_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32,
                                                   f32, vp, i32, vp]
     lib.kda_recurrent_step_fused_gate.restype = i32
+    lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32,
+                                      f32, vp, i32, vp]
+    lib.kda_recurrent_fwd.restype = i32
+    lib.kda_recurrent_fwd_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, i32, i32, i64,
+                                                 i32, i32, i32, f32, vp, i32, vp]
+    lib.kda_recurrent_fwd_fused_gate.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
@@ -255,6 +264,53 @@ def chunk_fwd_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logi
                                               T, H, K, V, int(chunk_size), float(scale), _ptr(out),
                                               _dtype_code(od), _stream(q))
     _check("kda_chunk_fwd_fused_gate", st)
+    return out, final_state
+
+
+def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
+                  beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                  output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+                  scale: float = 1.0, gate_is_log: bool = False, out_dtype: Optional[torch.dtype] = None,
+                  out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd``'s contract evaluated token by token (for short sequences); no chunk
+    size and no bound on the log-decay."""
+    q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
+        q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state)
+    gate = _dev(gate, "gate", torch.float32)
+    if gate.shape != q.shape:
+        raise ValueError("gate must be shaped like q")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    with torch.cuda.device(q.device):
+        st = _load().kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(gate),
+                                       GATE_LOG if gate_is_log else GATE_ALPHA, _ptr(beta), _ptr(initial_state),
+                                       _ptr(final_state), _ptr(cu_seqlens), N, B, T, H, K, V, float(scale),
+                                       _ptr(out), _dtype_code(od), _stream(q))
+    _check("kda_recurrent_fwd", st)
+    return out, final_state
+
+
+def recurrent_fwd_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: torch.Tensor,
+                             log_scale: torch.Tensor, beta: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                             lower_bound: float = -5.0, initial_state: Optional[torch.Tensor] = None,
+                             output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+                             scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
+                             out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+                             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``recurrent_fwd`` with the gate evaluated inside the kernel from its logits."""
+    q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
+        q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state)
+    logits, log_scale, bias = _gate_params(logits, log_scale, bias, q)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    with torch.cuda.device(q.device):
+        st = _load().kda_recurrent_fwd_fused_gate(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(logits),
+                                                  _ptr(log_scale), _ptr(bias), float(lower_bound), _ptr(beta),
+                                                  _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, B,
+                                                  T, H, K, V, float(scale), _ptr(out), _dtype_code(od),
+                                                  _stream(q))
+    _check("kda_recurrent_fwd_fused_gate", st)
     return out, final_state
 
 

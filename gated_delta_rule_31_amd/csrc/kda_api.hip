@@ -166,6 +166,55 @@ kda_status recurrent_step_impl(const void *q, const void *k, const void *v, kda_
     return e == hipSuccess ? KDA_OK : hip_fail(e);
 }
 
+// Shared body of the token-recurrent entry points (same contract as the chunk ones,
+// without a chunk size and without the chunk path's log-decay bound).
+kda_status recurrent_fwd_impl(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                              const kda::GateIn &gate, const float *beta, const float *initial_state,
+                              float *final_state, const int32_t *cu_seqlens, int num_seqs, int B, int64_t T,
+                              int H, int K, int V, float scale, void *out, kda_dtype out_dtype,
+                              hipStream_t stream) {
+    if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_BAD_DTYPE;
+    if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
+    if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_BAD_ARGUMENT;
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    if (B == 0 || T == 0 || N == 0) {
+        if (final_state && N > 0 && initial_state != final_state) {
+            hipError_t e = kda::launch_fill_copy(final_state, initial_state, N * H * K * V, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        return KDA_OK;
+    }
+    const void *gin = gate.mode == kda::GATE_LOGITS ? gate.logits : (const void *)gate.gate;
+    if (!q || !k || !v || !gin || !beta || !out) return KDA_ERR_NULL_POINTER;
+    if (gate.mode == kda::GATE_LOGITS && !gate.log_scale) return KDA_ERR_NULL_POINTER;
+    const void *ins[] = {q, k, v, gin, beta, initial_state, cu_seqlens, gate.log_scale, gate.bias};
+    for (const void *p : ins) {
+        if (p && (p == out || p == (const void *)final_state)) {
+            if (p == (const void *)initial_state && p == (const void *)final_state) continue;
+            return KDA_ERR_ALIAS;
+        }
+    }
+    if ((const void *)out == (const void *)final_state) return KDA_ERR_ALIAS;
+    if (N > (int64_t)(1 << 28) / H) return KDA_ERR_UNSUPPORTED;
+    kda::RecurrentArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.gate = gate;
+    a.beta = beta;
+    a.initial_state = initial_state;
+    a.final_state = final_state;
+    a.cu_seqlens = cu_seqlens;
+    a.out = out;
+    a.T = T;
+    a.H = H;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    a.scale = scale;
+    hipError_t e = kda::launch_recurrent_fwd(a, in_dtype == KDA_F32, K, V, (int)(N * H), stream);
+    return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
 kda::GateIn gate_given(const float *gate, kda_gate_kind kind) {
     kda::GateIn g{};
     g.mode = kind == KDA_GATE_LOG ? kda::GATE_LOG : kda::GATE_ALPHA;
@@ -210,6 +259,28 @@ kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v,
     return chunk_fwd_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), beta,
                           initial_state, final_state, cu_seqlens, num_seqs, B, T, H, K, V, chunk_size, scale,
                           out, out_dtype, stream);
+}
+
+kda_status kda_recurrent_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                             const float *gate, kda_gate_kind gate_kind, const float *beta,
+                             const float *initial_state, float *final_state, const int32_t *cu_seqlens,
+                             int num_seqs, int B, int64_t T, int H, int K, int V, float scale, void *out,
+                             kda_dtype out_dtype, hipStream_t stream) {
+    if (!gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
+    return recurrent_fwd_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), beta, initial_state, final_state,
+                              cu_seqlens, num_seqs, B, T, H, K, V, scale, out, out_dtype, stream);
+}
+
+kda_status kda_recurrent_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                                        const void *logits, const float *log_scale, const float *bias,
+                                        float lower_bound, const float *beta, const float *initial_state,
+                                        float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
+                                        int64_t T, int H, int K, int V, float scale, void *out,
+                                        kda_dtype out_dtype, hipStream_t stream) {
+    if (!(lower_bound < 0.f)) return KDA_ERR_BAD_ARGUMENT;
+    return recurrent_fwd_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), beta,
+                              initial_state, final_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, out,
+                              out_dtype, stream);
 }
 
 kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_dtype in_dtype,

@@ -46,6 +46,20 @@ struct StepArgs {
     float scale;
 };
 
+struct RecurrentArgs {
+    const void *q, *k, *v;          // [B*T, H, K] / [B*T, H, V], bf16 or fp32
+    GateIn gate;
+    const float *beta;              // [B*T, H]
+    const float *initial_state;     // [N, H, K, V] or null
+    float *final_state;             // [N, H, K, V] or null
+    const int32_t *cu_seqlens;      // [N+1] or null
+    void *out;                      // [B*T, H, V]
+    int64_t T;
+    int H;
+    int out_bf16;
+    float scale;
+};
+
 struct GateArgs {
     const void *logits;
     const float *log_scale;
@@ -68,6 +82,8 @@ hipError_t launch_chunk_fwd_logits(const ChunkArgs &a, bool fp32_inputs, int K, 
 int chunk_fwd_value_block(bool fp32_inputs, int K, int V, int C);
 hipError_t launch_recurrent_step(const StepArgs &a, bool fp32_inputs, int K, int V, int pairs,
                                  hipStream_t stream);
+hipError_t launch_recurrent_fwd(const RecurrentArgs &a, bool fp32_inputs, int K, int V, int num_pairs,
+                                hipStream_t stream);
 hipError_t launch_bounded_decay(const GateArgs &a, bool fp32_logits, hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for i < n
 hipError_t launch_fill_copy(float *dst, const float *src, int64_t n, hipStream_t stream);

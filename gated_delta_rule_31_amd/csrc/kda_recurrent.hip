@@ -1,0 +1,267 @@
+// kda_recurrent.hip -- multi-token fused recurrent KDA forward (gfx950).
+//
+// The recurrence itself, token after token, for short sequences (speculative decode,
+// short prompts) where the chunked form's per-chunk set-up does not pay off
+// (PaperLeet "Formula and conventions"; the model excerpt on the Kept-memory page has a
+// token-recurrent kernel beside the chunked one, taking any length and packed sequences):
+//   Sbar  = Diag(alpha_t) S
+//   delta = beta_t (v_t - Sbar^T k_t)
+//   S     = Sbar + k_t delta^T
+//   o_t   = scale S^T q_t = scale (Sbar^T q_t + (k_t . q_t) delta)
+// Any alpha in [0, 1] is allowed (no rescaling is involved).
+//
+// Mapping: one workgroup per (sequence, head, block of BV value columns), one wave per
+// 16 columns.  Lane l of a wave owns column l % 16 and key rows
+// [RQ * (l / 16), RQ * (l / 16) + RQ) with RQ = K / 4, so the state stays in registers
+// for the whole sequence and the reductions over K are a sum over the lane's own rows
+// plus two cross-lane steps.  The token inputs arrive in blocks of TB tokens: the
+// workgroup loads block b+1 with 16-byte loads while it runs block b from LDS, and
+// converts it to float32 (alpha and k.q included) once for all its columns.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int RW = 4;  // waves per workgroup (at most; fewer when V < 64)
+constexpr int TB = 8;  // tokens per staged block
+
+typedef __attribute__((ext_vector_type(8))) float f4x2;
+
+__device__ __forceinline__ f4x2 to_f4x2(f4x2 x) { return x; }
+__device__ __forceinline__ f4x2 to_f4x2(bf16x8 x) {
+    f4x2 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (float)x[e];
+    return y;
+}
+
+template <typename TIn, int K, int V, bool ZG>
+__global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a) {
+    constexpr int RQ = K / 4;                       // key rows per lane
+    constexpr int NW = V / 16 < RW ? V / 16 : RW;   // waves per workgroup
+    constexpr int NTH = 64 * NW;
+    constexpr int BV = 16 * NW;                     // value columns per workgroup
+    constexpr int NVB = V / BV;
+    constexpr int UK = K / 8;                       // 8-element units per key row
+    constexpr int NU = TB * UK;                     // key-row units of one block (per tensor)
+    constexpr int UPT = (NU + NTH - 1) / NTH;       // units per thread and tensor
+    constexpr int VU = TB * BV / 8;                 // value units of one block
+    constexpr int VPT = (VU + NTH - 1) / NTH;
+    using RawU = typename std::conditional<std::is_same<TIn, float>::value, f4x2, bf16x8>::type;
+    using RawG = typename std::conditional<ZG, RawU, f4x2>::type;
+
+    // two blocks of TB tokens staged in float32: k, q and alpha rows, k.q, v, beta
+    __shared__ __align__(16) float sk[2][TB][K];
+    __shared__ __align__(16) float sq[2][TB][K];
+    __shared__ __align__(16) float sa[2][TB][K];
+    __shared__ __align__(16) float sv[2][TB][BV];
+    __shared__ float skq[2][TB], sbeta[2][TB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;                        // row quarter
+    const int vb = blockIdx.x % NVB;
+    const int pair = blockIdx.x / NVB;
+    const int H = a.H;
+    const int h = pair % H;
+    const int s = pair / H;
+    int64_t bos, eos;
+    if (a.cu_seqlens) {
+        bos = a.cu_seqlens[s];
+        eos = a.cu_seqlens[s + 1];
+    } else {
+        bos = (int64_t)s * a.T;
+        eos = bos + a.T;
+    }
+    const int col = wave * 16 + (lane & 15);        // column within the workgroup's block
+    const int gcol = vb * BV + col;
+    const int r0 = RQ * g;
+
+    float S[RQ];
+    const float *s0 = a.initial_state ? a.initial_state + ((int64_t)s * H + h) * K * V : nullptr;
+#pragma unroll
+    for (int i = 0; i < RQ; ++i) S[i] = s0 ? s0[(int64_t)(r0 + i) * V + gcol] : 0.f;
+
+    const bool glog = a.gate.mode == GATE_LOG;
+    float s2 = 0.f, l2 = 0.f;
+    float zbias[UPT][8];
+#pragma unroll
+    for (int w = 0; w < UPT; ++w)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zbias[w][e] = 0.f;
+    if constexpr (ZG) {
+        s2 = expf(a.gate.log_scale[h]) * 1.44269504088896341f;
+        l2 = a.gate.lower_bound * 1.44269504088896341f;
+        if (a.gate.bias) {
+#pragma unroll
+            for (int w = 0; w < UPT; ++w) {
+                const int c = 8 * ((tid + NTH * w) % UK);  // the same column for every block
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zbias[w][e] = a.gate.bias[h * K + c + e];
+            }
+        }
+    }
+    const TIn *q = static_cast<const TIn *>(a.q);
+    const TIn *k = static_cast<const TIn *>(a.k);
+    const TIn *v = static_cast<const TIn *>(a.v);
+    const TIn *zl = static_cast<const TIn *>(a.gate.logits);
+    const int nblk = (int)((eos - bos + TB - 1) / TB);
+
+    // raw units of one block, held in registers between their load and their staging
+    RawU rk[UPT], rq[UPT], rv[VPT];
+    RawG ra[UPT];
+    float rb = 0.f;
+    auto load_block = [&](int b) {
+        const int64_t t0 = bos + (int64_t)b * TB;
+        const int64_t last = eos - 1;  // rows past the end read the last row (not used)
+#pragma unroll
+        for (int w = 0; w < UPT; ++w) {
+            const int u = tid + NTH * w < NU ? tid + NTH * w : 0;
+            const int j = u / UK, c = 8 * (u % UK);
+            const int64_t t = t0 + j < last ? t0 + j : last;
+            const int64_t o = (t * H + h) * K + c;
+            rk[w] = *reinterpret_cast<const RawU *>(k + o);
+            rq[w] = *reinterpret_cast<const RawU *>(q + o);
+            if constexpr (ZG)
+                ra[w] = *reinterpret_cast<const RawU *>(zl + o);
+            else
+                ra[w] = *reinterpret_cast<const f4x2 *>(a.gate.gate + o);
+        }
+#pragma unroll
+        for (int w = 0; w < VPT; ++w) {
+            const int u = tid + NTH * w < VU ? tid + NTH * w : 0;
+            const int j = u / (BV / 8), c = 8 * (u % (BV / 8));
+            const int64_t t = t0 + j < last ? t0 + j : last;
+            rv[w] = *reinterpret_cast<const RawU *>(v + (t * H + h) * V + vb * BV + c);
+        }
+        if (tid < TB) rb = a.beta[(t0 + tid < last ? t0 + tid : last) * H + h];
+    };
+    // convert the held units into LDS buffer `buf`; alpha and k.q are formed here, once
+    // per workgroup rather than once per value column
+    auto stage_block = [&](int buf) {
+#pragma unroll
+        for (int w = 0; w < UPT; ++w) {
+            const int u = tid + NTH * w;
+            const int j = u / UK, c = 8 * (u % UK);
+            const f4x2 kk = to_f4x2(rk[w]), qq = to_f4x2(rq[w]);
+            f4x2 al = to_f4x2(ra[w]);
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (ZG)
+                    al[e] = fast_bounded_alpha(al[e] + zbias[w][e], s2, l2);
+                else if (glog)
+                    al[e] = expf(al[e]);
+                dot += kk[e] * qq[e];
+            }
+            // k.q of the token: the UK units of a row sit in UK consecutive lanes
+#pragma unroll
+            for (int m = 1; m < UK; m <<= 1) dot += __shfl_xor(dot, m);
+            if (u < NU) {
+                *reinterpret_cast<f4x2 *>(&sk[buf][j][c]) = kk;
+                *reinterpret_cast<f4x2 *>(&sq[buf][j][c]) = qq;
+                *reinterpret_cast<f4x2 *>(&sa[buf][j][c]) = al;
+                if (c == 0) skq[buf][j] = dot;
+            }
+        }
+#pragma unroll
+        for (int w = 0; w < VPT; ++w) {
+            const int u = tid + NTH * w;
+            if (u < VU) {
+                const int j = u / (BV / 8), c = 8 * (u % (BV / 8));
+                *reinterpret_cast<f4x2 *>(&sv[buf][j][c]) = to_f4x2(rv[w]);
+            }
+        }
+        if (tid < TB) sbeta[buf][tid] = rb;
+    };
+
+    if (nblk > 0) {
+        load_block(0);
+        stage_block(0);
+    }
+    __syncthreads();
+    for (int b = 0; b < nblk; ++b) {
+        const int buf = b & 1;
+        if (b + 1 < nblk) load_block(b + 1);  // in flight while this block runs
+        const int64_t t0 = bos + (int64_t)b * TB;
+        for (int j = 0; j < TB; ++j) {
+            const int64_t t = t0 + j;
+            if (t >= eos) break;
+            const float *kr = &sk[buf][j][r0], *qr = &sq[buf][j][r0], *ar = &sa[buf][j][r0];
+            float p = 0.f, r = 0.f;
+#pragma unroll
+            for (int i = 0; i < RQ; i += 4) {
+                const float4 k4 = *reinterpret_cast<const float4 *>(kr + i);
+                const float4 q4 = *reinterpret_cast<const float4 *>(qr + i);
+                const float4 a4 = *reinterpret_cast<const float4 *>(ar + i);
+                S[i] *= a4.x; S[i + 1] *= a4.y; S[i + 2] *= a4.z; S[i + 3] *= a4.w;
+                p += S[i] * k4.x + S[i + 1] * k4.y + S[i + 2] * k4.z + S[i + 3] * k4.w;
+                r += S[i] * q4.x + S[i + 1] * q4.y + S[i + 2] * q4.z + S[i + 3] * q4.w;
+            }
+            // sum over the four row quarters (lanes l, l^16, l^32, l^48)
+            p += __shfl_xor(p, 16);
+            r += __shfl_xor(r, 16);
+            p += __shfl_xor(p, 32);
+            r += __shfl_xor(r, 32);
+            const float d = sbeta[buf][j] * (sv[buf][j][col] - p);
+            if (g == 0) st_out(a.out, a.out_bf16, (t * H + h) * V + gcol, a.scale * (r + skq[buf][j] * d));
+#pragma unroll
+            for (int i = 0; i < RQ; i += 4) {
+                const float4 k4 = *reinterpret_cast<const float4 *>(kr + i);
+                S[i] += k4.x * d; S[i + 1] += k4.y * d; S[i + 2] += k4.z * d; S[i + 3] += k4.w * d;
+            }
+        }
+        if (b + 1 < nblk) stage_block(buf ^ 1);
+        __syncthreads();
+    }
+    if (a.final_state) {
+        float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
+#pragma unroll
+        for (int i = 0; i < RQ; ++i) sf[(int64_t)(r0 + i) * V + gcol] = S[i];
+    }
+}
+
+template <typename TIn, bool ZG, int K>
+hipError_t launch_k(const RecurrentArgs &a, int V, int num_pairs, hipStream_t stream) {
+    switch (V) {
+#define KDA_REC_CASE(VV)                                                                          \
+    case VV: {                                                                                    \
+        constexpr int NW = VV / 16 < RW ? VV / 16 : RW;                                           \
+        hipLaunchKernelGGL((recurrent_fwd_kernel<TIn, K, VV, ZG>), dim3(num_pairs * (VV / (16 * NW))), \
+                           dim3(64 * NW), 0, stream, a);                                          \
+        return hipGetLastError();                                                                 \
+    }
+        KDA_REC_CASE(16)
+        KDA_REC_CASE(32)
+        KDA_REC_CASE(64)
+        KDA_REC_CASE(128)
+#undef KDA_REC_CASE
+        default: return hipErrorNotSupported;
+    }
+}
+
+template <typename TIn, bool ZG>
+hipError_t launch_t(const RecurrentArgs &a, int K, int V, int num_pairs, hipStream_t stream) {
+    switch (K) {
+        case 16: return launch_k<TIn, ZG, 16>(a, V, num_pairs, stream);
+        case 32: return launch_k<TIn, ZG, 32>(a, V, num_pairs, stream);
+        case 64: return launch_k<TIn, ZG, 64>(a, V, num_pairs, stream);
+        case 128: return launch_k<TIn, ZG, 128>(a, V, num_pairs, stream);
+        default: return hipErrorNotSupported;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent_fwd(const RecurrentArgs &a, bool fp32_inputs, int K, int V, int num_pairs,
+                                hipStream_t stream) {
+    const bool zg = a.gate.mode == GATE_LOGITS;
+    if (fp32_inputs)
+        return zg ? launch_t<float, true>(a, K, V, num_pairs, stream) : launch_t<float, false>(a, K, V, num_pairs, stream);
+    return zg ? launch_t<__bf16, true>(a, K, V, num_pairs, stream) : launch_t<__bf16, false>(a, K, V, num_pairs, stream);
+}
+
+}  // namespace kda

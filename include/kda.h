@@ -44,7 +44,8 @@
 extern "C" {
 #endif
 
-/* 1: gate, chunk and step entry points; 2: adds the fused-gate variants */
+/* 1: gate, chunk and step entry points; 2: adds the fused-gate variants and the
+ * token-recurrent prefill */
 #define KDA_ABI_VERSION 2
 
 typedef enum {
@@ -148,6 +149,34 @@ kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v,
                                     float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
                                     int64_t T, int H, int K, int V, int chunk_size, float scale, void *out,
                                     kda_dtype out_dtype, hipStream_t stream);
+
+/*
+ * kda_recurrent_fwd -- the same operation as kda_chunk_fwd (same arguments, layouts,
+ * state rules, varlen and empty-sequence behaviour) evaluated token by token with the
+ * state held in registers (PaperLeet "Formula and conventions"; the model excerpt on the
+ * Kept-memory page runs a token-recurrent kernel beside the chunked one for any length).
+ * Meant for short sequences (speculative decoding, short prompts), where the chunked
+ * form's per-chunk work does not pay off.  No chunk size; any alpha in [0, 1] is
+ * allowed (no log-decay bound); all arithmetic is float32 on the vector units.
+ * Supported: K, V in {16, 32, 64, 128}.
+ */
+kda_status kda_recurrent_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                             const float *gate, kda_gate_kind gate_kind, const float *beta,
+                             const float *initial_state, float *final_state, const int32_t *cu_seqlens,
+                             int num_seqs, int B, int64_t T, int H, int K, int V, float scale, void *out,
+                             kda_dtype out_dtype, hipStream_t stream);
+
+/*
+ * kda_recurrent_fwd_fused_gate -- kda_recurrent_fwd with the gate evaluated inside the
+ * kernel from logits [B, T, H, K] (in in_dtype), log_scale [H], bias [H*K] or NULL and
+ * any lower_bound < 0 (the formula of kda_chunk_fwd_fused_gate).
+ */
+kda_status kda_recurrent_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                                        const void *logits, const float *log_scale, const float *bias,
+                                        float lower_bound, const float *beta, const float *initial_state,
+                                        float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
+                                        int64_t T, int H, int K, int V, float scale, void *out,
+                                        kda_dtype out_dtype, hipStream_t stream);
 
 /*
  * kda_recurrent_step -- one decode token over a kept state, updated IN PLACE

@@ -171,6 +171,23 @@ def decode(device="cpu", seed=4, B=64, H=96, K=128, V=128, steps=256,
                         q=q, k=k, v=v, z=z, log_scale=torch.zeros(H, device=device), beta=beta)
 
 
+def short_prompts(device="cpu", seed=6, B=64, T=16, H=96, K=128, V=128,
+                  dtype=torch.bfloat16) -> PrefillInputs:
+    """Short continuations over a kept state (speculative decoding / short prompts):
+    B sequences of T tokens each, kept fp32 state ~ N(0,0.05), the decode workload's
+    per-token recipe (q,k L2norm(N(0,1)), v N(0,1), z N(0,1) with A=0, beta sigmoid(N(0,1)))."""
+    gen = _gen(device, seed)
+    s0 = _normal((B, H, K, V), gen, device, 0.0, 0.05)
+    q = _l2norm(_normal((B, T, H, K), gen, device)).to(dtype)
+    k = _l2norm(_normal((B, T, H, K), gen, device)).to(dtype)
+    v = _normal((B, T, H, V), gen, device).to(dtype)
+    z = _normal((B, T, H, K), gen, device).to(dtype)
+    beta = torch.sigmoid(_normal((B, T, H), gen, device))
+    return PrefillInputs(name="short_prompts_B%d_T%d_H%d_K%d_V%d" % (B, T, H, K, V), q=q, k=k, v=v, z=z,
+                         log_scale=torch.zeros(H, device=device), beta=beta.float(), initial_state=s0,
+                         cu_seqlens=None, g_min=-5.0, chunk_size=16, meta=dict(seed=seed, seqlens=None))
+
+
 def retention(shape, seed=0, device="cpu", lo_log=-5.0, hi_log=0.0) -> torch.Tensor:
     """Random retention factors drawn log-uniformly in [e^lo_log, e^hi_log] (an input
     distribution for scan-only tests, not the gate)."""

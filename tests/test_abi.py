@@ -124,3 +124,28 @@ def test_fused_gate_validation(lib):
     assert g(1, 2, 3, 1, 4, 8, None, -9.0, 5, None, 2, 2, 16, 16, 1.0, 7, 1, None) == 1  # any bound; NULL state
     assert g(1, 2, 3, 1, None, 8, None, -5.0, 5, 16, 2, 2, 16, 16, 1.0, 7, 1, None) == 1  # NULL logits
     assert g(1, 2, 3, 1, 4, 8, None, -5.0, 5, 16, 2, 2, 16, 16, 1.0, 4, 1, None) == 6   # out aliases logits
+
+
+def test_recurrent_fwd_validation(lib):
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    f = lib.kda_recurrent_fwd
+    f.restype = i32
+    f.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32, i32, i32, f32, vp,
+                  i32, vp]
+
+    def call(q=1, gk=0, K=16, T=8, B=1, cu=None, out=6, sf=None):
+        return f(q, 2, 3, 1, 4, gk, 5, None, sf, cu, 0, B, T, 2, K, 16, 1.0, out, 1, None)
+    assert call(K=24) == 4
+    assert call(gk=3) == 3
+    assert call(T=-1) == 2
+    assert call(q=None) == 1
+    assert call(out=2) == 6
+    assert call(sf=3) == 6
+    assert call(cu=9, B=2) == 5
+    assert call(T=0, q=None, out=None) == 0   # empty: nothing to do without a final state
+    g = lib.kda_recurrent_fwd_fused_gate
+    g.restype = i32
+    g.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32, i32, i32, f32,
+                  vp, i32, vp]
+    assert g(1, 2, 3, 1, 4, 8, None, 0.0, 5, None, None, None, 0, 1, 8, 2, 16, 16, 1.0, 6, 1, None) == 5
+    assert g(1, 2, 3, 1, 4, None, None, -9.0, 5, None, None, None, 0, 1, 8, 2, 16, 16, 1.0, 6, 1, None) == 1

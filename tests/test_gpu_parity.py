@@ -393,6 +393,90 @@ def test_fused_gate_step_sequence(dtype):
     assert_close(state, es, fp32, "state")
 
 
+# ---- token-recurrent prefill ------------------------------------------------------------
+
+def _gpu_recurrent(inp, fused=False, out_dtype=torch.float32, alpha=None, final_state=None, init=None):
+    d = lambda x: None if x is None else x.cuda()
+    s0 = d(inp.initial_state) if init is None else init
+    if fused:
+        return kda.recurrent_fwd_fused_gate(d(inp.q), d(inp.k), d(inp.v), d(inp.z), d(inp.log_scale), d(inp.beta),
+                                            lower_bound=inp.g_min, initial_state=s0,
+                                            cu_seqlens=d(inp.cu_seqlens), out_dtype=out_dtype,
+                                            final_state=final_state)
+    if alpha is None:
+        alpha = kda.bounded_decay(d(inp.z), d(inp.log_scale), lower_bound=inp.g_min)
+    return kda.recurrent_fwd(d(inp.q), d(inp.k), d(inp.v), alpha, d(inp.beta), initial_state=s0,
+                             cu_seqlens=d(inp.cu_seqlens), out_dtype=out_dtype, final_state=final_state)
+
+
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 16, 16), (torch.float32, 64, 32), (torch.float32, 128, 128),
+                                       (torch.bfloat16, 128, 128), (torch.bfloat16, 32, 64)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_recurrent_fwd_matches_oracle(dtype, K, V, fused):
+    _case("recurrent fwd %s K=%d V=%d fused=%s" % (dtype, K, V, fused))
+    inp = synth.make_prefill(2, 45, 3, K, V, dtype=dtype, seed=3 * K + V, alog_std=0.5, state_std=0.1)
+    o, f = _gpu_recurrent(inp, fused=fused)
+    eo, ef = oracle_prefill(inp)
+    fp32 = dtype == torch.float32
+    assert_close(o, eo, fp32, "out")
+    assert_close(f, ef, fp32, "final state")
+
+
+def test_recurrent_fwd_varlen_and_empty():
+    _case("recurrent fwd varlen")
+    lens = [9, 0, 33, 1, 0, 17]
+    inp = synth.make_prefill(1, sum(lens), 2, 64, 64, seed=21, seqlens=lens, state_std=0.1)
+    o, f = _gpu_recurrent(inp, fused=True)
+    eo, ef = oracle_prefill(inp)
+    assert_close(o, eo, False, "out")
+    assert_close(f, ef, False, "final states")
+
+
+def test_recurrent_fwd_any_alpha():
+    """No log-decay bound on the token path: a lower bound of -20 and exact zeros."""
+    _case("recurrent fwd, alpha down to e^-20 and 0")
+    inp = synth.make_prefill(1, 40, 2, 64, 64, dtype=torch.float32, seed=23, z_mean=2.0, state_std=0.1)
+    inp.g_min = -20.0
+    o, f = _gpu_recurrent(inp, fused=True)
+    eo, ef = oracle_prefill(inp)
+    assert_close(o, eo, True, "out (g_min -20)")
+    assert_close(f, ef, True, "state (g_min -20)")
+    alpha = kda.bounded_decay(inp.z.cuda(), inp.log_scale.cuda(), lower_bound=-5.0)
+    alpha[:, 7] = 0.0
+    o, f = _gpu_recurrent(inp, alpha=alpha)
+    ea, es = oracle.scan(f64(inp.q), f64(inp.k), f64(inp.v), f64(alpha), f64(inp.beta), f64(inp.initial_state))
+    assert_close(o, ea, True, "out (alpha = 0 at one token)")
+    assert_close(f, es, True, "state (alpha = 0 at one token)")
+
+
+def test_recurrent_fwd_equals_chunk_fp32_and_in_place():
+    _case("recurrent fwd == chunk fwd (fp32), in-place state")
+    inp = synth.make_prefill(2, 70, 3, 64, 64, dtype=torch.float32, seed=25, alog_std=0.5, state_std=0.1)
+    o1, f1 = _gpu_recurrent(inp, fused=True)
+    o2, f2 = gpu_prefill_fused(inp, chunk_size=32)
+    assert err_fp32(o1, o2) < 2 * FP32_TOL and err_fp32(f1, f2) < 2 * FP32_TOL
+    st = inp.initial_state.cuda().clone()
+    o3, f3 = _gpu_recurrent(inp, fused=True, init=st, final_state=st)
+    assert f3 is st and torch.equal(o3, o1) and torch.equal(st, f1)
+
+
+def test_short_prompts_full_size_sampled():
+    """The short-continuation workload the benchmark times (B=64 T=16 H=96 K=V=128, bf16,
+    kept state, gate in the kernel); the oracle checks a sample of (sequence, head) pairs."""
+    _case("short prompts full size, sampled pairs")
+    inp = synth.short_prompts(device="cuda")
+    o, f = _gpu_recurrent(inp, fused=True)
+    ob, fb = _gpu_recurrent(inp, fused=True, out_dtype=torch.bfloat16)
+    assert torch.equal(ob, o.to(torch.bfloat16)) and torch.equal(fb, f)
+    for b, h in [(0, 0), (17, 50), (63, 95)]:
+        sl = lambda x: x[b:b + 1, :, h:h + 1]
+        al = oracle.bounded_decay(f64(sl(inp.z)), f64(inp.log_scale[h:h + 1]), g_min=inp.g_min)
+        eo, ef = oracle.scan(f64(sl(inp.q)), f64(sl(inp.k)), f64(sl(inp.v)), al, f64(sl(inp.beta)),
+                             f64(inp.initial_state[b:b + 1, h:h + 1]))
+        assert_close(o[b:b + 1, :, h:h + 1], eo, False, "out (b=%d h=%d)" % (b, h))
+        assert_close(f[b:b + 1, h:h + 1], ef, False, "state (b=%d h=%d)" % (b, h))
+
+
 # ---- full-size workloads, sampled ------------------------------------------------------
 
 def test_k3_prefill_full_size_sampled_heads():
