@@ -40,6 +40,11 @@ _LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 GATE_ALPHA, GATE_LOG = 0, 1
+QK_L2NORM, BETA_LOGITS, STATE_VK = 1, 2, 4  # input-preparation flags of the fused-gate calls
+
+
+def _flags(qk_l2norm: bool, beta_logits: bool, state_vk: bool) -> int:
+    return (QK_L2NORM if qk_l2norm else 0) | (BETA_LOGITS if beta_logits else 0) | (STATE_VK if state_vk else 0)
 _STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "bad dtype", 4: "unsupported",
            5: "bad argument", 6: "alias", 7: "hip error"}
 
@@ -65,7 +70,7 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError("libkda.so is not built (%s); run gated_delta_rule_31_amd/build.py" % _LIB_PATH)
     lib = ctypes.CDLL(_LIB_PATH)
-    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    vp, i32, i64, f32, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_uint
     lib.kda_bounded_decay.argtypes = [vp, i32, vp, vp, f32, i64, i32, i32, i32, vp, vp]
     lib.kda_bounded_decay.restype = i32
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i64, i32, i32,
@@ -74,17 +79,17 @@ def _load():
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, f32, vp,
                                        i32, vp]
     lib.kda_recurrent_step.restype = i32
-    lib.kda_chunk_fwd_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, i32, i32, i64,
-                                             i32, i32, i32, i32, f32, vp, i32, vp]
+    lib.kda_chunk_fwd_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, vp, vp, i32, i32,
+                                             i64, i32, i32, i32, i32, f32, vp, i32, vp]
     lib.kda_chunk_fwd_fused_gate.restype = i32
-    lib.kda_recurrent_step_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32,
-                                                  f32, vp, i32, vp]
+    lib.kda_recurrent_step_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, i32, i32, i32,
+                                                  i32, f32, vp, i32, vp]
     lib.kda_recurrent_step_fused_gate.restype = i32
     lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32,
                                       f32, vp, i32, vp]
     lib.kda_recurrent_fwd.restype = i32
-    lib.kda_recurrent_fwd_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, i32, i32, i64,
-                                                 i32, i32, i32, f32, vp, i32, vp]
+    lib.kda_recurrent_fwd_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, vp, vp, i32, i32,
+                                                 i64, i32, i32, i32, f32, vp, i32, vp]
     lib.kda_recurrent_fwd_fused_gate.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -171,7 +176,8 @@ def bounded_decay(logits: torch.Tensor, log_scale: torch.Tensor, lower_bound: fl
     return out
 
 
-def _chunk_common(q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state):
+def _chunk_common(q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state,
+                  state_vk: bool = False):
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k and v must share one dtype")
@@ -186,18 +192,19 @@ def _chunk_common(q, k, v, beta, initial_state, output_final_state, cu_seqlens, 
         raise ValueError("inconsistent shapes: q %s k %s v %s beta %s" % (
             tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(beta.shape)))
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    if initial_state is not None and initial_state.shape != (N, H, K, V):
-        raise ValueError("initial_state must be [%d, %d, %d, %d]" % (N, H, K, V))
+    sshape = (N, H, V, K) if state_vk else (N, H, K, V)
+    if initial_state is not None and initial_state.shape != sshape:
+        raise ValueError("initial_state must be %s" % (list(sshape),))
     od = out_dtype or v.dtype
     if out is None:
         out = torch.empty((B, T, H, V), dtype=od, device=q.device)
     elif out.shape != (B, T, H, V) or out.dtype != od or not out.is_contiguous():
         raise ValueError("out must be contiguous [B,T,H,V] of the output dtype")
     if output_final_state and final_state is None:
-        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
-    if final_state is not None and (final_state.shape != (N, H, K, V) or final_state.dtype != torch.float32
+        final_state = torch.empty(sshape, dtype=torch.float32, device=q.device)
+    if final_state is not None and (final_state.shape != sshape or final_state.dtype != torch.float32
                                     or not final_state.is_contiguous()):
-        raise ValueError("final_state must be contiguous float32 [N,H,K,V]")
+        raise ValueError("final_state must be contiguous float32 %s" % (list(sshape),))
     return q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state
 
 
@@ -247,19 +254,23 @@ def chunk_fwd_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logi
                          lower_bound: float = -5.0, initial_state: Optional[torch.Tensor] = None,
                          output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
                          chunk_size: int = 32, scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
-                         out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+                         out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                         qk_l2norm: bool = False, beta_logits: bool = False, state_vk: bool = False
                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """``chunk_fwd`` with alpha = exp(lower_bound * sigmoid(e^log_scale (logits + bias)))
     computed inside the kernel.  logits [B,T,H,K] in the dtype of q; log_scale [H] and
-    bias [H,K] float32; lower_bound in [-5, 0)."""
+    bias [H,K] float32; lower_bound in [-5, 0).  ``qk_l2norm``: q and k are normalised
+    over K in the kernel; ``beta_logits``: beta holds logits (sigmoid in the kernel);
+    ``state_vk``: states are [N,H,V,K]."""
     q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
-        q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state)
+        q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state, state_vk)
     logits, log_scale, bias = _gate_params(logits, log_scale, bias, q)
     B, T, H, K = q.shape
     V = v.shape[-1]
     with torch.cuda.device(q.device):
         st = _load().kda_chunk_fwd_fused_gate(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(logits),
-                                              _ptr(log_scale), _ptr(bias), float(lower_bound), _ptr(beta),
+                                              _ptr(log_scale), _ptr(bias), float(lower_bound),
+                                              _flags(qk_l2norm, beta_logits, state_vk), _ptr(beta),
                                               _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, B,
                                               T, H, K, V, int(chunk_size), float(scale), _ptr(out),
                                               _dtype_code(od), _stream(q))
@@ -296,17 +307,20 @@ def recurrent_fwd_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                              lower_bound: float = -5.0, initial_state: Optional[torch.Tensor] = None,
                              output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
                              scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
-                             out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+                             out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                             qk_l2norm: bool = False, beta_logits: bool = False, state_vk: bool = False
                              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """``recurrent_fwd`` with the gate evaluated inside the kernel from its logits."""
+    """``recurrent_fwd`` with the gate evaluated inside the kernel from its logits (and
+    the input-preparation options of ``chunk_fwd_fused_gate``)."""
     q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
-        q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state)
+        q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state, state_vk)
     logits, log_scale, bias = _gate_params(logits, log_scale, bias, q)
     B, T, H, K = q.shape
     V = v.shape[-1]
     with torch.cuda.device(q.device):
         st = _load().kda_recurrent_fwd_fused_gate(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(logits),
-                                                  _ptr(log_scale), _ptr(bias), float(lower_bound), _ptr(beta),
+                                                  _ptr(log_scale), _ptr(bias), float(lower_bound),
+                                                  _flags(qk_l2norm, beta_logits, state_vk), _ptr(beta),
                                                   _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, B,
                                                   T, H, K, V, float(scale), _ptr(out), _dtype_code(od),
                                                   _stream(q))
@@ -314,7 +328,7 @@ def recurrent_fwd_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     return out, final_state
 
 
-def _step_common(q, k, v, beta, state, out_dtype, out):
+def _step_common(q, k, v, beta, state, out_dtype, out, state_vk: bool = False):
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k and v must share one dtype")
@@ -326,7 +340,8 @@ def _step_common(q, k, v, beta, state, out_dtype, out):
         raise ValueError("q must be [B, H, K]")
     B, H, K = q.shape
     V = v.shape[-1]
-    if k.shape != q.shape or v.shape != (B, H, V) or beta.shape != (B, H) or state.shape != (B, H, K, V):
+    sshape = (B, H, V, K) if state_vk else (B, H, K, V)
+    if k.shape != q.shape or v.shape != (B, H, V) or beta.shape != (B, H) or state.shape != sshape:
         raise ValueError("inconsistent shapes")
     od = out_dtype or v.dtype
     if out is None:
@@ -360,16 +375,20 @@ def recurrent_step_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               log_scale: torch.Tensor, beta: torch.Tensor, state: torch.Tensor,
                               bias: Optional[torch.Tensor] = None, lower_bound: float = -5.0,
                               scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
-                              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                              out: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                              beta_logits: bool = False, state_vk: bool = False) -> torch.Tensor:
     """``recurrent_step`` with the gate computed inside the kernel from logits [B,H,K]
-    (dtype of q), log_scale [H], bias [H,K] or None and lower_bound < 0."""
-    q, k, v, beta, od, out = _step_common(q, k, v, beta, state, out_dtype, out)
+    (dtype of q), log_scale [H], bias [H,K] or None and lower_bound < 0; the
+    input-preparation options of ``chunk_fwd_fused_gate`` (state [B,H,V,K] with
+    ``state_vk``)."""
+    q, k, v, beta, od, out = _step_common(q, k, v, beta, state, out_dtype, out, state_vk)
     logits, log_scale, bias = _gate_params(logits, log_scale, bias, q)
     B, H, K = q.shape
     V = v.shape[-1]
     with torch.cuda.device(q.device):
         st = _load().kda_recurrent_step_fused_gate(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(logits),
-                                                   _ptr(log_scale), _ptr(bias), float(lower_bound), _ptr(beta),
+                                                   _ptr(log_scale), _ptr(bias), float(lower_bound),
+                                                   _flags(qk_l2norm, beta_logits, state_vk), _ptr(beta),
                                                    _ptr(state), B, H, K, V, float(scale), _ptr(out),
                                                    _dtype_code(od), _stream(q))
     _check("kda_recurrent_step_fused_gate", st)

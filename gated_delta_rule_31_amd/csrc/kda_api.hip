@@ -81,12 +81,13 @@ namespace {
 
 // Shared body of the chunk entry points; `gate` says how the retention arrives.
 kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, kda_dtype in_dtype,
-                          const kda::GateIn &gate, const float *beta, const float *initial_state,
+                          const kda::GateIn &gate, unsigned flags, const float *beta, const float *initial_state,
                           float *final_state, const int32_t *cu_seqlens, int num_seqs, int B, int64_t T,
                           int H, int K, int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
                           hipStream_t stream) {
     if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_BAD_DTYPE;
+    if (flags & ~(unsigned)(KDA_QK_L2NORM | KDA_BETA_LOGITS | KDA_STATE_VK)) return KDA_ERR_BAD_ARGUMENT;
     if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
     if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_BAD_ARGUMENT;
@@ -129,17 +130,21 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, kda_dtype
     a.H = H;
     a.out_bf16 = out_dtype == KDA_BF16;
     a.scale = scale;
+    a.qk_l2norm = (flags & KDA_QK_L2NORM) != 0;
+    a.beta_logits = (flags & KDA_BETA_LOGITS) != 0;
+    a.state_vk = (flags & KDA_STATE_VK) != 0;
     int bv = 0;
     hipError_t e = kda::launch_chunk_fwd(a, in_dtype == KDA_F32, K, V, chunk_size, (int)(N * H), stream, &bv);
     return e == hipSuccess ? KDA_OK : hip_fail(e);
 }
 
 kda_status recurrent_step_impl(const void *q, const void *k, const void *v, kda_dtype in_dtype,
-                               const kda::GateIn &gate, const float *beta, float *state, int B, int H,
+                               const kda::GateIn &gate, unsigned flags, const float *beta, float *state, int B, int H,
                                int K, int V, float scale, void *out, kda_dtype out_dtype,
                                hipStream_t stream) {
     if (B < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_BAD_DTYPE;
+    if (flags & ~(unsigned)(KDA_QK_L2NORM | KDA_BETA_LOGITS | KDA_STATE_VK)) return KDA_ERR_BAD_ARGUMENT;
     if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
     if (B == 0) return KDA_OK;
     const void *gin = gate.mode == kda::GATE_LOGITS ? gate.logits : (const void *)gate.gate;
@@ -162,6 +167,9 @@ kda_status recurrent_step_impl(const void *q, const void *k, const void *v, kda_
     a.H = H;
     a.out_bf16 = out_dtype == KDA_BF16;
     a.scale = scale;
+    a.qk_l2norm = (flags & KDA_QK_L2NORM) != 0;
+    a.beta_logits = (flags & KDA_BETA_LOGITS) != 0;
+    a.state_vk = (flags & KDA_STATE_VK) != 0;
     hipError_t e = kda::launch_recurrent_step(a, in_dtype == KDA_F32, K, V, B * H, stream);
     return e == hipSuccess ? KDA_OK : hip_fail(e);
 }
@@ -169,12 +177,13 @@ kda_status recurrent_step_impl(const void *q, const void *k, const void *v, kda_
 // Shared body of the token-recurrent entry points (same contract as the chunk ones,
 // without a chunk size and without the chunk path's log-decay bound).
 kda_status recurrent_fwd_impl(const void *q, const void *k, const void *v, kda_dtype in_dtype,
-                              const kda::GateIn &gate, const float *beta, const float *initial_state,
+                              const kda::GateIn &gate, unsigned flags, const float *beta, const float *initial_state,
                               float *final_state, const int32_t *cu_seqlens, int num_seqs, int B, int64_t T,
                               int H, int K, int V, float scale, void *out, kda_dtype out_dtype,
                               hipStream_t stream) {
     if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_BAD_DTYPE;
+    if (flags & ~(unsigned)(KDA_QK_L2NORM | KDA_BETA_LOGITS | KDA_STATE_VK)) return KDA_ERR_BAD_ARGUMENT;
     if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
     if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_BAD_ARGUMENT;
     const int64_t N = cu_seqlens ? num_seqs : B;
@@ -211,6 +220,9 @@ kda_status recurrent_fwd_impl(const void *q, const void *k, const void *v, kda_d
     a.H = H;
     a.out_bf16 = out_dtype == KDA_BF16;
     a.scale = scale;
+    a.qk_l2norm = (flags & KDA_QK_L2NORM) != 0;
+    a.beta_logits = (flags & KDA_BETA_LOGITS) != 0;
+    a.state_vk = (flags & KDA_STATE_VK) != 0;
     hipError_t e = kda::launch_recurrent_fwd(a, in_dtype == KDA_F32, K, V, (int)(N * H), stream);
     return e == hipSuccess ? KDA_OK : hip_fail(e);
 }
@@ -243,20 +255,20 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
                          int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
                          hipStream_t stream) {
     if (!gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
-    return chunk_fwd_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), beta, initial_state, final_state,
+    return chunk_fwd_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), 0u, beta, initial_state, final_state,
                           cu_seqlens, num_seqs, B, T, H, K, V, chunk_size, scale, out, out_dtype, stream);
 }
 
 kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
                                     const void *logits, const float *log_scale, const float *bias,
-                                    float lower_bound, const float *beta, const float *initial_state,
+                                    float lower_bound, unsigned flags, const float *beta, const float *initial_state,
                                     float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
                                     int64_t T, int H, int K, int V, int chunk_size, float scale, void *out,
                                     kda_dtype out_dtype, hipStream_t stream) {
     // the chunk path needs every log-decay >= -5, which the bound guarantees when
     // lower_bound >= -5
     if (!(lower_bound < 0.f) || lower_bound < -5.f) return KDA_ERR_BAD_ARGUMENT;
-    return chunk_fwd_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), beta,
+    return chunk_fwd_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), flags, beta,
                           initial_state, final_state, cu_seqlens, num_seqs, B, T, H, K, V, chunk_size, scale,
                           out, out_dtype, stream);
 }
@@ -267,18 +279,19 @@ kda_status kda_recurrent_fwd(const void *q, const void *k, const void *v, kda_dt
                              int num_seqs, int B, int64_t T, int H, int K, int V, float scale, void *out,
                              kda_dtype out_dtype, hipStream_t stream) {
     if (!gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
-    return recurrent_fwd_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), beta, initial_state, final_state,
+    return recurrent_fwd_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), 0u, beta, initial_state, final_state,
                               cu_seqlens, num_seqs, B, T, H, K, V, scale, out, out_dtype, stream);
 }
 
 kda_status kda_recurrent_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
                                         const void *logits, const float *log_scale, const float *bias,
-                                        float lower_bound, const float *beta, const float *initial_state,
+                                        float lower_bound, unsigned flags, const float *beta,
+                                        const float *initial_state,
                                         float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
                                         int64_t T, int H, int K, int V, float scale, void *out,
                                         kda_dtype out_dtype, hipStream_t stream) {
     if (!(lower_bound < 0.f)) return KDA_ERR_BAD_ARGUMENT;
-    return recurrent_fwd_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), beta,
+    return recurrent_fwd_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), flags, beta,
                               initial_state, final_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, out,
                               out_dtype, stream);
 }
@@ -288,17 +301,19 @@ kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_d
                               float *state, int B, int H, int K, int V, float scale, void *out,
                               kda_dtype out_dtype, hipStream_t stream) {
     if (!gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
-    return recurrent_step_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), beta, state, B, H, K, V, scale,
+    return recurrent_step_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), 0u, beta, state, B, H, K, V, scale,
                                out, out_dtype, stream);
 }
 
 kda_status kda_recurrent_step_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
                                          const void *logits, const float *log_scale, const float *bias,
-                                         float lower_bound, const float *beta, float *state, int B, int H,
+                                         float lower_bound, unsigned flags, const float *beta, float *state, int B,
+                                         int H,
                                          int K, int V, float scale, void *out, kda_dtype out_dtype,
                                          hipStream_t stream) {
     if (!(lower_bound < 0.f)) return KDA_ERR_BAD_ARGUMENT;
-    return recurrent_step_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), beta, state,
+    return recurrent_step_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), flags, beta,
+                               state,
                                B, H, K, V, scale, out, out_dtype, stream);
 }
 

@@ -1,6 +1,7 @@
 // kda_chunk.hip -- chunkwise prefill entry into the kernels of kda_chunk_kernel.h, with
 // the gate given as a float32 tensor (alpha or ln alpha); a gate given as logits goes
-// to the instantiations in kda_chunk_logits.hip.
+// to the instantiations in kda_chunk_logits.hip (and kda_chunk_logits_norm.hip when q
+// and k are normalised in the kernel).
 #include "kda_chunk_kernel.h"
 
 namespace kda {
@@ -8,16 +9,18 @@ namespace kda {
 int chunk_fwd_value_block(bool fp32_inputs, int K, int V, int C) {
     ChunkArgs q{};  // q == nullptr: query
     int bv = 0;
-    (void)(fp32_inputs ? launch_p<PrecF32, false>(q, K, V, C, 0, nullptr, &bv)
-                       : launch_p<PrecMixed, false>(q, K, V, C, 0, nullptr, &bv));
+    (void)(fp32_inputs ? launch_p<PrecF32, 0>(q, K, V, C, 0, nullptr, &bv)
+                       : launch_p<PrecMixed, 0>(q, K, V, C, 0, nullptr, &bv));
     return bv;
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                             hipStream_t stream, int *bv) {
-    if (a.gate.mode == GATE_LOGITS) return launch_chunk_fwd_logits(a, fp32_inputs, K, V, C, num_pairs, stream, bv);
-    return fp32_inputs ? launch_p<PrecF32, false>(a, K, V, C, num_pairs, stream, bv)
-                       : launch_p<PrecMixed, false>(a, K, V, C, num_pairs, stream, bv);
+    if (a.gate.mode == GATE_LOGITS)
+        return a.qk_l2norm ? launch_chunk_fwd_logits_norm(a, fp32_inputs, K, V, C, num_pairs, stream, bv)
+                           : launch_chunk_fwd_logits(a, fp32_inputs, K, V, C, num_pairs, stream, bv);
+    return fp32_inputs ? launch_p<PrecF32, 0>(a, K, V, C, num_pairs, stream, bv)
+                       : launch_p<PrecMixed, 0>(a, K, V, C, num_pairs, stream, bv);
 }
 
 }  // namespace kda

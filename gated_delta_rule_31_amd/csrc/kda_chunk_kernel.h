@@ -97,7 +97,10 @@ struct Layout {
     static constexpr int NST = sX + NX * 16 * LKS;
     static constexpr size_t oAkk = oSt + al16((size_t)NST * sizeof(TA) * (P::kSplit ? 2 : 1));
     static constexpr size_t oTf = oAkk + al16((size_t)C * LCF * 4);
-    static constexpr size_t oTP = oTf + al16((size_t)C * LCF * 4);
+    // per-row partial sums of q^2 and k^2 from each wave that holds part of a tile's row
+    static constexpr int NPART = K / 2 > 32 ? K / 64 : 1;
+    static constexpr size_t oNrm = oTf + al16((size_t)C * LCF * 4);  // [NP][2][16][NPART]
+    static constexpr size_t oTP = oNrm + al16((size_t)NP * 2 * 16 * NPART * 4);
     static constexpr size_t oBt = oTP + al16((size_t)NP * K * 4);
     static constexpr size_t oPkg = oBt + al16((size_t)C * 4);
     // package (two copies)
@@ -413,10 +416,13 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
         }
 }
 
-// ZG: the gate arrives as logits (GATE_LOGITS) and is evaluated in the prep waves;
-// otherwise it is a float32 tensor of alpha or ln alpha (a.gate.mode).
-template <class P, int K, int V, int C, int BV, bool ZG>
+// GM = 0: the gate is a float32 tensor of alpha or ln alpha (a.gate.mode); GM = 1: it
+// arrives as logits (GATE_LOGITS) and is evaluated in the prep waves; GM = 2: as 1, and q
+// and k are also divided by their L2 norms over K in the prep waves.
+template <class P, int K, int V, int C, int BV, int GM>
 __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
+    constexpr bool ZG = GM >= 1;
+    constexpr bool NORM = GM == 2;
     using L = Layout<P, K, V, C, BV>;
     using TA = typename P::TA;
     using TM = typename P::TM;
@@ -467,8 +473,13 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 f4 x = {0.f, 0.f, 0.f, 0.f};
                 if (jt < L::NJT && s0) {
                     const int vc = vb * BV + jt * 16 + (lane & 15);
+                    if (a.state_vk) {
+                        const float4 y = *reinterpret_cast<const float4 *>(s0 + (int64_t)vc * K + 16 * t + 4 * g);
+                        x[0] = y.x; x[1] = y.y; x[2] = y.z; x[3] = y.w;
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = s0[(int64_t)(16 * t + 4 * g + e) * V + vc];
+                        for (int e = 0; e < 4; ++e) x[e] = s0[(int64_t)(16 * t + 4 * g + e) * V + vc];
+                    }
                 }
                 S[mj][t] = x;
             }
@@ -596,9 +607,15 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 if (jt >= L::NJT) continue;
                 const int vc = vb * BV + jt * 16 + (lane & 15);
 #pragma unroll
-                for (int t = 0; t < NKT_K; ++t)
+                for (int t = 0; t < NKT_K; ++t) {
+                    if (a.state_vk) {
+                        *reinterpret_cast<float4 *>(sf + (int64_t)vc * K + 16 * t + 4 * g) =
+                            float4{S[mj][t][0], S[mj][t][1], S[mj][t][2], S[mj][t][3]};
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sf[(int64_t)(16 * t + 4 * g + e) * V + vc] = S[mj][t][e];
+                        for (int e = 0; e < 4; ++e) sf[(int64_t)(16 * t + 4 * g + e) * V + vc] = S[mj][t][e];
+                    }
+                }
             }
         }
         return;
@@ -611,6 +628,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     TA *St = reinterpret_cast<TA *>(smem + L::oSt);         // Lq, Rd, Ro, X (+ low parts)
     float *TPv = reinterpret_cast<float *>(smem + L::oTP);  // [NP][K] tile decay products
     float *Btv = reinterpret_cast<float *>(smem + L::oBt);  // [C] beta of the chunk
+    float *Nrm = reinterpret_cast<float *>(smem + L::oNrm); // row-norm partials
 
     // The strictly upper 16x16 blocks of T and A_qk are zero in every chunk: write them
     // once, in both package buffers.  (The state waves first read a package after the
@@ -768,8 +786,40 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     const int c0 = 2 * (cm % NCP);
                     *reinterpret_cast<float2 *>(TPv + p * K + c0) = float2{run.x * oth.x, run.y * oth.y};
                 }
+                if constexpr (NORM) {
+                    // row sums of q^2 and k^2 over this wave's share of the row: the lanes of
+                    // one tile are NG consecutive lanes of the half-wave
+                    constexpr int NG = NCP < 32 ? NCP : 32;
+                    float sq[8], sk[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        float q0, q1, k0, k1;
+                        pair_f32(rq[u][i], q0, q1);
+                        pair_f32(rk[u][i], k0, k1);
+                        sq[i] = q0 * q0 + q1 * q1;
+                        sk[i] = k0 * k0 + k1 * k1;
+                    }
+#pragma unroll
+                    for (int m = 1; m < NG; m <<= 1)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            sq[i] += __shfl_xor(sq[i], m);
+                            sk[i] += __shfl_xor(sk[i], m);
+                        }
+                    if ((lane & (NG - 1)) == 0 && cm < NCOMBO) {
+                        const int part = (cm % NCP) / 32;  // which wave's share of the row
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            Nrm[((p * 2 + 0) * 16 + 8 * hf + i) * L::NPART + part] = sq[i];
+                            Nrm[((p * 2 + 1) * 16 + 8 * hf + i) * L::NPART + part] = sk[i];
+                        }
+                    }
+                }
             }
-            if (tp < C) Btv[tp] = tp < n_it ? rbeta : 0.f;
+            if (tp < C) {
+                const float b = a.beta_logits ? 1.f / (1.f + __expf(-rbeta)) : rbeta;
+                Btv[tp] = tp < n_it ? b : 0.f;
+            }
         }
         lds_barrier();  // B1
         // ---- phase 1b: A-matrix operand staging of chunk `it` ---------------------------
@@ -829,6 +879,22 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 float2 pre = pin[u];  // gamma_i / R_p
                 keR[u] = eR;
                 keCE[u] = eCE;
+                float iq[8], ik[8];  // reciprocal row norms of q and k (1 without normalisation)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    iq[i] = 1.f;
+                    ik[i] = 1.f;
+                    if constexpr (NORM) {
+                        float nq = 0.f, nk = 0.f;
+#pragma unroll
+                        for (int w = 0; w < L::NPART; ++w) {
+                            nq += Nrm[((p * 2 + 0) * 16 + 8 * hf + i) * L::NPART + w];
+                            nk += Nrm[((p * 2 + 1) * 16 + 8 * hf + i) * L::NPART + w];
+                        }
+                        iq[i] = 1.f / fmaxf(sqrtf(nq), 1e-6f);
+                        ik[i] = 1.f / fmaxf(sqrtf(nk), 1e-6f);
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int r = 16 * p + 8 * hf + i;
@@ -838,6 +904,12 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     float q0, q1, k0, k1;
                     pair_f32(rq[u][i], q0, q1);
                     pair_f32(rk[u][i], k0, k1);
+                    if constexpr (NORM) {
+                        q0 *= iq[i];
+                        q1 *= iq[i];
+                        k0 *= ik[i];
+                        k1 *= ik[i];
+                    }
                     if (!ok) q0 = q1 = k0 = k1 = 0.f;
                     const float2 lq = {q0 * pre.x, q1 * pre.y};
                     const float2 lk = {bet[i] * k0 * pre.x, bet[i] * k1 * pre.y};
@@ -921,14 +993,14 @@ constexpr int pick_bv() {
     else return 0;
 }
 
-template <class P, bool ZG, int K, int V, int C>
+template <class P, int GM, int K, int V, int C>
 hipError_t launch_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream, int *bv_out) {
     constexpr int BV = pick_bv<P, K, V, C>();
     if constexpr (BV == 0) {
         return hipErrorNotSupported;
     } else {
         using L = Layout<P, K, V, C, BV>;
-        auto kern = chunk_fwd_kernel<P, K, V, C, BV, ZG>;
+        auto kern = chunk_fwd_kernel<P, K, V, C, BV, GM>;
         static bool attr_set = false;  // per instantiation, once per process
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -943,7 +1015,7 @@ hipError_t launch_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream, int
     }
 }
 
-template <class P, bool ZG, int K, int V>
+template <class P, int GM, int K, int V>
 hipError_t launch_kv(const ChunkArgs &a, int C, int num_pairs, hipStream_t stream, int *bv) {
     if (!a.q) {  // query only: report the value block, launch nothing
         const int b = C == 16 ? pick_bv<P, K, V, 16>() : C == 32 ? pick_bv<P, K, V, 32>()
@@ -952,31 +1024,31 @@ hipError_t launch_kv(const ChunkArgs &a, int C, int num_pairs, hipStream_t strea
         return b ? hipSuccess : hipErrorNotSupported;
     }
     switch (C) {
-        case 16: return launch_kvc<P, ZG, K, V, 16>(a, num_pairs, stream, bv);
-        case 32: return launch_kvc<P, ZG, K, V, 32>(a, num_pairs, stream, bv);
-        case 64: return launch_kvc<P, ZG, K, V, 64>(a, num_pairs, stream, bv);
+        case 16: return launch_kvc<P, GM, K, V, 16>(a, num_pairs, stream, bv);
+        case 32: return launch_kvc<P, GM, K, V, 32>(a, num_pairs, stream, bv);
+        case 64: return launch_kvc<P, GM, K, V, 64>(a, num_pairs, stream, bv);
         default: return hipErrorNotSupported;
     }
 }
 
-template <class P, bool ZG, int K>
+template <class P, int GM, int K>
 hipError_t launch_k(const ChunkArgs &a, int V, int C, int num_pairs, hipStream_t stream, int *bv) {
     switch (V) {
-        case 16: return launch_kv<P, ZG, K, 16>(a, C, num_pairs, stream, bv);
-        case 32: return launch_kv<P, ZG, K, 32>(a, C, num_pairs, stream, bv);
-        case 64: return launch_kv<P, ZG, K, 64>(a, C, num_pairs, stream, bv);
-        case 128: return launch_kv<P, ZG, K, 128>(a, C, num_pairs, stream, bv);
+        case 16: return launch_kv<P, GM, K, 16>(a, C, num_pairs, stream, bv);
+        case 32: return launch_kv<P, GM, K, 32>(a, C, num_pairs, stream, bv);
+        case 64: return launch_kv<P, GM, K, 64>(a, C, num_pairs, stream, bv);
+        case 128: return launch_kv<P, GM, K, 128>(a, C, num_pairs, stream, bv);
         default: return hipErrorNotSupported;
     }
 }
 
-template <class P, bool ZG>
+template <class P, int GM>
 hipError_t launch_p(const ChunkArgs &a, int K, int V, int C, int num_pairs, hipStream_t stream, int *bv) {
     switch (K) {
-        case 16: return launch_k<P, ZG, 16>(a, V, C, num_pairs, stream, bv);
-        case 32: return launch_k<P, ZG, 32>(a, V, C, num_pairs, stream, bv);
-        case 64: return launch_k<P, ZG, 64>(a, V, C, num_pairs, stream, bv);
-        case 128: return launch_k<P, ZG, 128>(a, V, C, num_pairs, stream, bv);
+        case 16: return launch_k<P, GM, 16>(a, V, C, num_pairs, stream, bv);
+        case 32: return launch_k<P, GM, 32>(a, V, C, num_pairs, stream, bv);
+        case 64: return launch_k<P, GM, 64>(a, V, C, num_pairs, stream, bv);
+        case 128: return launch_k<P, GM, 128>(a, V, C, num_pairs, stream, bv);
         default: return hipErrorNotSupported;
     }
 }

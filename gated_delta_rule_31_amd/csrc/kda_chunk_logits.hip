@@ -6,8 +6,8 @@ namespace kda {
 
 hipError_t launch_chunk_fwd_logits(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                                    hipStream_t stream, int *bv) {
-    return fp32_inputs ? launch_p<PrecF32, true>(a, K, V, C, num_pairs, stream, bv)
-                       : launch_p<PrecMixed, true>(a, K, V, C, num_pairs, stream, bv);
+    return fp32_inputs ? launch_p<PrecF32, 1>(a, K, V, C, num_pairs, stream, bv)
+                       : launch_p<PrecMixed, 1>(a, K, V, C, num_pairs, stream, bv);
 }
 
 }  // namespace kda

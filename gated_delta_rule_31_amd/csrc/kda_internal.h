@@ -33,6 +33,9 @@ struct ChunkArgs {
     int H;
     int out_bf16;
     float scale;
+    int qk_l2norm;                  // q, k divided by their L2 norm over K in the kernel
+    int beta_logits;                // beta holds logits; the kernel applies sigmoid
+    int state_vk;                   // states are [N, H, V, K] (K contiguous)
 };
 
 struct StepArgs {
@@ -44,6 +47,7 @@ struct StepArgs {
     int H;
     int out_bf16;
     float scale;
+    int qk_l2norm, beta_logits, state_vk;  // as in ChunkArgs
 };
 
 struct RecurrentArgs {
@@ -58,6 +62,7 @@ struct RecurrentArgs {
     int H;
     int out_bf16;
     float scale;
+    int qk_l2norm, beta_logits, state_vk;  // as in ChunkArgs
 };
 
 struct GateArgs {
@@ -74,7 +79,10 @@ struct GateArgs {
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                             hipStream_t stream, int *bv);
-// the same for a.gate.mode == GATE_LOGITS (kernels that evaluate the gate themselves)
+// the same for a.gate.mode == GATE_LOGITS (kernels that evaluate the gate themselves),
+// without and with the in-kernel L2 normalisation of q and k
+hipError_t launch_chunk_fwd_logits_norm(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
+                                        hipStream_t stream, int *bv);
 hipError_t launch_chunk_fwd_logits(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                                    hipStream_t stream, int *bv);
 // value-block width the chunk kernel uses for this shape, 0 if the shape is not compiled

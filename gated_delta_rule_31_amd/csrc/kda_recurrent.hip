@@ -83,7 +83,8 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
     float S[RQ];
     const float *s0 = a.initial_state ? a.initial_state + ((int64_t)s * H + h) * K * V : nullptr;
 #pragma unroll
-    for (int i = 0; i < RQ; ++i) S[i] = s0 ? s0[(int64_t)(r0 + i) * V + gcol] : 0.f;
+    for (int i = 0; i < RQ; ++i)
+        S[i] = !s0 ? 0.f : a.state_vk ? s0[(int64_t)gcol * K + r0 + i] : s0[(int64_t)(r0 + i) * V + gcol];
 
     const bool glog = a.gate.mode == GATE_LOG;
     float s2 = 0.f, l2 = 0.f;
@@ -146,9 +147,9 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
         for (int w = 0; w < UPT; ++w) {
             const int u = tid + NTH * w;
             const int j = u / UK, c = 8 * (u % UK);
-            const f4x2 kk = to_f4x2(rk[w]), qq = to_f4x2(rq[w]);
+            f4x2 kk = to_f4x2(rk[w]), qq = to_f4x2(rq[w]);
             f4x2 al = to_f4x2(ra[w]);
-            float dot = 0.f;
+            float dot = 0.f, nk = 0.f, nq = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 if constexpr (ZG)
@@ -156,10 +157,25 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
                 else if (glog)
                     al[e] = expf(al[e]);
                 dot += kk[e] * qq[e];
+                nk += kk[e] * kk[e];
+                nq += qq[e] * qq[e];
             }
-            // k.q of the token: the UK units of a row sit in UK consecutive lanes
+            // row sums over the token: the UK units of a row sit in UK consecutive lanes
 #pragma unroll
-            for (int m = 1; m < UK; m <<= 1) dot += __shfl_xor(dot, m);
+            for (int m = 1; m < UK; m <<= 1) {
+                dot += __shfl_xor(dot, m);
+                nk += __shfl_xor(nk, m);
+                nq += __shfl_xor(nq, m);
+            }
+            if (a.qk_l2norm) {
+                const float ik = 1.f / fmaxf(sqrtf(nk), 1e-6f), iq = 1.f / fmaxf(sqrtf(nq), 1e-6f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kk[e] *= ik;
+                    qq[e] *= iq;
+                }
+                dot *= ik * iq;
+            }
             if (u < NU) {
                 *reinterpret_cast<f4x2 *>(&sk[buf][j][c]) = kk;
                 *reinterpret_cast<f4x2 *>(&sq[buf][j][c]) = qq;
@@ -175,7 +191,7 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
                 *reinterpret_cast<f4x2 *>(&sv[buf][j][c]) = to_f4x2(rv[w]);
             }
         }
-        if (tid < TB) sbeta[buf][tid] = rb;
+        if (tid < TB) sbeta[buf][tid] = a.beta_logits ? 1.f / (1.f + __expf(-rb)) : rb;
     };
 
     if (nblk > 0) {
@@ -220,7 +236,12 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
     if (a.final_state) {
         float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
 #pragma unroll
-        for (int i = 0; i < RQ; ++i) sf[(int64_t)(r0 + i) * V + gcol] = S[i];
+        for (int i = 0; i < RQ; ++i) {
+            if (a.state_vk)
+                sf[(int64_t)gcol * K + r0 + i] = S[i];
+            else
+                sf[(int64_t)(r0 + i) * V + gcol] = S[i];
+        }
     }
 }
 

@@ -36,9 +36,9 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
     constexpr int CQ = Cf::CQ, RPT = Cf::RPT, NRG = Cf::NRG;
     __shared__ float red_p[NRG][V];
     __shared__ float red_r[NRG][V];
-    __shared__ float red_kq[NRG];
+    __shared__ float red_kq[3][NRG];  // k.q, k.k, q.q partials
     __shared__ float dlt[V];
-    __shared__ float kq_s;
+    __shared__ float kq_s, ik_s, iq_s;
 
     const int pair = blockIdx.x;  // b * H + h
     const int tid = threadIdx.x;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
     }
 
     float4 pp = {0.f, 0.f, 0.f, 0.f}, rr = {0.f, 0.f, 0.f, 0.f};
-    float kq = 0.f;
+    float kq = 0.f, kk = 0.f, qq = 0.f;
     float kr[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -84,6 +84,8 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
         const float kv = ld_f32(k, row), qv = ld_f32(q, row);
         kr[i] = kv;
         kq += kv * qv;
+        kk += kv * kv;
+        qq += qv * qv;
         s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
         pp.x += s[i].x * kv; pp.y += s[i].y * kv; pp.z += s[i].z * kv; pp.w += s[i].w * kv;
         rr.x += s[i].x * qv; rr.y += s[i].y * qv; rr.z += s[i].z * qv; rr.w += s[i].w * qv;
@@ -92,12 +94,26 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
     red_p[rg][4 * cq + 2] = pp.z; red_p[rg][4 * cq + 3] = pp.w;
     red_r[rg][4 * cq + 0] = rr.x; red_r[rg][4 * cq + 1] = rr.y;
     red_r[rg][4 * cq + 2] = rr.z; red_r[rg][4 * cq + 3] = rr.w;
-    if (cq == 0) red_kq[rg] = kq;
+    if (cq == 0) {
+        red_kq[0][rg] = kq;
+        red_kq[1][rg] = kk;
+        red_kq[2][rg] = qq;
+    }
     __syncthreads();
     if (tid == 0) {
-        float x = 0.f;
-        for (int g2 = 0; g2 < NRG; ++g2) x += red_kq[g2];
-        kq_s = x;
+        float x = 0.f, nk = 0.f, nq = 0.f;
+        for (int g2 = 0; g2 < NRG; ++g2) {
+            x += red_kq[0][g2];
+            nk += red_kq[1][g2];
+            nq += red_kq[2][g2];
+        }
+        // with in-kernel normalisation the reductions above used the raw k and q:
+        // S^T (k/|k|) = (S^T k)/|k|, so only the results are rescaled
+        const float ik = a.qk_l2norm ? 1.f / fmaxf(sqrtf(nk), 1e-6f) : 1.f;
+        const float iq = a.qk_l2norm ? 1.f / fmaxf(sqrtf(nq), 1e-6f) : 1.f;
+        kq_s = x * ik * iq;
+        ik_s = ik;
+        iq_s = iq;
     }
     __syncthreads();
     if (tid < V) {
@@ -106,9 +122,11 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
             p += red_p[g2][tid];
             r += red_r[g2][tid];
         }
-        const float d = a.beta[pair] * (ld_f32(v, tid) - p);
-        dlt[tid] = d;
-        st_out(a.out, a.out_bf16, (int64_t)pair * V + tid, a.scale * (r + kq_s * d));
+        const float bl = a.beta[pair];
+        const float bt = a.beta_logits ? 1.f / (1.f + __expf(-bl)) : bl;
+        const float d = bt * (ld_f32(v, tid) - p * ik_s);
+        dlt[tid] = d * ik_s;  // the state update adds (k/|k|) d^T
+        st_out(a.out, a.out_bf16, (int64_t)pair * V + tid, a.scale * (r * iq_s + kq_s * d));
     }
     __syncthreads();
     const float4 d4 = {dlt[4 * cq], dlt[4 * cq + 1], dlt[4 * cq + 2], dlt[4 * cq + 3]};
@@ -120,17 +138,111 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
     }
 }
 
+// The same step with the state stored [V, K] (K contiguous, the transposed layout some
+// model code keeps): thread (cq, rg) holds keys 4cq..4cq+3 of value rows rg + NRG*i, so
+// the reductions over K run across the CQ consecutive lanes of a row group and every lane
+// ends with the sums it needs; no LDS, no barrier.
+template <typename TIn, int K, int V, bool ZG>
+__global__ __launch_bounds__((StepCfg<V, K>::NT)) void recurrent_step_vk_kernel(StepArgs a) {
+    using Cf = StepCfg<V, K>;  // rows = value rows, float4 groups along K
+    constexpr int CQ = Cf::CQ, RPT = Cf::RPT, NRG = Cf::NRG;
+    static_assert(64 % CQ == 0, "a row group's lanes sit in one wave");
+    const int pair = blockIdx.x;  // b * H + h
+    const int tid = threadIdx.x;
+    const int cq = tid % CQ;      // keys 4*cq .. 4*cq+3
+    const int rg = tid / CQ;      // value rows rg + NRG * i
+    const int h = pair % a.H;
+    const int c0 = 4 * cq;
+    const TIn *q = static_cast<const TIn *>(a.q) + (int64_t)pair * K;
+    const TIn *k = static_cast<const TIn *>(a.k) + (int64_t)pair * K;
+    const TIn *v = static_cast<const TIn *>(a.v) + (int64_t)pair * V;
+    float4 *S = reinterpret_cast<float4 *>(a.state + (int64_t)pair * K * V);
+
+    float4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * CQ + cq]));
+        s[i] = float4{x[0], x[1], x[2], x[3]};
+    }
+    float al[4], kv[4], qv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        kv[e] = ld_f32(k, c0 + e);
+        qv[e] = ld_f32(q, c0 + e);
+        if constexpr (ZG) {
+            const float s2 = expf(a.gate.log_scale[h]) * 1.44269504088896341f;
+            const float l2 = a.gate.lower_bound * 1.44269504088896341f;
+            const float z = ld_f32(static_cast<const TIn *>(a.gate.logits) + (int64_t)pair * K, c0 + e) +
+                            (a.gate.bias ? a.gate.bias[h * K + c0 + e] : 0.f);
+            al[e] = fast_bounded_alpha(z, s2, l2);
+        } else {
+            const float g = a.gate.gate[(int64_t)pair * K + c0 + e];
+            al[e] = a.gate.mode == GATE_LOG ? expf(g) : g;
+        }
+    }
+    float kq = 0.f, nk = 0.f, nq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        kq += kv[e] * qv[e];
+        nk += kv[e] * kv[e];
+        nq += qv[e] * qv[e];
+    }
+#pragma unroll
+    for (int m = 1; m < CQ; m <<= 1) {
+        kq += __shfl_xor(kq, m);
+        nk += __shfl_xor(nk, m);
+        nq += __shfl_xor(nq, m);
+    }
+    const float ik = a.qk_l2norm ? 1.f / fmaxf(sqrtf(nk), 1e-6f) : 1.f;
+    const float iq = a.qk_l2norm ? 1.f / fmaxf(sqrtf(nq), 1e-6f) : 1.f;
+    kq *= ik * iq;
+    const float bl = a.beta[pair];
+    const float bt = a.beta_logits ? 1.f / (1.f + __expf(-bl)) : bl;
+    float p[RPT], r[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        s[i].x *= al[0]; s[i].y *= al[1]; s[i].z *= al[2]; s[i].w *= al[3];
+        p[i] = s[i].x * kv[0] + s[i].y * kv[1] + s[i].z * kv[2] + s[i].w * kv[3];
+        r[i] = s[i].x * qv[0] + s[i].y * qv[1] + s[i].z * qv[2] + s[i].w * qv[3];
+    }
+#pragma unroll
+    for (int m = 1; m < CQ; m <<= 1)
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            p[i] += __shfl_xor(p[i], m);
+            r[i] += __shfl_xor(r[i], m);
+        }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + NRG * i;
+        const float d = bt * (ld_f32(v, row) - p[i] * ik);
+        if (cq == 0) st_out(a.out, a.out_bf16, (int64_t)pair * V + row, a.scale * (r[i] * iq + kq * d));
+        const float dk = d * ik;
+        float4 x = s[i];
+        x.x += kv[0] * dk; x.y += kv[1] * dk; x.z += kv[2] * dk; x.w += kv[3] * dk;
+        __builtin_nontemporal_store(f4{x.x, x.y, x.z, x.w}, reinterpret_cast<f4 *>(&S[row * CQ + cq]));
+    }
+}
+
 template <typename TIn, int K>
 hipError_t launch_k(const StepArgs &a, int V, int pairs, hipStream_t stream) {
     switch (V) {
 #define KDA_STEP_CASE(VV)                                                                         \
     case VV:                                                                                      \
-        if (a.gate.mode == GATE_LOGITS)                                                           \
+        if (a.state_vk) {                                                                         \
+            if (a.gate.mode == GATE_LOGITS)                                                       \
+                hipLaunchKernelGGL((recurrent_step_vk_kernel<TIn, K, VV, true>), dim3(pairs),     \
+                                   dim3(StepCfg<VV, K>::NT), 0, stream, a);                       \
+            else                                                                                  \
+                hipLaunchKernelGGL((recurrent_step_vk_kernel<TIn, K, VV, false>), dim3(pairs),    \
+                                   dim3(StepCfg<VV, K>::NT), 0, stream, a);                       \
+        } else if (a.gate.mode == GATE_LOGITS) {                                                  \
             hipLaunchKernelGGL((recurrent_step_kernel<TIn, K, VV, true>), dim3(pairs),            \
                                dim3(StepCfg<K, VV>::NT), 0, stream, a);                           \
-        else                                                                                      \
+        } else {                                                                                  \
             hipLaunchKernelGGL((recurrent_step_kernel<TIn, K, VV, false>), dim3(pairs),           \
                                dim3(StepCfg<K, VV>::NT), 0, stream, a);                           \
+        }                                                                                         \
         return hipGetLastError();
         KDA_STEP_CASE(16)
         KDA_STEP_CASE(32)

@@ -65,6 +65,19 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * logarithm g = ln(alpha) <= 0. */
 typedef enum { KDA_GATE_ALPHA = 0, KDA_GATE_LOG = 1 } kda_gate_kind;
 
+/* Input preparation the *_fused_gate entry points can do inside the kernels (the model
+ * excerpt on the Kept-memory page asks its kernels for all three; PaperLeet's contract
+ * expects prepared inputs, which is what the plain entry points take).  Bits of `flags`:
+ *   KDA_QK_L2NORM    q and k are divided by their L2 norm over K, x / max(|x|, 1e-6)
+ *                    (the KDARecurrent page's unit normalisation of q and k)
+ *   KDA_BETA_LOGITS  beta holds the write-strength logits; the kernel applies the sigmoid
+ *   KDA_STATE_VK     every state argument is [.., V, K] (K contiguous) instead of
+ *                    [.., K, V] (the transposed storage some model code keeps)
+ * Any other bit set returns KDA_ERR_BAD_ARGUMENT. */
+#define KDA_QK_L2NORM 1u
+#define KDA_BETA_LOGITS 2u
+#define KDA_STATE_VK 4u
+
 /*
  * kda_bounded_decay -- the bounded per-channel decay gate (PaperLeet "Formula and
  * conventions", operator bounded_decay; cheat sheet gate table, Kimi K3 column).
@@ -137,6 +150,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
  *   log_scale [H] float32;  bias [H*K] float32 or NULL
  *   lower_bound  in [-5, 0): the bound itself is the chunk path's precondition
  *                (every log-decay >= -5), so it is checked here (KDA_ERR_BAD_ARGUMENT)
+ *   flags     KDA_QK_L2NORM | KDA_BETA_LOGITS | KDA_STATE_VK or 0 (see above)
  * Every other argument, the supported set and the empty-sequence rule are those of
  * kda_chunk_fwd.  The gate is evaluated in float32 on the hardware exp2/reciprocal
  * (a few ulp from kda_bounded_decay's value), never written to memory, and needs no
@@ -145,7 +159,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
  */
 kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
                                     const void *logits, const float *log_scale, const float *bias,
-                                    float lower_bound, const float *beta, const float *initial_state,
+                                    float lower_bound, unsigned flags, const float *beta, const float *initial_state,
                                     float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
                                     int64_t T, int H, int K, int V, int chunk_size, float scale, void *out,
                                     kda_dtype out_dtype, hipStream_t stream);
@@ -169,11 +183,12 @@ kda_status kda_recurrent_fwd(const void *q, const void *k, const void *v, kda_dt
 /*
  * kda_recurrent_fwd_fused_gate -- kda_recurrent_fwd with the gate evaluated inside the
  * kernel from logits [B, T, H, K] (in in_dtype), log_scale [H], bias [H*K] or NULL and
- * any lower_bound < 0 (the formula of kda_chunk_fwd_fused_gate).
+ * any lower_bound < 0 (the formula of kda_chunk_fwd_fused_gate); `flags` as there.
  */
 kda_status kda_recurrent_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
                                         const void *logits, const float *log_scale, const float *bias,
-                                        float lower_bound, const float *beta, const float *initial_state,
+                                        float lower_bound, unsigned flags, const float *beta,
+                                        const float *initial_state,
                                         float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
                                         int64_t T, int H, int K, int V, float scale, void *out,
                                         kda_dtype out_dtype, hipStream_t stream);
@@ -199,13 +214,15 @@ kda_status kda_recurrent_step(const void *q, const void *k, const void *v, kda_d
 /*
  * kda_recurrent_step_fused_gate -- kda_recurrent_step with the gate applied inside the
  * kernel from logits [B, H, K] (in in_dtype), log_scale [H], bias [H*K] or NULL and
- * lower_bound < 0 (any value: the step accepts every alpha in [0, 1]); the formula is
- * that of kda_chunk_fwd_fused_gate.  The state is updated in place as in
+ * lower_bound < 0 (any value: the step accepts every alpha in [0, 1]); the formula and
+ * `flags` are those of kda_chunk_fwd_fused_gate (with KDA_STATE_VK the state is
+ * [B, H, V, K]).  The state is updated in place as in
  * kda_recurrent_step.
  */
 kda_status kda_recurrent_step_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
                                          const void *logits, const float *log_scale, const float *bias,
-                                         float lower_bound, const float *beta, float *state, int B, int H,
+                                         float lower_bound, unsigned flags, const float *beta, float *state, int B,
+                                         int H,
                                          int K, int V, float scale, void *out, kda_dtype out_dtype,
                                          hipStream_t stream);
 

@@ -105,11 +105,12 @@ def test_fused_gate_validation(lib):
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     f = lib.kda_chunk_fwd_fused_gate
     f.restype = i32
-    f.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32, i32, i32, i32,
-                  f32, vp, i32, vp]
+    u32 = ctypes.c_uint
+    f.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32, i32, i32,
+                  i32, f32, vp, i32, vp]
 
-    def chunk(z=4, ls=8, bias=None, lb=-5.0, out=6, K=16):
-        return f(1, 2, 3, 1, z, ls, bias, lb, 5, None, None, None, 0, 1, 64, 2, K, 16, 16, 1.0, out, 1, None)
+    def chunk(z=4, ls=8, bias=None, lb=-5.0, out=6, K=16, flags=0):
+        return f(1, 2, 3, 1, z, ls, bias, lb, flags, 5, None, None, None, 0, 1, 64, 2, K, 16, 16, 1.0, out, 1, None)
     assert chunk(lb=0.0) == 5        # lower bound must be negative
     assert chunk(lb=-6.0) == 5       # and >= -5 on the chunk path (the tile rescale bound)
     assert chunk(z=None) == 1        # NULL logits
@@ -117,13 +118,15 @@ def test_fused_gate_validation(lib):
     assert chunk(out=4) == 6         # out aliases the logits
     assert chunk(out=8) == 6         # out aliases log_scale
     assert chunk(K=24) == 4          # unsupported width
+    assert chunk(flags=8) == 5       # unknown preparation flag
     g = lib.kda_recurrent_step_fused_gate
     g.restype = i32
-    g.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp]
-    assert g(1, 2, 3, 1, 4, 8, None, 0.0, 5, 16, 2, 2, 16, 16, 1.0, 7, 1, None) == 5   # lower bound >= 0
-    assert g(1, 2, 3, 1, 4, 8, None, -9.0, 5, None, 2, 2, 16, 16, 1.0, 7, 1, None) == 1  # any bound; NULL state
-    assert g(1, 2, 3, 1, None, 8, None, -5.0, 5, 16, 2, 2, 16, 16, 1.0, 7, 1, None) == 1  # NULL logits
-    assert g(1, 2, 3, 1, 4, 8, None, -5.0, 5, 16, 2, 2, 16, 16, 1.0, 4, 1, None) == 6   # out aliases logits
+    g.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp]
+    assert g(1, 2, 3, 1, 4, 8, None, 0.0, 0, 5, 16, 2, 2, 16, 16, 1.0, 7, 1, None) == 5   # lower bound >= 0
+    assert g(1, 2, 3, 1, 4, 8, None, -9.0, 0, 5, None, 2, 2, 16, 16, 1.0, 7, 1, None) == 1  # any bound; NULL state
+    assert g(1, 2, 3, 1, None, 8, None, -5.0, 0, 5, 16, 2, 2, 16, 16, 1.0, 7, 1, None) == 1  # NULL logits
+    assert g(1, 2, 3, 1, 4, 8, None, -5.0, 0, 5, 16, 2, 2, 16, 16, 1.0, 4, 1, None) == 6   # out aliases logits
+    assert g(1, 2, 3, 1, 4, 8, None, -5.0, 16, 5, 16, 2, 2, 16, 16, 1.0, 7, 1, None) == 5  # unknown flag
 
 
 def test_recurrent_fwd_validation(lib):
@@ -145,7 +148,7 @@ def test_recurrent_fwd_validation(lib):
     assert call(T=0, q=None, out=None) == 0   # empty: nothing to do without a final state
     g = lib.kda_recurrent_fwd_fused_gate
     g.restype = i32
-    g.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32, i32, i32, f32,
-                  vp, i32, vp]
-    assert g(1, 2, 3, 1, 4, 8, None, 0.0, 5, None, None, None, 0, 1, 8, 2, 16, 16, 1.0, 6, 1, None) == 5
-    assert g(1, 2, 3, 1, 4, None, None, -9.0, 5, None, None, None, 0, 1, 8, 2, 16, 16, 1.0, 6, 1, None) == 1
+    g.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, ctypes.c_uint, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32,
+                  i32, i32, f32, vp, i32, vp]
+    assert g(1, 2, 3, 1, 4, 8, None, 0.0, 0, 5, None, None, None, 0, 1, 8, 2, 16, 16, 1.0, 6, 1, None) == 5
+    assert g(1, 2, 3, 1, 4, None, None, -9.0, 0, 5, None, None, None, 0, 1, 8, 2, 16, 16, 1.0, 6, 1, None) == 1

@@ -477,6 +477,115 @@ def test_short_prompts_full_size_sampled():
         assert_close(f[b:b + 1, h:h + 1], ef, False, "state (b=%d h=%d)" % (b, h))
 
 
+# ---- input preparation inside the kernels (q/k unit norm, beta sigmoid, [V,K] states) ----
+
+def _raw_inputs(B, T, H, K, V, dtype, seed, seqlens=None):
+    """Unprepared inputs: q, k not normalised (norms spread over two decades), beta as
+    logits, states in [.., V, K] order."""
+    g = torch.Generator().manual_seed(seed)
+    n = lambda *shape: torch.randn(*shape, generator=g)
+    q = n(B, T, H, K) * torch.exp(n(B, T, H, 1))
+    k = n(B, T, H, K) * torch.exp(n(B, T, H, 1))
+    v, z = n(B, T, H, V), n(B, T, H, K)
+    bl = n(B, T, H)
+    N = B if seqlens is None else len(seqlens)
+    s0_vk = 0.1 * n(N, H, V, K)
+    cu = None
+    if seqlens is not None:
+        cu = torch.zeros(len(seqlens) + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(seqlens), 0).to(torch.int32)
+    ls = 0.5 * n(H)
+    return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), z=z.to(dtype), beta_logits=bl, s0_vk=s0_vk,
+                cu=cu, log_scale=ls)
+
+
+def _oracle_prepared(r, qk_norm=True, beta_sig=True):
+    """The oracle on the inputs prepared as the pages describe (unit-norm q, k over the
+    feature axis; beta = sigmoid of its logits), states back in [.., K, V] order."""
+    q, k = f64(r["q"]), f64(r["k"])
+    if qk_norm:
+        q = q / np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), 1e-6)
+        k = k / np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), 1e-6)
+    b = f64(r["beta_logits"])
+    beta = 1.0 / (1.0 + np.exp(-b)) if beta_sig else b
+    alpha = oracle.bounded_decay(f64(r["z"]), f64(r["log_scale"]), g_min=-5.0)
+    s0 = np.swapaxes(f64(r["s0_vk"]), -1, -2)
+    cu = None if r["cu"] is None else f64(r["cu"]).astype(np.int64)
+    o, f = oracle.scan(q, k, f64(r["v"]), alpha, beta, s0, cu_seqlens=cu)
+    return o, np.swapaxes(f, -1, -2)
+
+
+@pytest.mark.parametrize("dtype,K,V,C", [(torch.float32, 64, 32, 32), (torch.bfloat16, 128, 128, 32),
+                                         (torch.bfloat16, 32, 64, 64)])
+def test_prepared_in_kernel_chunk(dtype, K, V, C):
+    _case("in-kernel preparation, chunk %s K=%d V=%d C=%d" % (dtype, K, V, C))
+    r = _raw_inputs(2, 70, 3, K, V, dtype, seed=K + V)
+    d = lambda x: None if x is None else x.cuda()
+    o, f = kda.chunk_fwd_fused_gate(d(r["q"]), d(r["k"]), d(r["v"]), d(r["z"]), d(r["log_scale"]),
+                                    d(r["beta_logits"]), initial_state=d(r["s0_vk"]), chunk_size=C,
+                                    out_dtype=torch.float32, qk_l2norm=True, beta_logits=True, state_vk=True)
+    eo, ef = _oracle_prepared(r)
+    fp32 = dtype == torch.float32
+    assert_close(o, eo, fp32, "out")
+    assert_close(f, ef, fp32, "final state [V,K]")
+
+
+def test_prepared_in_kernel_chunk_varlen_separate_flags():
+    _case("in-kernel preparation, chunk varlen, flags one at a time")
+    lens = [33, 0, 70]
+    r = _raw_inputs(1, sum(lens), 2, 64, 64, torch.bfloat16, seed=5, seqlens=lens)
+    d = lambda x: None if x is None else x.cuda()
+    # state layout only (q, k already unit-norm, beta already a probability)
+    rq = dict(r)
+    rq["q"] = (r["q"].float() / r["q"].float().norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    rq["k"] = (r["k"].float() / r["k"].float().norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    rq["beta_logits"] = torch.sigmoid(r["beta_logits"])
+    o, f = kda.chunk_fwd_fused_gate(d(rq["q"]), d(rq["k"]), d(r["v"]), d(r["z"]), d(r["log_scale"]),
+                                    d(rq["beta_logits"]), initial_state=d(r["s0_vk"]), cu_seqlens=d(r["cu"]),
+                                    chunk_size=32, out_dtype=torch.float32, state_vk=True)
+    eo, ef = _oracle_prepared(rq, qk_norm=False, beta_sig=False)
+    assert_close(o, eo, False, "out (state layout only)")
+    assert_close(f, ef, False, "final states (state layout only)")
+    # normalisation only, [K,V] states
+    o, f = kda.chunk_fwd_fused_gate(d(r["q"]), d(r["k"]), d(r["v"]), d(r["z"]), d(r["log_scale"]),
+                                    d(rq["beta_logits"]), initial_state=d(r["s0_vk"].transpose(-1, -2).contiguous()),
+                                    cu_seqlens=d(r["cu"]), chunk_size=32, out_dtype=torch.float32, qk_l2norm=True)
+    eo, ef = _oracle_prepared(dict(r, beta_logits=rq["beta_logits"]), beta_sig=False)
+    assert_close(o, eo, False, "out (normalisation only)")
+    assert_close(f.transpose(-1, -2), ef, False, "final states (normalisation only)")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prepared_in_kernel_recurrent(dtype):
+    _case("in-kernel preparation, recurrent %s" % dtype)
+    r = _raw_inputs(2, 21, 3, 128, 64, dtype, seed=31)
+    d = lambda x: None if x is None else x.cuda()
+    o, f = kda.recurrent_fwd_fused_gate(d(r["q"]), d(r["k"]), d(r["v"]), d(r["z"]), d(r["log_scale"]),
+                                        d(r["beta_logits"]), initial_state=d(r["s0_vk"]), out_dtype=torch.float32,
+                                        qk_l2norm=True, beta_logits=True, state_vk=True)
+    eo, ef = _oracle_prepared(r)
+    fp32 = dtype == torch.float32
+    assert_close(o, eo, fp32, "out")
+    assert_close(f, ef, fp32, "final state [V,K]")
+
+
+@pytest.mark.parametrize("state_vk", [False, True])
+@pytest.mark.parametrize("K,V", [(128, 128), (16, 64), (64, 16)])
+def test_prepared_in_kernel_step(state_vk, K, V):
+    _case("in-kernel preparation, decode step K=%d V=%d vk=%s" % (K, V, state_vk))
+    r = _raw_inputs(3, 6, 2, K, V, torch.bfloat16, seed=K * 3 + V)
+    d = lambda x: x.cuda()
+    st = d(r["s0_vk"]) if state_vk else d(r["s0_vk"].transpose(-1, -2).contiguous())
+    outs = [kda.recurrent_step_fused_gate(d(r["q"][:, t]), d(r["k"][:, t]), d(r["v"][:, t]), d(r["z"][:, t]),
+                                          d(r["log_scale"]), d(r["beta_logits"][:, t]), st,
+                                          out_dtype=torch.float32, qk_l2norm=True, beta_logits=True,
+                                          state_vk=state_vk) for t in range(6)]
+    eo, ef = _oracle_prepared(r)
+    o = torch.stack(outs, 1)
+    assert_close(o, eo, False, "outs")
+    assert_close(st if state_vk else st.transpose(-1, -2), ef, False, "state")
+
+
 # ---- full-size workloads, sampled ------------------------------------------------------
 
 def test_k3_prefill_full_size_sampled_heads():
