@@ -228,6 +228,32 @@ def main():
         "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
     }
+    if fused:
+        # the same layer with the model's in-kernel input preparation: q/k unit norm, beta
+        # from its logits, state stored [V,K]
+        bl = torch.logit(beta)
+        fin_vk = torch.empty(B, H, V, K, dtype=torch.float32, device=dev)
+
+        def pstep():
+            kda.chunk_fwd_fused_gate(q, k, v, z, ls, bl, lower_bound=-5.0, chunk_size=args.chunk, out=out,
+                                     final_state=fin_vk, qk_l2norm=True, beta_logits=True, state_vk=True)
+        pstep()
+        torch.cuda.synchronize()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a_, b_ in pev:
+            a_.record(stream)
+            pstep()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        p_ms = sum(a_.elapsed_time(b_) for a_, b_ in pev) / len(pev)
+        p_gbs = alg_bytes / (p_ms * 1e-3) / 1e9
+        log("prefill with in-kernel preparation: %.3f ms" % p_ms)
+        result["prefill_prepared_in_kernel"] = {
+            "workload": "k3_prefill_B1_T8192_H96_K128_V128", "call": "chunk_fwd_fused_gate(qk_l2norm, beta_logits, "
+            "state_vk)", "tokens_per_s": B * T / (p_ms * 1e-3), "launch_ms": p_ms,
+            "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": p_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg_bytes}}
+        del bl, fin_vk
     del g, out
 
     # ---------------- decode ------------------------------------------------------------
@@ -297,6 +323,26 @@ def main():
         torch.cuda.synchronize()
         copy_ms = sum(a_.elapsed_time(b_) for a_, b_ in cev) / len(cev)
         result["decode"]["device_copy_GBps_same_bytes"] = 2 * half / (copy_ms * 1e-3) / 1e9
+        if fused:
+            # the step with the model's in-kernel preparation and the state stored [V,K]
+            st_vk = state.transpose(-1, -2).contiguous()
+            blog = torch.logit(dec.beta)
+            vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
+            for t, (a_, b_) in enumerate(vev):
+                a_.record(stream)
+                kda.recurrent_step_fused_gate(dec.q[t], dec.k[t], dec.v[t], dec.z[t], dec.log_scale, blog[t], st_vk,
+                                              out=od, qk_l2norm=True, beta_logits=True, state_vk=True)
+                b_.record(stream)
+            torch.cuda.synchronize()
+            v_us = sum(a_.elapsed_time(b_) for a_, b_ in vev[4:]) / (len(vev) - 4) * 1e3
+            v_gbs = d_bytes / (v_us * 1e-6) / 1e9
+            log("decode with in-kernel preparation, [V,K] state: %.1f us per step" % v_us)
+            result["decode_prepared_in_kernel"] = {
+                "workload": "decode_B64_H96_K128_V128", "call": "recurrent_step_fused_gate(qk_l2norm, beta_logits, "
+                "state_vk)", "launch_us_avg": v_us,
+                "roofline": {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": v_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": d_bytes}}
+            del st_vk, blog
         del dec, state, src, dst
 
     # ---------------- short continuations: the token-recurrent prefill ------------------

@@ -349,11 +349,33 @@ __device__ __forceinline__ f4 unit_lower_inverse16(const f4 a, int lane) {
     return mma16_reg<T>(Mr, Dc);
 }
 
+// One step of a recursive-halving sum over lanes: lanes with bit M set keep the upper
+// HALF of their 2*HALF partial sums, the others the lower half, and each adds what the
+// partner (lane ^ M) sends of the same half.  Compile-time sizes keep every array index
+// static (a select between two indices would become a dynamic index into the array).
+template <int HALF, bool ON, int M>
+__device__ __forceinline__ void halve_sums(float (&x)[16], int lane, int &base) {
+    if constexpr (ON) {
+        const bool up = (lane & M) != 0;
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            const float lo = x[i], hi = x[i + HALF];
+            const float keep = up ? hi : lo;
+            const float send = up ? lo : hi;
+            x[i] = keep + __shfl_xor(send, M);
+        }
+        base += up ? HALF : 0;
+    }
+}
+
 // The A-matrix work of one chunk, shared out over four waves (w = 0..3).  Wave p % 4
 // computes A_kk's diagonal tile p and inverts I + A_pp, giving T's diagonal block p; the off-diagonal A_kk tiles (kept in fp32 for T's off-diagonal
 // blocks) and the lower A_qk tiles are dealt round-robin after them.  Reads the operand
 // staging of the chunk; writes Akk, Tf and the Tm / Aqk tiles of package `pk`.
-template <class P, int K, int V, int C, int BV>
+// With NORM the staged operands carry the raw q and k; the tiles are scaled by the
+// reciprocal row norms (A_kk[i,j] by 1/(|k_i||k_j|), A_qk[i,j] by 1/(|q_i||k_j|)),
+// which the prep waves left in LDS as per-wave partial sums of squares.
+template <class P, int K, int V, int C, int BV, bool NORM>
 __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char *pk, int w, int lane) {
     using L = Layout<P, K, V, C, BV>;
     using TA = typename P::TA;
@@ -366,6 +388,14 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
     float *Tf = reinterpret_cast<float *>(smem + L::oTf);
     TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
     TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
+    const float *Nrm = reinterpret_cast<const float *>(smem + L::oNrm);
+    // 1 / max(|x_r|, 1e-6) of chunk row r, for x = q (qk = 0) or k (qk = 1)
+    auto inv_norm = [&](int qk, int r) -> float {
+        float n = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < L::NPART; ++pt) n += Nrm[(((r >> 4) * 2 + qk) * 16 + (r & 15)) * L::NPART + pt];
+        return __builtin_amdgcn_rsqf(fmaxf(n, 1e-12f));
+    };
     // right operand of tile (p, qt)
     auto right_of = [&](int p, int qt) -> const TA * {
         if (qt == p) return St + L::sRd + qt * 16 * L::LKS;
@@ -379,6 +409,11 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
         if ((p & 3) != w) continue;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
         mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, p), L::LKS, 0, lane);
+        if constexpr (NORM) {
+            const float cj = inv_norm(1, p * 16 + (lane & 15));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] *= cj * inv_norm(1, p * 16 + 4 * g + e);
+        }
         const f4 t = unit_lower_inverse16<TM>(acc, lane);
         const int j = lane & 15;
 #pragma unroll
@@ -399,6 +434,11 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
             f4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKS, 0, lane);
             const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+            if constexpr (NORM) {
+                const float cj = inv_norm(1, j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= cj * inv_norm(1, i0 + e);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) Akk[(i0 + e) * L::LCF + j] = acc[e];
         }
@@ -411,6 +451,11 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
             f4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_stage<P, P::kSplit, K>(acc, St + L::sLq + p * 16 * L::LKS, L::LKS, right_of(p, qt), L::LKS, L::NST, lane);
             const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+            if constexpr (NORM) {
+                const float cj = inv_norm(1, j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= cj * inv_norm(0, i0 + e);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) Aqk[(i0 + e) * L::LCM + j] = from_f32<TM>((j <= i0 + e) ? acc[e] : 0.f);
         }
@@ -596,7 +641,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 }
             }
             lds_barrier();  // B2: prep waves have written the A-matrix operands
-            if (it < nchunks) a_matrix_work<P, K, V, C, BV>(smem, pkg(it & 1), wave, lane);
+            if (it < nchunks) a_matrix_work<P, K, V, C, BV, NORM>(smem, pkg(it & 1), wave, lane);
             lds_barrier();  // B3: the next package is complete
         }
         if (a.final_state) {
@@ -786,35 +831,6 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     const int c0 = 2 * (cm % NCP);
                     *reinterpret_cast<float2 *>(TPv + p * K + c0) = float2{run.x * oth.x, run.y * oth.y};
                 }
-                if constexpr (NORM) {
-                    // row sums of q^2 and k^2 over this wave's share of the row: the lanes of
-                    // one tile are NG consecutive lanes of the half-wave
-                    constexpr int NG = NCP < 32 ? NCP : 32;
-                    float sq[8], sk[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        float q0, q1, k0, k1;
-                        pair_f32(rq[u][i], q0, q1);
-                        pair_f32(rk[u][i], k0, k1);
-                        sq[i] = q0 * q0 + q1 * q1;
-                        sk[i] = k0 * k0 + k1 * k1;
-                    }
-#pragma unroll
-                    for (int m = 1; m < NG; m <<= 1)
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            sq[i] += __shfl_xor(sq[i], m);
-                            sk[i] += __shfl_xor(sk[i], m);
-                        }
-                    if ((lane & (NG - 1)) == 0 && cm < NCOMBO) {
-                        const int part = (cm % NCP) / 32;  // which wave's share of the row
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            Nrm[((p * 2 + 0) * 16 + 8 * hf + i) * L::NPART + part] = sq[i];
-                            Nrm[((p * 2 + 1) * 16 + 8 * hf + i) * L::NPART + part] = sk[i];
-                        }
-                    }
-                }
             }
             if (tp < C) {
                 const float b = a.beta_logits ? 1.f / (1.f + __expf(-rbeta)) : rbeta;
@@ -879,22 +895,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 float2 pre = pin[u];  // gamma_i / R_p
                 keR[u] = eR;
                 keCE[u] = eCE;
-                float iq[8], ik[8];  // reciprocal row norms of q and k (1 without normalisation)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    iq[i] = 1.f;
-                    ik[i] = 1.f;
-                    if constexpr (NORM) {
-                        float nq = 0.f, nk = 0.f;
-#pragma unroll
-                        for (int w = 0; w < L::NPART; ++w) {
-                            nq += Nrm[((p * 2 + 0) * 16 + 8 * hf + i) * L::NPART + w];
-                            nk += Nrm[((p * 2 + 1) * 16 + 8 * hf + i) * L::NPART + w];
-                        }
-                        iq[i] = 1.f / fmaxf(sqrtf(nq), 1e-6f);
-                        ik[i] = 1.f / fmaxf(sqrtf(nk), 1e-6f);
-                    }
-                }
+                float x2[16];  // with NORM: this thread's share of the row sums of q^2 (0..7), k^2
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int r = 16 * p + 8 * hf + i;
@@ -904,13 +905,11 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     float q0, q1, k0, k1;
                     pair_f32(rq[u][i], q0, q1);
                     pair_f32(rk[u][i], k0, k1);
-                    if constexpr (NORM) {
-                        q0 *= iq[i];
-                        q1 *= iq[i];
-                        k0 *= ik[i];
-                        k1 *= ik[i];
-                    }
                     if (!ok) q0 = q1 = k0 = k1 = 0.f;
+                    if constexpr (NORM) {
+                        x2[i] = q0 * q0 + q1 * q1;
+                        x2[8 + i] = k0 * k0 + k1 * k1;
+                    }
                     const float2 lq = {q0 * pre.x, q1 * pre.y};
                     const float2 lk = {bet[i] * k0 * pre.x, bet[i] * k1 * pre.y};
                     const float2 ro = {k0 * suf[i].x, k1 * suf[i].y};  // k E_p / gamma <= |k|
@@ -932,6 +931,29 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     kq[u][i] = lq;
                     kk[u][i] = lk;
                     kr[u][i] = ro;
+                }
+                if constexpr (NORM) {
+                    // sum the row shares over the NG lanes of this tile in this half-wave by
+                    // recursive halving (each exchange keeps half of the remaining sums and
+                    // adds the partner's half: 16 sums over 32 lanes in 16 exchanges); the
+                    // waves' partial sums meet in LDS
+                    constexpr int NG = NCP < 32 ? NCP : 32;
+                    constexpr int NH = NG >= 16 ? 4 : NG == 8 ? 3 : NG == 4 ? 2 : 1;
+                    int base = 0;  // index of x2[0] among the 16 sums
+                    halve_sums<8, (NH > 0), NG / 2>(x2, lane, base);
+                    halve_sums<4, (NH > 1), NG / 4>(x2, lane, base);
+                    halve_sums<2, (NH > 2), NG / 8>(x2, lane, base);
+                    halve_sums<1, (NH > 3), NG / 16>(x2, lane, base);
+                    constexpr int REM = 16 >> NH;
+                    if constexpr (NG == 32) x2[0] += __shfl_xor(x2[0], 1);  // one sum on two lanes
+                    if (NG != 32 || (lane & 1) == 0) {
+                        const int part = (cm % NCP) / 32;  // which wave's share of the row
+#pragma unroll
+                        for (int r2 = 0; r2 < REM; ++r2) {
+                            const int id = base + r2;
+                            Nrm[((p * 2 + (id >> 3)) * 16 + 8 * hf + (id & 7)) * L::NPART + part] = x2[r2];
+                        }
+                    }
                 }
             }
 #pragma unroll
@@ -959,15 +981,32 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 if (cm >= NCOMBO) continue;
                 const int c0 = 2 * (cm % NCP), p = cm / NCP;
                 const float2 eR = keR[u], eCE = keCE[u];
+                float iq[8], ik[8];  // reciprocal row norms (1 without normalisation)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    iq[i] = 1.f;
+                    ik[i] = 1.f;
+                    if constexpr (NORM) {
+                        float nq = 0.f, nk = 0.f;
+#pragma unroll
+                        for (int pt = 0; pt < L::NPART; ++pt) {
+                            nq += Nrm[((p * 2 + 0) * 16 + 8 * hf + i) * L::NPART + pt];
+                            nk += Nrm[((p * 2 + 1) * 16 + 8 * hf + i) * L::NPART + pt];
+                        }
+                        iq[i] = __builtin_amdgcn_rsqf(fmaxf(nq, 1e-12f));
+                        ik[i] = __builtin_amdgcn_rsqf(fmaxf(nk, 1e-12f));
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int r = 16 * p + 8 * hf + i;
-                    st2<TM>(Qt + r * L::LKM + c0, kq[u][i].x * eR.x, kq[u][i].y * eR.y);
-                    st2<TM>(Bw + r * L::LKM + c0, -kk[u][i].x * eR.x, -kk[u][i].y * eR.y);
+                    st2<TM>(Qt + r * L::LKM + c0, kq[u][i].x * eR.x * iq[i], kq[u][i].y * eR.y * iq[i]);
+                    st2<TM>(Bw + r * L::LKM + c0, -kk[u][i].x * eR.x * ik[i], -kk[u][i].y * eR.y * ik[i]);
                     if (i & 1) {
                         // two consecutive tokens per channel row of Kt
-                        st2<TM>(Kt + c0 * L::LCM + r - 1, kr[u][i - 1].x * eCE.x, kr[u][i].x * eCE.x);
-                        st2<TM>(Kt + (c0 + 1) * L::LCM + r - 1, kr[u][i - 1].y * eCE.y, kr[u][i].y * eCE.y);
+                        st2<TM>(Kt + c0 * L::LCM + r - 1, kr[u][i - 1].x * eCE.x * ik[i - 1], kr[u][i].x * eCE.x * ik[i]);
+                        st2<TM>(Kt + (c0 + 1) * L::LCM + r - 1, kr[u][i - 1].y * eCE.y * ik[i - 1],
+                                kr[u][i].y * eCE.y * ik[i]);
                     }
                 }
             }
