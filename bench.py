@@ -89,10 +89,17 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     write = _counter_means(write_csv, "WRITE_SIZE")
     out = {"_calibration": {"copy_kernel": cname[:120], "copy_bytes": COPY_BYTES, "fetch_kib": cf,
                             "write_kib": cw, "bytes_per_fetch_kib": f_scale, "bytes_per_write_kib": w_scale}}
-    for key, pat, src in (("k3_prefill_chunk_fwd_" + gate, "chunk_fwd_kernel", "kda_chunk_kernel.h"),
-                          ("decode_recurrent_step_" + gate, "recurrent_step_kernel", "kda_step.hip")):
-        fk = [v for k, v in fetch.items() if pat in k]
-        wk = [v for k, v in write.items() if pat in k]
+    zg = gate == "fused"
+    # the exact instantiations the benchmark times (K = V = 128, bf16, chunk 32)
+    chunk_pat = "PrecMixed, 128, 128, 32, 64, %d>" % (1 if zg else 0)
+    flag = "Lb1E" if zg else "Lb0E"  # (these two appear under their mangled names)
+    for key, pats, src in (("k3_prefill_chunk_fwd_" + gate, ("chunk_fwd_kernel<", chunk_pat), "kda_chunk_kernel.h"),
+                           ("decode_recurrent_step_" + gate, ("recurrent_step_kernelIDF16bLi128ELi128E" + flag,),
+                            "kda_step.hip"),
+                           ("short_recurrent_fwd_" + gate, ("recurrent_fwd_kernelIDF16bLi128ELi128E" + flag,),
+                            "kda_recurrent.hip")):
+        fk = [v for k, v in fetch.items() if all(p_ in k for p_ in pats)]
+        wk = [v for k, v in write.items() if all(p_ in k for p_ in pats)]
         if not fk or not wk:
             continue
         out[key] = {"fetch_kib": fk[0], "write_kib": wk[0],
@@ -327,14 +334,16 @@ def main():
             # the step with the model's in-kernel preparation and the state stored [V,K]
             st_vk = state.transpose(-1, -2).contiguous()
             blog = torch.logit(dec.beta)
-            vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
+            vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(min(64, nd))]
             for t, (a_, b_) in enumerate(vev):
                 a_.record(stream)
                 kda.recurrent_step_fused_gate(dec.q[t], dec.k[t], dec.v[t], dec.z[t], dec.log_scale, blog[t], st_vk,
                                               out=od, qk_l2norm=True, beta_logits=True, state_vk=True)
                 b_.record(stream)
             torch.cuda.synchronize()
-            v_us = sum(a_.elapsed_time(b_) for a_, b_ in vev[4:]) / (len(vev) - 4) * 1e3
+            skip = 4 if len(vev) > 8 else 0  # the first steps after the layout change warm up
+            v_us = sum(a_.elapsed_time(b_) for a_, b_ in vev[skip:]) / (len(vev) - skip) * 1e3
             v_gbs = d_bytes / (v_us * 1e-6) / 1e9
             log("decode with in-kernel preparation, [V,K] state: %.1f us per step" % v_us)
             result["decode_prepared_in_kernel"] = {
@@ -383,7 +392,9 @@ def main():
             "workload": sp.name, "call": "recurrent_fwd_fused_gate" if fused else "recurrent_fwd",
             "tokens_per_s": Bs * Ts / (r_ms * 1e-3), "us_per_call": r_ms * 1e3,
             "roofline": {"bound": "hbm", "achieved": r_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": r_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "recurrent_fwd_kernel",
+                         "frac": r_gbs / HBM_PEAK_GBS,
+                         "traffic": load_traffic("kda_recurrent.hip", "short_recurrent_fwd_" + args.gate),
+                         "kernel": "recurrent_fwd_kernel",
                          "algorithmic_bytes_per_launch": r_bytes},
         }
         del so, sf
