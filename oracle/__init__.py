@@ -52,6 +52,12 @@ def _open(path):
     lib.kda_oracle_scan.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.POINTER(i64), i64,
                                     i64, i64, i64, i64, i64, ctypes.c_double, dp, dp, ctypes.c_int]
     lib.kda_oracle_scan.restype = ctypes.c_int
+    lib.kda_oracle_bounded_decay_bwd.argtypes = [dp, dp, dp, ctypes.c_double, i64, i64, i64, dp, ctypes.c_int,
+                                                 dp, dp, dp]
+    lib.kda_oracle_bounded_decay_bwd.restype = None
+    lib.kda_oracle_scan_bwd.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.POINTER(i64), i64, i64, i64, i64, i64, i64,
+                                        ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.kda_oracle_scan_bwd.restype = ctypes.c_int
     lib.kda_oracle_max_threads.argtypes = []
     lib.kda_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -137,6 +143,64 @@ class Oracle:
         return out, fin
 
 
+    def bounded_decay_bwd(self, z, log_scale, grad, g_min: float = -5.0, bias=None, grad_is_log: bool = False):
+        """Gradients of bounded_decay: returns (dz [..., H, K], dlog_scale [H], dbias [H, K]).
+
+        grad is dL/dalpha, or dL/dg with ``grad_is_log``; dbias is returned whether or not a
+        bias is given (the gradient a featurewise bias would receive).
+        """
+        z = _f64(z)
+        H, K = z.shape[-2], z.shape[-1]
+        rows = int(np.prod(z.shape[:-2])) if z.ndim > 2 else 1
+        ls = _f64(log_scale).reshape(-1)
+        gr = _f64(grad)
+        if gr.shape != z.shape or ls.shape[0] != H:
+            raise ValueError("grad must match z and log_scale must have H entries")
+        b = None if bias is None else _f64(bias).reshape(-1)
+        dz = np.empty_like(z)
+        dls = np.empty(H)
+        db = np.empty(H * K)
+        self._lib.kda_oracle_bounded_decay_bwd(_ptr(z), _ptr(ls), _ptr(b), float(g_min), rows, H, K, _ptr(gr),
+                                             1 if grad_is_log else 0, _ptr(dz), _ptr(dls), _ptr(db))
+        return dz, dls, db.reshape(H, K)
+
+    def scan_bwd(self, q, k, v, alpha, beta, d_out, initial_state=None, d_final_state=None, cu_seqlens=None,
+                 scale: float = 1.0, nthreads: int = 0):
+        """Gradients of scan for L = <d_out, out> + <d_final_state, final_state>.
+
+        Returns (dq, dk, dv, dalpha, dbeta, d_initial_state) in float64, shaped like
+        q, k, v, alpha, beta and [N, H, K, V].  d_final_state None means zeros.
+        """
+        q, k, v, alpha, beta, d_out = (_f64(x) for x in (q, k, v, alpha, beta, d_out))
+        B, T, H, K = q.shape
+        V = v.shape[3]
+        if k.shape != q.shape or alpha.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H) \
+                or d_out.shape != v.shape:
+            raise ValueError("inconsistent shapes")
+        cu = None
+        if cu_seqlens is not None:
+            cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).reshape(-1))
+            N = cu.shape[0] - 1
+        else:
+            N = B
+        s0 = None if initial_state is None else _f64(initial_state)
+        dsT = None if d_final_state is None else _f64(d_final_state)
+        for x in (s0, dsT):
+            if x is not None and x.shape != (N, H, K, V):
+                raise ValueError("states must be [N,H,K,V]")
+        dq, dk, da = (np.zeros_like(q) for _ in range(3))
+        dv = np.zeros_like(v)
+        db = np.zeros_like(beta)
+        ds0 = np.zeros((N, H, K, V))
+        rc = self._lib.kda_oracle_scan_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(s0),
+                                         None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         N, B, T, H, K, V, float(scale), _ptr(d_out), _ptr(dsT), _ptr(dq), _ptr(dk),
+                                         _ptr(dv), _ptr(da), _ptr(db), _ptr(ds0), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (cu_seqlens inconsistent with B/T?)")
+        return dq, dk, dv, da, db, ds0
+
+
 _default = None
 
 
@@ -157,3 +221,11 @@ def bounded_decay(*a, **kw):
 
 def scan(*a, **kw):
     return _get().scan(*a, **kw)
+
+
+def scan_bwd(*a, **kw):
+    return _get().scan_bwd(*a, **kw)
+
+
+def bounded_decay_bwd(*a, **kw):
+    return _get().bounded_decay_bwd(*a, **kw)

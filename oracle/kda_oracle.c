@@ -28,9 +28,14 @@
  * parallelism is OpenMP over independent (sequence, head) pairs, which
  * does not change any result.
  *
+ * The gradients (kda_oracle_scan_bwd, kda_oracle_bounded_decay_bwd) are the
+ * reverse-mode derivatives of the same token loop and gate, written out step by
+ * step; PaperLeet's "Return requirements" ask for gradients into every input.
+ *
  * Parity status: every function here is pinned by CPU tests (worked
  * example, closed forms, invariants, an independent matrix-form
- * recurrence); nothing is "parity unpinned".
+ * recurrence; the gradients by element-wise central finite differences of
+ * the forward functions and by closed forms); nothing is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -166,6 +171,218 @@ int kda_oracle_scan(const double *q, const double *k, const double *v, const dou
         }
         free(S);
         free(pred);
+    }
+    return 0;
+}
+
+/*
+ * Gradients of the bounded decay (PaperLeet "Return requirements": bounded_decay keeps
+ * gradients into logits and log_scale; the function is g = g_min sigmoid(x),
+ * x = e^A (z + bias), alpha = e^g, differentiated by the chain rule):
+ *   dg = grad (grad_is_log) or grad * alpha (grad is dL/dalpha)
+ *   dx = dg * g_min * sigmoid(x) (1 - sigmoid(x)),  dz = dx * e^A
+ *   dbias[h,c] = sum over rows of dz,  dlog_scale[h] = sum over rows and c of dx * x
+ * dlog_scale and dbias may be NULL (not wanted); they are overwritten, not accumulated.
+ */
+void kda_oracle_bounded_decay_bwd(const double *z, const double *log_scale, const double *bias,
+                                  double g_min, int64_t rows, int64_t H, int64_t K,
+                                  const double *grad, int grad_is_log, double *dz,
+                                  double *dlog_scale, double *dbias) {
+    if (dlog_scale)
+        for (int64_t h = 0; h < H; ++h) dlog_scale[h] = 0.0;
+    if (dbias)
+        for (int64_t i = 0; i < H * K; ++i) dbias[i] = 0.0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t h = 0; h < H; ++h) {
+            double e = exp(log_scale[h]);
+            for (int64_t c = 0; c < K; ++c) {
+                int64_t i = (r * H + h) * K + c;
+                double x = e * (z[i] + (bias ? bias[h * K + c] : 0.0));
+                double s = sigmoid(x);
+                double g = g_min * s;
+                double dg = grad_is_log ? grad[i] : grad[i] * exp(g);
+                double dx = dg * g_min * s * (1.0 - s);
+                dz[i] = dx * e;
+                if (dbias) dbias[h * K + c] += dx * e;
+                if (dlog_scale) dlog_scale[h] += dx * x;
+            }
+        }
+}
+
+/*
+ * The state update of one token (fade, predict, correct; no read), used by the
+ * backward pass to rebuild the states it needs.
+ */
+static void advance(double *S, const double *kt, const double *vt, const double *at, double bt,
+                    int64_t K, int64_t V, double *pred) {
+    for (int64_t c = 0; c < K; ++c)
+        for (int64_t j = 0; j < V; ++j) S[c * V + j] *= at[c];
+    for (int64_t j = 0; j < V; ++j) pred[j] = 0.0;
+    for (int64_t c = 0; c < K; ++c)
+        for (int64_t j = 0; j < V; ++j) pred[j] += S[c * V + j] * kt[c];
+    for (int64_t c = 0; c < K; ++c)
+        for (int64_t j = 0; j < V; ++j) S[c * V + j] += bt * kt[c] * (vt[j] - pred[j]);
+}
+
+#define BWD_SEG 64 /* tokens between stored states in the backward pass */
+
+/*
+ * Reverse-mode derivative of one (sequence, head) pair (PaperLeet "Return requirements":
+ * gradients reach q, k, v, alpha, beta and the initial state through every non-empty
+ * scan).  The loss seen is L = <d_out, out> + <d_final, S_T>.  Walking the tokens
+ * backwards with dS = dL/dS_t:
+ *   read     o_t = scale S_t^T q_t:       dq_t = scale S_t do_t,  dS += scale q_t do_t^T
+ *   correct  S_t = P + beta_t k_t delta^T, P = Diag(alpha_t) S_{t-1}, delta = v_t - P^T k_t:
+ *            dbeta_t = k_t^T dS delta,  dk_t = beta_t dS delta,  ddelta = beta_t dS^T k_t,
+ *            dv_t = ddelta,  dP = dS - k_t ddelta^T,  dk_t -= P ddelta
+ *   fade     dalpha_t[c] = sum_j dP[c,j] S_{t-1}[c,j],  dS_{t-1} = Diag(alpha_t) dP.
+ * The states S_{t-1}, S_t are rebuilt from copies stored every BWD_SEG tokens (a
+ * replay of the same arithmetic, so they equal the forward's states exactly).
+ * work: (nseg + BWD_SEG + 3) * K * V + 3 * V doubles, nseg = ceil(len / BWD_SEG).
+ */
+static void bwd_pair(const double *q, const double *k, const double *v, const double *alpha,
+                     const double *beta, const double *s0, const double *dout, const double *dsT,
+                     int64_t t0, int64_t len, int64_t h, int64_t H, int64_t K, int64_t V,
+                     double scale, double *dq, double *dk, double *dv, double *dalpha,
+                     double *dbeta, double *ds0, double *work) {
+    const int64_t KV = K * V;
+    int64_t nseg = (len + BWD_SEG - 1) / BWD_SEG;
+    double *ckpt = work;                     /* nseg states: the state before each segment */
+    double *st = ckpt + nseg * KV;           /* BWD_SEG + 1 states of the replayed segment */
+    double *dS = st + (BWD_SEG + 1) * KV;
+    double *dP = dS + KV;
+    double *pred = dP + KV, *delta = pred + V, *dd = delta + V;
+
+    double *S = st; /* forward pass: store the checkpoints */
+    if (s0)
+        memcpy(S, s0, (size_t)KV * sizeof(double));
+    else
+        memset(S, 0, (size_t)KV * sizeof(double));
+    for (int64_t i = 0; i < nseg; ++i) {
+        memcpy(ckpt + i * KV, S, (size_t)KV * sizeof(double));
+        int64_t a = t0 + i * BWD_SEG, b = a + BWD_SEG < t0 + len ? a + BWD_SEG : t0 + len;
+        for (int64_t t = a; t < b; ++t)
+            advance(S, k + (t * H + h) * K, v + (t * H + h) * V, alpha + (t * H + h) * K, beta[t * H + h],
+                    K, V, pred);
+    }
+
+    if (dsT)
+        memcpy(dS, dsT, (size_t)KV * sizeof(double));
+    else
+        memset(dS, 0, (size_t)KV * sizeof(double));
+    for (int64_t i = nseg - 1; i >= 0; --i) {
+        int64_t a = t0 + i * BWD_SEG, b = a + BWD_SEG < t0 + len ? a + BWD_SEG : t0 + len;
+        memcpy(st, ckpt + i * KV, (size_t)KV * sizeof(double));
+        for (int64_t t = a; t < b; ++t) {
+            double *nx = st + (t - a + 1) * KV;
+            memcpy(nx, nx - KV, (size_t)KV * sizeof(double));
+            advance(nx, k + (t * H + h) * K, v + (t * H + h) * V, alpha + (t * H + h) * K, beta[t * H + h],
+                    K, V, pred);
+        }
+        for (int64_t t = b - 1; t >= a; --t) {
+            const double *Sprev = st + (t - a) * KV, *Scur = Sprev + KV;
+            const double *kt = k + (t * H + h) * K, *qt = q + (t * H + h) * K;
+            const double *vt = v + (t * H + h) * V, *at = alpha + (t * H + h) * K;
+            const double *dot = dout + (t * H + h) * V;
+            double bt = beta[t * H + h];
+
+            /* read */
+            for (int64_t c = 0; c < K; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < V; ++j) acc += Scur[c * V + j] * dot[j];
+                dq[(t * H + h) * K + c] = scale * acc;
+            }
+            for (int64_t c = 0; c < K; ++c)
+                for (int64_t j = 0; j < V; ++j) dS[c * V + j] += scale * qt[c] * dot[j];
+
+            /* correct: delta = v_t - P^T k_t with P = Diag(alpha_t) S_{t-1} */
+            for (int64_t j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < K; ++c) acc += at[c] * Sprev[c * V + j] * kt[c];
+                delta[j] = vt[j] - acc;
+            }
+            double db = 0.0;
+            for (int64_t c = 0; c < K; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < V; ++j) acc += dS[c * V + j] * delta[j];
+                db += kt[c] * acc;
+                dk[(t * H + h) * K + c] = bt * acc;
+            }
+            dbeta[t * H + h] = db;
+            for (int64_t j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < K; ++c) acc += dS[c * V + j] * kt[c];
+                dd[j] = bt * acc;
+                dv[(t * H + h) * V + j] = dd[j];
+            }
+            for (int64_t c = 0; c < K; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < V; ++j) {
+                    dP[c * V + j] = dS[c * V + j] - kt[c] * dd[j];
+                    acc += at[c] * Sprev[c * V + j] * dd[j];
+                }
+                dk[(t * H + h) * K + c] -= acc;
+            }
+
+            /* fade */
+            for (int64_t c = 0; c < K; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < V; ++j) acc += dP[c * V + j] * Sprev[c * V + j];
+                dalpha[(t * H + h) * K + c] = acc;
+                for (int64_t j = 0; j < V; ++j) dS[c * V + j] = at[c] * dP[c * V + j];
+            }
+        }
+    }
+    if (ds0) memcpy(ds0, dS, (size_t)KV * sizeof(double));
+}
+
+/*
+ * Gradients of kda_oracle_scan for L = <d_out, out> + <d_final_state, final_state>.
+ * Arguments as kda_oracle_scan, plus d_out [B, T, H, V] and d_final_state [N, H, K, V]
+ * (NULL = zeros); outputs dq, dk [B, T, H, K], dv [B, T, H, V], dalpha [B, T, H, K],
+ * dbeta [B, T, H] and d_initial_state [N, H, K, V] (NULL = not wanted; for an
+ * omitted initial state it is the gradient at the zero state).  An empty sequence
+ * passes d_final_state through to d_initial_state.  Returns 0, or -1 as kda_oracle_scan.
+ */
+int kda_oracle_scan_bwd(const double *q, const double *k, const double *v, const double *alpha,
+                        const double *beta, const double *initial_state, const int64_t *cu_seqlens,
+                        int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                        double scale, const double *d_out, const double *d_final_state, double *dq,
+                        double *dk, double *dv, double *dalpha, double *dbeta,
+                        double *d_initial_state, int nthreads) {
+    if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return -1;
+    int64_t N = cu_seqlens ? num_seqs : B;
+    if (cu_seqlens) {
+        if (B != 1 || num_seqs < 0 || cu_seqlens[0] != 0 || cu_seqlens[num_seqs] != T) return -1;
+        for (int64_t s = 0; s < num_seqs; ++s)
+            if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+    }
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int64_t maxlen = cu_seqlens ? 0 : T;
+    for (int64_t s = 0; cu_seqlens && s < num_seqs; ++s)
+        if (cu_seqlens[s + 1] - cu_seqlens[s] > maxlen) maxlen = cu_seqlens[s + 1] - cu_seqlens[s];
+    int64_t nseg = (maxlen + BWD_SEG - 1) / BWD_SEG;
+    size_t wsize = (size_t)((nseg + BWD_SEG + 3) * K * V + 3 * V);
+    int64_t pairs = N * H;
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(wsize * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t p = 0; p < pairs; ++p) {
+            int64_t s = p / H, h = p % H;
+            int64_t t0 = cu_seqlens ? cu_seqlens[s] : s * T;
+            int64_t len = cu_seqlens ? cu_seqlens[s + 1] - cu_seqlens[s] : T;
+            const double *s0 = initial_state ? initial_state + (s * H + h) * K * V : NULL;
+            const double *dsT = d_final_state ? d_final_state + (s * H + h) * K * V : NULL;
+            double *ds0 = d_initial_state ? d_initial_state + (s * H + h) * K * V : NULL;
+            bwd_pair(q, k, v, alpha, beta, s0, d_out, dsT, t0, len, h, H, K, V, scale, dq, dk, dv,
+                     dalpha, dbeta, ds0, work);
+        }
+        free(work);
     }
     return 0;
 }

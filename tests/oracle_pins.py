@@ -264,9 +264,150 @@ def pin_gate_range_and_limits(orc):
     assert ext[0] == 1.0 and abs(ext[1] - math.exp(-5.0)) < 1e-16
 
 
+# --- gradient pins ---------------------------------------------------------------------
+# PaperLeet "Return requirements": gradients reach q, k, v, alpha, beta and the initial
+# state through the scan, and logits and log_scale through bounded_decay.  The backward
+# functions are pinned to central differences of the forward functions (themselves
+# pinned above), element by element, and to closed forms.
+
+def _central_differences(f, arrays, eps=1e-6):
+    """d f / d x for every element of every array in ``arrays`` (modified in place and
+    restored), by (f(x + eps) - f(x - eps)) / (2 eps)."""
+    out = []
+    for a in arrays:
+        g = np.zeros_like(a)
+        flat, gf = a.reshape(-1), g.reshape(-1)
+        for i in range(flat.size):
+            x0 = flat[i]
+            flat[i] = x0 + eps
+            fp = f()
+            flat[i] = x0 - eps
+            fm = f()
+            flat[i] = x0
+            gf[i] = (fp - fm) / (2 * eps)
+        out.append(g)
+    return out
+
+
+def _assert_grads_close(got, ref, names, tol=1e-7):
+    for g, r, n in zip(got, ref, names):
+        assert g.shape == r.shape, (n, g.shape, r.shape)
+        err = np.max(np.abs(g - r) / np.maximum(1.0, np.abs(r))) if g.size else 0.0
+        assert err <= tol, "%s: gradient differs from central differences by %g" % (n, err)
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient of the scan, element by element, against central differences of
+    L = <d_out, out> + <d_final, final_state>, with an initial state and a read scale."""
+    rs = np.random.default_rng(30)
+    B, T, H, K, V = 2, 6, 2, 3, 2
+    q, k, v, alpha, beta, s0 = _rand_inputs(rs, B, T, H, K, V)
+    alpha = rs.uniform(0.3, 1.0, alpha.shape)
+    do = rs.standard_normal((B, T, H, V))
+    dsT = rs.standard_normal((B, H, K, V))
+    scale = 0.8
+
+    def loss():
+        o, f = orc.scan(q, k, v, alpha, beta, s0, scale=scale)
+        return float(np.sum(do * o) + np.sum(dsT * f))
+    got = orc.scan_bwd(q, k, v, alpha, beta, do, s0, dsT, scale=scale)
+    ref = _central_differences(loss, [q, k, v, alpha, beta, s0])
+    _assert_grads_close(got, ref, ["dq", "dk", "dv", "dalpha", "dbeta", "d_initial_state"])
+
+
+def pin_bwd_finite_differences_varlen(orc):
+    """Packed sequences with an empty one, no initial state (its gradient is taken at the
+    zero state), no final-state gradient, and gates at the endpoints alpha in {0, 1},
+    beta in {0, 1} that the contract accepts."""
+    rs = np.random.default_rng(31)
+    cu = np.array([0, 3, 3, 8])
+    T, H, K, V = 8, 1, 2, 3
+    q, k, v, alpha, beta, _ = _rand_inputs(rs, 1, T, H, K, V, unit_keys=False)
+    alpha[0, 1, 0, 0] = 0.0
+    alpha[0, 4, 0, 1] = 1.0
+    alpha[0, 5] = 1.0
+    beta[0, 2, 0] = 0.0
+    beta[0, 6, 0] = 1.0
+    do = rs.standard_normal((1, T, H, V))
+    zero = np.zeros((3, H, K, V))
+
+    def loss():
+        o, _ = orc.scan(q, k, v, alpha, beta, zero, cu_seqlens=cu)
+        return float(np.sum(do * o))
+    got = orc.scan_bwd(q, k, v, alpha, beta, do, None, None, cu_seqlens=cu)
+    ref = _central_differences(loss, [q, k, v, alpha, beta, zero])
+    _assert_grads_close(got, ref, ["dq", "dk", "dv", "dalpha", "dbeta", "d_initial_state"])
+
+
+def pin_bwd_single_token(orc):
+    """One token from a state S0: o = scale S_1^T q with S_1 = Diag(a) S0 + b k (v - k^T Diag(a) S0)^T.
+    From S0 = 0, o = scale b (k.q) v, so dq = scale b (v.do) k, dk = scale b (v.do) q,
+    dv = scale b (k.q) do, dbeta = scale (k.q)(v.do), dalpha = 0, and
+    dS0 = Diag(a) (I - b k k^T) scale q do^T."""
+    rs = np.random.default_rng(32)
+    K, V, scale = 4, 3, 0.6
+    q, k, v, alpha, beta, _ = _rand_inputs(rs, 1, 1, 1, K, V, unit_keys=False)
+    do = rs.standard_normal((1, 1, 1, V))
+    dq, dk, dv, da, db, ds0 = orc.scan_bwd(q, k, v, alpha, beta, do, None, None, scale=scale)
+    qq, kk, vv, aa, bb, dd = q[0, 0, 0], k[0, 0, 0], v[0, 0, 0], alpha[0, 0, 0], beta[0, 0, 0], do[0, 0, 0]
+    tol = dict(rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(dq[0, 0, 0], scale * bb * (vv @ dd) * kk, **tol)
+    np.testing.assert_allclose(dk[0, 0, 0], scale * bb * (vv @ dd) * qq, **tol)
+    np.testing.assert_allclose(dv[0, 0, 0], scale * bb * (kk @ qq) * dd, **tol)
+    np.testing.assert_allclose(db[0, 0, 0], scale * (kk @ qq) * (vv @ dd), **tol)
+    assert np.all(da == 0.0)
+    dS1 = scale * np.outer(qq, dd)
+    np.testing.assert_allclose(ds0[0, 0], aa[:, None] * ((np.eye(K) - bb * np.outer(kk, kk)) @ dS1), **tol)
+
+
+def pin_bwd_empty_sequence(orc):
+    """T = 0: no token gradients, and the final state's gradient passes straight through
+    to the initial state (final = initial for an empty scan)."""
+    rs = np.random.default_rng(33)
+    B, H, K, V = 2, 2, 3, 4
+    z = np.zeros((B, 0, H, K))
+    dsT = rs.standard_normal((B, H, K, V))
+    res = orc.scan_bwd(z, z, np.zeros((B, 0, H, V)), z, np.zeros((B, 0, H)), np.zeros((B, 0, H, V)),
+                       rs.standard_normal((B, H, K, V)), dsT)
+    assert res[0].shape == (B, 0, H, K) and res[2].shape == (B, 0, H, V)
+    assert np.array_equal(res[5], dsT)
+
+
+def pin_bwd_gate_finite_differences(orc):
+    """Gradients of bounded_decay into the logits, the per-head log-scale and the bias,
+    for a loss on alpha and on g = ln alpha, against central differences."""
+    rs = np.random.default_rng(34)
+    rows, H, K, gmin = 3, 2, 3, -4.0
+    z = rs.standard_normal((rows, H, K))
+    A = rs.standard_normal(H) * 0.5
+    bias = rs.standard_normal((H, K))
+    w = rs.standard_normal((rows, H, K))
+    for as_log in (False, True):
+        def loss():
+            return float(np.sum(w * orc.bounded_decay(z, A, g_min=gmin, bias=bias, out_log=as_log)))
+        got = orc.bounded_decay_bwd(z, A, w, g_min=gmin, bias=bias, grad_is_log=as_log)
+        ref = _central_differences(loss, [z, A, bias])
+        _assert_grads_close(got, ref, ["dz", "dlog_scale", "dbias"])
+
+
+def pin_bwd_gate_closed_form(orc):
+    """At z + bias = 0 the sigmoid is 1/2 with slope 1/4, so alpha = e^{g_min/2} and
+    dL/dz = w alpha g_min e^A / 4; the log-scale receives nothing (x = 0)."""
+    H, K, gmin = 2, 3, -5.0
+    A = np.array([0.0, math.log(3.0)])
+    w = np.arange(1.0, 1.0 + 2 * H * K).reshape(2, H, K)
+    dz, dls, db = orc.bounded_decay_bwd(np.zeros((2, H, K)), A, w, g_min=gmin)
+    ref = w * math.exp(gmin / 2) * gmin * np.exp(A)[None, :, None] / 4
+    np.testing.assert_allclose(dz, ref, rtol=1e-14)
+    assert np.all(dls == 0.0)
+    np.testing.assert_allclose(db, dz.sum(axis=0), rtol=1e-14)
+
+
 RECURRENCE_PINS = [pin_toy_memory, pin_empty_sequence, pin_exact_recall, pin_overwrite,
                    pin_zero_writes, pin_literal_matrix_form, pin_gated_deltanet,
                    pin_segmented_continuation, pin_causal_prefix, pin_varlen_equals_separate,
                    pin_scale_is_linear]
 GATE_PINS = [pin_gate_closed_forms, pin_gate_scale_and_bias, pin_gate_range_and_limits]
-ALL_PINS = RECURRENCE_PINS + GATE_PINS
+GRADIENT_PINS = [pin_bwd_finite_differences, pin_bwd_finite_differences_varlen, pin_bwd_single_token,
+                 pin_bwd_empty_sequence, pin_bwd_gate_finite_differences, pin_bwd_gate_closed_form]
+ALL_PINS = RECURRENCE_PINS + GATE_PINS + GRADIENT_PINS

@@ -41,6 +41,20 @@ MUTANTS = [
     ("gate_no_bias", "double x = z[i] + (bias ? bias[h * K + c] : 0.0);", "double x = z[i];"),
     ("gate_softplus", "double g = g_min * sigmoid(scale * x);", "double g = -scale * log1p(exp(x));"),
     ("gate_returns_log", "out[i] = out_log ? g : exp(g);", "out[i] = g;"),
+    # mistakes in the gradients
+    ("bwd_no_fade_chain", "dS[c * V + j] = at[c] * dP[c * V + j];", "dS[c * V + j] = dP[c * V + j];"),
+    ("bwd_dk_drops_prediction", "dk[(t * H + h) * K + c] -= acc;", "(void)acc;"),
+    ("bwd_dq_no_scale", "dq[(t * H + h) * K + c] = scale * acc;", "dq[(t * H + h) * K + c] = acc;"),
+    ("bwd_dbeta_sign", "db += kt[c] * acc;", "db -= kt[c] * acc;"),
+    ("bwd_dv_no_beta", "dd[j] = bt * acc;", "dd[j] = acc;"),
+    ("bwd_dalpha_new_state", "acc += dP[c * V + j] * Sprev[c * V + j];", "acc += dP[c * V + j] * Scur[c * V + j];"),
+    ("bwd_read_with_key", "dS[c * V + j] += scale * qt[c] * dot[j];", "dS[c * V + j] += scale * kt[c] * dot[j];"),
+    ("bwd_dP_no_correction", "dP[c * V + j] = dS[c * V + j] - kt[c] * dd[j];", "dP[c * V + j] = dS[c * V + j];"),
+    ("bwd_final_grad_ignored", "if (dsT)\n        memcpy(dS, dsT", "if (0)\n        memcpy(dS, dsT"),
+    ("bwd_delta_undecayed", "acc += at[c] * Sprev[c * V + j] * kt[c];", "acc += Sprev[c * V + j] * kt[c];"),
+    ("gate_bwd_no_exp_scale", "dz[i] = dx * e;", "dz[i] = dx;"),
+    ("gate_bwd_log_scale_no_x", "dlog_scale[h] += dx * x;", "dlog_scale[h] += dx;"),
+    ("gate_bwd_no_alpha_factor", "grad[i] * exp(g)", "grad[i]"),
 ]
 
 
