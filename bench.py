@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
+FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix cores
 
 
 def log(msg):
@@ -122,6 +123,7 @@ def main():
                     help="fused: the kernels take the gate logits; separate: bounded_decay writes a "
                          "float32 gate that the kernels read")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward (training) block")
     ap.add_argument("--no-short", action="store_true", help="skip the short-continuation (token-recurrent) block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48)
@@ -262,6 +264,51 @@ def main():
                          "frac": p_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg_bytes}}
         del bl, fin_vk
     del g, out
+
+    # ---------------- backward ----------------------------------------------------------
+    if not args.no_bwd:
+        # gradients of the same K3 prefill: bf16 q, k, v and d_out, float32 retention (the
+        # gate tensor the backward takes), bf16 dq, dk, dv, float32 dgate and dbeta
+        alpha_b = kda.bounded_decay(z, ls, lower_bound=-5.0)
+        d_out_b, d_fin_b = synth.cotangents(B, T, H, V, K, 1, seed=7, device="cuda")
+        d_out_b = d_out_b.to(torch.bfloat16)
+        ws = torch.empty(kda.chunk_bwd_workspace_size(B, T, H, K, V), dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return kda.chunk_bwd(q, k, v, alpha_b, beta, d_out_b, d_final_state=d_fin_b,
+                                 grad_dtype=torch.bfloat16, workspace=ws)
+        for _ in range(2):
+            bstep()
+        torch.cuda.synchronize()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a_, b_ in bev:
+            a_.record(stream)
+            bstep()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        b_ms = sum(a_.elapsed_time(b_) for a_, b_ in bev) / len(bev)
+        # per token-head: q, k, v, d_out bf16 + alpha fp32 + beta in; dq, dk, dv bf16 + dgate fp32 + dbeta out
+        b_bytes = th * (2 * (2 * K + V) + 4 * K + 4 + 2 * V + 2 * (2 * K + V) + 4 * K + 4)
+        # dense products per 64-token chunk and head (C = 64): recomputed forward (A matrices, W, U,
+        # states) and the reverse (state gradients, the V contractions, dT, dA, adjoints)
+        C_, ckv, cck, ccv = 64, 2 * 64 * K * V, 64 * 64 * K, 64 * 64 * V   # flops of one full / triangular product
+        per_chunk = (2 * cck + cck + ccv                    # prep: Abar, A_qk, W = T(.), U = T(.) (triangular)
+                     + 2 * ckv                              # states: W S, Kd^T Vt
+                     + 3 * ckv + ccv                        # dstates: Kd dS', Qg^T dO, W^T dVt, A_qk^T dO
+                     + 3 * ckv + 4 * ccv + ccv              # vgrads: dO S^T, dVt S^T, Vt dS'^T, dO Vt^T, dVt V^T, T^T dVt
+                     + 2 * cck + 4 * C_ ** 3 + cck + 4 * cck)  # kgrads: dT, T products, T^T dW, adjoints
+        b_flops = (T // C_) * B * H * per_chunk
+        b_tf = b_flops / (b_ms * 1e-3) / 1e12
+        b_gbs = b_bytes / (b_ms * 1e-3) / 1e9
+        log("backward: %.3f ms, %.1f TFLOP/s fp32 matrix, %.1f GB/s" % (b_ms, b_tf, b_gbs))
+        result["prefill_backward"] = {
+            "workload": "k3_prefill_B1_T8192_H96_K128_V128", "call": "chunk_bwd (5 kernels, float32)",
+            "tokens_per_s": B * T / (b_ms * 1e-3), "launch_ms": b_ms,
+            "roofline": {"bound": "mfma", "achieved": b_tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": b_tf / FP32_PEAK_TFLOPS, "algorithmic_flops_per_call": b_flops},
+            "hbm": {"achieved": b_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": b_gbs / HBM_PEAK_GBS,
+                    "algorithmic_bytes_per_call": b_bytes}}
+        del ws, alpha_b, d_out_b, d_fin_b
 
     # ---------------- decode ------------------------------------------------------------
     if not args.no_decode:

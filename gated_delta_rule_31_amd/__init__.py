@@ -20,8 +20,13 @@ Entry points (same names as the C ABI, minus the ``kda_`` prefix where noted):
   -- the same calls with
   the gate applied inside the kernel from its logits (``log_scale``, ``bias``,
   ``lower_bound``), so no float32 gate tensor is made.
+* ``chunk_bwd(q, k, v, gate, beta, d_out, ...)`` -- gradients of ``chunk_fwd`` into q, k,
+  v, the gate, beta and the initial state; ``bounded_decay_bwd`` -- gradients of the gate
+  into its logits, log-scale and bias.
 * ``recurrent_kda(q, k, v, alpha, beta, initial_state=None)`` -- the functional
-  (output, final_state) form of the pages' operator contract, on ``chunk_fwd``.
+  (output, final_state) form of the pages' operator contract, on ``chunk_fwd``; it is
+  differentiable (autograd through ``chunk_bwd``), and so is ``bounded_decay`` when its
+  inputs require grad (through ``bounded_decay_bwd``).
 """
 from __future__ import annotations
 
@@ -33,7 +38,8 @@ import torch
 
 __all__ = ["bounded_decay", "chunk_fwd", "recurrent_step", "recurrent_kda", "KDAError", "chunk_fwd_supported",
            "chunk_fwd_fused_gate", "recurrent_step_fused_gate", "recurrent_fwd", "recurrent_fwd_fused_gate",
-           "library_path", "abi_version", "GATE_ALPHA", "GATE_LOG"]
+           "library_path", "abi_version", "GATE_ALPHA", "GATE_LOG", "chunk_bwd", "chunk_bwd_workspace_size",
+           "bounded_decay_bwd"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -91,6 +97,13 @@ def _load():
     lib.kda_recurrent_fwd_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, vp, vp, i32, i32,
                                                  i64, i32, i32, i32, f32, vp, i32, vp]
     lib.kda_recurrent_fwd_fused_gate.restype = i32
+    lib.kda_chunk_bwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_bwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp, i32,
+                                  vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.kda_chunk_bwd.restype = i32
+    lib.kda_bounded_decay_bwd.argtypes = [vp, i32, vp, vp, f32, i64, i32, i32, vp, i32, vp, i32, vp, vp, vp]
+    lib.kda_bounded_decay_bwd.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
@@ -135,8 +148,9 @@ def _dev(x: Optional[torch.Tensor], name: str, dtype=None) -> Optional[torch.Ten
         raise TypeError("%s must be a torch.Tensor" % name)
     if x.device.type != "cuda":
         raise ValueError("%s must be on the GPU (got %s)" % (name, x.device))
-    if x.requires_grad:
-        raise ValueError("%s requires grad: the library provides no backward" % name)
+    if x.requires_grad and torch.is_grad_enabled():
+        raise ValueError("%s requires grad: the raw kernels do not record autograd; use recurrent_kda / "
+                         "bounded_decay, or call chunk_bwd yourself" % name)
     if dtype is not None and x.dtype != dtype:
         raise ValueError("%s must be %s (got %s)" % (name, dtype, x.dtype))
     return x.contiguous()
@@ -150,11 +164,21 @@ def _stream(x: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)
 
 
+def _needs_grad(*xs) -> bool:
+    return torch.is_grad_enabled() and any(isinstance(x, torch.Tensor) and x.requires_grad for x in xs)
+
+
 def bounded_decay(logits: torch.Tensor, log_scale: torch.Tensor, lower_bound: float = -5.0,
                   bias: Optional[torch.Tensor] = None, out_log: bool = False,
                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Retention factors alpha [..., H, K] (float32) from logits [..., H, K]
-    (float32 or bfloat16); with ``out_log`` the log-decay g instead."""
+    (float32 or bfloat16); with ``out_log`` the log-decay g instead.  Differentiable in
+    logits, log_scale and bias when any of them requires grad (``out`` is then not
+    accepted)."""
+    if _needs_grad(logits, log_scale, bias):
+        if out is not None:
+            raise ValueError("out= is not supported when gradients are recorded")
+        return _BoundedDecayFn.apply(logits, log_scale, bias, float(lower_bound), bool(out_log))
     logits = _dev(logits, "logits")
     log_scale = _dev(log_scale, "log_scale", torch.float32)
     bias = _dev(bias, "bias", torch.float32)
@@ -395,9 +419,141 @@ def recurrent_step_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out
 
 
-def recurrent_kda(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 32):
+def chunk_bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, num_seqs: int = 0,
+                             varlen: bool = False) -> int:
+    """Bytes of device workspace ``chunk_bwd`` needs for this shape (0: unsupported)."""
+    return int(_load().kda_chunk_bwd_workspace_size(int(B), int(T), int(H), int(K), int(V), int(num_seqs),
+                                                     1 if varlen else 0))
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor, beta: torch.Tensor,
+              d_out: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              d_final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+              scale: float = 1.0, gate_is_log: bool = False, grad_dtype: Optional[torch.dtype] = None,
+              want_d_initial_state: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Gradients of ``chunk_fwd`` (same q, k, v, gate, beta, initial_state, cu_seqlens,
+    scale) for L = <d_out, out> + <d_final_state, final_state>.  Returns (dq, dk, dv,
+    dgate, dbeta, d_initial_state): dq, dk, dv in ``grad_dtype`` (default: the dtype of
+    q), dgate float32 (dL/dalpha, or dL/d ln alpha with ``gate_is_log``), dbeta float32,
+    d_initial_state [N,H,K,V] float32 or None.  ``workspace``: a uint8 CUDA tensor of at
+    least ``chunk_bwd_workspace_size`` bytes, allocated here if not given."""
+    q, k, v, beta, initial_state, cu_seqlens, N, _, _, _ = _chunk_common(
+        q, k, v, beta, initial_state, False, cu_seqlens, None, None, None)
+    gate = _dev(gate, "gate", torch.float32)
+    d_out = _dev(d_out, "d_out")
+    d_final_state = _dev(d_final_state, "d_final_state", torch.float32)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if gate.shape != q.shape or d_out.shape != v.shape:
+        raise ValueError("gate must be shaped like q and d_out like v")
+    if d_final_state is not None and d_final_state.shape != (N, H, K, V):
+        raise ValueError("d_final_state must be [N,H,K,V]")
+    gd = grad_dtype or q.dtype
+    dev = q.device
+    dq = torch.empty(q.shape, dtype=gd, device=dev)
+    dk = torch.empty(q.shape, dtype=gd, device=dev)
+    dv = torch.empty(v.shape, dtype=gd, device=dev)
+    dgate = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dbeta = torch.empty(beta.shape, dtype=torch.float32, device=dev)
+    ds0 = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if want_d_initial_state else None
+    need = chunk_bwd_workspace_size(B, T, H, K, V, N, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError("workspace must be a uint8 tensor of at least %d bytes on %s" % (need, dev))
+    with torch.cuda.device(dev):
+        st = _load().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(gate),
+                                   GATE_LOG if gate_is_log else GATE_ALPHA, _ptr(beta), _ptr(initial_state),
+                                   _ptr(cu_seqlens), N, B, T, H, K, V, float(scale), _ptr(d_out),
+                                   _dtype_code(d_out.dtype), _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _dtype_code(gd), _ptr(dgate), _ptr(dbeta), _ptr(ds0), _ptr(workspace),
+                                   workspace.numel(), _stream(q))
+    _check("kda_chunk_bwd", st)
+    return dq, dk, dv, dgate, dbeta, ds0
+
+
+def bounded_decay_bwd(logits: torch.Tensor, log_scale: torch.Tensor, grad: torch.Tensor,
+                      lower_bound: float = -5.0, bias: Optional[torch.Tensor] = None, grad_is_log: bool = False,
+                      dlogits_dtype: Optional[torch.dtype] = None):
+    """Gradients of ``bounded_decay`` given grad = dL/dalpha (or dL/dg with
+    ``grad_is_log``).  Returns (d_logits in ``dlogits_dtype`` (default: the logits'
+    dtype), d_log_scale [H] float32, d_bias [H, K] float32)."""
+    logits = _dev(logits, "logits")
+    log_scale = _dev(log_scale, "log_scale", torch.float32)
+    bias = _dev(bias, "bias", torch.float32)
+    grad = _dev(grad, "grad", torch.float32)
+    if logits.dim() < 2 or grad.shape != logits.shape:
+        raise ValueError("logits must be [..., H, K] and grad shaped like it")
+    H, K = logits.shape[-2], logits.shape[-1]
+    if log_scale.numel() != H or (bias is not None and bias.numel() != H * K):
+        raise ValueError("log_scale must be [H] and bias [H, K]")
+    rows = logits.numel() // (H * K) if H * K else 0
+    dd = dlogits_dtype or logits.dtype
+    dz = torch.empty(logits.shape, dtype=dd, device=logits.device)
+    dls = torch.empty(H, dtype=torch.float32, device=logits.device)
+    db = torch.empty((H, K), dtype=torch.float32, device=logits.device)
+    with torch.cuda.device(logits.device):
+        st = _load().kda_bounded_decay_bwd(_ptr(logits), _dtype_code(logits.dtype), _ptr(log_scale), _ptr(bias),
+                                           float(lower_bound), rows, H, K, _ptr(grad),
+                                           GATE_LOG if grad_is_log else GATE_ALPHA, _ptr(dz), _dtype_code(dd),
+                                           _ptr(dls), _ptr(db), _stream(logits))
+    _check("kda_bounded_decay_bwd", st)
+    return dz, dls, db
+
+
+class _BoundedDecayFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, log_scale, bias, lower_bound, out_log):
+        with torch.no_grad():
+            out = bounded_decay(logits.detach(), log_scale.detach(), lower_bound,
+                                None if bias is None else bias.detach(), out_log)
+        ctx.save_for_backward(logits, log_scale, bias)
+        ctx.lower_bound, ctx.out_log = lower_bound, out_log
+        return out
+
+    @staticmethod
+    def backward(ctx, grad):
+        logits, log_scale, bias = ctx.saved_tensors
+        with torch.no_grad():
+            dz, dls, db = bounded_decay_bwd(logits.detach(), log_scale.detach(), grad.float().contiguous(),
+                                            ctx.lower_bound, None if bias is None else bias.detach(), ctx.out_log)
+        return (dz, dls.reshape(log_scale.shape).to(log_scale.dtype),
+                None if bias is None else db.reshape(bias.shape).to(bias.dtype), None, None)
+
+
+class _ChunkKDAFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, alpha, beta, initial_state, chunk_size, scale):
+        with torch.no_grad():
+            d = lambda x: None if x is None else x.detach()
+            out, fin = chunk_fwd(d(q), d(k), d(v), d(alpha), d(beta), initial_state=d(initial_state),
+                                 output_final_state=True, chunk_size=chunk_size, scale=scale)
+        ctx.save_for_backward(q, k, v, alpha, beta, initial_state)
+        ctx.scale = scale
+        ctx.has_s0 = initial_state is not None
+        return out, fin
+
+    @staticmethod
+    def backward(ctx, d_out, d_fin):
+        q, k, v, alpha, beta, s0 = ctx.saved_tensors
+        if d_out is None:
+            d_out = torch.zeros(v.shape, dtype=v.dtype, device=v.device)
+        with torch.no_grad():
+            d = lambda x: None if x is None else x.detach()
+            dq, dk, dv, da, db, ds0 = chunk_bwd(d(q), d(k), d(v), d(alpha), d(beta), d_out.contiguous(),
+                                                initial_state=d(s0),
+                                                d_final_state=None if d_fin is None else d_fin.float().contiguous(),
+                                                scale=ctx.scale, want_d_initial_state=ctx.has_s0)
+        return dq, dk, dv, da, db, ds0, None, None
+
+
+def recurrent_kda(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 32, scale: float = 1.0):
     """PaperLeet ``recurrent_kda`` contract: (output [B,T,H,V], final_state [B,H,K,V]),
     output in the inputs' dtype, every output read after its token's update, inputs
-    untouched; T == 0 returns the supplied state (or zeros)."""
+    untouched; T == 0 returns the supplied state (or zeros).  When any input requires
+    grad the call is recorded for autograd: the backward is ``chunk_bwd`` (gradients to
+    q, k, v, alpha, beta and initial_state)."""
+    if _needs_grad(q, k, v, alpha, beta, initial_state):
+        return _ChunkKDAFn.apply(q, k, v, alpha, beta, initial_state, chunk_size, float(scale))
     return chunk_fwd(q, k, v, alpha, beta, initial_state=initial_state, output_final_state=True,
-                     chunk_size=chunk_size)
+                     chunk_size=chunk_size, scale=scale)

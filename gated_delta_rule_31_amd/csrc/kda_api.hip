@@ -318,3 +318,115 @@ kda_status kda_recurrent_step_fused_gate(const void *q, const void *k, const voi
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t kda_chunk_bwd_workspace_size(int B, int64_t T, int H, int K, int V, int num_seqs, int varlen) {
+    if (B < 0 || T < 0 || H <= 0 || !dim_ok(K) || !dim_ok(V) || num_seqs < 0) return 0;
+    const int64_t slots = kda::chunk_bwd_slots(B, T, num_seqs, varlen != 0);
+    return (size_t)slots * (size_t)H * kda::chunk_bwd_floats_per_slot(K, V) * sizeof(float);
+}
+
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, kda_dtype in_dtype, const float *gate,
+                         kda_gate_kind gate_kind, const float *beta, const float *initial_state,
+                         const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H, int K, int V,
+                         float scale, const void *d_out, kda_dtype dout_dtype, const float *d_final_state,
+                         void *dq, void *dk, void *dv, kda_dtype grad_dtype, float *dgate, float *dbeta,
+                         float *d_initial_state, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
+    if (!dtype_ok(in_dtype) || !dtype_ok(dout_dtype) || !dtype_ok(grad_dtype) || !gate_ok(gate_kind))
+        return KDA_ERR_BAD_DTYPE;
+    if (!dim_ok(K) || !dim_ok(V)) return KDA_ERR_UNSUPPORTED;
+    if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_BAD_ARGUMENT;
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    if (B == 0 || T == 0 || N == 0) {
+        // empty scan: final = initial, so the initial state's gradient is the final state's
+        if (d_initial_state && N > 0 && (const float *)d_initial_state != d_final_state) {
+            hipError_t e = kda::launch_fill_copy(d_initial_state, d_final_state, N * H * (int64_t)K * V, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        return KDA_OK;
+    }
+    if (!q || !k || !v || !gate || !beta || !d_out || !dq || !dk || !dv || !dgate || !dbeta || !workspace)
+        return KDA_ERR_NULL_POINTER;
+    const size_t need = kda_chunk_bwd_workspace_size(B, T, H, K, V, num_seqs, cu_seqlens != nullptr);
+    if (workspace_bytes < need) return KDA_ERR_BAD_ARGUMENT;
+    if (N > 65535 || H > 65535) return KDA_ERR_UNSUPPORTED;
+    const void *ins[] = {q, k, v, gate, beta, initial_state, cu_seqlens, d_out, d_final_state};
+    const void *outs[] = {dq, dk, dv, dgate, dbeta, d_initial_state, workspace};
+    for (int i = 0; i < 7; ++i) {
+        if (!outs[i]) continue;
+        for (const void *p : ins)
+            if (p == outs[i]) return KDA_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return KDA_ERR_ALIAS;
+    }
+    const int64_t slots = kda::chunk_bwd_slots(B, T, num_seqs, cu_seqlens != nullptr);
+    if (slots > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+
+    kda::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.gate = gate_given(gate, gate_kind);
+    a.beta = beta;
+    a.initial_state = initial_state;
+    a.cu_seqlens = cu_seqlens;
+    a.num_seqs = (int)N;
+    a.T = T;
+    a.H = H;
+    a.scale = scale;
+    a.d_out = d_out;
+    a.dout_bf16 = dout_dtype == KDA_BF16;
+    a.d_final_state = d_final_state;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.grad_bf16 = grad_dtype == KDA_BF16;
+    a.dgate = dgate;
+    a.dbeta = dbeta;
+    a.d_initial_state = d_initial_state;
+    a.slots = (int)slots;
+    kda::chunk_bwd_carve(a.w, static_cast<float *>(workspace), slots * H, K, V);
+    hipError_t e = kda::launch_chunk_bwd(a, in_dtype == KDA_F32, K, V, (int)N, stream);
+    return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
+kda_status kda_bounded_decay_bwd(const void *logits, kda_dtype logits_dtype, const float *log_scale,
+                                 const float *bias, float lower_bound, int64_t rows, int H, int K,
+                                 const float *grad, kda_gate_kind grad_kind, void *d_logits,
+                                 kda_dtype dlogits_dtype, float *d_log_scale, float *d_bias, hipStream_t stream) {
+    if (rows < 0 || H <= 0 || K <= 0) return KDA_ERR_BAD_SHAPE;
+    if (!dtype_ok(logits_dtype) || !dtype_ok(dlogits_dtype) || !gate_ok(grad_kind)) return KDA_ERR_BAD_DTYPE;
+    if (!(lower_bound < 0.f)) return KDA_ERR_BAD_ARGUMENT;
+    if (!log_scale) return KDA_ERR_NULL_POINTER;
+    if (rows > 0 && (!logits || !grad || !d_logits)) return KDA_ERR_NULL_POINTER;
+    const void *ins[] = {logits, log_scale, bias, grad};
+    const void *outs[] = {d_logits, d_log_scale, d_bias};
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i]) continue;
+        for (const void *p : ins)
+            if (p == outs[i]) return KDA_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return KDA_ERR_ALIAS;
+    }
+    if (rows == 0 && !d_log_scale && !d_bias) return KDA_OK;
+    kda::GateBwdArgs a;
+    a.logits = logits;
+    a.log_scale = log_scale;
+    a.bias = bias;
+    a.grad = grad;
+    a.d_logits = d_logits;
+    a.d_log_scale = d_log_scale;
+    a.d_bias = d_bias;
+    a.rows = rows;
+    a.H = H;
+    a.K = K;
+    a.lower_bound = lower_bound;
+    a.grad_is_log = grad_kind == KDA_GATE_LOG;
+    a.dlogits_bf16 = dlogits_dtype == KDA_BF16;
+    hipError_t e = kda::launch_bounded_decay_bwd(a, logits_dtype == KDA_F32, stream);
+    return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
+}  // extern "C"

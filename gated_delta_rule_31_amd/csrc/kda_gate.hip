@@ -72,7 +72,69 @@ __global__ __launch_bounds__(256) void bounded_decay_kernel(GateArgs a) {
     }
 }
 
+// Gradients of the gate (the chain rule through g = lower sigmoid(x), x = e^A (z + bias),
+// alpha = e^g): dx = dg lower sigmoid'(x), with dg = grad (grad is dL/dg) or grad alpha,
+// sigmoid'(x) = e^{-|x|} / (1 + e^{-|x|})^2 (no cancellation at either end); dz = e^A dx,
+// d bias[h,c] = sum over rows of dz, d log_scale[h] = sum over rows and channels of x dx.
+// One workgroup per head: thread (row group, channel) walks its rows, the sums over rows
+// are finished in a fixed order in LDS, so every result is reproducible bit for bit.
+template <typename TIn>
+__global__ __launch_bounds__(256) void bounded_decay_bwd_kernel(GateBwdArgs a) {
+    __shared__ float sPart[256];
+    const TIn *z = static_cast<const TIn *>(a.logits);
+    const int h = blockIdx.x, tid = threadIdx.x, K = a.K, H = a.H;
+    const int CW = K < 256 ? K : 256, RG = 256 / CW;  // channels per pass, row groups
+    const int cl = tid % CW, rg = tid / CW;
+    const float sc = expf(a.log_scale[h]), lo = a.lower_bound;
+    float ls = 0.f;
+    for (int cb = 0; cb < K; cb += CW) {
+        const int c = cb + cl;
+        float bsum = 0.f;
+        if (rg < RG && c < K) {
+            const float b = a.bias ? a.bias[h * K + c] : 0.f;
+#pragma unroll 4
+            for (int64_t r = rg; r < a.rows; r += RG) {
+                const int64_t i = (r * H + h) * K + c;
+                const float x = sc * (ld_f32(z, i) + b);
+                const float ex = expf(-fabsf(x));
+                const float inv = 1.f / (1.f + ex);
+                const float sg = x >= 0.f ? inv : ex * inv;
+                const float dg = a.grad_is_log ? a.grad[i] : a.grad[i] * expf(lo * sg);
+                const float dx = dg * lo * ex * inv * inv;
+                const float dz = dx * sc;
+                st_out(a.d_logits, a.dlogits_bf16, i, dz);
+                bsum += dz;
+                ls += dx * x;
+            }
+        }
+        __syncthreads();
+        sPart[tid] = bsum;
+        __syncthreads();
+        if (a.d_bias && tid < CW && cb + tid < K) {
+            float acc = 0.f;
+            for (int j = 0; j < RG; ++j) acc += sPart[j * CW + tid];
+            a.d_bias[h * K + cb + tid] = acc;
+        }
+    }
+    __syncthreads();
+    sPart[tid] = ls;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) sPart[tid] += sPart[tid + s];
+        __syncthreads();
+    }
+    if (tid == 0 && a.d_log_scale) a.d_log_scale[h] = sPart[0];
+}
+
 }  // namespace
+
+hipError_t launch_bounded_decay_bwd(const GateBwdArgs &a, bool fp32_logits, hipStream_t stream) {
+    if (fp32_logits)
+        hipLaunchKernelGGL(bounded_decay_bwd_kernel<float>, dim3(a.H), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(bounded_decay_bwd_kernel<__bf16>, dim3(a.H), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_bounded_decay(const GateArgs &a, bool fp32_logits, hipStream_t stream) {
     const int64_t work = a.vec8 ? a.n / 8 : a.n;

@@ -77,6 +77,58 @@ struct GateArgs {
     int vec8;                       // K % 8 == 0 and 16-byte aligned logits/out
 };
 
+// Intermediates of the chunkwise backward, each [slots * H, ...] float32 (slot = chunk slot)
+struct BwdWork {
+    float *W, *Kd, *Qg, *Kg, *PS, *PdK, *PW;  // [.., C, K]
+    float *U, *Vt, *dVt;                      // [.., C, V]
+    float *Aqk, *Tm, *Abar, *MA, *MT;         // [.., C, C]
+    float *h, *dh;                            // [.., K, V] chunk start state, end-state gradient
+    float *gC, *rs;                           // [.., K]
+    float *dbv;                               // [.., C]
+};
+
+struct BwdArgs {
+    const void *q, *k, *v;          // [B*T, H, K] / [B*T, H, V], bf16 or fp32
+    GateIn gate;                    // GATE_ALPHA or GATE_LOG
+    const float *beta;              // [B*T, H]
+    const float *initial_state;     // [N, H, K, V] or null
+    const int32_t *cu_seqlens;      // [N+1] or null
+    int num_seqs;                   // N with cu_seqlens
+    int64_t T;
+    int H;
+    float scale;
+    const void *d_out;              // [B*T, H, V]
+    int dout_bf16;
+    const float *d_final_state;     // [N, H, K, V] or null
+    void *dq, *dk, *dv;             // like q, k, v
+    int grad_bf16;
+    float *dgate;                   // [B*T, H, K]
+    float *dbeta;                   // [B*T, H]
+    float *d_initial_state;         // [N, H, K, V] or null
+    int slots;                      // chunk slots per head
+    BwdWork w;
+};
+
+// chunk slots per head, workspace floats per (slot, head), and the carving of a workspace
+int64_t chunk_bwd_slots(int B, int64_t T, int num_seqs, bool varlen);
+size_t chunk_bwd_floats_per_slot(int K, int V);
+void chunk_bwd_carve(BwdWork &w, float *base, int64_t slot_heads, int K, int V);
+hipError_t launch_chunk_bwd(const BwdArgs &a, bool fp32_inputs, int K, int V, int num_seqs, hipStream_t stream);
+
+struct GateBwdArgs {
+    const void *logits;
+    const float *log_scale, *bias;
+    const float *grad;              // dL/dalpha or dL/dg
+    void *d_logits;
+    float *d_log_scale, *d_bias;    // [H], [H*K]; either may be null
+    int64_t rows;
+    int H, K;
+    float lower_bound;
+    int grad_is_log;
+    int dlogits_bf16;
+};
+hipError_t launch_bounded_decay_bwd(const GateBwdArgs &a, bool fp32_logits, hipStream_t stream);
+
 hipError_t launch_chunk_fwd(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                             hipStream_t stream, int *bv);
 // the same for a.gate.mode == GATE_LOGITS (kernels that evaluate the gate themselves),

@@ -45,8 +45,8 @@ extern "C" {
 #endif
 
 /* 1: gate, chunk and step entry points; 2: adds the fused-gate variants and the
- * token-recurrent prefill */
-#define KDA_ABI_VERSION 2
+ * token-recurrent prefill; 3: adds the backward (kda_chunk_bwd, kda_bounded_decay_bwd) */
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -232,6 +232,56 @@ kda_status kda_recurrent_step_fused_gate(const void *q, const void *k, const voi
  * if kda_chunk_fwd would return KDA_ERR_UNSUPPORTED for it.
  */
 int kda_chunk_fwd_supported(kda_dtype in_dtype, int K, int V, int chunk_size);
+
+/*
+ * kda_chunk_bwd -- gradients of kda_chunk_fwd (PaperLeet "Return requirements": the scan
+ * passes gradients to q, k, v, alpha, beta and the initial state; "Formula and
+ * conventions": the operations are differentiable).  For the loss
+ *     L = <d_out, out> + <d_final_state, final_state>
+ * of the forward call with the same inputs it writes
+ *   dq, dk [B, T, H, K] and dv [B, T, H, V] in grad_dtype,
+ *   dgate  [B, T, H, K] float32: dL/dalpha (KDA_GATE_ALPHA) or dL/d ln alpha (KDA_GATE_LOG),
+ *          matching how `gate` is given,
+ *   dbeta  [B, T, H] float32,
+ *   d_initial_state [N, H, K, V] float32, or NULL (not wanted).  With initial_state NULL
+ *          the forward started from zeros and this is the gradient at the zero state.
+ * Inputs: q, k, v, gate, gate_kind, beta, initial_state, cu_seqlens, num_seqs, B, T, H,
+ * K, V and scale exactly as given to the forward; d_out [B, T, H, V] in dout_dtype;
+ * d_final_state [N, H, K, V] float32 or NULL (zeros).
+ * The forward is recomputed chunk by chunk (64 tokens) from the inputs; its intermediates
+ * (chunk start states, their gradients, the per-chunk matrices) live in `workspace`, a
+ * device buffer of at least kda_chunk_bwd_workspace_size(...) bytes that the caller owns
+ * (about 0.55 MB per 64-token chunk and head at K = V = 128); its contents on entry do not
+ * matter and on return are unspecified.  KDA_ERR_BAD_ARGUMENT if it is too small.
+ * All arithmetic is float32 (matrix cores for the products).  Supported: K, V in
+ * {16, 32, 64, 128}, N and H up to 65535.  Preconditions as kda_chunk_fwd: every log-decay
+ * >= -5 (alpha > 0).  No output may overlap an input or another output.
+ * T == 0 (or B == 0): no token gradients; d_initial_state = d_final_state (or zeros).
+ */
+size_t kda_chunk_bwd_workspace_size(int B, int64_t T, int H, int K, int V, int num_seqs, int varlen);
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, kda_dtype in_dtype, const float *gate,
+                         kda_gate_kind gate_kind, const float *beta, const float *initial_state,
+                         const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H, int K, int V,
+                         float scale, const void *d_out, kda_dtype dout_dtype, const float *d_final_state,
+                         void *dq, void *dk, void *dv, kda_dtype grad_dtype, float *dgate, float *dbeta,
+                         float *d_initial_state, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_bounded_decay_bwd -- gradients of kda_bounded_decay (PaperLeet "Return
+ * requirements": bounded_decay passes gradients to the logits and the log-scale).
+ *   grad        [rows, H, K] float32: dL/dalpha (grad_kind KDA_GATE_ALPHA) or dL/dg
+ *               (KDA_GATE_LOG), for the gate evaluated from logits, log_scale, bias and
+ *               lower_bound as in kda_bounded_decay
+ *   d_logits    [rows, H, K] in dlogits_dtype
+ *   d_log_scale [H] float32 or NULL;  d_bias [H*K] float32 or NULL (the gradient a
+ *               featurewise bias receives; valid whether or not `bias` is given)
+ * The sums over rows are done in a fixed order (bit-reproducible); float32 throughout.
+ * rows == 0 writes zeros to d_log_scale and d_bias.
+ */
+kda_status kda_bounded_decay_bwd(const void *logits, kda_dtype logits_dtype, const float *log_scale,
+                                 const float *bias, float lower_bound, int64_t rows, int H, int K,
+                                 const float *grad, kda_gate_kind grad_kind, void *d_logits,
+                                 kda_dtype dlogits_dtype, float *d_log_scale, float *d_bias, hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 const char *kda_status_string(kda_status s);

@@ -194,3 +194,12 @@ def retention(shape, seed=0, device="cpu", lo_log=-5.0, hi_log=0.0) -> torch.Ten
     gen = _gen(device, seed)
     u = torch.rand(shape, generator=gen, device=device, dtype=torch.float64)
     return torch.exp(lo_log + (hi_log - lo_log) * u).float()
+
+
+def cotangents(B, T, H, V, K, N, seed=0, device="cpu", final=True):
+    """Seeded upstream gradients for a backward call: d_out ~ N(0,1) [B,T,H,V] float32 and
+    d_final_state ~ N(0,1) [N,H,K,V] float32 (None when ``final`` is False)."""
+    gen = _gen(device, seed)
+    d_out = _normal((B, T, H, V), gen, device)
+    d_fin = _normal((N, H, K, V), gen, device) if final else None
+    return d_out, d_fin

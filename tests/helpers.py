@@ -37,6 +37,26 @@ def err_bf16(got, ref) -> float:
     return float(np.max(np.abs(got - ref)) / (rms if rms > 0 else 1.0))
 
 
+def dg_scale(q, dq, k, dk) -> float:
+    """Size of the per-row terms q*dq and k*dk whose reverse in-chunk sum is d ln alpha.
+    Token pairs that both lie in the summed range contribute equal and opposite terms, so
+    d ln alpha can be far smaller than its terms and its rounding error scales with the
+    terms: the gate gradient's error is measured against max(rms(d ln alpha), this)."""
+    q, dq, k, dk = f64(q), f64(dq), f64(k), f64(dk)
+    return float(np.sqrt(np.mean((q * dq) ** 2)) + np.sqrt(np.mean((k * dk) ** 2)))
+
+
+def err_floor(got, ref, floor: float, fp32: bool) -> float:
+    """err_fp32 / err_bf16 with the RMS in the denominator raised to at least ``floor``."""
+    got, ref = f64(got), f64(ref)
+    if ref.size == 0:
+        return 0.0
+    den0 = max(float(np.sqrt(np.mean(ref ** 2))), floor)
+    if fp32:
+        return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), den0)))
+    return float(np.max(np.abs(got - ref)) / den0)
+
+
 def assert_close(got, ref, fp32: bool, what: str = ""):
     e = err_fp32(got, ref) if fp32 else err_bf16(got, ref)
     tol = FP32_TOL if fp32 else BF16_TOL

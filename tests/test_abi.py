@@ -37,7 +37,7 @@ def test_status_strings_and_version(lib):
     assert lib.kda_status_string(0) == b"ok"
     for s in range(1, 8):
         assert lib.kda_status_string(s) not in (b"", b"unknown status")
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
 
 
 def _chunk(lib, **kw):
@@ -56,7 +56,8 @@ def _chunk(lib, **kw):
              a["out_dtype"], None)
 
 
-# Each case is rejected on the host before any HIP call (the pointers are fake).
+# Each case is rejected on the host before any HIP call (the pointers are fake); the same
+# holds for every call in the backward validation tests below.
 @pytest.mark.parametrize("kw,status", [
     (dict(K=17), 4), (dict(V=256), 4), (dict(C=48), 4), (dict(H=0), 2), (dict(T=-1), 2),
     (dict(in_dtype=7), 3), (dict(gate_kind=5), 3), (dict(q=None), 1), (dict(out=None), 1),
@@ -152,3 +153,53 @@ def test_recurrent_fwd_validation(lib):
                   i32, i32, f32, vp, i32, vp]
     assert g(1, 2, 3, 1, 4, 8, None, 0.0, 0, 5, None, None, None, 0, 1, 8, 2, 16, 16, 1.0, 6, 1, None) == 5
     assert g(1, 2, 3, 1, 4, None, None, -9.0, 0, 5, None, None, None, 0, 1, 8, 2, 16, 16, 1.0, 6, 1, None) == 1
+
+
+def test_chunk_bwd_validation(lib):
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    ws = lib.kda_chunk_bwd_workspace_size
+    ws.restype = sz
+    ws.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    need = ws(1, 64, 2, 16, 16, 0, 0)
+    assert need > 0 and ws(1, 64, 2, 24, 16, 0, 0) == 0
+    assert ws(2, 130, 3, 32, 64, 0, 0) == 6 * ws(1, 64, 3, 32, 64, 0, 0)  # 3 chunks per batch row
+    assert ws(1, 130, 3, 32, 64, 4, 1) == 6 * ws(1, 64, 3, 32, 64, 0, 0)  # varlen: T // 64 + N slots
+    f = lib.kda_chunk_bwd
+    f.restype = i32
+    f.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp, i32, vp, vp, vp,
+                  vp, i32, vp, vp, vp, vp, sz, vp]
+
+    def call(q=1, K=16, T=64, B=1, cu=None, ns=0, dq=11, dgate=14, gk=0, dt=1, wsz=need, work=20, ds0=None):
+        return f(q, 2, 3, dt, 4, gk, 5, None, cu, ns, B, T, 2, K, 16, 1.0, 6, 1, None, dq, 12, 13, 1, dgate, 15,
+                 ds0, work, wsz, None)
+    assert call(K=24) == 4
+    assert call(T=-1) == 2
+    assert call(dt=5) == 3
+    assert call(gk=4) == 3
+    assert call(q=None) == 1
+    assert call(work=None) == 1
+    assert call(wsz=need - 1) == 5           # workspace too small
+    assert call(dq=2) == 6                   # dq aliases k
+    assert call(dgate=11) == 6               # two outputs share a buffer
+    assert call(ds0=6) == 6                  # d_initial_state aliases d_out
+    assert call(cu=9, B=2, ns=1) == 5
+    assert call(T=0, q=None, work=None) == 0  # empty: no token gradients, no d_initial_state asked
+
+
+def test_bounded_decay_bwd_validation(lib):
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    f = lib.kda_bounded_decay_bwd
+    f.restype = i32
+    f.argtypes = [vp, i32, vp, vp, f32, i64, i32, i32, vp, i32, vp, i32, vp, vp, vp]
+
+    def call(z=1, ls=2, lb=-5.0, rows=4, H=2, K=8, g=3, gk=0, dz=4, dt=0, dls=5, db=6):
+        return f(z, 1, ls, None, lb, rows, H, K, g, gk, dz, dt, dls, db, None)
+    assert call(lb=0.0) == 5
+    assert call(H=0) == 2
+    assert call(gk=3) == 3
+    assert call(dt=7) == 3
+    assert call(ls=None) == 1
+    assert call(g=None) == 1
+    assert call(dz=3) == 6                   # d_logits aliases grad
+    assert call(db=5) == 6                   # d_bias and d_log_scale share a buffer
+    assert call(rows=0, z=None, g=None, dz=None, dls=None, db=None) == 0

@@ -3,7 +3,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.chunk_model import _bf16, chunk_scan
+from tests.chunk_model import _bf16, chunk_scan, chunk_scan_bwd
+from tests.helpers import dg_scale
 
 
 def _inputs(rs, T, K, V, regime):
@@ -68,3 +69,46 @@ def test_chunk_model_mixed_operands_within_bf16_tolerance(regime, C):
     for got, ref in ((o, eo), (f, ef)):
         err = np.abs(got - ref).max() / np.sqrt(np.mean(ref ** 2))
         assert err < 1e-2, err
+
+
+# --- backward ---------------------------------------------------------------------------
+
+def _oracle_bwd(q, k, v, g, beta, s0, do, dsT, scale):
+    E = lambda x: x[None, :, None]
+    r = oracle.scan_bwd(E(q), E(k), E(v), E(np.exp(g)), E(beta), E(do), s0[None, None], dsT[None, None],
+                        scale=scale)
+    # the chunked form differentiates with respect to g = ln alpha: dg = alpha * dalpha
+    return [r[0][0, :, 0], r[1][0, :, 0], r[2][0, :, 0], r[3][0, :, 0] * np.exp(g), r[4][0, :, 0], r[5][0, 0]]
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("regime", ["mid", "fast", "slow"])
+def test_chunk_model_bwd_fp64_equals_oracle(C, regime):
+    rs = np.random.default_rng(200 + C)
+    q, k, v, g, beta, s0 = _inputs(rs, 150, 32, 24, regime)
+    do = rs.standard_normal((150, 24))
+    dsT = rs.standard_normal((32, 24))
+    ref = _oracle_bwd(q, k, v, g, beta, s0, do, dsT, 0.7)
+    got = chunk_scan_bwd(q, k, v, g, beta, do, s0, dsT, C=C, scale=0.7)
+    for name, a, b in zip("dq dk dv dg dbeta ds0".split(), got, ref):
+        assert np.abs(a - b).max() <= 1e-11 * np.abs(b).max(), name
+
+
+@pytest.mark.parametrize("regime", ["mid", "fast", "slow"])
+def test_chunk_model_bwd_fp32_within_tolerance(regime):
+    """float32 with the 16-row middle-row rescaling: no overflow near the decay bound, every
+    gradient within 1e-4 (d ln alpha relative to the size of its terms, see dg_scale)."""
+    rs = np.random.default_rng(5)
+    q, k, v, g, beta, s0 = _inputs(rs, 200, 128, 128, regime)
+    do = rs.standard_normal((200, 128))
+    dsT = rs.standard_normal((128, 128))
+    ref = _oracle_bwd(q, k, v, g, beta, s0, do, dsT, 0.5)
+    f32 = [x.astype(np.float32) for x in (q, k, v, g, beta, do, s0, dsT)]
+    with np.errstate(over="raise", invalid="raise"):
+        got = chunk_scan_bwd(*f32[:6], s0=f32[6], dsT=f32[7], C=64, scale=0.5, dtype=np.float32)
+    for name, a, b in zip("dq dk dv dg dbeta ds0".split(), got, ref):
+        floor = np.sqrt(np.mean(b ** 2))
+        if name == "dg":
+            floor = max(floor, dg_scale(q, ref[0], k, ref[1]))
+        err = np.abs(a - b) / np.maximum(np.abs(b), floor)
+        assert err.max() < 1e-4, (name, err.max())

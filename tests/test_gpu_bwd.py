@@ -1,0 +1,222 @@
+"""GPU parity of the backward (kda_chunk_bwd, kda_bounded_decay_bwd and the autograd
+wrappers) against the fp64 oracle's gradients, on seeded inputs.
+
+Tolerances: float32 inputs -- max relative error 1e-4 (element error relative to
+max(|ref|, rms(ref))); bfloat16 inputs -- max error 2e-2 of the oracle's RMS.  The gate
+gradient d ln alpha is a reverse in-chunk sum of per-row terms q*dq - k*dk that cancel in
+pairs, so its error is measured against the size of those terms as well (helpers.dg_scale).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import BF16_TOL, FP32_TOL, dg_scale, err_bf16, err_floor, err_fp32, f64
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dgate", "dbeta", "d_initial_state")
+
+
+def _case(B, T, H, K, V, dtype=torch.float32, seed=0, seqlens=None, state=True, dstate=True):
+    inp = synth.make_prefill(B, T, H, K, V, dtype=dtype, seed=seed, state_std=0.3 if state else None,
+                             seqlens=seqlens)
+    alpha = synth.retention((B, T, H, K), seed=seed + 100)
+    N = inp.num_seqs
+    d_out, d_fin = synth.cotangents(B, T, H, V, K, N, seed=seed + 200, final=dstate)
+    return inp, alpha, d_out, d_fin
+
+
+def _oracle(inp, alpha, d_out, d_fin, scale):
+    cu = None if inp.cu_seqlens is None else f64(inp.cu_seqlens).astype(np.int64)
+    return oracle.scan_bwd(f64(inp.q), f64(inp.k), f64(inp.v), f64(alpha), f64(inp.beta), f64(d_out),
+                           None if inp.initial_state is None else f64(inp.initial_state),
+                           None if d_fin is None else f64(d_fin), cu_seqlens=cu, scale=scale)
+
+
+def _gpu(inp, alpha, d_out, d_fin, scale, gate_is_log=False, grad_dtype=torch.float32, dout_dtype=None):
+    import gated_delta_rule_31_amd as kda
+    d = lambda x: None if x is None else x.cuda()
+    gate = alpha.cuda()
+    if gate_is_log:
+        gate = torch.log(gate)
+    do = d_out.to(dout_dtype or torch.float32).cuda()
+    return kda.chunk_bwd(d(inp.q), d(inp.k), d(inp.v), gate, d(inp.beta), do, initial_state=d(inp.initial_state),
+                         d_final_state=d(d_fin), cu_seqlens=d(inp.cu_seqlens), scale=scale, gate_is_log=gate_is_log,
+                         grad_dtype=grad_dtype)
+
+
+def _compare(got, ref, inp, alpha, gate_is_log, fp32, what=""):
+    """Every gradient against the oracle; the gate gradient compared as d ln alpha."""
+    a64 = f64(alpha)
+    errs = {}
+    for i, name in enumerate(NAMES):
+        g, r = f64(got[i]), ref[i]
+        if name == "dgate":
+            r = r * a64                         # oracle gives dL/dalpha
+            if not gate_is_log:
+                g = g * a64
+            floor = dg_scale(inp.q, ref[0], inp.k, ref[1])
+            e = err_floor(g, r, floor, fp32)
+        else:
+            e = err_fp32(g, r) if fp32 else err_bf16(g, r)
+        assert np.all(np.isfinite(g)), "%s %s: non-finite" % (what, name)
+        errs[name] = e
+    tol = FP32_TOL if fp32 else BF16_TOL
+    bad = {n: e for n, e in errs.items() if e > tol}
+    assert not bad, "%s: %s (tol %.0e; all %s)" % (what, bad, tol, errs)
+    return errs
+
+
+@pytest.mark.parametrize("gate_is_log", [False, True])
+def test_bwd_fp32_oracle(gate_is_log):
+    """B2 T150 (two full chunks and a ragged tail) H3 K32 V64, initial state, final-state
+    gradient, read scale 0.7."""
+    inp, alpha, d_out, d_fin = _case(2, 150, 3, 32, 64, seed=11)
+    ref = _oracle(inp, alpha, d_out, d_fin, 0.7)
+    got = _gpu(inp, alpha, d_out, d_fin, 0.7, gate_is_log=gate_is_log)
+    _compare(got, ref, inp, alpha, gate_is_log, True, "fp32 log=%s" % gate_is_log)
+
+
+@pytest.mark.parametrize("K,V,T", [(16, 16, 64), (64, 128, 70), (128, 32, 129), (128, 128, 100)])
+def test_bwd_fp32_shapes(K, V, T):
+    inp, alpha, d_out, d_fin = _case(1, T, 2, K, V, seed=12 + K + V)
+    ref = _oracle(inp, alpha, d_out, d_fin, 1.0)
+    got = _gpu(inp, alpha, d_out, d_fin, 1.0)
+    _compare(got, ref, inp, alpha, False, True, "K%d V%d T%d" % (K, V, T))
+
+
+def test_bwd_bf16_inputs():
+    """bf16 q, k, v and d_out (the model's types) at K = V = 128.  Parity is judged on the
+    float32 gradients; bf16 gradients are those values rounded once more (that rounding
+    alone can exceed 2e-2 of the RMS on heavy-tailed gradients), checked bit for bit."""
+    inp, alpha, d_out, d_fin = _case(1, 300, 2, 128, 128, dtype=torch.bfloat16, seed=13)
+    d_out = d_out.to(torch.bfloat16)
+    ref = _oracle(inp, alpha, d_out, d_fin, 1.0)
+    got = _gpu(inp, alpha, d_out, d_fin, 1.0, dout_dtype=torch.bfloat16)
+    _compare(got, ref, inp, alpha, False, False, "bf16 inputs")
+    low = _gpu(inp, alpha, d_out, d_fin, 1.0, grad_dtype=torch.bfloat16, dout_dtype=torch.bfloat16)
+    for i in range(3):
+        assert low[i].dtype == torch.bfloat16
+        assert torch.equal(low[i], got[i].to(torch.bfloat16)), NAMES[i]
+    for i in range(3, 6):
+        assert torch.equal(low[i], got[i]), NAMES[i]
+
+
+def test_bwd_varlen():
+    """Packed sequences with a zero-length one (its initial-state gradient is its final-
+    state gradient), a one-token one and chunk-aligned / ragged lengths."""
+    lens = [5, 0, 130, 64, 1, 77]
+    inp, alpha, d_out, d_fin = _case(1, sum(lens), 2, 64, 64, seed=14, seqlens=lens)
+    ref = _oracle(inp, alpha, d_out, d_fin, 1.0)
+    got = _gpu(inp, alpha, d_out, d_fin, 1.0)
+    _compare(got, ref, inp, alpha, False, True, "varlen")
+    assert torch.equal(got[5][1].cpu(), d_fin[1])
+
+
+def test_bwd_no_states():
+    """No initial state (the gradient is taken at the zero state) and no final-state
+    gradient."""
+    inp, alpha, d_out, _ = _case(2, 90, 2, 32, 32, seed=15, state=False, dstate=False)
+    ref = _oracle(inp, alpha, d_out, None, 1.0)
+    got = _gpu(inp, alpha, d_out, None, 1.0)
+    _compare(got, ref, inp, alpha, False, True, "no states")
+
+
+def test_bwd_empty_sequence():
+    import gated_delta_rule_31_amd as kda
+    inp, alpha, d_out, d_fin = _case(2, 0, 2, 16, 32, seed=16)
+    d = lambda x: x.cuda()
+    res = kda.chunk_bwd(d(inp.q), d(inp.k), d(inp.v), d(alpha), d(inp.beta), d(d_out),
+                        initial_state=d(inp.initial_state), d_final_state=d(d_fin))
+    torch.cuda.synchronize()
+    assert res[0].shape == (2, 0, 2, 16) and res[2].shape == (2, 0, 2, 32)
+    assert torch.equal(res[5].cpu(), d_fin)
+
+
+def test_bwd_deterministic():
+    """No atomics: two calls give bitwise equal gradients."""
+    inp, alpha, d_out, d_fin = _case(1, 200, 3, 64, 64, dtype=torch.bfloat16, seed=17)
+    a = _gpu(inp, alpha, d_out, d_fin, 1.0)
+    b = _gpu(inp, alpha, d_out, d_fin, 1.0)
+    torch.cuda.synchronize()
+    for x, y, n in zip(a, b, NAMES):
+        assert torch.equal(x, y), n
+
+
+def test_bwd_k3_full_size_sampled_heads():
+    """The K3 prefill shape (B1 T8192 H96 K=V=128, bf16) in one call; two heads checked
+    against the oracle over the whole sequence (heads are independent)."""
+    inp = synth.k3_prefill()
+    B, T, H, K, V = inp.dims
+    alpha = synth.retention((B, T, H, K), seed=103)
+    d_out, d_fin = synth.cotangents(B, T, H, V, K, 1, seed=203)
+    d_out = d_out.to(torch.bfloat16)
+    got = _gpu(inp, alpha, d_out, d_fin, 1.0, dout_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    heads = [5, 71]
+    sub = synth.PrefillInputs(name="k3 heads", q=inp.q[:, :, heads], k=inp.k[:, :, heads], v=inp.v[:, :, heads],
+                              z=inp.z[:, :, heads], log_scale=inp.log_scale[heads], beta=inp.beta[:, :, heads],
+                              initial_state=None if inp.initial_state is None else inp.initial_state[:, heads],
+                              cu_seqlens=None)
+    ref = _oracle(sub, alpha[:, :, heads], d_out[:, :, heads], d_fin[:, heads], 1.0)
+    got_h = [x[:, :, heads] if i < 5 else x[:, heads] for i, x in enumerate(got)]
+    _compare(got_h, ref, sub, alpha[:, :, heads], False, False, "K3 heads %s" % heads)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("grad_is_log", [False, True])
+def test_bounded_decay_bwd(dtype, grad_is_log):
+    """Gate gradients into logits, log-scale and bias; K = 40 exercises partial channel
+    groups."""
+    import gated_delta_rule_31_amd as kda
+    g = torch.Generator().manual_seed(21)
+    rows, H, K = 300, 3, 40
+    z = torch.randn(rows, H, K, generator=g).to(dtype)
+    A = 0.5 * torch.randn(H, generator=g)
+    bias = torch.randn(H, K, generator=g)
+    w = torch.randn(rows, H, K, generator=g)
+    dz, dls, db = kda.bounded_decay_bwd(z.cuda(), A.cuda(), w.cuda(), lower_bound=-5.0, bias=bias.cuda(),
+                                        grad_is_log=grad_is_log, dlogits_dtype=torch.float32)
+    rz, rls, rb = oracle.bounded_decay_bwd(f64(z), f64(A), f64(w), g_min=-5.0, bias=f64(bias),
+                                           grad_is_log=grad_is_log)
+    for got, ref, n in ((dz, rz, "dz"), (dls, rls, "dlog_scale"), (db, rb, "dbias")):
+        e = err_fp32(got, ref)
+        assert e <= FP32_TOL, (n, e)
+
+
+def test_autograd_recurrent_kda():
+    """recurrent_kda records autograd: out and final state feed a loss, backward reaches q,
+    k, v, alpha, beta and the initial state with the oracle's gradients."""
+    import gated_delta_rule_31_amd as kda
+    inp, alpha, d_out, d_fin = _case(2, 100, 2, 32, 32, seed=22)
+    leaves = [x.cuda().requires_grad_() for x in (inp.q, inp.k, inp.v, alpha, inp.beta, inp.initial_state)]
+    out, fin = kda.recurrent_kda(*leaves)
+    loss = (out.float() * d_out.cuda()).sum() + (fin * d_fin.cuda()).sum()
+    loss.backward()
+    got = [x.grad for x in leaves]
+    ref = _oracle(inp, alpha, d_out, d_fin, 1.0)
+    _compare(got, ref, inp, alpha, False, True, "autograd")
+
+
+def test_autograd_gate_into_scan():
+    """bounded_decay -> recurrent_kda end to end: the logits, log-scale and bias receive the
+    chain of the scan's alpha gradient through the gate."""
+    import gated_delta_rule_31_amd as kda
+    inp, _, d_out, d_fin = _case(1, 96, 2, 32, 32, seed=23)
+    bias = 0.3 * torch.randn(2, 32, generator=torch.Generator().manual_seed(24))
+    z, ls, b = (x.cuda().requires_grad_() for x in (inp.z, inp.log_scale, bias))
+    alpha = kda.bounded_decay(z, ls, lower_bound=-5.0, bias=b)
+    out, fin = kda.recurrent_kda(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), alpha, inp.beta.cuda(),
+                                 inp.initial_state.cuda())
+    ((out.float() * d_out.cuda()).sum() + (fin * d_fin.cuda()).sum()).backward()
+    a64 = oracle.bounded_decay(f64(inp.z), f64(inp.log_scale), g_min=-5.0, bias=f64(bias))
+    r = oracle.scan_bwd(f64(inp.q), f64(inp.k), f64(inp.v), a64, f64(inp.beta), f64(d_out),
+                        f64(inp.initial_state), f64(d_fin))
+    rz, rls, rb = oracle.bounded_decay_bwd(f64(inp.z), f64(inp.log_scale), r[3], g_min=-5.0, bias=f64(bias))
+    # dz is dalpha times a bounded factor; its terms cancel like d ln alpha's
+    floor = dg_scale(inp.q, r[0], inp.k, r[1]) * 5.0 / 4.0
+    assert err_floor(z.grad, rz, floor, True) <= FP32_TOL
+    assert err_fp32(b.grad, rb) <= 10 * FP32_TOL
+    assert err_fp32(ls.grad, rls) <= 10 * FP32_TOL
