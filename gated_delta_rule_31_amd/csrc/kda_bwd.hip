@@ -98,6 +98,30 @@ __device__ __forceinline__ float ld_any(const void *p, int is_bf16, int64_t i) {
     return is_bf16 ? (float)static_cast<const __bf16 *>(p)[i] : static_cast<const float *>(p)[i];
 }
 
+// Workgroups go to the 8 XCDs round-robin by block index, and each XCD has its own L2.
+// Block b is mapped to (unit, sub) so that the nsub blocks of one unit, which read the same
+// per-chunk data, run on the same XCD one after another: the grid is 8 * nsub * ceil(units / 8)
+// blocks and a unit index past the last unit has no work.
+__device__ __forceinline__ void xcd_map(int b, int nsub, int &unit, int &sub) {
+    const int x = b & 7, j = b >> 3;
+    sub = j % nsub;
+    unit = (j / nsub) * 8 + x;
+}
+
+// four consecutive elements as float (16-byte / 8-byte aligned loads)
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 ld4(const __bf16 *p) {
+    const s16x4 x = *reinterpret_cast<const s16x4 *>(p);
+    return make_float4(__builtin_bit_cast(float, (uint32_t)(uint16_t)x[0] << 16),
+                       __builtin_bit_cast(float, (uint32_t)(uint16_t)x[1] << 16),
+                       __builtin_bit_cast(float, (uint32_t)(uint16_t)x[2] << 16),
+                       __builtin_bit_cast(float, (uint32_t)(uint16_t)x[3] << 16));
+}
+__device__ __forceinline__ float4 ld4_any(const void *p, int is_bf16, int64_t i) {
+    return is_bf16 ? ld4(static_cast<const __bf16 *>(p) + i) : ld4(static_cast<const float *>(p) + i);
+}
+__device__ __forceinline__ void st4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
+
 // sum over the 16 lanes that share lane >> 4 (one accumulator row)
 __device__ __forceinline__ float row16_sum(float x) {
     x += __shfl_xor(x, 1);
@@ -269,17 +293,26 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// states: the forward over chunks, one workgroup per (value block, head, sequence)
+// states: the forward over chunks, one workgroup per (value block, head, sequence).
+// A chunk step has two phases: the pseudo-values Vt = U - W S (wave w: rows of tile w),
+// then S = gamma_C S + Kd^T Vt (wave w: key tiles w, w + 4, ...).  Each phase's matrix
+// operands go straight from memory into registers in fragment order (the reduction index
+// permuted as k = 16 q + 4 (lane / 16) + s on both operands), and each wave loads one
+// phase's operands while the other phase computes.
 constexpr int SBV = 16;  // value columns per workgroup in the serial passes
 
 template <int K, int V>
 __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdArgs a) {
-    constexpr int LB = SBV + 4;
+    constexpr int LB = SBV + 4, KQ = K / 16, NST = (K / 16 + 3) / 4;
     __shared__ float sS[K * LB];
     __shared__ float sV[BC * LB];
-    const int vb = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = a.H;
+    int hs, vb;  // (sequence, head) unit; the value blocks of one unit share an XCD
+    xcd_map(blockIdx.x, V / SBV, hs, vb);
+    const int H = a.H;
+    if (hs >= a.num_seqs * H) return;
+    const int h = hs % H, s = hs / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
-    const int j0 = vb * SBV;
+    const int j0 = vb * SBV, p = w;
     int64_t t0, len;
     int base;
     seq_range(s, a.cu_seqlens, a.T, t0, len, base);
@@ -288,58 +321,99 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdArgs a) {
         const int r = i / SBV, c = i % SBV;
         sS[r * LB + c] = a.initial_state ? a.initial_state[(((int64_t)s * H + h) * K + r) * V + j0 + c] : 0.f;
     }
+    float4 wf[KQ];
+    float uf[4], kdf[NST][16], gcf[NST][4];
+    auto loadA = [&](int64_t sh) {  // W rows of tile p, U on the tile's outputs
+        const float *W = a.w.W + sh * BC * K + (16 * p + i16) * K + 4 * g4;
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) wf[q] = ld4(W + 16 * q);
+        const float *U = a.w.U + sh * BC * V + j0 + i16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uf[e] = U[(16 * p + 4 * g4 + e) * V];
+    };
+    auto loadB = [&](int64_t sh) {  // Kd columns of this wave's key tiles, gamma_C on their rows
+        const float *Kd = a.w.Kd + sh * BC * K, *gC = a.w.gC + sh * K;
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int rt = w + 4 * i;
+            if (rt < K / 16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) kdf[i][4 * q + u] = Kd[(16 * q + 4 * g4 + u) * K + 16 * rt + i16];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gcf[i][e] = gC[16 * rt + 4 * g4 + e];
+            }
+        }
+    };
+    if (nch > 0) loadA((int64_t)base * H + h);
     for (int j = 0; j < nch; ++j) {
         const int64_t sh = (int64_t)(base + j) * H + h;
+        loadB(sh);
         __syncthreads();
         float *hp = a.w.h + sh * K * V;
         for (int i = tid; i < K * SBV; i += NTH) {
             const int r = i / SBV, c = i % SBV;
             hp[r * V + j0 + c] = sS[r * LB + c];
         }
-        const float *W = a.w.W + sh * BC * K, *U = a.w.U + sh * BC * V;
-        float *Vt = a.w.Vt + sh * BC * V;
-        for (int t = w; t < NP * (SBV / 16); t += 4) {
-            const int p = t / (SBV / 16), ct = t % (SBV / 16);
+        {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int k0 = 0; k0 < K; k0 += 4)
-                acc = mf(W[(16 * p + i16) * K + k0 + g4], sS[(k0 + g4) * LB + 16 * ct + i16], acc);
+#pragma unroll
+            for (int q = 0; q < KQ; ++q) {
+                const float *b = sS + (16 * q + 4 * g4) * LB + i16;
+                acc = mf(wf[q].x, b[0], acc);
+                acc = mf(wf[q].y, b[LB], acc);
+                acc = mf(wf[q].z, b[2 * LB], acc);
+                acc = mf(wf[q].w, b[3 * LB], acc);
+            }
+            float *Vt = a.w.Vt + sh * BC * V + j0 + i16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = 16 * p + 4 * g4 + e, col = 16 * ct + i16;
-                const float vt = U[row * V + j0 + col] - acc[e];
-                sV[row * LB + col] = vt;
-                Vt[row * V + j0 + col] = vt;
+                const int row = 16 * p + 4 * g4 + e;
+                const float vt = uf[e] - acc[e];
+                sV[row * LB + i16] = vt;
+                Vt[row * V] = vt;
             }
         }
         __syncthreads();
-        const float *Kd = a.w.Kd + sh * BC * K, *gC = a.w.gC + sh * K;
-        for (int t = w; t < (K / 16) * (SBV / 16); t += 4) {
-            const int rt = t / (SBV / 16), ct = t % (SBV / 16);
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int r0 = 0; r0 < BC; r0 += 4)
-                acc = mf(Kd[(r0 + g4) * K + 16 * rt + i16], sV[(r0 + g4) * LB + 16 * ct + i16], acc);
+        if (j + 1 < nch) loadA(sh + H);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = 16 * rt + 4 * g4 + e, col = 16 * ct + i16;
-                sS[m * LB + col] = gC[m] * sS[m * LB + col] + acc[e];
+        for (int i = 0; i < NST; ++i) {
+            const int rt = w + 4 * i;
+            if (rt < K / 16) {
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        acc = mf(kdf[i][4 * q + u], sV[(16 * q + 4 * g4 + u) * LB + i16], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 16 * rt + 4 * g4 + e;
+                    sS[m * LB + i16] = gcf[i][e] * sS[m * LB + i16] + acc[e];
+                }
             }
         }
     }
 }
 
 // ------------------------------------------------------------------------------------
-// dstates: the reverse over chunks
+// dstates: the reverse over chunks, the same two-phase structure:
+//   dVt = Kd dS' + A_qk^T dO (wave w: rows of tile w),
+//   dS  = gamma_C dS' + Qg^T dO - W^T dVt (wave w: key tiles w, w + 4, ...)
 template <int K, int V>
 __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
-    constexpr int LB = SBV + 4;
+    constexpr int LB = SBV + 4, KQ = K / 16, NST = (K / 16 + 3) / 4;
     __shared__ float sD[K * LB];
     __shared__ float sO[BC * LB];
     __shared__ float sV[BC * LB];
-    const int vb = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = a.H;
+    int hs, vb;
+    xcd_map(blockIdx.x, V / SBV, hs, vb);
+    const int H = a.H;
+    if (hs >= a.num_seqs * H) return;
+    const int h = hs % H, s = hs / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
-    const int j0 = vb * SBV;
+    const int j0 = vb * SBV, p = w;
     int64_t t0, len;
     int base;
     seq_range(s, a.cu_seqlens, a.T, t0, len, base);
@@ -349,54 +423,103 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
         const int r = i / SBV, c = i % SBV;
         sD[r * LB + c] = a.d_final_state ? a.d_final_state[(st + r) * V + j0 + c] : 0.f;
     }
-    for (int j = nch - 1; j >= 0; --j) {
+    const int sr = tid >> 2, sg = 4 * (tid & 3);  // dO staging: row and first column of this thread
+    float4 kdf[KQ], dof;
+    float aqf[16], qgf[NST][16], wwf[NST][16], gcf[NST][4];
+    auto loadA = [&](int j) {  // Kd rows and A_qk columns of tile p, and this chunk's dO slice
         const int64_t sh = (int64_t)(base + j) * H + h;
+        const float *Kd = a.w.Kd + sh * BC * K + (16 * p + i16) * K + 4 * g4;
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) kdf[q] = ld4(Kd + 16 * q);
+        const float *Aqk = a.w.Aqk + sh * BC * BC + 16 * p + i16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) aqf[4 * q + u] = q >= p ? Aqk[(16 * q + 4 * g4 + u) * BC] : 0.f;
         const int64_t tc = t0 + (int64_t)j * BC;
         const int L = (int)min((int64_t)BC, len - (int64_t)j * BC);
+        dof = sr < L ? ld4_any(a.d_out, a.dout_bf16, ((tc + sr) * H + h) * V + j0 + sg)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto loadB = [&](int j) {  // Qg and W columns of this wave's key tiles, gamma_C on their rows
+        const int64_t sh = (int64_t)(base + j) * H + h;
+        const float *Qg = a.w.Qg + sh * BC * K, *W = a.w.W + sh * BC * K, *gC = a.w.gC + sh * K;
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int rt = w + 4 * i;
+            if (rt < K / 16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = 16 * q + 4 * g4 + u;
+                        qgf[i][4 * q + u] = Qg[r * K + 16 * rt + i16];
+                        wwf[i][4 * q + u] = W[r * K + 16 * rt + i16];
+                    }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gcf[i][e] = gC[16 * rt + 4 * g4 + e];
+            }
+        }
+    };
+    if (nch > 0) loadA(nch - 1);
+    for (int j = nch - 1; j >= 0; --j) {
+        const int64_t sh = (int64_t)(base + j) * H + h;
+        loadB(j);
         __syncthreads();
         float *dhp = a.w.dh + sh * K * V;
         for (int i = tid; i < K * SBV; i += NTH) {
             const int r = i / SBV, c = i % SBV;
             dhp[r * V + j0 + c] = sD[r * LB + c];
         }
-        for (int i = tid; i < BC * SBV; i += NTH) {
-            const int r = i / SBV, c = i % SBV;
-            sO[r * LB + c] = r < L ? a.scale * ld_any(a.d_out, a.dout_bf16, ((tc + r) * H + h) * V + j0 + c) : 0.f;
-        }
+        const float sc = a.scale;
+        *reinterpret_cast<float4 *>(sO + sr * LB + sg) = make_float4(sc * dof.x, sc * dof.y, sc * dof.z, sc * dof.w);
         __syncthreads();
-        const float *Kd = a.w.Kd + sh * BC * K, *Aqk = a.w.Aqk + sh * BC * BC;
-        float *dVt = a.w.dVt + sh * BC * V;
-        for (int t = w; t < NP * (SBV / 16); t += 4) {
-            const int p = t / (SBV / 16), ct = t % (SBV / 16);
+        {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int k0 = 0; k0 < K; k0 += 4)
-                acc = mf(Kd[(16 * p + i16) * K + k0 + g4], sD[(k0 + g4) * LB + 16 * ct + i16], acc);
-            // A_qk^T dO: A_qk[s][r] is zero for s < r
-            for (int s0 = 16 * p; s0 < BC; s0 += 4)
-                acc = mf(Aqk[(s0 + g4) * BC + 16 * p + i16], sO[(s0 + g4) * LB + 16 * ct + i16], acc);
+#pragma unroll
+            for (int q = 0; q < KQ; ++q) {
+                const float *b = sD + (16 * q + 4 * g4) * LB + i16;
+                acc = mf(kdf[q].x, b[0], acc);
+                acc = mf(kdf[q].y, b[LB], acc);
+                acc = mf(kdf[q].z, b[2 * LB], acc);
+                acc = mf(kdf[q].w, b[3 * LB], acc);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q >= p) {  // A_qk[s][r] is zero for s < r
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        acc = mf(aqf[4 * q + u], sO[(16 * q + 4 * g4 + u) * LB + i16], acc);
+                }
+            }
+            float *dVt = a.w.dVt + sh * BC * V + j0 + i16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = 16 * p + 4 * g4 + e, col = 16 * ct + i16;
-                sV[row * LB + col] = acc[e];
-                dVt[row * V + j0 + col] = acc[e];
+                const int row = 16 * p + 4 * g4 + e;
+                sV[row * LB + i16] = acc[e];
+                dVt[row * V] = acc[e];
             }
         }
         __syncthreads();
-        const float *Qg = a.w.Qg + sh * BC * K, *W = a.w.W + sh * BC * K, *gC = a.w.gC + sh * K;
-        for (int t = w; t < (K / 16) * (SBV / 16); t += 4) {
-            const int rt = t / (SBV / 16), ct = t % (SBV / 16);
-            f4 acc = {0.f, 0.f, 0.f, 0.f}, neg = acc;
-#pragma unroll 8
-            for (int r0 = 0; r0 < BC; r0 += 4) {
-                const int r = r0 + g4;
-                acc = mf(Qg[r * K + 16 * rt + i16], sO[r * LB + 16 * ct + i16], acc);
-                neg = mf(W[r * K + 16 * rt + i16], sV[r * LB + 16 * ct + i16], neg);
-            }
+        if (j > 0) loadA(j - 1);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = 16 * rt + 4 * g4 + e, col = 16 * ct + i16;
-                sD[m * LB + col] = gC[m] * sD[m * LB + col] + acc[e] - neg[e];
+        for (int i = 0; i < NST; ++i) {
+            const int rt = w + 4 * i;
+            if (rt < K / 16) {
+                f4 acc = {0.f, 0.f, 0.f, 0.f}, neg = acc;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = 16 * q + 4 * g4 + u;
+                        acc = mf(qgf[i][4 * q + u], sO[r * LB + i16], acc);
+                        neg = mf(wwf[i][4 * q + u], sV[r * LB + i16], neg);
+                    }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 16 * rt + 4 * g4 + e;
+                    sD[m * LB + i16] = gcf[i][e] * sD[m * LB + i16] + acc[e] - neg[e];
+                }
             }
         }
     }
@@ -409,212 +532,290 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// vgrads: contractions over the value dimension, one workgroup per (chunk slot, head)
-template <int V>
+// vgrads: contractions over the value dimension, one workgroup per (chunk slot, head).
+// The value axis is walked in 16-column slices staged in LDS (coalesced 16-byte loads; the
+// next slice is loaded into registers while the matrix cores work on the current one);
+// the C x K and C x C results accumulate in registers over the slices.
+template <int K>
 struct VgLds {
-    static constexpr int LV = V + 4;
-    static constexpr size_t bytes = sizeof(float) * (2 * BC * LV + BC + (V / 16) * BC);
+    static constexpr int JS = 16, LJ = JS + 4;  // slice width; row stride 20 keeps fragment reads conflict-free
+    static constexpr int LK = K + 4;
+    static constexpr int SLICES = 2 * K * LJ + 4 * BC * LJ;           // the value slices
+    static constexpr int TAIL = 2 * BC * LK + 2 * BC * LDC;           // PW, beta Kg, MT / Y, dT (after the slices)
+    static constexpr int R1 = SLICES > TAIL ? SLICES : TAIL;
+    static constexpr size_t bytes = sizeof(float) * (R1 + BC * LDC + BC + NTH + (1 + K / 16 + NP) * BC);
 };
+
 
 template <typename TIn, int K, int V>
 __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
-    constexpr int LV = VgLds<V>::LV;
+    constexpr int JS = VgLds<K>::JS, LJ = VgLds<K>::LJ, KT = K / 16, NOWN = NP * KT / 4;
+    constexpr int KP = (K * 4 + NTH - 1) / NTH;  // 4-column groups of the K x 16 slices per thread
     extern __shared__ __align__(16) unsigned char smem[];
-    float *sO = reinterpret_cast<float *>(smem);  // scale * dO
-    float *sVr = sO + BC * LV;                     // v
-    float *sB = sVr + BC * LV;                     // beta
-    float *sRed = sB + BC;                         // [V/16][BC] partial row sums
+    float *sH = reinterpret_cast<float *>(smem);  // S      [K][16] slice
+    float *sDH = sH + K * LJ;                      // dS'    [K][16]
+    float *sO = sDH + K * LJ;                      // scale dO [C][16]
+    float *sVt = sO + BC * LJ;                     // Vt     [C][16]
+    float *sdVt = sVt + BC * LJ;                   // dVt    [C][16]
+    float *sVr = sdVt + BC * LJ;                   // v      [C][16]
+    float *sT = reinterpret_cast<float *>(smem) + VgLds<K>::R1;  // T [C][C]
+    float *sB = sT + BC * LDC;                     // beta
+    float *sRs = sB + BC;                          // partial rowsum(S dS')
+    float *sRv = sRs + NTH;                        // [C] rowsum(V T^T dVt)
+    float *sRk = sRv + BC;                         // [K/16][C] partial rowsum(K e^Gamma dBk)
+    float *sRa = sRk + KT * BC;                    // [NP][C] partial rowsum(dA Abar)
     const int n = blockIdx.x, h = blockIdx.y, H = a.H;
     const ChunkPos cp = slot_chunk(n, a.cu_seqlens, a.num_seqs, a.T);
     if (cp.L == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
     const int64_t sh = (int64_t)n * H + h;
     const TIn *v = static_cast<const TIn *>(a.v);
-    for (int i = tid; i < BC * V; i += NTH) {
-        const int r = i / V, c = i % V;
-        float ov = 0.f, vv = 0.f;
-        if (r < cp.L) {
-            const int64_t gi = ((cp.t0 + r) * H + h) * V + c;
-            ov = a.scale * ld_any(a.d_out, a.dout_bf16, gi);
-            vv = ld_f32(v, gi);
-        }
-        sO[r * LV + c] = ov;
-        sVr[r * LV + c] = vv;
-    }
-    if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
-    __syncthreads();
-
     const float *hp = a.w.h + sh * K * V, *dhp = a.w.dh + sh * K * V;
-    const float *Vt = a.w.Vt + sh * BC * V, *dVt = a.w.dVt + sh * BC * V, *Tm = a.w.Tm + sh * BC * BC;
-    float *PS = a.w.PS + sh * BC * K, *PW = a.w.PW + sh * BC * K, *PdK = a.w.PdK + sh * BC * K;
-    // dO S^T, dVt S^T and Vt dS'^T  [C x K]
-    for (int t = w; t < NP * (K / 16); t += 4) {
-        const int p = t / (K / 16), ct = t % (K / 16);
-        f4 ps = {0.f, 0.f, 0.f, 0.f}, pw = ps, pd = ps;
-        const int r = 16 * p + i16, c = 16 * ct + i16;
-#pragma unroll 4
-        for (int j0 = 0; j0 < V; j0 += 4) {
-            const int j = j0 + g4;
-            const float hb = hp[c * V + j], db = dhp[c * V + j];
-            ps = mf(sO[r * LV + j], hb, ps);
-            pw = mf(dVt[r * V + j], hb, pw);
-            pd = mf(Vt[r * V + j], db, pd);
-        }
+    const float *Vtp = a.w.Vt + sh * BC * V, *dVtp = a.w.dVt + sh * BC * V, *Tm = a.w.Tm + sh * BC * BC;
+
+    float4 rh[KP], rdh[KP], ro, rvt, rdvt, rv;
+    const int sr = tid >> 2, sg = 4 * (tid & 3);  // staging: row and first column of this thread's group
+    const int64_t tok = ((cp.t0 + sr) * H + h) * V + sg;
+    auto load = [&](int j0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e;
-            PS[row * K + c] = ps[e];
-            PW[row * K + c] = pw[e];
-            PdK[row * K + c] = pd[e];
+        for (int i = 0; i < KP; ++i) {
+            const int idx = tid + NTH * i;
+            if (idx < K * 4) {
+                const int c = idx >> 2, g = 4 * (idx & 3);
+                rh[i] = ld4(hp + c * V + j0 + g);
+                rdh[i] = ld4(dhp + c * V + j0 + g);
+            }
         }
-    }
-    // dO Vt^T and dVt (beta V)^T  [C x C]
-    float *MA = a.w.MA + sh * BC * BC, *MT = a.w.MT + sh * BC * BC;
-    for (int t = w; t < NP * NP; t += 4) {
-        const int p = t / NP, qt = t % NP;
-        f4 ma = {0.f, 0.f, 0.f, 0.f}, mt = ma;
-        const int r = 16 * p + i16, s = 16 * qt + i16;
-        const float bs = sB[s];
-#pragma unroll 4
-        for (int j0 = 0; j0 < V; j0 += 4) {
-            const int j = j0 + g4;
-            ma = mf(sO[r * LV + j], Vt[s * V + j], ma);
-            mt = mf(dVt[r * V + j], bs * sVr[s * LV + j], mt);
+        rvt = ld4(Vtp + sr * V + j0 + sg);
+        rdvt = ld4(dVtp + sr * V + j0 + sg);
+        if (sr < cp.L) {
+            ro = ld4_any(a.d_out, a.dout_bf16, tok + j0);
+            rv = ld4(v + tok + j0);
+        } else {
+            ro = rv = make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    };
+    auto store = [&]() {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e;
-            MA[row * BC + s] = ma[e];
-            MT[row * BC + s] = mt[e];
+        for (int i = 0; i < KP; ++i) {
+            const int idx = tid + NTH * i;
+            if (idx < K * 4) {
+                const int c = idx >> 2, g = 4 * (idx & 3);
+                st4(sH + c * LJ + g, rh[i]);
+                st4(sDH + c * LJ + g, rdh[i]);
+            }
         }
-    }
-    // T^T dVt: dv = beta T^T dVt, and its beta part rowsum(V T^T dVt)
-    void *dv = a.dv;
-    for (int t = w; t < NP * (V / 16); t += 4) {
-        const int p = t / (V / 16), ct = t % (V / 16);
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int c = 16 * ct + i16;
-        for (int s0 = 16 * p; s0 < BC; s0 += 4)
-            acc = mf(Tm[(s0 + g4) * BC + 16 * p + i16], dVt[(s0 + g4) * V + c], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e;
-            if (row < cp.L) st_out(dv, a.grad_bf16, ((cp.t0 + row) * H + h) * V + c, sB[row] * acc[e]);
-            const float part = row16_sum(sVr[row * LV + c] * acc[e]);
-            if (i16 == 0) sRed[ct * BC + row] = part;
-        }
-    }
-    // gamma_C's partner: rowsum(S dS') per key channel
-    for (int c = tid; c < K; c += NTH) {
-        float acc = 0.f;
-        for (int j = 0; j < V; ++j) acc += hp[c * V + j] * dhp[c * V + j];
-        a.w.rs[sh * K + c] = acc;
-    }
-    __syncthreads();
-    if (tid < BC) {
-        float acc = 0.f;
-        for (int ct = 0; ct < V / 16; ++ct) acc += sRed[ct * BC + tid];
-        a.w.dbv[sh * BC + tid] = acc;
-    }
-}
+        const float sc = a.scale;
+        st4(sO + sr * LJ + sg, make_float4(sc * ro.x, sc * ro.y, sc * ro.z, sc * ro.w));
+        st4(sVt + sr * LJ + sg, rvt);
+        st4(sdVt + sr * LJ + sg, rdvt);
+        st4(sVr + sr * LJ + sg, rv);
+    };
 
-// ------------------------------------------------------------------------------------
-// kgrads: everything in key space, one workgroup per (chunk slot, head)
-template <int K>
-struct KgLds {
-    static constexpr int LK = K + 4;
-    static constexpr size_t bytes = sizeof(float) * (3 * BC * LK + 3 * BC * LDC + BC + K + (K / 16) * BC + NP * BC);
-};
-
-template <typename TIn, int K, int V>
-__global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
-    constexpr int LK = KgLds<K>::LK;
-    constexpr int KT = K / 16;
-    extern __shared__ __align__(16) unsigned char smem[];
-    float *sQ = reinterpret_cast<float *>(smem);
-    float *sK = sQ + BC * LK;
-    float *sG = sK + BC * LK;
-    float *sT = sG + BC * LK;
-    float *sM = sT + BC * LDC;   // dT, then beta dA
-    float *sY = sM + BC * LDC;   // dT T^T
-    float *sB = sY + BC * LDC;
-    float *sE = sB + BC;
-    float *sRk = sE + K;         // [K/16][BC] partial rowsum(K e^Gamma dBk)
-    float *sRa = sRk + KT * BC;  // [NP][BC] partial rowsum(dA Abar)
-
-    const int n = blockIdx.x, h = blockIdx.y, H = a.H;
-    const ChunkPos cp = slot_chunk(n, a.cu_seqlens, a.num_seqs, a.T);
-    if (cp.L == 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
-    const int64_t sh = (int64_t)n * H + h;
-    const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
-
-    for (int i = tid; i < BC * K; i += NTH) {
-        const int r = i / K, c = i % K;
-        float qv = 0.f, kv = 0.f, gv = 0.f;
-        if (r < cp.L) {
-            const int64_t gi = ((cp.t0 + r) * H + h) * K + c;
-            qv = ld_f32(q, gi);
-            kv = ld_f32(k, gi);
-            gv = gate_log(a.gate, gi);
-        }
-        sQ[r * LK + c] = qv;
-        sK[r * LK + c] = kv;
-        sG[r * LK + c] = gv;
-    }
-    if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
-    const float *Tm = a.w.Tm + sh * BC * BC;
+    load(0);
     for (int i = tid; i < BC * BC; i += NTH) sT[(i / BC) * LDC + i % BC] = Tm[i];
+    if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
+    store();
     __syncthreads();
-    if (tid < K) {
-        float run = 0.f;
-        for (int r = 0; r < BC; ++r) {
-            run += sG[r * LK + tid];
-            sG[r * LK + tid] = run;
+
+    f4 ps[NOWN], pw[NOWN], pd[NOWN], ma[4], mt[4];
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i) ps[i] = pw[i] = pd[i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ma[i] = mt[i] = f4{0.f, 0.f, 0.f, 0.f};
+    float dbacc[4] = {0.f, 0.f, 0.f, 0.f}, rsacc = 0.f;
+    constexpr int PARTS = NTH / K, CW = JS / PARTS;  // rowsum(S dS'): threads per key row, columns each
+
+    for (int js = 0; js < V / JS; ++js) {
+        const bool more = js + 1 < V / JS;
+        if (more) load((js + 1) * JS);
+        // dO S^T, dVt S^T, Vt dS'^T on this wave's C x K tiles.  The slice's 16-wide
+        // reduction is split as k = 4*(lane/16) + s on both operands, so one 16-byte LDS
+        // read per operand feeds four matrix-core steps.
+#pragma unroll
+        for (int i = 0; i < NOWN; ++i) {
+            const int t = w + 4 * i, p = t / KT, ct = t % KT;
+            const int ra = (16 * p + i16) * LJ + 4 * g4, rb = (16 * ct + i16) * LJ + 4 * g4;
+            const float4 ao = *reinterpret_cast<const float4 *>(sO + ra);
+            const float4 avt = *reinterpret_cast<const float4 *>(sVt + ra);
+            const float4 adv = *reinterpret_cast<const float4 *>(sdVt + ra);
+            const float4 bh = *reinterpret_cast<const float4 *>(sH + rb);
+            const float4 bdh = *reinterpret_cast<const float4 *>(sDH + rb);
+            ps[i] = mf(ao.x, bh.x, ps[i]); pw[i] = mf(adv.x, bh.x, pw[i]); pd[i] = mf(avt.x, bdh.x, pd[i]);
+            ps[i] = mf(ao.y, bh.y, ps[i]); pw[i] = mf(adv.y, bh.y, pw[i]); pd[i] = mf(avt.y, bdh.y, pd[i]);
+            ps[i] = mf(ao.z, bh.z, ps[i]); pw[i] = mf(adv.z, bh.z, pw[i]); pd[i] = mf(avt.z, bdh.z, pd[i]);
+            ps[i] = mf(ao.w, bh.w, ps[i]); pw[i] = mf(adv.w, bh.w, pw[i]); pd[i] = mf(avt.w, bdh.w, pd[i]);
         }
-        sE[tid] = run;
+        // dO Vt^T and dVt V^T on this wave's C x C tiles
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = w + 4 * i, p = t / NP, qt = t % NP;
+            const int ra = (16 * p + i16) * LJ + 4 * g4, rb = (16 * qt + i16) * LJ + 4 * g4;
+            const float4 ao = *reinterpret_cast<const float4 *>(sO + ra);
+            const float4 adv = *reinterpret_cast<const float4 *>(sdVt + ra);
+            const float4 bvt = *reinterpret_cast<const float4 *>(sVt + rb);
+            const float4 bv = *reinterpret_cast<const float4 *>(sVr + rb);
+            ma[i] = mf(ao.x, bvt.x, ma[i]); mt[i] = mf(adv.x, bv.x, mt[i]);
+            ma[i] = mf(ao.y, bvt.y, ma[i]); mt[i] = mf(adv.y, bv.y, mt[i]);
+            ma[i] = mf(ao.z, bvt.z, ma[i]); mt[i] = mf(adv.z, bv.z, mt[i]);
+            ma[i] = mf(ao.w, bvt.w, ma[i]); mt[i] = mf(adv.w, bv.w, mt[i]);
+        }
+        // T^T dVt on row tile p = w of this slice: dv = beta T^T dVt, rowsum(V T^T dVt) for dbeta
+        {
+            const int p = w;
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 16 * p; s0 < BC; s0 += 4)
+                acc = mf(sT[(s0 + g4) * LDC + 16 * p + i16], sdVt[(s0 + g4) * LJ + i16], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * p + 4 * g4 + e;
+                if (row < cp.L)
+                    st_out(a.dv, a.grad_bf16, ((cp.t0 + row) * H + h) * V + js * JS + i16, sB[row] * acc[e]);
+                dbacc[e] += row16_sum(sVr[row * LJ + i16] * acc[e]);
+            }
+        }
+        {
+            const int c = tid % K, part = tid / K;
+#pragma unroll
+            for (int j = 0; j < CW; ++j) rsacc += sH[c * LJ + part * CW + j] * sDH[c * LJ + part * CW + j];
+        }
+        __syncthreads();
+        if (more) {
+            store();
+            __syncthreads();
+        }
     }
 
-    // dT = dVt (beta V)^T + dW (beta K e^Gamma)^T, dW = -dVt S^T
-    const float *PW = a.w.PW + sh * BC * K, *Kg = a.w.Kg + sh * BC * K, *MT = a.w.MT + sh * BC * BC;
-    for (int t = w; t < NP * NP; t += 4) {
-        const int p = t / NP, qt = t % NP;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * p + i16, s = 16 * qt + i16;
+    // the slices are done: their LDS now holds PW (-dW), beta K e^Gamma, MT and the C x C work
+    constexpr int LK = VgLds<K>::LK;
+    float *sPW = reinterpret_cast<float *>(smem);  // [C][K+4]
+    float *sKg = sPW + BC * LK;                    // [C][K+4] K e^Gamma
+    float *sM = sKg + BC * LK;                     // [C][C] beta MT, then Y = dT T^T
+    float *sY = sM + BC * LDC;                     // [C][C] dT
+    const float *Kg = a.w.Kg + sh * BC * K;
+    float4 kg4[(BC * K / 4 + NTH - 1) / NTH];
+#pragma unroll
+    for (int i = 0; i < (BC * K / 4 + NTH - 1) / NTH; ++i) {
+        const int idx = tid + NTH * i;
+        if (idx < BC * K / 4) kg4[i] = ld4(Kg + 4 * idx);
+    }
+    float *PS = a.w.PS + sh * BC * K, *PdK = a.w.PdK + sh * BC * K, *MA = a.w.MA + sh * BC * BC;
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i) {
+        const int t = w + 4 * i, p = t / KT, ct = t % KT, c = 16 * ct + i16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * p + 4 * g4 + e;
+            PS[row * K + c] = ps[i][e];
+            PdK[row * K + c] = pd[i][e];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) MA[(16 * p + 4 * g4 + e) * BC + s] = ma[i][e];
+    }
+    if (i16 == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sRv[16 * w + 4 * g4 + e] = dbacc[e];
+    }
+    sRs[tid] = rsacc;
+    __syncthreads();  // every wave is past the slices
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i) {
+        const int t = w + 4 * i, p = t / KT, ct = t % KT, c = 16 * ct + i16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sPW[(16 * p + 4 * g4 + e) * LK + c] = pw[i][e];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
         const float bs = sB[s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sM[(16 * p + 4 * g4 + e) * LDC + s] = bs * mt[i][e];
+    }
+#pragma unroll
+    for (int i = 0; i < (BC * K / 4 + NTH - 1) / NTH; ++i) {
+        const int idx = tid + NTH * i;
+        if (idx < BC * K / 4) {
+            const int r = (4 * idx) / K, c = (4 * idx) % K;
+            st4(sKg + r * LK + c, kg4[i]);
+        }
+    }
+    if (tid < K) {
+        float acc = 0.f;
+        for (int part = 0; part < PARTS; ++part) acc += sRs[part * K + tid];
+        a.w.rs[sh * K + tid] = acc;
+    }
+    __syncthreads();
+    // dT = MT + dW (beta K e^Gamma)^T with dW = -PW (beta_s applied to the column)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float *ar = sPW + (16 * p + i16) * LK + 4 * g4, *br = sKg + s * LK + 4 * g4;
 #pragma unroll 4
-        for (int c0 = 0; c0 < K; c0 += 4) {
-            const int c = c0 + g4;
-            acc = mf(PW[r * K + c], bs * Kg[s * K + c], acc);
+        for (int c0 = 0; c0 < K; c0 += 16) {
+            const float4 x = *reinterpret_cast<const float4 *>(ar + c0);
+            const float4 y = *reinterpret_cast<const float4 *>(br + c0);
+            acc = mf(x.x, y.x, acc);
+            acc = mf(x.y, y.y, acc);
+            acc = mf(x.z, y.z, acc);
+            acc = mf(x.w, y.w, acc);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * p + 4 * g4 + e;
-            sM[row * LDC + s] = MT[row * BC + s] - acc[e];
+            sY[row * LDC + s] = sM[row * LDC + s] - sB[s] * acc[e];
+        }
+    }
+    // dBk = T^T dW = -T^T PW on this wave's C x K tiles; rowsum(K e^Gamma dBk) for dbeta
+    float *dBk = a.w.PW + sh * BC * K;
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i) {
+        const int t = w + 4 * i, p = t / KT, ct = t % KT, c = 16 * ct + i16;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 16 * p; s0 < BC; s0 += 4)
+            acc = mf(sT[(s0 + g4) * LDC + 16 * p + i16], sPW[(s0 + g4) * LK + c], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * p + 4 * g4 + e;
+            dBk[row * K + c] = -acc[e];
+            const float part = row16_sum(-acc[e] * sKg[row * LK + c]);
+            if (i16 == 0) sRk[ct * BC + row] = part;
         }
     }
     __syncthreads();
     // Y = dT T^T
-    for (int t = w; t < NP * NP; t += 4) {
-        const int p = t / NP, qt = t % NP;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * p + i16, s = 16 * qt + i16;
-#pragma unroll 4
-        for (int j0 = 0; j0 < BC; j0 += 4) acc = mf(sM[r * LDC + j0 + g4], sT[s * LDC + j0 + g4], acc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sY[(16 * p + 4 * g4 + e) * LDC + s] = acc[e];
+    for (int i = 0; i < 4; ++i) {
+        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float *ar = sY + (16 * p + i16) * LDC + 4 * g4, *br = sT + s * LDC + 4 * g4;
+#pragma unroll
+        for (int j0 = 0; j0 < BC; j0 += 16) {
+            const float4 x = *reinterpret_cast<const float4 *>(ar + j0);
+            const float4 y = *reinterpret_cast<const float4 *>(br + j0);
+            acc = mf(x.x, y.x, acc);
+            acc = mf(x.y, y.y, acc);
+            acc = mf(x.z, y.z, acc);
+            acc = mf(x.w, y.w, acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sM[(16 * p + 4 * g4 + e) * LDC + s] = acc[e];
     }
     __syncthreads();
-    // dA = -strict_tril(T^T Y); rowsum(dA Abar) for dbeta; beta dA replaces dT
+    // dA = -strict_tril(T^T Y); rowsum(dA Abar) for dbeta; beta dA is what the key space needs
     const float *Abar = a.w.Abar + sh * BC * BC;
-    for (int t = w; t < NP * NP; t += 4) {
-        const int p = t / NP, qt = t % NP;
+    float *dAb = a.w.MT + sh * BC * BC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int s = 16 * qt + i16;
         if (qt <= p) {
-#pragma unroll 4
-            for (int j0 = 0; j0 < BC; j0 += 4)
-                acc = mf(sT[(j0 + g4) * LDC + 16 * p + i16], sY[(j0 + g4) * LDC + s], acc);
+            for (int j0 = 16 * p; j0 < BC; j0 += 4)
+                acc = mf(sT[(j0 + g4) * LDC + 16 * p + i16], sM[(j0 + g4) * LDC + s], acc);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -622,108 +823,223 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             const float da = row > s ? -acc[e] : 0.f;
             const float part = row16_sum(da * Abar[row * BC + s]);
             if (i16 == 0) sRa[qt * BC + row] = part;
-            sM[row * LDC + s] = sB[row] * da;
+            dAb[row * BC + s] = sB[row] * da;
         }
     }
     __syncthreads();
+    if (tid < cp.L) {
+        float acc = sRv[tid];
+        for (int ct = 0; ct < KT; ++ct) acc += sRk[ct * BC + tid];
+        for (int qt = 0; qt < NP; ++qt) acc += sRa[qt * BC + tid];
+        a.dbeta[(cp.t0 + tid) * H + h] = acc;
+    }
+}
 
-    // per owned C x K tile: dq, dk and the per-row terms of d ln alpha
-    const float *PS = a.w.PS + sh * BC * K, *PdK = a.w.PdK + sh * BC * K, *MA = a.w.MA + sh * BC * BC;
-    float *dGt = a.w.PS + sh * BC * K;   // overwritten element by element by its only reader
-    float *eSt = a.w.PdK + sh * BC * K;
-    for (int t = w; t < NP * KT; t += 4) {
-        const int rt = t / KT, ct = t % KT;
-        const int c = 16 * ct + i16;
-        // T^T dW = -T^T (dVt S^T)
-        f4 bk = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 16 * rt; s0 < BC; s0 += 4)
-            bk = mf(sT[(s0 + g4) * LDC + 16 * rt + i16], PW[(s0 + g4) * K + c], bk);
-        // row side of the decayed adjoints (rows of tile rt): A_qk -> dq, beta dA -> dk
+// ------------------------------------------------------------------------------------
+// kgrads: the key-space gradients, one workgroup per (chunk slot, head, block of KB key
+// channels).  The products over tokens (the decayed adjoints) are independent per key
+// channel, so a block needs only its own columns of q, k and Gamma, plus the two C x C
+// matrices tril(dO Vt^T) and beta dA; everything is staged in LDS.  No exponential is
+// taken inside the products: with m_p = Gamma at the middle row of row tile p,
+//   e^{Gamma_r - Gamma_s} = F1_r E[p][q] F2_s,  F1 = e^{Gamma - m_tile(r)}, F2 = e^{m_tile(s) - Gamma},
+//   E[p][q] = e^{m_p - m_q}  (q <= p: at most 1),
+// and e^Gamma, e^{Gamma_C - Gamma} come from the same factors and two per-tile tables.
+template <int K>
+struct KgLds {
+    static constexpr int KB = K < 32 ? K : 32, LKB = KB + 4;
+    static constexpr size_t bytes = sizeof(float) * (4 * BC * LKB + 2 * BC * LDC + BC + (NP * NP + 3 * NP) * KB);
+};
+
+template <typename TIn, int K, int V>
+__global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
+    constexpr int KB = KgLds<K>::KB, LKB = KgLds<K>::LKB, NCB = K / KB, KBT = KB / 16;
+    constexpr int NOWN = NP * KBT / 4;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *sQ = reinterpret_cast<float *>(smem);  // q, later the row terms of d ln alpha
+    float *sK = sQ + BC * LKB;                     // k, later the Kd terms
+    float *sF1 = sK + BC * LKB;                    // e^{Gamma - m_tile}
+    float *sF2 = sF1 + BC * LKB;                   // Gamma, then e^{m_tile - Gamma}
+    float *sMA = sF2 + BC * LKB;                   // tril(dO Vt^T)
+    float *sdA = sMA + BC * LDC;                   // beta dA (strictly lower)
+    float *sB = sdA + BC * LDC;
+    float *sEpq = sB + BC;                         // [NP][NP][KB] e^{m_p - m_q}
+    float *sEm = sEpq + NP * NP * KB;              // [NP][KB] e^{m_p}
+    float *sEe = sEm + NP * KB;                    // [NP][KB] e^{Gamma_C - m_p}
+    float *sMid = sEe + NP * KB;                   // [NP][KB] m_p
+
+    int u, cb;  // (chunk slot, head) unit; its channel blocks share an XCD
+    xcd_map(blockIdx.x, NCB, u, cb);
+    const int H = a.H;
+    if (u >= a.slots * H) return;
+    const int n = u / H, h = u % H, c0 = cb * KB;
+    const ChunkPos cp = slot_chunk(n, a.cu_seqlens, a.num_seqs, a.T);
+    if (cp.L == 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
+    const int64_t sh = (int64_t)n * H + h;
+    const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
+
+    for (int i = tid; i < BC * KB; i += NTH) {
+        const int r = i / KB, c = i % KB;
+        float qv = 0.f, kv = 0.f, gv = 0.f;
+        if (r < cp.L) {
+            const int64_t gi = ((cp.t0 + r) * H + h) * K + c0 + c;
+            qv = ld_f32(q, gi);
+            kv = ld_f32(k, gi);
+            gv = gate_log(a.gate, gi);
+        }
+        sQ[r * LKB + c] = qv;
+        sK[r * LKB + c] = kv;
+        sF2[r * LKB + c] = gv;
+    }
+    const float *MA = a.w.MA + sh * BC * BC, *dAb = a.w.MT + sh * BC * BC;
+    for (int i = tid; i < BC * BC / 4; i += NTH) {
+        const int r = (4 * i) / BC, c = (4 * i) % BC;
+        const float4 m = ld4(MA + 4 * i);
+        st4(sMA + r * LDC + c, make_float4(c <= r ? m.x : 0.f, c + 1 <= r ? m.y : 0.f, c + 2 <= r ? m.z : 0.f,
+                                           c + 3 <= r ? m.w : 0.f));
+        st4(sdA + r * LDC + c, ld4(dAb + 4 * i));
+    }
+    if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
+    __syncthreads();
+    if (tid < KB) {
+        float run = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            run += sF2[r * LKB + tid];
+            sF2[r * LKB + tid] = run;
+        }
+    }
+    __syncthreads();
+    // tables per channel, from the tile middles m_p and the chunk end
+    for (int i = tid; i < (NP * NP + 3 * NP) * KB; i += NTH) {
+        const int c = i % KB, j = i / KB;
+        if (j < NP * NP) {
+            const int pp = j / NP, qq = j % NP;
+            sEpq[j * KB + c] = qq <= pp ? expf(sF2[(16 * pp + 7) * LKB + c] - sF2[(16 * qq + 7) * LKB + c]) : 0.f;
+        } else if (j < NP * NP + NP) {
+            sEm[(j - NP * NP) * KB + c] = expf(sF2[(16 * (j - NP * NP) + 7) * LKB + c]);
+        } else if (j < NP * NP + 2 * NP) {
+            const int pp = j - NP * NP - NP;
+            sEe[pp * KB + c] = expf(sF2[(BC - 1) * LKB + c] - sF2[(16 * pp + 7) * LKB + c]);
+        } else {
+            const int pp = j - NP * NP - 2 * NP;
+            sMid[pp * KB + c] = sF2[(16 * pp + 7) * LKB + c];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < BC * KB; i += NTH) {  // each element rewritten by the thread that reads it
+        const int r = i / KB, c = i % KB;
+        const float d = sF2[r * LKB + c] - sMid[(r >> 4) * KB + c];
+        sF1[r * LKB + c] = expf(d);
+        sF2[r * LKB + c] = expf(-d);
+    }
+    __syncthreads();
+
+    const float *PS = a.w.PS + sh * BC * K, *PdK = a.w.PdK + sh * BC * K, *dBk = a.w.PW + sh * BC * K;
+    float dgt[NOWN][4], est[NOWN][4];
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i) {
+        const int t = w + 4 * i, rt = t / KBT, ct = t % KBT;
+        const int c = 16 * ct + i16, gc = c0 + c;
+        float ps_[4], pdk_[4], dbk_[4];  // element-wise inputs, in flight during the products
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * rt + 4 * g4 + e;
+            ps_[e] = PS[row * K + gc];
+            pdk_[e] = PdK[row * K + gc];
+            dbk_[e] = dBk[row * K + gc];
+        }
+        // row side of the decayed adjoints (rows of tile rt): A_qk -> dq, beta dA -> dk;
+        // column s of tile qs enters as k_s F2_s E[rt][qs], the result is scaled by F1_r
         f4 xq = {0.f, 0.f, 0.f, 0.f}, xk = xq;
         {
-            const float m = sG[(16 * rt + 7) * LK + c];
             const int r = 16 * rt + i16;
-            for (int s0 = 0; s0 < 16 * rt + 16; s0 += 4) {
-                const int s = s0 + g4;
-                const float b = sK[s * LK + c] * expf(m - sG[s * LK + c]);
-                const float ma = s <= r ? MA[r * BC + s] : 0.f;
-                xq = mf(ma, b, xq);
-                xk = mf(sM[r * LDC + s], b, xk);
+            for (int qs = 0; qs <= rt; ++qs) {
+                const float epq = sEpq[(rt * NP + qs) * KB + c];
+#pragma unroll
+                for (int u = 0; u < 16; u += 4) {
+                    const int s = 16 * qs + u + g4;
+                    const float b = sK[s * LKB + c] * sF2[s * LKB + c] * epq;
+                    xq = mf(sMA[r * LDC + s], b, xq);
+                    xk = mf(sdA[r * LDC + s], b, xk);
+                }
             }
         }
-        // column side (rows of tile rt as the later index s): sums over every row tile p >= rt
+        // column side (rows of tile rt as the earlier index s): row r of tile p >= rt enters
+        // as q_r F1_r (k_r F1_r), the result for row s is scaled by E[p][rt] F2_s
         f4 yq = {0.f, 0.f, 0.f, 0.f}, yk = yq;
         for (int p = rt; p < NP; ++p) {
-            const float m = sG[(16 * p + 7) * LK + c];
             f4 aq = {0.f, 0.f, 0.f, 0.f}, akk = aq;
             const int s = 16 * rt + i16;
 #pragma unroll
-            for (int r0 = 0; r0 < 16; r0 += 4) {
-                const int r = 16 * p + r0 + g4;
-                const float er = expf(sG[r * LK + c] - m);
-                const float ma = r >= s ? MA[r * BC + s] : 0.f;
-                aq = mf(ma, sQ[r * LK + c] * er, aq);
-                akk = mf(sM[r * LDC + s], sK[r * LK + c] * er, akk);
+            for (int u = 0; u < 16; u += 4) {
+                const int r = 16 * p + u + g4;
+                const float f1 = sF1[r * LKB + c];
+                aq = mf(sMA[r * LDC + s], sQ[r * LKB + c] * f1, aq);
+                akk = mf(sdA[r * LDC + s], sK[r * LKB + c] * f1, akk);
             }
+            const float epr = sEpq[(p * NP + rt) * KB + c];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float fs = expf(m - sG[(16 * rt + 4 * g4 + e) * LK + c]);
+                const float fs = epr * sF2[(16 * rt + 4 * g4 + e) * LKB + c];
                 yq[e] += fs * aq[e];
                 yk[e] += fs * akk[e];
             }
         }
-        const float mr = sG[(16 * rt + 7) * LK + c];
+        const float em = sEm[rt * KB + c], ee = sEe[rt * KB + c];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * rt + 4 * g4 + e;
-            const float G = sG[row * LK + c], eg = expf(G), kv = sK[row * LK + c], qv = sQ[row * LK + c];
-            const float fr = expf(G - mr);
-            const float dBk = -bk[e];
-            const float dKW = sB[row] * eg * dBk;
-            const float dQ = PS[row * K + c] * eg + fr * xq[e];
-            const float dKS = PdK[row * K + c] * expf(sE[c] - G);
+            const float fr = sF1[row * LKB + c], kv = sK[row * LKB + c], qv = sQ[row * LKB + c];
+            const float eg = fr * em;                          // e^Gamma
+            const float dKW = sB[row] * eg * dbk_[e];
+            const float dQ = ps_[e] * eg + fr * xq[e];
+            const float dKS = pdk_[e] * (ee * sF2[row * LKB + c]);  // e^{Gamma_C - Gamma}
             const float dK1 = fr * xk[e];
             const float dK = yq[e] + dKS + dKW + dK1 + yk[e];
-            dGt[row * K + c] = qv * dQ + kv * (dK1 + dKW - yq[e] - yk[e]);
-            eSt[row * K + c] = kv * dKS;
-            const float part = row16_sum(kv * eg * dBk);
-            if (i16 == 0) sRk[ct * BC + row] = part;
+            dgt[i][e] = qv * dQ + kv * (dK1 + dKW - yq[e] - yk[e]);
+            est[i][e] = kv * dKS;
             if (row < cp.L) {
-                const int64_t gi = ((cp.t0 + row) * H + h) * K + c;
+                const int64_t gi = ((cp.t0 + row) * H + h) * K + gc;
                 st_out(a.dq, a.grad_bf16, gi, dQ);
                 st_out(a.dk, a.grad_bf16, gi, dK);
             }
         }
     }
-    __syncthreads();
-    if (tid < cp.L) {
-        float acc = a.w.dbv[sh * BC + tid];
-        for (int ct = 0; ct < KT; ++ct) acc += sRk[ct * BC + tid];
-        for (int qt = 0; qt < NP; ++qt) acc += sRa[qt * BC + tid];
-        a.dbeta[(cp.t0 + tid) * H + h] = acc;
+    __syncthreads();  // q, k are no longer read: their LDS takes the row terms
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i) {
+        const int t = w + 4 * i, rt = t / KBT, ct = t % KBT, c = 16 * ct + i16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * rt + 4 * g4 + e;
+            sQ[row * LKB + c] = dgt[i][e];
+            sK[row * LKB + c] = est[i][e];
+        }
     }
-    // d ln alpha per key channel: reverse in-chunk sum of the row terms, plus the
-    // chunk-end terms gamma_C rowsum(S dS') and the exclusive forward sum of the Kd terms
-    if (tid < K) {
-        const int c = tid;
+    __syncthreads();
+    // d ln alpha per key channel: reverse in-chunk sum of the row terms, plus the chunk-end
+    // terms gamma_C rowsum(S dS') and the exclusive forward sum of the Kd terms
+    if (tid < KB) {
+        const int c = tid, gc = c0 + c;
         float dl[BC];
-        float f = a.w.gC[sh * K + c] * a.w.rs[sh * K + c];
+        float f = a.w.gC[sh * K + gc] * a.w.rs[sh * K + gc];
 #pragma unroll
         for (int r = 0; r < BC; ++r) {
             dl[r] = f;
-            f += eSt[r * K + c];
+            f += sK[r * LKB + c];
         }
         float rv = 0.f;
 #pragma unroll
         for (int r = BC - 1; r >= 0; --r) {
-            rv += dGt[r * K + c];
+            rv += sQ[r * LKB + c];
             dl[r] += rv;
         }
+        const bool log_gate = a.gate.mode == GATE_LOG;
 #pragma unroll
         for (int r = 0; r < BC; ++r)
             if (r < cp.L) {
-                const int64_t gi = ((cp.t0 + r) * H + h) * K + c;
-                a.dgate[gi] = a.gate.mode == GATE_LOG ? dl[r] : dl[r] / a.gate.gate[gi];
+                const int64_t gi = ((cp.t0 + r) * H + h) * K + gc;
+                a.dgate[gi] = log_gate ? dl[r] : dl[r] * __builtin_amdgcn_rcpf(a.gate.gate[gi]);
             }
     }
 }
@@ -741,17 +1057,18 @@ hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
     auto kkg = bwd_kgrads_kernel<TIn, K, V>;
     if (!attr) {
         hipError_t e = set_lds<K, V>(reinterpret_cast<const void *>(kprep), PrepLds<K>::bytes);
-        if (e == hipSuccess) e = set_lds<K, V>(reinterpret_cast<const void *>(kvg), VgLds<V>::bytes);
+        if (e == hipSuccess) e = set_lds<K, V>(reinterpret_cast<const void *>(kvg), VgLds<K>::bytes);
         if (e == hipSuccess) e = set_lds<K, V>(reinterpret_cast<const void *>(kkg), KgLds<K>::bytes);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    const dim3 gp(a.slots, a.H), gs(V / SBV, a.H, num_seqs);
+    const int hs8 = (num_seqs * a.H + 7) / 8, sh8 = (int)(((int64_t)a.slots * a.H + 7) / 8);
+    const dim3 gp(a.slots, a.H), gs(8 * (V / SBV) * hs8), gk(8 * (K / KgLds<K>::KB) * sh8);
     hipLaunchKernelGGL(kprep, gp, dim3(NTH), PrepLds<K>::bytes, stream, a);
     hipLaunchKernelGGL((bwd_states_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL((bwd_dstates_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
-    hipLaunchKernelGGL(kvg, gp, dim3(NTH), VgLds<V>::bytes, stream, a);
-    hipLaunchKernelGGL(kkg, gp, dim3(NTH), KgLds<K>::bytes, stream, a);
+    hipLaunchKernelGGL(kvg, gp, dim3(NTH), VgLds<K>::bytes, stream, a);
+    hipLaunchKernelGGL(kkg, gk, dim3(NTH), KgLds<K>::bytes, stream, a);
     return hipGetLastError();
 }
 
