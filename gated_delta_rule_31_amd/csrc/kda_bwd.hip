@@ -94,6 +94,13 @@ __device__ __forceinline__ float gate_log(const GateIn &g, int64_t i) {
     return g.mode == GATE_LOG ? g.gate[i] : logf(g.gate[i]);
 }
 
+// gate values of four consecutive elements as log-decay (rows past the chunk: 0, no decay)
+__device__ __forceinline__ float4 gate_log4(const GateIn &g, float4 x, bool ok) {
+    if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
+    if (g.mode == GATE_LOG) return x;
+    return make_float4(logf(x.x), logf(x.y), logf(x.z), logf(x.w));
+}
+
 __device__ __forceinline__ float ld_any(const void *p, int is_bf16, int64_t i) {
     return is_bf16 ? (float)static_cast<const __bf16 *>(p)[i] : static_cast<const float *>(p)[i];
 }
@@ -132,24 +139,39 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // ------------------------------------------------------------------------------------
-// prep: one workgroup per (chunk slot, head)
-template <int K>
+// prep: one workgroup per (chunk slot, head).  After the in-chunk cumulative sum, Gamma is
+// replaced in LDS by F1 = e^{Gamma - m_tile} (m_p: Gamma at the middle row of row tile p);
+// every decay factor is then a product of F1, its reciprocal and per-channel tables
+// (e^{m_p - m_q}, e^{m_p}, e^{Gamma_C - m_p}), so no exponential is taken in the products.
+template <int K, int V>
 struct PrepLds {
-    static constexpr int LK = K + 4;
-    static constexpr size_t bytes = sizeof(float) * (3 * BC * LK + 2 * BC * LDC + BC + K);
+    static constexpr int LK = K + 4;                 // q, k, F1: 16-row fragment reads
+    static constexpr int LW = K + 16, LV = V + 16;   // beta K e^Gamma, beta v: 4-row fragment reads
+    static constexpr int R0 = 3 * BC * LK, RW = BC * LW + BC * LV;
+    static constexpr int R = R0 > RW ? R0 : RW;
+    static constexpr int TAB = (NP * NP + 3 * NP) * K;
+    static constexpr size_t bytes = sizeof(float) * (R + 2 * BC * LDC + BC + TAB + K);
 };
 
 template <typename TIn, int K, int V>
 __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
-    constexpr int LK = PrepLds<K>::LK;
+    constexpr int LK = PrepLds<K, V>::LK, LW = PrepLds<K, V>::LW, LV = PrepLds<K, V>::LV;
+    constexpr int NV4 = (BC * V / 4 + NTH - 1) / NTH;  // float4 groups of v per thread
+    constexpr int NK4 = (BC * K / 4 + NTH - 1) / NTH;  // float4 groups of a C x K tile per thread
     extern __shared__ __align__(16) unsigned char smem[];
-    float *sQ = reinterpret_cast<float *>(smem);  // q, later beta k e^Gamma
-    float *sK = sQ + BC * LK;
-    float *sG = sK + BC * LK;                     // log-decay, then Gamma
-    float *sA = sG + BC * LK;                     // Abar
-    float *sT = sA + BC * LDC;                    // T
-    float *sB = sT + BC * LDC;                    // beta
-    float *sE = sB + BC;                          // Gamma at the chunk end
+    float *sQ = reinterpret_cast<float *>(smem);     // q
+    float *sK = sQ + BC * LK;                          // k
+    float *sG = sK + BC * LK;                          // log-decay, Gamma, then F1
+    float *sW = reinterpret_cast<float *>(smem);     // beta K e^Gamma  (after the element-wise phase)
+    float *sBV = sW + BC * LW;                         // beta v          (after the element-wise phase)
+    float *sA = reinterpret_cast<float *>(smem) + PrepLds<K, V>::R;  // Abar
+    float *sT = sA + BC * LDC;                         // T
+    float *sB = sT + BC * LDC;                         // beta
+    float *sEpq = sB + BC;                             // [NP][NP][K] e^{m_p - m_q}
+    float *sEm = sEpq + NP * NP * K;                   // [NP][K] e^{m_p}
+    float *sEe = sEm + NP * K;                         // [NP][K] e^{Gamma_C - m_p}
+    float *sMid = sEe + NP * K;                        // [NP][K] m_p
+    float *sE = sMid + NP * K;                         // [K] Gamma_C
 
     const int n = blockIdx.x, h = blockIdx.y, H = a.H;
     const ChunkPos cp = slot_chunk(n, a.cu_seqlens, a.num_seqs, a.T);
@@ -158,58 +180,118 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     const int64_t sh = (int64_t)n * H + h;
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
     const TIn *v = static_cast<const TIn *>(a.v);
-
-    for (int i = tid; i < BC * K; i += NTH) {
-        const int r = i / K, c = i % K;
-        float qv = 0.f, kv = 0.f, gv = 0.f;  // rows past the chunk: no token, no decay
-        if (r < cp.L) {
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 rv[NV4];  // this chunk's v, in flight until U is formed
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int idx = tid + NTH * i, r = (4 * idx) / V, c = (4 * idx) % V;
+        rv[i] = (idx < BC * V / 4 && r < cp.L) ? ld4(v + ((cp.t0 + r) * H + h) * V + c) : z4;
+    }
+    {
+        // all loads first (four elements per load), then the LDS stores
+        float4 rq[NK4], rk[NK4], rg[NK4];
+#pragma unroll
+        for (int i = 0; i < NK4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
+            const bool ok = idx < BC * K / 4 && r < cp.L;  // rows past the chunk: no token, no decay
             const int64_t gi = ((cp.t0 + r) * H + h) * K + c;
-            qv = ld_f32(q, gi);
-            kv = ld_f32(k, gi);
-            gv = gate_log(a.gate, gi);
+            rq[i] = ok ? ld4(q + gi) : z4;
+            rk[i] = ok ? ld4(k + gi) : z4;
+            rg[i] = ok ? ld4(a.gate.gate + gi) : z4;
         }
-        sQ[r * LK + c] = qv;
-        sK[r * LK + c] = kv;
-        sG[r * LK + c] = gv;
+#pragma unroll
+        for (int i = 0; i < NK4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
+            if (idx < BC * K / 4) {
+                st4(sQ + r * LK + c, rq[i]);
+                st4(sK + r * LK + c, rk[i]);
+                st4(sG + r * LK + c, gate_log4(a.gate, rg[i], r < cp.L));
+            }
+        }
     }
     if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
     __syncthreads();
     if (tid < K) {
         float run = 0.f;
+#pragma unroll 8
         for (int r = 0; r < BC; ++r) {
             run += sG[r * LK + tid];
             sG[r * LK + tid] = run;
         }
         sE[tid] = run;
+        a.w.gC[sh * K + tid] = expf(run);
     }
     __syncthreads();
+    for (int i = tid; i < (NP * NP + 3 * NP) * K; i += NTH) {
+        const int c = i % K, j = i / K;
+        if (j < NP * NP) {
+            const int pp = j / NP, qq = j % NP;
+            sEpq[j * K + c] = qq <= pp ? expf(sG[(16 * pp + 7) * LK + c] - sG[(16 * qq + 7) * LK + c]) : 0.f;
+        } else if (j < NP * NP + NP) {
+            sEm[(j - NP * NP) * K + c] = expf(sG[(16 * (j - NP * NP) + 7) * LK + c]);
+        } else if (j < NP * NP + 2 * NP) {
+            const int pp = j - NP * NP - NP;
+            sEe[pp * K + c] = expf(sE[c] - sG[(16 * pp + 7) * LK + c]);
+        } else {
+            const int pp = j - NP * NP - 2 * NP;
+            sMid[pp * K + c] = sG[(16 * pp + 7) * LK + c];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < BC * K; i += NTH) {  // F1 replaces Gamma, element by element
+        const int r = i / K, c = i % K;
+        sG[r * LK + c] = expf(sG[r * LK + c] - sMid[(r >> 4) * K + c]);
+    }
+    __syncthreads();
+    float *sF1 = sG;
 
-    // Abar (strictly lower) and A_qk (lower) in 16x16 tiles, split at the row tile's middle
+    // Abar (strictly lower) and A_qk (lower): the ten tiles on or below the diagonal, spread
+    // over the waves.  Row r of tile p enters as k_r F1_r (q_r F1_r); column s of tile q as
+    // k_s / F1_s * e^{m_p - m_q}; the channel axis is read four at a time.
     float *Aqk = a.w.Aqk + sh * BC * BC, *Abar = a.w.Abar + sh * BC * BC;
-    for (int t = w; t < NP * NP; t += 4) {
-        const int p = t / NP, qt = t % NP;
+    for (int t = w; t < NP * (NP + 1) / 2; t += 4) {
+        int p = 0;
+        while ((p + 1) * (p + 2) / 2 <= t) ++p;
+        const int qt = t - p * (p + 1) / 2;
         f4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
-        if (qt <= p) {
-            const float *mref = sG + (16 * p + 7) * LK;
-            const int r = 16 * p + i16, s = 16 * qt + i16;
-#pragma unroll 4
-            for (int c0 = 0; c0 < K; c0 += 4) {
-                const int c = c0 + g4;
-                const float m = mref[c];
-                const float er = expf(sG[r * LK + c] - m);
-                const float b = sK[s * LK + c] * expf(m - sG[s * LK + c]);
-                ak = mf(sK[r * LK + c] * er, b, ak);
-                aq = mf(sQ[r * LK + c] * er, b, aq);
-            }
+        const int r = 16 * p + i16, sc = 16 * qt + i16;
+        const float *e = sEpq + (p * NP + qt) * K + 4 * g4;
+#pragma unroll 2
+        for (int c0 = 0; c0 < K; c0 += 16) {
+            const float4 f1r = *reinterpret_cast<const float4 *>(sF1 + r * LK + c0 + 4 * g4);
+            const float4 kr = *reinterpret_cast<const float4 *>(sK + r * LK + c0 + 4 * g4);
+            const float4 qr = *reinterpret_cast<const float4 *>(sQ + r * LK + c0 + 4 * g4);
+            const float4 f1s = *reinterpret_cast<const float4 *>(sF1 + sc * LK + c0 + 4 * g4);
+            const float4 ks = *reinterpret_cast<const float4 *>(sK + sc * LK + c0 + 4 * g4);
+            const float4 ep = *reinterpret_cast<const float4 *>(e + c0);
+            const float b0 = ks.x * __builtin_amdgcn_rcpf(f1s.x) * ep.x, b1 = ks.y * __builtin_amdgcn_rcpf(f1s.y) * ep.y;
+            const float b2 = ks.z * __builtin_amdgcn_rcpf(f1s.z) * ep.z, b3 = ks.w * __builtin_amdgcn_rcpf(f1s.w) * ep.w;
+            ak = mf(kr.x * f1r.x, b0, ak);
+            aq = mf(qr.x * f1r.x, b0, aq);
+            ak = mf(kr.y * f1r.y, b1, ak);
+            aq = mf(qr.y * f1r.y, b1, aq);
+            ak = mf(kr.z * f1r.z, b2, ak);
+            aq = mf(qr.z * f1r.z, b2, aq);
+            ak = mf(kr.w * f1r.w, b3, ak);
+            aq = mf(qr.w * f1r.w, b3, aq);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e, col = 16 * qt + i16;
-            const float vk = row > col ? ak[e] : 0.f;  // selects: masked entries may be inf
-            const float vq = row >= col ? aq[e] : 0.f;
+        for (int u = 0; u < 4; ++u) {
+            const int row = 16 * p + 4 * g4 + u, col = 16 * qt + i16;
+            const float vk = row > col ? ak[u] : 0.f;  // selects: masked entries may be inf
+            const float vq = row >= col ? aq[u] : 0.f;
             sA[row * LDC + col] = vk;
             Abar[row * BC + col] = vk;
             Aqk[row * BC + col] = vq;
+        }
+    }
+    for (int i = tid; i < BC * BC; i += NTH) {  // the tiles above the diagonal are zero
+        const int r = i / BC, c = i % BC;
+        if ((c >> 4) > (r >> 4)) {
+            sA[r * LDC + c] = 0.f;
+            sT[r * LDC + c] = 0.f;
+            Abar[i] = 0.f;
+            Aqk[i] = 0.f;
         }
     }
     __syncthreads();
@@ -217,56 +299,82 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     // T = (I + diag(beta) Abar)^-1: diagonal 16x16 blocks by the blocked inverse, then
     // block forward substitution T_pq = -T_pp sum_{q<=u<p} A_pu T_uq
     if (w < NP) {
-        const int p = w;
+        const int pb = w;
         f4 av;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e;
-            av[e] = sB[row] * sA[row * LDC + 16 * p + i16];
+        for (int u = 0; u < 4; ++u) {
+            const int row = 16 * pb + 4 * g4 + u;
+            av[u] = sB[row] * sA[row * LDC + 16 * pb + i16];
         }
         const f4 tb = unit_lower_inverse16<float>(av, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sT[(16 * p + 4 * g4 + e) * LDC + 16 * p + i16] = tb[e];
-    }
-    for (int i = tid; i < BC * BC; i += NTH) {
-        const int r = i / BC, c = i % BC;
-        if ((c >> 4) > (r >> 4)) sT[r * LDC + c] = 0.f;
+        for (int u = 0; u < 4; ++u) sT[(16 * pb + 4 * g4 + u) * LDC + 16 * pb + i16] = tb[u];
     }
     __syncthreads();
-    for (int p = 1; p < NP; ++p) {
-        if (w < p) {
+    for (int pb = 1; pb < NP; ++pb) {
+        if (w < pb) {
             const int qb = w;
             f4 x = {0.f, 0.f, 0.f, 0.f};
-            for (int u = qb; u < p; ++u) {
+            for (int u = qb; u < pb; ++u) {
 #pragma unroll
                 for (int s0 = 0; s0 < 16; s0 += 4) {
-                    const int r = 16 * p + i16, s = 16 * u + s0 + g4;
-                    x = mf(sB[r] * sA[r * LDC + s], sT[s * LDC + 16 * qb + i16], x);
+                    const int r = 16 * pb + i16, sc = 16 * u + s0 + g4;
+                    x = mf(sB[r] * sA[r * LDC + sc], sT[sc * LDC + 16 * qb + i16], x);
                 }
             }
             f4 xr;  // row-operand form of T_pp: lane (g, r) holds T_pp[r][4g + s]
 #pragma unroll
-            for (int s = 0; s < 4; ++s) xr[s] = sT[(16 * p + i16) * LDC + 16 * p + 4 * g4 + s];
+            for (int u = 0; u < 4; ++u) xr[u] = sT[(16 * pb + i16) * LDC + 16 * pb + 4 * g4 + u];
             const f4 y = mma16_reg<float>(xr, x);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sT[(16 * p + 4 * g4 + e) * LDC + 16 * qb + i16] = -y[e];
+            for (int u = 0; u < 4; ++u) sT[(16 * pb + 4 * g4 + u) * LDC + 16 * qb + i16] = -y[u];
         }
         __syncthreads();
     }
 
-    // elementwise products and the chunk-end decay; beta K e^Gamma replaces q in LDS
+    // element-wise products: e^Gamma = F1 e^{m_p}, e^{Gamma_C - Gamma} = e^{Gamma_C - m_p} / F1
     float *Qg = a.w.Qg + sh * BC * K, *Kd = a.w.Kd + sh * BC * K, *Kg = a.w.Kg + sh * BC * K;
-    for (int i = tid; i < BC * K; i += NTH) {
-        const int r = i / K, c = i % K;
-        const float G = sG[r * LK + c], eg = expf(G), kv = sK[r * LK + c];
-        Qg[r * K + c] = sQ[r * LK + c] * eg;
-        Kd[r * K + c] = kv * expf(sE[c] - G);
-        Kg[r * K + c] = kv * eg;
-        sQ[r * LK + c] = sB[r] * kv * eg;
+    float4 bkg[NK4];
+#pragma unroll
+    for (int i = 0; i < NK4; ++i) {
+        const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
+        if (idx < BC * K / 4) {
+            const int pp = r >> 4;
+            const float4 f1 = *reinterpret_cast<const float4 *>(sF1 + r * LK + c);
+            const float4 kv = *reinterpret_cast<const float4 *>(sK + r * LK + c);
+            const float4 qv = *reinterpret_cast<const float4 *>(sQ + r * LK + c);
+            const float4 em = *reinterpret_cast<const float4 *>(sEm + pp * K + c);
+            const float4 ee = *reinterpret_cast<const float4 *>(sEe + pp * K + c);
+            const float4 eg = make_float4(f1.x * em.x, f1.y * em.y, f1.z * em.z, f1.w * em.w);
+            const float4 ed = make_float4(ee.x * __builtin_amdgcn_rcpf(f1.x), ee.y * __builtin_amdgcn_rcpf(f1.y),
+                                          ee.z * __builtin_amdgcn_rcpf(f1.z), ee.w * __builtin_amdgcn_rcpf(f1.w));
+            const float4 kg = make_float4(kv.x * eg.x, kv.y * eg.y, kv.z * eg.z, kv.w * eg.w);
+            st4(Qg + r * K + c, make_float4(qv.x * eg.x, qv.y * eg.y, qv.z * eg.z, qv.w * eg.w));
+            st4(Kd + r * K + c, make_float4(kv.x * ed.x, kv.y * ed.y, kv.z * ed.z, kv.w * ed.w));
+            st4(Kg + r * K + c, kg);
+            const float b = sB[r];
+            bkg[i] = make_float4(b * kg.x, b * kg.y, b * kg.z, b * kg.w);
+        }
     }
-    if (tid < K) a.w.gC[sh * K + tid] = expf(sE[tid]);
     float *Tm = a.w.Tm + sh * BC * BC;
-    for (int i = tid; i < BC * BC; i += NTH) Tm[i] = sT[(i / BC) * LDC + i % BC];
+    for (int i = tid; i < BC * BC / 4; i += NTH) {
+        const int e = 4 * i;
+        st4(Tm + e, *reinterpret_cast<const float4 *>(sT + (e / BC) * LDC + e % BC));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NK4; ++i) {  // q, k and F1 are consumed: their LDS takes beta K e^Gamma
+        const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
+        if (idx < BC * K / 4) st4(sW + r * LW + c, bkg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {  // and beta v
+        const int idx = tid + NTH * i, r = (4 * idx) / V, c = (4 * idx) % V;
+        if (idx < BC * V / 4) {
+            const float b = sB[r];
+            st4(sBV + r * LV + c, make_float4(b * rv[i].x, b * rv[i].y, b * rv[i].z, b * rv[i].w));
+        }
+    }
     __syncthreads();
 
     // W = T (beta K e^Gamma), U = T (beta V); T is lower triangular
@@ -275,20 +383,17 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
         const int p = t / (K / 16), ct = t % (K / 16);
         f4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int s0 = 0; s0 < 16 * (p + 1); s0 += 4)
-            acc = mf(sT[(16 * p + i16) * LDC + s0 + g4], sQ[(s0 + g4) * LK + 16 * ct + i16], acc);
+            acc = mf(sT[(16 * p + i16) * LDC + s0 + g4], sW[(s0 + g4) * LW + 16 * ct + i16], acc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) W[(16 * p + 4 * g4 + e) * K + 16 * ct + i16] = acc[e];
+        for (int u = 0; u < 4; ++u) W[(16 * p + 4 * g4 + u) * K + 16 * ct + i16] = acc[u];
     }
     for (int t = w; t < NP * (V / 16); t += 4) {
         const int p = t / (V / 16), ct = t % (V / 16);
         f4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < 16 * (p + 1); s0 += 4) {
-            const int s = s0 + g4;
-            const float bv = s < cp.L ? sB[s] * ld_f32(v, ((cp.t0 + s) * H + h) * V + 16 * ct + i16) : 0.f;
-            acc = mf(sT[(16 * p + i16) * LDC + s], bv, acc);
-        }
+        for (int s0 = 0; s0 < 16 * (p + 1); s0 += 4)
+            acc = mf(sT[(16 * p + i16) * LDC + s0 + g4], sBV[(s0 + g4) * LV + 16 * ct + i16], acc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) U[(16 * p + 4 * g4 + e) * V + 16 * ct + i16] = acc[e];
+        for (int u = 0; u < 4; ++u) U[(16 * p + 4 * g4 + u) * V + 16 * ct + i16] = acc[u];
     }
 }
 
@@ -317,9 +422,21 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdArgs a) {
     int base;
     seq_range(s, a.cu_seqlens, a.T, t0, len, base);
     const int nch = (int)((len + BC - 1) / BC);
-    for (int i = tid; i < K * SBV; i += NTH) {
-        const int r = i / SBV, c = i % SBV;
-        sS[r * LB + c] = a.initial_state ? a.initial_state[(((int64_t)s * H + h) * K + r) * V + j0 + c] : 0.f;
+    {
+        constexpr int N4 = (K * SBV / 4 + NTH - 1) / NTH;
+        float4 x[N4];
+#pragma unroll
+        for (int i = 0; i < N4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / SBV, c = (4 * idx) % SBV;
+            x[i] = (idx < K * SBV / 4 && a.initial_state)
+                       ? ld4(a.initial_state + (((int64_t)s * H + h) * K + r) * V + j0 + c)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < N4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / SBV, c = (4 * idx) % SBV;
+            if (idx < K * SBV / 4) st4(sS + r * LB + c, x[i]);
+        }
     }
     float4 wf[KQ];
     float uf[4], kdf[NST][16], gcf[NST][4];
@@ -419,9 +536,20 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
     seq_range(s, a.cu_seqlens, a.T, t0, len, base);
     const int nch = (int)((len + BC - 1) / BC);
     const int64_t st = ((int64_t)s * H + h) * K;
-    for (int i = tid; i < K * SBV; i += NTH) {
-        const int r = i / SBV, c = i % SBV;
-        sD[r * LB + c] = a.d_final_state ? a.d_final_state[(st + r) * V + j0 + c] : 0.f;
+    {
+        constexpr int N4 = (K * SBV / 4 + NTH - 1) / NTH;
+        float4 x[N4];
+#pragma unroll
+        for (int i = 0; i < N4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / SBV, c = (4 * idx) % SBV;
+            x[i] = (idx < K * SBV / 4 && a.d_final_state) ? ld4(a.d_final_state + (st + r) * V + j0 + c)
+                                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < N4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / SBV, c = (4 * idx) % SBV;
+            if (idx < K * SBV / 4) st4(sD + r * LB + c, x[i]);
+        }
     }
     const int sr = tid >> 2, sg = 4 * (tid & 3);  // dO staging: row and first column of this thread
     float4 kdf[KQ], dof;
@@ -613,7 +741,16 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
     };
 
     load(0);
-    for (int i = tid; i < BC * BC; i += NTH) sT[(i / BC) * LDC + i % BC] = Tm[i];
+    {
+        float4 x[BC * BC / 4 / NTH];
+#pragma unroll
+        for (int i = 0; i < BC * BC / 4 / NTH; ++i) x[i] = ld4(Tm + 4 * (tid + NTH * i));
+#pragma unroll
+        for (int i = 0; i < BC * BC / 4 / NTH; ++i) {
+            const int e = 4 * (tid + NTH * i);
+            st4(sT + (e / BC) * LDC + e % BC, x[i]);
+        }
+    }
     if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
     store();
     __syncthreads();
@@ -692,7 +829,14 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
     float *sKg = sPW + BC * LK;                    // [C][K+4] K e^Gamma
     float *sM = sKg + BC * LK;                     // [C][C] beta MT, then Y = dT T^T
     float *sY = sM + BC * LDC;                     // [C][C] dT
-    const float *Kg = a.w.Kg + sh * BC * K;
+    const float *Kg = a.w.Kg + sh * BC * K, *Abar = a.w.Abar + sh * BC * BC;
+    float abr[4][4];  // Abar on this wave's C x C tiles, for rowsum(dA Abar)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = w + 4 * i, p = t / NP, qt = t % NP;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) abr[i][e] = Abar[(16 * p + 4 * g4 + e) * BC + 16 * qt + i16];
+    }
     float4 kg4[(BC * K / 4 + NTH - 1) / NTH];
 #pragma unroll
     for (int i = 0; i < (BC * K / 4 + NTH - 1) / NTH; ++i) {
@@ -807,7 +951,6 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
     }
     __syncthreads();
     // dA = -strict_tril(T^T Y); rowsum(dA Abar) for dbeta; beta dA is what the key space needs
-    const float *Abar = a.w.Abar + sh * BC * BC;
     float *dAb = a.w.MT + sh * BC * BC;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -821,7 +964,7 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * p + 4 * g4 + e;
             const float da = row > s ? -acc[e] : 0.f;
-            const float part = row16_sum(da * Abar[row * BC + s]);
+            const float part = row16_sum(da * abr[i][e]);
             if (i16 == 0) sRa[qt * BC + row] = part;
             dAb[row * BC + s] = sB[row] * da;
         }
@@ -877,27 +1020,61 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
     const int64_t sh = (int64_t)n * H + h;
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
-
-    for (int i = tid; i < BC * KB; i += NTH) {
-        const int r = i / KB, c = i % KB;
-        float qv = 0.f, kv = 0.f, gv = 0.f;
-        if (r < cp.L) {
-            const int64_t gi = ((cp.t0 + r) * H + h) * K + c0 + c;
-            qv = ld_f32(q, gi);
-            kv = ld_f32(k, gi);
-            gv = gate_log(a.gate, gi);
+    // element-wise inputs of this thread's output tiles (dO S^T, Vt dS'^T, T^T dW), in
+    // flight during the staging and the products
+    float pre[NOWN][3][4];
+    {
+        const float *PS = a.w.PS + sh * BC * K, *PdK = a.w.PdK + sh * BC * K, *dBk = a.w.PW + sh * BC * K;
+#pragma unroll
+        for (int i = 0; i < NOWN; ++i) {
+            const int t = w + 4 * i, rt = t / KBT, ct = t % KBT, gc = c0 + 16 * ct + i16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * rt + 4 * g4 + e;
+                pre[i][0][e] = PS[row * K + gc];
+                pre[i][1][e] = PdK[row * K + gc];
+                pre[i][2][e] = dBk[row * K + gc];
+            }
         }
-        sQ[r * LKB + c] = qv;
-        sK[r * LKB + c] = kv;
-        sF2[r * LKB + c] = gv;
     }
-    const float *MA = a.w.MA + sh * BC * BC, *dAb = a.w.MT + sh * BC * BC;
-    for (int i = tid; i < BC * BC / 4; i += NTH) {
-        const int r = (4 * i) / BC, c = (4 * i) % BC;
-        const float4 m = ld4(MA + 4 * i);
-        st4(sMA + r * LDC + c, make_float4(c <= r ? m.x : 0.f, c + 1 <= r ? m.y : 0.f, c + 2 <= r ? m.z : 0.f,
-                                           c + 3 <= r ? m.w : 0.f));
-        st4(sdA + r * LDC + c, ld4(dAb + 4 * i));
+
+    {
+        // all loads first (four elements per load), then the LDS stores
+        constexpr int NK4 = (BC * KB / 4 + NTH - 1) / NTH, NM4 = BC * BC / 4 / NTH;
+        float4 rq[NK4], rk[NK4], rg[NK4], rm[NM4], rd[NM4];
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < NK4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
+            const bool ok = idx < BC * KB / 4 && r < cp.L;
+            const int64_t gi = ((cp.t0 + r) * H + h) * K + c0 + c;
+            rq[i] = ok ? ld4(q + gi) : z4;
+            rk[i] = ok ? ld4(k + gi) : z4;
+            rg[i] = ok ? ld4(a.gate.gate + gi) : z4;
+        }
+        const float *MA = a.w.MA + sh * BC * BC, *dAb = a.w.MT + sh * BC * BC;
+#pragma unroll
+        for (int i = 0; i < NM4; ++i) {
+            rm[i] = ld4(MA + 4 * (tid + NTH * i));
+            rd[i] = ld4(dAb + 4 * (tid + NTH * i));
+        }
+#pragma unroll
+        for (int i = 0; i < NK4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
+            if (idx < BC * KB / 4) {
+                st4(sQ + r * LKB + c, rq[i]);
+                st4(sK + r * LKB + c, rk[i]);
+                st4(sF2 + r * LKB + c, gate_log4(a.gate, rg[i], r < cp.L));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NM4; ++i) {
+            const int e = 4 * (tid + NTH * i), r = e / BC, c = e % BC;
+            const float4 m = rm[i];  // tril(dO Vt^T): entries with s > r are dropped
+            st4(sMA + r * LDC + c, make_float4(c <= r ? m.x : 0.f, c + 1 <= r ? m.y : 0.f, c + 2 <= r ? m.z : 0.f,
+                                               c + 3 <= r ? m.w : 0.f));
+            st4(sdA + r * LDC + c, rd[i]);
+        }
     }
     if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
     __syncthreads();
@@ -934,20 +1111,12 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    const float *PS = a.w.PS + sh * BC * K, *PdK = a.w.PdK + sh * BC * K, *dBk = a.w.PW + sh * BC * K;
     float dgt[NOWN][4], est[NOWN][4];
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
         const int t = w + 4 * i, rt = t / KBT, ct = t % KBT;
         const int c = 16 * ct + i16, gc = c0 + c;
-        float ps_[4], pdk_[4], dbk_[4];  // element-wise inputs, in flight during the products
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * rt + 4 * g4 + e;
-            ps_[e] = PS[row * K + gc];
-            pdk_[e] = PdK[row * K + gc];
-            dbk_[e] = dBk[row * K + gc];
-        }
+        const float *ps_ = pre[i][0], *pdk_ = pre[i][1], *dbk_ = pre[i][2];
         // row side of the decayed adjoints (rows of tile rt): A_qk -> dq, beta dA -> dk;
         // column s of tile qs enters as k_s F2_s E[rt][qs], the result is scaled by F1_r
         f4 xq = {0.f, 0.f, 0.f, 0.f}, xk = xq;
@@ -1018,7 +1187,8 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     }
     __syncthreads();
     // d ln alpha per key channel: reverse in-chunk sum of the row terms, plus the chunk-end
-    // terms gamma_C rowsum(S dS') and the exclusive forward sum of the Kd terms
+    // terms gamma_C rowsum(S dS') and the exclusive forward sum of the Kd terms; the result
+    // replaces the row terms in LDS
     if (tid < KB) {
         const int c = tid, gc = c0 + c;
         float dl[BC];
@@ -1032,15 +1202,36 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = BC - 1; r >= 0; --r) {
             rv += sQ[r * LKB + c];
-            dl[r] += rv;
+            sQ[r * LKB + c] = dl[r] + rv;
         }
+    }
+    __syncthreads();
+    // dgate in four-element groups over the whole workgroup (alpha read in one batch)
+    {
+        constexpr int NK4 = (BC * KB / 4 + NTH - 1) / NTH;
         const bool log_gate = a.gate.mode == GATE_LOG;
+        float4 al[NK4];
 #pragma unroll
-        for (int r = 0; r < BC; ++r)
-            if (r < cp.L) {
-                const int64_t gi = ((cp.t0 + r) * H + h) * K + gc;
-                a.dgate[gi] = log_gate ? dl[r] : dl[r] * __builtin_amdgcn_rcpf(a.gate.gate[gi]);
+        for (int i = 0; i < NK4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
+            al[i] = (!log_gate && idx < BC * KB / 4 && r < cp.L) ? ld4(a.gate.gate + ((cp.t0 + r) * H + h) * K + c0 + c)
+                                                               : make_float4(1.f, 1.f, 1.f, 1.f);
+        }
+#pragma unroll
+        for (int i = 0; i < NK4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
+            if (idx < BC * KB / 4 && r < cp.L) {
+                const float *x = sQ + r * LKB + c;
+                float4 o = make_float4(x[0], x[1], x[2], x[3]);
+                if (!log_gate) {
+                    o.x *= __builtin_amdgcn_rcpf(al[i].x);
+                    o.y *= __builtin_amdgcn_rcpf(al[i].y);
+                    o.z *= __builtin_amdgcn_rcpf(al[i].z);
+                    o.w *= __builtin_amdgcn_rcpf(al[i].w);
+                }
+                st4(a.dgate + ((cp.t0 + r) * H + h) * K + c0 + c, o);
             }
+        }
     }
 }
 
@@ -1056,7 +1247,7 @@ hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
     auto kvg = bwd_vgrads_kernel<TIn, K, V>;
     auto kkg = bwd_kgrads_kernel<TIn, K, V>;
     if (!attr) {
-        hipError_t e = set_lds<K, V>(reinterpret_cast<const void *>(kprep), PrepLds<K>::bytes);
+        hipError_t e = set_lds<K, V>(reinterpret_cast<const void *>(kprep), PrepLds<K, V>::bytes);
         if (e == hipSuccess) e = set_lds<K, V>(reinterpret_cast<const void *>(kvg), VgLds<K>::bytes);
         if (e == hipSuccess) e = set_lds<K, V>(reinterpret_cast<const void *>(kkg), KgLds<K>::bytes);
         if (e != hipSuccess) return e;
@@ -1064,7 +1255,8 @@ hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
     }
     const int hs8 = (num_seqs * a.H + 7) / 8, sh8 = (int)(((int64_t)a.slots * a.H + 7) / 8);
     const dim3 gp(a.slots, a.H), gs(8 * (V / SBV) * hs8), gk(8 * (K / KgLds<K>::KB) * sh8);
-    hipLaunchKernelGGL(kprep, gp, dim3(NTH), PrepLds<K>::bytes, stream, a);
+    constexpr size_t prep_bytes = PrepLds<K, V>::bytes;
+    hipLaunchKernelGGL(kprep, gp, dim3(NTH), prep_bytes, stream, a);
     hipLaunchKernelGGL((bwd_states_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL((bwd_dstates_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL(kvg, gp, dim3(NTH), VgLds<K>::bytes, stream, a);
