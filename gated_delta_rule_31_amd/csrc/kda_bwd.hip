@@ -129,12 +129,23 @@ __device__ __forceinline__ float4 ld4_any(const void *p, int is_bf16, int64_t i)
 }
 __device__ __forceinline__ void st4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
 
-// sum over the 16 lanes that share lane >> 4 (one accumulator row)
+// Loads are issued from addresses that are always valid (rows past the chunk read its last
+// row) and masked where the value is used: a load under a per-lane condition is compiled
+// into its own branch with a wait for it, which would serialise a batch of loads.
+__device__ __forceinline__ int crow(int r, int L) { return r < L ? r : L - 1; }
+__device__ __forceinline__ float4 mask4(float4 x, bool ok) { return ok ? x : make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// sum over the 16 lanes that share lane >> 4 (one accumulator row): DPP row rotations by
+// 8, 4, 2 and 1 stay inside each 16-lane row, and every lane ends with the row's sum
+template <int ROR>
+__device__ __forceinline__ float row_ror(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + ROR, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    x += row_ror<8>(x);
+    x += row_ror<4>(x);
+    x += row_ror<2>(x);
+    x += row_ror<1>(x);
     return x;
 }
 
@@ -180,12 +191,12 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     const int64_t sh = (int64_t)n * H + h;
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
     const TIn *v = static_cast<const TIn *>(a.v);
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    static_assert(BC * K / 4 % NTH == 0 && BC * V / 4 % NTH == 0, "whole float4 groups per thread");
     float4 rv[NV4];  // this chunk's v, in flight until U is formed
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
         const int idx = tid + NTH * i, r = (4 * idx) / V, c = (4 * idx) % V;
-        rv[i] = (idx < BC * V / 4 && r < cp.L) ? ld4(v + ((cp.t0 + r) * H + h) * V + c) : z4;
+        rv[i] = ld4(v + ((cp.t0 + crow(r, cp.L)) * H + h) * V + c);
     }
     {
         // all loads first (four elements per load), then the LDS stores
@@ -193,20 +204,17 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < NK4; ++i) {
             const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
-            const bool ok = idx < BC * K / 4 && r < cp.L;  // rows past the chunk: no token, no decay
-            const int64_t gi = ((cp.t0 + r) * H + h) * K + c;
-            rq[i] = ok ? ld4(q + gi) : z4;
-            rk[i] = ok ? ld4(k + gi) : z4;
-            rg[i] = ok ? ld4(a.gate.gate + gi) : z4;
+            const int64_t gi = ((cp.t0 + crow(r, cp.L)) * H + h) * K + c;
+            rq[i] = ld4(q + gi);
+            rk[i] = ld4(k + gi);
+            rg[i] = ld4(a.gate.gate + gi);
         }
 #pragma unroll
-        for (int i = 0; i < NK4; ++i) {
+        for (int i = 0; i < NK4; ++i) {  // rows past the chunk: no token, no decay
             const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
-            if (idx < BC * K / 4) {
-                st4(sQ + r * LK + c, rq[i]);
-                st4(sK + r * LK + c, rk[i]);
-                st4(sG + r * LK + c, gate_log4(a.gate, rg[i], r < cp.L));
-            }
+            st4(sQ + r * LK + c, mask4(rq[i], r < cp.L));
+            st4(sK + r * LK + c, mask4(rk[i], r < cp.L));
+            st4(sG + r * LK + c, gate_log4(a.gate, rg[i], r < cp.L));
         }
     }
     if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
@@ -368,12 +376,10 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
         if (idx < BC * K / 4) st4(sW + r * LW + c, bkg[i]);
     }
 #pragma unroll
-    for (int i = 0; i < NV4; ++i) {  // and beta v
+    for (int i = 0; i < NV4; ++i) {  // and beta v (beta is zero past the chunk)
         const int idx = tid + NTH * i, r = (4 * idx) / V, c = (4 * idx) % V;
-        if (idx < BC * V / 4) {
-            const float b = sB[r];
-            st4(sBV + r * LV + c, make_float4(b * rv[i].x, b * rv[i].y, b * rv[i].z, b * rv[i].w));
-        }
+        const float b = sB[r];
+        st4(sBV + r * LV + c, make_float4(b * rv[i].x, b * rv[i].y, b * rv[i].z, b * rv[i].w));
     }
     __syncthreads();
 
@@ -518,43 +524,56 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdArgs a) {
 // dstates: the reverse over chunks, the same two-phase structure:
 //   dVt = Kd dS' + A_qk^T dO (wave w: rows of tile w),
 //   dS  = gamma_C dS' + Qg^T dO - W^T dVt (wave w: key tiles w, w + 4, ...)
+// on DBV value columns per workgroup (the prefetched fragments serve every column tile).
+template <int V>
+struct DstCfg {
+    static constexpr int DBV = V < 32 ? V : 32, NCT = DBV / 16;
+};
+
 template <int K, int V>
 __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
-    constexpr int LB = SBV + 4, KQ = K / 16, NST = (K / 16 + 3) / 4;
+    constexpr int DBV = DstCfg<V>::DBV, NCT = DstCfg<V>::NCT;
+    constexpr int LB = DBV + 4, KQ = K / 16, NST = (K / 16 + 3) / 4;
     __shared__ float sD[K * LB];
     __shared__ float sO[BC * LB];
     __shared__ float sV[BC * LB];
     int hs, vb;
-    xcd_map(blockIdx.x, V / SBV, hs, vb);
+    xcd_map(blockIdx.x, V / DBV, hs, vb);
     const int H = a.H;
     if (hs >= a.num_seqs * H) return;
     const int h = hs % H, s = hs / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
-    const int j0 = vb * SBV, p = w;
+    const int j0 = vb * DBV, p = w;
     int64_t t0, len;
     int base;
     seq_range(s, a.cu_seqlens, a.T, t0, len, base);
     const int nch = (int)((len + BC - 1) / BC);
     const int64_t st = ((int64_t)s * H + h) * K;
+    static_assert(BC * DBV / 4 % NTH == 0, "whole float4 groups per thread");
     {
-        constexpr int N4 = (K * SBV / 4 + NTH - 1) / NTH;
+        constexpr int N4 = (K * DBV / 4 + NTH - 1) / NTH;
         float4 x[N4];
+        if (a.d_final_state) {
 #pragma unroll
-        for (int i = 0; i < N4; ++i) {
-            const int idx = tid + NTH * i, r = (4 * idx) / SBV, c = (4 * idx) % SBV;
-            x[i] = (idx < K * SBV / 4 && a.d_final_state) ? ld4(a.d_final_state + (st + r) * V + j0 + c)
-                                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int i = 0; i < N4; ++i) {
+                const int idx = min(tid + NTH * i, K * DBV / 4 - 1), r = (4 * idx) / DBV, c = (4 * idx) % DBV;
+                x[i] = ld4(a.d_final_state + (st + r) * V + j0 + c);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < N4; ++i) x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int i = 0; i < N4; ++i) {
-            const int idx = tid + NTH * i, r = (4 * idx) / SBV, c = (4 * idx) % SBV;
-            if (idx < K * SBV / 4) st4(sD + r * LB + c, x[i]);
+            const int idx = tid + NTH * i, r = (4 * idx) / DBV, c = (4 * idx) % DBV;
+            if (idx < K * DBV / 4) st4(sD + r * LB + c, x[i]);
         }
     }
-    const int sr = tid >> 2, sg = 4 * (tid & 3);  // dO staging: row and first column of this thread
-    float4 kdf[KQ], dof;
+    constexpr int NO4 = BC * DBV / 4 / NTH;  // dO staging: float4 groups per thread
+    float4 kdf[KQ], dof[NO4];
+    bool dok[NO4];
     float aqf[16], qgf[NST][16], wwf[NST][16], gcf[NST][4];
-    auto loadA = [&](int j) {  // Kd rows and A_qk columns of tile p, and this chunk's dO slice
+    auto loadA = [&](int j) {  // Kd rows and A_qk columns of tile p, and this chunk's dO block
         const int64_t sh = (int64_t)(base + j) * H + h;
         const float *Kd = a.w.Kd + sh * BC * K + (16 * p + i16) * K + 4 * g4;
 #pragma unroll
@@ -563,30 +582,32 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) aqf[4 * q + u] = q >= p ? Aqk[(16 * q + 4 * g4 + u) * BC] : 0.f;
+            for (int u = 0; u < 4; ++u) aqf[4 * q + u] = Aqk[(16 * q + 4 * g4 + u) * BC];  // used for q >= p
         const int64_t tc = t0 + (int64_t)j * BC;
         const int L = (int)min((int64_t)BC, len - (int64_t)j * BC);
-        dof = sr < L ? ld4_any(a.d_out, a.dout_bf16, ((tc + sr) * H + h) * V + j0 + sg)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < NO4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / DBV, c = (4 * idx) % DBV;
+            dof[i] = ld4_any(a.d_out, a.dout_bf16, ((tc + crow(r, L)) * H + h) * V + j0 + c);
+            dok[i] = r < L;
+        }
     };
     auto loadB = [&](int j) {  // Qg and W columns of this wave's key tiles, gamma_C on their rows
         const int64_t sh = (int64_t)(base + j) * H + h;
         const float *Qg = a.w.Qg + sh * BC * K, *W = a.w.W + sh * BC * K, *gC = a.w.gC + sh * K;
 #pragma unroll
         for (int i = 0; i < NST; ++i) {
-            const int rt = w + 4 * i;
-            if (rt < K / 16) {
+            const int rt = min(w + 4 * i, K / 16 - 1);  // a wave with no second tile reloads its first
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int r = 16 * q + 4 * g4 + u;
-                        qgf[i][4 * q + u] = Qg[r * K + 16 * rt + i16];
-                        wwf[i][4 * q + u] = W[r * K + 16 * rt + i16];
-                    }
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 16 * q + 4 * g4 + u;
+                    qgf[i][4 * q + u] = Qg[r * K + 16 * rt + i16];
+                    wwf[i][4 * q + u] = W[r * K + 16 * rt + i16];
+                }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) gcf[i][e] = gC[16 * rt + 4 * g4 + e];
-            }
+            for (int e = 0; e < 4; ++e) gcf[i][e] = gC[16 * rt + 4 * g4 + e];
         }
     };
     if (nch > 0) loadA(nch - 1);
@@ -595,38 +616,52 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
         loadB(j);
         __syncthreads();
         float *dhp = a.w.dh + sh * K * V;
-        for (int i = tid; i < K * SBV; i += NTH) {
-            const int r = i / SBV, c = i % SBV;
-            dhp[r * V + j0 + c] = sD[r * LB + c];
+        for (int i = tid; i < K * DBV / 4; i += NTH) {
+            const int r = (4 * i) / DBV, c = (4 * i) % DBV;
+            st4(dhp + r * V + j0 + c, *reinterpret_cast<const float4 *>(sD + r * LB + c));
         }
         const float sc = a.scale;
-        *reinterpret_cast<float4 *>(sO + sr * LB + sg) = make_float4(sc * dof.x, sc * dof.y, sc * dof.z, sc * dof.w);
+#pragma unroll
+        for (int i = 0; i < NO4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / DBV, c = (4 * idx) % DBV;
+            const float f = dok[i] ? sc : 0.f;
+            st4(sO + r * LB + c, make_float4(f * dof[i].x, f * dof[i].y, f * dof[i].z, f * dof[i].w));
+        }
         __syncthreads();
         {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            f4 acc[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < KQ; ++q) {
                 const float *b = sD + (16 * q + 4 * g4) * LB + i16;
-                acc = mf(kdf[q].x, b[0], acc);
-                acc = mf(kdf[q].y, b[LB], acc);
-                acc = mf(kdf[q].z, b[2 * LB], acc);
-                acc = mf(kdf[q].w, b[3 * LB], acc);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    acc[ct] = mf(kdf[q].x, b[16 * ct], acc[ct]);
+                    acc[ct] = mf(kdf[q].y, b[16 * ct + LB], acc[ct]);
+                    acc[ct] = mf(kdf[q].z, b[16 * ct + 2 * LB], acc[ct]);
+                    acc[ct] = mf(kdf[q].w, b[16 * ct + 3 * LB], acc[ct]);
+                }
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (q >= p) {  // A_qk[s][r] is zero for s < r
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        acc = mf(aqf[4 * q + u], sO[(16 * q + 4 * g4 + u) * LB + i16], acc);
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+                            acc[ct] = mf(aqf[4 * q + u], sO[(16 * q + 4 * g4 + u) * LB + 16 * ct + i16], acc[ct]);
                 }
             }
             float *dVt = a.w.dVt + sh * BC * V + j0 + i16;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * p + 4 * g4 + e;
-                sV[row * LB + i16] = acc[e];
-                dVt[row * V] = acc[e];
-            }
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * p + 4 * g4 + e;
+                    sV[row * LB + 16 * ct + i16] = acc[ct][e];
+                    dVt[row * V + 16 * ct] = acc[ct][e];
+                }
         }
         __syncthreads();
         if (j > 0) loadA(j - 1);
@@ -634,28 +669,35 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
         for (int i = 0; i < NST; ++i) {
             const int rt = w + 4 * i;
             if (rt < K / 16) {
-                f4 acc = {0.f, 0.f, 0.f, 0.f}, neg = acc;
+                f4 acc[NCT], neg[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acc[ct] = neg[ct] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int r = 16 * q + 4 * g4 + u;
-                        acc = mf(qgf[i][4 * q + u], sO[r * LB + i16], acc);
-                        neg = mf(wwf[i][4 * q + u], sV[r * LB + i16], neg);
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) {
+                            acc[ct] = mf(qgf[i][4 * q + u], sO[r * LB + 16 * ct + i16], acc[ct]);
+                            neg[ct] = mf(wwf[i][4 * q + u], sV[r * LB + 16 * ct + i16], neg[ct]);
+                        }
                     }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = 16 * rt + 4 * g4 + e;
-                    sD[m * LB + i16] = gcf[i][e] * sD[m * LB + i16] + acc[e] - neg[e];
-                }
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = 16 * rt + 4 * g4 + e, col = 16 * ct + i16;
+                        sD[m * LB + col] = gcf[i][e] * sD[m * LB + col] + acc[ct][e] - neg[ct][e];
+                    }
             }
         }
     }
     __syncthreads();
     if (a.d_initial_state)
-        for (int i = tid; i < K * SBV; i += NTH) {
-            const int r = i / SBV, c = i % SBV;
-            a.d_initial_state[(st + r) * V + j0 + c] = sD[r * LB + c];
+        for (int i = tid; i < K * DBV / 4; i += NTH) {
+            const int r = (4 * i) / DBV, c = (4 * i) % DBV;
+            st4(a.d_initial_state + (st + r) * V + j0 + c, *reinterpret_cast<const float4 *>(sD + r * LB + c));
         }
 }
 
@@ -703,25 +745,19 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
 
     float4 rh[KP], rdh[KP], ro, rvt, rdvt, rv;
     const int sr = tid >> 2, sg = 4 * (tid & 3);  // staging: row and first column of this thread's group
-    const int64_t tok = ((cp.t0 + sr) * H + h) * V + sg;
+    const int64_t tok = ((cp.t0 + crow(sr, cp.L)) * H + h) * V + sg;
     auto load = [&](int j0) {
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
-            const int idx = tid + NTH * i;
-            if (idx < K * 4) {
-                const int c = idx >> 2, g = 4 * (idx & 3);
-                rh[i] = ld4(hp + c * V + j0 + g);
-                rdh[i] = ld4(dhp + c * V + j0 + g);
-            }
+            const int idx = min(tid + NTH * i, K * 4 - 1);
+            const int c = idx >> 2, g = 4 * (idx & 3);
+            rh[i] = ld4(hp + c * V + j0 + g);
+            rdh[i] = ld4(dhp + c * V + j0 + g);
         }
         rvt = ld4(Vtp + sr * V + j0 + sg);
         rdvt = ld4(dVtp + sr * V + j0 + sg);
-        if (sr < cp.L) {
-            ro = ld4_any(a.d_out, a.dout_bf16, tok + j0);
-            rv = ld4(v + tok + j0);
-        } else {
-            ro = rv = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        ro = ld4_any(a.d_out, a.dout_bf16, tok + j0);  // masked past the chunk when stored
+        rv = ld4(v + tok + j0);
     };
     auto store = [&]() {
 #pragma unroll
@@ -733,11 +769,11 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
                 st4(sDH + c * LJ + g, rdh[i]);
             }
         }
-        const float sc = a.scale;
+        const float sc = sr < cp.L ? a.scale : 0.f;
         st4(sO + sr * LJ + sg, make_float4(sc * ro.x, sc * ro.y, sc * ro.z, sc * ro.w));
         st4(sVt + sr * LJ + sg, rvt);
         st4(sdVt + sr * LJ + sg, rdvt);
-        st4(sVr + sr * LJ + sg, rv);
+        st4(sVr + sr * LJ + sg, mask4(rv, sr < cp.L));
     };
 
     load(0);
@@ -808,7 +844,7 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
                 const int row = 16 * p + 4 * g4 + e;
                 if (row < cp.L)
                     st_out(a.dv, a.grad_bf16, ((cp.t0 + row) * H + h) * V + js * JS + i16, sB[row] * acc[e]);
-                dbacc[e] += row16_sum(sVr[row * LJ + i16] * acc[e]);
+                dbacc[e] += sVr[row * LJ + i16] * acc[e];  // summed over the row's lanes at the end
             }
         }
         {
@@ -860,6 +896,8 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) MA[(16 * p + 4 * g4 + e) * BC + s] = ma[i][e];
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dbacc[e] = row16_sum(dbacc[e]);
     if (i16 == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sRv[16 * w + 4 * g4 + e] = dbacc[e];
@@ -1041,16 +1079,15 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     {
         // all loads first (four elements per load), then the LDS stores
         constexpr int NK4 = (BC * KB / 4 + NTH - 1) / NTH, NM4 = BC * BC / 4 / NTH;
+        static_assert(BC * KB / 4 % NTH == 0, "whole float4 groups per thread");
         float4 rq[NK4], rk[NK4], rg[NK4], rm[NM4], rd[NM4];
-        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < NK4; ++i) {
             const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
-            const bool ok = idx < BC * KB / 4 && r < cp.L;
-            const int64_t gi = ((cp.t0 + r) * H + h) * K + c0 + c;
-            rq[i] = ok ? ld4(q + gi) : z4;
-            rk[i] = ok ? ld4(k + gi) : z4;
-            rg[i] = ok ? ld4(a.gate.gate + gi) : z4;
+            const int64_t gi = ((cp.t0 + crow(r, cp.L)) * H + h) * K + c0 + c;
+            rq[i] = ld4(q + gi);
+            rk[i] = ld4(k + gi);
+            rg[i] = ld4(a.gate.gate + gi);
         }
         const float *MA = a.w.MA + sh * BC * BC, *dAb = a.w.MT + sh * BC * BC;
 #pragma unroll
@@ -1061,11 +1098,9 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < NK4; ++i) {
             const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
-            if (idx < BC * KB / 4) {
-                st4(sQ + r * LKB + c, rq[i]);
-                st4(sK + r * LKB + c, rk[i]);
-                st4(sF2 + r * LKB + c, gate_log4(a.gate, rg[i], r < cp.L));
-            }
+            st4(sQ + r * LKB + c, mask4(rq[i], r < cp.L));
+            st4(sK + r * LKB + c, mask4(rk[i], r < cp.L));
+            st4(sF2 + r * LKB + c, gate_log4(a.gate, rg[i], r < cp.L));
         }
 #pragma unroll
         for (int i = 0; i < NM4; ++i) {
@@ -1214,13 +1249,12 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < NK4; ++i) {
             const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
-            al[i] = (!log_gate && idx < BC * KB / 4 && r < cp.L) ? ld4(a.gate.gate + ((cp.t0 + r) * H + h) * K + c0 + c)
-                                                               : make_float4(1.f, 1.f, 1.f, 1.f);
+            al[i] = ld4(a.gate.gate + ((cp.t0 + crow(r, cp.L)) * H + h) * K + c0 + c);
         }
 #pragma unroll
         for (int i = 0; i < NK4; ++i) {
             const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
-            if (idx < BC * KB / 4 && r < cp.L) {
+            if (r < cp.L) {
                 const float *x = sQ + r * LKB + c;
                 float4 o = make_float4(x[0], x[1], x[2], x[3]);
                 if (!log_gate) {
@@ -1254,11 +1288,12 @@ hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
         attr = true;
     }
     const int hs8 = (num_seqs * a.H + 7) / 8, sh8 = (int)(((int64_t)a.slots * a.H + 7) / 8);
-    const dim3 gp(a.slots, a.H), gs(8 * (V / SBV) * hs8), gk(8 * (K / KgLds<K>::KB) * sh8);
+    const dim3 gp(a.slots, a.H), gs(8 * (V / SBV) * hs8), gd(8 * (V / DstCfg<V>::DBV) * hs8);
+    const dim3 gk(8 * (K / KgLds<K>::KB) * sh8);
     constexpr size_t prep_bytes = PrepLds<K, V>::bytes;
     hipLaunchKernelGGL(kprep, gp, dim3(NTH), prep_bytes, stream, a);
     hipLaunchKernelGGL((bwd_states_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dstates_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dstates_kernel<K, V>), gd, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL(kvg, gp, dim3(NTH), VgLds<K>::bytes, stream, a);
     hipLaunchKernelGGL(kkg, gk, dim3(NTH), KgLds<K>::bytes, stream, a);
     return hipGetLastError();
