@@ -94,13 +94,20 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     # the exact instantiations the benchmark times (K = V = 128, bf16, chunk 32)
     chunk_pat = "PrecMixed, 128, 128, 32, 64, %d>" % (1 if zg else 0)
     flag = "Lb1E" if zg else "Lb0E"  # (these two appear under their mangled names)
-    for key, pats, src in (("k3_prefill_chunk_fwd_" + gate, ("chunk_fwd_kernel<", chunk_pat), "kda_chunk_kernel.h"),
-                           ("decode_recurrent_step_" + gate, ("recurrent_step_kernelIDF16bLi128ELi128E" + flag,),
-                            "kda_step.hip"),
-                           ("short_recurrent_fwd_" + gate, ("recurrent_fwd_kernelIDF16bLi128ELi128E" + flag,),
-                            "kda_recurrent.hip")):
-        fk = [v for k, v in fetch.items() if all(p_ in k for p_ in pats)]
-        wk = [v for k, v in write.items() if all(p_ in k for p_ in pats)]
+    entries = [("k3_prefill_chunk_fwd_" + gate, [("chunk_fwd_kernel<", chunk_pat)], "kda_chunk_kernel.h"),
+               ("decode_recurrent_step_" + gate, [("recurrent_step_kernelIDF16bLi128ELi128E" + flag,)], "kda_step.hip"),
+               ("short_recurrent_fwd_" + gate, [("recurrent_fwd_kernelIDF16bLi128ELi128E" + flag,)],
+                "kda_recurrent.hip")]
+    # the backward's kernels at the K3 shape (bf16 inputs); a name may appear mangled or not
+    for kern in ("prep", "vgrads", "kgrads"):
+        entries.append(("k3_bwd_" + kern, [("bwd_%s_kernelIDF16bLi128ELi128E" % kern,)], "kda_bwd.hip"))
+    for kern in ("states", "dstates"):
+        entries.append(("k3_bwd_" + kern, [("bwd_%s_kernel<128, 128>" % kern,), ("bwd_%s_kernelILi128ELi128E" % kern,)],
+                        "kda_bwd.hip"))
+    for key, alts, src in entries:
+        match = lambda k: any(all(p_ in k for p_ in pats) for pats in alts)
+        fk = [v for k, v in fetch.items() if match(k)]
+        wk = [v for k, v in write.items() if match(k)]
         if not fk or not wk:
             continue
         out[key] = {"fetch_kib": fk[0], "write_kib": wk[0],

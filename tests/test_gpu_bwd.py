@@ -215,7 +215,10 @@ def test_autograd_gate_into_scan():
     r = oracle.scan_bwd(f64(inp.q), f64(inp.k), f64(inp.v), a64, f64(inp.beta), f64(d_out),
                         f64(inp.initial_state), f64(d_fin))
     rz, rls, rb = oracle.bounded_decay_bwd(f64(inp.z), f64(inp.log_scale), r[3], g_min=-5.0, bias=f64(bias))
-    # dz is dalpha times a bounded factor; its terms cancel like d ln alpha's
+    # dz is dalpha times a bounded factor (|g_min sigmoid'| e^A <= 5/4 here, A = 0), so its
+    # terms cancel like d ln alpha's; the bias and log-scale gradients are sums of dz over
+    # the 96 rows (and x dz over the channels), whose cancellation multiplies that relative
+    # error again, hence 10x the element tolerance for those two sums
     floor = dg_scale(inp.q, r[0], inp.k, r[1]) * 5.0 / 4.0
     assert err_floor(z.grad, rz, floor, True) <= FP32_TOL
     assert err_fp32(b.grad, rb) <= 10 * FP32_TOL
