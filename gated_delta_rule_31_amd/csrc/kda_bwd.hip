@@ -157,7 +157,9 @@ __device__ __forceinline__ float row16_sum(float x) {
 template <int K, int V>
 struct PrepLds {
     static constexpr int LK = K + 4;                 // q, k, F1: 16-row fragment reads
-    static constexpr int LW = K + 16, LV = V + 16;   // beta K e^Gamma, beta v: 4-row fragment reads
+    // beta K e^Gamma, beta v: read as B fragments whose rows are 4 apart (k = 16 m + 4 (lane/16) + u),
+    // which a row stride of 4 mod 16 words keeps on distinct banks
+    static constexpr int LW = K + 4, LV = V + 4;
     static constexpr int R0 = 3 * BC * LK, RW = BC * LW + BC * LV;
     static constexpr int R = R0 > RW ? R0 : RW;
     static constexpr int TAB = (NP * NP + 3 * NP) * K;
@@ -383,23 +385,63 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // W = T (beta K e^Gamma), U = T (beta V); T is lower triangular
+    // W = T (beta K e^Gamma), U = T (beta V); T is lower triangular.  Wave w owns the
+    // column tiles w, w + 4, ... of W and of U over all four row tiles, so one read of a
+    // T fragment serves every column tile and one B read every row tile; the reduction
+    // runs in 16-row groups m with k = 16 m + 4 (lane / 16) + u, and group m only feeds
+    // row tiles p >= m.
+    constexpr int NWT = (K / 16 + 3) / 4, NUT = (V / 16 + 3) / 4;
     float *W = a.w.W + sh * BC * K, *U = a.w.U + sh * BC * V;
-    for (int t = w; t < NP * (K / 16); t += 4) {
-        const int p = t / (K / 16), ct = t % (K / 16);
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < 16 * (p + 1); s0 += 4)
-            acc = mf(sT[(16 * p + i16) * LDC + s0 + g4], sW[(s0 + g4) * LW + 16 * ct + i16], acc);
+    f4 aw[NP][NWT], au[NP][NUT];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) W[(16 * p + 4 * g4 + u) * K + 16 * ct + i16] = acc[u];
+    for (int pp = 0; pp < NP; ++pp) {
+#pragma unroll
+        for (int i = 0; i < NWT; ++i) aw[pp][i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NUT; ++i) au[pp][i] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int t = w; t < NP * (V / 16); t += 4) {
-        const int p = t / (V / 16), ct = t % (V / 16);
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < 16 * (p + 1); s0 += 4)
-            acc = mf(sT[(16 * p + i16) * LDC + s0 + g4], sBV[(s0 + g4) * LV + 16 * ct + i16], acc);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) U[(16 * p + 4 * g4 + u) * V + 16 * ct + i16] = acc[u];
+    for (int m = 0; m < NP; ++m) {
+        float4 ta[NP];
+#pragma unroll
+        for (int pp = m; pp < NP; ++pp)
+            ta[pp] = *reinterpret_cast<const float4 *>(sT + (16 * pp + i16) * LDC + 16 * m + 4 * g4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 16 * m + 4 * g4 + u;
+            float bw[NWT], bu[NUT];
+#pragma unroll
+            for (int i = 0; i < NWT; ++i) bw[i] = sW[r * LW + 16 * min(w + 4 * i, K / 16 - 1) + i16];
+#pragma unroll
+            for (int i = 0; i < NUT; ++i) bu[i] = sBV[r * LV + 16 * min(w + 4 * i, V / 16 - 1) + i16];
+#pragma unroll
+            for (int pp = m; pp < NP; ++pp) {
+                const float av = u == 0 ? ta[pp].x : u == 1 ? ta[pp].y : u == 2 ? ta[pp].z : ta[pp].w;
+#pragma unroll
+                for (int i = 0; i < NWT; ++i) aw[pp][i] = mf(av, bw[i], aw[pp][i]);
+#pragma unroll
+                for (int i = 0; i < NUT; ++i) au[pp][i] = mf(av, bu[i], au[pp][i]);
+            }
+        }
+    }
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+#pragma unroll
+        for (int i = 0; i < NWT; ++i) {
+            const int ct = w + 4 * i;
+            if (ct < K / 16) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) W[(16 * pp + 4 * g4 + u) * K + 16 * ct + i16] = aw[pp][i][u];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NUT; ++i) {
+            const int ct = w + 4 * i;
+            if (ct < V / 16) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) U[(16 * pp + 4 * g4 + u) * V + 16 * ct + i16] = au[pp][i][u];
+            }
+        }
     }
 }
 
@@ -837,8 +879,12 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
         {
             const int p = w;
             f4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s0 = 16 * p; s0 < BC; s0 += 4)
-                acc = mf(sT[(s0 + g4) * LDC + 16 * p + i16], sdVt[(s0 + g4) * LJ + i16], acc);
+            for (int m = p; m < NP; ++m)  // rows s = 16 m + 4 (lane/16) + u: 4 apart per lane group
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int sr = 16 * m + 4 * g4 + u;
+                    acc = mf(sT[sr * LDC + 16 * p + i16], sdVt[sr * LJ + i16], acc);
+                }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * p + 4 * g4 + e;
@@ -958,8 +1004,12 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
     for (int i = 0; i < NOWN; ++i) {
         const int t = w + 4 * i, p = t / KT, ct = t % KT, c = 16 * ct + i16;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 16 * p; s0 < BC; s0 += 4)
-            acc = mf(sT[(s0 + g4) * LDC + 16 * p + i16], sPW[(s0 + g4) * LK + c], acc);
+        for (int m = p; m < NP; ++m)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int sr = 16 * m + 4 * g4 + u;
+                acc = mf(sT[sr * LDC + 16 * p + i16], sPW[sr * LK + c], acc);
+            }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * p + 4 * g4 + e;
@@ -995,8 +1045,12 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
         const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
         if (qt <= p) {
-            for (int j0 = 16 * p; j0 < BC; j0 += 4)
-                acc = mf(sT[(j0 + g4) * LDC + 16 * p + i16], sM[(j0 + g4) * LDC + s], acc);
+            for (int m = p; m < NP; ++m)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int jr = 16 * m + 4 * g4 + u;
+                    acc = mf(sT[jr * LDC + 16 * p + i16], sM[jr * LDC + s], acc);
+                }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1159,12 +1213,15 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             const int r = 16 * rt + i16;
             for (int qs = 0; qs <= rt; ++qs) {
                 const float epq = sEpq[(rt * NP + qs) * KB + c];
+                // k = 16 qs + 4 (lane/16) + u: one 16-byte read of each A row, B rows 4 apart
+                const float4 ma = *reinterpret_cast<const float4 *>(sMA + r * LDC + 16 * qs + 4 * g4);
+                const float4 da = *reinterpret_cast<const float4 *>(sdA + r * LDC + 16 * qs + 4 * g4);
 #pragma unroll
-                for (int u = 0; u < 16; u += 4) {
-                    const int s = 16 * qs + u + g4;
+                for (int u = 0; u < 4; ++u) {
+                    const int s = 16 * qs + 4 * g4 + u;
                     const float b = sK[s * LKB + c] * sF2[s * LKB + c] * epq;
-                    xq = mf(sMA[r * LDC + s], b, xq);
-                    xk = mf(sdA[r * LDC + s], b, xk);
+                    xq = mf(u == 0 ? ma.x : u == 1 ? ma.y : u == 2 ? ma.z : ma.w, b, xq);
+                    xk = mf(u == 0 ? da.x : u == 1 ? da.y : u == 2 ? da.z : da.w, b, xk);
                 }
             }
         }
@@ -1175,8 +1232,8 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             f4 aq = {0.f, 0.f, 0.f, 0.f}, akk = aq;
             const int s = 16 * rt + i16;
 #pragma unroll
-            for (int u = 0; u < 16; u += 4) {
-                const int r = 16 * p + u + g4;
+            for (int u = 0; u < 4; ++u) {
+                const int r = 16 * p + 4 * g4 + u;  // rows 4 apart per lane group
                 const float f1 = sF1[r * LKB + c];
                 aq = mf(sMA[r * LDC + s], sQ[r * LKB + c] * f1, aq);
                 akk = mf(sdA[r * LDC + s], sK[r * LKB + c] * f1, akk);
