@@ -101,10 +101,6 @@ __device__ __forceinline__ float4 gate_log4(const GateIn &g, float4 x, bool ok) 
     return make_float4(logf(x.x), logf(x.y), logf(x.z), logf(x.w));
 }
 
-__device__ __forceinline__ float ld_any(const void *p, int is_bf16, int64_t i) {
-    return is_bf16 ? (float)static_cast<const __bf16 *>(p)[i] : static_cast<const float *>(p)[i];
-}
-
 // Workgroups go to the 8 XCDs round-robin by block index, and each XCD has its own L2.
 // Block b is mapped to (unit, sub) so that the nsub blocks of one unit, which read the same
 // per-chunk data, run on the same XCD one after another: the grid is 8 * nsub * ceil(units / 8)
@@ -124,8 +120,14 @@ __device__ __forceinline__ float4 ld4(const __bf16 *p) {
                        __builtin_bit_cast(float, (uint32_t)(uint16_t)x[2] << 16),
                        __builtin_bit_cast(float, (uint32_t)(uint16_t)x[3] << 16));
 }
+// Four elements of a tensor given in either format, without a branch: both loads are issued
+// (the unused one reads the tensor's first four elements, valid for any tensor of at least 16
+// bytes) and the wanted value is selected.  A branch per format would wait for the load
+// inside it, and with it for every load issued before.
 __device__ __forceinline__ float4 ld4_any(const void *p, int is_bf16, int64_t i) {
-    return is_bf16 ? ld4(static_cast<const __bf16 *>(p) + i) : ld4(static_cast<const float *>(p) + i);
+    const float4 f = ld4(static_cast<const float *>(p) + (is_bf16 ? 0 : i));
+    const float4 b = ld4(static_cast<const __bf16 *>(p) + (is_bf16 ? i : 0));
+    return is_bf16 ? b : f;
 }
 __device__ __forceinline__ void st4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
 
@@ -746,32 +748,32 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------
 // vgrads: contractions over the value dimension, one workgroup per (chunk slot, head).
 // The value axis is walked in 16-column slices staged in LDS (coalesced 16-byte loads; the
-// next slice is loaded into registers while the matrix cores work on the current one);
-// the C x K and C x C results accumulate in registers over the slices.
+// next slice is loaded into registers while the matrix cores work on the current one and
+// stored into the other of two slice buffers, so one barrier per slice suffices); the
+// C x K and C x C results accumulate in registers over the slices.
 template <int K>
 struct VgLds {
     static constexpr int JS = 16, LJ = JS + 4;  // slice width; row stride 20 keeps fragment reads conflict-free
     static constexpr int LK = K + 4;
-    static constexpr int SLICES = 2 * K * LJ + 4 * BC * LJ;           // the value slices
+    static constexpr int SL = 2 * K * LJ + 4 * BC * LJ;               // one slice buffer
+    static constexpr int SLICES = 2 * SL;                              // two slice buffers
     static constexpr int TAIL = 2 * BC * LK + 2 * BC * LDC;           // PW, beta Kg, MT / Y, dT (after the slices)
     static constexpr int R1 = SLICES > TAIL ? SLICES : TAIL;
-    static constexpr size_t bytes = sizeof(float) * (R1 + BC * LDC + BC + NTH + (1 + K / 16 + NP) * BC);
+    static constexpr size_t bytes = sizeof(float) * (R1 + 2 * BC * LDC + BC + NTH + (1 + K / 16 + NP) * BC);
 };
 
 
+// (LDS limits this kernel to one workgroup per CU: the register allocation may use a whole SIMD)
 template <typename TIn, int K, int V>
-__global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
-    constexpr int JS = VgLds<K>::JS, LJ = VgLds<K>::LJ, KT = K / 16, NOWN = NP * KT / 4;
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_vgrads_kernel(BwdArgs a) {
+    constexpr int JS = VgLds<K>::JS, LJ = VgLds<K>::LJ, KT = K / 16, NOWN = NP * KT / 4, SL = VgLds<K>::SL;
     constexpr int KP = (K * 4 + NTH - 1) / NTH;  // 4-column groups of the K x 16 slices per thread
     extern __shared__ __align__(16) unsigned char smem[];
-    float *sH = reinterpret_cast<float *>(smem);  // S      [K][16] slice
-    float *sDH = sH + K * LJ;                      // dS'    [K][16]
-    float *sO = sDH + K * LJ;                      // scale dO [C][16]
-    float *sVt = sO + BC * LJ;                     // Vt     [C][16]
-    float *sdVt = sVt + BC * LJ;                   // dVt    [C][16]
-    float *sVr = sdVt + BC * LJ;                   // v      [C][16]
+    // slice buffer b: S [K][16], dS' [K][16], scale dO [C][16], Vt [C][16], dVt [C][16], v [C][16]
+    constexpr int oDH = K * LJ, oO = 2 * K * LJ, oVt = oO + BC * LJ, odVt = oVt + BC * LJ, oVr = odVt + BC * LJ;
     float *sT = reinterpret_cast<float *>(smem) + VgLds<K>::R1;  // T [C][C]
-    float *sB = sT + BC * LDC;                     // beta
+    float *sTt = sT + BC * LDC;                    // T^T [C][C]: the A operand of the T^T products
+    float *sB = sTt + BC * LDC;                    // beta
     float *sRs = sB + BC;                          // partial rowsum(S dS')
     float *sRv = sRs + NTH;                        // [C] rowsum(V T^T dVt)
     float *sRk = sRv + BC;                         // [K/16][C] partial rowsum(K e^Gamma dBk)
@@ -779,7 +781,8 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
     const int n = blockIdx.x, h = blockIdx.y, H = a.H;
     const ChunkPos cp = slot_chunk(n, a.cu_seqlens, a.num_seqs, a.T);
     if (cp.L == 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int64_t sh = (int64_t)n * H + h;
     const TIn *v = static_cast<const TIn *>(a.v);
     const float *hp = a.w.h + sh * K * V, *dhp = a.w.dh + sh * K * V;
@@ -801,21 +804,21 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
         ro = ld4_any(a.d_out, a.dout_bf16, tok + j0);  // masked past the chunk when stored
         rv = ld4(v + tok + j0);
     };
-    auto store = [&]() {
+    auto store = [&](float *sb) {
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             const int idx = tid + NTH * i;
             if (idx < K * 4) {
                 const int c = idx >> 2, g = 4 * (idx & 3);
-                st4(sH + c * LJ + g, rh[i]);
-                st4(sDH + c * LJ + g, rdh[i]);
+                st4(sb + c * LJ + g, rh[i]);
+                st4(sb + oDH + c * LJ + g, rdh[i]);
             }
         }
         const float sc = sr < cp.L ? a.scale : 0.f;
-        st4(sO + sr * LJ + sg, make_float4(sc * ro.x, sc * ro.y, sc * ro.z, sc * ro.w));
-        st4(sVt + sr * LJ + sg, rvt);
-        st4(sdVt + sr * LJ + sg, rdvt);
-        st4(sVr + sr * LJ + sg, mask4(rv, sr < cp.L));
+        st4(sb + oO + sr * LJ + sg, make_float4(sc * ro.x, sc * ro.y, sc * ro.z, sc * ro.w));
+        st4(sb + oVt + sr * LJ + sg, rvt);
+        st4(sb + odVt + sr * LJ + sg, rdvt);
+        st4(sb + oVr + sr * LJ + sg, mask4(rv, sr < cp.L));
     };
 
     load(0);
@@ -825,12 +828,16 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
         for (int i = 0; i < BC * BC / 4 / NTH; ++i) x[i] = ld4(Tm + 4 * (tid + NTH * i));
 #pragma unroll
         for (int i = 0; i < BC * BC / 4 / NTH; ++i) {
-            const int e = 4 * (tid + NTH * i);
-            st4(sT + (e / BC) * LDC + e % BC, x[i]);
+            const int e = 4 * (tid + NTH * i), r = e / BC, c = e % BC;
+            st4(sT + r * LDC + c, x[i]);
+            sTt[c * LDC + r] = x[i].x;
+            sTt[(c + 1) * LDC + r] = x[i].y;
+            sTt[(c + 2) * LDC + r] = x[i].z;
+            sTt[(c + 3) * LDC + r] = x[i].w;
         }
     }
     if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
-    store();
+    store(reinterpret_cast<float *>(smem));
     __syncthreads();
 
     f4 ps[NOWN], pw[NOWN], pd[NOWN], ma[4], mt[4];
@@ -842,8 +849,11 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
     constexpr int PARTS = NTH / K, CW = JS / PARTS;  // rowsum(S dS'): threads per key row, columns each
 
     for (int js = 0; js < V / JS; ++js) {
+        float *sb = reinterpret_cast<float *>(smem) + (js & 1) * SL;
+        const float *sH = sb, *sDH = sb + oDH, *sO = sb + oO, *sVt = sb + oVt, *sdVt = sb + odVt, *sVr = sb + oVr;
         const bool more = js + 1 < V / JS;
         if (more) load((js + 1) * JS);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products they overlap
         // dO S^T, dVt S^T, Vt dS'^T on this wave's C x K tiles.  The slice's 16-wide
         // reduction is split as k = 4*(lane/16) + s on both operands, so one 16-byte LDS
         // read per operand feeds four matrix-core steps.
@@ -875,22 +885,39 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
             ma[i] = mf(ao.z, bvt.z, ma[i]); mt[i] = mf(adv.z, bv.z, mt[i]);
             ma[i] = mf(ao.w, bvt.w, ma[i]); mt[i] = mf(adv.w, bv.w, mt[i]);
         }
-        // T^T dVt on row tile p = w of this slice: dv = beta T^T dVt, rowsum(V T^T dVt) for dbeta
+        // T^T dVt on row tile p = w of this slice: dv = beta T^T dVt, rowsum(V T^T dVt) for dbeta.
+        // k = s = 16 m + 4 (lane/16) + u over every m: the blocks m < p of T^T are zero, and the
+        // wave with p = 0, which needs them all, sets the pace anyway.  All operands are read
+        // before the first product.
         {
             const int p = w;
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int m = p; m < NP; ++m)  // rows s = 16 m + 4 (lane/16) + u: 4 apart per lane group
+            float4 at[NP];
+            float bt[NP][4], bs[4], vr[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int sr = 16 * m + 4 * g4 + u;
-                    acc = mf(sT[sr * LDC + 16 * p + i16], sdVt[sr * LJ + i16], acc);
-                }
+            for (int m = 0; m < NP; ++m) {
+                at[m] = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) bt[m][u] = sdVt[(16 * m + 4 * g4 + u) * LJ + i16];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bs[e] = sB[16 * p + 4 * g4 + e];
+                vr[e] = sVr[(16 * p + 4 * g4 + e) * LJ + i16];
+            }
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                acc = mf(at[m].x, bt[m][0], acc);
+                acc = mf(at[m].y, bt[m][1], acc);
+                acc = mf(at[m].z, bt[m][2], acc);
+                acc = mf(at[m].w, bt[m][3], acc);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * p + 4 * g4 + e;
                 if (row < cp.L)
-                    st_out(a.dv, a.grad_bf16, ((cp.t0 + row) * H + h) * V + js * JS + i16, sB[row] * acc[e]);
-                dbacc[e] += sVr[row * LJ + i16] * acc[e];  // summed over the row's lanes at the end
+                    st_out(a.dv, a.grad_bf16, ((cp.t0 + row) * H + h) * V + js * JS + i16, bs[e] * acc[e]);
+                dbacc[e] += vr[e] * acc[e];  // summed over the row's lanes at the end
             }
         }
         {
@@ -898,11 +925,8 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < CW; ++j) rsacc += sH[c * LJ + part * CW + j] * sDH[c * LJ + part * CW + j];
         }
+        if (more) store(reinterpret_cast<float *>(smem) + ((js + 1) & 1) * SL);
         __syncthreads();
-        if (more) {
-            store();
-            __syncthreads();
-        }
     }
 
     // the slices are done: their LDS now holds PW (-dW), beta K e^Gamma, MT and the C x C work
@@ -998,17 +1022,22 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
             sY[row * LDC + s] = sM[row * LDC + s] - sB[s] * acc[e];
         }
     }
-    // dBk = T^T dW = -T^T PW on this wave's C x K tiles; rowsum(K e^Gamma dBk) for dbeta
+    // dBk = T^T dW = -T^T PW on this wave's C x K tiles; rowsum(K e^Gamma dBk) for dbeta.
+    // With K/16 a multiple of 4 the row tile of tile w + 4 i does not depend on the wave.
     float *dBk = a.w.PW + sh * BC * K;
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
-        const int t = w + 4 * i, p = t / KT, ct = t % KT, c = 16 * ct + i16;
+        const int t = w + 4 * i, p = KT % 4 == 0 ? (4 * i) / KT : t / KT, ct = t % KT, c = 16 * ct + i16;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int m = p; m < NP; ++m)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int sr = 16 * m + 4 * g4 + u;
-                acc = mf(sT[sr * LDC + 16 * p + i16], sPW[sr * LK + c], acc);
+        for (int m = 0; m < NP; ++m)
+            if (m >= p) {
+                const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
+                const float *br = sPW + (16 * m + 4 * g4) * LK + c;
+                acc = mf(at.x, br[0], acc);
+                acc = mf(at.y, br[LK], acc);
+                acc = mf(at.z, br[2 * LK], acc);
+                acc = mf(at.w, br[3 * LK], acc);
             }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1040,17 +1069,21 @@ __global__ __launch_bounds__(NTH) void bwd_vgrads_kernel(BwdArgs a) {
     __syncthreads();
     // dA = -strict_tril(T^T Y); rowsum(dA Abar) for dbeta; beta dA is what the key space needs
     float *dAb = a.w.MT + sh * BC * BC;
+    static_assert(NP == 4, "the C x C tiles w + 4 i of a wave are row tile i, column tile w");
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
+        const int p = i, qt = w, s = 16 * qt + i16;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
         if (qt <= p) {
-            for (int m = p; m < NP; ++m)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int jr = 16 * m + 4 * g4 + u;
-                    acc = mf(sT[jr * LDC + 16 * p + i16], sM[jr * LDC + s], acc);
-                }
+            for (int m = p; m < NP; ++m) {
+                const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
+                const float *br = sM + (16 * m + 4 * g4) * LDC + s;
+                acc = mf(at.x, br[0], acc);
+                acc = mf(at.y, br[LDC], acc);
+                acc = mf(at.z, br[2 * LDC], acc);
+                acc = mf(at.w, br[3 * LDC], acc);
+            }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
