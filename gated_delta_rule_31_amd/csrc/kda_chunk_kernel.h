@@ -25,19 +25,20 @@
 // All factors are products of retention factors (in-tile prefix and suffix
 // products), so no per-element exponential is needed.
 //
-// Work decomposition: one workgroup of 8 waves per (sequence, head, block of BV
-// value columns); value columns evolve independently, so the split is exact.
+// Work decomposition: one workgroup of 12 waves (three per SIMD) per (sequence, head,
+// block of BV value columns); value columns evolve independently, so the split is exact.
+// Each chunk period has two workgroup barriers, B1 and B2.
 //  * 4 state waves own the float32 state S[K x BV] in registers (one 16-column tile
-//    each) and run the serial part for chunk n: Y = beta V - Bw S, Vt = T Y,
-//    O = Qt S + A_qk Vt, S = gamma_C S + Kt^T Vt.  Their matrix-core operands come
-//    straight from the accumulators of the previous product (the k order of each
-//    product is permuted to match the accumulator layout), so the state never
-//    round-trips through LDS.  In the rest of the chunk period they compute chunk
-//    n+1's A-matrix tiles and T from the operands the prep waves staged.
-//  * 4 prep waves turn chunk n+1's raw inputs into the staged A-matrix operands and
-//    the package (Qt, -Bw, Kt, beta V, gamma_C) in the other half of a
-//    double-buffered LDS area, and prefetch chunk n+2's raw inputs into registers.
-//    Three workgroup barriers per chunk.
+//    each).  Before B1 they compute the A-matrix tiles and T's diagonal blocks of the
+//    chunk staged in the previous period; after it, T's off-diagonal blocks (every
+//    state wave computes all of them, so no further barrier is needed) and the serial
+//    part for that chunk: Y = beta V - Bw S, Vt = T Y, O = Qt S + A_qk Vt,
+//    S = gamma_C S + Kt^T Vt.  Their matrix-core operands come straight from the
+//    accumulators of the previous product (the k order of each product is permuted to
+//    match the accumulator layout), so the state never round-trips through LDS.
+//  * 8 prep waves form the next chunk's decay products before B1; after it they stage
+//    the A-matrix operands, send the prefetch of the chunk after, and store the package
+//    (Qt, -Bw, Kt, beta V, gamma_C) in the other half of a double-buffered LDS area.
 //
 // Precision (bf16 inputs): the A-matrix operands carry factors up to e^80 and use
 // bf16; A_qk, which carries each token's own value to its output, is formed from
@@ -53,9 +54,10 @@ namespace kda {
 
 namespace {
 
-constexpr int NT = 512;   // threads per workgroup
-constexpr int NSW = 4;    // state waves: 0..3
-constexpr int NPT = 256;  // prep threads: waves 4..7
+constexpr int NSW = 4;           // state waves: 0..3
+constexpr int NPW = 8;           // prep waves: 4..11
+constexpr int NPT = 64 * NPW;    // prep threads
+constexpr int NT = 64 * NSW + NPT;  // threads per workgroup (three waves per SIMD)
 
 constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
 
@@ -98,9 +100,10 @@ struct Layout {
     static constexpr size_t oAkk = oSt + al16((size_t)NST * sizeof(TA) * (P::kSplit ? 2 : 1));
     static constexpr size_t oTf = oAkk + al16((size_t)C * LCF * 4);
     // per-row partial sums of q^2 and k^2 from each wave that holds part of a tile's row
-    static constexpr int NPART = K / 2 > 32 ? K / 64 : 1;
-    static constexpr size_t oNrm = oTf + al16((size_t)C * LCF * 4);  // [NP][2][16][NPART]
-    static constexpr size_t oTP = oNrm + al16((size_t)NP * 2 * 16 * NPART * 4);
+    static constexpr int NPART = K / 2 > 16 ? K / 32 : 1;
+    static constexpr int NNRM = NP * 2 * 16 * NPART;                  // floats per buffer
+    static constexpr size_t oNrm = oTf + al16((size_t)C * LCF * 4);  // [2][NP][2][16][NPART], by chunk parity
+    static constexpr size_t oTP = oNrm + al16((size_t)2 * NNRM * 4);
     static constexpr size_t oBt = oTP + al16((size_t)NP * K * 4);
     static constexpr size_t oPkg = oBt + al16((size_t)C * 4);
     // package (two copies)
@@ -353,8 +356,8 @@ __device__ __forceinline__ f4 unit_lower_inverse16(const f4 a, int lane) {
 // HALF of their 2*HALF partial sums, the others the lower half, and each adds what the
 // partner (lane ^ M) sends of the same half.  Compile-time sizes keep every array index
 // static (a select between two indices would become a dynamic index into the array).
-template <int HALF, bool ON, int M>
-__device__ __forceinline__ void halve_sums(float (&x)[16], int lane, int &base) {
+template <int HALF, bool ON, int M, int N>
+__device__ __forceinline__ void halve_sums(float (&x)[N], int lane, int &base) {
     if constexpr (ON) {
         const bool up = (lane & M) != 0;
 #pragma unroll
@@ -376,7 +379,7 @@ __device__ __forceinline__ void halve_sums(float (&x)[16], int lane, int &base) 
 // reciprocal row norms (A_kk[i,j] by 1/(|k_i||k_j|), A_qk[i,j] by 1/(|q_i||k_j|)),
 // which the prep waves left in LDS as per-wave partial sums of squares.
 template <class P, int K, int V, int C, int BV, bool NORM>
-__device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char *pk, int w, int lane) {
+__device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char *pk, int nb, int w, int lane) {
     using L = Layout<P, K, V, C, BV>;
     using TA = typename P::TA;
     using TM = typename P::TM;
@@ -388,7 +391,7 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
     float *Tf = reinterpret_cast<float *>(smem + L::oTf);
     TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
     TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
-    const float *Nrm = reinterpret_cast<const float *>(smem + L::oNrm);
+    const float *Nrm = reinterpret_cast<const float *>(smem + L::oNrm) + nb * L::NNRM;
     // 1 / max(|x_r|, 1e-6) of chunk row r, for x = q (qk = 0) or k (qk = 1)
     auto inv_norm = [&](int qk, int r) -> float {
         float n = 0.f;
@@ -536,10 +539,17 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
         float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
         float *Tf = reinterpret_cast<float *>(smem + L::oTf);
         for (int it = 0; it <= nchunks; ++it) {
-            if (NP > 1 && wave == 0 && it >= 1) {
+            // the A-matrix tiles and T's diagonal blocks of the chunk staged in the previous
+            // period, whose package the serial part consumes after the next barrier
+            if (it >= 1) a_matrix_work<P, K, V, C, BV, NORM>(smem, pkg((it - 1) & 1), (it - 1) & 1, wave, lane);
+            lds_barrier();  // B1: chunk it-1's A-matrix tiles are done; chunk it's decay products are in LDS
+            if (NP > 1 && it >= 1) {
                 // T's off-diagonal blocks of the chunk about to be consumed, one block
                 // distance at a time on fp32 matrix cores:
                 //   M = sum_{r=q}^{p-1} A_pr T_rq,   T_pq = -T_pp M
+                // Every state wave computes all of them: it reads back only what it wrote
+                // itself, and the other waves write the same values to the same places, so
+                // no barrier is needed before the serial part uses them.
                 TM *Tm = reinterpret_cast<TM *>(pkg((it - 1) & 1) + L::pTm);
                 for (int d = 1; d < NP; ++d) {
                     for (int qb = 0; qb + d < NP; ++qb) {
@@ -567,7 +577,6 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     lds_fence();
                 }
             }
-            lds_barrier();  // B1: prep waves have produced their tile products
             f4 Vt[L::MJ][NP];
             BFrag<TM, NP> Vh[L::MJ];
             const int cn = it - 1;  // chunk handled by the state waves in this iteration
@@ -640,9 +649,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     Sh[mj].set(S[mj]);
                 }
             }
-            lds_barrier();  // B2: prep waves have written the A-matrix operands
-            if (it < nchunks) a_matrix_work<P, K, V, C, BV, NORM>(smem, pkg(it & 1), wave, lane);
-            lds_barrier();  // B3: the next package is complete
+            lds_barrier();  // B2: chunk it is staged and its package operands are stored
         }
         if (a.final_state) {
             float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
@@ -668,7 +675,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
 
     // ====================================== prep waves =======================================
     const int tp = tid - NSW * 64;  // 0 .. NPT-1
-    const int pw = wave - NSW;      // prep wave 0..3
+    const int pw = wave - NSW;      // prep wave 0..NPW-1
     TA *Lk = reinterpret_cast<TA *>(smem + L::oLk);         // [C][LKA]
     TA *St = reinterpret_cast<TA *>(smem + L::oSt);         // Lq, Rd, Ro, X (+ low parts)
     float *TPv = reinterpret_cast<float *>(smem + L::oTP);  // [NP][K] tile decay products
@@ -691,23 +698,25 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     }
 
     // Prep mapping: a "combo" is a (channel pair, 16-row tile); each combo is handled by
-    // two lanes of one wave, lane l (rows 0..7 of the tile) and lane l ^ 32 (rows 8..15),
-    // so in-tile prefix and suffix decay products need one exchange between them.
+    // four lanes of one wave, lanes l, l + 16, l + 32 and l + 48 (l < 16) taking rows
+    // 0..3, 4..7, 8..11 and 12..15 of the tile, so in-tile prefix and suffix decay
+    // products need one exchange among the four.
     constexpr int NCP = K / 2;                   // channel pairs
     constexpr int NCOMBO = NCP * NP;
-    constexpr int CPT = (NCOMBO + 127) / 128;    // combos per lane pair (4 prep waves x 32)
-    const int hf = lane >> 5;                    // which half of the tile
-    auto combo_of = [&](int u) { return 128 * u + 32 * pw + (lane & 31); };
+    constexpr int CPR = 16 * NPW;                // combos per round (16 lane quadruples per wave)
+    constexpr int CPT = (NCOMBO + CPR - 1) / CPR;  // combos per lane quadruple
+    const int qd = lane >> 4;                    // which quarter of the tile
+    auto combo_of = [&](int u) { return CPR * u + 16 * pw + (lane & 15); };
 
-    // Raw inputs of one chunk: for each combo, 8 rows x 2 channels of the gate, q and k;
+    // Raw inputs of one chunk: for each combo, 4 rows x 2 channels of the gate, q and k;
     // beta of row tp; this thread's share of the value block.  The loads are
     // unconditional (rows past the sequence end read its last row) and nothing is
     // computed from them until they are used in the next iteration, so they stay in
     // flight while the current chunk is processed; the padding rows are masked at use.
     using RawIn = typename std::conditional<std::is_same<TIn, float>::value, float, unsigned short>::type;
     using RawPair = typename std::conditional<std::is_same<TIn, float>::value, float2, uint32_t>::type;
-    float2 ral[CPT][8];
-    RawPair rq[CPT][8], rk[CPT][8];
+    float2 ral[CPT][4];
+    RawPair rq[CPT][4], rk[CPT][4];
     float rbeta = 0.f;
     constexpr int NVE = (BV * C / 2 + NPT - 1) / NPT;  // (column, token pair) items per prep thread
     RawIn rv[NVE][2];
@@ -743,10 +752,10 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
             const int cm = combo_of(u) < NCOMBO ? combo_of(u) : 0;
             const int c0 = 2 * (cm % NCP);
             int p = cm / NCP;
-            if constexpr (NCP % 32 == 0) p = __builtin_amdgcn_readfirstlane(p);  // one tile per wave
+            if constexpr (NCP % 16 == 0) p = __builtin_amdgcn_readfirstlane(p);  // one tile per wave
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = 16 * p + 8 * hf + i;
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * p + 4 * qd + i;
                 const uint32_t o = (uint32_t)((r < last ? r : last) * rs + c0);
                 if constexpr (!ZG) {
                     ral[u][i] = *reinterpret_cast<const float2 *>(gb + o);
@@ -784,8 +793,8 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     };
     if (nchunks > 0) load_raw(0);
 
-    // per combo: decay factor entering this half from the other one (prefix: product of
-    // rows 0..7 for the second half; suffix: product of rows 8..15 for the first half)
+    // per combo: decay factors entering this quarter from the others (prefix: product of the
+    // tile's rows before it; suffix: product of the rows after it)
     float2 pin[CPT], sin[CPT];
     for (int it = 0; it <= nchunks; ++it) {
         const bool work = it < nchunks;
@@ -798,7 +807,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 const int p = cm / NCP;
                 float2 run = {1.f, 1.f};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < 4; ++i) {
                     float2 al = ral[u][i];
                     if constexpr (!ZG) {
                         if (glog) {
@@ -816,20 +825,63 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                         al.x = fast_bounded_alpha(z0 + zbias[u].x, gs2, gl2);
                         al.y = fast_bounded_alpha(z1 + zbias[u].y, gs2, gl2);
                     }
-                    if (16 * p + 8 * hf + i >= n_it) al = float2{1.f, 1.f};
+                    if (16 * p + 4 * qd + i >= n_it) al = float2{1.f, 1.f};
                     ral[u][i] = al;
                     run.x *= al.x;
                     run.y *= al.y;
                 }
-                // the other half's product
-                float2 oth;
-                oth.x = __shfl_xor(run.x, 32);
-                oth.y = __shfl_xor(run.y, 32);
-                pin[u] = hf ? oth : float2{1.f, 1.f};
-                sin[u] = hf ? float2{1.f, 1.f} : oth;
-                if (hf == 0 && cm < NCOMBO) {
+                // the four quarters' products: lane quarter qd ^ d sends its own
+                float2 xq[4];
+                xq[0] = run;
+                xq[1] = float2{__shfl_xor(run.x, 16), __shfl_xor(run.y, 16)};
+                xq[2] = float2{__shfl_xor(run.x, 32), __shfl_xor(run.y, 32)};
+                xq[3] = float2{__shfl_xor(run.x, 48), __shfl_xor(run.y, 48)};
+                float2 qp[4];  // product of quarter j
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d = qd ^ j;
+                    qp[j] = d == 0 ? xq[0] : d == 1 ? xq[1] : d == 2 ? xq[2] : xq[3];
+                }
+                float2 pi = {1.f, 1.f}, si = {1.f, 1.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (j < qd) { pi.x *= qp[j].x; pi.y *= qp[j].y; }
+                    if (j > qd) { si.x *= qp[j].x; si.y *= qp[j].y; }
+                }
+                pin[u] = pi;
+                sin[u] = si;
+                if (qd == 0 && cm < NCOMBO) {
                     const int c0 = 2 * (cm % NCP);
-                    *reinterpret_cast<float2 *>(TPv + p * K + c0) = float2{run.x * oth.x, run.y * oth.y};
+                    *reinterpret_cast<float2 *>(TPv + p * K + c0) =
+                        float2{(qp[0].x * qp[1].x) * (qp[2].x * qp[3].x), (qp[0].y * qp[1].y) * (qp[2].y * qp[3].y)};
+                }
+                if constexpr (NORM) {
+                    // this thread's share of the row sums of q^2 (0..3) and k^2 (4..7)
+                    float x2[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float q0, q1, k0, k1;
+                        pair_f32(rq[u][i], q0, q1);
+                        pair_f32(rk[u][i], k0, k1);
+                        const bool ok = 16 * p + 4 * qd + i < n_it;
+                        x2[i] = ok ? q0 * q0 + q1 * q1 : 0.f;
+                        x2[4 + i] = ok ? k0 * k0 + k1 * k1 : 0.f;
+                    }
+                    // sum the row shares over the NG lanes of this tile in this quarter-wave
+                    // by recursive halving (each exchange keeps half of the remaining sums
+                    // and adds the partner's half: 8 sums over 16 lanes in 7 exchanges); the
+                    // waves' partial sums meet in LDS
+                    constexpr int NG = NCP < 16 ? NCP : 16;
+                    static_assert(NG == 8 || NG == 16, "8 or 16 lanes share a tile row");
+                    int base = 0;  // index of x2[0] among the 8 sums
+                    halve_sums<4, true, NG / 2>(x2, lane, base);
+                    halve_sums<2, true, NG / 4>(x2, lane, base);
+                    halve_sums<1, true, NG / 8>(x2, lane, base);
+                    if constexpr (NG == 16) x2[0] += __shfl_xor(x2[0], 1);  // one sum on two lanes
+                    if (cm < NCOMBO && (NG != 16 || (lane & 1) == 0)) {
+                        const int part = (cm % NCP) / 16;  // which wave's share of the row
+                        Nrm[(it & 1) * L::NNRM + ((p * 2 + (base >> 2)) * 16 + 4 * qd + (base & 3)) * L::NPART + part] = x2[0];
+                    }
                 }
             }
             if (tp < C) {
@@ -841,7 +893,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
         // ---- phase 1b: A-matrix operand staging of chunk `it` ---------------------------
         // The package operands are computed here too but kept in registers and stored in
         // phase 2, after the prefetch has gone out.
-        float2 kq[CPT][8], kk[CPT][8], kr[CPT][8];  // q gamma/R, beta k gamma/R, k E/gamma per row
+        float2 kq[CPT][4], kk[CPT][4], kr[CPT][4];  // q gamma/R, beta k gamma/R, k E/gamma per row
         float2 keR[CPT], keCE[CPT];                 // R_p and E_C / E_p of the combo's tile
         float2 bvv[NVE];                            // beta v pairs of this thread's value items
         if (work) {
@@ -864,7 +916,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     eAll.x *= tpr[pp].x;
                     eAll.y *= tpr[pp].y;
                 }
-                if (p == 0 && hf == 0) *reinterpret_cast<float2 *>(eGC + c0) = eAll;
+                if (p == 0 && qd == 0) *reinterpret_cast<float2 *>(eGC + c0) = eAll;
                 const float2 rT = {1.f / own.x, 1.f / own.y};
                 // extra right-operand versions for tiles (pp, p) with pp >= p + 2
                 float2 xf[NP];
@@ -876,17 +928,16 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                         if (r2 > p && r2 < pp) { f.x *= tpr[r2].x; f.y *= tpr[r2].y; }
                     xf[pp] = f;
                 }
-                float bet[8];
-#pragma unroll
-                for (int i = 0; i < 8; i += 4) {
-                    const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + 8 * hf + i);
-                    bet[i] = b4.x; bet[i + 1] = b4.y; bet[i + 2] = b4.z; bet[i + 3] = b4.w;
+                float bet[4];
+                {
+                    const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + 4 * qd);
+                    bet[0] = b4.x; bet[1] = b4.y; bet[2] = b4.z; bet[3] = b4.w;
                 }
-                float2 suf[8];  // E_p / gamma_i: product of the tile's later factors
+                float2 suf[4];  // E_p / gamma_i: product of the tile's later factors
                 {
                     float2 run = sin[u];
 #pragma unroll
-                    for (int i = 7; i >= 0; --i) {
+                    for (int i = 3; i >= 0; --i) {
                         suf[i] = run;
                         run.x *= ral[u][i].x;
                         run.y *= ral[u][i].y;
@@ -895,10 +946,9 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 float2 pre = pin[u];  // gamma_i / R_p
                 keR[u] = eR;
                 keCE[u] = eCE;
-                float x2[16];  // with NORM: this thread's share of the row sums of q^2 (0..7), k^2
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = 16 * p + 8 * hf + i;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * p + 4 * qd + i;
                     pre.x *= ral[u][i].x;
                     pre.y *= ral[u][i].y;
                     const bool ok = r < n_it;
@@ -906,10 +956,6 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     pair_f32(rq[u][i], q0, q1);
                     pair_f32(rk[u][i], k0, k1);
                     if (!ok) q0 = q1 = k0 = k1 = 0.f;
-                    if constexpr (NORM) {
-                        x2[i] = q0 * q0 + q1 * q1;
-                        x2[8 + i] = k0 * k0 + k1 * k1;
-                    }
                     const float2 lq = {q0 * pre.x, q1 * pre.y};
                     const float2 lk = {bet[i] * k0 * pre.x, bet[i] * k1 * pre.y};
                     const float2 ro = {k0 * suf[i].x, k1 * suf[i].y};  // k E_p / gamma <= |k|
@@ -925,35 +971,12 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                             for (int qq = 0; qq + 2 <= pp; ++qq, ++xi)
                                 if (qq == p)
-                                    st2_stage<P>(St + L::sX + (xi * 16 + 8 * hf + i) * L::LKS + c0, L::NST,
+                                    st2_stage<P>(St + L::sX + (xi * 16 + 4 * qd + i) * L::LKS + c0, L::NST,
                                                  ro.x * xf[pp].x, ro.y * xf[pp].y);
                     }
                     kq[u][i] = lq;
                     kk[u][i] = lk;
                     kr[u][i] = ro;
-                }
-                if constexpr (NORM) {
-                    // sum the row shares over the NG lanes of this tile in this half-wave by
-                    // recursive halving (each exchange keeps half of the remaining sums and
-                    // adds the partner's half: 16 sums over 32 lanes in 16 exchanges); the
-                    // waves' partial sums meet in LDS
-                    constexpr int NG = NCP < 32 ? NCP : 32;
-                    constexpr int NH = NG >= 16 ? 4 : NG == 8 ? 3 : NG == 4 ? 2 : 1;
-                    int base = 0;  // index of x2[0] among the 16 sums
-                    halve_sums<8, (NH > 0), NG / 2>(x2, lane, base);
-                    halve_sums<4, (NH > 1), NG / 4>(x2, lane, base);
-                    halve_sums<2, (NH > 2), NG / 8>(x2, lane, base);
-                    halve_sums<1, (NH > 3), NG / 16>(x2, lane, base);
-                    constexpr int REM = 16 >> NH;
-                    if constexpr (NG == 32) x2[0] += __shfl_xor(x2[0], 1);  // one sum on two lanes
-                    if (NG != 32 || (lane & 1) == 0) {
-                        const int part = (cm % NCP) / 32;  // which wave's share of the row
-#pragma unroll
-                        for (int r2 = 0; r2 < REM; ++r2) {
-                            const int id = base + r2;
-                            Nrm[((p * 2 + (id >> 3)) * 16 + 8 * hf + (id & 7)) * L::NPART + part] = x2[r2];
-                        }
-                    }
                 }
             }
 #pragma unroll
@@ -965,9 +988,8 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 }
             }
         }
-        lds_barrier();  // B2
-        // ---- phase 2: the state waves compute the A-matrix tiles; the prep waves send the
-        // prefetch of the next chunk, then store the package operands of this one
+        // ---- phase 2: send the prefetch of the next chunk, then store the package operands
+        // of this one (the state waves run the serial part of the previous chunk meanwhile)
         if (work) {
             if (it + 1 < nchunks) load_raw(it + 1);  // consumed next iteration
             unsigned char *pk = pkg(it & 1);
@@ -981,25 +1003,25 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 if (cm >= NCOMBO) continue;
                 const int c0 = 2 * (cm % NCP), p = cm / NCP;
                 const float2 eR = keR[u], eCE = keCE[u];
-                float iq[8], ik[8];  // reciprocal row norms (1 without normalisation)
+                float iq[4], ik[4];  // reciprocal row norms (1 without normalisation)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < 4; ++i) {
                     iq[i] = 1.f;
                     ik[i] = 1.f;
                     if constexpr (NORM) {
                         float nq = 0.f, nk = 0.f;
 #pragma unroll
                         for (int pt = 0; pt < L::NPART; ++pt) {
-                            nq += Nrm[((p * 2 + 0) * 16 + 8 * hf + i) * L::NPART + pt];
-                            nk += Nrm[((p * 2 + 1) * 16 + 8 * hf + i) * L::NPART + pt];
+                            nq += Nrm[(it & 1) * L::NNRM + ((p * 2 + 0) * 16 + 4 * qd + i) * L::NPART + pt];
+                            nk += Nrm[(it & 1) * L::NNRM + ((p * 2 + 1) * 16 + 4 * qd + i) * L::NPART + pt];
                         }
                         iq[i] = __builtin_amdgcn_rsqf(fmaxf(nq, 1e-12f));
                         ik[i] = __builtin_amdgcn_rsqf(fmaxf(nk, 1e-12f));
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = 16 * p + 8 * hf + i;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * p + 4 * qd + i;
                     st2<TM>(Qt + r * L::LKM + c0, kq[u][i].x * eR.x * iq[i], kq[u][i].y * eR.y * iq[i]);
                     st2<TM>(Bw + r * L::LKM + c0, -kk[u][i].x * eR.x * ik[i], -kk[u][i].y * eR.y * ik[i]);
                     if (i & 1) {
@@ -1019,7 +1041,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 }
             }
         }
-        lds_barrier();  // B3
+        lds_barrier();  // B2
     }
 }
 
