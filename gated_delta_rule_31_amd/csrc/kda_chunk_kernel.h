@@ -231,6 +231,13 @@ __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)
 // chunk does); __syncthreads() would drain them at every barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Load a T at a 32-bit byte offset from a workgroup-uniform base: the address is formed by
+// the load itself (scalar base + vector offset), with no 64-bit address arithmetic.
+template <typename T>
+__device__ __forceinline__ T ld_at(const void *base, uint32_t byte_off) {
+    return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
 // acc += A[16 x kdim] * B[kdim x 16] for the A-matrix tiles: A rows and B^T rows staged
 // in the A-operand type (k contiguous).  With SPLIT both operands also have low parts
 // (x - hi) `lo` elements further on, and the product is hi*hi + hi*lo + lo*hi (about 16
@@ -621,10 +628,18 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                         mma_bfrag<NKT_K>(o, Qt + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
                         mma_bfrag<NP>(o, Aqk + (16 * p + (lane & 15)) * L::LCM, Vh[mj], p + 1, lane);
                         const int j = vb * BV + jt * 16 + (lane & 15);
+                        // output rows of the chunk from a uniform base, 32-bit element offsets
+                        unsigned char *ob = static_cast<unsigned char *>(a.out) + (t0 * H + h) * V * (a.out_bf16 ? 2 : 4);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int i = 16 * p + 4 * g + e;
-                            if (i < n) st_out(a.out, a.out_bf16, ((t0 + i) * H + h) * V + j, a.scale * o[e]);
+                            const uint32_t off = (uint32_t)(i * H * V + j);
+                            if (i < n) {
+                                if (a.out_bf16)
+                                    *reinterpret_cast<__bf16 *>(ob + 2u * off) = (__bf16)(a.scale * o[e]);
+                                else
+                                    *reinterpret_cast<float *>(ob + 4u * off) = a.scale * o[e];
+                            }
                         }
                     }
                 }
@@ -757,25 +772,26 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * p + 4 * qd + i;
                 const uint32_t o = (uint32_t)((r < last ? r : last) * rs + c0);
+                const uint32_t ob = o * (uint32_t)sizeof(RawIn);  // byte offsets from uniform bases
                 if constexpr (!ZG) {
-                    ral[u][i] = *reinterpret_cast<const float2 *>(gb + o);
+                    ral[u][i] = ld_at<float2>(gb, 4u * o);
                 } else if constexpr (std::is_same<RawPair, float2>::value) {
-                    ral[u][i] = *reinterpret_cast<const float2 *>(zb + o);
+                    ral[u][i] = ld_at<float2>(zb, ob);
                 } else {
-                    ral[u][i].x = __builtin_bit_cast(float, *reinterpret_cast<const RawPair *>(zb + o));
+                    ral[u][i].x = __builtin_bit_cast(float, ld_at<RawPair>(zb, ob));
                 }
-                rq[u][i] = *reinterpret_cast<const RawPair *>(qb + o);
-                rk[u][i] = *reinterpret_cast<const RawPair *>(kb + o);
+                rq[u][i] = ld_at<RawPair>(qb, ob);
+                rk[u][i] = ld_at<RawPair>(kb, ob);
             }
         }
-        rbeta = a.beta[(t0 + (tp < last ? tp : last)) * H + h];
+        rbeta = ld_at<float>(a.beta + t0 * H + h, 4u * (uint32_t)((tp < last ? tp : last) * H));
         const RawIn *vbp = reinterpret_cast<const RawIn *>(v) + (t0 * H + h) * V + vb * BV;
 #pragma unroll
         for (int w = 0; w < NVE; ++w) {
             const int e = (tp + NPT * w) % (BV * C / 2);
             const int j = e % BV, r = 2 * (e / BV);
-            rv[w][0] = vbp[(uint32_t)((r < last ? r : last) * H * V + j)];
-            rv[w][1] = vbp[(uint32_t)((r + 1 < last ? r + 1 : last) * H * V + j)];
+            rv[w][0] = ld_at<RawIn>(vbp, (uint32_t)sizeof(RawIn) * (uint32_t)((r < last ? r : last) * H * V + j));
+            rv[w][1] = ld_at<RawIn>(vbp, (uint32_t)sizeof(RawIn) * (uint32_t)((r + 1 < last ? r + 1 : last) * H * V + j));
         }
     };
     auto raw_f32 = [&](RawIn x) -> float {
@@ -885,7 +901,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 }
             }
             if (tp < C) {
-                const float b = a.beta_logits ? 1.f / (1.f + __expf(-rbeta)) : rbeta;
+                const float b = a.beta_logits ? __builtin_amdgcn_rcpf(1.f + __expf(-rbeta)) : rbeta;
                 Btv[tp] = tp < n_it ? b : 0.f;
             }
         }
@@ -917,7 +933,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                     eAll.y *= tpr[pp].y;
                 }
                 if (p == 0 && qd == 0) *reinterpret_cast<float2 *>(eGC + c0) = eAll;
-                const float2 rT = {1.f / own.x, 1.f / own.y};
+                const float2 rT = {__builtin_amdgcn_rcpf(own.x), __builtin_amdgcn_rcpf(own.y)};
                 // extra right-operand versions for tiles (pp, p) with pp >= p + 2
                 float2 xf[NP];
 #pragma unroll
