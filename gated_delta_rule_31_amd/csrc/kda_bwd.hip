@@ -854,70 +854,119 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool more = js + 1 < V / JS;
         if (more) load((js + 1) * JS);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products they overlap
-        // dO S^T, dVt S^T, Vt dS'^T on this wave's C x K tiles.  The slice's 16-wide
-        // reduction is split as k = 4*(lane/16) + s on both operands, so one 16-byte LDS
-        // read per operand feeds four matrix-core steps.
+        // Operands of T^T dVt (below), read first so that they arrive during the products.
+        // k = s = 16 m + 4 (lane/16) + u over every m: the blocks m < p of T^T are zero, and
+        // the wave with p = 0, which needs them all, sets the pace anyway.
+        float4 at[NP];
+        float bt[NP][4], bs[4], vr[4];
 #pragma unroll
-        for (int i = 0; i < NOWN; ++i) {
-            const int t = w + 4 * i, p = t / KT, ct = t % KT;
-            const int ra = (16 * p + i16) * LJ + 4 * g4, rb = (16 * ct + i16) * LJ + 4 * g4;
-            const float4 ao = *reinterpret_cast<const float4 *>(sO + ra);
-            const float4 avt = *reinterpret_cast<const float4 *>(sVt + ra);
-            const float4 adv = *reinterpret_cast<const float4 *>(sdVt + ra);
-            const float4 bh = *reinterpret_cast<const float4 *>(sH + rb);
-            const float4 bdh = *reinterpret_cast<const float4 *>(sDH + rb);
-            ps[i] = mf(ao.x, bh.x, ps[i]); pw[i] = mf(adv.x, bh.x, pw[i]); pd[i] = mf(avt.x, bdh.x, pd[i]);
-            ps[i] = mf(ao.y, bh.y, ps[i]); pw[i] = mf(adv.y, bh.y, pw[i]); pd[i] = mf(avt.y, bdh.y, pd[i]);
-            ps[i] = mf(ao.z, bh.z, ps[i]); pw[i] = mf(adv.z, bh.z, pw[i]); pd[i] = mf(avt.z, bdh.z, pd[i]);
-            ps[i] = mf(ao.w, bh.w, ps[i]); pw[i] = mf(adv.w, bh.w, pw[i]); pd[i] = mf(avt.w, bdh.w, pd[i]);
-        }
-        // dO Vt^T and dVt V^T on this wave's C x C tiles
+        for (int m = 0; m < NP; ++m) {
+            at[m] = *reinterpret_cast<const float4 *>(sTt + (16 * w + i16) * LDC + 16 * m + 4 * g4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = w + 4 * i, p = t / NP, qt = t % NP;
-            const int ra = (16 * p + i16) * LJ + 4 * g4, rb = (16 * qt + i16) * LJ + 4 * g4;
-            const float4 ao = *reinterpret_cast<const float4 *>(sO + ra);
-            const float4 adv = *reinterpret_cast<const float4 *>(sdVt + ra);
-            const float4 bvt = *reinterpret_cast<const float4 *>(sVt + rb);
-            const float4 bv = *reinterpret_cast<const float4 *>(sVr + rb);
-            ma[i] = mf(ao.x, bvt.x, ma[i]); mt[i] = mf(adv.x, bv.x, mt[i]);
-            ma[i] = mf(ao.y, bvt.y, ma[i]); mt[i] = mf(adv.y, bv.y, mt[i]);
-            ma[i] = mf(ao.z, bvt.z, ma[i]); mt[i] = mf(adv.z, bv.z, mt[i]);
-            ma[i] = mf(ao.w, bvt.w, ma[i]); mt[i] = mf(adv.w, bv.w, mt[i]);
+            for (int u = 0; u < 4; ++u) bt[m][u] = sdVt[(16 * m + 4 * g4 + u) * LJ + i16];
         }
-        // T^T dVt on row tile p = w of this slice: dv = beta T^T dVt, rowsum(V T^T dVt) for dbeta.
-        // k = s = 16 m + 4 (lane/16) + u over every m: the blocks m < p of T^T are zero, and the
-        // wave with p = 0, which needs them all, sets the pace anyway.  All operands are read
-        // before the first product.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bs[e] = sB[16 * w + 4 * g4 + e];
+            vr[e] = sVr[(16 * w + 4 * g4 + e) * LJ + i16];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep these reads here, ahead of the products
+        // dO S^T, dVt S^T, Vt dS'^T on this wave's C x K tiles and dO Vt^T, dVt V^T on its
+        // C x C tiles.  The slice's 16-wide reduction is split as k = 4*(lane/16) + s on both
+        // operands, so one 16-byte LDS read per operand feeds four matrix-core steps.
+        if constexpr (KT % 4 == 0) {
+            // Row tile p's fragments of dO, Vt and dVt feed this wave's KT/4 C x K tiles
+            // (column tiles w + 4c) and its C x C tile (p, w); the next row tile's fragments
+            // are read while the current one's products run.
+            constexpr int CT = KT / 4;
+            float4 bh[CT], bdh[CT];
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                const int rb = (16 * (w + 4 * c) + i16) * LJ + 4 * g4;
+                bh[c] = *reinterpret_cast<const float4 *>(sH + rb);
+                bdh[c] = *reinterpret_cast<const float4 *>(sDH + rb);
+            }
+            const int rq = (16 * w + i16) * LJ + 4 * g4;
+            const float4 bvt = *reinterpret_cast<const float4 *>(sVt + rq);
+            const float4 bv = *reinterpret_cast<const float4 *>(sVr + rq);
+            float4 fa[2][3];
+            auto frag = [&](int p, float4 (&f)[3]) {
+                const int ra = (16 * p + i16) * LJ + 4 * g4;
+                f[0] = *reinterpret_cast<const float4 *>(sO + ra);
+                f[1] = *reinterpret_cast<const float4 *>(sVt + ra);
+                f[2] = *reinterpret_cast<const float4 *>(sdVt + ra);
+            };
+            frag(0, fa[0]);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                if (p + 1 < NP) frag(p + 1, fa[(p + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);  // the next row tile's reads go out first
+                const float4 ao = fa[p & 1][0], avt = fa[p & 1][1], adv = fa[p & 1][2];
+#pragma unroll
+                for (int c = 0; c < CT; ++c) {
+                    const int i = p * CT + c;  // tile w + 4 i: row tile p, column tile w + 4 c
+                    ps[i] = mf(ao.x, bh[c].x, ps[i]); pw[i] = mf(adv.x, bh[c].x, pw[i]); pd[i] = mf(avt.x, bdh[c].x, pd[i]);
+                    ps[i] = mf(ao.y, bh[c].y, ps[i]); pw[i] = mf(adv.y, bh[c].y, pw[i]); pd[i] = mf(avt.y, bdh[c].y, pd[i]);
+                    ps[i] = mf(ao.z, bh[c].z, ps[i]); pw[i] = mf(adv.z, bh[c].z, pw[i]); pd[i] = mf(avt.z, bdh[c].z, pd[i]);
+                    ps[i] = mf(ao.w, bh[c].w, ps[i]); pw[i] = mf(adv.w, bh[c].w, pw[i]); pd[i] = mf(avt.w, bdh[c].w, pd[i]);
+                }
+                ma[p] = mf(ao.x, bvt.x, ma[p]); mt[p] = mf(adv.x, bv.x, mt[p]);
+                ma[p] = mf(ao.y, bvt.y, ma[p]); mt[p] = mf(adv.y, bv.y, mt[p]);
+                ma[p] = mf(ao.z, bvt.z, ma[p]); mt[p] = mf(adv.z, bv.z, mt[p]);
+                ma[p] = mf(ao.w, bvt.w, ma[p]); mt[p] = mf(adv.w, bv.w, mt[p]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NOWN; ++i) {
+                const int t = w + 4 * i, p = t / KT, ct = t % KT;
+                const int ra = (16 * p + i16) * LJ + 4 * g4, rb = (16 * ct + i16) * LJ + 4 * g4;
+                const float4 ao = *reinterpret_cast<const float4 *>(sO + ra);
+                const float4 avt = *reinterpret_cast<const float4 *>(sVt + ra);
+                const float4 adv = *reinterpret_cast<const float4 *>(sdVt + ra);
+                const float4 bh = *reinterpret_cast<const float4 *>(sH + rb);
+                const float4 bdh = *reinterpret_cast<const float4 *>(sDH + rb);
+                ps[i] = mf(ao.x, bh.x, ps[i]); pw[i] = mf(adv.x, bh.x, pw[i]); pd[i] = mf(avt.x, bdh.x, pd[i]);
+                ps[i] = mf(ao.y, bh.y, ps[i]); pw[i] = mf(adv.y, bh.y, pw[i]); pd[i] = mf(avt.y, bdh.y, pd[i]);
+                ps[i] = mf(ao.z, bh.z, ps[i]); pw[i] = mf(adv.z, bh.z, pw[i]); pd[i] = mf(avt.z, bdh.z, pd[i]);
+                ps[i] = mf(ao.w, bh.w, ps[i]); pw[i] = mf(adv.w, bh.w, pw[i]); pd[i] = mf(avt.w, bdh.w, pd[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = w + 4 * i, p = t / NP, qt = t % NP;
+                const int ra = (16 * p + i16) * LJ + 4 * g4, rb = (16 * qt + i16) * LJ + 4 * g4;
+                const float4 ao = *reinterpret_cast<const float4 *>(sO + ra);
+                const float4 adv = *reinterpret_cast<const float4 *>(sdVt + ra);
+                const float4 bvt = *reinterpret_cast<const float4 *>(sVt + rb);
+                const float4 bv = *reinterpret_cast<const float4 *>(sVr + rb);
+                ma[i] = mf(ao.x, bvt.x, ma[i]); mt[i] = mf(adv.x, bv.x, mt[i]);
+                ma[i] = mf(ao.y, bvt.y, ma[i]); mt[i] = mf(adv.y, bv.y, mt[i]);
+                ma[i] = mf(ao.z, bvt.z, ma[i]); mt[i] = mf(adv.z, bv.z, mt[i]);
+                ma[i] = mf(ao.w, bvt.w, ma[i]); mt[i] = mf(adv.w, bv.w, mt[i]);
+            }
+        }
+        // T^T dVt on row tile p = w of this slice: dv = beta T^T dVt, rowsum(V T^T dVt) for
+        // dbeta (even and odd k blocks in two accumulators, so the products overlap)
         {
             const int p = w;
-            float4 at[NP];
-            float bt[NP][4], bs[4], vr[4];
+            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < NP; ++m) {
-                at[m] = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) bt[m][u] = sdVt[(16 * m + 4 * g4 + u) * LJ + i16];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bs[e] = sB[16 * p + 4 * g4 + e];
-                vr[e] = sVr[(16 * p + 4 * g4 + e) * LJ + i16];
-            }
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < NP; ++m) {
-                acc = mf(at[m].x, bt[m][0], acc);
-                acc = mf(at[m].y, bt[m][1], acc);
-                acc = mf(at[m].z, bt[m][2], acc);
-                acc = mf(at[m].w, bt[m][3], acc);
+            for (int m = 0; m < NP; m += 2) {
+                acc0 = mf(at[m].x, bt[m][0], acc0);
+                if (m + 1 < NP) acc1 = mf(at[m + 1].x, bt[m + 1][0], acc1);
+                acc0 = mf(at[m].y, bt[m][1], acc0);
+                if (m + 1 < NP) acc1 = mf(at[m + 1].y, bt[m + 1][1], acc1);
+                acc0 = mf(at[m].z, bt[m][2], acc0);
+                if (m + 1 < NP) acc1 = mf(at[m + 1].z, bt[m + 1][2], acc1);
+                acc0 = mf(at[m].w, bt[m][3], acc0);
+                if (m + 1 < NP) acc1 = mf(at[m + 1].w, bt[m + 1][3], acc1);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * p + 4 * g4 + e;
+                const float x = acc0[e] + acc1[e];
                 if (row < cp.L)
-                    st_out(a.dv, a.grad_bf16, ((cp.t0 + row) * H + h) * V + js * JS + i16, bs[e] * acc[e]);
-                dbacc[e] += vr[e] * acc[e];  // summed over the row's lanes at the end
+                    st_out(a.dv, a.grad_bf16, ((cp.t0 + row) * H + h) * V + js * JS + i16, bs[e] * x);
+                dbacc[e] += vr[e] * x;  // summed over the row's lanes at the end
             }
         }
         {
