@@ -362,7 +362,7 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, kda_dtype 
             if (outs[j] == outs[i]) return KDA_ERR_ALIAS;
     }
     const int64_t slots = kda::chunk_bwd_slots(B, T, num_seqs, cu_seqlens != nullptr);
-    if (slots > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (slots * H > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;  // (chunk slot, head) units index as int
 
     kda::BwdArgs a;
     a.q = q;

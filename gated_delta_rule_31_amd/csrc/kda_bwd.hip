@@ -31,6 +31,9 @@
 //                                  dVt, and writes the initial-state gradient
 //   vgrads  (chunk, head)          the contractions over V; writes dv
 //   kgrads  (chunk, head)          dT, dA and the decayed adjoints; writes dq, dk, dgate, dbeta
+// The waves of a workgroup exchange data through LDS only (global memory is read, or
+// written for later launches, never read back in the same kernel), so every workgroup
+// barrier is an LDS-only barrier: global loads and stores stay in flight across it.
 // Chunk slots: without cu_seqlens slot b*NT + j is chunk j of batch row b; with them,
 // sequence s owns slots floor(cu[s]/C) + s + j, j < ceil(len_s / C) (disjoint, fewer than
 // T/C + N in all); a slot no sequence owns is skipped.
@@ -130,6 +133,14 @@ __device__ __forceinline__ float4 ld4_any(const void *p, int is_bf16, int64_t i)
     return is_bf16 ? b : f;
 }
 __device__ __forceinline__ void st4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
+// four loaded elements as float: float4 as is, bf16 by widening
+__device__ __forceinline__ float4 raw_f4(float4 x) { return x; }
+__device__ __forceinline__ float4 raw_f4(s16x4 x) {
+    return make_float4(__builtin_bit_cast(float, (uint32_t)(uint16_t)x[0] << 16),
+                       __builtin_bit_cast(float, (uint32_t)(uint16_t)x[1] << 16),
+                       __builtin_bit_cast(float, (uint32_t)(uint16_t)x[2] << 16),
+                       __builtin_bit_cast(float, (uint32_t)(uint16_t)x[3] << 16));
+}
 
 // Loads are issued from addresses that are always valid (rows past the chunk read its last
 // row) and masked where the value is used: a load under a per-lane condition is compiled
@@ -168,8 +179,11 @@ struct PrepLds {
     static constexpr size_t bytes = sizeof(float) * (R + 2 * BC * LDC + BC + TAB + K);
 };
 
+// Persistent: workgroup b takes the (chunk slot, head) units b, b + G, b + 2G, ... (G the
+// grid size, one workgroup per CU: LDS allows no more) and loads the next unit's q, k, gate
+// and beta while it processes the current one.
 template <typename TIn, int K, int V>
-__global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_prep_kernel(BwdArgs a) {
     constexpr int LK = PrepLds<K, V>::LK, LW = PrepLds<K, V>::LW, LV = PrepLds<K, V>::LV;
     constexpr int NV4 = (BC * V / 4 + NTH - 1) / NTH;  // float4 groups of v per thread
     constexpr int NK4 = (BC * K / 4 + NTH - 1) / NTH;  // float4 groups of a C x K tile per thread
@@ -188,41 +202,69 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     float *sMid = sEe + NP * K;                        // [NP][K] m_p
     float *sE = sMid + NP * K;                         // [K] Gamma_C
 
-    const int n = blockIdx.x, h = blockIdx.y, H = a.H;
-    const ChunkPos cp = slot_chunk(n, a.cu_seqlens, a.num_seqs, a.T);
-    if (cp.L == 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
-    const int64_t sh = (int64_t)n * H + h;
+    const int H = a.H;
+    const int units = a.slots * H;  // below 2^31 (checked by the host)
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
     const TIn *v = static_cast<const TIn *>(a.v);
     static_assert(BC * K / 4 % NTH == 0 && BC * V / 4 % NTH == 0, "whole float4 groups per thread");
-    float4 rv[NV4];  // this chunk's v, in flight until U is formed
+    // q, k, gate and beta of the next unit (four elements per load; rows past the chunk
+    // read its last row and are masked when stored), kept in the input format until then
+    using Raw4 = typename std::conditional<std::is_same<TIn, float>::value, float4, s16x4>::type;
+    Raw4 rq[NK4], rk[NK4];
+    float4 rg[NK4];
+    float rb = 0.f;
+    // Unconditional, so that the loads land directly in the registers the next iteration
+    // reads (a load under a condition would be merged through copies that wait for it);
+    // an unused slot, or a unit past the last one, reads row 0.
+    auto fetch = [&](int un, ChunkPos c) {
+        const int h = un % H, tid = threadIdx.x;
+        if (c.L == 0) c = ChunkPos{0, 1};
+#pragma unroll
+        for (int i = 0; i < NK4; ++i) {
+            const int idx = tid + NTH * i, r = (4 * idx) / K, col = (4 * idx) % K;
+            const int64_t gi = ((c.t0 + crow(r, c.L)) * H + h) * K + col;
+            rq[i] = *reinterpret_cast<const Raw4 *>(q + gi);
+            rk[i] = *reinterpret_cast<const Raw4 *>(k + gi);
+            rg[i] = ld4(a.gate.gate + gi);
+        }
+        rb = a.beta[(c.t0 + crow(tid & (BC - 1), c.L)) * H + h];
+    };
+    int unit = blockIdx.x;
+    ChunkPos cpn = {0, 0};
+    if (unit < units) cpn = slot_chunk(unit / H, a.cu_seqlens, a.num_seqs, a.T);
+    fetch(unit, cpn);
+    for (; unit < units; unit += gridDim.x) {
+    // The thread index is re-read in every iteration through an opaque copy, so that the
+    // compiler does not hoist the unit's many index computations out of the loop and keep
+    // them all in registers.
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g4 = lane >> 4, i16 = lane & 15;
+    const ChunkPos cp = cpn;
+    const int n = unit / H, h = unit % H;
+    const int un = unit + (int)gridDim.x;
+    cpn = un < units ? slot_chunk(un / H, a.cu_seqlens, a.num_seqs, a.T) : ChunkPos{0, 0};
+    if (cp.L == 0) {  // an unused slot (uniform): only the next unit's loads
+        fetch(un, cpn);
+        continue;
+    }
+    const int64_t sh = (int64_t)n * H + h;
+    Raw4 rv[NV4];  // this chunk's v, in flight (in the input format) until U is formed
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
         const int idx = tid + NTH * i, r = (4 * idx) / V, c = (4 * idx) % V;
-        rv[i] = ld4(v + ((cp.t0 + crow(r, cp.L)) * H + h) * V + c);
+        rv[i] = *reinterpret_cast<const Raw4 *>(v + ((cp.t0 + crow(r, cp.L)) * H + h) * V + c);
     }
-    {
-        // all loads first (four elements per load), then the LDS stores
-        float4 rq[NK4], rk[NK4], rg[NK4];
 #pragma unroll
-        for (int i = 0; i < NK4; ++i) {
-            const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
-            const int64_t gi = ((cp.t0 + crow(r, cp.L)) * H + h) * K + c;
-            rq[i] = ld4(q + gi);
-            rk[i] = ld4(k + gi);
-            rg[i] = ld4(a.gate.gate + gi);
-        }
-#pragma unroll
-        for (int i = 0; i < NK4; ++i) {  // rows past the chunk: no token, no decay
-            const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
-            st4(sQ + r * LK + c, mask4(rq[i], r < cp.L));
-            st4(sK + r * LK + c, mask4(rk[i], r < cp.L));
-            st4(sG + r * LK + c, gate_log4(a.gate, rg[i], r < cp.L));
-        }
+    for (int i = 0; i < NK4; ++i) {  // rows past the chunk: no token, no decay
+        const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
+        st4(sQ + r * LK + c, mask4(raw_f4(rq[i]), r < cp.L));
+        st4(sK + r * LK + c, mask4(raw_f4(rk[i]), r < cp.L));
+        st4(sG + r * LK + c, gate_log4(a.gate, rg[i], r < cp.L));
     }
-    if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
-    __syncthreads();
+    if (tid < BC) sB[tid] = tid < cp.L ? rb : 0.f;
+    lds_barrier();
+    fetch(un, cpn);  // in flight while this unit is processed
     if (tid < K) {
         float run = 0.f;
 #pragma unroll 8
@@ -233,7 +275,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
         sE[tid] = run;
         a.w.gC[sh * K + tid] = expf(run);
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < (NP * NP + 3 * NP) * K; i += NTH) {
         const int c = i % K, j = i / K;
         if (j < NP * NP) {
@@ -249,12 +291,12 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
             sMid[pp * K + c] = sG[(16 * pp + 7) * LK + c];
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < BC * K; i += NTH) {  // F1 replaces Gamma, element by element
         const int r = i / K, c = i % K;
         sG[r * LK + c] = expf(sG[r * LK + c] - sMid[(r >> 4) * K + c]);
     }
-    __syncthreads();
+    lds_barrier();
     float *sF1 = sG;
 
     // Abar (strictly lower) and A_qk (lower): the ten tiles on or below the diagonal, spread
@@ -306,7 +348,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
             Aqk[i] = 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // T = (I + diag(beta) Abar)^-1: diagonal 16x16 blocks by the blocked inverse, then
     // block forward substitution T_pq = -T_pp sum_{q<=u<p} A_pu T_uq
@@ -322,7 +364,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) sT[(16 * pb + 4 * g4 + u) * LDC + 16 * pb + i16] = tb[u];
     }
-    __syncthreads();
+    lds_barrier();
     for (int pb = 1; pb < NP; ++pb) {
         if (w < pb) {
             const int qb = w;
@@ -341,7 +383,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) sT[(16 * pb + 4 * g4 + u) * LDC + 16 * qb + i16] = -y[u];
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // element-wise products: e^Gamma = F1 e^{m_p}, e^{Gamma_C - Gamma} = e^{Gamma_C - m_p} / F1
@@ -373,7 +415,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
         const int e = 4 * i;
         st4(Tm + e, *reinterpret_cast<const float4 *>(sT + (e / BC) * LDC + e % BC));
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < NK4; ++i) {  // q, k and F1 are consumed: their LDS takes beta K e^Gamma
         const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
@@ -383,9 +425,10 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     for (int i = 0; i < NV4; ++i) {  // and beta v (beta is zero past the chunk)
         const int idx = tid + NTH * i, r = (4 * idx) / V, c = (4 * idx) % V;
         const float b = sB[r];
-        st4(sBV + r * LV + c, make_float4(b * rv[i].x, b * rv[i].y, b * rv[i].z, b * rv[i].w));
+        const float4 x = raw_f4(rv[i]);
+        st4(sBV + r * LV + c, make_float4(b * x.x, b * x.y, b * x.z, b * x.w));
     }
-    __syncthreads();
+    lds_barrier();
 
     // W = T (beta K e^Gamma), U = T (beta V); T is lower triangular.  Wave w owns the
     // column tiles w, w + 4, ... of W and of U over all four row tiles, so one read of a
@@ -445,6 +488,8 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
             }
         }
     }
+    lds_barrier();  // this unit's LDS is consumed before the next unit's inputs are stored
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -457,7 +502,8 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 constexpr int SBV = 16;  // value columns per workgroup in the serial passes
 
 template <int K, int V>
-__global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdArgs a) {
+// (three workgroups per CU)
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3, 3))) void bwd_states_kernel(BwdArgs a) {
     constexpr int LB = SBV + 4, KQ = K / 16, NST = (K / 16 + 3) / 4;
     __shared__ float sS[K * LB];
     __shared__ float sV[BC * LB];
@@ -466,7 +512,7 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdArgs a) {
     const int H = a.H;
     if (hs >= a.num_seqs * H) return;
     const int h = hs % H, s = hs / H;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g4 = lane >> 4, i16 = lane & 15;
     const int j0 = vb * SBV, p = w;
     int64_t t0, len;
     int base;
@@ -517,47 +563,59 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdArgs a) {
     for (int j = 0; j < nch; ++j) {
         const int64_t sh = (int64_t)(base + j) * H + h;
         loadB(sh);
-        __syncthreads();
+        lds_barrier();
         float *hp = a.w.h + sh * K * V;
         for (int i = tid; i < K * SBV; i += NTH) {
             const int r = i / SBV, c = i % SBV;
             hp[r * V + j0 + c] = sS[r * LB + c];
         }
         {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            // two accumulators (even and odd key tiles), so consecutive products overlap
+            f4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int q = 0; q < KQ; ++q) {
                 const float *b = sS + (16 * q + 4 * g4) * LB + i16;
-                acc = mf(wf[q].x, b[0], acc);
-                acc = mf(wf[q].y, b[LB], acc);
-                acc = mf(wf[q].z, b[2 * LB], acc);
-                acc = mf(wf[q].w, b[3 * LB], acc);
+                acc[q & 1] = mf(wf[q].x, b[0], acc[q & 1]);
+                acc[q & 1] = mf(wf[q].y, b[LB], acc[q & 1]);
+                acc[q & 1] = mf(wf[q].z, b[2 * LB], acc[q & 1]);
+                acc[q & 1] = mf(wf[q].w, b[3 * LB], acc[q & 1]);
             }
             float *Vt = a.w.Vt + sh * BC * V + j0 + i16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * p + 4 * g4 + e;
-                const float vt = uf[e] - acc[e];
+                const float vt = uf[e] - (acc[0][e] + acc[1][e]);
                 sV[row * LB + i16] = vt;
                 Vt[row * V] = vt;
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (j + 1 < nch) loadA(sh + H);
+        {
+            // this wave's key tiles side by side, so their products overlap
+            float bv[16];  // the pseudo-value column of this lane, read before the products
 #pragma unroll
-        for (int i = 0; i < NST; ++i) {
-            const int rt = w + 4 * i;
-            if (rt < K / 16) {
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int u = 0; u < 4; ++u) bv[4 * q + u] = sV[(16 * q + 4 * g4 + u) * LB + i16];
+            __builtin_amdgcn_sched_barrier(0);
+            f4 acc[NST];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        acc = mf(kdf[i][4 * q + u], sV[(16 * q + 4 * g4 + u) * LB + i16], acc);
+            for (int i = 0; i < NST; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = 16 * rt + 4 * g4 + e;
-                    sS[m * LB + i16] = gcf[i][e] * sS[m * LB + i16] + acc[e];
+            for (int x = 0; x < 16; ++x)
+#pragma unroll
+                for (int i = 0; i < NST; ++i)
+                    if (w + 4 * i < K / 16) acc[i] = mf(kdf[i][x], bv[x], acc[i]);
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                const int rt = w + 4 * i;
+                if (rt < K / 16) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = 16 * rt + 4 * g4 + e;
+                        sS[m * LB + i16] = gcf[i][e] * sS[m * LB + i16] + acc[i][e];
+                    }
                 }
             }
         }
@@ -575,7 +633,8 @@ struct DstCfg {
 };
 
 template <int K, int V>
-__global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
+// (two workgroups per CU: the register allocation stays within half a SIMD's file)
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dstates_kernel(BwdArgs a) {
     constexpr int DBV = DstCfg<V>::DBV, NCT = DstCfg<V>::NCT;
     constexpr int LB = DBV + 4, KQ = K / 16, NST = (K / 16 + 3) / 4;
     __shared__ float sD[K * LB];
@@ -586,7 +645,7 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
     const int H = a.H;
     if (hs >= a.num_seqs * H) return;
     const int h = hs % H, s = hs / H;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g4 = lane >> 4, i16 = lane & 15;
     const int j0 = vb * DBV, p = w;
     int64_t t0, len;
     int base;
@@ -658,7 +717,7 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
     for (int j = nch - 1; j >= 0; --j) {
         const int64_t sh = (int64_t)(base + j) * H + h;
         loadB(j);
-        __syncthreads();
+        lds_barrier();
         float *dhp = a.w.dh + sh * K * V;
         for (int i = tid; i < K * DBV / 4; i += NTH) {
             const int r = (4 * i) / DBV, c = (4 * i) % DBV;
@@ -671,7 +730,7 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
             const float f = dok[i] ? sc : 0.f;
             st4(sO + r * LB + c, make_float4(f * dof[i].x, f * dof[i].y, f * dof[i].z, f * dof[i].w));
         }
-        __syncthreads();
+        lds_barrier();
         {
             f4 acc[NCT];
 #pragma unroll
@@ -707,7 +766,7 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
                     dVt[row * V + 16 * ct] = acc[ct][e];
                 }
         }
-        __syncthreads();
+        lds_barrier();
         if (j > 0) loadA(j - 1);
 #pragma unroll
         for (int i = 0; i < NST; ++i) {
@@ -737,7 +796,7 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (a.d_initial_state)
         for (int i = tid; i < K * DBV / 4; i += NTH) {
             const int r = (4 * i) / DBV, c = (4 * i) % DBV;
@@ -838,7 +897,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
     store(reinterpret_cast<float *>(smem));
-    __syncthreads();
+    lds_barrier();
 
     f4 ps[NOWN], pw[NOWN], pd[NOWN], ma[4], mt[4];
 #pragma unroll
@@ -975,7 +1034,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int j = 0; j < CW; ++j) rsacc += sH[c * LJ + part * CW + j] * sDH[c * LJ + part * CW + j];
         }
         if (more) store(reinterpret_cast<float *>(smem) + ((js + 1) & 1) * SL);
-        __syncthreads();
+        lds_barrier();
     }
 
     // the slices are done: their LDS now holds PW (-dW), beta K e^Gamma, MT and the C x C work
@@ -1022,7 +1081,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int e = 0; e < 4; ++e) sRv[16 * w + 4 * g4 + e] = dbacc[e];
     }
     sRs[tid] = rsacc;
-    __syncthreads();  // every wave is past the slices
+    lds_barrier();  // every wave is past the slices
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
         const int t = w + 4 * i, p = t / KT, ct = t % KT, c = 16 * ct + i16;
@@ -1049,7 +1108,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int part = 0; part < PARTS; ++part) acc += sRs[part * K + tid];
         a.w.rs[sh * K + tid] = acc;
     }
-    __syncthreads();
+    lds_barrier();
     // dT = MT + dW (beta K e^Gamma)^T with dW = -PW (beta_s applied to the column)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1096,7 +1155,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (i16 == 0) sRk[ct * BC + row] = part;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // Y = dT T^T
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1115,7 +1174,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int e = 0; e < 4; ++e) sM[(16 * p + 4 * g4 + e) * LDC + s] = acc[e];
     }
-    __syncthreads();
+    lds_barrier();
     // dA = -strict_tril(T^T Y); rowsum(dA Abar) for dbeta; beta dA is what the key space needs
     float *dAb = a.w.MT + sh * BC * BC;
     static_assert(NP == 4, "the C x C tiles w + 4 i of a wave are row tile i, column tile w");
@@ -1143,7 +1202,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             dAb[row * BC + s] = sB[row] * da;
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < cp.L) {
         float acc = sRv[tid];
         for (int ct = 0; ct < KT; ++ct) acc += sRk[ct * BC + tid];
@@ -1191,7 +1250,7 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     const int n = u / H, h = u % H, c0 = cb * KB;
     const ChunkPos cp = slot_chunk(n, a.cu_seqlens, a.num_seqs, a.T);
     if (cp.L == 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, i16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g4 = lane >> 4, i16 = lane & 15;
     const int64_t sh = (int64_t)n * H + h;
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
     // element-wise inputs of this thread's output tiles (dO S^T, Vt dS'^T, T^T dW), in
@@ -1248,7 +1307,7 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
         }
     }
     if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
-    __syncthreads();
+    lds_barrier();
     if (tid < KB) {
         float run = 0.f;
         for (int r = 0; r < BC; ++r) {
@@ -1256,7 +1315,7 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             sF2[r * LKB + tid] = run;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // tables per channel, from the tile middles m_p and the chunk end
     for (int i = tid; i < (NP * NP + 3 * NP) * KB; i += NTH) {
         const int c = i % KB, j = i / KB;
@@ -1273,14 +1332,14 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             sMid[pp * KB + c] = sF2[(16 * pp + 7) * LKB + c];
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < BC * KB; i += NTH) {  // each element rewritten by the thread that reads it
         const int r = i / KB, c = i % KB;
         const float d = sF2[r * LKB + c] - sMid[(r >> 4) * KB + c];
         sF1[r * LKB + c] = expf(d);
         sF2[r * LKB + c] = expf(-d);
     }
-    __syncthreads();
+    lds_barrier();
 
     float dgt[NOWN][4], est[NOWN][4];
 #pragma unroll
@@ -1348,7 +1407,7 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             }
         }
     }
-    __syncthreads();  // q, k are no longer read: their LDS takes the row terms
+    lds_barrier();  // q, k are no longer read: their LDS takes the row terms
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
         const int t = w + 4 * i, rt = t / KBT, ct = t % KBT, c = 16 * ct + i16;
@@ -1359,7 +1418,7 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             sK[row * LKB + c] = est[i][e];
         }
     }
-    __syncthreads();
+    lds_barrier();
     // d ln alpha per key channel: reverse in-chunk sum of the row terms, plus the chunk-end
     // terms gamma_C rowsum(S dS') and the exclusive forward sum of the Kd terms; the result
     // replaces the row terms in LDS
@@ -1379,7 +1438,7 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             sQ[r * LKB + c] = dl[r] + rv;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dgate in four-element groups over the whole workgroup (alpha read in one batch)
     {
         constexpr int NK4 = (BC * KB / 4 + NTH - 1) / NTH;
@@ -1408,6 +1467,19 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     }
 }
 
+// compute units of the current device (queried once per device)
+int num_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 template <int K, int V>
 hipError_t set_lds(const void *kern, size_t bytes) {
     return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -1428,9 +1500,11 @@ hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
     }
     const int hs8 = (num_seqs * a.H + 7) / 8, sh8 = (int)(((int64_t)a.slots * a.H + 7) / 8);
     const dim3 gp(a.slots, a.H), gs(8 * (V / SBV) * hs8), gd(8 * (V / DstCfg<V>::DBV) * hs8);
+    const int64_t units = (int64_t)a.slots * a.H;
+    const dim3 gpp((unsigned)(units < num_cus() ? units : num_cus()));  // persistent prep
     const dim3 gk(8 * (K / KgLds<K>::KB) * sh8);
     constexpr size_t prep_bytes = PrepLds<K, V>::bytes;
-    hipLaunchKernelGGL(kprep, gp, dim3(NTH), prep_bytes, stream, a);
+    hipLaunchKernelGGL(kprep, gpp, dim3(NTH), prep_bytes, stream, a);
     hipLaunchKernelGGL((bwd_states_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL((bwd_dstates_kernel<K, V>), gd, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL(kvg, gp, dim3(NTH), VgLds<K>::bytes, stream, a);

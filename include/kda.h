@@ -254,7 +254,8 @@ int kda_chunk_fwd_supported(kda_dtype in_dtype, int K, int V, int chunk_size);
  * (about 0.55 MB per 64-token chunk and head at K = V = 128); its contents on entry do not
  * matter and on return are unspecified.  KDA_ERR_BAD_ARGUMENT if it is too small.
  * All arithmetic is float32 (matrix cores for the products).  Supported: K, V in
- * {16, 32, 64, 128}, N and H up to 65535.  Preconditions as kda_chunk_fwd: every log-decay
+ * {16, 32, 64, 128}, N and H up to 65535, and (64-token chunk slots) x H below 2^31 (else
+ * KDA_ERR_UNSUPPORTED).  Preconditions as kda_chunk_fwd: every log-decay
  * >= -5 (alpha > 0).  No output may overlap an input or another output.
  * T == 0 (or B == 0): no token gradients; d_initial_state = d_final_state (or zeros).
  */
