@@ -93,15 +93,13 @@ __device__ __forceinline__ void seq_range(int s, const int32_t *cu, int64_t T, i
     }
 }
 
-__device__ __forceinline__ float gate_log(const GateIn &g, int64_t i) {
-    return g.mode == GATE_LOG ? g.gate[i] : logf(g.gate[i]);
-}
-
-// gate values of four consecutive elements as log-decay (rows past the chunk: 0, no decay)
+// gate values of four consecutive elements as log-decay (rows past the chunk: 0, no decay);
+// a retention alpha goes through the hardware base-2 logarithm (1 ulp) times ln 2
+__device__ __forceinline__ float ln_alpha(float x) { return __builtin_amdgcn_logf(x) * 0.69314718055994531f; }
 __device__ __forceinline__ float4 gate_log4(const GateIn &g, float4 x, bool ok) {
     if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
     if (g.mode == GATE_LOG) return x;
-    return make_float4(logf(x.x), logf(x.y), logf(x.z), logf(x.w));
+    return make_float4(ln_alpha(x.x), ln_alpha(x.y), ln_alpha(x.z), ln_alpha(x.w));
 }
 
 // Workgroups go to the 8 XCDs round-robin by block index, and each XCD has its own L2.
@@ -133,6 +131,9 @@ __device__ __forceinline__ float4 ld4_any(const void *p, int is_bf16, int64_t i)
     return is_bf16 ? b : f;
 }
 __device__ __forceinline__ void st4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
+// e^x for |x| <= 40 (a log-decay difference inside one 16-row tile): the hardware base-2
+// exponential of x log2(e); the rounding of the product adds at most 3e-6 relative error
+__device__ __forceinline__ float exp_in_tile(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 // four loaded elements as float: float4 as is, bf16 by widening
 __device__ __forceinline__ float4 raw_f4(float4 x) { return x; }
 __device__ __forceinline__ float4 raw_f4(s16x4 x) {
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     lds_barrier();
     for (int i = tid; i < BC * K; i += NTH) {  // F1 replaces Gamma, element by element
         const int r = i / K, c = i % K;
-        sG[r * LK + c] = expf(sG[r * LK + c] - sMid[(r >> 4) * K + c]);
+        sG[r * LK + c] = exp_in_tile(sG[r * LK + c] - sMid[(r >> 4) * K + c]);
     }
     lds_barrier();
     float *sF1 = sG;
@@ -1109,98 +1110,135 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         a.w.rs[sh * K + tid] = acc;
     }
     lds_barrier();
+    // The C x C tiles w + 4 i of a wave are row tile i, column tile w; the products below
+    // run the wave's tiles side by side (independent accumulators) and share the operand
+    // that does not depend on the tile.
+    static_assert(NP == 4, "four 16-row tiles per chunk");
     // dT = MT + dW (beta K e^Gamma)^T with dW = -PW (beta_s applied to the column)
+    {
+        f4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        const float *ar = sPW + (16 * p + i16) * LK + 4 * g4, *br = sKg + s * LK + 4 * g4;
-#pragma unroll 4
+        for (int i = 0; i < 4; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+        const float *br = sKg + (16 * w + i16) * LK + 4 * g4;
+#pragma unroll 2
         for (int c0 = 0; c0 < K; c0 += 16) {
-            const float4 x = *reinterpret_cast<const float4 *>(ar + c0);
             const float4 y = *reinterpret_cast<const float4 *>(br + c0);
-            acc = mf(x.x, y.x, acc);
-            acc = mf(x.y, y.y, acc);
-            acc = mf(x.z, y.z, acc);
-            acc = mf(x.w, y.w, acc);
-        }
+            float4 x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e;
-            sY[row * LDC + s] = sM[row * LDC + s] - sB[s] * acc[e];
+            for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const float4 *>(sPW + (16 * i + i16) * LK + 4 * g4 + c0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].x, y.x, acc[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].y, y.y, acc[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].z, y.z, acc[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].w, y.w, acc[i]);
         }
+        const int s = 16 * w + i16;
+        const float bs = sB[s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * i + 4 * g4 + e;
+                sY[row * LDC + s] = sM[row * LDC + s] - bs * acc[i][e];
+            }
     }
     // dBk = T^T dW = -T^T PW on this wave's C x K tiles; rowsum(K e^Gamma dBk) for dbeta.
     // With K/16 a multiple of 4 the row tile of tile w + 4 i does not depend on the wave.
     float *dBk = a.w.PW + sh * BC * K;
+    {
+        f4 acc[NOWN];
 #pragma unroll
-    for (int i = 0; i < NOWN; ++i) {
-        const int t = w + 4 * i, p = KT % 4 == 0 ? (4 * i) / KT : t / KT, ct = t % KT, c = 16 * ct + i16;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NOWN; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < NP; ++m)
-            if (m >= p) {
-                const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
-                const float *br = sPW + (16 * m + 4 * g4) * LK + c;
-                acc = mf(at.x, br[0], acc);
-                acc = mf(at.y, br[LK], acc);
-                acc = mf(at.z, br[2 * LK], acc);
-                acc = mf(at.w, br[3 * LK], acc);
+        for (int m = 0; m < NP; ++m) {
+#pragma unroll
+            for (int i = 0; i < NOWN; ++i) {
+                const int t = w + 4 * i, p = KT % 4 == 0 ? (4 * i) / KT : t / KT, c = 16 * (t % KT) + i16;
+                if (m >= p) {
+                    const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
+                    const float *br = sPW + (16 * m + 4 * g4) * LK + c;
+                    acc[i] = mf(at.x, br[0], acc[i]);
+                    acc[i] = mf(at.y, br[LK], acc[i]);
+                    acc[i] = mf(at.z, br[2 * LK], acc[i]);
+                    acc[i] = mf(at.w, br[3 * LK], acc[i]);
+                }
             }
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e;
-            dBk[row * K + c] = -acc[e];
-            const float part = row16_sum(-acc[e] * sKg[row * LK + c]);
-            if (i16 == 0) sRk[ct * BC + row] = part;
+        for (int i = 0; i < NOWN; ++i) {
+            const int t = w + 4 * i, p = KT % 4 == 0 ? (4 * i) / KT : t / KT, ct = t % KT, c = 16 * ct + i16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * p + 4 * g4 + e;
+                dBk[row * K + c] = -acc[i][e];
+                const float part = row16_sum(-acc[i][e] * sKg[row * LK + c]);
+                if (i16 == 0) sRk[ct * BC + row] = part;
+            }
         }
     }
     lds_barrier();
     // Y = dT T^T
+    {
+        f4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        const float *ar = sY + (16 * p + i16) * LDC + 4 * g4, *br = sT + s * LDC + 4 * g4;
+        for (int i = 0; i < 4; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+        const float *br = sT + (16 * w + i16) * LDC + 4 * g4;
 #pragma unroll
         for (int j0 = 0; j0 < BC; j0 += 16) {
-            const float4 x = *reinterpret_cast<const float4 *>(ar + j0);
             const float4 y = *reinterpret_cast<const float4 *>(br + j0);
-            acc = mf(x.x, y.x, acc);
-            acc = mf(x.y, y.y, acc);
-            acc = mf(x.z, y.z, acc);
-            acc = mf(x.w, y.w, acc);
-        }
+            float4 x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sM[(16 * p + 4 * g4 + e) * LDC + s] = acc[e];
+            for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const float4 *>(sY + (16 * i + i16) * LDC + 4 * g4 + j0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].x, y.x, acc[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].y, y.y, acc[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].z, y.z, acc[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].w, y.w, acc[i]);
+        }
+        const int s = 16 * w + i16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sM[(16 * i + 4 * g4 + e) * LDC + s] = acc[i][e];
     }
     lds_barrier();
     // dA = -strict_tril(T^T Y); rowsum(dA Abar) for dbeta; beta dA is what the key space needs
     float *dAb = a.w.MT + sh * BC * BC;
-    static_assert(NP == 4, "the C x C tiles w + 4 i of a wave are row tile i, column tile w");
+    {
+        f4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = i, qt = w, s = 16 * qt + i16;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (qt <= p) {
+        for (int i = 0; i < 4; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+        const int s = 16 * w + i16;
 #pragma unroll
-            for (int m = p; m < NP; ++m) {
-                const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
-                const float *br = sM + (16 * m + 4 * g4) * LDC + s;
-                acc = mf(at.x, br[0], acc);
-                acc = mf(at.y, br[LDC], acc);
-                acc = mf(at.z, br[2 * LDC], acc);
-                acc = mf(at.w, br[3 * LDC], acc);
+        for (int m = 0; m < NP; ++m) {
+            const float *br = sM + (16 * m + 4 * g4) * LDC + s;
+            const float b0 = br[0], b1 = br[LDC], b2 = br[2 * LDC], b3 = br[3 * LDC];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (w <= i && i <= m) {  // tiles on or below the diagonal; T^T is upper
+                    const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * i + i16) * LDC + 16 * m + 4 * g4);
+                    acc[i] = mf(at.x, b0, acc[i]);
+                    acc[i] = mf(at.y, b1, acc[i]);
+                    acc[i] = mf(at.z, b2, acc[i]);
+                    acc[i] = mf(at.w, b3, acc[i]);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * i + 4 * g4 + e;
+                const float da = row > s ? -acc[i][e] : 0.f;
+                const float part = row16_sum(da * abr[i][e]);
+                if (i16 == 0) sRa[w * BC + row] = part;
+                dAb[row * BC + s] = sB[row] * da;
             }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e;
-            const float da = row > s ? -acc[e] : 0.f;
-            const float part = row16_sum(da * abr[i][e]);
-            if (i16 == 0) sRa[qt * BC + row] = part;
-            dAb[row * BC + s] = sB[row] * da;
-        }
     }
     lds_barrier();
     if (tid < cp.L) {
@@ -1336,8 +1374,8 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     for (int i = tid; i < BC * KB; i += NTH) {  // each element rewritten by the thread that reads it
         const int r = i / KB, c = i % KB;
         const float d = sF2[r * LKB + c] - sMid[(r >> 4) * KB + c];
-        sF1[r * LKB + c] = expf(d);
-        sF2[r * LKB + c] = expf(-d);
+        sF1[r * LKB + c] = exp_in_tile(d);
+        sF2[r * LKB + c] = exp_in_tile(-d);
     }
     lds_barrier();
 
