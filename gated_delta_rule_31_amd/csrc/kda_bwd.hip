@@ -131,6 +131,19 @@ __device__ __forceinline__ float4 ld4_any(const void *p, int is_bf16, int64_t i)
     return is_bf16 ? b : f;
 }
 __device__ __forceinline__ void st4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
+__device__ __forceinline__ void st2(float *p, float2 x) { *reinterpret_cast<float2 *>(p) = x; }
+// two consecutive elements as float (8-byte / 4-byte aligned loads)
+__device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+__device__ __forceinline__ float2 ld2(const __bf16 *p) {
+    const uint32_t x = *reinterpret_cast<const uint32_t *>(p);
+    return make_float2(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xffff0000u));
+}
+// two elements of a tensor given in either format, without a branch (as ld4_any)
+__device__ __forceinline__ float2 ld2_any(const void *p, int is_bf16, int64_t i) {
+    const float2 f = ld2(static_cast<const float *>(p) + (is_bf16 ? 0 : i));
+    const float2 b = ld2(static_cast<const __bf16 *>(p) + (is_bf16 ? i : 0));
+    return is_bf16 ? b : f;
+}
 // e^x for |x| <= 40 (a log-decay difference inside one 16-row tile): the hardware base-2
 // exponential of x log2(e); the rounding of the product adds at most 3e-6 relative error
 __device__ __forceinline__ float exp_in_tile(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
@@ -806,11 +819,13 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------------------------
-// vgrads: contractions over the value dimension, one workgroup per (chunk slot, head).
-// The value axis is walked in 16-column slices staged in LDS (coalesced 16-byte loads; the
-// next slice is loaded into registers while the matrix cores work on the current one and
-// stored into the other of two slice buffers, so one barrier per slice suffices); the
-// C x K and C x C results accumulate in registers over the slices.
+// vgrads: contractions over the value dimension, one workgroup of eight waves per (chunk
+// slot, head).  The value axis is walked in 16-column slices staged in LDS (the next slice
+// is loaded into registers while the matrix cores work on the current one and stored into
+// the other of two slice buffers, so one barrier per slice suffices); the C x K and C x C
+// results accumulate in registers over the slices.  Two waves share each SIMD, so one
+// wave's LDS reads and stores overlap the other's products.
+constexpr int VNW = 8, VNT = 64 * VNW;  // vgrads waves and threads
 template <int K>
 struct VgLds {
     static constexpr int JS = 16, LJ = JS + 4;  // slice width; row stride 20 keeps fragment reads conflict-free
@@ -819,15 +834,18 @@ struct VgLds {
     static constexpr int SLICES = 2 * SL;                              // two slice buffers
     static constexpr int TAIL = 2 * BC * LK + 2 * BC * LDC;           // PW, beta Kg, MT / Y, dT (after the slices)
     static constexpr int R1 = SLICES > TAIL ? SLICES : TAIL;
-    static constexpr size_t bytes = sizeof(float) * (R1 + 2 * BC * LDC + BC + NTH + (1 + K / 16 + NP) * BC);
+    static constexpr size_t bytes = sizeof(float) * (R1 + 2 * BC * LDC + BC + VNT + (1 + K / 16 + NP) * BC);
 };
 
-
-// (LDS limits this kernel to one workgroup per CU: the register allocation may use a whole SIMD)
+// Tiles of wave w: C x K tiles t = w + 8 i (row tile t / (K/16), column tile t % (K/16)),
+// C x C tiles (2 i + w / 4, w % 4) for i = 0, 1; T^T dVt on row tile w for w < 4.
+// (LDS limits this kernel to one workgroup per CU: each wave may use half a SIMD's registers)
 template <typename TIn, int K, int V>
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_vgrads_kernel(BwdArgs a) {
-    constexpr int JS = VgLds<K>::JS, LJ = VgLds<K>::LJ, KT = K / 16, NOWN = NP * KT / 4, SL = VgLds<K>::SL;
-    constexpr int KP = (K * 4 + NTH - 1) / NTH;  // 4-column groups of the K x 16 slices per thread
+__global__ __launch_bounds__(VNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_vgrads_kernel(BwdArgs a) {
+    constexpr int JS = VgLds<K>::JS, LJ = VgLds<K>::LJ, KT = K / 16, SL = VgLds<K>::SL;
+    constexpr int NCK = NP * KT, NOWN = (NCK + VNW - 1) / VNW;  // C x K tiles, per wave
+    constexpr int KP = (K * 4 + VNT - 1) / VNT;  // 4-column groups of the K x 16 slices per thread
+    static_assert(NP == 4, "four 16-row tiles per chunk");
     extern __shared__ __align__(16) unsigned char smem[];
     // slice buffer b: S [K][16], dS' [K][16], scale dO [C][16], Vt [C][16], dVt [C][16], v [C][16]
     constexpr int oDH = K * LJ, oO = 2 * K * LJ, oVt = oO + BC * LJ, odVt = oVt + BC * LJ, oVr = odVt + BC * LJ;
@@ -835,7 +853,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float *sTt = sT + BC * LDC;                    // T^T [C][C]: the A operand of the T^T products
     float *sB = sTt + BC * LDC;                    // beta
     float *sRs = sB + BC;                          // partial rowsum(S dS')
-    float *sRv = sRs + NTH;                        // [C] rowsum(V T^T dVt)
+    float *sRv = sRs + VNT;                        // [C] rowsum(V T^T dVt)
     float *sRk = sRv + BC;                         // [K/16][C] partial rowsum(K e^Gamma dBk)
     float *sRa = sRk + KT * BC;                    // [NP][C] partial rowsum(dA Abar)
     const int n = blockIdx.x, h = blockIdx.y, H = a.H;
@@ -843,52 +861,57 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (cp.L == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, i16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+    const int wq = w & 3, wh = w >> 2;                        // C x C tiles: column tile, row parity
     const int64_t sh = (int64_t)n * H + h;
     const TIn *v = static_cast<const TIn *>(a.v);
     const float *hp = a.w.h + sh * K * V, *dhp = a.w.dh + sh * K * V;
     const float *Vtp = a.w.Vt + sh * BC * V, *dVtp = a.w.dVt + sh * BC * V, *Tm = a.w.Tm + sh * BC * BC;
 
-    float4 rh[KP], rdh[KP], ro, rvt, rdvt, rv;
-    const int sr = tid >> 2, sg = 4 * (tid & 3);  // staging: row and first column of this thread's group
+    // slice staging: K x 16 of S and dS' in 16-byte groups, C x 16 of dO, Vt, dVt, v in
+    // 8-byte pairs (row tid / 8, columns 2 (tid % 8) + 0, 1)
+    float4 rh[KP], rdh[KP];
+    float2 ro, rvt, rdvt, rv;
+    const int sr = tid >> 3, sg = 2 * (tid & 7);
     const int64_t tok = ((cp.t0 + crow(sr, cp.L)) * H + h) * V + sg;
     auto load = [&](int j0) {
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
-            const int idx = min(tid + NTH * i, K * 4 - 1);
+            const int idx = min(tid + VNT * i, K * 4 - 1);
             const int c = idx >> 2, g = 4 * (idx & 3);
             rh[i] = ld4(hp + c * V + j0 + g);
             rdh[i] = ld4(dhp + c * V + j0 + g);
         }
-        rvt = ld4(Vtp + sr * V + j0 + sg);
-        rdvt = ld4(dVtp + sr * V + j0 + sg);
-        ro = ld4_any(a.d_out, a.dout_bf16, tok + j0);  // masked past the chunk when stored
-        rv = ld4(v + tok + j0);
+        rvt = ld2(Vtp + sr * V + j0 + sg);
+        rdvt = ld2(dVtp + sr * V + j0 + sg);
+        ro = ld2_any(a.d_out, a.dout_bf16, tok + j0);  // masked past the chunk when stored
+        rv = ld2(v + tok + j0);
     };
     auto store = [&](float *sb) {
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
-            const int idx = tid + NTH * i;
+            const int idx = tid + VNT * i;
             if (idx < K * 4) {
                 const int c = idx >> 2, g = 4 * (idx & 3);
                 st4(sb + c * LJ + g, rh[i]);
                 st4(sb + oDH + c * LJ + g, rdh[i]);
             }
         }
-        const float sc = sr < cp.L ? a.scale : 0.f;
-        st4(sb + oO + sr * LJ + sg, make_float4(sc * ro.x, sc * ro.y, sc * ro.z, sc * ro.w));
-        st4(sb + oVt + sr * LJ + sg, rvt);
-        st4(sb + odVt + sr * LJ + sg, rdvt);
-        st4(sb + oVr + sr * LJ + sg, mask4(rv, sr < cp.L));
+        const bool ok = sr < cp.L;
+        const float sc = ok ? a.scale : 0.f;
+        st2(sb + oO + sr * LJ + sg, make_float2(sc * ro.x, sc * ro.y));
+        st2(sb + oVt + sr * LJ + sg, rvt);
+        st2(sb + odVt + sr * LJ + sg, rdvt);
+        st2(sb + oVr + sr * LJ + sg, ok ? rv : make_float2(0.f, 0.f));
     };
 
     load(0);
     {
-        float4 x[BC * BC / 4 / NTH];
+        float4 x[BC * BC / 4 / VNT];
 #pragma unroll
-        for (int i = 0; i < BC * BC / 4 / NTH; ++i) x[i] = ld4(Tm + 4 * (tid + NTH * i));
+        for (int i = 0; i < BC * BC / 4 / VNT; ++i) x[i] = ld4(Tm + 4 * (tid + VNT * i));
 #pragma unroll
-        for (int i = 0; i < BC * BC / 4 / NTH; ++i) {
-            const int e = 4 * (tid + NTH * i), r = e / BC, c = e % BC;
+        for (int i = 0; i < BC * BC / 4 / VNT; ++i) {
+            const int e = 4 * (tid + VNT * i), r = e / BC, c = e % BC;
             st4(sT + r * LDC + c, x[i]);
             sTt[c * LDC + r] = x[i].x;
             sTt[(c + 1) * LDC + r] = x[i].y;
@@ -900,13 +923,14 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     store(reinterpret_cast<float *>(smem));
     lds_barrier();
 
-    f4 ps[NOWN], pw[NOWN], pd[NOWN], ma[4], mt[4];
+    f4 ps[NOWN], pw[NOWN], pd[NOWN], ma[2], mt[2];
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) ps[i] = pw[i] = pd[i] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ma[i] = mt[i] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2; ++i) ma[i] = mt[i] = f4{0.f, 0.f, 0.f, 0.f};
     float dbacc[4] = {0.f, 0.f, 0.f, 0.f}, rsacc = 0.f;
-    constexpr int PARTS = NTH / K, CW = JS / PARTS;  // rowsum(S dS'): threads per key row, columns each
+    // rowsum(S dS'): PARTS threads per key row, CW columns each
+    constexpr int PARTS = VNT / K < 16 ? VNT / K : 16, CW = JS / PARTS;
 
     for (int js = 0; js < V / JS; ++js) {
         float *sb = reinterpret_cast<float *>(smem) + (js & 1) * SL;
@@ -914,39 +938,29 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool more = js + 1 < V / JS;
         if (more) load((js + 1) * JS);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products they overlap
-        // Operands of T^T dVt (below), read first so that they arrive during the products.
-        // k = s = 16 m + 4 (lane/16) + u over every m: the blocks m < p of T^T are zero, and
-        // the wave with p = 0, which needs them all, sets the pace anyway.
+        // Operands of T^T dVt (waves 0..3, below), read first so that they arrive during the
+        // products.  k = s = 16 m + 4 (lane/16) + u over every m: the blocks m < p of T^T
+        // are zero, and the wave with p = 0, which needs them all, sets the pace anyway.
         float4 at[NP];
         float bt[NP][4], bs[4], vr[4];
+        const int pt = wq;  // row tile of T^T dVt (used by waves 0..3)
 #pragma unroll
         for (int m = 0; m < NP; ++m) {
-            at[m] = *reinterpret_cast<const float4 *>(sTt + (16 * w + i16) * LDC + 16 * m + 4 * g4);
+            at[m] = *reinterpret_cast<const float4 *>(sTt + (16 * pt + i16) * LDC + 16 * m + 4 * g4);
 #pragma unroll
             for (int u = 0; u < 4; ++u) bt[m][u] = sdVt[(16 * m + 4 * g4 + u) * LJ + i16];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            bs[e] = sB[16 * w + 4 * g4 + e];
-            vr[e] = sVr[(16 * w + 4 * g4 + e) * LJ + i16];
+            bs[e] = sB[16 * pt + 4 * g4 + e];
+            vr[e] = sVr[(16 * pt + 4 * g4 + e) * LJ + i16];
         }
         __builtin_amdgcn_sched_barrier(0);  // keep these reads here, ahead of the products
         // dO S^T, dVt S^T, Vt dS'^T on this wave's C x K tiles and dO Vt^T, dVt V^T on its
         // C x C tiles.  The slice's 16-wide reduction is split as k = 4*(lane/16) + s on both
         // operands, so one 16-byte LDS read per operand feeds four matrix-core steps.
-        if constexpr (KT % 4 == 0) {
-            // Row tile p's fragments of dO, Vt and dVt feed this wave's KT/4 C x K tiles
-            // (column tiles w + 4c) and its C x C tile (p, w); the next row tile's fragments
-            // are read while the current one's products run.
-            constexpr int CT = KT / 4;
-            float4 bh[CT], bdh[CT];
-#pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                const int rb = (16 * (w + 4 * c) + i16) * LJ + 4 * g4;
-                bh[c] = *reinterpret_cast<const float4 *>(sH + rb);
-                bdh[c] = *reinterpret_cast<const float4 *>(sDH + rb);
-            }
-            const int rq = (16 * w + i16) * LJ + 4 * g4;
+        {
+            const int rq = (16 * wq + i16) * LJ + 4 * g4;
             const float4 bvt = *reinterpret_cast<const float4 *>(sVt + rq);
             const float4 bv = *reinterpret_cast<const float4 *>(sVr + rq);
             float4 fa[2][3];
@@ -956,80 +970,93 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 f[1] = *reinterpret_cast<const float4 *>(sVt + ra);
                 f[2] = *reinterpret_cast<const float4 *>(sdVt + ra);
             };
-            frag(0, fa[0]);
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                if (p + 1 < NP) frag(p + 1, fa[(p + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);  // the next row tile's reads go out first
-                const float4 ao = fa[p & 1][0], avt = fa[p & 1][1], adv = fa[p & 1][2];
+            if constexpr (KT % VNW == 0) {
+                // Column tiles w + 8 c of every row tile p: row tile p's fragments of dO, Vt and
+                // dVt serve them all and, when p = 2 i + w/4, the C x C tile (p, w % 4); the next
+                // row tile's fragments are read while the current one's products run.
+                constexpr int CT = KT / VNW;
+                float4 bh[CT], bdh[CT];
 #pragma unroll
                 for (int c = 0; c < CT; ++c) {
-                    const int i = p * CT + c;  // tile w + 4 i: row tile p, column tile w + 4 c
-                    ps[i] = mf(ao.x, bh[c].x, ps[i]); pw[i] = mf(adv.x, bh[c].x, pw[i]); pd[i] = mf(avt.x, bdh[c].x, pd[i]);
-                    ps[i] = mf(ao.y, bh[c].y, ps[i]); pw[i] = mf(adv.y, bh[c].y, pw[i]); pd[i] = mf(avt.y, bdh[c].y, pd[i]);
-                    ps[i] = mf(ao.z, bh[c].z, ps[i]); pw[i] = mf(adv.z, bh[c].z, pw[i]); pd[i] = mf(avt.z, bdh[c].z, pd[i]);
-                    ps[i] = mf(ao.w, bh[c].w, ps[i]); pw[i] = mf(adv.w, bh[c].w, pw[i]); pd[i] = mf(avt.w, bdh[c].w, pd[i]);
+                    const int rb = (16 * (w + VNW * c) + i16) * LJ + 4 * g4;
+                    bh[c] = *reinterpret_cast<const float4 *>(sH + rb);
+                    bdh[c] = *reinterpret_cast<const float4 *>(sDH + rb);
                 }
-                ma[p] = mf(ao.x, bvt.x, ma[p]); mt[p] = mf(adv.x, bv.x, mt[p]);
-                ma[p] = mf(ao.y, bvt.y, ma[p]); mt[p] = mf(adv.y, bv.y, mt[p]);
-                ma[p] = mf(ao.z, bvt.z, ma[p]); mt[p] = mf(adv.z, bv.z, mt[p]);
-                ma[p] = mf(ao.w, bvt.w, ma[p]); mt[p] = mf(adv.w, bv.w, mt[p]);
-            }
-        } else {
+                frag(0, fa[0]);
 #pragma unroll
-            for (int i = 0; i < NOWN; ++i) {
-                const int t = w + 4 * i, p = t / KT, ct = t % KT;
-                const int ra = (16 * p + i16) * LJ + 4 * g4, rb = (16 * ct + i16) * LJ + 4 * g4;
-                const float4 ao = *reinterpret_cast<const float4 *>(sO + ra);
-                const float4 avt = *reinterpret_cast<const float4 *>(sVt + ra);
-                const float4 adv = *reinterpret_cast<const float4 *>(sdVt + ra);
-                const float4 bh = *reinterpret_cast<const float4 *>(sH + rb);
-                const float4 bdh = *reinterpret_cast<const float4 *>(sDH + rb);
-                ps[i] = mf(ao.x, bh.x, ps[i]); pw[i] = mf(adv.x, bh.x, pw[i]); pd[i] = mf(avt.x, bdh.x, pd[i]);
-                ps[i] = mf(ao.y, bh.y, ps[i]); pw[i] = mf(adv.y, bh.y, pw[i]); pd[i] = mf(avt.y, bdh.y, pd[i]);
-                ps[i] = mf(ao.z, bh.z, ps[i]); pw[i] = mf(adv.z, bh.z, pw[i]); pd[i] = mf(avt.z, bdh.z, pd[i]);
-                ps[i] = mf(ao.w, bh.w, ps[i]); pw[i] = mf(adv.w, bh.w, pw[i]); pd[i] = mf(avt.w, bdh.w, pd[i]);
-            }
+                for (int p = 0; p < NP; ++p) {
+                    if (p + 1 < NP) frag(p + 1, fa[(p + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);  // the next row tile's reads go out first
+                    const float4 ao = fa[p & 1][0], avt = fa[p & 1][1], adv = fa[p & 1][2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = w + 4 * i, p = t / NP, qt = t % NP;
-                const int ra = (16 * p + i16) * LJ + 4 * g4, rb = (16 * qt + i16) * LJ + 4 * g4;
-                const float4 ao = *reinterpret_cast<const float4 *>(sO + ra);
-                const float4 adv = *reinterpret_cast<const float4 *>(sdVt + ra);
-                const float4 bvt = *reinterpret_cast<const float4 *>(sVt + rb);
-                const float4 bv = *reinterpret_cast<const float4 *>(sVr + rb);
-                ma[i] = mf(ao.x, bvt.x, ma[i]); mt[i] = mf(adv.x, bv.x, mt[i]);
-                ma[i] = mf(ao.y, bvt.y, ma[i]); mt[i] = mf(adv.y, bv.y, mt[i]);
-                ma[i] = mf(ao.z, bvt.z, ma[i]); mt[i] = mf(adv.z, bv.z, mt[i]);
-                ma[i] = mf(ao.w, bvt.w, ma[i]); mt[i] = mf(adv.w, bv.w, mt[i]);
+                    for (int c = 0; c < CT; ++c) {
+                        const int i = p * CT + c;  // tile w + 8 i: row tile p, column tile w + 8 c
+                        ps[i] = mf(ao.x, bh[c].x, ps[i]); pw[i] = mf(adv.x, bh[c].x, pw[i]); pd[i] = mf(avt.x, bdh[c].x, pd[i]);
+                        ps[i] = mf(ao.y, bh[c].y, ps[i]); pw[i] = mf(adv.y, bh[c].y, pw[i]); pd[i] = mf(avt.y, bdh[c].y, pd[i]);
+                        ps[i] = mf(ao.z, bh[c].z, ps[i]); pw[i] = mf(adv.z, bh[c].z, pw[i]); pd[i] = mf(avt.z, bdh[c].z, pd[i]);
+                        ps[i] = mf(ao.w, bh[c].w, ps[i]); pw[i] = mf(adv.w, bh[c].w, pw[i]); pd[i] = mf(avt.w, bdh[c].w, pd[i]);
+                    }
+                    if ((p & 1) == wh) {
+                        const int i = p >> 1;
+                        ma[i] = mf(ao.x, bvt.x, ma[i]); mt[i] = mf(adv.x, bv.x, mt[i]);
+                        ma[i] = mf(ao.y, bvt.y, ma[i]); mt[i] = mf(adv.y, bv.y, mt[i]);
+                        ma[i] = mf(ao.z, bvt.z, ma[i]); mt[i] = mf(adv.z, bv.z, mt[i]);
+                        ma[i] = mf(ao.w, bvt.w, ma[i]); mt[i] = mf(adv.w, bv.w, mt[i]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NOWN; ++i) {
+                    const int t = w + VNW * i;
+                    if (t < NCK) {
+                        const int p = t / KT, ct = t % KT;
+                        const int rb = (16 * ct + i16) * LJ + 4 * g4;
+                        frag(p, fa[0]);
+                        const float4 ao = fa[0][0], avt = fa[0][1], adv = fa[0][2];
+                        const float4 bh = *reinterpret_cast<const float4 *>(sH + rb);
+                        const float4 bdh = *reinterpret_cast<const float4 *>(sDH + rb);
+                        ps[i] = mf(ao.x, bh.x, ps[i]); pw[i] = mf(adv.x, bh.x, pw[i]); pd[i] = mf(avt.x, bdh.x, pd[i]);
+                        ps[i] = mf(ao.y, bh.y, ps[i]); pw[i] = mf(adv.y, bh.y, pw[i]); pd[i] = mf(avt.y, bdh.y, pd[i]);
+                        ps[i] = mf(ao.z, bh.z, ps[i]); pw[i] = mf(adv.z, bh.z, pw[i]); pd[i] = mf(avt.z, bdh.z, pd[i]);
+                        ps[i] = mf(ao.w, bh.w, ps[i]); pw[i] = mf(adv.w, bh.w, pw[i]); pd[i] = mf(avt.w, bdh.w, pd[i]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    frag(2 * i + wh, fa[1]);
+                    const float4 ao = fa[1][0], adv = fa[1][2];
+                    ma[i] = mf(ao.x, bvt.x, ma[i]); mt[i] = mf(adv.x, bv.x, mt[i]);
+                    ma[i] = mf(ao.y, bvt.y, ma[i]); mt[i] = mf(adv.y, bv.y, mt[i]);
+                    ma[i] = mf(ao.z, bvt.z, ma[i]); mt[i] = mf(adv.z, bv.z, mt[i]);
+                    ma[i] = mf(ao.w, bvt.w, ma[i]); mt[i] = mf(adv.w, bv.w, mt[i]);
+                }
             }
         }
-        // T^T dVt on row tile p = w of this slice: dv = beta T^T dVt, rowsum(V T^T dVt) for
-        // dbeta (even and odd k blocks in two accumulators, so the products overlap)
-        {
-            const int p = w;
+        // T^T dVt on row tile p = w of this slice (waves 0..3): dv = beta T^T dVt,
+        // rowsum(V T^T dVt) for dbeta (even and odd k blocks in two accumulators)
+        if (w < 4) {
             f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NP; m += 2) {
                 acc0 = mf(at[m].x, bt[m][0], acc0);
-                if (m + 1 < NP) acc1 = mf(at[m + 1].x, bt[m + 1][0], acc1);
+                acc1 = mf(at[m + 1].x, bt[m + 1][0], acc1);
                 acc0 = mf(at[m].y, bt[m][1], acc0);
-                if (m + 1 < NP) acc1 = mf(at[m + 1].y, bt[m + 1][1], acc1);
+                acc1 = mf(at[m + 1].y, bt[m + 1][1], acc1);
                 acc0 = mf(at[m].z, bt[m][2], acc0);
-                if (m + 1 < NP) acc1 = mf(at[m + 1].z, bt[m + 1][2], acc1);
+                acc1 = mf(at[m + 1].z, bt[m + 1][2], acc1);
                 acc0 = mf(at[m].w, bt[m][3], acc0);
-                if (m + 1 < NP) acc1 = mf(at[m + 1].w, bt[m + 1][3], acc1);
+                acc1 = mf(at[m + 1].w, bt[m + 1][3], acc1);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = 16 * p + 4 * g4 + e;
+                const int row = 16 * pt + 4 * g4 + e;
                 const float x = acc0[e] + acc1[e];
                 if (row < cp.L)
                     st_out(a.dv, a.grad_bf16, ((cp.t0 + row) * H + h) * V + js * JS + i16, bs[e] * x);
                 dbacc[e] += vr[e] * x;  // summed over the row's lanes at the end
             }
         }
-        {
+        if (tid < K * PARTS) {
             const int c = tid % K, part = tid / K;
 #pragma unroll
             for (int j = 0; j < CW; ++j) rsacc += sH[c * LJ + part * CW + j] * sDH[c * LJ + part * CW + j];
@@ -1045,60 +1072,63 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float *sM = sKg + BC * LK;                     // [C][C] beta MT, then Y = dT T^T
     float *sY = sM + BC * LDC;                     // [C][C] dT
     const float *Kg = a.w.Kg + sh * BC * K, *Abar = a.w.Abar + sh * BC * BC;
-    float abr[4][4];  // Abar on this wave's C x C tiles, for rowsum(dA Abar)
+    float abr[2][4];  // Abar on this wave's C x C tiles, for rowsum(dA Abar)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = w + 4 * i, p = t / NP, qt = t % NP;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) abr[i][e] = Abar[(16 * p + 4 * g4 + e) * BC + 16 * qt + i16];
-    }
-    float4 kg4[(BC * K / 4 + NTH - 1) / NTH];
+        for (int e = 0; e < 4; ++e) abr[i][e] = Abar[(16 * (2 * i + wh) + 4 * g4 + e) * BC + 16 * wq + i16];
+    constexpr int NKG = (BC * K / 4 + VNT - 1) / VNT;
+    float4 kg4[NKG];
 #pragma unroll
-    for (int i = 0; i < (BC * K / 4 + NTH - 1) / NTH; ++i) {
-        const int idx = tid + NTH * i;
-        if (idx < BC * K / 4) kg4[i] = ld4(Kg + 4 * idx);
-    }
+    for (int i = 0; i < NKG; ++i) kg4[i] = ld4(Kg + 4 * min(tid + VNT * i, BC * K / 4 - 1));
     float *PS = a.w.PS + sh * BC * K, *PdK = a.w.PdK + sh * BC * K, *MA = a.w.MA + sh * BC * BC;
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
-        const int t = w + 4 * i, p = t / KT, ct = t % KT, c = 16 * ct + i16;
+        const int t = w + VNW * i;
+        if (t < NCK) {
+            const int p = t / KT, c = 16 * (t % KT) + i16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * g4 + e;
-            PS[row * K + c] = ps[i][e];
-            PdK[row * K + c] = pd[i][e];
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * p + 4 * g4 + e;
+                PS[row * K + c] = ps[i][e];
+                PdK[row * K + c] = pd[i][e];
+            }
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) MA[(16 * p + 4 * g4 + e) * BC + s] = ma[i][e];
-    }
+        for (int e = 0; e < 4; ++e) MA[(16 * (2 * i + wh) + 4 * g4 + e) * BC + 16 * wq + i16] = ma[i][e];
+    if (w < 4) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dbacc[e] = row16_sum(dbacc[e]);
-    if (i16 == 0) {
+        for (int e = 0; e < 4; ++e) dbacc[e] = row16_sum(dbacc[e]);
+        if (i16 == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sRv[16 * w + 4 * g4 + e] = dbacc[e];
+            for (int e = 0; e < 4; ++e) sRv[16 * w + 4 * g4 + e] = dbacc[e];
+        }
     }
     sRs[tid] = rsacc;
     lds_barrier();  // every wave is past the slices
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
-        const int t = w + 4 * i, p = t / KT, ct = t % KT, c = 16 * ct + i16;
+        const int t = w + VNW * i;
+        if (t < NCK) {
+            const int p = t / KT, c = 16 * (t % KT) + i16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sPW[(16 * p + 4 * g4 + e) * LK + c] = pw[i][e];
+            for (int e = 0; e < 4; ++e) sPW[(16 * p + 4 * g4 + e) * LK + c] = pw[i][e];
+        }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = w + 4 * i, p = t / NP, qt = t % NP, s = 16 * qt + i16;
+    {
+        const int s = 16 * wq + i16;
         const float bs = sB[s];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sM[(16 * p + 4 * g4 + e) * LDC + s] = bs * mt[i][e];
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sM[(16 * (2 * i + wh) + 4 * g4 + e) * LDC + s] = bs * mt[i][e];
     }
 #pragma unroll
-    for (int i = 0; i < (BC * K / 4 + NTH - 1) / NTH; ++i) {
-        const int idx = tid + NTH * i;
+    for (int i = 0; i < NKG; ++i) {
+        const int idx = tid + VNT * i;
         if (idx < BC * K / 4) {
             const int r = (4 * idx) / K, c = (4 * idx) % K;
             st4(sKg + r * LK + c, kg4[i]);
@@ -1110,43 +1140,39 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         a.w.rs[sh * K + tid] = acc;
     }
     lds_barrier();
-    // The C x C tiles w + 4 i of a wave are row tile i, column tile w; the products below
-    // run the wave's tiles side by side (independent accumulators) and share the operand
-    // that does not depend on the tile.
-    static_assert(NP == 4, "four 16-row tiles per chunk");
+    // The C x C tiles of a wave share their column tile w % 4; the products below run the
+    // two tiles side by side and share the operand of that column tile.
     // dT = MT + dW (beta K e^Gamma)^T with dW = -PW (beta_s applied to the column)
     {
-        f4 acc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-        const float *br = sKg + (16 * w + i16) * LK + 4 * g4;
+        f4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const float *br = sKg + (16 * wq + i16) * LK + 4 * g4;
 #pragma unroll 2
         for (int c0 = 0; c0 < K; c0 += 16) {
             const float4 y = *reinterpret_cast<const float4 *>(br + c0);
-            float4 x[4];
+            float4 x[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const float4 *>(sPW + (16 * i + i16) * LK + 4 * g4 + c0);
+            for (int i = 0; i < 2; ++i)
+                x[i] = *reinterpret_cast<const float4 *>(sPW + (16 * (2 * i + wh) + i16) * LK + 4 * g4 + c0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].x, y.x, acc[i]);
+            for (int i = 0; i < 2; ++i) acc[i] = mf(x[i].x, y.x, acc[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].y, y.y, acc[i]);
+            for (int i = 0; i < 2; ++i) acc[i] = mf(x[i].y, y.y, acc[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].z, y.z, acc[i]);
+            for (int i = 0; i < 2; ++i) acc[i] = mf(x[i].z, y.z, acc[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].w, y.w, acc[i]);
+            for (int i = 0; i < 2; ++i) acc[i] = mf(x[i].w, y.w, acc[i]);
         }
-        const int s = 16 * w + i16;
+        const int s = 16 * wq + i16;
         const float bs = sB[s];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = 16 * i + 4 * g4 + e;
+                const int row = 16 * (2 * i + wh) + 4 * g4 + e;
                 sY[row * LDC + s] = sM[row * LDC + s] - bs * acc[i][e];
             }
     }
     // dBk = T^T dW = -T^T PW on this wave's C x K tiles; rowsum(K e^Gamma dBk) for dbeta.
-    // With K/16 a multiple of 4 the row tile of tile w + 4 i does not depend on the wave.
     float *dBk = a.w.PW + sh * BC * K;
     {
         f4 acc[NOWN];
@@ -1156,8 +1182,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int m = 0; m < NP; ++m) {
 #pragma unroll
             for (int i = 0; i < NOWN; ++i) {
-                const int t = w + 4 * i, p = KT % 4 == 0 ? (4 * i) / KT : t / KT, c = 16 * (t % KT) + i16;
-                if (m >= p) {
+                const int t = w + VNW * i, p = KT % VNW == 0 ? (VNW * i) / KT : t / KT, c = 16 * (t % KT) + i16;
+                if (t < NCK && m >= p) {
                     const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
                     const float *br = sPW + (16 * m + 4 * g4) * LK + c;
                     acc[i] = mf(at.x, br[0], acc[i]);
@@ -1169,74 +1195,76 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
 #pragma unroll
         for (int i = 0; i < NOWN; ++i) {
-            const int t = w + 4 * i, p = KT % 4 == 0 ? (4 * i) / KT : t / KT, ct = t % KT, c = 16 * ct + i16;
+            const int t = w + VNW * i;
+            if (t < NCK) {
+                const int p = t / KT, ct = t % KT, c = 16 * ct + i16;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * p + 4 * g4 + e;
-                dBk[row * K + c] = -acc[i][e];
-                const float part = row16_sum(-acc[i][e] * sKg[row * LK + c]);
-                if (i16 == 0) sRk[ct * BC + row] = part;
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * p + 4 * g4 + e;
+                    dBk[row * K + c] = -acc[i][e];
+                    const float part = row16_sum(-acc[i][e] * sKg[row * LK + c]);
+                    if (i16 == 0) sRk[ct * BC + row] = part;
+                }
             }
         }
     }
     lds_barrier();
     // Y = dT T^T
     {
-        f4 acc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-        const float *br = sT + (16 * w + i16) * LDC + 4 * g4;
+        f4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const float *br = sT + (16 * wq + i16) * LDC + 4 * g4;
 #pragma unroll
         for (int j0 = 0; j0 < BC; j0 += 16) {
             const float4 y = *reinterpret_cast<const float4 *>(br + j0);
-            float4 x[4];
+            float4 x[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const float4 *>(sY + (16 * i + i16) * LDC + 4 * g4 + j0);
+            for (int i = 0; i < 2; ++i)
+                x[i] = *reinterpret_cast<const float4 *>(sY + (16 * (2 * i + wh) + i16) * LDC + 4 * g4 + j0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].x, y.x, acc[i]);
+            for (int i = 0; i < 2; ++i) acc[i] = mf(x[i].x, y.x, acc[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].y, y.y, acc[i]);
+            for (int i = 0; i < 2; ++i) acc[i] = mf(x[i].y, y.y, acc[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].z, y.z, acc[i]);
+            for (int i = 0; i < 2; ++i) acc[i] = mf(x[i].z, y.z, acc[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mf(x[i].w, y.w, acc[i]);
+            for (int i = 0; i < 2; ++i) acc[i] = mf(x[i].w, y.w, acc[i]);
         }
-        const int s = 16 * w + i16;
+        const int s = 16 * wq + i16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sM[(16 * i + 4 * g4 + e) * LDC + s] = acc[i][e];
+            for (int e = 0; e < 4; ++e) sM[(16 * (2 * i + wh) + 4 * g4 + e) * LDC + s] = acc[i][e];
     }
     lds_barrier();
     // dA = -strict_tril(T^T Y); rowsum(dA Abar) for dbeta; beta dA is what the key space needs
     float *dAb = a.w.MT + sh * BC * BC;
     {
-        f4 acc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-        const int s = 16 * w + i16;
+        f4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const int s = 16 * wq + i16;
 #pragma unroll
         for (int m = 0; m < NP; ++m) {
             const float *br = sM + (16 * m + 4 * g4) * LDC + s;
             const float b0 = br[0], b1 = br[LDC], b2 = br[2 * LDC], b3 = br[3 * LDC];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (w <= i && i <= m) {  // tiles on or below the diagonal; T^T is upper
-                    const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * i + i16) * LDC + 16 * m + 4 * g4);
+            for (int i = 0; i < 2; ++i) {
+                const int p = 2 * i + wh;
+                if (wq <= p && p <= m) {  // tiles on or below the diagonal; T^T is upper
+                    const float4 at = *reinterpret_cast<const float4 *>(sTt + (16 * p + i16) * LDC + 16 * m + 4 * g4);
                     acc[i] = mf(at.x, b0, acc[i]);
                     acc[i] = mf(at.y, b1, acc[i]);
                     acc[i] = mf(at.z, b2, acc[i]);
                     acc[i] = mf(at.w, b3, acc[i]);
                 }
+            }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = 16 * i + 4 * g4 + e;
+                const int row = 16 * (2 * i + wh) + 4 * g4 + e;
                 const float da = row > s ? -acc[i][e] : 0.f;
                 const float part = row16_sum(da * abr[i][e]);
-                if (i16 == 0) sRa[w * BC + row] = part;
+                if (i16 == 0) sRa[wq * BC + row] = part;
                 dAb[row * BC + s] = sB[row] * da;
             }
     }
@@ -1545,7 +1573,7 @@ hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
     hipLaunchKernelGGL(kprep, gpp, dim3(NTH), prep_bytes, stream, a);
     hipLaunchKernelGGL((bwd_states_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL((bwd_dstates_kernel<K, V>), gd, dim3(NTH), 0, stream, a);
-    hipLaunchKernelGGL(kvg, gp, dim3(NTH), VgLds<K>::bytes, stream, a);
+    hipLaunchKernelGGL(kvg, gp, dim3(VNT), VgLds<K>::bytes, stream, a);
     hipLaunchKernelGGL(kkg, gk, dim3(NTH), KgLds<K>::bytes, stream, a);
     return hipGetLastError();
 }
