@@ -194,13 +194,14 @@ struct PrepLds {
 };
 
 // Persistent: workgroup b takes the (chunk slot, head) units b, b + G, b + 2G, ... (G the
-// grid size, one workgroup per CU: LDS allows no more) and loads the next unit's q, k, gate
-// and beta while it processes the current one.
+// grid size, one workgroup of eight waves per CU: LDS allows no more) and loads the next
+// unit's q, k, gate and beta while it processes the current one.
+constexpr int PNW = 8, PNT = 64 * PNW;  // prep waves and threads
 template <typename TIn, int K, int V>
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(PNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_prep_kernel(BwdArgs a) {
     constexpr int LK = PrepLds<K, V>::LK, LW = PrepLds<K, V>::LW, LV = PrepLds<K, V>::LV;
-    constexpr int NV4 = (BC * V / 4 + NTH - 1) / NTH;  // float4 groups of v per thread
-    constexpr int NK4 = (BC * K / 4 + NTH - 1) / NTH;  // float4 groups of a C x K tile per thread
+    constexpr int NV4 = (BC * V / 4 + PNT - 1) / PNT;  // float4 groups of v per thread
+    constexpr int NK4 = (BC * K / 4 + PNT - 1) / PNT;  // float4 groups of a C x K tile per thread
     extern __shared__ __align__(16) unsigned char smem[];
     float *sQ = reinterpret_cast<float *>(smem);     // q
     float *sK = sQ + BC * LK;                          // k
@@ -220,7 +221,6 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int units = a.slots * H;  // below 2^31 (checked by the host)
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
     const TIn *v = static_cast<const TIn *>(a.v);
-    static_assert(BC * K / 4 % NTH == 0 && BC * V / 4 % NTH == 0, "whole float4 groups per thread");
     // q, k, gate and beta of the next unit (four elements per load; rows past the chunk
     // read its last row and are masked when stored), kept in the input format until then
     using Raw4 = typename std::conditional<std::is_same<TIn, float>::value, float4, s16x4>::type;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (c.L == 0) c = ChunkPos{0, 1};
 #pragma unroll
         for (int i = 0; i < NK4; ++i) {
-            const int idx = tid + NTH * i, r = (4 * idx) / K, col = (4 * idx) % K;
+            const int idx = min(tid + PNT * i, BC * K / 4 - 1), r = (4 * idx) / K, col = (4 * idx) % K;
             const int64_t gi = ((c.t0 + crow(r, c.L)) * H + h) * K + col;
             rq[i] = *reinterpret_cast<const Raw4 *>(q + gi);
             rk[i] = *reinterpret_cast<const Raw4 *>(k + gi);
@@ -266,15 +266,17 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     Raw4 rv[NV4];  // this chunk's v, in flight (in the input format) until U is formed
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
-        const int idx = tid + NTH * i, r = (4 * idx) / V, c = (4 * idx) % V;
+        const int idx = min(tid + PNT * i, BC * V / 4 - 1), r = (4 * idx) / V, c = (4 * idx) % V;
         rv[i] = *reinterpret_cast<const Raw4 *>(v + ((cp.t0 + crow(r, cp.L)) * H + h) * V + c);
     }
 #pragma unroll
     for (int i = 0; i < NK4; ++i) {  // rows past the chunk: no token, no decay
-        const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
-        st4(sQ + r * LK + c, mask4(raw_f4(rq[i]), r < cp.L));
-        st4(sK + r * LK + c, mask4(raw_f4(rk[i]), r < cp.L));
-        st4(sG + r * LK + c, gate_log4(a.gate, rg[i], r < cp.L));
+        const int idx = tid + PNT * i, r = (4 * idx) / K, c = (4 * idx) % K;
+        if (idx < BC * K / 4) {
+            st4(sQ + r * LK + c, mask4(raw_f4(rq[i]), r < cp.L));
+            st4(sK + r * LK + c, mask4(raw_f4(rk[i]), r < cp.L));
+            st4(sG + r * LK + c, gate_log4(a.gate, rg[i], r < cp.L));
+        }
     }
     if (tid < BC) sB[tid] = tid < cp.L ? rb : 0.f;
     lds_barrier();
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         a.w.gC[sh * K + tid] = expf(run);
     }
     lds_barrier();
-    for (int i = tid; i < (NP * NP + 3 * NP) * K; i += NTH) {
+    for (int i = tid; i < (NP * NP + 3 * NP) * K; i += PNT) {
         const int c = i % K, j = i / K;
         if (j < NP * NP) {
             const int pp = j / NP, qq = j % NP;
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     }
     lds_barrier();
-    for (int i = tid; i < BC * K; i += NTH) {  // F1 replaces Gamma, element by element
+    for (int i = tid; i < BC * K; i += PNT) {  // F1 replaces Gamma, element by element
         const int r = i / K, c = i % K;
         sG[r * LK + c] = exp_in_tile(sG[r * LK + c] - sMid[(r >> 4) * K + c]);
     }
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // over the waves.  Row r of tile p enters as k_r F1_r (q_r F1_r); column s of tile q as
     // k_s / F1_s * e^{m_p - m_q}; the channel axis is read four at a time.
     float *Aqk = a.w.Aqk + sh * BC * BC, *Abar = a.w.Abar + sh * BC * BC;
-    for (int t = w; t < NP * (NP + 1) / 2; t += 4) {
+    for (int t = w; t < NP * (NP + 1) / 2; t += PNW) {
         int p = 0;
         while ((p + 1) * (p + 2) / 2 <= t) ++p;
         const int qt = t - p * (p + 1) / 2;
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             Aqk[row * BC + col] = vq;
         }
     }
-    for (int i = tid; i < BC * BC; i += NTH) {  // the tiles above the diagonal are zero
+    for (int i = tid; i < BC * BC; i += PNT) {  // the tiles above the diagonal are zero
         const int r = i / BC, c = i % BC;
         if ((c >> 4) > (r >> 4)) {
             sA[r * LDC + c] = 0.f;
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float4 bkg[NK4];
 #pragma unroll
     for (int i = 0; i < NK4; ++i) {
-        const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
+        const int idx = tid + PNT * i, r = (4 * idx) / K, c = (4 * idx) % K;
         if (idx < BC * K / 4) {
             const int pp = r >> 4;
             const float4 f1 = *reinterpret_cast<const float4 *>(sF1 + r * LK + c);
@@ -425,31 +427,33 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     }
     float *Tm = a.w.Tm + sh * BC * BC;
-    for (int i = tid; i < BC * BC / 4; i += NTH) {
+    for (int i = tid; i < BC * BC / 4; i += PNT) {
         const int e = 4 * i;
         st4(Tm + e, *reinterpret_cast<const float4 *>(sT + (e / BC) * LDC + e % BC));
     }
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < NK4; ++i) {  // q, k and F1 are consumed: their LDS takes beta K e^Gamma
-        const int idx = tid + NTH * i, r = (4 * idx) / K, c = (4 * idx) % K;
+        const int idx = tid + PNT * i, r = (4 * idx) / K, c = (4 * idx) % K;
         if (idx < BC * K / 4) st4(sW + r * LW + c, bkg[i]);
     }
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {  // and beta v (beta is zero past the chunk)
-        const int idx = tid + NTH * i, r = (4 * idx) / V, c = (4 * idx) % V;
-        const float b = sB[r];
-        const float4 x = raw_f4(rv[i]);
-        st4(sBV + r * LV + c, make_float4(b * x.x, b * x.y, b * x.z, b * x.w));
+        const int idx = tid + PNT * i, r = (4 * idx) / V, c = (4 * idx) % V;
+        if (idx < BC * V / 4) {
+            const float b = sB[r];
+            const float4 x = raw_f4(rv[i]);
+            st4(sBV + r * LV + c, make_float4(b * x.x, b * x.y, b * x.z, b * x.w));
+        }
     }
     lds_barrier();
 
     // W = T (beta K e^Gamma), U = T (beta V); T is lower triangular.  Wave w owns the
-    // column tiles w, w + 4, ... of W and of U over all four row tiles, so one read of a
+    // column tiles w, w + 8, ... of W and of U over all four row tiles, so one read of a
     // T fragment serves every column tile and one B read every row tile; the reduction
     // runs in 16-row groups m with k = 16 m + 4 (lane / 16) + u, and group m only feeds
     // row tiles p >= m.
-    constexpr int NWT = (K / 16 + 3) / 4, NUT = (V / 16 + 3) / 4;
+    constexpr int NWT = (K / 16 + PNW - 1) / PNW, NUT = (V / 16 + PNW - 1) / PNW;
     float *W = a.w.W + sh * BC * K, *U = a.w.U + sh * BC * V;
     f4 aw[NP][NWT], au[NP][NUT];
 #pragma unroll
@@ -470,9 +474,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int r = 16 * m + 4 * g4 + u;
             float bw[NWT], bu[NUT];
 #pragma unroll
-            for (int i = 0; i < NWT; ++i) bw[i] = sW[r * LW + 16 * min(w + 4 * i, K / 16 - 1) + i16];
+            for (int i = 0; i < NWT; ++i) bw[i] = sW[r * LW + 16 * min(w + PNW * i, K / 16 - 1) + i16];
 #pragma unroll
-            for (int i = 0; i < NUT; ++i) bu[i] = sBV[r * LV + 16 * min(w + 4 * i, V / 16 - 1) + i16];
+            for (int i = 0; i < NUT; ++i) bu[i] = sBV[r * LV + 16 * min(w + PNW * i, V / 16 - 1) + i16];
 #pragma unroll
             for (int pp = m; pp < NP; ++pp) {
                 const float av = u == 0 ? ta[pp].x : u == 1 ? ta[pp].y : u == 2 ? ta[pp].z : ta[pp].w;
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int pp = 0; pp < NP; ++pp) {
 #pragma unroll
         for (int i = 0; i < NWT; ++i) {
-            const int ct = w + 4 * i;
+            const int ct = w + PNW * i;
             if (ct < K / 16) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) W[(16 * pp + 4 * g4 + u) * K + 16 * ct + i16] = aw[pp][i][u];
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
 #pragma unroll
         for (int i = 0; i < NUT; ++i) {
-            const int ct = w + 4 * i;
+            const int ct = w + PNW * i;
             if (ct < V / 16) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) U[(16 * pp + 4 * g4 + u) * V + 16 * ct + i16] = au[pp][i][u];
@@ -1570,7 +1574,7 @@ hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
     const dim3 gpp((unsigned)(units < num_cus() ? units : num_cus()));  // persistent prep
     const dim3 gk(8 * (K / KgLds<K>::KB) * sh8);
     constexpr size_t prep_bytes = PrepLds<K, V>::bytes;
-    hipLaunchKernelGGL(kprep, gpp, dim3(NTH), prep_bytes, stream, a);
+    hipLaunchKernelGGL(kprep, gpp, dim3(PNT), prep_bytes, stream, a);
     hipLaunchKernelGGL((bwd_states_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL((bwd_dstates_kernel<K, V>), gd, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL(kvg, gp, dim3(VNT), VgLds<K>::bytes, stream, a);
