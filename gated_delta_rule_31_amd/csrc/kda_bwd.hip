@@ -281,15 +281,32 @@ __global__ __launch_bounds__(PNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (tid < BC) sB[tid] = tid < cp.L ? rb : 0.f;
     lds_barrier();
     fetch(un, cpn);  // in flight while this unit is processed
-    if (tid < K) {
-        float run = 0.f;
-#pragma unroll 8
-        for (int r = 0; r < BC; ++r) {
-            run += sG[r * LK + tid];
-            sG[r * LK + tid] = run;
+    {
+        // Gamma: inclusive prefix sums over the chunk's rows per channel, in NSEG segments of
+        // SEG rows (each read into registers at once), offset by the earlier segments' totals
+        constexpr int NSEG = PNT / K < BC ? PNT / K : BC, SEG = BC / NSEG;
+        const int c = tid % K, sg = tid / K;
+        float x[SEG];
+        if (sg < NSEG) {
+#pragma unroll
+            for (int j = 0; j < SEG; ++j) x[j] = sG[(sg * SEG + j) * LK + c];
+#pragma unroll
+            for (int j = 1; j < SEG; ++j) x[j] += x[j - 1];
+            sA[sg * K + c] = x[SEG - 1];  // segment totals (sA is free until the A tiles)
         }
-        sE[tid] = run;
-        a.w.gC[sh * K + tid] = expf(run);
+        lds_barrier();
+        if (sg < NSEG) {
+            float off = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < NSEG - 1; ++s2)
+                if (s2 < sg) off += sA[s2 * K + c];
+#pragma unroll
+            for (int j = 0; j < SEG; ++j) sG[(sg * SEG + j) * LK + c] = x[j] + off;
+            if (sg == NSEG - 1) {
+                sE[c] = x[SEG - 1] + off;
+                a.w.gC[sh * K + c] = expf(x[SEG - 1] + off);
+            }
+        }
     }
     lds_barrier();
     for (int i = tid; i < (NP * NP + 3 * NP) * K; i += PNT) {
@@ -1378,11 +1395,27 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     }
     if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
     lds_barrier();
-    if (tid < KB) {
-        float run = 0.f;
-        for (int r = 0; r < BC; ++r) {
-            run += sF2[r * LKB + tid];
-            sF2[r * LKB + tid] = run;
+    {
+        // Gamma: inclusive prefix sums over the chunk's rows per channel, in NSEG segments of
+        // SEG rows (each read into registers at once), offset by the earlier segments' totals
+        constexpr int NSEG = NTH / KB < BC ? NTH / KB : BC, SEG = BC / NSEG;
+        const int c = tid % KB, sg = tid / KB;
+        float x[SEG];
+        if (sg < NSEG) {
+#pragma unroll
+            for (int j = 0; j < SEG; ++j) x[j] = sF2[(sg * SEG + j) * LKB + c];
+#pragma unroll
+            for (int j = 1; j < SEG; ++j) x[j] += x[j - 1];
+            sEpq[sg * KB + c] = x[SEG - 1];  // segment totals (the tables are written later)
+        }
+        lds_barrier();
+        if (sg < NSEG) {
+            float off = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < NSEG - 1; ++s2)
+                if (s2 < sg) off += sEpq[s2 * KB + c];
+#pragma unroll
+            for (int j = 0; j < SEG; ++j) sF2[(sg * SEG + j) * LKB + c] = x[j] + off;
         }
     }
     lds_barrier();
