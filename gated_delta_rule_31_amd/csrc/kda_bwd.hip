@@ -540,7 +540,7 @@ template <int K, int V>
 // (three workgroups per CU)
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3, 3))) void bwd_states_kernel(BwdArgs a) {
     constexpr int LB = SBV + 4, KQ = K / 16, NST = (K / 16 + 3) / 4;
-    __shared__ float sS[K * LB];
+    __shared__ __align__(16) float sS[K * LB];
     __shared__ float sV[BC * LB];
     int hs, vb;  // (sequence, head) unit; the value blocks of one unit share an XCD
     xcd_map(blockIdx.x, V / SBV, hs, vb);
@@ -600,9 +600,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         loadB(sh);
         lds_barrier();
         float *hp = a.w.h + sh * K * V;
-        for (int i = tid; i < K * SBV; i += NTH) {
-            const int r = i / SBV, c = i % SBV;
-            hp[r * V + j0 + c] = sS[r * LB + c];
+        for (int i = tid; i < K * SBV / 4; i += NTH) {
+            const int r = (4 * i) / SBV, c = (4 * i) % SBV;
+            st4(hp + r * V + j0 + c, *reinterpret_cast<const float4 *>(sS + r * LB + c));
         }
         {
             // two accumulators (even and odd key tiles), so consecutive products overlap
@@ -672,7 +672,7 @@ template <int K, int V>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dstates_kernel(BwdArgs a) {
     constexpr int DBV = DstCfg<V>::DBV, NCT = DstCfg<V>::NCT;
     constexpr int LB = DBV + 4, KQ = K / 16, NST = (K / 16 + 3) / 4;
-    __shared__ float sD[K * LB];
+    __shared__ __align__(16) float sD[K * LB];
     __shared__ float sO[BC * LB];
     __shared__ float sV[BC * LB];
     int hs, vb;
