@@ -1525,20 +1525,47 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     // d ln alpha per key channel: reverse in-chunk sum of the row terms, plus the chunk-end
     // terms gamma_C rowsum(S dS') and the exclusive forward sum of the Kd terms; the result
     // replaces the row terms in LDS
-    if (tid < KB) {
-        const int c = tid, gc = c0 + c;
-        float dl[BC];
-        float f = a.w.gC[sh * K + gc] * a.w.rs[sh * K + gc];
+    // (in NSEG segments of SEG rows per channel: segment sums first, then the offsets from
+    // the other segments)
+    {
+        constexpr int NSEG = NTH / KB < BC ? NTH / KB : BC, SEG = BC / NSEG;
+        float *sTot = sMA;  // [2][NSEG][KB] segment totals (tril(dO Vt^T) is consumed)
+        const int c = tid % KB, sg = tid / KB;
+        float kd[SEG], rw[SEG];
+        if (sg < NSEG) {
+            float tk = 0.f, tr = 0.f;
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
-            dl[r] = f;
-            f += sK[r * LKB + c];
+            for (int j = 0; j < SEG; ++j) {
+                kd[j] = sK[(sg * SEG + j) * LKB + c];
+                rw[j] = sQ[(sg * SEG + j) * LKB + c];
+                tk += kd[j];
+                tr += rw[j];
+            }
+            sTot[sg * KB + c] = tk;
+            sTot[(NSEG + sg) * KB + c] = tr;
         }
-        float rv = 0.f;
+        lds_barrier();
+        if (sg < NSEG) {
+            const int gc = c0 + c;
+            // forward exclusive sum of the Kd terms (from the chunk-end term), reverse
+            // inclusive sum of the row terms
+            float f = a.w.gC[sh * K + gc] * a.w.rs[sh * K + gc], rv = 0.f;
 #pragma unroll
-        for (int r = BC - 1; r >= 0; --r) {
-            rv += sQ[r * LKB + c];
-            sQ[r * LKB + c] = dl[r] + rv;
+            for (int s2 = 0; s2 < NSEG; ++s2) {
+                if (s2 < sg) f += sTot[s2 * KB + c];
+                if (s2 > sg) rv += sTot[(NSEG + s2) * KB + c];
+            }
+            float dl[SEG];
+#pragma unroll
+            for (int j = 0; j < SEG; ++j) {
+                dl[j] = f;
+                f += kd[j];
+            }
+#pragma unroll
+            for (int j = SEG - 1; j >= 0; --j) {
+                rv += rw[j];
+                sQ[(sg * SEG + j) * LKB + c] = dl[j] + rv;
+            }
         }
     }
     lds_barrier();
