@@ -25,12 +25,13 @@
 // the cheat sheet's gate table) neither factor exceeds e^40 on the kept entries.
 //
 // Five launches on one stream, all float32 on the matrix cores (16x16x4) and vector units:
-//   prep    (chunk, head)          Gamma, Abar, T (blocked 16x16 inverse), A_qk, W, U, Kd, Q e^Gamma, K e^Gamma
+//   prep    (chunk, head) units, persistent, eight waves:
+//                                  Gamma, Abar, T (blocked 16x16 inverse), A_qk, W, U, Kd, Q e^Gamma, K e^Gamma
 //   states  (value block, head, seq) serial over chunks: keeps each chunk's start state and Vt
 //   dstates (value block, head, seq) serial backwards: keeps each chunk's end-state gradient,
 //                                  dVt, and writes the initial-state gradient
-//   vgrads  (chunk, head)          the contractions over V; writes dv
-//   kgrads  (chunk, head)          dT, dA and the decayed adjoints; writes dq, dk, dgate, dbeta
+//   vgrads  (chunk, head), eight waves: the contractions over V, dT, dA and T^T dW; writes dv, dbeta
+//   kgrads  (chunk, head, block of 32 key channels): the decayed adjoints; writes dq, dk, dgate
 // The waves of a workgroup exchange data through LDS only (global memory is read, or
 // written for later launches, never read back in the same kernel), so every workgroup
 // barrier is an LDS-only barrier: global loads and stores stay in flight across it.
@@ -177,7 +178,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // ------------------------------------------------------------------------------------
-// prep: one workgroup per (chunk slot, head).  After the in-chunk cumulative sum, Gamma is
+// prep: per (chunk slot, head) unit.  After the in-chunk cumulative sum, Gamma is
 // replaced in LDS by F1 = e^{Gamma - m_tile} (m_p: Gamma at the middle row of row tile p);
 // every decay factor is then a product of F1, its reciprocal and per-channel tables
 // (e^{m_p - m_q}, e^{m_p}, e^{Gamma_C - m_p}), so no exponential is taken in the products.
