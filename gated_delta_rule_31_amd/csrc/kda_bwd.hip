@@ -1315,7 +1315,10 @@ struct KgLds {
 };
 
 template <typename TIn, int K, int V>
-__global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
+// Persistent: workgroup b takes the work items b, b + G, ... (G the grid size, a multiple
+// of 8 so that an item's XCD does not change), and loads the next item's inputs while it
+// processes the current one.  Two workgroups per CU.
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kgrads_kernel(BwdArgs a) {
     constexpr int KB = KgLds<K>::KB, LKB = KgLds<K>::LKB, NCB = K / KB, KBT = KB / 16;
     constexpr int NOWN = NP * KBT / 4;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1331,45 +1334,50 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
     float *sEe = sEm + NP * KB;                    // [NP][KB] e^{Gamma_C - m_p}
     float *sMid = sEe + NP * KB;                   // [NP][KB] m_p
 
-    int u, cb;  // (chunk slot, head) unit; its channel blocks share an XCD
-    xcd_map(blockIdx.x, NCB, u, cb);
-    const int H = a.H;
-    if (u >= a.slots * H) return;
-    const int n = u / H, h = u % H, c0 = cb * KB;
-    const ChunkPos cp = slot_chunk(n, a.cu_seqlens, a.num_seqs, a.T);
-    if (cp.L == 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g4 = lane >> 4, i16 = lane & 15;
-    const int64_t sh = (int64_t)n * H + h;
+    const int H = a.H, units = a.slots * H;
+    const int items = 8 * NCB * ((units + 7) / 8);
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
-    // element-wise inputs of this thread's output tiles (dO S^T, Vt dS'^T, T^T dW), in
-    // flight during the staging and the products
-    float pre[NOWN][3][4];
-    {
-        const float *PS = a.w.PS + sh * BC * K, *PdK = a.w.PdK + sh * BC * K, *dBk = a.w.PW + sh * BC * K;
-#pragma unroll
-        for (int i = 0; i < NOWN; ++i) {
-            const int t = w + 4 * i, rt = t / KBT, ct = t % KBT, gc = c0 + 16 * ct + i16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * rt + 4 * g4 + e;
-                pre[i][0][e] = PS[row * K + gc];
-                pre[i][1][e] = PdK[row * K + gc];
-                pre[i][2][e] = dBk[row * K + gc];
+    // An item: its (chunk slot, head) unit, channel block and chunk; an item with no work
+    // (past the last unit, or an unused slot) reads unit 0, row 0 (valid addresses).
+    struct Item {
+        int n, h, c0;
+        ChunkPos cp;
+        bool work;
+    };
+    auto item_of = [&](int it) {
+        Item x{0, 0, 0, ChunkPos{0, 0}, false};
+        if (it < items) {
+            int u, cb;  // the channel blocks of one unit share an XCD
+            xcd_map(it, NCB, u, cb);
+            if (u < units) {
+                x.n = u / H;
+                x.h = u % H;
+                x.c0 = cb * KB;
+                x.cp = slot_chunk(x.n, a.cu_seqlens, a.num_seqs, a.T);
+                x.work = x.cp.L > 0;
             }
         }
-    }
-
-    {
-        // all loads first (four elements per load), then the LDS stores
-        constexpr int NK4 = (BC * KB / 4 + NTH - 1) / NTH, NM4 = BC * BC / 4 / NTH;
-        static_assert(BC * KB / 4 % NTH == 0, "whole float4 groups per thread");
-        float4 rq[NK4], rk[NK4], rg[NK4], rm[NM4], rd[NM4];
+        if (!x.work) x = Item{0, 0, 0, ChunkPos{0, 1}, false};
+        return x;
+    };
+    // inputs of the next item, kept in the input format until they are stored in LDS;
+    // fetched unconditionally so that the loads land in the registers the next iteration
+    // reads (a load under a condition is merged through copies that wait for it)
+    using Raw4 = typename std::conditional<std::is_same<TIn, float>::value, float4, s16x4>::type;
+    constexpr int NK4 = (BC * KB / 4 + NTH - 1) / NTH, NM4 = BC * BC / 4 / NTH;
+    static_assert(BC * KB / 4 % NTH == 0, "whole float4 groups per thread");
+    Raw4 rq[NK4], rk[NK4];
+    float4 rg[NK4], rm[NM4], rd[NM4];
+    float rb;
+    auto fetch_in = [&](const Item &x) {
+        const int tid = threadIdx.x;
+        const int64_t sh = (int64_t)x.n * H + x.h;
 #pragma unroll
         for (int i = 0; i < NK4; ++i) {
             const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
-            const int64_t gi = ((cp.t0 + crow(r, cp.L)) * H + h) * K + c0 + c;
-            rq[i] = ld4(q + gi);
-            rk[i] = ld4(k + gi);
+            const int64_t gi = ((x.cp.t0 + crow(r, x.cp.L)) * H + x.h) * K + x.c0 + c;
+            rq[i] = *reinterpret_cast<const Raw4 *>(q + gi);
+            rk[i] = *reinterpret_cast<const Raw4 *>(k + gi);
             rg[i] = ld4(a.gate.gate + gi);
         }
         const float *MA = a.w.MA + sh * BC * BC, *dAb = a.w.MT + sh * BC * BC;
@@ -1378,24 +1386,73 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             rm[i] = ld4(MA + 4 * (tid + NTH * i));
             rd[i] = ld4(dAb + 4 * (tid + NTH * i));
         }
+        rb = a.beta[(x.cp.t0 + crow(tid & (BC - 1), x.cp.L)) * H + x.h];
+    };
+    // element-wise inputs of this thread's output tiles (dO S^T, Vt dS'^T, T^T dW): loaded
+    // once the current item's are used, in flight until the next item's products
+    float pre[NOWN][3][4];
+    auto fetch_pre = [&](const Item &x) {
+        const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int g4 = lane >> 4, i16 = lane & 15;
+        const int64_t sh = (int64_t)x.n * H + x.h;
+        const float *PS = a.w.PS + sh * BC * K, *PdK = a.w.PdK + sh * BC * K, *dBk = a.w.PW + sh * BC * K;
 #pragma unroll
-        for (int i = 0; i < NK4; ++i) {
-            const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
-            st4(sQ + r * LKB + c, mask4(rq[i], r < cp.L));
-            st4(sK + r * LKB + c, mask4(rk[i], r < cp.L));
-            st4(sF2 + r * LKB + c, gate_log4(a.gate, rg[i], r < cp.L));
-        }
+        for (int i = 0; i < NOWN; ++i) {
+            const int t = w + 4 * i, rt = t / KBT, ct = t % KBT, gc = x.c0 + 16 * ct + i16;
 #pragma unroll
-        for (int i = 0; i < NM4; ++i) {
-            const int e = 4 * (tid + NTH * i), r = e / BC, c = e % BC;
-            const float4 m = rm[i];  // tril(dO Vt^T): entries with s > r are dropped
-            st4(sMA + r * LDC + c, make_float4(c <= r ? m.x : 0.f, c + 1 <= r ? m.y : 0.f, c + 2 <= r ? m.z : 0.f,
-                                               c + 3 <= r ? m.w : 0.f));
-            st4(sdA + r * LDC + c, rd[i]);
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * rt + 4 * g4 + e;
+                pre[i][0][e] = PS[row * K + gc];
+                pre[i][1][e] = PdK[row * K + gc];
+                pre[i][2][e] = dBk[row * K + gc];
+            }
         }
+    };
+    int item = blockIdx.x;
+    Item nx = item_of(item);
+    fetch_in(nx);
+    fetch_pre(nx);
+    for (; item < items; item += gridDim.x) {
+    // the thread index is re-read through an opaque copy in every iteration, so that the
+    // item's index computations are not hoisted out of the loop into registers
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g4 = lane >> 4, i16 = lane & 15;
+    const Item cur = nx;
+    nx = item_of(item + gridDim.x);
+    if (!cur.work) {  // uniform: only the next item's loads
+        fetch_in(nx);
+        fetch_pre(nx);
+        continue;
     }
-    if (tid < BC) sB[tid] = tid < cp.L ? a.beta[(cp.t0 + tid) * H + h] : 0.f;
+    const int n = cur.n, h = cur.h, c0 = cur.c0;
+    const ChunkPos cp = cur.cp;
+    const int64_t sh = (int64_t)n * H + h;
+#pragma unroll
+    for (int i = 0; i < NK4; ++i) {
+        const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
+        st4(sQ + r * LKB + c, mask4(raw_f4(rq[i]), r < cp.L));
+        st4(sK + r * LKB + c, mask4(raw_f4(rk[i]), r < cp.L));
+        st4(sF2 + r * LKB + c, gate_log4(a.gate, rg[i], r < cp.L));
+    }
+#pragma unroll
+    for (int i = 0; i < NM4; ++i) {
+        const int e = 4 * (tid + NTH * i), r = e / BC, c = e % BC;
+        const float4 m = rm[i];  // tril(dO Vt^T): entries with s > r are dropped
+        st4(sMA + r * LDC + c, make_float4(c <= r ? m.x : 0.f, c + 1 <= r ? m.y : 0.f, c + 2 <= r ? m.z : 0.f,
+                                           c + 3 <= r ? m.w : 0.f));
+        st4(sdA + r * LDC + c, rd[i]);
+    }
+    if (tid < BC) sB[tid] = tid < cp.L ? rb : 0.f;
+    // kept for the end: the gate values (alpha, for dgate = d ln alpha / alpha) and the
+    // chunk-end term gamma_C rowsum(S dS') of this thread's channel, read before the next
+    // item's loads go out
+    float4 al[NK4];
+#pragma unroll
+    for (int i = 0; i < NK4; ++i) al[i] = rg[i];
+    const float gcrs = a.w.gC[sh * K + c0 + tid % KB] * a.w.rs[sh * K + c0 + tid % KB];
     lds_barrier();
+    fetch_in(nx);  // in flight while this item is processed
     {
         // Gamma: inclusive prefix sums over the chunk's rows per channel, in NSEG segments of
         // SEG rows (each read into registers at once), offset by the earlier segments' totals
@@ -1512,6 +1569,7 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
         }
     }
     lds_barrier();  // q, k are no longer read: their LDS takes the row terms
+    fetch_pre(nx);  // this item's tile inputs are used
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
         const int t = w + 4 * i, rt = t / KBT, ct = t % KBT, c = 16 * ct + i16;
@@ -1550,7 +1608,7 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
             const int gc = c0 + c;
             // forward exclusive sum of the Kd terms (from the chunk-end term), reverse
             // inclusive sum of the row terms
-            float f = a.w.gC[sh * K + gc] * a.w.rs[sh * K + gc], rv = 0.f;
+            float f = gcrs, rv = 0.f;
 #pragma unroll
             for (int s2 = 0; s2 < NSEG; ++s2) {
                 if (s2 < sg) f += sTot[s2 * KB + c];
@@ -1570,16 +1628,10 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
         }
     }
     lds_barrier();
-    // dgate in four-element groups over the whole workgroup (alpha read in one batch)
+    // dgate in four-element groups over the whole workgroup (alpha kept from the staging)
     {
         constexpr int NK4 = (BC * KB / 4 + NTH - 1) / NTH;
         const bool log_gate = a.gate.mode == GATE_LOG;
-        float4 al[NK4];
-#pragma unroll
-        for (int i = 0; i < NK4; ++i) {
-            const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
-            al[i] = ld4(a.gate.gate + ((cp.t0 + crow(r, cp.L)) * H + h) * K + c0 + c);
-        }
 #pragma unroll
         for (int i = 0; i < NK4; ++i) {
             const int idx = tid + NTH * i, r = (4 * idx) / KB, c = (4 * idx) % KB;
@@ -1595,6 +1647,8 @@ __global__ __launch_bounds__(NTH) void bwd_kgrads_kernel(BwdArgs a) {
                 st4(a.dgate + ((cp.t0 + r) * H + h) * K + c0 + c, o);
             }
         }
+    }
+    lds_barrier();  // this item's LDS is consumed before the next item's inputs are stored
     }
 }
 
@@ -1634,12 +1688,14 @@ hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
     const int64_t units = (int64_t)a.slots * a.H;
     const dim3 gpp((unsigned)(units < num_cus() ? units : num_cus()));  // persistent prep
     const dim3 gk(8 * (K / KgLds<K>::KB) * sh8);
+    const int gk_max = 2 * num_cus() / 8 * 8 > 8 ? 2 * num_cus() / 8 * 8 : 8;  // two per CU, a multiple of 8
+    const dim3 gkp(gk.x < (unsigned)gk_max ? gk.x : (unsigned)gk_max);         // persistent kgrads
     constexpr size_t prep_bytes = PrepLds<K, V>::bytes;
     hipLaunchKernelGGL(kprep, gpp, dim3(PNT), prep_bytes, stream, a);
     hipLaunchKernelGGL((bwd_states_kernel<K, V>), gs, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL((bwd_dstates_kernel<K, V>), gd, dim3(NTH), 0, stream, a);
     hipLaunchKernelGGL(kvg, gp, dim3(VNT), VgLds<K>::bytes, stream, a);
-    hipLaunchKernelGGL(kkg, gk, dim3(NTH), KgLds<K>::bytes, stream, a);
+    hipLaunchKernelGGL(kkg, gkp, dim3(NTH), KgLds<K>::bytes, stream, a);
     return hipGetLastError();
 }
 
