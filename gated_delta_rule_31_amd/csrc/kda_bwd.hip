@@ -966,16 +966,18 @@ __global__ __launch_bounds__(VNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float4 at[NP];
         float bt[NP][4], bs[4], vr[4];
         const int pt = wq;  // row tile of T^T dVt (used by waves 0..3)
+        if (w < 4) {
 #pragma unroll
-        for (int m = 0; m < NP; ++m) {
-            at[m] = *reinterpret_cast<const float4 *>(sTt + (16 * pt + i16) * LDC + 16 * m + 4 * g4);
+            for (int m = 0; m < NP; ++m) {
+                at[m] = *reinterpret_cast<const float4 *>(sTt + (16 * pt + i16) * LDC + 16 * m + 4 * g4);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) bt[m][u] = sdVt[(16 * m + 4 * g4 + u) * LJ + i16];
-        }
+                for (int u = 0; u < 4; ++u) bt[m][u] = sdVt[(16 * m + 4 * g4 + u) * LJ + i16];
+            }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bs[e] = sB[16 * pt + 4 * g4 + e];
-            vr[e] = sVr[(16 * pt + 4 * g4 + e) * LJ + i16];
+            for (int e = 0; e < 4; ++e) {
+                bs[e] = sB[16 * pt + 4 * g4 + e];
+                vr[e] = sVr[(16 * pt + 4 * g4 + e) * LJ + i16];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);  // keep these reads here, ahead of the products
         // dO S^T, dVt S^T, Vt dS'^T on this wave's C x K tiles and dO Vt^T, dVt V^T on its
@@ -1080,8 +1082,14 @@ __global__ __launch_bounds__(VNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         if (tid < K * PARTS) {
             const int c = tid % K, part = tid / K;
+            if constexpr (CW == 4) {  // one 16-byte read of each (rows 80 bytes apart: no bank conflict)
+                const float4 x = *reinterpret_cast<const float4 *>(sH + c * LJ + 4 * part);
+                const float4 y = *reinterpret_cast<const float4 *>(sDH + c * LJ + 4 * part);
+                rsacc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+            } else {
 #pragma unroll
-            for (int j = 0; j < CW; ++j) rsacc += sH[c * LJ + part * CW + j] * sDH[c * LJ + part * CW + j];
+                for (int j = 0; j < CW; ++j) rsacc += sH[c * LJ + part * CW + j] * sDH[c * LJ + part * CW + j];
+            }
         }
         if (more) store(reinterpret_cast<float *>(smem) + ((js + 1) & 1) * SL);
         lds_barrier();
