@@ -39,7 +39,7 @@ import torch
 __all__ = ["bounded_decay", "chunk_fwd", "recurrent_step", "recurrent_kda", "KDAError", "chunk_fwd_supported",
            "chunk_fwd_fused_gate", "recurrent_step_fused_gate", "recurrent_fwd", "recurrent_fwd_fused_gate",
            "library_path", "abi_version", "GATE_ALPHA", "GATE_LOG", "chunk_bwd", "chunk_bwd_workspace_size",
-           "bounded_decay_bwd"]
+           "bounded_decay_bwd", "chunk_fwd_workspace_size", "TWO_PASS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -79,14 +79,17 @@ def _load():
     vp, i32, i64, f32, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_uint
     lib.kda_bounded_decay.argtypes = [vp, i32, vp, vp, f32, i64, i32, i32, i32, vp, vp]
     lib.kda_bounded_decay.restype = i32
+    sz = ctypes.c_size_t
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i64, i32, i32,
-                                  i32, i32, f32, vp, i32, vp]
+                                  i32, i32, f32, vp, i32, vp, sz, vp]
     lib.kda_chunk_fwd.restype = i32
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, f32, vp,
                                        i32, vp]
     lib.kda_recurrent_step.restype = i32
     lib.kda_chunk_fwd_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, vp, vp, i32, i32,
-                                             i64, i32, i32, i32, i32, f32, vp, i32, vp]
+                                             i64, i32, i32, i32, i32, f32, vp, i32, vp, sz, vp]
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
+    lib.kda_chunk_fwd_workspace_size.restype = sz
     lib.kda_chunk_fwd_fused_gate.restype = i32
     lib.kda_recurrent_step_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, i32, i32, i32,
                                                   i32, f32, vp, i32, vp]
@@ -123,6 +126,38 @@ def abi_version() -> int:
 def chunk_fwd_supported(dtype: torch.dtype, K: int, V: int, chunk_size: int) -> int:
     """Value columns per workgroup kda_chunk_fwd uses for this shape, 0 if unsupported."""
     return int(_load().kda_chunk_fwd_supported(_dtype_code(dtype), int(K), int(V), int(chunk_size)))
+
+
+# Default of the ``two_pass`` argument of the chunk prefill calls: with True (and a shape
+# the two-kernel form supports) a workspace is taken from torch's allocator and the
+# pre-pass + chain kernels run; with False the single chunk kernel runs.
+TWO_PASS = True
+
+
+def chunk_fwd_workspace_size(dtype: torch.dtype, B: int, T: int, H: int, K: int, V: int, chunk_size: int = 32,
+                             num_seqs: int = 0, varlen: bool = False) -> int:
+    """Bytes of workspace the two-kernel prefill needs (0: that form does not support the shape)."""
+    return int(_load().kda_chunk_fwd_workspace_size(_dtype_code(dtype), int(B), int(T), int(num_seqs),
+                                                    1 if varlen else 0, int(H), int(K), int(V), int(chunk_size)))
+
+
+def _chunk_workspace(two_pass, workspace, q, N, V, chunk_size, varlen):
+    """The (pointer, bytes) workspace arguments of a chunk prefill call."""
+    if workspace is not None:
+        if workspace.device != q.device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the device of q")
+        return workspace, workspace.numel()
+    explicit = two_pass is not None
+    if not (two_pass if explicit else TWO_PASS):
+        return None, 0
+    B, T, H, K = q.shape
+    n = chunk_fwd_workspace_size(q.dtype, B, T, H, K, V, chunk_size, N, varlen)
+    if n == 0:
+        if explicit:  # asked for by name: no silent switch to the single kernel
+            raise KDAError("kda_chunk_fwd_workspace_size", 4, "the two-kernel form does not support this shape")
+        return None, 0
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    return ws, n
 
 
 def _check(fn: str, status: int):
@@ -237,13 +272,16 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Ten
               output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
               chunk_size: int = 32, scale: float = 1.0, gate_is_log: bool = False,
               out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-              final_state: Optional[torch.Tensor] = None
+              final_state: Optional[torch.Tensor] = None, two_pass: Optional[bool] = None,
+              workspace: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise prefill.  q, k [B,T,H,K]; v [B,T,H,V] (one dtype, float32 or
     bfloat16); gate [B,T,H,K] float32 (alpha, or ln alpha with ``gate_is_log``);
     beta [B,T,H] float32; initial_state [N,H,K,V] float32 or None; cu_seqlens
     int32 [N+1] (B == 1) or None.  Returns (out [B,T,H,V], final_state [N,H,K,V]
-    or None).  ``final_state`` may be passed in (it may be ``initial_state``)."""
+    or None).  ``final_state`` may be passed in (it may be ``initial_state``).
+    ``two_pass`` (default ``TWO_PASS``): pre-pass + chain kernels over a workspace
+    (``workspace``, uint8, or one from torch's allocator) instead of the single kernel."""
     q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
         q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state)
     gate = _dev(gate, "gate", torch.float32)
@@ -251,12 +289,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Ten
         raise ValueError("gate must be shaped like q")
     B, T, H, K = q.shape
     V = v.shape[-1]
+    ws, nws = _chunk_workspace(two_pass, workspace, q, N, V, chunk_size, cu_seqlens is not None)
     with torch.cuda.device(q.device):
         st = _load().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(gate),
                                    GATE_LOG if gate_is_log else GATE_ALPHA, _ptr(beta),
                                    _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, B, T,
                                    H, K, V, int(chunk_size), float(scale), _ptr(out), _dtype_code(od),
-                                   _stream(q))
+                                   _ptr(ws), nws, _stream(q))
     _check("kda_chunk_fwd", st)
     return out, final_state
 
@@ -279,25 +318,27 @@ def chunk_fwd_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logi
                          output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
                          chunk_size: int = 32, scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
                          out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                         qk_l2norm: bool = False, beta_logits: bool = False, state_vk: bool = False
+                         qk_l2norm: bool = False, beta_logits: bool = False, state_vk: bool = False,
+                         two_pass: Optional[bool] = None, workspace: Optional[torch.Tensor] = None
                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """``chunk_fwd`` with alpha = exp(lower_bound * sigmoid(e^log_scale (logits + bias)))
     computed inside the kernel.  logits [B,T,H,K] in the dtype of q; log_scale [H] and
     bias [H,K] float32; lower_bound in [-5, 0).  ``qk_l2norm``: q and k are normalised
     over K in the kernel; ``beta_logits``: beta holds logits (sigmoid in the kernel);
-    ``state_vk``: states are [N,H,V,K]."""
+    ``state_vk``: states are [N,H,V,K]; ``two_pass``, ``workspace``: as in ``chunk_fwd``."""
     q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
         q, k, v, beta, initial_state, output_final_state, cu_seqlens, out_dtype, out, final_state, state_vk)
     logits, log_scale, bias = _gate_params(logits, log_scale, bias, q)
     B, T, H, K = q.shape
     V = v.shape[-1]
+    ws, nws = _chunk_workspace(two_pass, workspace, q, N, V, chunk_size, cu_seqlens is not None)
     with torch.cuda.device(q.device):
         st = _load().kda_chunk_fwd_fused_gate(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(logits),
                                               _ptr(log_scale), _ptr(bias), float(lower_bound),
                                               _flags(qk_l2norm, beta_logits, state_vk), _ptr(beta),
                                               _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, B,
                                               T, H, K, V, int(chunk_size), float(scale), _ptr(out),
-                                              _dtype_code(od), _stream(q))
+                                              _dtype_code(od), _ptr(ws), nws, _stream(q))
     _check("kda_chunk_fwd_fused_gate", st)
     return out, final_state
 

@@ -84,7 +84,7 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, kda_dtype
                           const kda::GateIn &gate, unsigned flags, const float *beta, const float *initial_state,
                           float *final_state, const int32_t *cu_seqlens, int num_seqs, int B, int64_t T,
                           int H, int K, int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
-                          hipStream_t stream) {
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_BAD_SHAPE;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_BAD_DTYPE;
     if (flags & ~(unsigned)(KDA_QK_L2NORM | KDA_BETA_LOGITS | KDA_STATE_VK)) return KDA_ERR_BAD_ARGUMENT;
@@ -115,6 +115,20 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, kda_dtype
     }
     if ((const void *)out == (const void *)final_state) return KDA_ERR_ALIAS;
     if (N > (int64_t)(1 << 30) / H) return KDA_ERR_UNSUPPORTED;
+    int64_t slots = 0;
+    if (workspace) {
+        // the two-kernel form: one package per (chunk slot, head) in the workspace
+        const size_t pb = kda::chunk_pack_bytes(in_dtype == KDA_F32, K, V, chunk_size);
+        if (pb == 0) return KDA_ERR_UNSUPPORTED;
+        slots = kda::chunk_fwd_slots(B, T, num_seqs, cu_seqlens != nullptr, chunk_size);
+        if (slots * H > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;  // (slot, head) indexes as int
+        if (workspace_bytes < kda::chunk_fwd_workspace_bytes(in_dtype == KDA_F32, slots, N, H, K, V, chunk_size) ||
+            (uintptr_t)workspace % 16 != 0)
+            return KDA_ERR_BAD_ARGUMENT;
+        for (const void *p : ins)
+            if (p == workspace) return KDA_ERR_ALIAS;
+        if (workspace == out || workspace == (const void *)final_state) return KDA_ERR_ALIAS;
+    }
 
     kda::ChunkArgs a;
     a.q = q;
@@ -133,8 +147,15 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, kda_dtype
     a.qk_l2norm = (flags & KDA_QK_L2NORM) != 0;
     a.beta_logits = (flags & KDA_BETA_LOGITS) != 0;
     a.state_vk = (flags & KDA_STATE_VK) != 0;
+    a.num_seqs = (int)N;
+    a.pack = static_cast<unsigned char *>(workspace);
+    a.pack_slots = (int)slots;
+    a.c_begin = 0;
+    a.c_end = INT32_MAX;
     int bv = 0;
-    hipError_t e = kda::launch_chunk_fwd(a, in_dtype == KDA_F32, K, V, chunk_size, (int)(N * H), stream, &bv);
+    hipError_t e = workspace ? kda::launch_chunk_fwd_two_pass(a, in_dtype == KDA_F32, K, V, chunk_size, (int)(N * H),
+                                                              slots, stream, &bv)
+                             : kda::launch_chunk_fwd(a, in_dtype == KDA_F32, K, V, chunk_size, (int)(N * H), stream, &bv);
     return e == hipSuccess ? KDA_OK : hip_fail(e);
 }
 
@@ -253,10 +274,11 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype 
                          const float *initial_state, float *final_state,
                          const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H, int K,
                          int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
-                         hipStream_t stream) {
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!gate_ok(gate_kind)) return KDA_ERR_BAD_DTYPE;
     return chunk_fwd_impl(q, k, v, in_dtype, gate_given(gate, gate_kind), 0u, beta, initial_state, final_state,
-                          cu_seqlens, num_seqs, B, T, H, K, V, chunk_size, scale, out, out_dtype, stream);
+                          cu_seqlens, num_seqs, B, T, H, K, V, chunk_size, scale, out, out_dtype, workspace,
+                          workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v, kda_dtype in_dtype,
@@ -264,13 +286,26 @@ kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v,
                                     float lower_bound, unsigned flags, const float *beta, const float *initial_state,
                                     float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
                                     int64_t T, int H, int K, int V, int chunk_size, float scale, void *out,
-                                    kda_dtype out_dtype, hipStream_t stream) {
+                                    kda_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
     // the chunk path needs every log-decay >= -5, which the bound guarantees when
     // lower_bound >= -5
     if (!(lower_bound < 0.f) || lower_bound < -5.f) return KDA_ERR_BAD_ARGUMENT;
     return chunk_fwd_impl(q, k, v, in_dtype, gate_logits(logits, log_scale, bias, lower_bound), flags, beta,
                           initial_state, final_state, cu_seqlens, num_seqs, B, T, H, K, V, chunk_size, scale,
-                          out, out_dtype, stream);
+                          out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+size_t kda_chunk_fwd_workspace_size(kda_dtype in_dtype, int B, int64_t T, int num_seqs, int varlen, int H, int K,
+                                    int V, int chunk_size) {
+    if (!dtype_ok(in_dtype) || !dim_ok(K) || !dim_ok(V) || B < 0 || T < 0 || H <= 0 || num_seqs < 0) return 0;
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return 0;
+    const size_t pb = kda::chunk_pack_bytes(in_dtype == KDA_F32, K, V, chunk_size);
+    if (pb == 0) return 0;
+    const int64_t slots = kda::chunk_fwd_slots(B, T, num_seqs, varlen != 0, chunk_size);
+    if (slots * H > (int64_t)INT32_MAX) return 0;
+    const int64_t N = varlen ? num_seqs : B;
+    return kda::chunk_fwd_workspace_bytes(in_dtype == KDA_F32, slots, N, H, K, V, chunk_size);
 }
 
 kda_status kda_recurrent_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,

@@ -238,6 +238,12 @@ __device__ __forceinline__ T ld_at(const void *base, uint32_t byte_off) {
     return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
+// Store two consecutive T at a 32-bit byte offset from a workgroup-uniform base.
+template <typename T>
+__device__ __forceinline__ void st2_at(void *base, uint32_t byte_off, float a, float b) {
+    st2<T>(reinterpret_cast<T *>(reinterpret_cast<char *>(base) + byte_off), a, b);
+}
+
 // acc += A[16 x kdim] * B[kdim x 16] for the A-matrix tiles: A rows and B^T rows staged
 // in the A-operand type (k contiguous).  With SPLIT both operands also have low parts
 // (x - hi) `lo` elements further on, and the product is hi*hi + hi*lo + lo*hi (about 16
@@ -378,14 +384,14 @@ __device__ __forceinline__ void halve_sums(float (&x)[N], int lane, int &base) {
     }
 }
 
-// The A-matrix work of one chunk, shared out over four waves (w = 0..3).  Wave p % 4
+// The A-matrix work of one chunk, shared out over NW waves (w = 0..NW-1).  Wave p % NW
 // computes A_kk's diagonal tile p and inverts I + A_pp, giving T's diagonal block p; the off-diagonal A_kk tiles (kept in fp32 for T's off-diagonal
 // blocks) and the lower A_qk tiles are dealt round-robin after them.  Reads the operand
 // staging of the chunk; writes Akk, Tf and the Tm / Aqk tiles of package `pk`.
 // With NORM the staged operands carry the raw q and k; the tiles are scaled by the
 // reciprocal row norms (A_kk[i,j] by 1/(|k_i||k_j|), A_qk[i,j] by 1/(|q_i||k_j|)),
 // which the prep waves left in LDS as per-wave partial sums of squares.
-template <class P, int K, int V, int C, int BV, bool NORM>
+template <class P, int K, int V, int C, int BV, bool NORM, int NW = 4>
 __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char *pk, int nb, int w, int lane) {
     using L = Layout<P, K, V, C, BV>;
     using TA = typename P::TA;
@@ -416,7 +422,7 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
     };
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        if ((p & 3) != w) continue;
+        if ((p % NW) != w) continue;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
         mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, p), L::LKS, 0, lane);
         if constexpr (NORM) {
@@ -440,7 +446,7 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
     for (int p = 1; p < NP; ++p)
 #pragma unroll
         for (int qt = 0; qt < p; ++qt, ++t) {
-            if (((t + NP) & 3) != w) continue;
+            if (((t + NP) % NW) != w) continue;
             f4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_stage<P, false, K>(acc, Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKS, 0, lane);
             const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
@@ -457,7 +463,7 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
 #pragma unroll
         for (int qt = 0; qt <= p; ++qt) {
             const int tq = NOFF + p * (p + 1) / 2 + qt;
-            if (((tq + NP) & 3) != w) continue;
+            if (((tq + NP) % NW) != w) continue;
             f4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_stage<P, P::kSplit, K>(acc, St + L::sLq + p * 16 * L::LKS, L::LKS, right_of(p, qt), L::LKS, L::NST, lane);
             const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
@@ -469,6 +475,198 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
 #pragma unroll
             for (int e = 0; e < 4; ++e) Aqk[(i0 + e) * L::LCM + j] = from_f32<TM>((j <= i0 + e) ? acc[e] : 0.f);
         }
+}
+
+// The state waves (w = 0..NSW-1): the float32 state of this workgroup's value columns in
+// registers, advanced chunk by chunk through the serial part.  The packages sit at pkg0 in
+// two buffers, by chunk parity.  Without PK the state waves also do the A-matrix work of
+// the chunk staged in the previous period (two barriers a period); with PK each package
+// arrives complete from the pre-pass (one barrier a period).
+template <class P, int K, int V, int C, int BV, bool NORM, bool PK>
+__device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *smem, unsigned char *pkg0, int s,
+                                            int h, int vb, int64_t bos, int64_t eos, int nchunks, int wave,
+                                            int lane) {
+    using L = Layout<P, K, V, C, BV>;
+    using TM = typename P::TM;
+    constexpr int NP = L::NP;
+    constexpr int NKT_K = K / 16;
+    const int g = lane >> 4;
+    const int H = a.H;
+    auto pkg = [&](int buf) { return pkg0 + (size_t)buf * L::szPkg; };
+    f4 S[L::MJ][NKT_K];
+    const float *s0 = a.initial_state ? a.initial_state + ((int64_t)s * H + h) * K * V : nullptr;
+#pragma unroll
+    for (int mj = 0; mj < L::MJ; ++mj) {
+        const int jt = wave + NSW * mj;
+#pragma unroll
+        for (int t = 0; t < NKT_K; ++t) {
+            f4 x = {0.f, 0.f, 0.f, 0.f};
+            if (jt < L::NJT && s0) {
+                const int vc = vb * BV + jt * 16 + (lane & 15);
+                if (a.state_vk) {
+                    const float4 y = *reinterpret_cast<const float4 *>(s0 + (int64_t)vc * K + 16 * t + 4 * g);
+                    x[0] = y.x; x[1] = y.y; x[2] = y.z; x[3] = y.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = s0[(int64_t)(16 * t + 4 * g + e) * V + vc];
+                }
+            }
+            S[mj][t] = x;
+        }
+    }
+    BFrag<TM, NKT_K> Sh[L::MJ];
+#pragma unroll
+    for (int mj = 0; mj < L::MJ; ++mj) Sh[mj].set(S[mj]);
+
+    for (int it = 0; it <= nchunks; ++it) {
+        if constexpr (!PK) {
+            float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
+            float *Tf = reinterpret_cast<float *>(smem + L::oTf);
+            // the A-matrix tiles and T's diagonal blocks of the chunk staged in the previous
+            // period, whose package the serial part consumes after the next barrier
+            if (it >= 1) a_matrix_work<P, K, V, C, BV, NORM>(smem, pkg((it - 1) & 1), (it - 1) & 1, wave, lane);
+            lds_barrier();  // B1: chunk it-1's A-matrix tiles are done; chunk it's decay products are in LDS
+            if (NP > 1 && it >= 1) {
+                // T's off-diagonal blocks of the chunk about to be consumed, one block
+                // distance at a time on fp32 matrix cores:
+                //   M = sum_{r=q}^{p-1} A_pr T_rq,   T_pq = -T_pp M
+                // Every state wave computes all of them: it reads back only what it wrote
+                // itself, and the other waves write the same values to the same places, so
+                // no barrier is needed before the serial part uses them.
+                TM *Tm = reinterpret_cast<TM *>(pkg((it - 1) & 1) + L::pTm);
+                for (int d = 1; d < NP; ++d) {
+                    for (int qb = 0; qb + d < NP; ++qb) {
+                        const int p = qb + d;
+                        f4 m = {0.f, 0.f, 0.f, 0.f};
+                        for (int r = qb; r < p; ++r)
+#pragma unroll
+                            for (int s4 = 0; s4 < 4; ++s4)
+                                m = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    Akk[(p * 16 + (lane & 15)) * L::LCF + r * 16 + 4 * s4 + g],
+                                    Tf[(r * 16 + 4 * s4 + g) * L::LCF + qb * 16 + (lane & 15)], m, 0, 0, 0);
+                        // M's accumulator layout is the B operand with k = 4g + s4
+                        f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4)
+                            t = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                Tf[(p * 16 + (lane & 15)) * L::LCF + p * 16 + 4 * g + s4], m[s4], t, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = p * 16 + 4 * g + e, j = qb * 16 + (lane & 15);
+                            Tf[i * L::LCF + j] = -t[e];
+                            Tm[i * L::LCM + j] = from_f32<TM>(-t[e]);
+                        }
+                    }
+                    lds_fence();
+                }
+            }
+        }
+        f4 Vt[L::MJ][NP];
+        BFrag<TM, NP> Vh[L::MJ];
+        const int cn = it - 1;  // chunk handled by the state waves in this iteration
+        if (cn >= 0) {
+            const unsigned char *pk = pkg(cn & 1);
+            const TM *Qt = reinterpret_cast<const TM *>(pk + L::pQt);
+            const TM *Bw = reinterpret_cast<const TM *>(pk + L::pBw);
+            const TM *Tm = reinterpret_cast<const TM *>(pk + L::pTm);
+            const TM *Aqk = reinterpret_cast<const TM *>(pk + L::pAqk);
+            const TM *bV = reinterpret_cast<const TM *>(pk + L::pbV);
+            const int64_t t0 = bos + (int64_t)cn * C;
+            const int n = (int)((eos - t0) < C ? (eos - t0) : C);
+            // output rows of the chunk from a uniform base, 32-bit element offsets
+            unsigned char *ob = static_cast<unsigned char *>(a.out) + (t0 * H + h) * V * (a.out_bf16 ? 2 : 4);
+            auto store_o = [&](int p, int jt, f4 o) {
+                const int j = vb * BV + jt * 16 + (lane & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * p + 4 * g + e;
+                    const uint32_t off = (uint32_t)(i * H * V + j);
+                    if (i < n) {
+                        if (a.out_bf16)
+                            *reinterpret_cast<__bf16 *>(ob + 2u * off) = (__bf16)(a.scale * o[e]);
+                        else
+                            *reinterpret_cast<float *>(ob + 4u * off) = a.scale * o[e];
+                    }
+                }
+            };
+#pragma unroll
+            for (int mj = 0; mj < L::MJ; ++mj) {
+                const int jt = wave + NSW * mj;
+                if (jt >= L::NJT) continue;
+                // Y = beta V - Bw S   (rows: tokens of the chunk; this wave's 16 columns)
+                f4 Y[NP];
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    f4 y;
+                    const TM *bvr = bV + (jt * 16 + (lane & 15)) * L::LCM + 16 * p + 4 * g;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = to_f32(bvr[e]);
+                    mma_bfrag<NKT_K>(y, Bw + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
+                    Y[p] = y;
+                }
+                BFrag<TM, NP> Yh;
+                Yh.set(Y);
+                // Vt = T Y (T lower triangular: row tile p needs token tiles 0..p)
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    f4 x = {0.f, 0.f, 0.f, 0.f};
+                    mma_bfrag<NP>(x, Tm + (16 * p + (lane & 15)) * L::LCM, Yh, p + 1, lane);
+                    Vt[mj][p] = x;
+                }
+                Vh[mj].set(Vt[mj]);
+                // O = Qt S + A_qk Vt
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    f4 o = {0.f, 0.f, 0.f, 0.f};
+                    mma_bfrag<NKT_K>(o, Qt + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
+                    mma_bfrag<NP>(o, Aqk + (16 * p + (lane & 15)) * L::LCM, Vh[mj], p + 1, lane);
+                    store_o(p, jt, o);
+                }
+            }
+        }
+        if (cn >= 0) {  // S = gamma_C S + Kt^T Vt, still before B2
+            const unsigned char *pk = pkg(cn & 1);
+            const TM *Kt = reinterpret_cast<const TM *>(pk + L::pKt);
+            const float *eGC = reinterpret_cast<const float *>(pk + L::pGC);
+#pragma unroll
+            for (int mj = 0; mj < L::MJ; ++mj) {
+                const int jt = wave + NSW * mj;
+                if (jt >= L::NJT) continue;
+                // S = gamma_C S + Kt^T Vt
+#pragma unroll
+                for (int t = 0; t < NKT_K; ++t) {
+                    f4 x = S[mj][t];
+                    const float4 d = *reinterpret_cast<const float4 *>(eGC + 16 * t + 4 * g);
+                    x[0] *= d.x; x[1] *= d.y; x[2] *= d.z; x[3] *= d.w;
+                    mma_bfrag<NP>(x, Kt + (16 * t + (lane & 15)) * L::LCM, Vh[mj], NP, lane);
+                    S[mj][t] = x;
+                }
+                Sh[mj].set(S[mj]);
+            }
+        }
+        // B2 (with the package built in the workgroup: chunk it is staged and its package
+        // operands are stored); with PK the one barrier of the period: the next package is in LDS
+        lds_barrier();
+    }
+    if (a.final_state) {
+        float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
+#pragma unroll
+        for (int mj = 0; mj < L::MJ; ++mj) {
+            const int jt = wave + NSW * mj;
+            if (jt >= L::NJT) continue;
+            const int vc = vb * BV + jt * 16 + (lane & 15);
+#pragma unroll
+            for (int t = 0; t < NKT_K; ++t) {
+                if (a.state_vk) {
+                    *reinterpret_cast<float4 *>(sf + (int64_t)vc * K + 16 * t + 4 * g) =
+                        float4{S[mj][t][0], S[mj][t][1], S[mj][t][2], S[mj][t][3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sf[(int64_t)(16 * t + 4 * g + e) * V + vc] = S[mj][t][e];
+                }
+            }
+        }
+    }
 }
 
 // GM = 0: the gate is a float32 tensor of alpha or ln alpha (a.gate.mode); GM = 1: it
@@ -517,174 +715,8 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     auto pkg = [&](int buf) { return smem + L::oPkg + (size_t)buf * L::szPkg; };
 
     if (wave < NSW) {
-        // =================================== state waves ===================================
-        f4 S[L::MJ][NKT_K];
-        const float *s0 = a.initial_state ? a.initial_state + ((int64_t)s * H + h) * K * V : nullptr;
-#pragma unroll
-        for (int mj = 0; mj < L::MJ; ++mj) {
-            const int jt = wave + NSW * mj;
-#pragma unroll
-            for (int t = 0; t < NKT_K; ++t) {
-                f4 x = {0.f, 0.f, 0.f, 0.f};
-                if (jt < L::NJT && s0) {
-                    const int vc = vb * BV + jt * 16 + (lane & 15);
-                    if (a.state_vk) {
-                        const float4 y = *reinterpret_cast<const float4 *>(s0 + (int64_t)vc * K + 16 * t + 4 * g);
-                        x[0] = y.x; x[1] = y.y; x[2] = y.z; x[3] = y.w;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = s0[(int64_t)(16 * t + 4 * g + e) * V + vc];
-                    }
-                }
-                S[mj][t] = x;
-            }
-        }
-        BFrag<TM, NKT_K> Sh[L::MJ];
-#pragma unroll
-        for (int mj = 0; mj < L::MJ; ++mj) Sh[mj].set(S[mj]);
-
-        float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
-        float *Tf = reinterpret_cast<float *>(smem + L::oTf);
-        for (int it = 0; it <= nchunks; ++it) {
-            // the A-matrix tiles and T's diagonal blocks of the chunk staged in the previous
-            // period, whose package the serial part consumes after the next barrier
-            if (it >= 1) a_matrix_work<P, K, V, C, BV, NORM>(smem, pkg((it - 1) & 1), (it - 1) & 1, wave, lane);
-            lds_barrier();  // B1: chunk it-1's A-matrix tiles are done; chunk it's decay products are in LDS
-            if (NP > 1 && it >= 1) {
-                // T's off-diagonal blocks of the chunk about to be consumed, one block
-                // distance at a time on fp32 matrix cores:
-                //   M = sum_{r=q}^{p-1} A_pr T_rq,   T_pq = -T_pp M
-                // Every state wave computes all of them: it reads back only what it wrote
-                // itself, and the other waves write the same values to the same places, so
-                // no barrier is needed before the serial part uses them.
-                TM *Tm = reinterpret_cast<TM *>(pkg((it - 1) & 1) + L::pTm);
-                for (int d = 1; d < NP; ++d) {
-                    for (int qb = 0; qb + d < NP; ++qb) {
-                        const int p = qb + d;
-                        f4 m = {0.f, 0.f, 0.f, 0.f};
-                        for (int r = qb; r < p; ++r)
-#pragma unroll
-                            for (int s4 = 0; s4 < 4; ++s4)
-                                m = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                    Akk[(p * 16 + (lane & 15)) * L::LCF + r * 16 + 4 * s4 + g],
-                                    Tf[(r * 16 + 4 * s4 + g) * L::LCF + qb * 16 + (lane & 15)], m, 0, 0, 0);
-                        // M's accumulator layout is the B operand with k = 4g + s4
-                        f4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s4 = 0; s4 < 4; ++s4)
-                            t = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                Tf[(p * 16 + (lane & 15)) * L::LCF + p * 16 + 4 * g + s4], m[s4], t, 0, 0, 0);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int i = p * 16 + 4 * g + e, j = qb * 16 + (lane & 15);
-                            Tf[i * L::LCF + j] = -t[e];
-                            Tm[i * L::LCM + j] = from_f32<TM>(-t[e]);
-                        }
-                    }
-                    lds_fence();
-                }
-            }
-            f4 Vt[L::MJ][NP];
-            BFrag<TM, NP> Vh[L::MJ];
-            const int cn = it - 1;  // chunk handled by the state waves in this iteration
-            if (cn >= 0) {
-                const unsigned char *pk = pkg(cn & 1);
-                const TM *Qt = reinterpret_cast<const TM *>(pk + L::pQt);
-                const TM *Bw = reinterpret_cast<const TM *>(pk + L::pBw);
-                const TM *Tm = reinterpret_cast<const TM *>(pk + L::pTm);
-                const TM *Aqk = reinterpret_cast<const TM *>(pk + L::pAqk);
-                const TM *bV = reinterpret_cast<const TM *>(pk + L::pbV);
-                const int64_t t0 = bos + (int64_t)cn * C;
-                const int n = (int)((eos - t0) < C ? (eos - t0) : C);
-#pragma unroll
-                for (int mj = 0; mj < L::MJ; ++mj) {
-                    const int jt = wave + NSW * mj;
-                    if (jt >= L::NJT) continue;
-                    // Y = beta V - Bw S   (rows: tokens of the chunk; this wave's 16 columns)
-                    f4 Y[NP];
-#pragma unroll
-                    for (int p = 0; p < NP; ++p) {
-                        f4 y;
-                        const TM *bvr = bV + (jt * 16 + (lane & 15)) * L::LCM + 16 * p + 4 * g;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) y[e] = to_f32(bvr[e]);
-                        mma_bfrag<NKT_K>(y, Bw + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
-                        Y[p] = y;
-                    }
-                    BFrag<TM, NP> Yh;
-                    Yh.set(Y);
-                    // Vt = T Y (T lower triangular: row tile p needs token tiles 0..p)
-#pragma unroll
-                    for (int p = 0; p < NP; ++p) {
-                        f4 x = {0.f, 0.f, 0.f, 0.f};
-                        mma_bfrag<NP>(x, Tm + (16 * p + (lane & 15)) * L::LCM, Yh, p + 1, lane);
-                        Vt[mj][p] = x;
-                    }
-                    Vh[mj].set(Vt[mj]);
-                    // O = Qt S + A_qk Vt
-#pragma unroll
-                    for (int p = 0; p < NP; ++p) {
-                        f4 o = {0.f, 0.f, 0.f, 0.f};
-                        mma_bfrag<NKT_K>(o, Qt + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
-                        mma_bfrag<NP>(o, Aqk + (16 * p + (lane & 15)) * L::LCM, Vh[mj], p + 1, lane);
-                        const int j = vb * BV + jt * 16 + (lane & 15);
-                        // output rows of the chunk from a uniform base, 32-bit element offsets
-                        unsigned char *ob = static_cast<unsigned char *>(a.out) + (t0 * H + h) * V * (a.out_bf16 ? 2 : 4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int i = 16 * p + 4 * g + e;
-                            const uint32_t off = (uint32_t)(i * H * V + j);
-                            if (i < n) {
-                                if (a.out_bf16)
-                                    *reinterpret_cast<__bf16 *>(ob + 2u * off) = (__bf16)(a.scale * o[e]);
-                                else
-                                    *reinterpret_cast<float *>(ob + 4u * off) = a.scale * o[e];
-                            }
-                        }
-                    }
-                }
-            }
-            if (cn >= 0) {  // S = gamma_C S + Kt^T Vt, still before B2
-                const unsigned char *pk = pkg(cn & 1);
-                const TM *Kt = reinterpret_cast<const TM *>(pk + L::pKt);
-                const float *eGC = reinterpret_cast<const float *>(pk + L::pGC);
-#pragma unroll
-                for (int mj = 0; mj < L::MJ; ++mj) {
-                    const int jt = wave + NSW * mj;
-                    if (jt >= L::NJT) continue;
-                    // S = gamma_C S + Kt^T Vt
-#pragma unroll
-                    for (int t = 0; t < NKT_K; ++t) {
-                        f4 x = S[mj][t];
-                        const float4 d = *reinterpret_cast<const float4 *>(eGC + 16 * t + 4 * g);
-                        x[0] *= d.x; x[1] *= d.y; x[2] *= d.z; x[3] *= d.w;
-                        mma_bfrag<NP>(x, Kt + (16 * t + (lane & 15)) * L::LCM, Vh[mj], NP, lane);
-                        S[mj][t] = x;
-                    }
-                    Sh[mj].set(S[mj]);
-                }
-            }
-            lds_barrier();  // B2: chunk it is staged and its package operands are stored
-        }
-        if (a.final_state) {
-            float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
-#pragma unroll
-            for (int mj = 0; mj < L::MJ; ++mj) {
-                const int jt = wave + NSW * mj;
-                if (jt >= L::NJT) continue;
-                const int vc = vb * BV + jt * 16 + (lane & 15);
-#pragma unroll
-                for (int t = 0; t < NKT_K; ++t) {
-                    if (a.state_vk) {
-                        *reinterpret_cast<float4 *>(sf + (int64_t)vc * K + 16 * t + 4 * g) =
-                            float4{S[mj][t][0], S[mj][t][1], S[mj][t][2], S[mj][t][3]};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) sf[(int64_t)(16 * t + 4 * g + e) * V + vc] = S[mj][t][e];
-                    }
-                }
-            }
-        }
+        state_waves<P, K, V, C, BV, NORM, false>(a, smem, smem + L::oPkg, s, h, vb, bos, eos, nchunks, wave,
+                                                 lane);
         return;
     }
 

@@ -1,6 +1,6 @@
 // kda_chunk_logits.hip -- the chunk kernels of kda_chunk_kernel.h that evaluate the
 // bounded gate from its logits while staging each chunk (no float32 gate tensor).
-#include "kda_chunk_kernel.h"
+#include "kda_chunk_pack.h"
 
 namespace kda {
 
@@ -8,6 +8,12 @@ hipError_t launch_chunk_fwd_logits(const ChunkArgs &a, bool fp32_inputs, int K, 
                                    hipStream_t stream, int *bv) {
     return fp32_inputs ? launch_p<PrecF32, 1>(a, K, V, C, num_pairs, stream, bv)
                        : launch_p<PrecMixed, 1>(a, K, V, C, num_pairs, stream, bv);
+}
+
+hipError_t launch_chunk_pack_logits(const ChunkArgs &a, bool fp32_inputs, int K, int C, int64_t items, int max_wgs,
+                                    hipStream_t stream) {
+    return fp32_inputs ? launch_pack_p<PrecF32, 1>(a, K, C, items, max_wgs, stream)
+                       : launch_pack_p<PrecMixed, 1>(a, K, C, items, max_wgs, stream);
 }
 
 }  // namespace kda

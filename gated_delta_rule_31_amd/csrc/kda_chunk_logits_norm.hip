@@ -1,7 +1,7 @@
 // kda_chunk_logits_norm.hip -- the chunk kernels of kda_chunk_kernel.h that evaluate the
 // bounded gate from its logits and divide q and k by their L2 norms over K while
 // staging each chunk (the preparation the model's layer asks its kernels to do).
-#include "kda_chunk_kernel.h"
+#include "kda_chunk_pack.h"
 
 namespace kda {
 
@@ -9,6 +9,12 @@ hipError_t launch_chunk_fwd_logits_norm(const ChunkArgs &a, bool fp32_inputs, in
                                         hipStream_t stream, int *bv) {
     return fp32_inputs ? launch_p<PrecF32, 2>(a, K, V, C, num_pairs, stream, bv)
                        : launch_p<PrecMixed, 2>(a, K, V, C, num_pairs, stream, bv);
+}
+
+hipError_t launch_chunk_pack_logits_norm(const ChunkArgs &a, bool fp32_inputs, int K, int C, int64_t items, int max_wgs,
+                                         hipStream_t stream) {
+    return fp32_inputs ? launch_pack_p<PrecF32, 2>(a, K, C, items, max_wgs, stream)
+                       : launch_pack_p<PrecMixed, 2>(a, K, C, items, max_wgs, stream);
 }
 
 }  // namespace kda

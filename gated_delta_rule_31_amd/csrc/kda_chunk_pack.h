@@ -1,0 +1,746 @@
+// kda_chunk_pack.h -- the two-kernel form of the chunkwise prefill (KDA cheat sheet,
+// "Chunkwise parallel form"): the same arithmetic as chunk_fwd_kernel, split where the
+// work stops depending on the state.
+//
+//  * chunk_pack_kernel, one workgroup per (chunk, head), all chunks at once: the decay
+//    products, the A-matrix tiles, T = (I + A_kk)^-1 and A_qk of one chunk, written as a
+//    dense package (Qt, -Bw, Kt, T, A_qk, gamma_C, beta) into a caller-owned workspace.
+//    Nothing in it depends on the state or on the value columns, so it runs once per
+//    (chunk, head) instead of once per value block, on every compute unit.
+//  * chunk_chain_kernel, one workgroup per (sequence, head, value block): the state waves
+//    of chunk_fwd_kernel (the serial part), fed by four copy waves that move each package
+//    from the workspace into a double-buffered LDS area and form beta V; one barrier per
+//    chunk.
+//
+// Chunk slots: without cu_seqlens slot b * NC + j (NC = ceil(T / C)) is chunk j of batch
+// row b; with them, sequence s owns slots floor(cu[s] / C) + s + j for j < ceil(len_s / C)
+// (disjoint, fewer than T / C + N in all); a slot no sequence owns is left unwritten.
+#pragma once
+
+#include "kda_chunk_kernel.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int PPW = 8;          // waves of a pre-pass workgroup
+constexpr int PPT = 64 * PPW;
+constexpr int NCW = 4;          // copy waves of the chain kernel
+constexpr int NTC = 64 * (NSW + NCW);
+
+// One package in the workspace, dense, byte offsets: Qt and -Bw [C][K], Kt [K][C] (token
+// index contiguous, the LDS operand order), T and A_qk [C][C] (upper blocks zero), all in
+// the matrix-operand type; gamma_C [K] and beta [C] (0 on padding rows) in float32.
+template <class P, int K, int C>
+struct PackLayout {
+    using TM = typename P::TM;
+    static constexpr size_t gQt = 0;
+    static constexpr size_t gBw = gQt + (size_t)C * K * sizeof(TM);
+    static constexpr size_t gKt = gBw + (size_t)C * K * sizeof(TM);
+    static constexpr size_t gTm = gKt + (size_t)K * C * sizeof(TM);
+    static constexpr size_t gAqk = gTm + (size_t)C * C * sizeof(TM);
+    static constexpr size_t gGC = gAqk + (size_t)C * C * sizeof(TM);
+    static constexpr size_t gBt = gGC + (size_t)K * 4;
+    static constexpr size_t bytes = gBt + (size_t)C * 4;
+    static_assert(bytes % 16 == 0, "packages stay 16-byte aligned");
+};
+
+// LDS of the pre-pass: the chunk kernel's staging area, then T and A_qk (row stride LCM)
+// where a package's Tm and Aqk would sit, so a_matrix_work writes them unchanged.
+template <class P, int K, int C>
+struct PrepassLds {
+    using L = Layout<P, K, 16, C, 16>;
+    static constexpr size_t oTA = L::oPkg;
+    static constexpr size_t total = oTA + (L::pbV - L::pTm);
+    static_assert(L::oPkg >= L::pTm, "the package base lies inside the workgroup's LDS");
+    static constexpr bool fits = total <= 160 * 1024;
+};
+
+template <class P, int K, int V, int C, int BV>
+struct ChainLds {
+    static constexpr size_t total = 2 * Layout<P, K, V, C, BV>::szPkg;
+    static constexpr bool fits = total <= 160 * 1024;
+};
+
+// first token row and length of the chunk in slot n (length 0: no sequence owns it)
+template <int C>
+__device__ __forceinline__ void slot_span(int n, const int32_t *cu, int N, int64_t T, int64_t &t0, int &len) {
+    if (!cu) {
+        const int NC = (int)((T + C - 1) / C);
+        const int b = n / NC, j = n - b * NC;
+        t0 = (int64_t)b * T + (int64_t)j * C;
+        len = (int)min((int64_t)C, T - (int64_t)j * C);
+        return;
+    }
+    int lo = 0, hi = N - 1;  // last sequence whose first slot is <= n
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] / C + mid <= n) lo = mid;
+        else hi = mid - 1;
+    }
+    const int64_t a0 = cu[lo], l = (int64_t)cu[lo + 1] - a0;
+    const int64_t off = (int64_t)(n - (cu[lo] / C + lo)) * C;
+    t0 = a0 + off;
+    len = off < l ? (int)min((int64_t)C, l - off) : 0;
+}
+
+// GM as in chunk_fwd_kernel.  Persistent: workgroup b takes items b, b + G, ... of the
+// slots * H (chunk slot, head) items (slot-major, heads adjacent), skipping slots no
+// sequence owns, and has the raw inputs of its next item in flight while it works on the
+// current one.
+template <class P, int K, int C, int GM>
+__global__ __launch_bounds__(PPT) void chunk_pack_kernel(ChunkArgs a) {
+    constexpr bool ZG = GM >= 1;
+    constexpr bool NORM = GM == 2;
+    using L = Layout<P, K, 16, C, 16>;
+    using PL = PackLayout<P, K, C>;
+    using TA = typename P::TA;
+    using TM = typename P::TM;
+    using TIn = typename std::conditional<std::is_same<P, PrecF32>::value, float, __bf16>::type;
+    constexpr int NP = L::NP;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int H = a.H;
+    // items: without cu_seqlens, chunks [c0, c1) of every batch row (b, c, h order); with
+    // them, every chunk slot (slot-major).  Fewer than 2^31 (checked by the host).
+    const int NC = (int)((a.T + C - 1) / C);
+    const int c0 = a.c_begin < NC ? a.c_begin : NC;
+    const int W = (a.c_end < NC ? a.c_end : NC) - c0;
+    const int nitems = a.cu_seqlens ? a.pack_slots * H : (a.pack_slots / NC) * W * H;
+    const int G = (int)gridDim.x;
+
+    TA *Lk = reinterpret_cast<TA *>(smem + L::oLk);
+    TA *St = reinterpret_cast<TA *>(smem + L::oSt);
+    float *TPv = reinterpret_cast<float *>(smem + L::oTP);
+    float *Btv = reinterpret_cast<float *>(smem + L::oBt);
+    float *Nrm = reinterpret_cast<float *>(smem + L::oNrm);
+    float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
+    float *Tf = reinterpret_cast<float *>(smem + L::oTf);
+    using PXL = PrepassLds<P, K, C>;
+    TM *TmL = reinterpret_cast<TM *>(smem + PXL::oTA);
+    TM *AqL = reinterpret_cast<TM *>(smem + PXL::oTA + (L::pAqk - L::pTm));
+
+    // the strictly upper 16x16 blocks of T and A_qk are zero in every item (nothing else
+    // writes them); the first barrier below orders this before any read
+    for (int e = threadIdx.x; e < C * C; e += PPT) {
+        const int i = e / C, j = e % C;
+        if ((j >> 4) > (i >> 4)) {
+            TmL[i * L::LCM + j] = from_f32<TM>(0.f);
+            AqL[i * L::LCM + j] = from_f32<TM>(0.f);
+        }
+    }
+
+    // the next item at or after `from` whose slot some sequence owns (nitems if none)
+    struct Item {
+        int n, h, len;
+        int64_t t0;
+    };
+    auto find = [&](int from, Item &x) -> int {
+        for (int it = from; it < nitems; it += G) {
+            if (a.cu_seqlens) {
+                x.n = it / H;
+                x.h = it - x.n * H;
+            } else {
+                const int b = it / (W * H), rem = it - b * (W * H), c = rem / H;
+                x.h = rem - c * H;
+                x.n = b * NC + c0 + c;
+            }
+            slot_span<C>(x.n, a.cu_seqlens, a.num_seqs, a.T, x.t0, x.len);
+            if (x.len > 0) return it;
+        }
+        return nitems;
+    };
+
+    // Mapping as in the chunk kernel's prep waves: a combo is a (channel pair, 16-row
+    // tile), handled by lanes l, l + 16, l + 32, l + 48 of one wave (rows 0..3, 4..7,
+    // 8..11, 12..15 of the tile).
+    constexpr int NCP = K / 2;
+    constexpr int NCOMBO = NCP * NP;
+    constexpr int CPR = 16 * PPW;
+    constexpr int CPT = (NCOMBO + CPR - 1) / CPR;
+    using RawPair = typename std::conditional<std::is_same<TIn, float>::value, float2, uint32_t>::type;
+    using RawGate = typename std::conditional<ZG, RawPair, float2>::type;
+    auto pair_f32 = [&](RawPair x, float &lo, float &hi) {
+        if constexpr (std::is_same<RawPair, float2>::value) {
+            lo = x.x;
+            hi = x.y;
+        } else {
+            lo = __builtin_bit_cast(float, x << 16);
+            hi = __builtin_bit_cast(float, x & 0xffff0000u);
+        }
+    };
+    // raw inputs of one item, loaded unconditionally (rows past the end read the last row)
+    RawGate rg[CPT][4];
+    RawPair rq[CPT][4], rk[CPT][4];
+    float2 rzb[CPT];
+    float rbeta, rls;
+    auto fetch = [&](const Item &x) {
+        // the thread index, hidden from loop-invariant code motion: the per-combo offsets
+        // are recomputed per item instead of being held in registers across the loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = tid >> 6, qd = lane >> 4;
+        const int last = x.len - 1;
+        const int rs = H * K;
+        const int64_t cb = (x.t0 * H + x.h) * K;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            int cm = CPR * u + 16 * wave + (lane & 15);
+            cm = cm < NCOMBO ? cm : 0;
+            const int c0 = 2 * (cm % NCP), p = cm / NCP;
+            rzb[u] = float2{0.f, 0.f};
+            if constexpr (ZG) {
+                if (a.gate.bias) rzb[u] = *reinterpret_cast<const float2 *>(a.gate.bias + x.h * K + c0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * p + 4 * qd + i;
+                const uint32_t o = (uint32_t)((r < last ? r : last) * rs + c0);
+                if constexpr (ZG)
+                    rg[u][i] = ld_at<RawGate>(static_cast<const TIn *>(a.gate.logits) + cb, o * (uint32_t)sizeof(TIn));
+                else
+                    rg[u][i] = ld_at<RawGate>(a.gate.gate + cb, 4u * o);
+                rq[u][i] = ld_at<RawPair>(static_cast<const TIn *>(a.q) + cb, o * (uint32_t)sizeof(TIn));
+                rk[u][i] = ld_at<RawPair>(static_cast<const TIn *>(a.k) + cb, o * (uint32_t)sizeof(TIn));
+            }
+        }
+        rbeta = ld_at<float>(a.beta + x.t0 * H + x.h, 4u * (uint32_t)((tid < last ? tid : last) * H));
+        if constexpr (ZG) rls = a.gate.log_scale[x.h];
+    };
+
+    Item cur;
+    int item = find(blockIdx.x, cur);
+    if (item < nitems) fetch(cur);
+    while (item < nitems) {  // workgroup-uniform
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, qd = lane >> 4;
+        const int h = cur.h, last = cur.len - 1;
+        unsigned char *gp = a.pack + ((size_t)cur.n * H + h) * PL::bytes;
+        auto combo_of = [&](int u) { return CPR * u + 16 * wave + (lane & 15); };
+
+        // ---- phase 1: retention factors (1 on padding rows), tile totals, beta --------
+        const bool glog = a.gate.mode == GATE_LOG;
+        float gs2 = 0.f, gl2 = 0.f;
+        if constexpr (ZG) {
+            gs2 = expf(rls) * 1.44269504088896341f;  // e^A log2(e)
+            gl2 = a.gate.lower_bound * 1.44269504088896341f;
+        }
+        float2 ral[CPT][4], fq[CPT][4], fk[CPT][4];
+        float2 pin[CPT], sin[CPT];
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float2 al;
+                if constexpr (ZG) {
+                    float z0, z1;
+                    if constexpr (std::is_same<RawGate, float2>::value) {
+                        z0 = rg[u][i].x;
+                        z1 = rg[u][i].y;
+                    } else {
+                        pair_f32(rg[u][i], z0, z1);
+                    }
+                    al = float2{fast_bounded_alpha(z0 + rzb[u].x, gs2, gl2), fast_bounded_alpha(z1 + rzb[u].y, gs2, gl2)};
+                } else {
+                    al = rg[u][i];
+                    if (glog) al = float2{__expf(al.x), __expf(al.y)};
+                }
+                float q0, q1, k0, k1;
+                pair_f32(rq[u][i], q0, q1);
+                pair_f32(rk[u][i], k0, k1);
+                ral[u][i] = al;
+                fq[u][i] = float2{q0, q1};
+                fk[u][i] = float2{k0, k1};
+            }
+        }
+        if (last < C - 1) {  // a partial chunk (workgroup-uniform): padding rows get alpha 1, q = k = 0
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u);
+                const int p = (cm < NCOMBO ? cm : 0) / NCP;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (16 * p + 4 * qd + i > last) {
+                        ral[u][i] = float2{1.f, 1.f};
+                        fq[u][i] = float2{0.f, 0.f};
+                        fk[u][i] = float2{0.f, 0.f};
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int cm = combo_of(u);
+            const bool valid = cm < NCOMBO;
+            const int cmc = valid ? cm : 0;
+            const int c0 = 2 * (cmc % NCP), p = cmc / NCP;
+            float2 run = {1.f, 1.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                run.x *= ral[u][i].x;
+                run.y *= ral[u][i].y;
+            }
+            // the four quarters' products: lane quarter qd ^ d sends its own
+            float2 xq[4];
+            xq[0] = run;
+            xq[1] = float2{__shfl_xor(run.x, 16), __shfl_xor(run.y, 16)};
+            xq[2] = float2{__shfl_xor(run.x, 32), __shfl_xor(run.y, 32)};
+            xq[3] = float2{__shfl_xor(run.x, 48), __shfl_xor(run.y, 48)};
+            float2 qp[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = qd ^ j;
+                qp[j] = d == 0 ? xq[0] : d == 1 ? xq[1] : d == 2 ? xq[2] : xq[3];
+            }
+            float2 pi = {1.f, 1.f}, si = {1.f, 1.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < qd) { pi.x *= qp[j].x; pi.y *= qp[j].y; }
+                if (j > qd) { si.x *= qp[j].x; si.y *= qp[j].y; }
+            }
+            pin[u] = pi;
+            sin[u] = si;
+            if (qd == 0 && valid)
+                *reinterpret_cast<float2 *>(TPv + p * K + c0) =
+                    float2{(qp[0].x * qp[1].x) * (qp[2].x * qp[3].x), (qp[0].y * qp[1].y) * (qp[2].y * qp[3].y)};
+            if constexpr (NORM) {
+                // row sums of q^2 (0..3) and k^2 (4..7) over this tile's channel pairs
+                float x2[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x2[i] = fq[u][i].x * fq[u][i].x + fq[u][i].y * fq[u][i].y;
+                    x2[4 + i] = fk[u][i].x * fk[u][i].x + fk[u][i].y * fk[u][i].y;
+                }
+                constexpr int NG = NCP < 16 ? NCP : 16;
+                static_assert(NG == 8 || NG == 16, "8 or 16 lanes share a tile row");
+                int base = 0;
+                halve_sums<4, true, NG / 2>(x2, lane, base);
+                halve_sums<2, true, NG / 4>(x2, lane, base);
+                halve_sums<1, true, NG / 8>(x2, lane, base);
+                if constexpr (NG == 16) x2[0] += __shfl_xor(x2[0], 1);
+                if (valid && (NG != 16 || (lane & 1) == 0)) {
+                    const int part = (cm % NCP) / 16;
+                    Nrm[((p * 2 + (base >> 2)) * 16 + 4 * qd + (base & 3)) * L::NPART + part] = x2[0];
+                }
+            }
+        }
+        if (tid < C) {
+            const float b = a.beta_logits ? __builtin_amdgcn_rcpf(1.f + __expf(-rbeta)) : rbeta;
+            const float bt = tid <= last ? b : 0.f;
+            Btv[tid] = bt;
+            reinterpret_cast<float *>(gp + PL::gBt)[tid] = bt;
+        }
+        // the raw inputs are consumed: send the next item's loads
+        Item nx;
+        const int nxt = find(item + G, nx);
+        fetch(nxt < nitems ? nx : cur);
+        lds_barrier();
+
+        // ---- phase 2: A-matrix operand staging and the package's Qt, -Bw, Kt, gamma_C --
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int cm = combo_of(u);
+            if (cm >= NCOMBO) continue;
+            const int c0 = 2 * (cm % NCP), p = cm / NCP;
+            float2 tpr[NP];
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp) tpr[pp] = *reinterpret_cast<const float2 *>(TPv + pp * K + c0);
+            float2 eR = {1.f, 1.f}, eCE = {1.f, 1.f}, eAll = {1.f, 1.f}, own = {1.f, 1.f};
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp) {
+                if (pp < p) { eR.x *= tpr[pp].x; eR.y *= tpr[pp].y; }
+                if (pp > p) { eCE.x *= tpr[pp].x; eCE.y *= tpr[pp].y; }
+                if (pp == p) own = tpr[pp];
+                eAll.x *= tpr[pp].x;
+                eAll.y *= tpr[pp].y;
+            }
+            if (p == 0 && qd == 0) st2_at<float>(gp, (uint32_t)(PL::gGC + 4 * c0), eAll.x, eAll.y);
+            const float2 rT = {__builtin_amdgcn_rcpf(own.x), __builtin_amdgcn_rcpf(own.y)};
+            float2 xf[NP];  // extra right-operand factors for tiles (pp, p), pp >= p + 2
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp) {
+                float2 f = {1.f, 1.f};
+#pragma unroll
+                for (int r2 = 0; r2 < NP; ++r2)
+                    if (r2 > p && r2 < pp) { f.x *= tpr[r2].x; f.y *= tpr[r2].y; }
+                xf[pp] = f;
+            }
+            float bet[4];
+            {
+                const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + 4 * qd);
+                bet[0] = b4.x; bet[1] = b4.y; bet[2] = b4.z; bet[3] = b4.w;
+            }
+            float2 suf[4];  // E_p / gamma_i
+            {
+                float2 run = sin[u];
+#pragma unroll
+                for (int i = 3; i >= 0; --i) {
+                    suf[i] = run;
+                    run.x *= ral[u][i].x;
+                    run.y *= ral[u][i].y;
+                }
+            }
+            float iq[4], ik[4];  // reciprocal row norms (1 without normalisation)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                iq[i] = 1.f;
+                ik[i] = 1.f;
+                if constexpr (NORM) {
+                    float nq = 0.f, nk = 0.f;
+#pragma unroll
+                    for (int pt = 0; pt < L::NPART; ++pt) {
+                        nq += Nrm[((p * 2 + 0) * 16 + 4 * qd + i) * L::NPART + pt];
+                        nk += Nrm[((p * 2 + 1) * 16 + 4 * qd + i) * L::NPART + pt];
+                    }
+                    iq[i] = __builtin_amdgcn_rsqf(fmaxf(nq, 1e-12f));
+                    ik[i] = __builtin_amdgcn_rsqf(fmaxf(nk, 1e-12f));
+                }
+            }
+            float2 pre = pin[u];  // gamma_i / R_p
+            float2 kro[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * p + 4 * qd + i;
+                pre.x *= ral[u][i].x;
+                pre.y *= ral[u][i].y;
+                const float2 q2 = fq[u][i], k2 = fk[u][i];
+                const float2 lq = {q2.x * pre.x, q2.y * pre.y};
+                const float2 lk = {bet[i] * k2.x * pre.x, bet[i] * k2.y * pre.y};
+                const float2 ro = {k2.x * suf[i].x, k2.y * suf[i].y};  // k E_p / gamma <= |k|
+                const float2 rd = {ro.x * rT.x, ro.y * rT.y};        // k R_p / gamma <= e^80 |k|
+                st2<TA>(Lk + r * L::LKA + c0, lk.x, lk.y);
+                st2_stage<P>(St + L::sLq + r * L::LKS + c0, L::NST, lq.x, lq.y);
+                st2_stage<P>(St + L::sRd + r * L::LKS + c0, L::NST, rd.x, rd.y);
+                if (p < NP - 1) st2_stage<P>(St + L::sRo + r * L::LKS + c0, L::NST, ro.x, ro.y);
+                if constexpr (L::NX > 0) {
+                    int xi = 0;
+#pragma unroll
+                    for (int pp = 2; pp < NP; ++pp)
+#pragma unroll
+                        for (int qq = 0; qq + 2 <= pp; ++qq, ++xi)
+                            if (qq == p)
+                                st2_stage<P>(St + L::sX + (xi * 16 + 4 * qd + i) * L::LKS + c0, L::NST,
+                                             ro.x * xf[pp].x, ro.y * xf[pp].y);
+                }
+                constexpr uint32_t E = sizeof(TM);
+                st2_at<TM>(gp, (uint32_t)PL::gQt + E * (uint32_t)(r * K + c0), lq.x * eR.x * iq[i], lq.y * eR.y * iq[i]);
+                st2_at<TM>(gp, (uint32_t)PL::gBw + E * (uint32_t)(r * K + c0), -lk.x * eR.x * ik[i], -lk.y * eR.y * ik[i]);
+                kro[i] = float2{ro.x * eCE.x * ik[i], ro.y * eCE.y * ik[i]};
+                if (i & 1) {
+                    // two consecutive tokens per channel row of Kt
+                    st2_at<TM>(gp, (uint32_t)PL::gKt + E * (uint32_t)(c0 * C + r - 1), kro[i - 1].x, kro[i].x);
+                    st2_at<TM>(gp, (uint32_t)PL::gKt + E * (uint32_t)((c0 + 1) * C + r - 1), kro[i - 1].y, kro[i].y);
+                }
+            }
+        }
+        lds_barrier();
+
+        // ---- phase 3: A-matrix tiles, T's diagonal blocks, A_qk ------------------------
+        a_matrix_work<P, K, 16, C, 16, NORM, PPW>(smem, smem + PXL::oTA - L::pTm, 0, wave, lane);
+        lds_barrier();
+
+        // ---- phase 4: T's off-diagonal blocks.  Block column qb depends only on itself
+        // (T_pq = -T_pp sum_{r=q}^{p-1} A_pr T_rq), so wave qb fills column qb top down.
+        if (NP > 1 && wave < NP - 1) {
+            const int qb = wave;
+            for (int p = qb + 1; p < NP; ++p) {
+                f4 m = {0.f, 0.f, 0.f, 0.f};
+                for (int r = qb; r < p; ++r)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        m = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            Akk[(p * 16 + (lane & 15)) * L::LCF + r * 16 + 4 * s4 + g],
+                            Tf[(r * 16 + 4 * s4 + g) * L::LCF + qb * 16 + (lane & 15)], m, 0, 0, 0);
+                f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(Tf[(p * 16 + (lane & 15)) * L::LCF + p * 16 + 4 * g + s4],
+                                                             m[s4], t, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = p * 16 + 4 * g + e, j = qb * 16 + (lane & 15);
+                    Tf[i * L::LCF + j] = -t[e];
+                    TmL[i * L::LCM + j] = from_f32<TM>(-t[e]);
+                }
+                lds_fence();
+            }
+        }
+        lds_barrier();
+
+        // ---- T and A_qk to the package, 16 bytes per lane ------------------------------
+        // (the next item's phase 1 touches neither these nor the staging area, and its
+        // first barrier comes before anything here is written again)
+        constexpr int RC = C * (int)sizeof(TM) / 16;  // 16-byte pieces per row
+        for (int e = tid; e < 2 * C * RC; e += PPT) {
+            const int mat = e / (C * RC), rem = e - mat * C * RC;
+            const int row = rem / RC, pc = rem - row * RC;
+            const TM *src = (mat ? AqL : TmL) + row * L::LCM;
+            const uint4 x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(src) + 16 * pc);
+            *reinterpret_cast<uint4 *>(gp + (mat ? PL::gAqk : PL::gTm) + (size_t)row * C * sizeof(TM) + 16 * pc) = x;
+        }
+        item = nxt;
+        cur = nx;
+    }
+}
+
+// The chain kernel: state waves as in chunk_fwd_kernel, copy waves for the packages.
+template <class P, int K, int V, int C, int BV>
+__global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
+    using L = Layout<P, K, V, C, BV>;
+    using PL = PackLayout<P, K, C>;
+    using TM = typename P::TM;
+    using TIn = typename std::conditional<std::is_same<P, PrecF32>::value, float, __bf16>::type;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    constexpr int NVB = V / BV;
+    const int G = gridDim.x;
+    int lin = blockIdx.x;
+    if ((G & 7) == 0) lin = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // a head's value blocks
+    const int vb = lin % NVB;                                                   // share one XCD
+    const int pair = lin / NVB;
+    const int H = a.H;
+    const int h = pair % H;
+    const int s = pair / H;
+    int64_t bos, eos;
+    int base;  // first chunk slot of the sequence
+    if (a.cu_seqlens) {
+        bos = a.cu_seqlens[s];
+        eos = a.cu_seqlens[s + 1];
+        base = (int)(bos / C) + s;
+    } else {
+        bos = (int64_t)s * a.T;
+        eos = bos + a.T;
+        base = s * (int)((a.T + C - 1) / C);
+    }
+    // this launch's chunks of the sequence: [c_begin, c_end) clipped to it (the state
+    // comes in through a.initial_state and leaves through a.final_state)
+    const int nall = (int)((eos - bos + C - 1) / C);
+    const int cfirst = a.c_begin < nall ? a.c_begin : nall;
+    const int nchunks = (a.c_end < nall ? a.c_end : nall) - cfirst;
+    bos += (int64_t)cfirst * C;
+    base += cfirst;
+
+    // The pre-pass of the next chunk segment may share these compute units: the serial part
+    // issues first, then the copy waves that feed it.
+    if (wave < NSW) {
+        __builtin_amdgcn_s_setprio(3);
+        state_waves<P, K, V, C, BV, false, true>(a, smem, smem, s, h, vb, bos, eos, nchunks, wave, lane);
+        return;
+    }
+    __builtin_amdgcn_s_setprio(2);
+
+    // ====================================== copy waves =======================================
+    constexpr int NCT = 64 * NCW;
+    const int tp = tid - NSW * 64;
+    // 16-byte pieces of a package in workspace order (Qt, Bw, Kt, T, A_qk, gamma_C), each
+    // with its LDS destination; beta is read separately.
+    constexpr int RQ = K * (int)sizeof(TM) / 16, RC = C * (int)sizeof(TM) / 16;
+    constexpr int NQ = C * RQ, NKT = K * RC, NCC = C * RC, NGC = K * 4 / 16;
+    constexpr int NPC = 2 * NQ + NKT + 2 * NCC + NGC;
+    static_assert(PL::gGC + 16 * NGC == PL::gBt, "the pieces cover the package up to beta");
+    constexpr int CPT = (NPC + NCT - 1) / NCT;
+    uint32_t src[CPT], dst[CPT];
+#pragma unroll
+    for (int w = 0; w < CPT; ++w) {
+        int e = tp + NCT * w;
+        e = e < NPC ? e : NPC - 1;  // surplus lanes repeat the last piece (same value, same place)
+        src[w] = 16u * (uint32_t)e;
+        uint32_t d;
+        if (e < NQ) {
+            d = (uint32_t)(L::pQt + (e / RQ) * L::LKM * sizeof(TM) + 16 * (e % RQ));
+        } else if (e < 2 * NQ) {
+            const int x = e - NQ;
+            d = (uint32_t)(L::pBw + (x / RQ) * L::LKM * sizeof(TM) + 16 * (x % RQ));
+        } else if (e < 2 * NQ + NKT) {
+            const int x = e - 2 * NQ;
+            d = (uint32_t)(L::pKt + (x / RC) * L::LCM * sizeof(TM) + 16 * (x % RC));
+        } else if (e < 2 * NQ + NKT + NCC) {
+            const int x = e - 2 * NQ - NKT;
+            d = (uint32_t)(L::pTm + (x / RC) * L::LCM * sizeof(TM) + 16 * (x % RC));
+        } else if (e < 2 * NQ + NKT + 2 * NCC) {
+            const int x = e - 2 * NQ - NKT - NCC;
+            d = (uint32_t)(L::pAqk + (x / RC) * L::LCM * sizeof(TM) + 16 * (x % RC));
+        } else {
+            d = (uint32_t)(L::pGC + 16 * (e - 2 * NQ - NKT - 2 * NCC));
+        }
+        dst[w] = d;
+    }
+    // beta V items: four value columns of two consecutive tokens
+    using RawV = typename std::conditional<std::is_same<TIn, float>::value, float4, uint2>::type;
+    constexpr int NVI = BV / 4 * (C / 2);
+    constexpr int VPT = (NVI + NCT - 1) / NCT;
+    // Inputs of DP chunks in flight at once (register sets, by chunk index mod DP).
+    constexpr int DP = 1;
+    uint4 buf[DP][CPT];
+    RawV rv[DP][VPT][2];
+    float2 rb[DP][VPT];
+    auto load = [&](int cn, uint4 (&buf)[CPT], RawV (&rv)[VPT][2], float2 (&rb)[VPT]) {
+        const int64_t t0 = bos + (int64_t)cn * C;
+        const int last = (int)((eos - t0) < C ? (eos - t0) : C) - 1;
+        const unsigned char *gp = a.pack + ((size_t)(base + cn) * H + h) * PL::bytes;
+#pragma unroll
+        for (int w = 0; w < CPT; ++w) buf[w] = ld_at<uint4>(gp, src[w]);
+        const unsigned char *vbp = static_cast<const unsigned char *>(a.v) + ((t0 * H + h) * V + vb * BV) * sizeof(TIn);
+#pragma unroll
+        for (int w = 0; w < VPT; ++w) {
+            int e = tp + NCT * w;
+            e = e < NVI ? e : NVI - 1;
+            const int j = 4 * (e % (BV / 4)), r = 2 * (e / (BV / 4));
+            const int r0 = r < last ? r : last, r1 = r + 1 < last ? r + 1 : last;
+            rv[w][0] = ld_at<RawV>(vbp, (uint32_t)sizeof(TIn) * (uint32_t)(r0 * H * V + j));
+            rv[w][1] = ld_at<RawV>(vbp, (uint32_t)sizeof(TIn) * (uint32_t)(r1 * H * V + j));
+            rb[w] = ld_at<float2>(gp, (uint32_t)(PL::gBt + 4 * r));
+        }
+    };
+    auto raw4 = [](RawV x, float (&f)[4]) {
+        if constexpr (std::is_same<TIn, float>::value) {
+            f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
+        } else {
+            f[0] = __builtin_bit_cast(float, x.x << 16);
+            f[1] = __builtin_bit_cast(float, x.x & 0xffff0000u);
+            f[2] = __builtin_bit_cast(float, x.y << 16);
+            f[3] = __builtin_bit_cast(float, x.y & 0xffff0000u);
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < DP; ++d)
+        if (d < nchunks) load(d, buf[d], rv[d], rb[d]);
+    for (int it0 = 0; it0 <= nchunks; it0 += DP) {
+#pragma unroll
+        for (int d = 0; d < DP; ++d) {  // register set d holds chunk it = it0 + d
+            const int it = it0 + d;
+            if (it > nchunks) break;  // workgroup-uniform
+            if (it < nchunks) {
+                unsigned char *pk = smem + (size_t)(it & 1) * L::szPkg;
+#pragma unroll
+                for (int w = 0; w < CPT; ++w) *reinterpret_cast<uint4 *>(pk + dst[w]) = buf[d][w];
+                TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
+#pragma unroll
+                for (int w = 0; w < VPT; ++w) {
+                    int e = tp + NCT * w;
+                    e = e < NVI ? e : NVI - 1;
+                    const int j = 4 * (e % (BV / 4)), r = 2 * (e / (BV / 4));
+                    float f0[4], f1[4];
+                    raw4(rv[d][w][0], f0);
+                    raw4(rv[d][w][1], f1);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        st2<TM>(bV + (j + x) * L::LCM + r, f0[x] * rb[d][w].x, f1[x] * rb[d][w].y);
+                }
+                if (it + DP < nchunks) load(it + DP, buf[d], rv[d], rb[d]);  // consumed DP periods on
+            }
+            lds_barrier();  // the one barrier of the period: package it is in LDS
+        }
+    }
+}
+
+template <class P, int K, int V, int C>
+constexpr int pick_chain_bv() {
+    if constexpr (V >= 64 && ChainLds<P, K, V, C, 64>::fits) return 64;
+    else if constexpr (V >= 32 && ChainLds<P, K, V, C, 32>::fits) return 32;
+    else if constexpr (ChainLds<P, K, V, C, 16>::fits) return 16;
+    else return 0;
+}
+
+template <class P, int GM, int K, int C>
+hipError_t launch_pack_kc(const ChunkArgs &a, int64_t items, int max_wgs, hipStream_t stream) {
+    using X = PrepassLds<P, K, C>;
+    if constexpr (!X::fits) {
+        return hipErrorNotSupported;
+    } else {
+        auto kern = chunk_pack_kernel<P, K, C, GM>;
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)X::total);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        // persistent: at most as many workgroups as fit at once (LDS-bound), max_wgs and items
+        const int per_cu = (int)(160 * 1024 / X::total) < 4 ? (int)(160 * 1024 / X::total) : 4;
+        int64_t grid = (int64_t)device_cu_count() * per_cu;
+        if (max_wgs > 0 && grid > max_wgs) grid = max_wgs;
+        if (grid > items) grid = items;
+        if (grid <= 0) return hipSuccess;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(PPT), X::total, stream, a);
+        return hipGetLastError();
+    }
+}
+
+template <class P, int GM>
+hipError_t launch_pack_p(const ChunkArgs &a, int K, int C, int64_t items, int max_wgs, hipStream_t stream) {
+#define KDA_PACK_C(KK)                                                         \
+    switch (C) {                                                               \
+        case 16: return launch_pack_kc<P, GM, KK, 16>(a, items, max_wgs, stream);     \
+        case 32: return launch_pack_kc<P, GM, KK, 32>(a, items, max_wgs, stream);     \
+        case 64: return launch_pack_kc<P, GM, KK, 64>(a, items, max_wgs, stream);     \
+        default: return hipErrorNotSupported;                                  \
+    }
+    switch (K) {
+        case 16: KDA_PACK_C(16)
+        case 32: KDA_PACK_C(32)
+        case 64: KDA_PACK_C(64)
+        case 128: KDA_PACK_C(128)
+        default: return hipErrorNotSupported;
+    }
+#undef KDA_PACK_C
+}
+
+template <class P, int K, int V, int C>
+hipError_t launch_chain_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream, int *bv_out) {
+    constexpr int BV = pick_chain_bv<P, K, V, C>();
+    if constexpr (BV == 0 || !PrepassLds<P, K, C>::fits) {
+        return hipErrorNotSupported;
+    } else {
+        using X = ChainLds<P, K, V, C, BV>;
+        if (bv_out) *bv_out = BV;
+        if (!a.q) return hipSuccess;  // query only
+        auto kern = chunk_chain_kernel<P, K, V, C, BV>;
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)X::total);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        hipLaunchKernelGGL(kern, dim3(num_pairs * (V / BV)), dim3(NTC), X::total, stream, a);
+        return hipGetLastError();
+    }
+}
+
+template <class P>
+hipError_t launch_chain_p(const ChunkArgs &a, int K, int V, int C, int num_pairs, hipStream_t stream, int *bv) {
+#define KDA_CHAIN_C(KK, VV)                                                          \
+    switch (C) {                                                                     \
+        case 16: return launch_chain_kvc<P, KK, VV, 16>(a, num_pairs, stream, bv);   \
+        case 32: return launch_chain_kvc<P, KK, VV, 32>(a, num_pairs, stream, bv);   \
+        case 64: return launch_chain_kvc<P, KK, VV, 64>(a, num_pairs, stream, bv);   \
+        default: return hipErrorNotSupported;                                        \
+    }
+#define KDA_CHAIN_V(KK)                        \
+    switch (V) {                               \
+        case 16: KDA_CHAIN_C(KK, 16)           \
+        case 32: KDA_CHAIN_C(KK, 32)           \
+        case 64: KDA_CHAIN_C(KK, 64)           \
+        case 128: KDA_CHAIN_C(KK, 128)         \
+        default: return hipErrorNotSupported;  \
+    }
+    switch (K) {
+        case 16: KDA_CHAIN_V(16)
+        case 32: KDA_CHAIN_V(32)
+        case 64: KDA_CHAIN_V(64)
+        case 128: KDA_CHAIN_V(128)
+        default: return hipErrorNotSupported;
+    }
+#undef KDA_CHAIN_V
+#undef KDA_CHAIN_C
+}
+
+}  // namespace
+
+}  // namespace kda

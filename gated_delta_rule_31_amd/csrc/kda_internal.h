@@ -36,6 +36,11 @@ struct ChunkArgs {
     int qk_l2norm;                  // q, k divided by their L2 norm over K in the kernel
     int beta_logits;                // beta holds logits; the kernel applies sigmoid
     int state_vk;                   // states are [N, H, V, K] (K contiguous)
+    int num_seqs;                   // N with cu_seqlens
+    unsigned char *pack;            // two-kernel form: per (chunk slot, head) packages, or null
+    int pack_slots;                 // chunk slots per head in `pack`
+    int c_begin, c_end;             // two-kernel form, without cu_seqlens: chunks [c_begin, c_end) of
+                                    // every sequence (the pre-pass's items, the chain's steps)
 };
 
 struct StepArgs {
@@ -140,6 +145,26 @@ hipError_t launch_chunk_fwd_logits(const ChunkArgs &a, bool fp32_inputs, int K, 
 // value-block width the chunk kernel uses for this shape, 0 if the shape is not compiled
 // (its LDS layout would exceed 160 KB)
 int chunk_fwd_value_block(bool fp32_inputs, int K, int V, int C);
+// Two-kernel form (a.pack != null): the pre-pass writes one package per (chunk slot, head),
+// the chain kernel consumes them.  Chunk slots per head, package bytes (0 if the form does
+// not support the shape), and the launch of both kernels.
+int64_t chunk_fwd_slots(int B, int64_t T, int num_seqs, bool varlen, int C);
+size_t chunk_pack_bytes(bool fp32_inputs, int K, int V, int C);
+// workspace bytes of the two-kernel form: the packages, then one float32 state per
+// (sequence, head) carried between the chunk segments of one call
+size_t chunk_fwd_workspace_bytes(bool fp32_inputs, int64_t slots, int64_t N, int H, int K, int V, int C);
+hipError_t launch_chunk_fwd_two_pass(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
+                                     int64_t slots, hipStream_t stream, int *bv);
+// the pre-pass alone over `items` (chunk, head) items, at most max_wgs workgroups (0: as
+// many as fit); by gate mode (float32 gate, logits, logits with q/k normalisation)
+hipError_t launch_chunk_pack(const ChunkArgs &a, bool fp32_inputs, int K, int C, int64_t items, int max_wgs,
+                             hipStream_t stream);
+hipError_t launch_chunk_pack_logits(const ChunkArgs &a, bool fp32_inputs, int K, int C, int64_t items,
+                                    int max_wgs, hipStream_t stream);
+hipError_t launch_chunk_pack_logits_norm(const ChunkArgs &a, bool fp32_inputs, int K, int C, int64_t items,
+                                         int max_wgs, hipStream_t stream);
+hipError_t launch_chunk_chain(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
+                              hipStream_t stream, int *bv);
 hipError_t launch_recurrent_step(const StepArgs &a, bool fp32_inputs, int K, int V, int pairs,
                                  hipStream_t stream);
 hipError_t launch_recurrent_fwd(const RecurrentArgs &a, bool fp32_inputs, int K, int V, int num_pairs,
@@ -147,5 +172,7 @@ hipError_t launch_recurrent_fwd(const RecurrentArgs &a, bool fp32_inputs, int K,
 hipError_t launch_bounded_decay(const GateArgs &a, bool fp32_logits, hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for i < n
 hipError_t launch_fill_copy(float *dst, const float *src, int64_t n, hipStream_t stream);
+// compute units of the current device (queried once per device; 256 if the query fails)
+int device_cu_count();
 
 }  // namespace kda

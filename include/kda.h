@@ -46,7 +46,7 @@ extern "C" {
 
 /* 1: gate, chunk and step entry points; 2: adds the fused-gate variants and the
  * token-recurrent prefill; 3: adds the backward (kda_chunk_bwd, kda_bounded_decay_bwd) */
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -130,13 +130,35 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
  * below 6.5e4 in magnitude (they pass through fp16 matrix-core operands).
  * T == 0 (or B == 0): nothing is launched for the scan; final_state is set to
  * initial_state (copied unless the pointers are equal) or zeros.
+ *   workspace, workspace_bytes
+ *          NULL: one kernel per (sequence, head, value block) does all of a chunk's work.
+ *          Otherwise a device buffer, 16-byte aligned, of at least
+ *          kda_chunk_fwd_workspace_size() bytes, owned by the caller and overlapping no
+ *          other argument: a pre-pass over all (chunk, head) pairs at once forms each
+ *          chunk's state-independent products (the decayed query and key operands, T and
+ *          A_qk of the chunkwise form) into it, and a second kernel runs the serial part
+ *          from them (same results up to rounding order).  Its contents are scratch: they
+ *          are undefined after the call, and calls that share one workspace must not
+ *          overlap in time.  A shape the two-kernel form does not support (workspace size
+ *          0) returns KDA_ERR_UNSUPPORTED; a workspace too small or misaligned returns
+ *          KDA_ERR_BAD_ARGUMENT.
  */
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,
                          const float *gate, kda_gate_kind gate_kind, const float *beta,
                          const float *initial_state, float *final_state,
                          const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H, int K,
                          int V, int chunk_size, float scale, void *out, kda_dtype out_dtype,
-                         hipStream_t stream);
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_workspace_size -- host-only query: bytes of workspace the two-kernel form
+ * of kda_chunk_fwd / kda_chunk_fwd_fused_gate needs for this shape (varlen != 0: packed
+ * sequences, B == 1, T the total length, num_seqs sequences), or 0 if that form does not
+ * support it.  The size grows with the number of chunks: about 3 C K + 2 C^2 matrix
+ * operands (2 bytes each on the bf16 path, 4 on the float32 path) per (chunk, head).
+ */
+size_t kda_chunk_fwd_workspace_size(kda_dtype in_dtype, int B, int64_t T, int num_seqs, int varlen, int H,
+                                    int K, int V, int chunk_size);
 
 /*
  * kda_chunk_fwd_fused_gate -- kda_chunk_fwd with the gate applied inside the kernel
@@ -162,7 +184,8 @@ kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v,
                                     float lower_bound, unsigned flags, const float *beta, const float *initial_state,
                                     float *final_state, const int32_t *cu_seqlens, int num_seqs, int B,
                                     int64_t T, int H, int K, int V, int chunk_size, float scale, void *out,
-                                    kda_dtype out_dtype, hipStream_t stream);
+                                    kda_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /*
  * kda_recurrent_fwd -- the same operation as kda_chunk_fwd (same arguments, layouts,

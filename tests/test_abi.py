@@ -37,23 +37,23 @@ def test_status_strings_and_version(lib):
     assert lib.kda_status_string(0) == b"ok"
     for s in range(1, 8):
         assert lib.kda_status_string(s) not in (b"", b"unknown status")
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
 
 
 def _chunk(lib, **kw):
     vp = ctypes.c_void_p
     args = dict(q=1, k=2, v=3, in_dtype=1, gate=4, gate_kind=1, beta=5, s0=None, sf=None, cu=None,
-                num_seqs=0, B=1, T=64, H=2, K=16, V=16, C=16, scale=1.0, out=6, out_dtype=1)
+                num_seqs=0, B=1, T=64, H=2, K=16, V=16, C=16, scale=1.0, out=6, out_dtype=1, ws=None, ws_bytes=0)
     args.update(kw)
     f = lib.kda_chunk_fwd
     f.restype = ctypes.c_int
     f.argtypes = [vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
-                  vp, ctypes.c_int, vp]
+                  vp, ctypes.c_int, vp, ctypes.c_size_t, vp]
     a = args
     return f(a["q"], a["k"], a["v"], a["in_dtype"], a["gate"], a["gate_kind"], a["beta"], a["s0"], a["sf"],
              a["cu"], a["num_seqs"], a["B"], a["T"], a["H"], a["K"], a["V"], a["C"], a["scale"], a["out"],
-             a["out_dtype"], None)
+             a["out_dtype"], a["ws"], a["ws_bytes"], None)
 
 
 # Each case is rejected on the host before any HIP call (the pointers are fake); the same
@@ -64,6 +64,40 @@ def _chunk(lib, **kw):
     (dict(cu=9, B=2, num_seqs=1), 5), (dict(out=3), 6), (dict(sf=4), 6), (dict(sf=6), 6),
 ])
 def test_chunk_validation(lib, kw, status):
+    assert _chunk(lib, **kw) == status
+
+
+def _ws_size(lib, in_dtype=1, B=1, T=64, num_seqs=0, varlen=0, H=2, K=16, V=16, C=16):
+    f = lib.kda_chunk_fwd_workspace_size
+    f.restype = ctypes.c_size_t
+    i32 = ctypes.c_int
+    f.argtypes = [i32, i32, ctypes.c_int64, i32, i32, i32, i32, i32, i32]
+    return f(in_dtype, B, T, num_seqs, varlen, H, K, V, C)
+
+
+def test_chunk_workspace_size(lib):
+    # bf16 path, K = V = 128, C = 32: (3 C K + 2 C^2) fp16 operands + (K + C) floats per
+    # (chunk, head), T = 8192 being 256 chunks per head; then one float32 K x V state per
+    # (sequence, head)
+    per = 2 * (3 * 32 * 128 + 2 * 32 * 32) + 4 * (128 + 32)
+    st = 4 * 128 * 128
+    assert _ws_size(lib, T=8192, H=96, K=128, V=128, C=32) == 256 * 96 * per + 96 * st
+    # a ragged length rounds up; packed sequences get T / C + N slots
+    assert _ws_size(lib, T=8193, H=96, K=128, V=128, C=32) == 257 * 96 * per + 96 * st
+    assert _ws_size(lib, T=8192, num_seqs=8, varlen=1, H=96, K=128, V=128, C=32) == (256 + 8) * 96 * per + 8 * 96 * st
+    assert _ws_size(lib, B=2, T=64, K=16, V=16, C=16, in_dtype=0) == \
+        2 * 4 * 2 * (4 * (3 * 16 * 16 + 2 * 256) + 4 * 32) + 2 * 2 * 4 * 16 * 16
+    assert _ws_size(lib, K=24) == 0 and _ws_size(lib, C=48) == 0 and _ws_size(lib, H=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=64, ws_bytes=16), 5),                  # too small
+    (dict(ws=72, ws_bytes=1 << 20), 5),             # not 16-byte aligned
+    (dict(q=64, ws=64, ws_bytes=1 << 20), 6),       # the workspace is q
+    (dict(out=96, ws=96, ws_bytes=1 << 20), 6),     # the workspace is out
+    (dict(ws=64, ws_bytes=1 << 20, K=24), 4),       # unsupported width
+])
+def test_chunk_workspace_validation(lib, kw, status):
     assert _chunk(lib, **kw) == status
 
 
@@ -108,10 +142,11 @@ def test_fused_gate_validation(lib):
     f.restype = i32
     u32 = ctypes.c_uint
     f.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32, i32, i32,
-                  i32, f32, vp, i32, vp]
+                  i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
 
-    def chunk(z=4, ls=8, bias=None, lb=-5.0, out=6, K=16, flags=0):
-        return f(1, 2, 3, 1, z, ls, bias, lb, flags, 5, None, None, None, 0, 1, 64, 2, K, 16, 16, 1.0, out, 1, None)
+    def chunk(z=4, ls=8, bias=None, lb=-5.0, out=6, K=16, flags=0, ws=None, nws=0):
+        return f(1, 2, 3, 1, z, ls, bias, lb, flags, 5, None, None, None, 0, 1, 64, 2, K, 16, 16, 1.0, out, 1,
+                 ws, nws, None)
     assert chunk(lb=0.0) == 5        # lower bound must be negative
     assert chunk(lb=-6.0) == 5       # and >= -5 on the chunk path (the tile rescale bound)
     assert chunk(z=None) == 1        # NULL logits
@@ -120,6 +155,8 @@ def test_fused_gate_validation(lib):
     assert chunk(out=8) == 6         # out aliases log_scale
     assert chunk(K=24) == 4          # unsupported width
     assert chunk(flags=8) == 5       # unknown preparation flag
+    assert chunk(z=64, ws=64, nws=1 << 20) == 6   # the workspace is the logits
+    assert chunk(ws=64, nws=8) == 5        # workspace too small
     g = lib.kda_recurrent_step_fused_gate
     g.restype = i32
     g.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp]

@@ -24,6 +24,16 @@ def _case(msg):
     print("[case] " + msg, flush=True)
 
 
+@pytest.fixture(autouse=True, params=["two_pass", "one_kernel"])
+def chunk_form(request, monkeypatch):
+    """Every test runs with both forms of the chunk prefill: pre-pass + chain kernels over a
+    workspace, and the single chunk kernel (shapes the two-kernel form does not support
+    fall back to the single kernel in both)."""
+    monkeypatch.setattr(kda, "TWO_PASS", request.param == "two_pass")
+    print("[form] " + request.param, flush=True)
+    return request.param
+
+
 # ---- gate ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -61,7 +71,9 @@ def test_bounded_decay_odd_width_scalar_path():
 def test_tiny_fp32_all_chunk_sizes(C):
     inp = synth.tiny_fp32()
     _case("tiny fp32 C=%d" % C)
-    if not kda.chunk_fwd_supported(torch.float32, 16, 16, C):
+    form_ok = (kda.chunk_fwd_workspace_size(torch.float32, 1, 64, 2, 16, 16, C) > 0 if kda.TWO_PASS
+               else kda.chunk_fwd_supported(torch.float32, 16, 16, C) > 0)
+    if not form_ok and not kda.chunk_fwd_supported(torch.float32, 16, 16, C):
         with pytest.raises(ValueError, match="unsupported"):
             gpu_prefill(inp, chunk_size=C)
         pytest.skip("chunk size %d not compiled for fp32 K=V=16 (LDS budget)" % C)
@@ -655,3 +667,88 @@ def test_varlen_stress_full_size_sampled():
         a0, a1 = rows[0]
         assert_close(o[:, a0:a1, [h]], outs[0], False, "seq %d head %d out" % (s, h))
         assert_close(f[s, [h]], fins[0][0], False, "seq %d head %d state" % (s, h))
+
+
+# ---- the two forms of the chunk prefill ----------------------------------------------
+
+@pytest.mark.parametrize("dtype,K,V,C", [(torch.float32, 64, 64, 32), (torch.float32, 16, 128, 16),
+                                         (torch.bfloat16, 128, 128, 32), (torch.bfloat16, 32, 16, 64)])
+def test_two_pass_equals_one_kernel(dtype, K, V, C, chunk_form):
+    """The two forms do the same arithmetic in a different order of launches: outputs agree
+    to rounding; each also meets the oracle bar through the autouse parametrisation."""
+    if chunk_form != "two_pass":
+        pytest.skip("compares both forms once")
+    _case("two-pass vs one kernel %s K=%d V=%d C=%d" % (dtype, K, V, C))
+    if not kda.chunk_fwd_supported(dtype, K, V, C) or not kda.chunk_fwd_workspace_size(dtype, 1, 64, 1, K, V, C):
+        pytest.skip("shape not compiled for both forms")
+    inp = synth.make_prefill(2, 150, 3, K, V, dtype=dtype, seed=77, state_std=0.1)
+    d = lambda x: x.cuda()
+    q, k, v = d(inp.q), d(inp.k), d(inp.v)
+    g = kda.bounded_decay(d(inp.z), d(inp.log_scale), out_log=True)
+    args = dict(initial_state=d(inp.initial_state), gate_is_log=True, chunk_size=C, out_dtype=torch.float32)
+    o1, f1 = kda.chunk_fwd(q, k, v, g, d(inp.beta), two_pass=False, **args)
+    o2, f2 = kda.chunk_fwd(q, k, v, g, d(inp.beta), two_pass=True, **args)
+    tol = 1e-5 if dtype == torch.float32 else 2e-3
+    for a, b in ((o1, o2), (f1, f2)):
+        a, b = f64(a), f64(b)
+        assert np.max(np.abs(a - b)) <= tol * max(np.max(np.abs(a)), 1e-30)
+
+
+def test_two_pass_caller_workspace_reused(chunk_form):
+    """A caller-owned workspace serves calls of different sizes in a row (its contents are
+    scratch); a workspace too small is refused."""
+    if chunk_form != "two_pass":
+        pytest.skip("one form")
+    _case("two-pass caller workspace, two calls")
+    dtype, K, V, C = torch.bfloat16, 64, 64, 32
+    big = synth.make_prefill(1, 300, 4, K, V, dtype=dtype, seed=78)
+    small = synth.make_prefill(1, 70, 4, K, V, dtype=dtype, seed=79)
+    n = kda.chunk_fwd_workspace_size(dtype, 1, 300, 4, K, V, C)
+    assert n > kda.chunk_fwd_workspace_size(dtype, 1, 70, 4, K, V, C) > 0
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for inp in (big, small):
+        d = lambda x: x.cuda()
+        g = kda.bounded_decay(d(inp.z), d(inp.log_scale), out_log=True)
+        call = lambda **kw: kda.chunk_fwd(d(inp.q), d(inp.k), d(inp.v), g,
+                                          d(inp.beta), gate_is_log=True, chunk_size=C, out_dtype=torch.float32, **kw)
+        o_ws, f_ws = call(workspace=ws)
+        o_own, f_own = call(two_pass=True)
+        assert torch.equal(o_ws, o_own) and torch.equal(f_ws, f_own)
+        eo, ef = oracle_prefill(inp)
+        assert_close(o_ws, eo, False, "out")
+        assert_close(f_ws, ef, False, "state")
+    with pytest.raises(ValueError, match="bad argument"):
+        inp = big
+        g = kda.bounded_decay(inp.z.cuda(), inp.log_scale.cuda(), out_log=True)
+        kda.chunk_fwd(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), g, inp.beta.cuda(),
+                      gate_is_log=True, chunk_size=C, workspace=ws[:1024])
+
+
+@pytest.mark.parametrize("final", ["new", "none", "in_place"])
+def test_two_pass_chunk_segments(final, chunk_form):
+    """A fixed-length call long enough to be cut into chunk segments (66 chunks of 32: three
+    segments) carries its state from segment to segment through final_state, through the
+    workspace (no final state kept), or in place over the initial state."""
+    if chunk_form != "two_pass":
+        pytest.skip("segments exist in the two-kernel form only")
+    _case("two-pass segments final=%s" % final)
+    inp = synth.make_prefill(2, 2085, 2, 64, 64, dtype=torch.bfloat16, seed=81, state_std=0.1)
+    eo, ef = oracle_prefill(inp)
+    d = lambda x: x.cuda()
+    g = kda.bounded_decay(d(inp.z), d(inp.log_scale), out_log=True)
+    s0 = d(inp.initial_state).clone()
+    kw = dict(initial_state=s0, gate_is_log=True, chunk_size=32, out_dtype=torch.float32, two_pass=True)
+    if final == "none":
+        kw["output_final_state"] = False
+    elif final == "in_place":
+        kw["final_state"] = s0
+    o, f = kda.chunk_fwd(d(inp.q), d(inp.k), d(inp.v), g, d(inp.beta), **kw)
+    assert_close(o, eo, False, "out")
+    if final == "none":
+        assert f is None
+    else:
+        assert_close(f, ef, False, "state")
+        if final == "in_place":
+            assert f.data_ptr() == s0.data_ptr()
+    if final == "new":
+        assert torch.equal(s0, d(inp.initial_state))  # the initial state is only read
