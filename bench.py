@@ -2,14 +2,18 @@
 """Benchmark of the KDA hot path on one MI355X.
 
 One step = the whole prefill path over the Kimi K3 KDA layer workload (B=1, T=8192,
-H=96, K=V=128, bf16 q/k/v, fp32 gate/beta/state): the bounded-decay gate kernel on
-the raw logits, then the chunkwise prefill kernel (zero initial state, fp32 final
-state, bf16 output).  Inputs are resident in HBM before timing starts.  Reported:
+H=96, K=V=128, bf16 q/k/v, bf16 gate logits, fp32 beta/state): one chunk-prefill call
+with the bounded gate evaluated in its kernels (zero initial state, fp32 final state,
+bf16 output), in its two-kernel form -- a pre-pass over every (chunk, head) into a
+workspace allocated once beforehand, and the chain kernel for the serial part, the two
+overlapped over chunk segments on two streams.  Inputs are resident in HBM before
+timing starts.  Reported:
 
 * value: prefill tokens/s over K timed steps (ms_per_step = wall time per step);
-* roofline: the chunk kernel's algorithmic HBM traffic (1,540 B per token-head) and
-  algorithmic flops (6KV + 64(3K+2V) per token-head) per launch divided by its average
-  launch time (HIP events on the launch stream), against 8 TB/s and 2.5 PFLOP/s bf16;
+* roofline: the call's algorithmic HBM traffic (1,540 B per token-head) and algorithmic
+  flops (6KV + 64(3K+2V) per token-head) divided by its average time (HIP events on the
+  caller's stream, which waits for the side stream's pre-pass), against 8 TB/s and
+  2.5 PFLOP/s bf16; the single-kernel form is timed beside it;
 * decode: 256 successive single-token steps over a kept [64,96,128,128] fp32 state
   (gate kernel + fused step kernel per step), with the step kernel's algorithmic
   bytes (state read + write plus the token vectors) per launch over its launch time;
@@ -39,9 +43,12 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(name: str) -> str:
-    p = os.path.join(ROOT, "gated_delta_rule_31_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(name) -> str:
+    """Hash of a kernel source file, or of several (a list) taken in order."""
+    h = hashlib.sha256()
+    for n in ([name] if isinstance(name, str) else name):
+        h.update(open(os.path.join(ROOT, "gated_delta_rule_31_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel_file: str, workload: str):
@@ -61,6 +68,7 @@ def load_traffic(kernel_file: str, workload: str):
 
 
 COPY_BYTES = 1 << 30
+TWO_PASS_SOURCES = ["kda_chunk_pack.h", "kda_chunk_kernel.h", "kda_chunk_chain.hip"]
 
 
 def _counter_means(path, counter):
@@ -94,6 +102,8 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     # the exact instantiations the benchmark times (K = V = 128, bf16, chunk 32)
     chunk_pat = "PrecMixed, 128, 128, 32, 64, %d>" % (1 if zg else 0)
     flag = "Lb1E" if zg else "Lb0E"  # (these two appear under their mangled names)
+    two_pass = [("chunk_pack_kernel<", "PrecMixed, 128, 32, %d>" % (1 if zg else 0)),
+                ("chunk_chain_kernel<", "PrecMixed, 128, 128, 32, 64>")]
     entries = [("k3_prefill_chunk_fwd_" + gate, [("chunk_fwd_kernel<", chunk_pat)], "kda_chunk_kernel.h"),
                ("decode_recurrent_step_" + gate, [("recurrent_step_kernelIDF16bLi128ELi128E" + flag,)], "kda_step.hip"),
                ("short_recurrent_fwd_" + gate, [("recurrent_fwd_kernelIDF16bLi128ELi128E" + flag,)],
@@ -104,6 +114,16 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     for kern in ("states", "dstates"):
         entries.append(("k3_bwd_" + kern, [("bwd_%s_kernel<128, 128>" % kern,), ("bwd_%s_kernelILi128ELi128E" % kern,)],
                         "kda_bwd.hip"))
+    # the two-kernel form: both kernels' bytes per call (8 chunk segments: 8 launches of each)
+    segs = 8
+    fk = [sum(v for k, v in fetch.items() if all(p_ in k for p_ in pats)) for pats in two_pass]
+    wk = [sum(v for k, v in write.items() if all(p_ in k for p_ in pats)) for pats in two_pass]
+    if all(fk) and all(wk):
+        out["k3_prefill_two_pass_" + gate] = {
+            "fetch_kib_per_launch": {"pack": fk[0], "chain": fk[1]},
+            "write_kib_per_launch": {"pack": wk[0], "chain": wk[1]}, "launches_per_call": segs,
+            "bytes_per_launch": segs * ((fk[0] + fk[1]) * f_scale + (wk[0] + wk[1]) * w_scale),
+            "source_sha256_16": kernel_source_hash(TWO_PASS_SOURCES)}
     for key, alts, src in entries:
         match = lambda k: any(all(p_ in k for p_ in pats) for pats in alts)
         fk = [v for k, v in fetch.items() if match(k)]
@@ -178,18 +198,22 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     fused = args.gate == "fused"
+    nws = kda.chunk_fwd_workspace_size(q.dtype, B, T, H, K, V, args.chunk)
+    assert nws > 0, "the two-kernel form supports the K3 shape"
+    wsp = torch.empty(nws, dtype=torch.uint8, device=dev)  # allocated once, outside the timed steps
 
-    def step(ev_pair=None):
+    def step(ev_pair=None, two_pass=True):
         if not fused:
             kda.bounded_decay(z, ls, lower_bound=-5.0, out_log=False, out=g)
         if ev_pair is not None:
             ev_pair[0].record(stream)
+        w = dict(workspace=wsp) if two_pass else dict(two_pass=False)
         if fused:
             kda.chunk_fwd_fused_gate(q, k, v, z, ls, beta, lower_bound=-5.0, initial_state=None,
-                                     chunk_size=args.chunk, out=out, final_state=fin)
+                                     chunk_size=args.chunk, out=out, final_state=fin, **w)
         else:
             kda.chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=args.chunk, gate_is_log=False,
-                          out=out, final_state=fin)
+                          out=out, final_state=fin, **w)
         if ev_pair is not None:
             ev_pair[1].record(stream)
 
@@ -216,9 +240,19 @@ def main():
     alg_flops = th * (6 * K * V + 64 * (3 * K + 2 * V))
     achieved_gbs = alg_bytes / (chunk_ms * 1e-3) / 1e9
     achieved_tflops = alg_flops / (chunk_ms * 1e-3) / 1e12
-    traffic = load_traffic("kda_chunk_kernel.h", "k3_prefill_chunk_fwd_" + args.gate)
-    log("prefill: %.3f ms/step, chunk kernel %.3f ms, %.1f GB/s, %.1f TFLOP/s" %
+    traffic = load_traffic(TWO_PASS_SOURCES, "k3_prefill_two_pass_" + args.gate)
+    log("prefill: %.3f ms/step, prefill call %.3f ms, %.1f GB/s, %.1f TFLOP/s" %
         (ms_per_step, chunk_ms, achieved_gbs, achieved_tflops))
+    # the single-kernel form of the same call, beside it (not part of the timed steps)
+    for _ in range(2):
+        step(two_pass=False)
+    oev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for e_ in oev:
+        step(e_, two_pass=False)
+    torch.cuda.synchronize()
+    one_ms = sum(a_.elapsed_time(b_) for a_, b_ in oev) / len(oev)
+    one_gbs = alg_bytes / (one_ms * 1e-3) / 1e9
+    log("prefill, single-kernel form: %.3f ms" % one_ms)
 
     result = {
         "metric": "KDA prefill tokens/s (H=96,D=128) + % MFMA peak; decode state HBM GB/s",
@@ -239,10 +273,16 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel": "chunk_fwd_kernel",
+                     "traffic": traffic, "kernel": "chunk_pack_kernel + chunk_chain_kernel (one call, 8 chunk "
+                     "segments, overlapped on two streams)",
                      "launch_ms": chunk_ms, "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
+        "prefill_single_kernel": {"kernel": "chunk_fwd_kernel", "launch_ms": one_ms,
+                                  "tokens_per_s": B * T / (one_ms * 1e-3),
+                                  "hbm": {"achieved": one_gbs, "frac": one_gbs / HBM_PEAK_GBS,
+                                          "traffic": load_traffic("kda_chunk_kernel.h",
+                                                                  "k3_prefill_chunk_fwd_" + args.gate)}},
     }
     if fused:
         # the same layer with the model's in-kernel input preparation: q/k unit norm, beta
@@ -252,7 +292,8 @@ def main():
 
         def pstep():
             kda.chunk_fwd_fused_gate(q, k, v, z, ls, bl, lower_bound=-5.0, chunk_size=args.chunk, out=out,
-                                     final_state=fin_vk, qk_l2norm=True, beta_logits=True, state_vk=True)
+                                     final_state=fin_vk, qk_l2norm=True, beta_logits=True, state_vk=True,
+                                     workspace=wsp)
         pstep()
         torch.cuda.synchronize()
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
@@ -270,7 +311,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": p_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg_bytes}}
         del bl, fin_vk
-    del g, out
+    del g, out, wsp
 
     # ---------------- backward ----------------------------------------------------------
     if not args.no_bwd:

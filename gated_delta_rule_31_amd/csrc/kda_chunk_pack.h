@@ -2,11 +2,12 @@
 // "Chunkwise parallel form"): the same arithmetic as chunk_fwd_kernel, split where the
 // work stops depending on the state.
 //
-//  * chunk_pack_kernel, one workgroup per (chunk, head), all chunks at once: the decay
-//    products, the A-matrix tiles, T = (I + A_kk)^-1 and A_qk of one chunk, written as a
-//    dense package (Qt, -Bw, Kt, T, A_qk, gamma_C, beta) into a caller-owned workspace.
-//    Nothing in it depends on the state or on the value columns, so it runs once per
-//    (chunk, head) instead of once per value block, on every compute unit.
+//  * chunk_pack_kernel, a persistent grid over the (chunk, head) items, all chunks at
+//    once: per item the decay products, the A-matrix tiles, T = (I + A_kk)^-1 and A_qk
+//    of one chunk, written as a dense package (Qt, -Bw, Kt, T, A_qk, gamma_C, beta) into
+//    a caller-owned workspace.  Nothing in it depends on the state or on the value
+//    columns, so it runs once per (chunk, head) instead of once per value block, on every
+//    compute unit.
 //  * chunk_chain_kernel, one workgroup per (sequence, head, value block): the state waves
 //    of chunk_fwd_kernel (the serial part), fed by four copy waves that move each package
 //    from the workspace into a double-buffered LDS area and form beta V; one barrier per
