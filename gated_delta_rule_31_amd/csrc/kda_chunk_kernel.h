@@ -166,16 +166,20 @@ struct BFrag<float, NKT> {
 
 // acc += A[16 x 16*nkt] * B, A rows in LDS (arow = this lane's row, k contiguous), over
 // the first nkt (<= NKT) k tiles of b.  Callers pass nkt rounded up to even on the
-// 16-bit path only when the extra tile of A is zero.
-template <int NKT>
+// 16-bit path only when the extra tile of A is zero.  With SW the row is stored
+// swizzled: in rows whose index has bit 3 set (this lane's row, lane & 8) the two 8-byte
+// halves of every 16-byte piece are swapped, so the 16 rows one instruction reads fall
+// in distinct banks.
+template <int NKT, bool SW = false>
 __device__ __forceinline__ void mma_bfrag(f4 &acc, const _Float16 *arow, const BFrag<_Float16, NKT> &b,
                                           int nkt, int lane) {
     const int g = lane >> 4;
+    const int kg = (4 * g) ^ (SW && (lane & 8) ? 4 : 0);  // this lane's 4-element k group
 #pragma unroll
     for (int m = 0; m < NKT / 2; ++m) {
         if (2 * m < nkt) {
-            const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 32 * m + 4 * g);
-            const f16x4 hi = *reinterpret_cast<const f16x4 *>(arow + 32 * m + 16 + 4 * g);
+            const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 32 * m + kg);
+            const f16x4 hi = *reinterpret_cast<const f16x4 *>(arow + 32 * m + 16 + kg);
             const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b.pair[m], acc, 0, 0, 0);
         }
@@ -184,7 +188,7 @@ __device__ __forceinline__ void mma_bfrag(f4 &acc, const _Float16 *arow, const B
         // an odd last tile goes through the same 16x16x32 instruction with its upper half
         // zero, so one accumulation chain never mixes instruction shapes
         if (NKT - 1 < nkt) {
-            const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 16 * (NKT - 1) + 4 * g);
+            const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 16 * (NKT - 1) + kg);
             const f16x8 a = {lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
             const f16x8 bb = {b.tail[0], b.tail[1], b.tail[2], b.tail[3], 0, 0, 0, 0};
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bb, acc, 0, 0, 0);
@@ -192,16 +196,17 @@ __device__ __forceinline__ void mma_bfrag(f4 &acc, const _Float16 *arow, const B
     }
 }
 
-template <int NKT>
+template <int NKT, bool SW = false>
 __device__ __forceinline__ void mma_bfrag(f4 &acc, const float *arow, const BFrag<float, NKT> &b, int nkt,
                                           int lane) {
     const int g = lane >> 4;
+    const int sw = SW && (lane & 8) ? 2 : 0;  // 8-byte halves swapped: element ^ 2
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
         if (t < nkt) {
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[16 * t + 4 * g + s], b.t[t][s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[16 * t + 4 * g + (s ^ sw)], b.t[t][s], acc, 0, 0, 0);
         }
     }
 }
@@ -481,7 +486,8 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
 // registers, advanced chunk by chunk through the serial part.  The packages sit at pkg0 in
 // two buffers, by chunk parity.  Without PK the state waves also do the A-matrix work of
 // the chunk staged in the previous period (two barriers a period); with PK each package
-// arrives complete from the pre-pass (one barrier a period).
+// arrives complete from the pre-pass (one barrier a period), its matrix operands stored
+// with the row swizzle of mma_bfrag.
 template <class P, int K, int V, int C, int BV, bool NORM, bool PK>
 __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *smem, unsigned char *pkg0, int s,
                                             int h, int vb, int64_t bos, int64_t eos, int nchunks, int wave,
@@ -601,7 +607,7 @@ __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *s
                     const TM *bvr = bV + (jt * 16 + (lane & 15)) * L::LCM + 16 * p + 4 * g;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[e] = to_f32(bvr[e]);
-                    mma_bfrag<NKT_K>(y, Bw + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
+                    mma_bfrag<NKT_K, PK>(y, Bw + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
                     Y[p] = y;
                 }
                 BFrag<TM, NP> Yh;
@@ -610,7 +616,7 @@ __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *s
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
                     f4 x = {0.f, 0.f, 0.f, 0.f};
-                    mma_bfrag<NP>(x, Tm + (16 * p + (lane & 15)) * L::LCM, Yh, p + 1, lane);
+                    mma_bfrag<NP, PK>(x, Tm + (16 * p + (lane & 15)) * L::LCM, Yh, p + 1, lane);
                     Vt[mj][p] = x;
                 }
                 Vh[mj].set(Vt[mj]);
@@ -618,8 +624,8 @@ __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *s
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
                     f4 o = {0.f, 0.f, 0.f, 0.f};
-                    mma_bfrag<NKT_K>(o, Qt + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
-                    mma_bfrag<NP>(o, Aqk + (16 * p + (lane & 15)) * L::LCM, Vh[mj], p + 1, lane);
+                    mma_bfrag<NKT_K, PK>(o, Qt + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
+                    mma_bfrag<NP, PK>(o, Aqk + (16 * p + (lane & 15)) * L::LCM, Vh[mj], p + 1, lane);
                     store_o(p, jt, o);
                 }
             }
@@ -638,7 +644,7 @@ __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *s
                     f4 x = S[mj][t];
                     const float4 d = *reinterpret_cast<const float4 *>(eGC + 16 * t + 4 * g);
                     x[0] *= d.x; x[1] *= d.y; x[2] *= d.z; x[3] *= d.w;
-                    mma_bfrag<NP>(x, Kt + (16 * t + (lane & 15)) * L::LCM, Vh[mj], NP, lane);
+                    mma_bfrag<NP, PK>(x, Kt + (16 * t + (lane & 15)) * L::LCM, Vh[mj], NP, lane);
                     S[mj][t] = x;
                 }
                 Sh[mj].set(S[mj]);

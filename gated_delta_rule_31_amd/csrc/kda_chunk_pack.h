@@ -545,33 +545,45 @@ __global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
     constexpr int NPC = 2 * NQ + NKT + 2 * NCC + NGC;
     static_assert(PL::gGC + 16 * NGC == PL::gBt, "the pieces cover the package up to beta");
     constexpr int CPT = (NPC + NCT - 1) / NCT;
+    // The matrix operands go into LDS with the row swizzle the state waves read them with
+    // (mma_bfrag): in rows whose index has bit 3 set the two 8-byte halves of each piece
+    // trade places.
     uint32_t src[CPT], dst[CPT];
+    bool swp[CPT];
 #pragma unroll
     for (int w = 0; w < CPT; ++w) {
         int e = tp + NCT * w;
         e = e < NPC ? e : NPC - 1;  // surplus lanes repeat the last piece (same value, same place)
         src[w] = 16u * (uint32_t)e;
         uint32_t d;
+        int row = 0;
         if (e < NQ) {
-            d = (uint32_t)(L::pQt + (e / RQ) * L::LKM * sizeof(TM) + 16 * (e % RQ));
+            row = e / RQ;
+            d = (uint32_t)(L::pQt + row * L::LKM * sizeof(TM) + 16 * (e % RQ));
         } else if (e < 2 * NQ) {
             const int x = e - NQ;
-            d = (uint32_t)(L::pBw + (x / RQ) * L::LKM * sizeof(TM) + 16 * (x % RQ));
+            row = x / RQ;
+            d = (uint32_t)(L::pBw + row * L::LKM * sizeof(TM) + 16 * (x % RQ));
         } else if (e < 2 * NQ + NKT) {
             const int x = e - 2 * NQ;
-            d = (uint32_t)(L::pKt + (x / RC) * L::LCM * sizeof(TM) + 16 * (x % RC));
+            row = x / RC;
+            d = (uint32_t)(L::pKt + row * L::LCM * sizeof(TM) + 16 * (x % RC));
         } else if (e < 2 * NQ + NKT + NCC) {
             const int x = e - 2 * NQ - NKT;
-            d = (uint32_t)(L::pTm + (x / RC) * L::LCM * sizeof(TM) + 16 * (x % RC));
+            row = x / RC;
+            d = (uint32_t)(L::pTm + row * L::LCM * sizeof(TM) + 16 * (x % RC));
         } else if (e < 2 * NQ + NKT + 2 * NCC) {
             const int x = e - 2 * NQ - NKT - NCC;
-            d = (uint32_t)(L::pAqk + (x / RC) * L::LCM * sizeof(TM) + 16 * (x % RC));
+            row = x / RC;
+            d = (uint32_t)(L::pAqk + row * L::LCM * sizeof(TM) + 16 * (x % RC));
         } else {
-            d = (uint32_t)(L::pGC + 16 * (e - 2 * NQ - NKT - 2 * NCC));
+            d = (uint32_t)(L::pGC + 16 * (e - 2 * NQ - NKT - 2 * NCC));  // gamma_C: not a matrix
         }
         dst[w] = d;
+        swp[w] = (row & 8) != 0;
     }
-    // beta V items: four value columns of two consecutive tokens
+    // beta V items: four value columns of two consecutive tokens, the token pairs on
+    // consecutive lanes (the transposed LDS writes then fall in distinct banks)
     using RawV = typename std::conditional<std::is_same<TIn, float>::value, float4, uint2>::type;
     constexpr int NVI = BV / 4 * (C / 2);
     constexpr int VPT = (NVI + NCT - 1) / NCT;
@@ -591,7 +603,7 @@ __global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
         for (int w = 0; w < VPT; ++w) {
             int e = tp + NCT * w;
             e = e < NVI ? e : NVI - 1;
-            const int j = 4 * (e % (BV / 4)), r = 2 * (e / (BV / 4));
+            const int j = 4 * (e / (C / 2)), r = 2 * (e % (C / 2));
             const int r0 = r < last ? r : last, r1 = r + 1 < last ? r + 1 : last;
             rv[w][0] = ld_at<RawV>(vbp, (uint32_t)sizeof(TIn) * (uint32_t)(r0 * H * V + j));
             rv[w][1] = ld_at<RawV>(vbp, (uint32_t)sizeof(TIn) * (uint32_t)(r1 * H * V + j));
@@ -619,13 +631,16 @@ __global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
             if (it < nchunks) {
                 unsigned char *pk = smem + (size_t)(it & 1) * L::szPkg;
 #pragma unroll
-                for (int w = 0; w < CPT; ++w) *reinterpret_cast<uint4 *>(pk + dst[w]) = buf[d][w];
+                for (int w = 0; w < CPT; ++w) {
+                    const uint4 x = buf[d][w];
+                    *reinterpret_cast<uint4 *>(pk + dst[w]) = swp[w] ? uint4{x.z, x.w, x.x, x.y} : x;
+                }
                 TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
 #pragma unroll
                 for (int w = 0; w < VPT; ++w) {
                     int e = tp + NCT * w;
                     e = e < NVI ? e : NVI - 1;
-                    const int j = 4 * (e % (BV / 4)), r = 2 * (e / (BV / 4));
+                    const int j = 4 * (e / (C / 2)), r = 2 * (e % (C / 2));
                     float f0[4], f1[4];
                     raw4(rv[d][w][0], f0);
                     raw4(rv[d][w][1], f1);
