@@ -43,31 +43,13 @@ hipError_t launch_pack_any(const ChunkArgs &a, bool fp32_inputs, int K, int C, i
     return launch_chunk_pack(a, fp32_inputs, K, C, items, max_wgs, stream);
 }
 
-// A second stream and events per (host thread, device), made on first use, for running the
-// pre-pass of later chunk segments beside the chain kernel of earlier ones.
-constexpr int MAX_SEG = 16;
-struct Side {
-    hipStream_t stream = nullptr;
-    hipEvent_t start = nullptr;
-    hipEvent_t done[MAX_SEG] = {};
-};
-
-hipError_t side_of_current_device(Side *&out) {
-    static thread_local Side side[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorNotSupported;
-    Side &x = side[dev];
-    if (!x.stream) {
-        // default priority (the only one this library uses), no implicit sync with stream 0
-        if ((e = hipStreamCreateWithFlags(&x.stream, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&x.start, hipEventDisableTiming)) != hipSuccess) return e;
-        for (int i = 0; i < MAX_SEG; ++i)
-            if ((e = hipEventCreateWithFlags(&x.done[i], hipEventDisableTiming)) != hipSuccess) return e;
-    }
-    out = &x;
-    return hipSuccess;
+hipError_t launch_segment_any(const ChunkArgs &ca, const ChunkArgs &pa, bool fp32_inputs, int K, int V, int C,
+                              int num_pairs, int64_t items, int pack_wgs, hipStream_t stream) {
+    if (pa.gate.mode == GATE_LOGITS)
+        return pa.qk_l2norm
+                   ? launch_chunk_segment_logits_norm(ca, pa, fp32_inputs, K, V, C, num_pairs, items, pack_wgs, stream)
+                   : launch_chunk_segment_logits(ca, pa, fp32_inputs, K, V, C, num_pairs, items, pack_wgs, stream);
+    return launch_chunk_segment(ca, pa, fp32_inputs, K, V, C, num_pairs, items, pack_wgs, stream);
 }
 
 }  // namespace
@@ -77,21 +59,20 @@ hipError_t launch_chunk_fwd_two_pass(const ChunkArgs &a, bool fp32_inputs, int K
     const int64_t NC = (a.T + C - 1) / C;  // chunks per sequence (fixed-length batches)
     // Packed sequences, or few chunks: the pre-pass over every slot, then the chain.
     constexpr int64_t SEG_MIN = 32;  // chunks per segment, at least
+    constexpr int64_t MAX_SEG = 16;
     if (a.cu_seqlens || NC < 2 * SEG_MIN) {
         hipError_t e = launch_pack_any(a, fp32_inputs, K, C, slots * a.H, 0, stream);
         if (e != hipSuccess) return e;
         return launch_chunk_chain(a, fp32_inputs, K, V, C, num_pairs, stream, bv);
     }
-    // Fixed-length sequences: chunk segments.  The side stream runs the pre-pass of segment
-    // 0, 1, ... back to back; the caller's stream runs the chain over segment s once the
-    // pre-pass of s is done, so the chain of s overlaps the pre-pass of s + 1 (the chain
-    // is bound by its serial dependence, the pre-pass by vector arithmetic).  The state
-    // passes from segment to segment through the workspace's state area (or final_state
-    // when the caller keeps one).  Segments after the first keep the pre-pass to about
-    // 1.25 workgroups per compute unit, so every chain workgroup still finds room.
-    Side *sd = nullptr;
-    hipError_t e = side_of_current_device(sd);
-    if (e != hipSuccess) return e;
+    // Fixed-length sequences: chunk segments, all on the caller's stream.  Launch 0 is the
+    // pre-pass of segment 0; launch s + 1 holds the chain over segment s and the pre-pass
+    // of segment s + 1, so the chain (bound by its serial dependence, LDS and HBM) runs
+    // beside the pre-pass (bound by vector arithmetic).  The chain's workgroups come first
+    // in each launch and the pre-pass is held to about 1.25 workgroups per compute unit,
+    // so every chain workgroup is placed at once.  The state passes from segment to
+    // segment through the workspace's state area (or final_state when the caller keeps
+    // one).
     const int64_t seg = NC / SEG_MIN >= MAX_SEG ? (NC + MAX_SEG - 1) / MAX_SEG : SEG_MIN;
     const int nseg = (int)((NC + seg - 1) / seg);
     const size_t pb = chunk_pack_bytes(fp32_inputs, K, V, C);
@@ -99,25 +80,27 @@ hipError_t launch_chunk_fwd_two_pass(const ChunkArgs &a, bool fp32_inputs, int K
     float *mid = a.final_state ? a.final_state : carry;  // state between segments
     const int64_t B = slots / NC;
     const int cus = device_cu_count();
-    if ((e = hipEventRecord(sd->start, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(sd->stream, sd->start, 0)) != hipSuccess) return e;
-    for (int s = 0; s < nseg; ++s) {
+    auto seg_args = [&](int s) {
         ChunkArgs x = a;
         x.c_begin = (int)(s * seg);
         x.c_end = (int)((s + 1) * seg < NC ? (s + 1) * seg : NC);
-        const int64_t items = B * (x.c_end - x.c_begin) * a.H;
-        if ((e = launch_pack_any(x, fp32_inputs, K, C, items, s == 0 ? 0 : cus + cus / 4, sd->stream)) != hipSuccess)
-            return e;
-        if ((e = hipEventRecord(sd->done[s], sd->stream)) != hipSuccess) return e;
-    }
+        return x;
+    };
+    auto items_of = [&](const ChunkArgs &x) { return B * (x.c_end - x.c_begin) * a.H; };
+    ChunkArgs p0 = seg_args(0);
+    hipError_t e = launch_pack_any(p0, fp32_inputs, K, C, items_of(p0), 0, stream);
+    if (e != hipSuccess) return e;
     for (int s = 0; s < nseg; ++s) {
-        ChunkArgs x = a;
-        x.c_begin = (int)(s * seg);
-        x.c_end = (int)((s + 1) * seg < NC ? (s + 1) * seg : NC);
-        x.initial_state = s == 0 ? a.initial_state : mid;
-        x.final_state = s == nseg - 1 ? a.final_state : mid;
-        if ((e = hipStreamWaitEvent(stream, sd->done[s], 0)) != hipSuccess) return e;
-        if ((e = launch_chunk_chain(x, fp32_inputs, K, V, C, num_pairs, stream, bv)) != hipSuccess) return e;
+        ChunkArgs c = seg_args(s);
+        c.initial_state = s == 0 ? a.initial_state : mid;
+        c.final_state = s == nseg - 1 ? a.final_state : mid;
+        if (s + 1 < nseg) {
+            const ChunkArgs p = seg_args(s + 1);
+            e = launch_segment_any(c, p, fp32_inputs, K, V, C, num_pairs, items_of(p), cus + cus / 4, stream);
+        } else {
+            e = launch_chunk_chain(c, fp32_inputs, K, V, C, num_pairs, stream, bv);  // the last: chain alone
+        }
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }

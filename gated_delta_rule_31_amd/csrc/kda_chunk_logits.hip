@@ -16,4 +16,10 @@ hipError_t launch_chunk_pack_logits(const ChunkArgs &a, bool fp32_inputs, int K,
                        : launch_pack_p<PrecMixed, 1>(a, K, C, items, max_wgs, stream);
 }
 
+hipError_t launch_chunk_segment_logits(const ChunkArgs &ca, const ChunkArgs &pa, bool fp32_inputs, int K, int V, int C,
+                                       int num_pairs, int64_t items, int pack_wgs, hipStream_t stream) {
+    return fp32_inputs ? launch_segment_p<PrecF32, 1>(ca, pa, K, V, C, num_pairs, items, pack_wgs, stream)
+                       : launch_segment_p<PrecMixed, 1>(ca, pa, K, V, C, num_pairs, items, pack_wgs, stream);
+}
+
 }  // namespace kda

@@ -17,4 +17,10 @@ hipError_t launch_chunk_pack_logits_norm(const ChunkArgs &a, bool fp32_inputs, i
                        : launch_pack_p<PrecMixed, 2>(a, K, C, items, max_wgs, stream);
 }
 
+hipError_t launch_chunk_segment_logits_norm(const ChunkArgs &ca, const ChunkArgs &pa, bool fp32_inputs, int K, int V, int C,
+                                            int num_pairs, int64_t items, int pack_wgs, hipStream_t stream) {
+    return fp32_inputs ? launch_segment_p<PrecF32, 2>(ca, pa, K, V, C, num_pairs, items, pack_wgs, stream)
+                       : launch_segment_p<PrecMixed, 2>(ca, pa, K, V, C, num_pairs, items, pack_wgs, stream);
+}
+
 }  // namespace kda

@@ -90,7 +90,7 @@ __device__ __forceinline__ void slot_span(int n, const int32_t *cu, int N, int64
 // sequence owns, and has the raw inputs of its next item in flight while it works on the
 // current one.
 template <class P, int K, int C, int GM>
-__global__ __launch_bounds__(PPT) void chunk_pack_kernel(ChunkArgs a) {
+__device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
     constexpr bool ZG = GM >= 1;
     constexpr bool NORM = GM == 2;
     using L = Layout<P, K, 16, C, 16>;
@@ -108,7 +108,6 @@ __global__ __launch_bounds__(PPT) void chunk_pack_kernel(ChunkArgs a) {
     const int c0 = a.c_begin < NC ? a.c_begin : NC;
     const int W = (a.c_end < NC ? a.c_end : NC) - c0;
     const int nitems = a.cu_seqlens ? a.pack_slots * H : (a.pack_slots / NC) * W * H;
-    const int G = (int)gridDim.x;
 
     TA *Lk = reinterpret_cast<TA *>(smem + L::oLk);
     TA *St = reinterpret_cast<TA *>(smem + L::oSt);
@@ -210,7 +209,7 @@ __global__ __launch_bounds__(PPT) void chunk_pack_kernel(ChunkArgs a) {
     };
 
     Item cur;
-    int item = find(blockIdx.x, cur);
+    int item = find(bid, cur);
     if (item < nitems) fetch(cur);
     while (item < nitems) {  // workgroup-uniform
         int tid = threadIdx.x;
@@ -485,9 +484,15 @@ __global__ __launch_bounds__(PPT) void chunk_pack_kernel(ChunkArgs a) {
     }
 }
 
+template <class P, int K, int C, int GM>
+__global__ __launch_bounds__(PPT) void chunk_pack_kernel(ChunkArgs a) {
+    pack_body<P, K, C, GM>(a, (int)blockIdx.x, (int)gridDim.x);
+}
+
 // The chain kernel: state waves as in chunk_fwd_kernel, copy waves for the packages.
+// Workgroup bid of G (G a multiple of 8: a head's value blocks share one XCD).
 template <class P, int K, int V, int C, int BV>
-__global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
+__device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
     using L = Layout<P, K, V, C, BV>;
     using PL = PackLayout<P, K, C>;
     using TM = typename P::TM;
@@ -499,9 +504,8 @@ __global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
     const int wave = tid >> 6;
 
     constexpr int NVB = V / BV;
-    const int G = gridDim.x;
-    int lin = blockIdx.x;
-    if ((G & 7) == 0) lin = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // a head's value blocks
+    int lin = bid;
+    if ((G & 7) == 0) lin = (bid & 7) * (G >> 3) + (bid >> 3);  // a head's value blocks
     const int vb = lin % NVB;                                                   // share one XCD
     const int pair = lin / NVB;
     const int H = a.H;
@@ -655,6 +659,24 @@ __global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
     }
 }
 
+template <class P, int K, int V, int C, int BV>
+__global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
+    chain_body<P, K, V, C, BV>(a, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// One launch of a chunk segment: workgroups [0, nchain) run the chain over segment s
+// (arguments ca), the rest the pre-pass of segment s + 1 (arguments pa).  The chain's
+// workgroups come first in dispatch order, so they are placed before the pre-pass fills
+// the remaining room; nothing in one launch waits for another workgroup of it.
+template <class P, int K, int V, int C, int BV, int GM>
+__global__ __launch_bounds__(NTC) void chunk_segment_kernel(ChunkArgs ca, ChunkArgs pa, int nchain) {
+    static_assert(NTC == PPT, "both roles run with the same workgroup size");
+    if ((int)blockIdx.x < nchain)
+        chain_body<P, K, V, C, BV>(ca, (int)blockIdx.x, nchain);
+    else
+        pack_body<P, K, C, GM>(pa, (int)blockIdx.x - nchain, (int)gridDim.x - nchain);
+}
+
 template <class P, int K, int V, int C>
 constexpr int pick_chain_bv() {
     if constexpr (V >= 64 && ChainLds<P, K, V, C, 64>::fits) return 64;
@@ -755,6 +777,59 @@ hipError_t launch_chain_p(const ChunkArgs &a, int K, int V, int C, int num_pairs
     }
 #undef KDA_CHAIN_V
 #undef KDA_CHAIN_C
+}
+
+template <class P, int GM, int K, int V, int C>
+hipError_t launch_segment_kvc(const ChunkArgs &ca, const ChunkArgs &pa, int num_pairs, int64_t items, int pack_wgs,
+                              hipStream_t stream) {
+    constexpr int BV = pick_chain_bv<P, K, V, C>();
+    if constexpr (BV == 0 || !PrepassLds<P, K, C>::fits) {
+        return hipErrorNotSupported;
+    } else {
+        constexpr size_t lds = ChainLds<P, K, V, C, BV>::total > PrepassLds<P, K, C>::total
+                                   ? ChainLds<P, K, V, C, BV>::total : PrepassLds<P, K, C>::total;
+        auto kern = chunk_segment_kernel<P, K, V, C, BV, GM>;
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        const int nchain = num_pairs * (V / BV);
+        const int np = (int)(items < pack_wgs ? items : pack_wgs);
+        hipLaunchKernelGGL(kern, dim3(nchain + np), dim3(NTC), lds, stream, ca, pa, nchain);
+        return hipGetLastError();
+    }
+}
+
+template <class P, int GM>
+hipError_t launch_segment_p(const ChunkArgs &ca, const ChunkArgs &pa, int K, int V, int C, int num_pairs,
+                            int64_t items, int pack_wgs, hipStream_t stream) {
+#define KDA_SEG_C(KK, VV)                                                                                \
+    switch (C) {                                                                                         \
+        case 16: return launch_segment_kvc<P, GM, KK, VV, 16>(ca, pa, num_pairs, items, pack_wgs, stream); \
+        case 32: return launch_segment_kvc<P, GM, KK, VV, 32>(ca, pa, num_pairs, items, pack_wgs, stream); \
+        case 64: return launch_segment_kvc<P, GM, KK, VV, 64>(ca, pa, num_pairs, items, pack_wgs, stream); \
+        default: return hipErrorNotSupported;                                                            \
+    }
+#define KDA_SEG_V(KK)                          \
+    switch (V) {                               \
+        case 16: KDA_SEG_C(KK, 16)             \
+        case 32: KDA_SEG_C(KK, 32)             \
+        case 64: KDA_SEG_C(KK, 64)             \
+        case 128: KDA_SEG_C(KK, 128)           \
+        default: return hipErrorNotSupported;  \
+    }
+    switch (K) {
+        case 16: KDA_SEG_V(16)
+        case 32: KDA_SEG_V(32)
+        case 64: KDA_SEG_V(64)
+        case 128: KDA_SEG_V(128)
+        default: return hipErrorNotSupported;
+    }
+#undef KDA_SEG_V
+#undef KDA_SEG_C
 }
 
 }  // namespace

@@ -165,6 +165,14 @@ hipError_t launch_chunk_pack_logits_norm(const ChunkArgs &a, bool fp32_inputs, i
                                          int max_wgs, hipStream_t stream);
 hipError_t launch_chunk_chain(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                               hipStream_t stream, int *bv);
+// one launch holding the chain over the chunks of `ca` and the pre-pass of `pa` (`items`
+// items on at most pack_wgs workgroups), by the pre-pass's gate mode as above
+hipError_t launch_chunk_segment(const ChunkArgs &ca, const ChunkArgs &pa, bool fp32_inputs, int K, int V, int C,
+                                int num_pairs, int64_t items, int pack_wgs, hipStream_t stream);
+hipError_t launch_chunk_segment_logits(const ChunkArgs &ca, const ChunkArgs &pa, bool fp32_inputs, int K, int V,
+                                       int C, int num_pairs, int64_t items, int pack_wgs, hipStream_t stream);
+hipError_t launch_chunk_segment_logits_norm(const ChunkArgs &ca, const ChunkArgs &pa, bool fp32_inputs, int K, int V,
+                                            int C, int num_pairs, int64_t items, int pack_wgs, hipStream_t stream);
 hipError_t launch_recurrent_step(const StepArgs &a, bool fp32_inputs, int K, int V, int pairs,
                                  hipStream_t stream);
 hipError_t launch_recurrent_fwd(const RecurrentArgs &a, bool fp32_inputs, int K, int V, int num_pairs,
