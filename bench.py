@@ -6,14 +6,14 @@ H=96, K=V=128, bf16 q/k/v, bf16 gate logits, fp32 beta/state): one chunk-prefill
 with the bounded gate evaluated in its kernels (zero initial state, fp32 final state,
 bf16 output), in its two-kernel form -- a pre-pass over every (chunk, head) into a
 workspace allocated once beforehand, and the chain kernel for the serial part, the two
-overlapped over chunk segments on two streams.  Inputs are resident in HBM before
-timing starts.  Reported:
+overlapped over chunk segments (each launch runs the chain over one segment beside the
+pre-pass of the next).  Inputs are resident in HBM before timing starts.  Reported:
 
 * value: prefill tokens/s over K timed steps (ms_per_step = wall time per step);
-* roofline: the call's algorithmic HBM traffic (1,540 B per token-head) and algorithmic
-  flops (6KV + 64(3K+2V) per token-head) divided by its average time (HIP events on the
-  caller's stream, which waits for the side stream's pre-pass), against 8 TB/s and
-  2.5 PFLOP/s bf16; the single-kernel form is timed beside it;
+* roofline: the call's algorithmic HBM traffic (1,284 B per token-head with the gate
+  logits in bf16) and algorithmic flops (6KV + 64(3K+2V) per token-head) divided by its
+  average time (HIP events on the launch stream around the call's 9 launches), against
+  8 TB/s and 2.5 PFLOP/s bf16; the single-kernel form is timed beside it;
 * decode: 256 successive single-token steps over a kept [64,96,128,128] fp32 state
   (gate kernel + fused step kernel per step), with the step kernel's algorithmic
   bytes (state read + write plus the token vectors) per launch over its launch time;
@@ -102,8 +102,11 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     # the exact instantiations the benchmark times (K = V = 128, bf16, chunk 32)
     chunk_pat = "PrecMixed, 128, 128, 32, 64, %d>" % (1 if zg else 0)
     flag = "Lb1E" if zg else "Lb0E"  # (these two appear under their mangled names)
-    two_pass = [("chunk_pack_kernel<", "PrecMixed, 128, 32, %d>" % (1 if zg else 0)),
-                ("chunk_chain_kernel<", "PrecMixed, 128, 128, 32, 64>")]
+    # the two-kernel form per call: the pre-pass of the first chunk segment, 7 launches
+    # holding a chain segment and the next pre-pass segment, the chain of the last segment
+    two_pass = [(("chunk_pack_kernel<", "PrecMixed, 128, 32, %d>" % (1 if zg else 0)), 1),
+                (("chunk_segment_kernel<", "PrecMixed, 128, 128, 32, 64, %d>" % (1 if zg else 0)), 7),
+                (("chunk_chain_kernel<", "PrecMixed, 128, 128, 32, 64>"), 1)]
     entries = [("k3_prefill_chunk_fwd_" + gate, [("chunk_fwd_kernel<", chunk_pat)], "kda_chunk_kernel.h"),
                ("decode_recurrent_step_" + gate, [("recurrent_step_kernelIDF16bLi128ELi128E" + flag,)], "kda_step.hip"),
                ("short_recurrent_fwd_" + gate, [("recurrent_fwd_kernelIDF16bLi128ELi128E" + flag,)],
@@ -114,15 +117,15 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     for kern in ("states", "dstates"):
         entries.append(("k3_bwd_" + kern, [("bwd_%s_kernel<128, 128>" % kern,), ("bwd_%s_kernelILi128ELi128E" % kern,)],
                         "kda_bwd.hip"))
-    # the two-kernel form: both kernels' bytes per call (8 chunk segments: 8 launches of each)
-    segs = 8
-    fk = [sum(v for k, v in fetch.items() if all(p_ in k for p_ in pats)) for pats in two_pass]
-    wk = [sum(v for k, v in write.items() if all(p_ in k for p_ in pats)) for pats in two_pass]
+    # the two-kernel form: the bytes of all its launches per call
+    fk = [sum(v for k, v in fetch.items() if all(p_ in k for p_ in pats)) for pats, _ in two_pass]
+    wk = [sum(v for k, v in write.items() if all(p_ in k for p_ in pats)) for pats, _ in two_pass]
     if all(fk) and all(wk):
+        names = ("pack", "segment", "chain")
         out["k3_prefill_two_pass_" + gate] = {
-            "fetch_kib_per_launch": {"pack": fk[0], "chain": fk[1]},
-            "write_kib_per_launch": {"pack": wk[0], "chain": wk[1]}, "launches_per_call": segs,
-            "bytes_per_launch": segs * ((fk[0] + fk[1]) * f_scale + (wk[0] + wk[1]) * w_scale),
+            "fetch_kib_per_launch": dict(zip(names, fk)), "write_kib_per_launch": dict(zip(names, wk)),
+            "launches_per_call": dict(zip(names, [n for _, n in two_pass])),
+            "bytes_per_launch": sum(n * (f * f_scale + w * w_scale) for (_, n), f, w in zip(two_pass, fk, wk)),
             "source_sha256_16": kernel_source_hash(TWO_PASS_SOURCES)}
     for key, alts, src in entries:
         match = lambda k: any(all(p_ in k for p_ in pats) for pats in alts)
@@ -273,8 +276,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel": "chunk_pack_kernel + chunk_chain_kernel (one call, 8 chunk "
-                     "segments, overlapped on two streams)",
+                     "traffic": traffic, "kernel": "one prefill call: chunk_pack_kernel, 7 x chunk_segment_kernel "
+                     "(chain of a chunk segment beside the next pre-pass), chunk_chain_kernel",
                      "launch_ms": chunk_ms, "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
