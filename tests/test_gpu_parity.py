@@ -752,3 +752,38 @@ def test_two_pass_chunk_segments(final, chunk_form):
             assert f.data_ptr() == s0.data_ptr()
     if final == "new":
         assert torch.equal(s0, d(inp.initial_state))  # the initial state is only read
+
+
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.bfloat16, 64, 64)])
+def test_prepared_in_kernel_chunk_segments(dtype, K, V, chunk_form):
+    """The model-facing call (gate logits, q/k normalisation, beta logits, [V,K] states)
+    long enough for chunk segments in the two-kernel form (2 x 2100 tokens: 66 chunks of
+    32 per sequence, three segments), at the float32 and bf16 bars."""
+    if chunk_form != "two_pass":
+        pytest.skip("segments exist in the two-kernel form only")
+    _case("in-kernel preparation, segments %s K=%d V=%d" % (dtype, K, V))
+    r = _raw_inputs(2, 2100, 2, K, V, dtype, seed=5 * K + V)
+    d = lambda x: None if x is None else x.cuda()
+    o, f = kda.chunk_fwd_fused_gate(d(r["q"]), d(r["k"]), d(r["v"]), d(r["z"]), d(r["log_scale"]),
+                                    d(r["beta_logits"]), initial_state=d(r["s0_vk"]), chunk_size=32,
+                                    out_dtype=torch.float32, qk_l2norm=True, beta_logits=True, state_vk=True,
+                                    two_pass=True)
+    eo, ef = _oracle_prepared(r)
+    fp32 = dtype == torch.float32
+    assert_close(o, eo, fp32, "out")
+    assert_close(f, ef, fp32, "final state [V,K]")
+
+
+def test_two_pass_segments_fp32_and_ragged(chunk_form):
+    """Segments on float32 inputs at the 1e-4 bar, with a ragged last chunk (T = 2085)."""
+    if chunk_form != "two_pass":
+        pytest.skip("segments exist in the two-kernel form only")
+    _case("two-pass segments fp32 ragged")
+    inp = synth.make_prefill(1, 2085, 2, 32, 32, dtype=torch.float32, seed=83, state_std=0.1)
+    eo, ef = oracle_prefill(inp)
+    d = lambda x: x.cuda()
+    g = kda.bounded_decay(d(inp.z), d(inp.log_scale), out_log=True)
+    o, f = kda.chunk_fwd(d(inp.q), d(inp.k), d(inp.v), g, d(inp.beta), initial_state=d(inp.initial_state),
+                         gate_is_log=True, chunk_size=32, out_dtype=torch.float32, two_pass=True)
+    assert_close(o, eo, True, "out")
+    assert_close(f, ef, True, "state")
