@@ -12,6 +12,9 @@
 //    of chunk_fwd_kernel (the serial part), fed by four copy waves that move each package
 //    from the workspace into a double-buffered LDS area and form beta V; one barrier per
 //    chunk.
+//  * chunk_segment_kernel: one launch holding the chain over one segment of chunks in its
+//    first workgroups and the pre-pass of the next segment in the rest, so the two
+//    overlap on one stream (the host's schedule is in kda_chunk_chain.hip).
 //
 // Chunk slots: without cu_seqlens slot b * NC + j (NC = ceil(T / C)) is chunk j of batch
 // row b; with them, sequence s owns slots floor(cu[s] / C) + s + j for j < ceil(len_s / C)
