@@ -787,3 +787,41 @@ def test_two_pass_segments_fp32_and_ragged(chunk_form):
                          gate_is_log=True, chunk_size=32, out_dtype=torch.float32, two_pass=True)
     assert_close(o, eo, True, "out")
     assert_close(f, ef, True, "state")
+
+
+def test_two_pass_prefill_in_hip_graph(chunk_form):
+    """Every launch of the two-kernel prefill goes onto the caller's stream and nothing is
+    allocated inside the call, so it can be captured in a HIP graph: three replays, with
+    eager work between them, each equal to the eager result."""
+    if chunk_form != "two_pass":
+        pytest.skip("one form")
+    _case("two-pass prefill captured in a graph (segments)")
+    inp = synth.make_prefill(1, 2085, 4, 64, 64, dtype=torch.bfloat16, seed=91, state_std=0.1)
+    d = lambda x: x.cuda()
+    q, k, v, z, ls, be, s0 = (d(x) for x in (inp.q, inp.k, inp.v, inp.z, inp.log_scale, inp.beta, inp.initial_state))
+    n = kda.chunk_fwd_workspace_size(q.dtype, 1, 2085, 4, 64, 64, 32)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, 2085, 4, 64, dtype=torch.float32, device="cuda")
+    fin = torch.empty(1, 4, 64, 64, dtype=torch.float32, device="cuda")
+    call = lambda: kda.chunk_fwd_fused_gate(q, k, v, z, ls, be, initial_state=s0, chunk_size=32, out=out,
+                                            out_dtype=torch.float32, final_state=fin, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    eo, ef = out.clone(), fin.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(3):
+        out.zero_()
+        fin.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eo) and torch.equal(fin, ef), "replay %d differs from the eager call" % i
+        call()  # eager work between replays
+        torch.cuda.synchronize()
