@@ -240,3 +240,25 @@ def test_bounded_decay_bwd_validation(lib):
     assert call(dz=3) == 6                   # d_logits aliases grad
     assert call(db=5) == 6                   # d_bias and d_log_scale share a buffer
     assert call(rows=0, z=None, g=None, dz=None, dls=None, db=None) == 0
+
+
+def test_python_prefill_form_selection():
+    """The binding picks the prefill form from two_pass / TWO_PASS and the shape: a
+    workspace of the size the library asks for, none for two_pass=False or a shape the
+    two-kernel form lacks (by default), and an error when that form is asked for by name."""
+    import torch
+    import gated_delta_rule_31_amd as kda
+    q = torch.zeros(1, 100, 2, 64, dtype=torch.bfloat16)  # a host tensor: no device work happens here
+    ws, n = kda._chunk_workspace(None, None, q, 1, 64, 32, False)
+    assert n == kda.chunk_fwd_workspace_size(torch.bfloat16, 1, 100, 2, 64, 64, 32) > 0 and ws.numel() == n
+    assert kda._chunk_workspace(False, None, q, 1, 64, 32, False) == (None, 0)
+    # bf16 K = V = 128 at chunk 64 has no two-kernel form (its pre-pass exceeds the LDS)
+    q128 = torch.zeros(1, 100, 2, 128, dtype=torch.bfloat16)
+    assert kda.chunk_fwd_workspace_size(torch.bfloat16, 1, 100, 2, 128, 128, 64) == 0
+    assert kda._chunk_workspace(None, None, q128, 1, 128, 64, False) == (None, 0)
+    with pytest.raises(kda.KDAError):
+        kda._chunk_workspace(True, None, q128, 1, 128, 64, False)
+    given = torch.empty(n, dtype=torch.uint8)
+    assert kda._chunk_workspace(None, given, q, 1, 64, 32, False) == (given, n)
+    with pytest.raises(ValueError):
+        kda._chunk_workspace(None, torch.empty(n, dtype=torch.float32), q, 1, 64, 32, False)
