@@ -227,6 +227,10 @@ kda_status recurrent_fwd_impl(const void *q, const void *k, const void *v, kda_d
     }
     if ((const void *)out == (const void *)final_state) return KDA_ERR_ALIAS;
     if (N > (int64_t)(1 << 28) / H) return KDA_ERR_UNSUPPORTED;
+    // the kernel moves states and outputs in 16-byte (8-byte for bf16 outputs) pieces
+    const uintptr_t oal = out_dtype == KDA_BF16 ? 8 : 16;
+    if ((uintptr_t)initial_state % 16 != 0 || (uintptr_t)final_state % 16 != 0 || (uintptr_t)out % oal != 0)
+        return KDA_ERR_BAD_ARGUMENT;
     kda::RecurrentArgs a;
     a.q = q;
     a.k = k;

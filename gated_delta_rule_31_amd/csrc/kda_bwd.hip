@@ -163,19 +163,7 @@ __device__ __forceinline__ float4 raw_f4(s16x4 x) {
 __device__ __forceinline__ int crow(int r, int L) { return r < L ? r : L - 1; }
 __device__ __forceinline__ float4 mask4(float4 x, bool ok) { return ok ? x : make_float4(0.f, 0.f, 0.f, 0.f); }
 
-// sum over the 16 lanes that share lane >> 4 (one accumulator row): DPP row rotations by
-// 8, 4, 2 and 1 stay inside each 16-lane row, and every lane ends with the row's sum
-template <int ROR>
-__device__ __forceinline__ float row_ror(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + ROR, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x += row_ror<8>(x);
-    x += row_ror<4>(x);
-    x += row_ror<2>(x);
-    x += row_ror<1>(x);
-    return x;
-}
+// (row16_sum, the DPP sum over one 16-lane row of an accumulator tile, is in kda_device.h)
 
 // ------------------------------------------------------------------------------------
 // prep: per (chunk slot, head) unit.  After the in-chunk cumulative sum, Gamma is

@@ -26,6 +26,20 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
 
+// Sum over the 16 lanes that share lane >> 4 (one DPP row): row rotations by 8, 4, 2
+// and 1 stay inside the row, and every lane ends with the row's sum.
+template <int ROR>
+__device__ __forceinline__ float row_ror(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + ROR, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += row_ror<8>(x);
+    x += row_ror<4>(x);
+    x += row_ror<2>(x);
+    x += row_ror<1>(x);
+    return x;
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }

@@ -11,12 +11,13 @@
 // Any alpha in [0, 1] is allowed (no rescaling is involved).
 //
 // Mapping: one workgroup per (sequence, head, block of BV value columns), one wave per
-// 16 columns.  Lane l of a wave owns column l % 16 and key rows
-// [RQ * (l / 16), RQ * (l / 16) + RQ) with RQ = K / 4, so the state stays in registers
-// for the whole sequence and the reductions over K are a sum over the lane's own rows
-// plus two cross-lane steps.  The token inputs arrive in blocks of TB tokens: the
-// workgroup loads block b+1 with 16-byte loads while it runs block b from LDS, and
-// converts it to float32 (alpha and k.q included) once for all its columns.
+// 16 columns.  Lane l of a wave owns the four columns 4 (l / 16) .. + 3 and the key rows
+// [RL (l % 16), RL (l % 16) + RL) with RL = K / 16, so the state stays in registers for
+// the whole sequence, each token reads only the lane's RL rows of k, q and alpha from
+// LDS (shared by its four columns), and the reductions over K are a sum over the lane's
+// rows plus a DPP sum inside the 16-lane row.  The token inputs arrive in blocks of TB
+// tokens: the workgroup loads block b+1 with 16-byte loads while it runs block b from
+// LDS, and converts it to float32 (alpha and k.q included) once for all its columns.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -39,7 +40,7 @@ __device__ __forceinline__ f4x2 to_f4x2(bf16x8 x) {
 
 template <typename TIn, int K, int V, bool ZG>
 __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a) {
-    constexpr int RQ = K / 4;                       // key rows per lane
+    constexpr int RL = K / 16;                      // key rows per lane
     constexpr int NW = V / 16 < RW ? V / 16 : RW;   // waves per workgroup
     constexpr int NTH = 64 * NW;
     constexpr int BV = 16 * NW;                     // value columns per workgroup
@@ -62,7 +63,8 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int g = lane >> 4;                        // row quarter
+    const int rg = lane & 15;                       // key-row group: rows RL rg .. RL rg + RL - 1
+    const int cg = lane >> 4;                       // column group: columns 4 cg .. 4 cg + 3
     const int vb = blockIdx.x % NVB;
     const int pair = blockIdx.x / NVB;
     const int H = a.H;
@@ -76,15 +78,32 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
         bos = (int64_t)s * a.T;
         eos = bos + a.T;
     }
-    const int col = wave * 16 + (lane & 15);        // column within the workgroup's block
+    const int col = wave * 16 + 4 * cg;             // first of the lane's columns within the block
     const int gcol = vb * BV + col;
-    const int r0 = RQ * g;
+    const int r0 = RL * rg;
 
-    float S[RQ];
+    // the lane's RL x 4 block of the state: 16-byte accesses along V ([K, V] states) or
+    // along K ([V, K] states, RL a multiple of 4) keep a row of 16 lanes on 64 contiguous bytes
+    float S[RL][4];
     const float *s0 = a.initial_state ? a.initial_state + ((int64_t)s * H + h) * K * V : nullptr;
 #pragma unroll
-    for (int i = 0; i < RQ; ++i)
-        S[i] = !s0 ? 0.f : a.state_vk ? s0[(int64_t)gcol * K + r0 + i] : s0[(int64_t)(r0 + i) * V + gcol];
+    for (int i = 0; i < RL; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) S[i][c] = 0.f;
+    if (s0) {
+        if (!a.state_vk) {
+#pragma unroll
+            for (int i = 0; i < RL; ++i) {
+                const float4 x = *reinterpret_cast<const float4 *>(s0 + (int64_t)(r0 + i) * V + gcol);
+                S[i][0] = x.x; S[i][1] = x.y; S[i][2] = x.z; S[i][3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < RL; ++i) S[i][c] = s0[(int64_t)(gcol + c) * K + r0 + i];
+        }
+    }
 
     const bool glog = a.gate.mode == GATE_LOG;
     float s2 = 0.f, l2 = 0.f;
@@ -206,28 +225,48 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
         for (int j = 0; j < TB; ++j) {
             const int64_t t = t0 + j;
             if (t >= eos) break;
-            const float *kr = &sk[buf][j][r0], *qr = &sq[buf][j][r0], *ar = &sa[buf][j][r0];
-            float p = 0.f, r = 0.f;
+            float kx[RL], qx[RL], ax[RL];
 #pragma unroll
-            for (int i = 0; i < RQ; i += 4) {
-                const float4 k4 = *reinterpret_cast<const float4 *>(kr + i);
-                const float4 q4 = *reinterpret_cast<const float4 *>(qr + i);
-                const float4 a4 = *reinterpret_cast<const float4 *>(ar + i);
-                S[i] *= a4.x; S[i + 1] *= a4.y; S[i + 2] *= a4.z; S[i + 3] *= a4.w;
-                p += S[i] * k4.x + S[i + 1] * k4.y + S[i + 2] * k4.z + S[i + 3] * k4.w;
-                r += S[i] * q4.x + S[i + 1] * q4.y + S[i + 2] * q4.z + S[i + 3] * q4.w;
+            for (int i = 0; i < RL; ++i) {
+                kx[i] = sk[buf][j][r0 + i];
+                qx[i] = sq[buf][j][r0 + i];
+                ax[i] = sa[buf][j][r0 + i];
             }
-            // sum over the four row quarters (lanes l, l^16, l^32, l^48)
-            p += __shfl_xor(p, 16);
-            r += __shfl_xor(r, 16);
-            p += __shfl_xor(p, 32);
-            r += __shfl_xor(r, 32);
-            const float d = sbeta[buf][j] * (sv[buf][j][col] - p);
-            if (g == 0) st_out(a.out, a.out_bf16, (t * H + h) * V + gcol, a.scale * (r + skq[buf][j] * d));
+            float p[4], r[4];
 #pragma unroll
-            for (int i = 0; i < RQ; i += 4) {
-                const float4 k4 = *reinterpret_cast<const float4 *>(kr + i);
-                S[i] += k4.x * d; S[i + 1] += k4.y * d; S[i + 2] += k4.z * d; S[i + 3] += k4.w * d;
+            for (int c = 0; c < 4; ++c) {
+                p[c] = 0.f;
+                r[c] = 0.f;
+#pragma unroll
+                for (int i = 0; i < RL; ++i) {
+                    S[i][c] *= ax[i];
+                    p[c] += S[i][c] * kx[i];
+                    r[c] += S[i][c] * qx[i];
+                }
+                // sum over the 16 row groups (the lanes of this DPP row)
+                p[c] = row16_sum(p[c]);
+                r[c] = row16_sum(r[c]);
+            }
+            const float4 v4 = *reinterpret_cast<const float4 *>(&sv[buf][j][col]);
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            const float bj = sbeta[buf][j], kq = skq[buf][j];
+            float o[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float d = bj * (vv[c] - p[c]);
+                o[c] = a.scale * (r[c] + kq * d);
+#pragma unroll
+                for (int i = 0; i < RL; ++i) S[i][c] += kx[i] * d;
+            }
+            if (rg == 0) {  // the row's four columns in one store
+                const int64_t oi = (t * H + h) * V + gcol;
+                if (a.out_bf16) {
+                    typedef __attribute__((ext_vector_type(4))) __bf16 bf4;
+                    *reinterpret_cast<bf4 *>(static_cast<__bf16 *>(a.out) + oi) =
+                        bf4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                } else {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + oi) = float4{o[0], o[1], o[2], o[3]};
+                }
             }
         }
         if (b + 1 < nblk) stage_block(buf ^ 1);
@@ -235,12 +274,15 @@ __global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a)
     }
     if (a.final_state) {
         float *sf = a.final_state + ((int64_t)s * H + h) * K * V;
+        if (!a.state_vk) {
 #pragma unroll
-        for (int i = 0; i < RQ; ++i) {
-            if (a.state_vk)
-                sf[(int64_t)gcol * K + r0 + i] = S[i];
-            else
-                sf[(int64_t)(r0 + i) * V + gcol] = S[i];
+            for (int i = 0; i < RL; ++i)
+                *reinterpret_cast<float4 *>(sf + (int64_t)(r0 + i) * V + gcol) = float4{S[i][0], S[i][1], S[i][2], S[i][3]};
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < RL; ++i) sf[(int64_t)(gcol + c) * K + r0 + i] = S[i][c];
         }
     }
 }

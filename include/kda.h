@@ -189,8 +189,9 @@ kda_status kda_chunk_fwd_fused_gate(const void *q, const void *k, const void *v,
 
 /*
  * kda_recurrent_fwd -- the same operation as kda_chunk_fwd (same arguments, layouts,
- * state rules, varlen and empty-sequence behaviour) evaluated token by token with the
- * state held in registers (PaperLeet "Formula and conventions"; the model excerpt on the
+ * state rules, varlen and empty-sequence behaviour; the states must be 16-byte aligned
+ * and out 16-byte aligned, 8-byte for bf16 output, else KDA_ERR_BAD_ARGUMENT)
+ * evaluated token by token with the state held in registers (PaperLeet "Formula and conventions"; the model excerpt on the
  * Kept-memory page runs a token-recurrent kernel beside the chunked one for any length).
  * Meant for short sequences (speculative decoding, short prompts), where the chunked
  * form's per-chunk work does not pay off.  No chunk size; any alpha in [0, 1] is

@@ -184,6 +184,8 @@ def test_recurrent_fwd_validation(lib):
     assert call(sf=3) == 6
     assert call(cu=9, B=2) == 5
     assert call(T=0, q=None, out=None) == 0   # empty: nothing to do without a final state
+    assert call(out=66) == 5                  # bf16 output not 8-byte aligned
+    assert call(out=64, sf=72) == 5           # final state not 16-byte aligned
     g = lib.kda_recurrent_fwd_fused_gate
     g.restype = i32
     g.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, ctypes.c_uint, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32,
