@@ -38,8 +38,11 @@ __device__ __forceinline__ f4x2 to_f4x2(bf16x8 x) {
     return y;
 }
 
+// Four waves per SIMD (at most 128 registers; five would spill): more workgroups in
+// flight hide the state loads at their start.
 template <typename TIn, int K, int V, bool ZG>
-__global__ __launch_bounds__(64 * RW) void recurrent_fwd_kernel(RecurrentArgs a) {
+__global__ __launch_bounds__(64 * RW) __attribute__((amdgpu_waves_per_eu(4))) void recurrent_fwd_kernel(
+    RecurrentArgs a) {
     constexpr int RL = K / 16;                      // key rows per lane
     constexpr int NW = V / 16 < RW ? V / 16 : RW;   // waves per workgroup
     constexpr int NTH = 64 * NW;
