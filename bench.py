@@ -202,10 +202,11 @@ def main():
 
     fused = args.gate == "fused"
     nws = kda.chunk_fwd_workspace_size(q.dtype, B, T, H, K, V, args.chunk)
-    assert nws > 0, "the two-kernel form supports the K3 shape"
-    wsp = torch.empty(nws, dtype=torch.uint8, device=dev)  # allocated once, outside the timed steps
+    if nws == 0:
+        log("chunk size %d has no two-kernel form at this shape: timing the single-kernel form" % args.chunk)
+    wsp = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)  # allocated once, outside the timed steps
 
-    def step(ev_pair=None, two_pass=True):
+    def step(ev_pair=None, two_pass=nws > 0):
         if not fused:
             kda.bounded_decay(z, ls, lower_bound=-5.0, out_log=False, out=g)
         if ev_pair is not None:
@@ -276,8 +277,9 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel": "one prefill call: chunk_pack_kernel, 7 x chunk_segment_kernel "
-                     "(chain of a chunk segment beside the next pre-pass), chunk_chain_kernel",
+                     "traffic": traffic if nws > 0 else None,
+                     "kernel": "one prefill call: chunk_pack_kernel, 7 x chunk_segment_kernel (chain of a chunk "
+                     "segment beside the next pre-pass), chunk_chain_kernel" if nws > 0 else "chunk_fwd_kernel",
                      "launch_ms": chunk_ms, "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
@@ -296,7 +298,7 @@ def main():
         def pstep():
             kda.chunk_fwd_fused_gate(q, k, v, z, ls, bl, lower_bound=-5.0, chunk_size=args.chunk, out=out,
                                      final_state=fin_vk, qk_l2norm=True, beta_logits=True, state_vk=True,
-                                     workspace=wsp)
+                                     **(dict(workspace=wsp) if nws > 0 else dict(two_pass=False)))
         pstep()
         torch.cuda.synchronize()
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
