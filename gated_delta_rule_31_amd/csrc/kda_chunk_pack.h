@@ -340,7 +340,9 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         fetch(nxt < nitems ? nx : cur);
         lds_barrier();
 
-        // ---- phase 2: A-matrix operand staging and the package's Qt, -Bw, Kt, gamma_C --
+        // ---- phase 2: A-matrix operand staging and the package's Qt, -Bw, gamma_C; Kt is
+        // kept in registers and goes out through LDS after phase 3 (16-byte stores)
+        float2 ktk[CPT][4];
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int cm = combo_of(u);
@@ -430,11 +432,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
                 st2_at<TM>(gp, (uint32_t)PL::gQt + E * (uint32_t)(r * K + c0), lq.x * eR.x * iq[i], lq.y * eR.y * iq[i]);
                 st2_at<TM>(gp, (uint32_t)PL::gBw + E * (uint32_t)(r * K + c0), -lk.x * eR.x * ik[i], -lk.y * eR.y * ik[i]);
                 kro[i] = float2{ro.x * eCE.x * ik[i], ro.y * eCE.y * ik[i]};
-                if (i & 1) {
-                    // two consecutive tokens per channel row of Kt
-                    st2_at<TM>(gp, (uint32_t)PL::gKt + E * (uint32_t)(c0 * C + r - 1), kro[i - 1].x, kro[i].x);
-                    st2_at<TM>(gp, (uint32_t)PL::gKt + E * (uint32_t)((c0 + 1) * C + r - 1), kro[i - 1].y, kro[i].y);
-                }
+                ktk[u][i] = kro[i];
             }
         }
         lds_barrier();
@@ -442,6 +440,24 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         // ---- phase 3: A-matrix tiles, T's diagonal blocks, A_qk ------------------------
         a_matrix_work<P, K, 16, C, 16, NORM, PPW>(smem, smem + PXL::oTA - L::pTm, 0, wave, lane);
         lds_barrier();
+
+        // Kt [K][C] into the staging area, free now (row stride LCT), two tokens per store
+        constexpr int LCT = C + 16 / (int)sizeof(TM);
+        static_assert((size_t)K * LCT * sizeof(TM) <= (size_t)L::NST * sizeof(TA) * (P::kSplit ? 2 : 1),
+                      "the Kt tile fits in the operand staging area");
+        TM *KtL = reinterpret_cast<TM *>(St);
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int cm = combo_of(u);
+            if (cm >= NCOMBO) continue;
+            const int c0 = 2 * (cm % NCP), p = cm / NCP;
+#pragma unroll
+            for (int i = 1; i < 4; i += 2) {
+                const int r = 16 * p + 4 * qd + i;
+                st2<TM>(KtL + c0 * LCT + r - 1, ktk[u][i - 1].x, ktk[u][i].x);
+                st2<TM>(KtL + (c0 + 1) * LCT + r - 1, ktk[u][i - 1].y, ktk[u][i].y);
+            }
+        }
 
         // ---- phase 4: T's off-diagonal blocks.  Block column qb depends only on itself
         // (T_pq = -T_pp sum_{r=q}^{p-1} A_pr T_rq), so wave qb fills column qb top down.
@@ -471,16 +487,26 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         }
         lds_barrier();
 
-        // ---- T and A_qk to the package, 16 bytes per lane ------------------------------
+        // ---- Kt, T and A_qk to the package, 16 bytes per lane ---------------------------
         // (the next item's phase 1 touches neither these nor the staging area, and its
         // first barrier comes before anything here is written again)
         constexpr int RC = C * (int)sizeof(TM) / 16;  // 16-byte pieces per row
-        for (int e = tid; e < 2 * C * RC; e += PPT) {
-            const int mat = e / (C * RC), rem = e - mat * C * RC;
-            const int row = rem / RC, pc = rem - row * RC;
-            const TM *src = (mat ? AqL : TmL) + row * L::LCM;
+        for (int e = tid; e < (K + 2 * C) * RC; e += PPT) {
+            const int row = e / RC, pc = e - row * RC;  // rows: Kt's K, then T's C, then A_qk's C
+            const TM *src;
+            size_t dst;
+            if (row < K) {
+                src = KtL + row * LCT;
+                dst = PL::gKt + (size_t)row * C * sizeof(TM);
+            } else if (row < K + C) {
+                src = TmL + (row - K) * L::LCM;
+                dst = PL::gTm + (size_t)(row - K) * C * sizeof(TM);
+            } else {
+                src = AqL + (row - K - C) * L::LCM;
+                dst = PL::gAqk + (size_t)(row - K - C) * C * sizeof(TM);
+            }
             const uint4 x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(src) + 16 * pc);
-            *reinterpret_cast<uint4 *>(gp + (mat ? PL::gAqk : PL::gTm) + (size_t)row * C * sizeof(TM) + 16 * pc) = x;
+            *reinterpret_cast<uint4 *>(gp + dst + 16 * pc) = x;
         }
         item = nxt;
         cur = nx;
