@@ -825,3 +825,23 @@ def test_two_pass_prefill_in_hip_graph(chunk_form):
         assert torch.equal(out, eo) and torch.equal(fin, ef), "replay %d differs from the eager call" % i
         call()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("K,V,C,H", [(16, 16, 16, 1), (128, 16, 32, 3), (16, 128, 32, 2)])
+def test_two_pass_segments_small_and_lopsided_shapes(K, V, C, H, chunk_form):
+    """Chunk segments at the narrow ends of the supported widths (one chain workgroup in
+    all, a wide key with a narrow value block and the reverse), fp32 at 1e-4."""
+    if chunk_form != "two_pass":
+        pytest.skip("segments exist in the two-kernel form only")
+    if not kda.chunk_fwd_workspace_size(torch.float32, 1, 64 * C + 5, H, K, V, C):
+        pytest.skip("no two-kernel form for this shape")
+    T = 64 * C + 5  # 65 chunks: segments of 32, 32 and 1
+    _case("two-pass segments fp32 K=%d V=%d C=%d H=%d T=%d" % (K, V, C, H, T))
+    inp = synth.make_prefill(1, T, H, K, V, dtype=torch.float32, seed=K + V + C, state_std=0.1)
+    eo, ef = oracle_prefill(inp)
+    d = lambda x: x.cuda()
+    g = kda.bounded_decay(d(inp.z), d(inp.log_scale), out_log=True)
+    o, f = kda.chunk_fwd(d(inp.q), d(inp.k), d(inp.v), g, d(inp.beta), initial_state=d(inp.initial_state),
+                         gate_is_log=True, chunk_size=C, out_dtype=torch.float32, two_pass=True)
+    assert_close(o, eo, True, "out")
+    assert_close(f, ef, True, "state")
