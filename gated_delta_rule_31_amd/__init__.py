@@ -11,7 +11,11 @@ Entry points (same names as the C ABI, minus the ``kda_`` prefix where noted):
 * ``bounded_decay(logits, log_scale, lower_bound=-5, bias=None, out_log=False)``
   -- the K3 gate alpha = exp(g_min * sigmoid(e^A (z + bias))) (or g itself).
 * ``chunk_fwd(q, k, v, gate, beta, ...)`` -- chunkwise prefill with optional
-  initial / final state and packed sequences (``cu_seqlens``).
+  initial / final state and packed sequences (``cu_seqlens``).  By default
+  (``TWO_PASS``) it runs in its two-kernel form over a workspace (a pre-pass over all
+  chunks, then the serial part); ``two_pass=False`` selects the single kernel, and
+  ``workspace=`` passes a caller-owned buffer of ``chunk_fwd_workspace_size(...)``
+  bytes.
 * ``recurrent_step(q, k, v, gate, beta, state, ...)`` -- one decode token, state
   updated in place.
 * ``recurrent_fwd(q, k, v, gate, beta, ...)`` -- the prefill contract of ``chunk_fwd``
