@@ -1657,7 +1657,7 @@ hipError_t set_lds(const void *kern, size_t bytes) {
 
 template <typename TIn, int K, int V>
 hipError_t launch_kv(const BwdArgs &a, int num_seqs, hipStream_t stream) {
-    static bool attr = false;  // per instantiation, once per process
+    static std::atomic<bool> attr{false};  // per instantiation, once per process
     auto kprep = bwd_prep_kernel<TIn, K, V>;
     auto kvg = bwd_vgrads_kernel<TIn, K, V>;
     auto kkg = bwd_kgrads_kernel<TIn, K, V>;

@@ -1116,7 +1116,7 @@ hipError_t launch_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream, int
     } else {
         using L = Layout<P, K, V, C, BV>;
         auto kern = chunk_fwd_kernel<P, K, V, C, BV, GM>;
-        static bool attr_set = false;  // per instantiation, once per process
+        static std::atomic<bool> attr_set{false};  // per instantiation, once per process
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::total);

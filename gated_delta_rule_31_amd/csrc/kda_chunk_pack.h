@@ -721,7 +721,7 @@ hipError_t launch_pack_kc(const ChunkArgs &a, int64_t items, int max_wgs, hipStr
         return hipErrorNotSupported;
     } else {
         auto kern = chunk_pack_kernel<P, K, C, GM>;
-        static bool attr_set = false;
+        static std::atomic<bool> attr_set{false};
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)X::total);
@@ -768,7 +768,7 @@ hipError_t launch_chain_kvc(const ChunkArgs &a, int num_pairs, hipStream_t strea
         if (bv_out) *bv_out = BV;
         if (!a.q) return hipSuccess;  // query only
         auto kern = chunk_chain_kernel<P, K, V, C, BV>;
-        static bool attr_set = false;
+        static std::atomic<bool> attr_set{false};
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)X::total);
@@ -818,7 +818,7 @@ hipError_t launch_segment_kvc(const ChunkArgs &ca, const ChunkArgs &pa, int num_
         constexpr size_t lds = ChainLds<P, K, V, C, BV>::total > PrepassLds<P, K, C>::total
                                    ? ChainLds<P, K, V, C, BV>::total : PrepassLds<P, K, C>::total;
         auto kern = chunk_segment_kernel<P, K, V, C, BV, GM>;
-        static bool attr_set = false;
+        static std::atomic<bool> attr_set{false};
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -1,6 +1,8 @@
 // kda_util.hip -- small fill / copy kernels for the empty-sequence path (kernels rather
 // than hipMemsetAsync / hipMemcpyAsync so that a caller may capture the call in a HIP
 // graph), and the compute-unit count that sizes the persistent grids.
+#include <atomic>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -16,15 +18,16 @@ __global__ __launch_bounds__(256) void fill_copy_kernel(float *dst, const float 
 }  // namespace
 
 int device_cu_count() {
-    static int cache[64] = {0};
+    // per device, filled on first use; threads that race to fill it store the same value
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cache[dev]) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 hipError_t launch_fill_copy(float *dst, const float *src, int64_t n, hipStream_t stream) {
