@@ -145,8 +145,8 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--chunk", type=int, default=32)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--gate", choices=("fused", "separate"), default="fused",
