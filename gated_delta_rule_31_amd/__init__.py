@@ -35,6 +35,7 @@ Entry points (same names as the C ABI, minus the ``kda_`` prefix where noted):
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Tuple
 
@@ -592,13 +593,41 @@ class _ChunkKDAFn(torch.autograd.Function):
         return dq, dk, dv, da, db, ds0, None, None
 
 
-def recurrent_kda(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 32, scale: float = 1.0):
+# Smallest retention the chunked prefill accepts: its 16-token rescale factors stay finite
+# only while every log-decay is at least -5 (the bounded gate's range, g_min = -5).
+CHUNK_MIN_ALPHA = math.exp(-5.0) * (1.0 - 1e-6)
+
+
+def gate_within_chunk_bound(alpha: torch.Tensor) -> bool:
+    """True when every retention factor is at least e^-5, the chunked prefill's
+    precondition (one device reduction and a host synchronisation)."""
+    return alpha.numel() == 0 or bool(alpha.detach().min() >= CHUNK_MIN_ALPHA)
+
+
+def recurrent_kda(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 32, scale: float = 1.0,
+                  bounded: Optional[bool] = None):
     """PaperLeet ``recurrent_kda`` contract: (output [B,T,H,V], final_state [B,H,K,V]),
     output in the inputs' dtype, every output read after its token's update, inputs
-    untouched; T == 0 returns the supplied state (or zeros).  When any input requires
-    grad the call is recorded for autograd: the backward is ``chunk_bwd`` (gradients to
-    q, k, v, alpha, beta and initial_state)."""
-    if _needs_grad(q, k, v, alpha, beta, initial_state):
+    untouched; T == 0 returns the supplied state (or zeros); any alpha in [0, 1].
+
+    The chunked prefill needs every alpha >= e^-5 (the bounded gate's range); the
+    token-recurrent kernel takes any alpha in [0, 1].  ``bounded`` picks the path:
+    None checks the smallest alpha on the device (one reduction and a host sync) and
+    takes the chunked prefill when the bound holds, the token-recurrent kernel when it
+    does not; True takes the chunked prefill (the caller vouches for the bound); False
+    the token-recurrent kernel.  When any input requires grad the call is recorded for
+    autograd through the chunked prefill, whose backward (``chunk_bwd``, gradients to
+    q, k, v, alpha, beta and initial_state) needs the same bound: a gate outside it
+    raises ValueError."""
+    grad = _needs_grad(q, k, v, alpha, beta, initial_state)
+    if bounded is None:
+        bounded = gate_within_chunk_bound(alpha)
+    if grad:
+        if not bounded:
+            raise ValueError("recurrent_kda with autograd needs every alpha >= e^-5 (the chunked prefill and "
+                             "its backward are defined for the bounded gate)")
         return _ChunkKDAFn.apply(q, k, v, alpha, beta, initial_state, chunk_size, float(scale))
-    return chunk_fwd(q, k, v, alpha, beta, initial_state=initial_state, output_final_state=True,
-                     chunk_size=chunk_size, scale=scale)
+    if bounded:
+        return chunk_fwd(q, k, v, alpha, beta, initial_state=initial_state, output_final_state=True,
+                         chunk_size=chunk_size, scale=scale)
+    return recurrent_fwd(q, k, v, alpha, beta, initial_state=initial_state, output_final_state=True, scale=scale)

@@ -115,6 +115,8 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, kda_dtype
     }
     if ((const void *)out == (const void *)final_state) return KDA_ERR_ALIAS;
     if (N > (int64_t)(1 << 30) / H) return KDA_ERR_UNSUPPORTED;
+    // the kernels write four value columns of a token per store (8 or 16 bytes)
+    if ((uintptr_t)out % (out_dtype == KDA_BF16 ? 8 : 16) != 0) return KDA_ERR_BAD_ARGUMENT;
     int64_t slots = 0;
     if (workspace) {
         // the two-kernel form: one package per (chunk slot, head) in the workspace

@@ -4,7 +4,7 @@
 
 namespace kda {
 
-static_assert(PackLayout<PrecMixed, 128, 32>::bytes == 2 * (3 * 32 * 128 + 2 * 32 * 32) + 4 * 128 + 4 * 32,
+static_assert(PackLayout<PrecMixed, 128, 32>::bytes == 2 * (3 * 32 * 128 + 3 * 32 * 32) + 4 * 128 + 4 * 32,
               "chunk_pack_bytes follows PackLayout");
 static_assert(PackLayout<PrecF32, 64, 16>::bytes == 4 * (3 * 16 * 64 + 2 * 16 * 16) + 4 * 64 + 4 * 16,
               "chunk_pack_bytes follows PackLayout");
@@ -24,7 +24,8 @@ size_t chunk_pack_bytes(bool fp32_inputs, int K, int V, int C) {
     int bv = 0;
     if (launch_chunk_chain(q, fp32_inputs, K, V, C, 0, nullptr, &bv) != hipSuccess || bv == 0) return 0;
     const size_t tm = fp32_inputs ? 4 : 2;  // matrix-operand bytes (PackLayout)
-    return tm * (3 * (size_t)C * K + 2 * (size_t)C * C) + 4 * (size_t)K + 4 * (size_t)C;
+    const size_t aq = fp32_inputs ? 1 : 2;  // A_qk parts (PackLayout)
+    return tm * (3 * (size_t)C * K + (1 + aq) * (size_t)C * C) + 4 * (size_t)K + 4 * (size_t)C;
 }
 
 size_t chunk_fwd_workspace_bytes(bool fp32_inputs, int64_t slots, int64_t N, int H, int K, int V, int C) {

@@ -61,15 +61,24 @@ constexpr int NT = 64 * NSW + NPT;  // threads per workgroup (three waves per SI
 
 constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
 
+// kSegWaves: waves per SIMD the segment kernel (chain beside pre-pass) is compiled for --
+// four on the 16-bit path, so a chain workgroup and a pre-pass workgroup share a compute
+// unit; two with float32 operands, whose fragments take twice the registers.
 struct PrecMixed {
     using TA = __bf16;    // operands of the decay-rescaled key/query products
     using TM = _Float16;  // every other matrix-core operand
     static constexpr bool kSplit = true;
+    static constexpr int kSegWaves = 4;
+    // A_qk reaches the serial part as hi + lo fp16 parts: the product that carries each
+    // token's own pseudo-value to its output needs more than fp16's 11 mantissa bits
+    static constexpr int kAqParts = 2;
 };
 struct PrecF32 {
     using TA = float;
     using TM = float;
     static constexpr bool kSplit = false;
+    static constexpr int kSegWaves = 2;
+    static constexpr int kAqParts = 1;
 };
 
 template <class P, int K, int V, int C, int BV>
@@ -112,9 +121,13 @@ struct Layout {
     static constexpr size_t pKt = pBw + al16((size_t)C * LKM * sizeof(TM));
     static constexpr size_t pTm = pKt + al16((size_t)K * LCM * sizeof(TM));
     static constexpr size_t pAqk = pTm + al16((size_t)C * LCM * sizeof(TM));
-    static constexpr size_t pbV = pAqk + al16((size_t)C * LCM * sizeof(TM));
+    static constexpr size_t pAql = pAqk + al16((size_t)C * LCM * sizeof(TM));  // low part (16-bit path)
+    // the raw values of the chunk's value block, [BV][LCM] in the input type (same size
+    // as TM); gamma_C [K] and beta [C] in float32, adjacent as in the workspace package
+    static constexpr size_t pbV = pAql + (P::kAqParts - 1) * al16((size_t)C * LCM * sizeof(TM));
     static constexpr size_t pGC = pbV + al16((size_t)BV * LCM * sizeof(TM));
-    static constexpr size_t szPkg = al16(pGC + (size_t)K * 4);
+    static constexpr size_t pBt = pGC + (size_t)K * 4;
+    static constexpr size_t szPkg = al16(pBt + (size_t)C * 4);
     static constexpr size_t total = oPkg + 2 * szPkg;
     static constexpr bool fits = total <= 160 * 1024;
 };
@@ -210,6 +223,89 @@ __device__ __forceinline__ void mma_bfrag(f4 &acc, const float *arow, const BFra
         }
     }
 }
+
+// The A operand of mma_bfrag held in registers: this lane's part of one 16-row tile over
+// NKT k tiles, in the permuted k order of BFrag.  Loading a whole phase's fragments before
+// its products keeps the LDS reads in flight together instead of one read per product.
+template <typename TM, int NKT>
+struct AFrag;
+
+template <int NKT>
+struct AFrag<_Float16, NKT> {
+    f16x8 pair[NKT / 2 > 0 ? NKT / 2 : 1];
+    f16x4 tail;
+    // the first nkt k tiles of row `arow` (rows with bit 3 set swizzled when SW)
+    template <bool SW>
+    __device__ __forceinline__ void load(const _Float16 *arow, int nkt, int lane) {
+        const int kg = (4 * (lane >> 4)) ^ (SW && (lane & 8) ? 4 : 0);
+#pragma unroll
+        for (int m = 0; m < NKT / 2; ++m) {
+            if (2 * m < nkt) {
+                const f16x4 lo = *reinterpret_cast<const f16x4 *>(arow + 32 * m + kg);
+                const f16x4 hi = *reinterpret_cast<const f16x4 *>(arow + 32 * m + 16 + kg);
+                pair[m] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        }
+        if constexpr (NKT % 2 == 1) {
+            if (NKT - 1 < nkt) tail = *reinterpret_cast<const f16x4 *>(arow + 16 * (NKT - 1) + kg);
+        }
+    }
+};
+
+template <int NKT>
+struct AFrag<float, NKT> {
+    f4 t[NKT];
+    template <bool SW>
+    __device__ __forceinline__ void load(const float *arow, int nkt, int lane) {
+        const int g = lane >> 4;
+        const int sw = SW && (lane & 8) ? 2 : 0;
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) {
+            if (i < nkt) {
+                f4 x;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) x[s] = arow[16 * i + 4 * g + (s ^ sw)];
+                t[i] = x;
+            }
+        }
+    }
+};
+
+// acc += A B over the first nkt k tiles, A from registers (AFrag), B from accumulators
+// (BFrag): rows of the result are A's rows.  With TR the operands trade places, giving
+// the transposed tile (B^T A^T): rows are B's columns and columns are A's rows.
+template <bool TR, int NKT>
+__device__ __forceinline__ void mma_frag(f4 &acc, const AFrag<_Float16, NKT> &a, const BFrag<_Float16, NKT> &b,
+                                         int nkt) {
+#pragma unroll
+    for (int m = 0; m < NKT / 2; ++m)
+        if (2 * m < nkt)
+            acc = TR ? __builtin_amdgcn_mfma_f32_16x16x32_f16(b.pair[m], a.pair[m], acc, 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_16x16x32_f16(a.pair[m], b.pair[m], acc, 0, 0, 0);
+    if constexpr (NKT % 2 == 1) {
+        if (NKT - 1 < nkt) {
+            const f16x8 x = {a.tail[0], a.tail[1], a.tail[2], a.tail[3], 0, 0, 0, 0};
+            const f16x8 y = {b.tail[0], b.tail[1], b.tail[2], b.tail[3], 0, 0, 0, 0};
+            acc = TR ? __builtin_amdgcn_mfma_f32_16x16x32_f16(y, x, acc, 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, acc, 0, 0, 0);
+        }
+    }
+}
+
+template <bool TR, int NKT>
+__device__ __forceinline__ void mma_frag(f4 &acc, const AFrag<float, NKT> &a, const BFrag<float, NKT> &b, int nkt) {
+#pragma unroll
+    for (int i = 0; i < NKT; ++i)
+        if (i < nkt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc = TR ? __builtin_amdgcn_mfma_f32_16x16x4f32(b.t[i][s], a.t[i][s], acc, 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_16x16x4f32(a.t[i][s], b.t[i][s], acc, 0, 0, 0);
+}
+
+// Compiler scheduling fence: no instruction moves across it, so LDS reads issued before
+// it stay ahead of the products after it.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // store two consecutive elements (a at p[0], b at p[1]) as one packed write
 template <typename T>
@@ -409,6 +505,7 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
     float *Tf = reinterpret_cast<float *>(smem + L::oTf);
     TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
     TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
+    TM *Aql = reinterpret_cast<TM *>(pk + L::pAql);
     const float *Nrm = reinterpret_cast<const float *>(smem + L::oNrm) + nb * L::NNRM;
     // 1 / max(|x_r|, 1e-6) of chunk row r, for x = q (qk = 0) or k (qk = 1)
     auto inv_norm = [&](int qk, int r) -> float {
@@ -478,8 +575,80 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
                 for (int e = 0; e < 4; ++e) acc[e] *= cj * inv_norm(0, i0 + e);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Aqk[(i0 + e) * L::LCM + j] = from_f32<TM>((j <= i0 + e) ? acc[e] : 0.f);
+            for (int e = 0; e < 4; ++e) {
+                const float x = (j <= i0 + e) ? acc[e] : 0.f;
+                const TM hi = from_f32<TM>(x);
+                Aqk[(i0 + e) * L::LCM + j] = hi;
+                if constexpr (P::kAqParts == 2) Aql[(i0 + e) * L::LCM + j] = from_f32<TM>(x - to_f32(hi));
+            }
         }
+}
+
+// 2^e as a float (e clamped to the normal range)
+__device__ __forceinline__ float pow2f(int e) {
+    e = e < -126 ? -126 : (e > 127 ? 127 : e);
+    return __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
+}
+
+// largest magnitude over this lane's accumulator tiles
+template <int N>
+__device__ __forceinline__ float maxabs(const f4 (&x)[N]) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(x[i][e]));
+    return m;
+}
+
+// The exponent s >= 0 of the power-of-two scale that brings the wave's largest magnitude
+// m below 2^15, inside the 16-bit float range (0 whenever m < 2^15).
+__device__ __forceinline__ int wave_scale_exp(float m) {
+    m = fmaxf(m, row_ror<8>(m));
+    m = fmaxf(m, row_ror<4>(m));
+    m = fmaxf(m, row_ror<2>(m));
+    m = fmaxf(m, row_ror<1>(m));
+    const int b = __builtin_bit_cast(int, m);
+    const int r = max(max(__builtin_amdgcn_readlane(b, 0), __builtin_amdgcn_readlane(b, 16)),
+                      max(__builtin_amdgcn_readlane(b, 32), __builtin_amdgcn_readlane(b, 48)));
+    const int e = (r >> 23) & 0xff;  // biased exponent of the wave's maximum
+    return e > 141 ? e - 141 : 0;
+}
+
+// hi + lo 16-bit operand parts of accumulator tiles (lo = the rounded remainder x - hi):
+// with both parts a product keeps about 22 mantissa bits of x
+template <int NKT>
+__device__ __forceinline__ void set_split(BFrag<_Float16, NKT> &hi, BFrag<_Float16, NKT> &lo, const f4 (&t)[NKT]) {
+    hi.set(t);
+    f4 r[NKT];
+#pragma unroll
+    for (int i = 0; i < NKT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[i][e] = t[i][e] - (float)(_Float16)t[i][e];
+    lo.set(r);
+}
+template <int NKT>
+__device__ __forceinline__ void set_split(BFrag<float, NKT> &hi, BFrag<float, NKT> &, const f4 (&t)[NKT]) {
+    hi.set(t);  // float32 operands: no low part
+}
+
+// Sh = the 16-bit operand form of the state S 2^-sS, with sS from the state's magnitude on
+// the 16-bit path (always 0 on the float32 path).
+template <bool P16, typename TM, int NKT>
+__device__ __forceinline__ void set_state_frag(BFrag<TM, NKT> &Sh, int &sS, const f4 (&S)[NKT]) {
+    sS = 0;
+    if constexpr (P16) {
+        sS = wave_scale_exp(maxabs(S));
+        if (sS) {
+            const float d = pow2f(-sS);
+            f4 x[NKT];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) x[t] = S[t] * d;
+            Sh.set(x);
+            return;
+        }
+    }
+    Sh.set(S);
 }
 
 // The state waves (w = 0..NSW-1): the float32 state of this workgroup's value columns in
@@ -488,12 +657,17 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
 // the chunk staged in the previous period (two barriers a period); with PK each package
 // arrives complete from the pre-pass (one barrier a period), its matrix operands stored
 // with the row swizzle of mma_bfrag.
-template <class P, int K, int V, int C, int BV, bool NORM, bool PK>
+template <class P, int K, int V, int C, int BV, bool NORM, bool PK, bool FEW_REGS = false>
 __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *smem, unsigned char *pkg0, int s,
                                             int h, int vb, int64_t bos, int64_t eos, int nchunks, int wave,
                                             int lane) {
     using L = Layout<P, K, V, C, BV>;
     using TM = typename P::TM;
+    using TIn = typename std::conditional<std::is_same<P, PrecF32>::value, float, __bf16>::type;
+    constexpr bool P16 = !std::is_same<TM, float>::value;  // 16-bit matrix-core operands
+    // Lean order (fewer fragments live at once): the single kernel, whose twelve waves have
+    // fewer registers each, and float32 fragments of 64-token chunks.
+    constexpr bool LEAN = FEW_REGS || !PK || (!P16 && C >= 64);
     constexpr int NP = L::NP;
     constexpr int NKT_K = K / 16;
     const int g = lane >> 4;
@@ -520,9 +694,10 @@ __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *s
             S[mj][t] = x;
         }
     }
-    BFrag<TM, NKT_K> Sh[L::MJ];
+    BFrag<TM, NKT_K> Sh[L::MJ];  // the state as a 16-bit operand: S 2^-sS
+    int sS[L::MJ];
 #pragma unroll
-    for (int mj = 0; mj < L::MJ; ++mj) Sh[mj].set(S[mj]);
+    for (int mj = 0; mj < L::MJ; ++mj) set_state_frag<P16>(Sh[mj], sS[mj], S[mj]);
 
     for (int it = 0; it <= nchunks; ++it) {
         if constexpr (!PK) {
@@ -567,87 +742,172 @@ __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *s
                 }
             }
         }
-        f4 Vt[L::MJ][NP];
-        BFrag<TM, NP> Vh[L::MJ];
         const int cn = it - 1;  // chunk handled by the state waves in this iteration
         if (cn >= 0) {
+            // The package of chunk cn is complete in LDS.  Its operand fragments are read in
+            // three groups, each issued before the products of the phase ahead of it, so their
+            // LDS latency overlaps the previous phase instead of stalling every product.
             const unsigned char *pk = pkg(cn & 1);
             const TM *Qt = reinterpret_cast<const TM *>(pk + L::pQt);
             const TM *Bw = reinterpret_cast<const TM *>(pk + L::pBw);
+            const TM *Kt = reinterpret_cast<const TM *>(pk + L::pKt);
             const TM *Tm = reinterpret_cast<const TM *>(pk + L::pTm);
             const TM *Aqk = reinterpret_cast<const TM *>(pk + L::pAqk);
-            const TM *bV = reinterpret_cast<const TM *>(pk + L::pbV);
-            const int64_t t0 = bos + (int64_t)cn * C;
-            const int n = (int)((eos - t0) < C ? (eos - t0) : C);
-            // output rows of the chunk from a uniform base, 32-bit element offsets
-            unsigned char *ob = static_cast<unsigned char *>(a.out) + (t0 * H + h) * V * (a.out_bf16 ? 2 : 4);
-            auto store_o = [&](int p, int jt, f4 o) {
-                const int j = vb * BV + jt * 16 + (lane & 15);
+            const TM *Aql = reinterpret_cast<const TM *>(pk + L::pAql);
+            const TIn *vL = reinterpret_cast<const TIn *>(pk + L::pbV);
+            const float *eGC = reinterpret_cast<const float *>(pk + L::pGC);
+            const float *bL = reinterpret_cast<const float *>(pk + L::pBt);
+            const int r16 = lane & 15;
+            // group 1: -Bw and T (Y and Vt), beta V in float32
+            AFrag<TM, NKT_K> fb[NP];
+            AFrag<TM, NP> ft[NP];
+            f4 bv[L::MJ][NP];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * p + 4 * g + e;
-                    const uint32_t off = (uint32_t)(i * H * V + j);
-                    if (i < n) {
-                        if (a.out_bf16)
-                            *reinterpret_cast<__bf16 *>(ob + 2u * off) = (__bf16)(a.scale * o[e]);
-                        else
-                            *reinterpret_cast<float *>(ob + 4u * off) = a.scale * o[e];
-                    }
+            for (int p = 0; p < NP; ++p) {
+                fb[p].template load<PK>(Bw + (16 * p + r16) * L::LKM, NKT_K, lane);
+                ft[p].template load<PK>(Tm + (16 * p + r16) * L::LCM, p + 1, lane);
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(bL + 16 * p + 4 * g);
+#pragma unroll
+                for (int mj = 0; mj < L::MJ; ++mj) {
+                    const int jt = wave + NSW * mj < L::NJT ? wave + NSW * mj : 0;
+                    const TIn *vr = vL + (jt * 16 + r16) * L::LCM + 16 * p + 4 * g;
+                    bv[mj][p] = f4{b4.x * to_f32(vr[0]), b4.y * to_f32(vr[1]), b4.z * to_f32(vr[2]),
+                                   b4.w * to_f32(vr[3])};
                 }
+            }
+            sched_fence();
+            // group 2: Qt and A_qk (the output); in the lean order after Y and Vt
+            AFrag<TM, NKT_K> fq[NP];
+            AFrag<TM, NP> fa[NP], fl[NP];  // A_qk, and its low part on the 16-bit path
+            auto load_group2 = [&]() {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    fq[p].template load<PK>(Qt + (16 * p + r16) * L::LKM, NKT_K, lane);
+                    fa[p].template load<PK>(Aqk + (16 * p + r16) * L::LCM, p + 1, lane);
+                    if constexpr (P16) fl[p].template load<PK>(Aql + (16 * p + r16) * L::LCM, p + 1, lane);
+                }
+                sched_fence();
             };
+            if constexpr (!LEAN) load_group2();
+            // With 16-bit operands every product input goes through an exact power-of-two
+            // scale 2^-x chosen per wave so its largest magnitude stays below 2^15 (x = 0
+            // unless a value reaches that): sS for the state, sY for Y, sV for Vt, each
+            // relative to the one before.  The float32 quantities are rescaled by the same
+            // powers of two, so any finite state or value magnitude stays in range.
+            // On the 16-bit path Y and Vt enter their products as hi + lo parts: the
+            // products that carry a token's own value into its output and into the state
+            // need more than fp16's 11 bits for the workload's largest outputs.
+            BFrag<TM, NP> Vh[L::MJ], Vl[L::MJ];
+            int sV[L::MJ];  // Vh (+ Vl) holds Vt 2^-(sS + sY + sV)
 #pragma unroll
             for (int mj = 0; mj < L::MJ; ++mj) {
-                const int jt = wave + NSW * mj;
-                if (jt >= L::NJT) continue;
-                // Y = beta V - Bw S   (rows: tokens of the chunk; this wave's 16 columns)
+                sV[mj] = 0;
+                if (wave + NSW * mj >= L::NJT) continue;
+                // Y = beta V - Bw S   (rows: tokens; this wave's 16 columns), kept as Y 2^-sS
+                const float dS = pow2f(-sS[mj]);
                 f4 Y[NP];
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
-                    f4 y;
-                    const TM *bvr = bV + (jt * 16 + (lane & 15)) * L::LCM + 16 * p + 4 * g;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) y[e] = to_f32(bvr[e]);
-                    mma_bfrag<NKT_K, PK>(y, Bw + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
-                    Y[p] = y;
+                    Y[p] = bv[mj][p] * dS;
+                    mma_frag<false>(Y[p], fb[p], Sh[mj], NKT_K);
                 }
-                BFrag<TM, NP> Yh;
-                Yh.set(Y);
+                int sY = 0;
+                if constexpr (P16) {
+                    sY = wave_scale_exp(maxabs(Y));
+                    if (sY) {
+                        const float d = pow2f(-sY);
+#pragma unroll
+                        for (int p = 0; p < NP; ++p) Y[p] *= d;
+                    }
+                }
+                BFrag<TM, NP> Yh, Yl;
+                set_split(Yh, Yl, Y);
                 // Vt = T Y (T lower triangular: row tile p needs token tiles 0..p)
+                f4 Vt[NP];
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
-                    f4 x = {0.f, 0.f, 0.f, 0.f};
-                    mma_bfrag<NP, PK>(x, Tm + (16 * p + (lane & 15)) * L::LCM, Yh, p + 1, lane);
-                    Vt[mj][p] = x;
+                    Vt[p] = f4{0.f, 0.f, 0.f, 0.f};
+                    mma_frag<false>(Vt[p], ft[p], Yh, p + 1);
+                    if constexpr (P16) mma_frag<false>(Vt[p], ft[p], Yl, p + 1);
                 }
-                Vh[mj].set(Vt[mj]);
-                // O = Qt S + A_qk Vt
+                int sv = 0;
+                if constexpr (P16) {
+                    sv = wave_scale_exp(maxabs(Vt));
+                    if (sv) {
+                        const float d = pow2f(-sv);
 #pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    f4 o = {0.f, 0.f, 0.f, 0.f};
-                    mma_bfrag<NKT_K, PK>(o, Qt + (16 * p + (lane & 15)) * L::LKM, Sh[mj], NKT_K, lane);
-                    mma_bfrag<NP, PK>(o, Aqk + (16 * p + (lane & 15)) * L::LCM, Vh[mj], p + 1, lane);
-                    store_o(p, jt, o);
+                        for (int p = 0; p < NP; ++p) Vt[p] *= d;
+                    }
                 }
+                set_split(Vh[mj], Vl[mj], Vt);
+                sV[mj] = sY + sv;
             }
-        }
-        if (cn >= 0) {  // S = gamma_C S + Kt^T Vt, still before B2
-            const unsigned char *pk = pkg(cn & 1);
-            const TM *Kt = reinterpret_cast<const TM *>(pk + L::pKt);
-            const float *eGC = reinterpret_cast<const float *>(pk + L::pGC);
+            if constexpr (LEAN) load_group2();
+            // group 3: Kt and gamma_C (the state update); in the lean order after the output
+            AFrag<TM, NP> fk[NKT_K];
+            f4 gc[NKT_K];
+            auto load_group3 = [&]() {
+#pragma unroll
+                for (int t = 0; t < NKT_K; ++t) {
+                    fk[t].template load<PK>(Kt + (16 * t + r16) * L::LCM, NP, lane);
+                    const float4 d = *reinterpret_cast<const float4 *>(eGC + 16 * t + 4 * g);
+                    gc[t] = f4{d.x, d.y, d.z, d.w};
+                }
+                sched_fence();
+            };
+            if constexpr (!LEAN) load_group3();
+            const int64_t t0 = bos + (int64_t)cn * C;
+            const int n = (int)((eos - t0) < C ? (eos - t0) : C);
+            unsigned char *ob = static_cast<unsigned char *>(a.out) + (t0 * H + h) * V * (a.out_bf16 ? 2 : 4);
 #pragma unroll
             for (int mj = 0; mj < L::MJ; ++mj) {
                 const int jt = wave + NSW * mj;
                 if (jt >= L::NJT) continue;
-                // S = gamma_C S + Kt^T Vt
+                // O^T = S^T Qt^T + Vt^T A_qk^T: lane (g, r16) holds value columns 4g..4g+3 of
+                // token r16 of the tile, one 8- or 16-byte store per tile
+                const int j0 = vb * BV + jt * 16 + 4 * g;
+                const float dV = pow2f(-sV[mj]);                       // S-scaled -> Vt-scaled
+                const float uO = a.scale * pow2f(sS[mj] + sV[mj]);     // Vt-scaled -> output
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    f4 o = {0.f, 0.f, 0.f, 0.f};
+                    mma_frag<true>(o, fq[p], Sh[mj], NKT_K);
+                    o *= dV;
+                    mma_frag<true>(o, fa[p], Vh[mj], p + 1);
+                    if constexpr (P16) {
+                        mma_frag<true>(o, fa[p], Vl[mj], p + 1);
+                        mma_frag<true>(o, fl[p], Vh[mj], p + 1);
+                    }
+                    o *= uO;
+                    const int i = 16 * p + r16;
+                    const uint32_t off = (uint32_t)(i * H * V + j0);
+                    if (i < n) {
+                        if (a.out_bf16) {
+                            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+                            *reinterpret_cast<bf16x4 *>(ob + 2u * off) =
+                                bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                        } else {
+                            *reinterpret_cast<float4 *>(ob + 4u * off) = float4{o[0], o[1], o[2], o[3]};
+                        }
+                    }
+                }
+                if (LEAN && mj == 0) load_group3();
+                // S = gamma_C S + Kt^T Vt, accumulated as S 2^-w with w the scale of Vh
+                const int w = sS[mj] + sV[mj];
+                const float dW = pow2f(-w), uW = pow2f(w);
 #pragma unroll
                 for (int t = 0; t < NKT_K; ++t) {
                     f4 x = S[mj][t];
-                    const float4 d = *reinterpret_cast<const float4 *>(eGC + 16 * t + 4 * g);
-                    x[0] *= d.x; x[1] *= d.y; x[2] *= d.z; x[3] *= d.w;
-                    mma_bfrag<NP, PK>(x, Kt + (16 * t + (lane & 15)) * L::LCM, Vh[mj], NP, lane);
-                    S[mj][t] = x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] *= gc[t][e] * dW;
+                    mma_frag<false>(x, fk[t], Vh[mj], NP);
+                    if constexpr (P16) mma_frag<false>(x, fk[t], Vl[mj], NP);
+                    S[mj][t] = x * uW;
                 }
-                Sh[mj].set(S[mj]);
+                set_state_frag<P16>(Sh[mj], sS[mj], S[mj]);
             }
         }
         // B2 (with the package built in the workgroup: chunk it is staged and its package
@@ -741,11 +1001,13 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
     for (int buf = 0; buf < 2; ++buf) {
         TM *Tm = reinterpret_cast<TM *>(pkg(buf) + L::pTm);
         TM *Aq = reinterpret_cast<TM *>(pkg(buf) + L::pAqk);
+        TM *Al = reinterpret_cast<TM *>(pkg(buf) + L::pAql);
         for (int e = tp; e < C * C; e += NPT) {
             const int i = e / C, j = e % C;
             if ((j >> 4) > (i >> 4)) {
                 Tm[i * L::LCM + j] = from_f32<TM>(0.f);
                 Aq[i * L::LCM + j] = from_f32<TM>(0.f);
+                if constexpr (P::kAqParts == 2) Al[i * L::LCM + j] = from_f32<TM>(0.f);
             }
         }
     }
@@ -1037,8 +1299,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
             for (int w = 0; w < NVE; ++w) {
                 const int e = tp + NPT * w;
                 if (e < BV * C / 2) {
-                    const int r = 2 * (e / BV);
-                    bvv[w] = float2{raw_f32(rv[w][0]) * Btv[r], raw_f32(rv[w][1]) * Btv[r + 1]};
+                    bvv[w] = float2{raw_f32(rv[w][0]), raw_f32(rv[w][1])};  // raw values (exact)
                 }
             }
         }
@@ -1050,7 +1311,8 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
             TM *Qt = reinterpret_cast<TM *>(pk + L::pQt);
             TM *Bw = reinterpret_cast<TM *>(pk + L::pBw);
             TM *Kt = reinterpret_cast<TM *>(pk + L::pKt);
-            TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
+            TIn *vL = reinterpret_cast<TIn *>(pk + L::pbV);
+            if (tp < C) reinterpret_cast<float *>(pk + L::pBt)[tp] = Btv[tp];
 #pragma unroll
             for (int u = 0; u < CPT; ++u) {
                 const int cm = combo_of(u);
@@ -1091,7 +1353,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs a) {
                 const int e = tp + NPT * w;
                 if (e < BV * C / 2) {
                     const int j = e % BV, r = 2 * (e / BV);
-                    st2<TM>(bV + j * L::LCM + r, bvv[w].x, bvv[w].y);
+                    st2<TIn>(vL + j * L::LCM + r, bvv[w].x, bvv[w].y);
                 }
             }
         }

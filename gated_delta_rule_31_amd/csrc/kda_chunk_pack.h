@@ -33,8 +33,9 @@ constexpr int NCW = 4;          // copy waves of the chain kernel
 constexpr int NTC = 64 * (NSW + NCW);
 
 // One package in the workspace, dense, byte offsets: Qt and -Bw [C][K], Kt [K][C] (token
-// index contiguous, the LDS operand order), T and A_qk [C][C] (upper blocks zero), all in
-// the matrix-operand type; gamma_C [K] and beta [C] (0 on padding rows) in float32.
+// index contiguous, the LDS operand order), T and A_qk [C][C] (upper blocks zero; A_qk as
+// hi and lo parts on the 16-bit path), all in the matrix-operand type; gamma_C [K] and
+// beta [C] (0 on padding rows) in float32.
 template <class P, int K, int C>
 struct PackLayout {
     using TM = typename P::TM;
@@ -43,7 +44,7 @@ struct PackLayout {
     static constexpr size_t gKt = gBw + (size_t)C * K * sizeof(TM);
     static constexpr size_t gTm = gKt + (size_t)K * C * sizeof(TM);
     static constexpr size_t gAqk = gTm + (size_t)C * C * sizeof(TM);
-    static constexpr size_t gGC = gAqk + (size_t)C * C * sizeof(TM);
+    static constexpr size_t gGC = gAqk + (size_t)P::kAqParts * C * C * sizeof(TM);
     static constexpr size_t gBt = gGC + (size_t)K * 4;
     static constexpr size_t bytes = gBt + (size_t)C * 4;
     static_assert(bytes % 16 == 0, "packages stay 16-byte aligned");
@@ -122,6 +123,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
     using PXL = PrepassLds<P, K, C>;
     TM *TmL = reinterpret_cast<TM *>(smem + PXL::oTA);
     TM *AqL = reinterpret_cast<TM *>(smem + PXL::oTA + (L::pAqk - L::pTm));
+    TM *AlL = reinterpret_cast<TM *>(smem + PXL::oTA + (L::pAql - L::pTm));
 
     // the strictly upper 16x16 blocks of T and A_qk are zero in every item (nothing else
     // writes them); the first barrier below orders this before any read
@@ -130,6 +132,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         if ((j >> 4) > (i >> 4)) {
             TmL[i * L::LCM + j] = from_f32<TM>(0.f);
             AqL[i * L::LCM + j] = from_f32<TM>(0.f);
+            if constexpr (P::kAqParts == 2) AlL[i * L::LCM + j] = from_f32<TM>(0.f);
         }
     }
 
@@ -491,8 +494,8 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         // (the next item's phase 1 touches neither these nor the staging area, and its
         // first barrier comes before anything here is written again)
         constexpr int RC = C * (int)sizeof(TM) / 16;  // 16-byte pieces per row
-        for (int e = tid; e < (K + 2 * C) * RC; e += PPT) {
-            const int row = e / RC, pc = e - row * RC;  // rows: Kt's K, then T's C, then A_qk's C
+        for (int e = tid; e < (K + (1 + P::kAqParts) * C) * RC; e += PPT) {
+            const int row = e / RC, pc = e - row * RC;  // rows: Kt's K, then T's C, then A_qk's C (twice)
             const TM *src;
             size_t dst;
             if (row < K) {
@@ -501,9 +504,12 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
             } else if (row < K + C) {
                 src = TmL + (row - K) * L::LCM;
                 dst = PL::gTm + (size_t)(row - K) * C * sizeof(TM);
-            } else {
+            } else if (row < K + 2 * C) {
                 src = AqL + (row - K - C) * L::LCM;
                 dst = PL::gAqk + (size_t)(row - K - C) * C * sizeof(TM);
+            } else {
+                src = AlL + (row - K - 2 * C) * L::LCM;
+                dst = PL::gAqk + (size_t)(row - K - C) * C * sizeof(TM);  // the lo part follows
             }
             const uint4 x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(src) + 16 * pc);
             *reinterpret_cast<uint4 *>(gp + dst + 16 * pc) = x;
@@ -520,7 +526,9 @@ __global__ __launch_bounds__(PPT) void chunk_pack_kernel(ChunkArgs a) {
 
 // The chain kernel: state waves as in chunk_fwd_kernel, copy waves for the packages.
 // Workgroup bid of G (G a multiple of 8: a head's value blocks share one XCD).
-template <class P, int K, int V, int C, int BV>
+// FEW_REGS: the state waves keep fewer operand fragments live (the chain beside the pre-pass
+// in one launch, at four waves per SIMD).
+template <class P, int K, int V, int C, int BV, bool FEW_REGS = false>
 __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
     using L = Layout<P, K, V, C, BV>;
     using PL = PackLayout<P, K, C>;
@@ -563,7 +571,7 @@ __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
     // issues first, then the copy waves that feed it.
     if (wave < NSW) {
         __builtin_amdgcn_s_setprio(3);
-        state_waves<P, K, V, C, BV, false, true>(a, smem, smem, s, h, vb, bos, eos, nchunks, wave, lane);
+        state_waves<P, K, V, C, BV, false, true, FEW_REGS>(a, smem, smem, s, h, vb, bos, eos, nchunks, wave, lane);
         return;
     }
     __builtin_amdgcn_s_setprio(2);
@@ -571,12 +579,14 @@ __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
     // ====================================== copy waves =======================================
     constexpr int NCT = 64 * NCW;
     const int tp = tid - NSW * 64;
-    // 16-byte pieces of a package in workspace order (Qt, Bw, Kt, T, A_qk, gamma_C), each
-    // with its LDS destination; beta is read separately.
+    // 16-byte pieces of a package in workspace order (Qt, Bw, Kt, T, A_qk, then gamma_C and
+    // beta, adjacent in both places), each with its LDS destination
     constexpr int RQ = K * (int)sizeof(TM) / 16, RC = C * (int)sizeof(TM) / 16;
-    constexpr int NQ = C * RQ, NKT = K * RC, NCC = C * RC, NGC = K * 4 / 16;
-    constexpr int NPC = 2 * NQ + NKT + 2 * NCC + NGC;
-    static_assert(PL::gGC + 16 * NGC == PL::gBt, "the pieces cover the package up to beta");
+    constexpr int NQ = C * RQ, NKT = K * RC, NCC = C * RC, NGC = (K + C) * 4 / 16;
+    constexpr int NAQ = P::kAqParts * NCC;  // A_qk's pieces (hi, then lo)
+    constexpr int NPC = 2 * NQ + NKT + NCC + NAQ + NGC;
+    static_assert(PL::gGC + 16 * NGC == PL::bytes, "the pieces cover the whole package");
+    static_assert(L::pBt == L::pGC + (size_t)K * 4, "gamma_C and beta adjacent in LDS");
     constexpr int CPT = (NPC + NCT - 1) / NCT;
     // The matrix operands go into LDS with the row swizzle the state waves read them with
     // (mma_bfrag): in rows whose index has bit 3 set the two 8-byte halves of each piece
@@ -605,17 +615,17 @@ __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
             const int x = e - 2 * NQ - NKT;
             row = x / RC;
             d = (uint32_t)(L::pTm + row * L::LCM * sizeof(TM) + 16 * (x % RC));
-        } else if (e < 2 * NQ + NKT + 2 * NCC) {
-            const int x = e - 2 * NQ - NKT - NCC;
-            row = x / RC;
-            d = (uint32_t)(L::pAqk + row * L::LCM * sizeof(TM) + 16 * (x % RC));
+        } else if (e < 2 * NQ + NKT + NCC + NAQ) {
+            const int x = e - 2 * NQ - NKT - NCC;  // A_qk rows 0..C-1, then its lo part's
+            row = (x / RC) % C;
+            d = (uint32_t)((x < NCC ? L::pAqk : L::pAql) + row * L::LCM * sizeof(TM) + 16 * (x % RC));
         } else {
-            d = (uint32_t)(L::pGC + 16 * (e - 2 * NQ - NKT - 2 * NCC));  // gamma_C: not a matrix
+            d = (uint32_t)(L::pGC + 16 * (e - 2 * NQ - NKT - NCC - NAQ));  // gamma_C, beta: no matrix
         }
         dst[w] = d;
         swp[w] = (row & 8) != 0;
     }
-    // beta V items: four value columns of two consecutive tokens, the token pairs on
+    // value items: four value columns of two consecutive tokens, the token pairs on
     // consecutive lanes (the transposed LDS writes then fall in distinct banks)
     using RawV = typename std::conditional<std::is_same<TIn, float>::value, float4, uint2>::type;
     constexpr int NVI = BV / 4 * (C / 2);
@@ -624,8 +634,7 @@ __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
     constexpr int DP = 1;
     uint4 buf[DP][CPT];
     RawV rv[DP][VPT][2];
-    float2 rb[DP][VPT];
-    auto load = [&](int cn, uint4 (&buf)[CPT], RawV (&rv)[VPT][2], float2 (&rb)[VPT]) {
+    auto load = [&](int cn, uint4 (&buf)[CPT], RawV (&rv)[VPT][2]) {
         const int64_t t0 = bos + (int64_t)cn * C;
         const int last = (int)((eos - t0) < C ? (eos - t0) : C) - 1;
         const unsigned char *gp = a.pack + ((size_t)(base + cn) * H + h) * PL::bytes;
@@ -640,7 +649,6 @@ __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
             const int r0 = r < last ? r : last, r1 = r + 1 < last ? r + 1 : last;
             rv[w][0] = ld_at<RawV>(vbp, (uint32_t)sizeof(TIn) * (uint32_t)(r0 * H * V + j));
             rv[w][1] = ld_at<RawV>(vbp, (uint32_t)sizeof(TIn) * (uint32_t)(r1 * H * V + j));
-            rb[w] = ld_at<float2>(gp, (uint32_t)(PL::gBt + 4 * r));
         }
     };
     auto raw4 = [](RawV x, float (&f)[4]) {
@@ -655,7 +663,7 @@ __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
     };
 #pragma unroll
     for (int d = 0; d < DP; ++d)
-        if (d < nchunks) load(d, buf[d], rv[d], rb[d]);
+        if (d < nchunks) load(d, buf[d], rv[d]);
     for (int it0 = 0; it0 <= nchunks; it0 += DP) {
 #pragma unroll
         for (int d = 0; d < DP; ++d) {  // register set d holds chunk it = it0 + d
@@ -668,7 +676,7 @@ __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
                     const uint4 x = buf[d][w];
                     *reinterpret_cast<uint4 *>(pk + dst[w]) = swp[w] ? uint4{x.z, x.w, x.x, x.y} : x;
                 }
-                TM *bV = reinterpret_cast<TM *>(pk + L::pbV);
+                TIn *vL = reinterpret_cast<TIn *>(pk + L::pbV);
 #pragma unroll
                 for (int w = 0; w < VPT; ++w) {
                     int e = tp + NCT * w;
@@ -678,10 +686,9 @@ __device__ __forceinline__ void chain_body(const ChunkArgs &a, int bid, int G) {
                     raw4(rv[d][w][0], f0);
                     raw4(rv[d][w][1], f1);
 #pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        st2<TM>(bV + (j + x) * L::LCM + r, f0[x] * rb[d][w].x, f1[x] * rb[d][w].y);
+                    for (int x = 0; x < 4; ++x) st2<TIn>(vL + (j + x) * L::LCM + r, f0[x], f1[x]);
                 }
-                if (it + DP < nchunks) load(it + DP, buf[d], rv[d], rb[d]);  // consumed DP periods on
+                if (it + DP < nchunks) load(it + DP, buf[d], rv[d]);  // consumed DP periods on
             }
             lds_barrier();  // the one barrier of the period: package it is in LDS
         }
@@ -698,10 +705,11 @@ __global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
 // workgroups come first in dispatch order, so they are placed before the pre-pass fills
 // the remaining room; nothing in one launch waits for another workgroup of it.
 template <class P, int K, int V, int C, int BV, int GM>
-__global__ __launch_bounds__(NTC) void chunk_segment_kernel(ChunkArgs ca, ChunkArgs pa, int nchain) {
+__global__ __launch_bounds__(NTC) __attribute__((amdgpu_waves_per_eu(P::kSegWaves))) void chunk_segment_kernel(
+    ChunkArgs ca, ChunkArgs pa, int nchain) {
     static_assert(NTC == PPT, "both roles run with the same workgroup size");
     if ((int)blockIdx.x < nchain)
-        chain_body<P, K, V, C, BV>(ca, (int)blockIdx.x, nchain);
+        chain_body<P, K, V, C, BV, (P::kSegWaves > 2)>(ca, (int)blockIdx.x, nchain);
     else
         pack_body<P, K, C, GM>(pa, (int)blockIdx.x - nchain, (int)gridDim.x - nchain);
 }

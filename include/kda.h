@@ -126,8 +126,11 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
  * float32 master state.
  * Preconditions: every log-decay ln(alpha) >= -5 (the K3 bound; it is what keeps
  * the chunk's rescale factors inside float range; alpha = 0 is not allowed here);
- * on the bf16 path the state, the values and the per-chunk pseudo-values stay
- * below 6.5e4 in magnitude (they pass through fp16 matrix-core operands).
+ * on the bf16 path q and k at unit scale (each row's L2 norm at most about 1, as the
+ * KDA layer normalises them: the decayed key and query operands pass through fp16
+ * matrix-core operands).  Values and states may have any finite magnitude: the state,
+ * the pseudo-values and their products go through 16-bit operands with an exact
+ * power-of-two scale chosen per chunk from their largest magnitude.
  * T == 0 (or B == 0): nothing is launched for the scan; final_state is set to
  * initial_state (copied unless the pointers are equal) or zeros.
  *   workspace, workspace_bytes
@@ -142,6 +145,8 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
  *          overlap in time.  A shape the two-kernel form does not support (workspace size
  *          0) returns KDA_ERR_UNSUPPORTED; a workspace too small or misaligned returns
  *          KDA_ERR_BAD_ARGUMENT.
+ * `out` must be 8-byte aligned for bf16 output and 16-byte aligned for float32 output
+ * (KDA_ERR_BAD_ARGUMENT otherwise): each store writes four value columns of a token.
  */
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype in_dtype,
                          const float *gate, kda_gate_kind gate_kind, const float *beta,

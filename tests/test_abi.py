@@ -43,7 +43,8 @@ def test_status_strings_and_version(lib):
 def _chunk(lib, **kw):
     vp = ctypes.c_void_p
     args = dict(q=1, k=2, v=3, in_dtype=1, gate=4, gate_kind=1, beta=5, s0=None, sf=None, cu=None,
-                num_seqs=0, B=1, T=64, H=2, K=16, V=16, C=16, scale=1.0, out=6, out_dtype=1, ws=None, ws_bytes=0)
+                num_seqs=0, B=1, T=64, H=2, K=16, V=16, C=16, scale=1.0, out=0x1000, out_dtype=1, ws=None,
+                ws_bytes=0)
     args.update(kw)
     f = lib.kda_chunk_fwd
     f.restype = ctypes.c_int
@@ -61,7 +62,9 @@ def _chunk(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(K=17), 4), (dict(V=256), 4), (dict(C=48), 4), (dict(H=0), 2), (dict(T=-1), 2),
     (dict(in_dtype=7), 3), (dict(gate_kind=5), 3), (dict(q=None), 1), (dict(out=None), 1),
-    (dict(cu=9, B=2, num_seqs=1), 5), (dict(out=3), 6), (dict(sf=4), 6), (dict(sf=6), 6),
+    (dict(cu=9, B=2, num_seqs=1), 5), (dict(out=3), 6), (dict(sf=4), 6), (dict(sf=0x1000), 6),
+    # the output must be 8-byte aligned (bf16) or 16-byte aligned (float32)
+    (dict(out=0x1004), 5), (dict(out=0x1008, out_dtype=0), 5),
 ])
 def test_chunk_validation(lib, kw, status):
     assert _chunk(lib, **kw) == status
@@ -76,10 +79,10 @@ def _ws_size(lib, in_dtype=1, B=1, T=64, num_seqs=0, varlen=0, H=2, K=16, V=16, 
 
 
 def test_chunk_workspace_size(lib):
-    # bf16 path, K = V = 128, C = 32: (3 C K + 2 C^2) fp16 operands + (K + C) floats per
-    # (chunk, head), T = 8192 being 256 chunks per head; then one float32 K x V state per
-    # (sequence, head)
-    per = 2 * (3 * 32 * 128 + 2 * 32 * 32) + 4 * (128 + 32)
+    # bf16 path, K = V = 128, C = 32: (3 C K + 3 C^2) fp16 operands (Qt, Bw, Kt; T, A_qk
+    # hi and lo) + (K + C) floats per (chunk, head), T = 8192 being 256 chunks per head;
+    # then one float32 K x V state per (sequence, head)
+    per = 2 * (3 * 32 * 128 + 3 * 32 * 32) + 4 * (128 + 32)
     st = 4 * 128 * 128
     assert _ws_size(lib, T=8192, H=96, K=128, V=128, C=32) == 256 * 96 * per + 96 * st
     # a ragged length rounds up; packed sequences get T / C + N slots
@@ -94,7 +97,7 @@ def test_chunk_workspace_size(lib):
     (dict(ws=64, ws_bytes=16), 5),                  # too small
     (dict(ws=72, ws_bytes=1 << 20), 5),             # not 16-byte aligned
     (dict(q=64, ws=64, ws_bytes=1 << 20), 6),       # the workspace is q
-    (dict(out=96, ws=96, ws_bytes=1 << 20), 6),     # the workspace is out
+    (dict(out=0x2000, ws=0x2000, ws_bytes=1 << 20), 6),  # the workspace is out
     (dict(ws=64, ws_bytes=1 << 20, K=24), 4),       # unsupported width
 ])
 def test_chunk_workspace_validation(lib, kw, status):
@@ -144,7 +147,7 @@ def test_fused_gate_validation(lib):
     f.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, vp, vp, i32, i32, ctypes.c_int64, i32, i32, i32,
                   i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
 
-    def chunk(z=4, ls=8, bias=None, lb=-5.0, out=6, K=16, flags=0, ws=None, nws=0):
+    def chunk(z=4, ls=8, bias=None, lb=-5.0, out=0x1000, K=16, flags=0, ws=None, nws=0):
         return f(1, 2, 3, 1, z, ls, bias, lb, flags, 5, None, None, None, 0, 1, 64, 2, K, 16, 16, 1.0, out, 1,
                  ws, nws, None)
     assert chunk(lb=0.0) == 5        # lower bound must be negative

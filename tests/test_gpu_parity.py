@@ -92,10 +92,22 @@ def test_tiny_fp32_explicit_zero_state_equals_none():
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
-def test_mixed_widths_with_resume():
+def _form_supports(dtype, K, V, C, B=1, T=64, H=1):
+    """Whether the chunk form under test (kda.TWO_PASS) supports this shape."""
+    if kda.TWO_PASS:
+        return kda.chunk_fwd_workspace_size(dtype, B, T, H, K, V, C) > 0
+    return kda.chunk_fwd_supported(dtype, K, V, C) > 0
+
+
+@pytest.mark.parametrize("C", [64, 32])
+def test_mixed_widths_with_resume(C):
+    """The mixed-widths workload (B2 T1024 H8 K64 V128, bf16, initial state) at its stated
+    chunk size 64, and at 32; one call and a resume split at an unaligned token."""
     inp = synth.mixed_resume()
-    _case("mixed widths B2 T1024 H8 K64 V128 bf16, one call")
-    o, f = gpu_prefill(inp)
+    if not _form_supports(torch.bfloat16, 64, 128, C, 2, 1024, 8):
+        pytest.skip("this form has no chunk size %d at K=64, V=128" % C)
+    _case("mixed widths B2 T1024 H8 K64 V128 bf16 C=%d, one call" % C)
+    o, f = gpu_prefill(inp, chunk_size=C)
     eo, ef = oracle_prefill(inp)
     assert_close(o, eo, False, "out")
     assert_close(f, ef, False, "final state")
@@ -106,9 +118,10 @@ def test_mixed_widths_with_resume():
     g = kda.bounded_decay(d(inp.z), d(inp.log_scale), out_log=True)
     o1, f1 = kda.chunk_fwd(d(inp.q[:, :t1]), d(inp.k[:, :t1]), d(inp.v[:, :t1]), g[:, :t1].contiguous(),
                            d(inp.beta[:, :t1]), initial_state=d(inp.initial_state), gate_is_log=True,
-                           out_dtype=torch.float32)
+                           chunk_size=C, out_dtype=torch.float32)
     o2, f2 = kda.chunk_fwd(d(inp.q[:, t1:]), d(inp.k[:, t1:]), d(inp.v[:, t1:]), g[:, t1:].contiguous(),
-                           d(inp.beta[:, t1:]), initial_state=f1, gate_is_log=True, out_dtype=torch.float32)
+                           d(inp.beta[:, t1:]), initial_state=f1, gate_is_log=True, chunk_size=C,
+                           out_dtype=torch.float32)
     assert_close(torch.cat([o1, o2], 1), eo, False, "resumed out")
     assert_close(f2, ef, False, "resumed final state")
 
@@ -124,6 +137,45 @@ def test_width_combinations(K, V, dtype):
     fp32 = dtype == torch.float32
     assert_close(o, eo, fp32, "out")
     assert_close(f, ef, fp32, "final state")
+
+
+@pytest.mark.parametrize("K,V", [(16, 16), (16, 128), (32, 32), (32, 128), (64, 64), (64, 128), (128, 64),
+                                 (128, 128)])
+def test_fast_decay_chunk64(K, V):
+    """Retention near e^-5 at chunk size 64 (the in-chunk log-decay reaches about -320 and
+    every 16-token rescale is at its widest), for every width pair the form under test
+    compiles at chunk size 64; bf16, with an initial state, ragged last chunk."""
+    if not _form_supports(torch.bfloat16, K, V, 64):
+        pytest.skip("no chunk size 64 at K=%d V=%d in this form" % (K, V))
+    _case("fast decay C=64 K=%d V=%d" % (K, V))
+    inp = synth.make_prefill(1, 301, 3, K, V, dtype=torch.bfloat16, seed=K + 7 * V, state_std=0.1,
+                             z_mean=3.0, alog_const=1.0, beta_mean=2.0)
+    o, f = gpu_prefill(inp, chunk_size=64)
+    eo, ef = oracle_prefill(inp)
+    assert_close(o, eo, False, "out")
+    assert_close(f, ef, False, "final state")
+
+
+@pytest.mark.parametrize("K,V,C", [(128, 128, 32), (64, 64, 64), (64, 128, 32)])
+@pytest.mark.parametrize("regime", ["slow", "k3"])
+def test_bf16_large_values_and_state(K, V, C, regime):
+    """Values and an initial state near 1e5 on the bf16 path, beyond the fp16
+    range of the 16-bit matrix-core operands (finite inputs of any magnitude are in the
+    contract): the state, the pseudo-values and their products are scaled by exact powers
+    of two, so the 2e-2 rule holds for the output and the state, with the gate tensor and
+    with the gate inside the kernel."""
+    if not _form_supports(torch.bfloat16, K, V, C):
+        pytest.skip("shape not compiled in this form")
+    _case("large values K=%d V=%d C=%d %s" % (K, V, C, regime))
+    kw = dict(slow=dict(z_mean=-4.0, alog_const=1.0), k3=dict(qk="silu", v_kind="silu", z_std=1.5, alog_std=0.5))
+    inp = synth.make_prefill(1, 333, 2, K, V, dtype=torch.bfloat16, seed=K + V + C, state_std=0.1, **kw[regime])
+    inp.v = (inp.v.float() * 1.0e5).to(torch.bfloat16)  # values near 1e5
+    inp.initial_state = inp.initial_state * 1.0e6       # a state near 1e5
+    eo, ef = oracle_prefill(inp)
+    for fused in (False, True):
+        o, f = (gpu_prefill_fused if fused else gpu_prefill)(inp, chunk_size=C)
+        assert_close(o, eo, False, "out (fused gate %s)" % fused)
+        assert_close(f, ef, False, "final state (fused gate %s)" % fused)
 
 
 @pytest.mark.parametrize("regime", ["slow", "fast", "alpha_one"])
@@ -146,6 +198,8 @@ def test_repeated_key_full_overwrite(dtype, K, C):
     """Every token writes the same key with beta = 1 and no decay.  The strictly lower part
     of each chunk's key-key matrix is then all ones: the in-chunk inverse sees its largest
     intermediate terms."""
+    if not _form_supports(dtype, K, 64, C):
+        pytest.skip("shape not compiled in this form")
     _case("repeated key K=%d C=%d %s" % (K, C, dtype))
     inp = synth.make_prefill(1, 150, 2, K, 64, dtype=dtype, seed=57, z_mean=-200.0, state_std=0.1)
     inp.k = inp.k[:, :1].expand_as(inp.k).contiguous()
@@ -340,6 +394,8 @@ def _oracle_prefill_bias(inp, bias):
 @pytest.mark.parametrize("dtype,K,V,C", [(torch.float32, 16, 16, 16), (torch.float32, 64, 32, 32),
                                          (torch.bfloat16, 128, 128, 32), (torch.bfloat16, 32, 64, 64)])
 def test_fused_gate_prefill_matches_oracle(dtype, K, V, C):
+    if not _form_supports(dtype, K, V, C):
+        pytest.skip("shape not compiled in this form")
     _case("fused gate prefill %s K=%d V=%d C=%d" % (dtype, K, V, C))
     inp = synth.make_prefill(2, 77, 3, K, V, dtype=dtype, seed=7 * K + V, alog_std=0.5, state_std=0.1)
     o, f = gpu_prefill_fused(inp, chunk_size=C)
@@ -461,6 +517,42 @@ def test_recurrent_fwd_any_alpha():
     assert_close(f, es, True, "state (alpha = 0 at one token)")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_recurrent_kda_gate_endpoints(dtype):
+    """PaperLeet recurrent_kda accepts the gate's endpoints: alpha = 0 at one token (outside
+    the chunked prefill's bound, where its rescale factors would be infinite) and alpha = 1
+    elsewhere goes to the token-recurrent kernel; a bounded gate goes to the chunked
+    prefill; autograd with an unbounded gate is refused.  Float32 inputs are compared with
+    the oracle at 1e-4; bf16 inputs return bf16, bit for bit the routed kernel's output."""
+    _case("recurrent_kda with alpha = 0 at one token, %s" % dtype)
+    inp = synth.make_prefill(1, 90, 2, 64, 64, dtype=dtype, seed=29, state_std=0.1)
+    alpha = torch.ones(1, 90, 2, 64)
+    alpha[:, 41] = 0.0
+    d = lambda x: x.cuda()
+    q, k, v, be, s0 = d(inp.q), d(inp.k), d(inp.v), d(inp.beta), d(inp.initial_state)
+    assert not kda.gate_within_chunk_bound(d(alpha))
+    o, f = kda.recurrent_kda(q, k, v, d(alpha), be, s0)
+    assert o.dtype == dtype
+    ro, rf = kda.recurrent_fwd(q, k, v, d(alpha), be, initial_state=s0)
+    assert torch.equal(o, ro) and torch.equal(f, rf)
+    if dtype == torch.float32:
+        eo, ef = oracle.scan(f64(inp.q), f64(inp.k), f64(inp.v), f64(alpha), f64(inp.beta), f64(inp.initial_state))
+        assert_close(o, eo, True, "out (alpha 0 and 1)")
+        assert_close(f, ef, True, "state (alpha 0 and 1)")
+    # bounded retention: the chunked prefill, same contract
+    al = kda.bounded_decay(d(inp.z), d(inp.log_scale))
+    assert kda.gate_within_chunk_bound(al)
+    o, f = kda.recurrent_kda(q, k, v, al, be, s0)
+    co, cf = kda.chunk_fwd(q, k, v, al, be, initial_state=s0)
+    assert o.dtype == dtype and torch.equal(o, co) and torch.equal(f, cf)
+    if dtype == torch.float32:
+        eo, ef = oracle_prefill(inp)
+        assert_close(o, eo, True, "out (bounded gate)")
+        assert_close(f, ef, True, "state (bounded gate)")
+    with pytest.raises(ValueError, match="e\\^-5"):
+        kda.recurrent_kda(q.float().requires_grad_(), k.float(), v.float(), d(alpha), be, None)
+
+
 def test_recurrent_fwd_equals_chunk_fp32_and_in_place():
     _case("recurrent fwd == chunk fwd (fp32), in-place state")
     inp = synth.make_prefill(2, 70, 3, 64, 64, dtype=torch.float32, seed=25, alog_std=0.5, state_std=0.1)
@@ -530,6 +622,8 @@ def _oracle_prepared(r, qk_norm=True, beta_sig=True):
 @pytest.mark.parametrize("dtype,K,V,C", [(torch.float32, 64, 32, 32), (torch.bfloat16, 128, 128, 32),
                                          (torch.bfloat16, 32, 64, 64)])
 def test_prepared_in_kernel_chunk(dtype, K, V, C):
+    if not _form_supports(dtype, K, V, C):
+        pytest.skip("shape not compiled in this form")
     _case("in-kernel preparation, chunk %s K=%d V=%d C=%d" % (dtype, K, V, C))
     r = _raw_inputs(2, 70, 3, K, V, dtype, seed=K + V)
     d = lambda x: None if x is None else x.cuda()
@@ -600,73 +694,81 @@ def test_prepared_in_kernel_step(state_vk, K, V):
 
 # ---- full-size workloads, sampled ------------------------------------------------------
 
-def test_k3_prefill_full_size_sampled_heads():
-    """Kimi K3 layer prefill at its full size (T=8192, H=96, K=V=128, bf16), in the
-    launch configuration the benchmark times; the oracle checks three heads."""
-    _case("k3 prefill full size, sampled heads")
+_K3_ORACLE = {}
+
+
+def _k3_oracle(inp):
+    """The oracle over every head of the K3 prefill workload (computed once per session)."""
+    if "r" not in _K3_ORACLE:
+        _K3_ORACLE["r"] = oracle_prefill(inp)
+    return _K3_ORACLE["r"]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_k3_prefill_full_size_all_heads(fused):
+    """Kimi K3 layer prefill at its full size (T=8192, H=96, K=V=128, bf16) in the launch
+    configuration the benchmark times, through the gate tensor and with the gate inside the
+    kernel; the oracle checks all 96 heads, output and final state."""
+    _case("k3 prefill full size, all heads, fused gate %s" % fused)
     inp = synth.k3_prefill(device="cuda")
-    o, f = gpu_prefill(inp, chunk_size=32)
-    ob, fb = gpu_prefill(inp, chunk_size=32, out_dtype=torch.bfloat16)
+    run = gpu_prefill_fused if fused else gpu_prefill
+    o, f = run(inp, chunk_size=32)
+    ob, fb = run(inp, chunk_size=32, out_dtype=torch.bfloat16)
     assert torch.equal(ob, o.to(torch.bfloat16)) and torch.equal(fb, f)
-    heads = [0, 47, 95]
-    eo, ef = oracle_prefill(inp, heads=heads)
-    assert_close(o[:, :, heads], eo, False, "out (heads %s)" % heads)
-    assert_close(f[:, heads], ef, False, "final state (heads %s)" % heads)
-    assert torch.isfinite(o).all() and torch.isfinite(f).all()
+    eo, ef = _k3_oracle(inp)
+    for h0 in range(0, 96, 24):  # per block of heads (each block's own RMS)
+        hs = slice(h0, h0 + 24)
+        assert_close(o[:, :, hs], eo[:, :, hs], False, "out (heads %d..%d)" % (h0, h0 + 23))
+        assert_close(f[:, hs], ef[:, hs], False, "final state (heads %d..%d)" % (h0, h0 + 23))
+    assert_close(o, eo, False, "out (all heads)")
+    assert_close(f, ef, False, "final state (all heads)")
 
 
-def test_k3_prefill_fused_gate_full_size_sampled_heads():
-    """The same layer through the fused-gate entry point, as the benchmark times it."""
-    _case("k3 prefill fused gate full size, sampled heads")
-    inp = synth.k3_prefill(device="cuda")
-    o, f = gpu_prefill_fused(inp, chunk_size=32)
-    ob, fb = gpu_prefill_fused(inp, chunk_size=32, out_dtype=torch.bfloat16)
-    assert torch.equal(ob, o.to(torch.bfloat16)) and torch.equal(fb, f)
-    heads = [1, 50, 94]
-    eo, ef = oracle_prefill(inp, heads=heads)
-    assert_close(o[:, :, heads], eo, False, "out (heads %s)" % heads)
-    assert_close(f[:, heads], ef, False, "final state (heads %s)" % heads)
-    assert torch.isfinite(o).all() and torch.isfinite(f).all()
-
-
-def test_decode_full_size_sampled_pairs():
-    """Decode at B=64, H=96, K=V=128 (the full kept state), 4 steps; the oracle checks
-    a sample of (b, h) pairs; the rest must stay finite."""
-    _case("decode full size, sampled")
-    steps = 4
+def test_decode_full_size_all_steps_fused_gate():
+    """Decode at B=64, H=96, K=V=128 over all 256 steps of the workload through the step
+    kernel with the gate inside it (the benchmark's decode call), state updated in place:
+    64 sampled (b, h) pairs are compared with the oracle at every step and in the final
+    state; the whole state stays finite."""
+    _case("decode full size, 256 steps, fused gate, 64 sampled pairs")
+    steps = 256
     dec = synth.decode(device="cuda", steps=steps)
     state = dec.state.clone()
+    g = torch.Generator().manual_seed(404)
+    sel = torch.randperm(64 * 96, generator=g)[:64]
+    bs, hs = (sel // 96).tolist(), (sel % 96).tolist()
+    bi, hi = torch.tensor(bs, device="cuda"), torch.tensor(hs, device="cuda")
     outs = []
     for t in range(steps):
-        al = kda.bounded_decay(dec.z[t], dec.log_scale)
-        outs.append(kda.recurrent_step(dec.q[t], dec.k[t], dec.v[t], al, dec.beta[t], state,
-                                       out_dtype=torch.float32))
-    bs, hs = [0, 31, 63], [0, 50, 95]
-    sub = synth.DecodeInputs(name="sub", state=dec.state[bs][:, hs].cpu(), q=dec.q[:, bs][:, :, hs].cpu(),
-                             k=dec.k[:, bs][:, :, hs].cpu(), v=dec.v[:, bs][:, :, hs].cpu(),
-                             z=dec.z[:, bs][:, :, hs].cpu(), log_scale=dec.log_scale[hs].cpu(),
-                             beta=dec.beta[:, bs][:, :, hs].cpu())
-    eo, es = _oracle_steps(sub, sub.state, steps)
+        o = kda.recurrent_step_fused_gate(dec.q[t], dec.k[t], dec.v[t], dec.z[t], dec.log_scale, dec.beta[t], state,
+                                          out_dtype=torch.float32)
+        outs.append(o[bi, hi].cpu())
+    got = torch.stack(outs, 1)  # [64 pairs, steps, V]
+    # the oracle: each pair's 256 tokens as one sequence from its kept state
+    pick = lambda x: f64(x[:, bi, hi].transpose(0, 1))[:, :, None]  # [pairs, steps, 1, D]
+    assert not dec.log_scale.any()  # A = 0 for every head in this workload
+    al = oracle.bounded_decay(pick(dec.z), f64(dec.log_scale[:1]))
+    eo, es = oracle.scan(pick(dec.q), pick(dec.k), pick(dec.v), al, f64(dec.beta[:, bi, hi].transpose(0, 1))[:, :, None],
+                         f64(dec.state[bi, hi])[:, None])
     for t in range(steps):
-        assert_close(outs[t][bs][:, hs], eo[t], False, "step %d out" % t)
-    assert_close(state[bs][:, hs], es, False, "state")
+        assert_close(got[:, t], eo[:, t, 0], False, "step %d out" % t)
+    assert_close(state[bi, hi], es[:, 0], False, "final state (sampled pairs)")
     assert torch.isfinite(state).all()
 
 
 def test_varlen_stress_full_size_sampled():
     """8 packed sequences (~121k tokens) at H=96, K=V=128 with retention near e^-5
-    (the largest in-tile rescales); the oracle checks one head of every sequence."""
-    _case("varlen stress full size, sampled")
+    (the largest in-tile rescales); the oracle checks 8 heads of every sequence."""
+    _case("varlen stress full size, 8 heads per sequence")
     inp = synth.varlen_stress(device="cuda")
     o, f = gpu_prefill(inp, chunk_size=32)
     assert torch.isfinite(o).all() and torch.isfinite(f).all()
     cu = inp.cu_seqlens.tolist()
     for s in range(len(cu) - 1):
-        h = (s * 13) % 96
-        outs, fins, rows = oracle_prefill(inp, heads=[h], seqs=[s])
+        hs = [(s * 13 + 12 * j) % 96 for j in range(8)]
+        outs, fins, rows = oracle_prefill(inp, heads=hs, seqs=[s])
         a0, a1 = rows[0]
-        assert_close(o[:, a0:a1, [h]], outs[0], False, "seq %d head %d out" % (s, h))
-        assert_close(f[s, [h]], fins[0][0], False, "seq %d head %d state" % (s, h))
+        assert_close(o[:, a0:a1, hs], outs[0], False, "seq %d heads %s out" % (s, hs))
+        assert_close(f[s, hs], fins[0][0], False, "seq %d heads %s state" % (s, hs))
 
 
 # ---- the two forms of the chunk prefill ----------------------------------------------
