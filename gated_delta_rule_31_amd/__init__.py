@@ -96,6 +96,11 @@ def _load():
     lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
     lib.kda_chunk_fwd_workspace_size.restype = sz
     lib.kda_chunk_fwd_fused_gate.restype = i32
+    lib.kda_chunk_fwd_fused_gate_noalloc.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, vp, vp, i32, i32,
+                                                     i64, i32, i32, i32, i32, f32, vp, i32, vp]
+    lib.kda_chunk_fwd_fused_gate_noalloc.restype = i32
+    lib.kda_noalloc_scratch_bytes.argtypes = []
+    lib.kda_noalloc_scratch_bytes.restype = sz
     lib.kda_recurrent_step_fused_gate.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, u32, vp, vp, i32, i32, i32,
                                                   i32, f32, vp, i32, vp]
     lib.kda_recurrent_step_fused_gate.restype = i32
@@ -345,6 +350,40 @@ def chunk_fwd_fused_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logi
                                               T, H, K, V, int(chunk_size), float(scale), _ptr(out),
                                               _dtype_code(od), _ptr(ws), nws, _stream(q))
     _check("kda_chunk_fwd_fused_gate", st)
+    return out, final_state
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the library's fixed per-device workspace used by the ``*_noalloc`` call."""
+    return int(_load().kda_noalloc_scratch_bytes())
+
+
+def chunk_fwd_fused_gate_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: torch.Tensor,
+                                 log_scale: torch.Tensor, beta: torch.Tensor, out: torch.Tensor,
+                                 bias: Optional[torch.Tensor] = None, lower_bound: float = -5.0,
+                                 initial_state: Optional[torch.Tensor] = None,
+                                 final_state: Optional[torch.Tensor] = None,
+                                 cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 32,
+                                 scale: float = 1.0, qk_l2norm: bool = False, beta_logits: bool = False,
+                                 state_vk: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd_fused_gate`` in its two-kernel form with its workspace in the library's
+    fixed per-device array (``noalloc_scratch_bytes()``): nothing is allocated, by the
+    library or here -- ``out`` (and ``final_state`` if wanted) come from the caller.  Shapes
+    whose workspace exceeds the array raise ValueError (unsupported).  Calls that overlap
+    on one GPU race on the array."""
+    q, k, v, beta, initial_state, cu_seqlens, N, od, out, final_state = _chunk_common(
+        q, k, v, beta, initial_state, False, cu_seqlens, out.dtype, out, final_state, state_vk)
+    logits, log_scale, bias = _gate_params(logits, log_scale, bias, q)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    with torch.cuda.device(q.device):
+        st = _load().kda_chunk_fwd_fused_gate_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype),
+                                                      _ptr(logits), _ptr(log_scale), _ptr(bias), float(lower_bound),
+                                                      _flags(qk_l2norm, beta_logits, state_vk), _ptr(beta),
+                                                      _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
+                                                      B, T, H, K, V, int(chunk_size), float(scale), _ptr(out),
+                                                      _dtype_code(od), _stream(q))
+    _check("kda_chunk_fwd_fused_gate_noalloc", st)
     return out, final_state
 
 

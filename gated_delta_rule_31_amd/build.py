@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_chunk_logits.hip", "kda_chunk_logits_norm.hip", "kda_chunk_chain.hip", "kda_recurrent.hip", "kda_step.hip", "kda_gate.hip", "kda_util.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_chunk_logits.hip", "kda_chunk_logits_norm.hip", "kda_chunk_chain.hip", "kda_recurrent.hip", "kda_step.hip", "kda_gate.hip", "kda_util.hip", "kda_bwd.hip", "kda_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # no packed-fp32 instructions in device code

@@ -313,6 +313,31 @@ kda_status kda_bounded_decay_bwd(const void *logits, kda_dtype logits_dtype, con
                                  const float *grad, kda_gate_kind grad_kind, void *d_logits,
                                  kda_dtype dlogits_dtype, float *d_log_scale, float *d_bias, hipStream_t stream);
 
+/*
+ * kda_chunk_fwd_fused_gate_noalloc -- kda_chunk_fwd_fused_gate in its two-kernel form with
+ * no workspace argument: the pre-pass packages and the carried state live in a fixed device
+ * array of the library (KDA_NOALLOC_SCRATCH_BYTES, 64 MiB on every GPU the library runs on,
+ * held until the process ends).  For callers that cannot allocate device memory: code under
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Nothing is
+ * allocated or freed by the call.  Arguments, layouts, results and errors are those of
+ * kda_chunk_fwd_fused_gate (same kernels); a shape whose workspace
+ * (kda_chunk_fwd_workspace_size) exceeds the array, or that has no two-kernel form, returns
+ * KDA_ERR_UNSUPPORTED -- at H = 96, K = V = 128 and chunk size 32 about 600 tokens fit.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time on the same
+ * GPU (other streams, other threads) race and must be serialised by the caller.  The
+ * array's contents are scratch: nothing in it needs clearing between calls.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+kda_status kda_chunk_fwd_fused_gate_noalloc(const void *q, const void *k, const void *v, kda_dtype in_dtype,
+                                            const void *logits, const float *log_scale, const float *bias,
+                                            float lower_bound, unsigned flags, const float *beta,
+                                            const float *initial_state, float *final_state,
+                                            const int32_t *cu_seqlens, int num_seqs, int B, int64_t T, int H,
+                                            int K, int V, int chunk_size, float scale, void *out,
+                                            kda_dtype out_dtype, hipStream_t stream);
+/* bytes of that device array (KDA_NOALLOC_SCRATCH_BYTES) */
+size_t kda_noalloc_scratch_bytes(void);
+
 /* A static, human-readable name for a status code. */
 const char *kda_status_string(kda_status s);
 
