@@ -590,15 +590,17 @@ __device__ __forceinline__ float pow2f(int e) {
     return __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
 }
 
-// largest magnitude over this lane's accumulator tiles
+// largest magnitude over this lane's accumulator tiles (a pairwise tree: short dependences)
 template <int N>
 __device__ __forceinline__ float maxabs(const f4 (&x)[N]) {
-    float m = 0.f;
+    float m[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i)
+    for (int i = 0; i < N; ++i) m[i] = fmaxf(fmaxf(fabsf(x[i][0]), fabsf(x[i][1])), fmaxf(fabsf(x[i][2]), fabsf(x[i][3])));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(x[i][e]));
-    return m;
+    for (int w = 1; w < N; w *= 2)
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w) m[i] = fmaxf(m[i], m[i + w]);
+    return m[0];
 }
 
 // The exponent s >= 0 of the power-of-two scale that brings the wave's largest magnitude

@@ -700,16 +700,23 @@ __global__ __launch_bounds__(NTC) void chunk_chain_kernel(ChunkArgs a) {
     chain_body<P, K, V, C, BV>(a, (int)blockIdx.x, (int)gridDim.x);
 }
 
+// Waves per SIMD the segment kernel is compiled for: the precision's choice for chunks of
+// up to 32 tokens, two for 64-token chunks (too many live fragments for four).
+template <class P, int C>
+constexpr int seg_waves() {
+    return C <= 32 ? P::kSegWaves : 2;
+}
+
 // One launch of a chunk segment: workgroups [0, nchain) run the chain over segment s
 // (arguments ca), the rest the pre-pass of segment s + 1 (arguments pa).  The chain's
 // workgroups come first in dispatch order, so they are placed before the pre-pass fills
 // the remaining room; nothing in one launch waits for another workgroup of it.
 template <class P, int K, int V, int C, int BV, int GM>
-__global__ __launch_bounds__(NTC) __attribute__((amdgpu_waves_per_eu(P::kSegWaves))) void chunk_segment_kernel(
+__global__ __launch_bounds__(NTC) __attribute__((amdgpu_waves_per_eu(seg_waves<P, C>()))) void chunk_segment_kernel(
     ChunkArgs ca, ChunkArgs pa, int nchain) {
     static_assert(NTC == PPT, "both roles run with the same workgroup size");
     if ((int)blockIdx.x < nchain)
-        chain_body<P, K, V, C, BV, (P::kSegWaves > 2)>(ca, (int)blockIdx.x, nchain);
+        chain_body<P, K, V, C, BV, (seg_waves<P, C>() > 2)>(ca, (int)blockIdx.x, nchain);
     else
         pack_body<P, K, C, GM>(pa, (int)blockIdx.x - nchain, (int)gridDim.x - nchain);
 }
