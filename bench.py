@@ -5,14 +5,14 @@ One step = the whole prefill path over the Kimi K3 KDA layer workload (B=1, T=81
 H=96, K=V=128, bf16 q/k/v, bf16 gate logits, fp32 beta/state): one chunk-prefill call
 with the bounded gate evaluated in its kernels (zero initial state, fp32 final state,
 bf16 output), in its two-kernel form -- a pre-pass over every (chunk, head) into a
-workspace allocated once beforehand, and the chain kernel for the serial part, the two
-overlapped over chunk segments (each launch runs the chain over one segment beside the
-pre-pass of the next).  Inputs are resident in HBM before timing starts.  Reported:
+workspace allocated once beforehand, then the chain kernel for the serial part, fed by
+direct global-to-LDS copies of the packages.  Inputs are resident in HBM before timing
+starts.  Reported:
 
 * value: prefill tokens/s over K timed steps (ms_per_step = wall time per step);
 * roofline: the call's algorithmic HBM traffic (1,284 B per token-head with the gate
   logits in bf16) and algorithmic flops (6KV + 64(3K+2V) per token-head) divided by its
-  average time (HIP events on the launch stream around the call's 9 launches), against
+  average time (HIP events on the launch stream around the call's 2 launches), against
   8 TB/s and 2.5 PFLOP/s bf16; the single-kernel form is timed beside it;
 * decode: 256 successive single-token steps over a kept [64,96,128,128] fp32 state
   (gate kernel + fused step kernel per step), with the step kernel's algorithmic
@@ -68,7 +68,7 @@ def load_traffic(kernel_file: str, workload: str):
 
 
 COPY_BYTES = 1 << 30
-TWO_PASS_SOURCES = ["kda_chunk_pack.h", "kda_chunk_kernel.h", "kda_chunk_chain.hip"]
+TWO_PASS_SOURCES = ["kda_chunk_pack.h", "kda_chunk_kernel.h", "kda_chunk_chain.hip", "kda_chunk_chain2.h"]
 
 
 def _counter_means(path, counter):
@@ -102,11 +102,10 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     # the exact instantiations the benchmark times (K = V = 128, bf16, chunk 32)
     chunk_pat = "PrecMixed, 128, 128, 32, 64, %d>" % (1 if zg else 0)
     flag = "Lb1E" if zg else "Lb0E"  # (these two appear under their mangled names)
-    # the two-kernel form per call: the pre-pass of the first chunk segment, 7 launches
-    # holding a chain segment and the next pre-pass segment, the chain of the last segment
-    two_pass = [(("chunk_pack_kernel<", "PrecMixed, 128, 32, %d>" % (1 if zg else 0)), 1),
-                (("chunk_segment_kernel<", "PrecMixed, 128, 128, 32, 64, %d>" % (1 if zg else 0)), 7),
-                (("chunk_chain_kernel<", "PrecMixed, 128, 128, 32, 64>"), 1)]
+    # the two-kernel form per call: the pre-pass over every (chunk, head) item (packages in
+    # the paired column order), then the DMA-fed chain kernel
+    two_pass = [(("chunk_pack_kernel<", "PrecMixed, 128, 32, %d, true>" % (1 if zg else 0)), 1),
+                (("chunk_chain2_kernel<128, 128, 32>",), 1)]
     entries = [("k3_prefill_chunk_fwd_" + gate, [("chunk_fwd_kernel<", chunk_pat)], "kda_chunk_kernel.h"),
                ("decode_recurrent_step_" + gate, [("recurrent_step_kernelIDF16bLi128ELi128E" + flag,)], "kda_step.hip"),
                ("short_recurrent_fwd_" + gate, [("recurrent_fwd_kernelIDF16bLi128ELi128E" + flag,)],
@@ -121,7 +120,7 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     fk = [sum(v for k, v in fetch.items() if all(p_ in k for p_ in pats)) for pats, _ in two_pass]
     wk = [sum(v for k, v in write.items() if all(p_ in k for p_ in pats)) for pats, _ in two_pass]
     if all(fk) and all(wk):
-        names = ("pack", "segment", "chain")
+        names = ("pack", "chain")
         out["k3_prefill_two_pass_" + gate] = {
             "fetch_kib_per_launch": dict(zip(names, fk)), "write_kib_per_launch": dict(zip(names, wk)),
             "launches_per_call": dict(zip(names, [n for _, n in two_pass])),
@@ -278,8 +277,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": traffic if nws > 0 else None,
-                     "kernel": "one prefill call: chunk_pack_kernel, 7 x chunk_segment_kernel (chain of a chunk "
-                     "segment beside the next pre-pass), chunk_chain_kernel" if nws > 0 else "chunk_fwd_kernel",
+                     "kernel": "one prefill call: chunk_pack_kernel (pre-pass over all chunks), then "
+                     "chunk_chain2_kernel (the serial chain)" if nws > 0 else "chunk_fwd_kernel",
                      "launch_ms": chunk_ms, "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},

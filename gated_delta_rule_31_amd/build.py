@@ -16,6 +16,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # no packed-fp32 instructions in device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
+# per-source extra flags: the DMA-fed chain kernel keeps its matrix-core accumulators in
+# ordinary vector registers (the float32 state is rescaled by vector instructions every
+# chunk; accumulation registers would need a move each way)
+EXTRA = {"kda_chunk_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -24,7 +28,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr[-4000:]))

@@ -154,6 +154,7 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, kda_dtype
     a.pack_slots = (int)slots;
     a.c_begin = 0;
     a.c_end = INT32_MAX;
+    a.pack_paired = 0;
     int bv = 0;
     hipError_t e = workspace ? kda::launch_chunk_fwd_two_pass(a, in_dtype == KDA_F32, K, V, chunk_size, (int)(N * H),
                                                               slots, stream, &bv)

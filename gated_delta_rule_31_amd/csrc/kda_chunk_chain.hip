@@ -1,5 +1,6 @@
 // kda_chunk_chain.hip -- the two-kernel form of the chunkwise prefill (kda_chunk_pack.h):
 // the chain kernels, the package size and the launch of pre-pass plus chain.
+#include "kda_chunk_chain2.h"
 #include "kda_chunk_pack.h"
 
 namespace kda {
@@ -53,10 +54,64 @@ hipError_t launch_segment_any(const ChunkArgs &ca, const ChunkArgs &pa, bool fp3
     return launch_chunk_segment(ca, pa, fp32_inputs, K, V, C, num_pairs, items, pack_wgs, stream);
 }
 
+// The 16-bit chain kernel with direct global-to-LDS copies (kda_chunk_chain2.h), where its
+// layout fits; else hipErrorNotSupported.
+template <int K, int V, int C>
+hipError_t launch_chain2_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream) {
+    using L2 = Chain2Layout<K, V, C>;
+    if constexpr (!L2::ok) {
+        return hipErrorNotSupported;
+    } else {
+        if (!a.q) return hipSuccess;  // query only
+        // the kernel's LDS is static (its four chunk buffers)
+        auto kern = chunk_chain2_kernel<K, V, C>;
+        hipLaunchKernelGGL(kern, dim3(num_pairs * (V / L2::BV)), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
+}
+
+hipError_t launch_chain2(const ChunkArgs &a, int K, int V, int C, int num_pairs, hipStream_t stream) {
+#define KDA_CHAIN2_C(KK, VV)                                                       \
+    switch (C) {                                                                   \
+        case 32: return launch_chain2_kvc<KK, VV, 32>(a, num_pairs, stream);       \
+        case 64: return launch_chain2_kvc<KK, VV, 64>(a, num_pairs, stream);       \
+        default: return hipErrorNotSupported;                                      \
+    }
+#define KDA_CHAIN2_V(KK)                        \
+    switch (V) {                                \
+        case 64: KDA_CHAIN2_C(KK, 64)           \
+        case 128: KDA_CHAIN2_C(KK, 128)         \
+        default: return hipErrorNotSupported;   \
+    }
+    switch (K) {
+        case 32: KDA_CHAIN2_V(32)
+        case 64: KDA_CHAIN2_V(64)
+        case 128: KDA_CHAIN2_V(128)
+        default: return hipErrorNotSupported;
+    }
+#undef KDA_CHAIN2_V
+#undef KDA_CHAIN2_C
+}
+
+bool chain2_supported(int K, int V, int C) {
+    ChunkArgs q{};  // q == nullptr: query
+    return launch_chain2(q, K, V, C, 0, nullptr) == hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs &a, bool fp32_inputs, int K, int V, int C, int num_pairs,
                                      int64_t slots, hipStream_t stream, int *bv) {
+    // 16-bit operands: the whole pre-pass, then the chain kernel fed by direct copies (one
+    // pass each over the full device; the same schedule with and without cu_seqlens).
+    if (!fp32_inputs && chain2_supported(K, V, C)) {
+        ChunkArgs b = a;
+        b.pack_paired = 1;
+        hipError_t e = launch_pack_any(b, fp32_inputs, K, C, slots * a.H, 0, stream);
+        if (e != hipSuccess) return e;
+        if (bv) *bv = 64;
+        return launch_chain2(b, K, V, C, num_pairs, stream);
+    }
     const int64_t NC = (a.T + C - 1) / C;  // chunks per sequence (fixed-length batches)
     // Packed sequences, or few chunks: the pre-pass over every slot, then the chain.
     constexpr int64_t SEG_MIN = 32;  // chunks per segment, at least

@@ -89,12 +89,22 @@ __device__ __forceinline__ void slot_span(int n, const int32_t *cu, int N, int64
     len = off < l ? (int)min((int64_t)C, l - off) : 0;
 }
 
+// Column k = 32m + 16h + 4g + e of a matrix stored in the paired order sits at
+// 32m + 8g + 4h + e: the eight k values one lane group takes in a 16x16x32 step over k tiles
+// 2m, 2m+1 (in the permuted order the accumulator tiles give) become one 16-byte piece.
+__device__ __forceinline__ int paired_col(int k) {
+    return (k & ~31) | (k & 3) | (((k >> 4) & 1) << 2) | (((k >> 2) & 3) << 3);
+}
+
 // GM as in chunk_fwd_kernel.  Persistent: workgroup b takes items b, b + G, ... of the
 // slots * H (chunk slot, head) items (slot-major, heads adjacent), skipping slots no
 // sequence owns, and has the raw inputs of its next item in flight while it works on the
-// current one.
-template <class P, int K, int C, int GM>
+// current one.  PERM: the matrices go out in the paired column order (the reduction index
+// of every product: Qt, Bw by key column; Kt, T, A_qk by token), for the chain kernel that
+// reads 16-byte fragments.
+template <class P, int K, int C, int GM, bool PERM = false>
 __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
+    static_assert(!PERM || (K % 32 == 0 && C % 32 == 0), "the paired order works on 32-wide blocks");
     constexpr bool ZG = GM >= 1;
     constexpr bool NORM = GM == 2;
     using L = Layout<P, K, 16, C, 16>;
@@ -432,8 +442,9 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
                                              ro.x * xf[pp].x, ro.y * xf[pp].y);
                 }
                 constexpr uint32_t E = sizeof(TM);
-                st2_at<TM>(gp, (uint32_t)PL::gQt + E * (uint32_t)(r * K + c0), lq.x * eR.x * iq[i], lq.y * eR.y * iq[i]);
-                st2_at<TM>(gp, (uint32_t)PL::gBw + E * (uint32_t)(r * K + c0), -lk.x * eR.x * ik[i], -lk.y * eR.y * ik[i]);
+                const int cq = PERM ? paired_col(c0) : c0;  // (c0 even: c0, c0 + 1 stay adjacent)
+                st2_at<TM>(gp, (uint32_t)PL::gQt + E * (uint32_t)(r * K + cq), lq.x * eR.x * iq[i], lq.y * eR.y * iq[i]);
+                st2_at<TM>(gp, (uint32_t)PL::gBw + E * (uint32_t)(r * K + cq), -lk.x * eR.x * ik[i], -lk.y * eR.y * ik[i]);
                 kro[i] = float2{ro.x * eCE.x * ik[i], ro.y * eCE.y * ik[i]};
                 ktk[u][i] = kro[i];
             }
@@ -511,7 +522,16 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
                 src = AlL + (row - K - 2 * C) * L::LCM;
                 dst = PL::gAqk + (size_t)(row - K - C) * C * sizeof(TM);  // the lo part follows
             }
-            const uint4 x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(src) + 16 * pc);
+            uint4 x;
+            if constexpr (PERM && !std::is_same<TM, float>::value) {
+                // piece pc of the paired row: tokens 32m + 4g + 0..3 and 32m + 16 + 4g + 0..3
+                const int k0 = 32 * (pc >> 2) + 4 * (pc & 3);
+                const uint2 lo = *reinterpret_cast<const uint2 *>(src + k0);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(src + k0 + 16);
+                x = uint4{lo.x, lo.y, hi.x, hi.y};
+            } else {
+                x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(src) + 16 * pc);
+            }
             *reinterpret_cast<uint4 *>(gp + dst + 16 * pc) = x;
         }
         item = nxt;
@@ -519,9 +539,9 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
     }
 }
 
-template <class P, int K, int C, int GM>
+template <class P, int K, int C, int GM, bool PERM>
 __global__ __launch_bounds__(PPT) void chunk_pack_kernel(ChunkArgs a) {
-    pack_body<P, K, C, GM>(a, (int)blockIdx.x, (int)gridDim.x);
+    pack_body<P, K, C, GM, PERM>(a, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // The chain kernel: state waves as in chunk_fwd_kernel, copy waves for the packages.
@@ -729,13 +749,13 @@ constexpr int pick_chain_bv() {
     else return 0;
 }
 
-template <class P, int GM, int K, int C>
-hipError_t launch_pack_kc(const ChunkArgs &a, int64_t items, int max_wgs, hipStream_t stream) {
+template <class P, int GM, int K, int C, bool PERM>
+hipError_t launch_pack_kcp(const ChunkArgs &a, int64_t items, int max_wgs, hipStream_t stream) {
     using X = PrepassLds<P, K, C>;
-    if constexpr (!X::fits) {
+    if constexpr (!X::fits || (PERM && (K % 32 != 0 || C % 32 != 0))) {
         return hipErrorNotSupported;
     } else {
-        auto kern = chunk_pack_kernel<P, K, C, GM>;
+        auto kern = chunk_pack_kernel<P, K, C, GM, PERM>;
         static std::atomic<bool> attr_set{false};
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -752,6 +772,16 @@ hipError_t launch_pack_kc(const ChunkArgs &a, int64_t items, int max_wgs, hipStr
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(PPT), X::total, stream, a);
         return hipGetLastError();
     }
+}
+
+// the pre-pass in the plain order, or in the paired order when a.pack_paired is set
+template <class P, int GM, int K, int C>
+hipError_t launch_pack_kc(const ChunkArgs &a, int64_t items, int max_wgs, hipStream_t stream) {
+    if (a.pack_paired) {
+        if constexpr (std::is_same<P, PrecMixed>::value) return launch_pack_kcp<P, GM, K, C, true>(a, items, max_wgs, stream);
+        return hipErrorNotSupported;
+    }
+    return launch_pack_kcp<P, GM, K, C, false>(a, items, max_wgs, stream);
 }
 
 template <class P, int GM>

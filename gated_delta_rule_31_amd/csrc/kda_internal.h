@@ -42,6 +42,7 @@ struct ChunkArgs {
     int pack_slots;                 // chunk slots per head in `pack`
     int c_begin, c_end;             // two-kernel form, without cu_seqlens: chunks [c_begin, c_end) of
                                     // every sequence (the pre-pass's items, the chain's steps)
+    int pack_paired;                // two-kernel form: packages in the paired column order
 };
 
 struct StepArgs {
