@@ -317,6 +317,31 @@ def main():
         del bl, fin_vk
     del g, out, wsp
 
+    # ---------------- the gate alone: bounded_decay over the same logits ----------------
+    # (the separate elementwise kernel of the unfused path: bf16 logits in, float32
+    # retention out, 6 B per element)
+    ga = torch.empty(B, T, H, K, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        kda.bounded_decay(z, ls, lower_bound=-5.0, out=ga)
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a_, b_ in gev:
+        a_.record(stream)
+        kda.bounded_decay(z, ls, lower_bound=-5.0, out=ga)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    g_us = sum(a_.elapsed_time(b_) for a_, b_ in gev) / len(gev) * 1e3
+    g_bytes = th * K * (2 + 4)
+    g_gbs = g_bytes / (g_us * 1e-6) / 1e9
+    log("bounded_decay: %.1f us per call, %.0f GB/s" % (g_us, g_gbs))
+    result["bounded_decay"] = {
+        "workload": "k3_prefill_B1_T8192_H96_K128 logits (bf16) -> alpha (fp32)", "calls": len(gev),
+        "launch_us_avg": g_us,
+        "roofline": {"bound": "hbm", "achieved": g_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": g_gbs / HBM_PEAK_GBS, "kernel": "bounded_decay_kernel",
+                     "algorithmic_bytes_per_launch": g_bytes}}
+    del ga
+
     # ---------------- backward ----------------------------------------------------------
     if not args.no_bwd:
         # gradients of the same K3 prefill: bf16 q, k, v and d_out, float32 retention (the

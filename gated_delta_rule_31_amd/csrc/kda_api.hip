@@ -70,7 +70,9 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
     a.K = K;
     a.lower_bound = lower_bound;
     a.out_log = out_kind == KDA_GATE_LOG;
-    a.vec8 = (K % 8 == 0) && ((uintptr_t)logits % 16 == 0) && ((uintptr_t)out % 16 == 0);
+    const size_t esz = logits_dtype == KDA_F32 ? 4 : 2;
+    a.vec4 = (K % 4 == 0) && (256 % (K / 4) == 0) && ((uintptr_t)logits % (4 * esz) == 0) &&
+             ((uintptr_t)out % 16 == 0);
     hipError_t e = kda::launch_bounded_decay(a, logits_dtype == KDA_F32, stream);
     return e == hipSuccess ? KDA_OK : hip_fail(e);
 }

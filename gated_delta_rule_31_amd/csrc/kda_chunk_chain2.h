@@ -32,12 +32,15 @@ namespace kda {
 
 namespace {
 
-// XOR swizzle of the 16-byte pieces of a row of R pieces (R = 4, 8 or 16): reads of one
-// piece index by eight consecutive rows land in distinct bank groups
+// XOR swizzle of the 16-byte pieces of a row of R pieces (R = 4, 8 or 16).  16 / R rows
+// share one 256-byte span of the LDS banks; the swizzle of row r is its span index mod R,
+// so the reads of one piece index by sixteen consecutive rows (one LDS cycle of a 16-byte
+// read) fall on sixteen distinct 16-byte bank groups.
+__device__ __forceinline__ constexpr int swz_of(int R, int r) { return (r * R / 16) & (R - 1); }
 template <int R>
 __device__ __forceinline__ int row_swz(int r) {
     static_assert(R == 4 || R == 8 || R == 16, "rows of 64, 128 or 256 bytes");
-    return R == 4 ? ((r >> 1) & 3) : (r & 7);
+    return swz_of(R, r);
 }
 
 template <int K, int V, int C>
@@ -152,6 +155,7 @@ __device__ __forceinline__ int wave_exp(float m) {
 template <int K, int V, int C>
 __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
     using L2 = Chain2Layout<K, V, C>;
+    constexpr int NB = L2::NB;
     using PL = PackLayout<PrecMixed, K, C>;
     using F = Chain2Frags<K, V, C>;
     constexpr int NP = C / 16, NKT = K / 16, BV = L2::BV, J = L2::J;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
     // distinct objects, so the compiler need not wait for the copies before every LDS read.
     __shared__ __align__(16) unsigned char lds0[L2::buf], lds1[L2::buf], lds2[L2::buf], lds3[L2::buf];
     auto bufp = [&](auto I) -> unsigned char * {
-        constexpr int i = decltype(I)::value % 4;
+        constexpr int i = decltype(I)::value % NB;
         if constexpr (i == 0) return lds0;
         else if constexpr (i == 1) return lds1;
         else if constexpr (i == 2) return lds2;
@@ -188,7 +192,11 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         eos = bos + a.T;
         base = s * (int)((a.T + C - 1) / C);
     }
-    const int nchunks = (int)((eos - bos + C - 1) / C);
+    // this launch's chunks of the sequence: [c_begin, c_end) clipped to it; the state comes
+    // from initial_state and goes to final_state at the ends of the range
+    const int nall = (int)((eos - bos + C - 1) / C);
+    const int cfirst = a.c_begin < nall ? a.c_begin : nall;
+    const int nchunks = (a.c_end < nall ? a.c_end : nall) - cfirst;
 
     // ---- the copy: piece x of a chunk buffer <- 16 source bytes ------------------------------
     // Package pieces (instructions j < JV) map to package bytes (rows of Qt, Bw, Kt, T, A_qk
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         if (b < PL::bytes) {
             auto mat = [&](size_t o0, int R) {  // a swizzled matrix region starting at o0
                 const int rel = (int)((b - o0) / 16), r = rel / R, ps = rel % R;
-                const int swz = R == 4 ? ((r >> 1) & 3) : (r & 7);
+                const int swz = swz_of(R, r);
                 return (uint32_t)(o0 + 16 * (size_t)(r * R + (ps ^ swz)));
             };
             if (b < PL::gBw) off = mat(PL::gQt, RK);
@@ -229,7 +237,8 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         const unsigned char *gp;    // the chunk's package
         const unsigned char *vsrc;  // this lane's value piece
     };
-    auto copy_src = [&](int cn) {
+    auto copy_src = [&](int ci) {  // the range's chunk ci
+        const int cn = cfirst + ci;
         const int64_t t0 = bos + (int64_t)cn * C;
         const int last = (int)((eos - t0) < C ? (eos - t0) : C) - 1;
         const unsigned char *vp = static_cast<const unsigned char *>(a.v) + ((t0 * H + h) * V + vb * BV) * 2;
@@ -250,8 +259,8 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
             __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lb + 1024 * (wv + 4 * j)), 16, 0, 0);
         }
     };
-    auto copy_chunk = [&](int cn, unsigned char *lb) {
-        const CopySrc cs = copy_src(cn);
+    auto copy_chunk = [&](int ci, unsigned char *lb) {
+        const CopySrc cs = copy_src(ci);
         copy_group(cs, lb, IC<0>{});
         copy_group(cs, lb, IC<1>{});
         copy_group(cs, lb, IC<2>{});
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         }
         issue(IC<3>{});
         read_o(nb, f);
-        const int64_t t0 = bos + (int64_t)cn * C;
+        const int64_t t0 = bos + (int64_t)(cfirst + cn) * C;
         t_pend = t0;
         n_pend = (int)((eos - t0) < C ? (eos - t0) : C);
         // S = gamma_C S + Kt^T Vt, accumulated as S 2^-w with w the scale of Vh (the rare
@@ -488,7 +497,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         asm volatile("s_barrier" ::: "memory");
     };
 
-    // ---- prologue: chunks 0..3 copied, chunk 0's fragments read -------------------------------
+    // ---- prologue: the range's first NB chunks copied, chunk 0's fragments read ----------------
     F f;
     if (nchunks > 0) copy_chunk(0, bufp(IC<0>{}));
     if (nchunks > 1) copy_chunk(1, bufp(IC<1>{}));
@@ -499,17 +508,20 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
     read_t(bufp(IC<0>{}), f);
     read_o(bufp(IC<0>{}), f);
     read_s(bufp(IC<0>{}), f);
+    // every wave's reads of buffer 0 are done before period 0 copies into it
+    wait_barrier(IC<0>{});
 
-    // Period c (chunk c in buffer c % 4): store chunk c-1's output; copy chunk c+4 into chunk
-    // c's buffer (its fragments are in registers); compute chunk c while reading chunk c+1's
-    // fragments (past the last chunk they are read and not used); then wait until chunk c+2
-    // is in LDS and every wave's LDS reads are done, and barrier.  The vector-memory counter
-    // retires in issue order, so "at most n in flight" with the copies of chunks c+3 and c+4
-    // (J each, issued after chunk c+2's) the last ones means chunk c+2 has landed.
+    // Period c (chunk c of the range in buffer c % 4): store chunk c-1's output; copy chunk
+    // c+4 into chunk c's buffer (its fragments are in registers); compute chunk c while
+    // reading chunk c+1's fragments (past the last chunk they are read and not used); then
+    // wait until chunk c+2 is in LDS and every wave's LDS reads are done, and barrier.  The
+    // vector-memory counter retires in issue order, so "at most n in flight" with the copies
+    // of chunks c+3 and c+4 (J each, issued after chunk c+2's) the last ones means chunk c+2
+    // has landed.
     auto period = [&](auto I, int c) __attribute__((always_inline)) {
         store_pending();
-        const bool cp = c + 4 < nchunks;
-        const CopySrc cs = copy_src(cp ? c + 4 : c);
+        const bool cp = c + NB < nchunks;
+        const CopySrc cs = copy_src(cp ? c + NB : c);
         compute(f, bufp(IC<decltype(I)::value + 1>{}), c, [&](auto G) {
             if (cp) copy_group(cs, bufp(I), G);
         });

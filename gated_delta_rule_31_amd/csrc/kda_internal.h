@@ -81,7 +81,7 @@ struct GateArgs {
     int H, K;
     float lower_bound;
     int out_log;
-    int vec8;                       // K % 8 == 0 and 16-byte aligned logits/out
+    int vec4;                       // K % 4 == 0, 256 % (K / 4) == 0, logits aligned to 4 elements, out to 16 bytes
 };
 
 // Intermediates of the chunkwise backward, each [slots * H, ...] float32 (slot = chunk slot)
