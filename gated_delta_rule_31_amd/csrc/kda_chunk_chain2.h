@@ -134,9 +134,11 @@ __device__ __forceinline__ float amax(const f4 (&x)[N]) {
 }
 
 // The exponent s >= 0 of the power-of-two scale that brings the wave's largest magnitude m
-// below 2^15 (0 whenever m < 2^15): a rotate-and-maximum within each row of 16 lanes, then
-// the row broadcasts of lanes 15 and 31, so lane 63 holds the wave's maximum.
+// below 2^15: 0 when no lane reaches 2^15 (one vote, the usual case); else a
+// rotate-and-maximum within each row of 16 lanes, then the row broadcasts of lanes 15 and
+// 31, so lane 63 holds the wave's maximum.
 __device__ __forceinline__ int wave_exp(float m) {
+    if (__builtin_amdgcn_ballot_w64(m >= 32768.f) == 0) return 0;
     auto step = [&](auto ctrl, auto rows) {
         const int b = __builtin_bit_cast(int, m);
         const int t = __builtin_amdgcn_update_dpp(b, b, decltype(ctrl)::value, decltype(rows)::value, 0xf, false);
