@@ -154,6 +154,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward (training) block")
     ap.add_argument("--no-short", action="store_true", help="skip the short-continuation (token-recurrent) block")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed-sequence (8 sequences) prefill block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -317,6 +318,62 @@ def main():
         del bl, fin_vk
     del g, out, wsp
 
+    # ---------------- packed sequences: 8 sequences of 1,024-32,768 tokens --------------
+    if not args.no_varlen:
+        log("generating packed-sequence inputs")
+        vl = synth.varlen_stress(device="cuda")
+        Tv = vl.q.shape[1]
+        Nv = vl.num_seqs
+        vo = torch.empty(1, Tv, H, V, dtype=torch.bfloat16, device=dev)
+        vf = torch.empty(Nv, H, K, V, dtype=torch.float32, device=dev)
+        vws_n = kda.chunk_fwd_workspace_size(vl.q.dtype, 1, Tv, H, K, V, args.chunk, num_seqs=Nv, varlen=True)
+        vws = torch.empty(max(vws_n, 1), dtype=torch.uint8, device=dev)
+
+        def vcall():
+            kda.chunk_fwd_fused_gate(vl.q, vl.k, vl.v, vl.z, vl.log_scale, vl.beta, lower_bound=-5.0,
+                                     cu_seqlens=vl.cu_seqlens, chunk_size=args.chunk, out=vo, final_state=vf,
+                                     **(dict(workspace=vws) if vws_n > 0 else dict(two_pass=False)))
+        vcall()
+        torch.cuda.synchronize()
+        vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        t0 = time.perf_counter()
+        for a_, b_ in vev:
+            a_.record(stream)
+            vcall()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        vwall = (time.perf_counter() - t0) / len(vev)
+        v_ms = sum(a_.elapsed_time(b_) for a_, b_ in vev) / len(vev)
+        vth = Tv * H
+        v_bytes = vth * (3 * 2 * K + 2 * K + 4 + 2 * V)   # the same 1,284 B per token-head as above
+        v_gbs = v_bytes / (v_ms * 1e-3) / 1e9
+        log("packed sequences (%d tokens): %.3f ms per call, %.0f GB/s" % (Tv, v_ms, v_gbs))
+        result["varlen"] = {
+            "workload": vl.name, "tokens": Tv, "sequences": Nv,
+            "lengths": [int(x) for x in (vl.cu_seqlens[1:] - vl.cu_seqlens[:-1]).tolist()],
+            "call": "chunk_fwd_fused_gate(cu_seqlens)", "tokens_per_s": Tv / (v_ms * 1e-3), "launch_ms": v_ms,
+            "ms_per_call_wall": vwall * 1e3,
+            "roofline": {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": v_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": v_bytes}}
+        if not args.no_cpu_baseline:
+            import oracle
+            from tests.helpers import f64
+            hs = list(range(0, H, 4))  # 24 of the 96 heads, every sequence
+            cu = vl.cu_seqlens.cpu().tolist()
+            sl = lambda x: f64(x[:, :, hs])
+            threads = oracle.max_threads()
+            t0 = time.perf_counter()
+            al = oracle.bounded_decay(sl(vl.z), f64(vl.log_scale)[hs], g_min=-5.0)
+            qs, ks, vs, bs = sl(vl.q), sl(vl.k), sl(vl.v), sl(vl.beta)
+            oracle.scan(qs, ks, vs, al, bs, cu_seqlens=cu)
+            vcpu = (time.perf_counter() - t0) * H / len(hs)
+            result["varlen"]["cpu_baseline"] = {
+                "value": Tv / vcpu, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": "fp64 gate + token scan of %d of the %d heads over all %d sequences, scaled by %d/%d"
+                          % (len(hs), H, Nv, H, len(hs))}
+            del al, qs, ks, vs, bs
+        del vl, vo, vf, vws
+
     # ---------------- the gate alone: bounded_decay over the same logits ----------------
     # (the separate elementwise kernel of the unfused path: bf16 logits in, float32
     # retention out, 6 B per element)
@@ -476,6 +533,23 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": v_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": d_bytes}}
             del st_vk, blog
+        if not args.no_cpu_baseline:
+            # the oracle on a sample of the (sequence, head) pairs: the same 256 steps from the
+            # same kept state, one token scan per pair
+            import oracle
+            from tests.helpers import f64
+            npairs = 192
+            threads = oracle.max_threads()
+            t0 = time.perf_counter()
+            for i in range(npairs):
+                b_i, h_i = (i * 37) % Bd, (i * 53) % Hd
+                slx = lambda x: f64(x[:, b_i:b_i + 1, h_i:h_i + 1]).swapaxes(0, 1)  # [1, steps, 1, ...]
+                al_ = oracle.bounded_decay(slx(dec.z), f64(dec.log_scale[h_i:h_i + 1]), g_min=-5.0)
+                oracle.scan(slx(dec.q), slx(dec.k), slx(dec.v), al_, slx(dec.beta), f64(dec.state[b_i:b_i + 1, h_i:h_i + 1]))
+            d_cpu = (time.perf_counter() - t0) * (Bd * Hd) / npairs
+            result["decode"]["cpu_baseline"] = {
+                "value": Bd * nd / d_cpu, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": "%d of the %d (sequence, head) pairs over all %d steps, scaled" % (npairs, Bd * Hd, nd)}
         del dec, state, src, dst
 
     # ---------------- short continuations: the token-recurrent prefill ------------------

@@ -176,13 +176,38 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r16 = lane & 15;
 
-    // which (sequence, head, value block): a head's value blocks on one XCD
+    // Which (sequence, head, value block).  Workgroups go out in blockIdx order, round-robin
+    // over the 8 XCDs: block b = 8 (NVB q + v) + x takes pair 8q + x and value block v, so
+    // a head's value blocks share an XCD (and its L2) while consecutive pairs spread over
+    // all XCDs.  With packed sequences (up to 256) the pairs are numbered longest sequence
+    // first, so the longest chains start first.
     constexpr int NVB = V / BV;
     const int G = gridDim.x;
-    int lin = blockIdx.x;
-    if ((G & 7) == 0) lin = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    const int vb = lin % NVB, pair = lin / NVB;
-    const int H = a.H, h = pair % H, s = pair / H;
+    int vb, pair;
+    if (G % (8 * NVB) == 0) {
+        const int x = blockIdx.x & 7, rest = blockIdx.x >> 3;
+        vb = rest % NVB;
+        pair = (rest / NVB) * 8 + x;
+    } else {
+        vb = blockIdx.x % NVB;
+        pair = blockIdx.x / NVB;
+    }
+    const int H = a.H, h = pair % H;
+    int s = pair / H;
+    if (a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= 256) {  // workgroup-uniform
+        __shared__ int slen[256], sorder[256];
+        const int N = a.num_seqs;
+        if (tid < N) slen[tid] = a.cu_seqlens[tid + 1] - a.cu_seqlens[tid];
+        __syncthreads();
+        if (tid < N) {
+            const int lj = slen[tid];
+            int rank = 0;  // sequences before this one: longer, or as long with a lower index
+            for (int i = 0; i < N; ++i) rank += (slen[i] > lj) || (slen[i] == lj && i < tid);
+            sorder[rank] = tid;
+        }
+        __syncthreads();
+        s = sorder[s];
+    }
     int64_t bos, eos;
     int base;  // first chunk slot of the sequence
     if (a.cu_seqlens) {
