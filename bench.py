@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward (training) block")
     ap.add_argument("--no-short", action="store_true", help="skip the short-continuation (token-recurrent) block")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed-sequence (8 sequences) prefill block")
+    ap.add_argument("--only", choices=("prefill", "varlen", "gate", "bwd", "decode", "short"),
+                    help="run one workload block alone (for per-workload kernel traces); the JSON line then "
+                         "holds that block only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -190,6 +193,9 @@ def main():
         log("copied %d bytes 4 times" % n)
         return
 
+    run = lambda name: args.only is None or args.only == name
+    run_prefill = run("prefill")
+
     # ---------------- prefill ---------------------------------------------------------
     B, T, H, K, V = 1, 8192, 96, 128, 128
     log("generating prefill inputs")
@@ -221,105 +227,110 @@ def main():
         if ev_pair is not None:
             ev_pair[1].record(stream)
 
-    log("warmup %d" % args.warmup)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    log("timing %d steps" % args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    chunk_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-    ms_per_step = wall * 1e3 / args.steps
-    tokens_per_s = B * T / (wall / args.steps)
-
     th = B * T * H
     gate_bytes = 2 * K if fused else 4 * K                  # bf16 logits, or the fp32 gate tensor
-    alg_bytes = th * (3 * 2 * K + gate_bytes + 4 + 2 * V)   # q,k,v bf16 + gate + beta + out bf16
-    alg_flops = th * (6 * K * V + 64 * (3 * K + 2 * V))
-    achieved_gbs = alg_bytes / (chunk_ms * 1e-3) / 1e9
-    achieved_tflops = alg_flops / (chunk_ms * 1e-3) / 1e12
-    traffic = load_traffic(TWO_PASS_SOURCES, "k3_prefill_two_pass_" + args.gate)
-    log("prefill: %.3f ms/step, prefill call %.3f ms, %.1f GB/s, %.1f TFLOP/s" %
-        (ms_per_step, chunk_ms, achieved_gbs, achieved_tflops))
-    # the single-kernel form of the same call, beside it (not part of the timed steps)
-    for _ in range(2):
-        step(two_pass=False)
-    oev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-    for e_ in oev:
-        step(e_, two_pass=False)
-    torch.cuda.synchronize()
-    one_ms = sum(a_.elapsed_time(b_) for a_, b_ in oev) / len(oev)
-    one_gbs = alg_bytes / (one_ms * 1e-3) / 1e9
-    log("prefill, single-kernel form: %.3f ms" % one_ms)
-
-    result = {
-        "metric": "KDA prefill tokens/s (H=96,D=128) + % MFMA peak; decode state HBM GB/s",
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "k3_prefill_B1_T8192_H96_K128_V128", "global_batch": B, "seq_len": T,
-                   "heads": H, "key_dim": K, "value_dim": V, "chunk_size": args.chunk,
-                   "step": "chunk_fwd_fused_gate" if fused else "bounded_decay + chunk_fwd",
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic if nws > 0 else None,
-                     "kernel": "one prefill call: chunk_pack_kernel (pre-pass over all chunks), then "
-                     "chunk_chain2_kernel (the serial chain)" if nws > 0 else "chunk_fwd_kernel",
-                     "launch_ms": chunk_ms, "algorithmic_bytes_per_launch": alg_bytes},
-        "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
-        "prefill_single_kernel": {"kernel": "chunk_fwd_kernel", "launch_ms": one_ms,
-                                  "tokens_per_s": B * T / (one_ms * 1e-3),
-                                  "hbm": {"achieved": one_gbs, "frac": one_gbs / HBM_PEAK_GBS,
-                                          "traffic": load_traffic("kda_chunk_kernel.h",
-                                                                  "k3_prefill_chunk_fwd_" + args.gate)}},
-    }
-    if fused:
-        # the same layer with the model's in-kernel input preparation: q/k unit norm, beta
-        # from its logits, state stored [V,K]
-        bl = torch.logit(beta)
-        fin_vk = torch.empty(B, H, V, K, dtype=torch.float32, device=dev)
-
-        def pstep():
-            kda.chunk_fwd_fused_gate(q, k, v, z, ls, bl, lower_bound=-5.0, chunk_size=args.chunk, out=out,
-                                     final_state=fin_vk, qk_l2norm=True, beta_logits=True, state_vk=True,
-                                     **(dict(workspace=wsp) if nws > 0 else dict(two_pass=False)))
-        pstep()
+    if run_prefill:
+        log("warmup %d" % args.warmup)
+        for _ in range(args.warmup):
+            step()
         torch.cuda.synchronize()
-        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for a_, b_ in pev:
-            a_.record(stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        log("timing %d steps" % args.steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        chunk_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        ms_per_step = wall * 1e3 / args.steps
+        tokens_per_s = B * T / (wall / args.steps)
+
+        alg_bytes = th * (3 * 2 * K + gate_bytes + 4 + 2 * V)   # q,k,v bf16 + gate + beta + out bf16
+        alg_flops = th * (6 * K * V + 64 * (3 * K + 2 * V))
+        achieved_gbs = alg_bytes / (chunk_ms * 1e-3) / 1e9
+        achieved_tflops = alg_flops / (chunk_ms * 1e-3) / 1e12
+        traffic = load_traffic(TWO_PASS_SOURCES, "k3_prefill_two_pass_" + args.gate)
+        log("prefill: %.3f ms/step, prefill call %.3f ms, %.1f GB/s, %.1f TFLOP/s" %
+            (ms_per_step, chunk_ms, achieved_gbs, achieved_tflops))
+        # the single-kernel form of the same call, beside it (not part of the timed steps)
+        full = args.only is None
+        for _ in range(2 if full else 0):
+            step(two_pass=False)
+        oev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10 if full else 1)]
+        for e_ in (oev if full else []):
+            step(e_, two_pass=False)
+        torch.cuda.synchronize()
+        one_ms = sum(a_.elapsed_time(b_) for a_, b_ in oev) / len(oev) if full else float("nan")
+        one_gbs = alg_bytes / (one_ms * 1e-3) / 1e9
+        log("prefill, single-kernel form: %.3f ms" % one_ms)
+
+        result = {
+            "metric": "KDA prefill tokens/s (H=96,D=128) + % MFMA peak; decode state HBM GB/s",
+            "value": tokens_per_s,
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms_per_step,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "k3_prefill_B1_T8192_H96_K128_V128", "global_batch": B, "seq_len": T,
+                       "heads": H, "key_dim": K, "value_dim": V, "chunk_size": args.chunk,
+                       "step": "chunk_fwd_fused_gate" if fused else "bounded_decay + chunk_fwd",
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved_gbs / HBM_PEAK_GBS,
+                         "traffic": traffic if nws > 0 else None,
+                         "kernel": "one prefill call: chunk_pack_kernel (pre-pass over all chunks), then "
+                         "chunk_chain2_kernel (the serial chain)" if nws > 0 else "chunk_fwd_kernel",
+                         "launch_ms": chunk_ms, "algorithmic_bytes_per_launch": alg_bytes},
+            "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
+            "prefill_single_kernel": {"kernel": "chunk_fwd_kernel", "launch_ms": one_ms,
+                                      "tokens_per_s": B * T / (one_ms * 1e-3),
+                                      "hbm": {"achieved": one_gbs, "frac": one_gbs / HBM_PEAK_GBS,
+                                              "traffic": load_traffic("kda_chunk_kernel.h",
+                                                                      "k3_prefill_chunk_fwd_" + args.gate)}},
+        }
+        if fused and full:
+            # the same layer with the model's in-kernel input preparation: q/k unit norm, beta
+            # from its logits, state stored [V,K]
+            bl = torch.logit(beta)
+            fin_vk = torch.empty(B, H, V, K, dtype=torch.float32, device=dev)
+
+            def pstep():
+                kda.chunk_fwd_fused_gate(q, k, v, z, ls, bl, lower_bound=-5.0, chunk_size=args.chunk, out=out,
+                                         final_state=fin_vk, qk_l2norm=True, beta_logits=True, state_vk=True,
+                                         **(dict(workspace=wsp) if nws > 0 else dict(two_pass=False)))
             pstep()
-            b_.record(stream)
-        torch.cuda.synchronize()
-        p_ms = sum(a_.elapsed_time(b_) for a_, b_ in pev) / len(pev)
-        p_gbs = alg_bytes / (p_ms * 1e-3) / 1e9
-        log("prefill with in-kernel preparation: %.3f ms" % p_ms)
-        result["prefill_prepared_in_kernel"] = {
-            "workload": "k3_prefill_B1_T8192_H96_K128_V128", "call": "chunk_fwd_fused_gate(qk_l2norm, beta_logits, "
-            "state_vk)", "tokens_per_s": B * T / (p_ms * 1e-3), "launch_ms": p_ms,
-            "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": p_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg_bytes}}
-        del bl, fin_vk
+            torch.cuda.synchronize()
+            pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+            for a_, b_ in pev:
+                a_.record(stream)
+                pstep()
+                b_.record(stream)
+            torch.cuda.synchronize()
+            p_ms = sum(a_.elapsed_time(b_) for a_, b_ in pev) / len(pev)
+            p_gbs = alg_bytes / (p_ms * 1e-3) / 1e9
+            log("prefill with in-kernel preparation: %.3f ms" % p_ms)
+            result["prefill_prepared_in_kernel"] = {
+                "workload": "k3_prefill_B1_T8192_H96_K128_V128", "call": "chunk_fwd_fused_gate(qk_l2norm, beta_logits, "
+                "state_vk)", "tokens_per_s": B * T / (p_ms * 1e-3), "launch_ms": p_ms,
+                "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": p_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg_bytes}}
+            del bl, fin_vk
+    else:
+        result = {"metric": "KDA prefill tokens/s (H=96,D=128) + % MFMA peak; decode state HBM GB/s",
+                  "only": args.only, "n_gpus": 1, "dtype": "bf16", "data": "synthetic"}
     del g, out, wsp
 
     # ---------------- packed sequences: 8 sequences of 1,024-32,768 tokens --------------
-    if not args.no_varlen:
+    if not args.no_varlen and run("varlen"):
         log("generating packed-sequence inputs")
         vl = synth.varlen_stress(device="cuda")
         Tv = vl.q.shape[1]
@@ -355,7 +366,7 @@ def main():
             "ms_per_call_wall": vwall * 1e3,
             "roofline": {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": v_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": v_bytes}}
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and args.only is None:
             import oracle
             from tests.helpers import f64
             hs = list(range(0, H, 4))  # 24 of the 96 heads, every sequence
@@ -377,30 +388,31 @@ def main():
     # ---------------- the gate alone: bounded_decay over the same logits ----------------
     # (the separate elementwise kernel of the unfused path: bf16 logits in, float32
     # retention out, 6 B per element)
-    ga = torch.empty(B, T, H, K, dtype=torch.float32, device=dev)
-    for _ in range(3):
-        kda.bounded_decay(z, ls, lower_bound=-5.0, out=ga)
-    torch.cuda.synchronize()
-    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    for a_, b_ in gev:
-        a_.record(stream)
-        kda.bounded_decay(z, ls, lower_bound=-5.0, out=ga)
-        b_.record(stream)
-    torch.cuda.synchronize()
-    g_us = sum(a_.elapsed_time(b_) for a_, b_ in gev) / len(gev) * 1e3
-    g_bytes = th * K * (2 + 4)
-    g_gbs = g_bytes / (g_us * 1e-6) / 1e9
-    log("bounded_decay: %.1f us per call, %.0f GB/s" % (g_us, g_gbs))
-    result["bounded_decay"] = {
-        "workload": "k3_prefill_B1_T8192_H96_K128 logits (bf16) -> alpha (fp32)", "calls": len(gev),
-        "launch_us_avg": g_us,
-        "roofline": {"bound": "hbm", "achieved": g_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": g_gbs / HBM_PEAK_GBS, "kernel": "bounded_decay_kernel",
-                     "algorithmic_bytes_per_launch": g_bytes}}
-    del ga
+    if run("gate"):
+        ga = torch.empty(B, T, H, K, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            kda.bounded_decay(z, ls, lower_bound=-5.0, out=ga)
+        torch.cuda.synchronize()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a_, b_ in gev:
+            a_.record(stream)
+            kda.bounded_decay(z, ls, lower_bound=-5.0, out=ga)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        g_us = sum(a_.elapsed_time(b_) for a_, b_ in gev) / len(gev) * 1e3
+        g_bytes = th * K * (2 + 4)
+        g_gbs = g_bytes / (g_us * 1e-6) / 1e9
+        log("bounded_decay: %.1f us per call, %.0f GB/s" % (g_us, g_gbs))
+        result["bounded_decay"] = {
+            "workload": "k3_prefill_B1_T8192_H96_K128 logits (bf16) -> alpha (fp32)", "calls": len(gev),
+            "launch_us_avg": g_us,
+            "roofline": {"bound": "hbm", "achieved": g_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": g_gbs / HBM_PEAK_GBS, "kernel": "bounded_decay_kernel",
+                         "algorithmic_bytes_per_launch": g_bytes}}
+        del ga
 
     # ---------------- backward ----------------------------------------------------------
-    if not args.no_bwd:
+    if not args.no_bwd and run("bwd"):
         # gradients of the same K3 prefill: bf16 q, k, v and d_out, float32 retention (the
         # gate tensor the backward takes), bf16 dq, dk, dv, float32 dgate and dbeta
         alpha_b = kda.bounded_decay(z, ls, lower_bound=-5.0)
@@ -445,7 +457,7 @@ def main():
         del ws, alpha_b, d_out_b, d_fin_b
 
     # ---------------- decode ------------------------------------------------------------
-    if not args.no_decode:
+    if not args.no_decode and run("decode"):
         nd = args.decode_steps
         log("generating decode inputs (%d steps)" % nd)
         dec = synth.decode(device="cuda", steps=nd)
@@ -533,7 +545,7 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": v_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": d_bytes}}
             del st_vk, blog
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and args.only is None:
             # the oracle on a sample of the (sequence, head) pairs: the same 256 steps from the
             # same kept state, one token scan per pair
             import oracle
@@ -553,7 +565,7 @@ def main():
         del dec, state, src, dst
 
     # ---------------- short continuations: the token-recurrent prefill ------------------
-    if not args.no_short:
+    if not args.no_short and run("short"):
         log("generating short-continuation inputs")
         sp = synth.short_prompts(device="cuda")
         Bs, Ts, Hs = sp.q.shape[0], sp.q.shape[1], sp.q.shape[2]
@@ -598,7 +610,7 @@ def main():
         del so, sf
 
     # ---------------- CPU baseline: the oracle on a head sample -------------------------
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.only is None:
         import oracle
         from tests.helpers import f64
         hs = list(range(0, H, max(1, H // args.cpu_heads)))[:args.cpu_heads]
@@ -615,7 +627,7 @@ def main():
         result["cpu_baseline"] = {"value": cpu_tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                   "sample": "fp64 gate + token scan of %d of the %d heads (T=8192), %.1f s wall, "
                                             "scaled by %d/%d" % (len(hs), H, cpu_s, H, len(hs))}
-        if not args.no_short:
+        if not args.no_short and run("short"):
             # the same oracle on a sample of the short-continuation (sequence, head) pairs
             npairs = 48
             t0 = time.perf_counter()
