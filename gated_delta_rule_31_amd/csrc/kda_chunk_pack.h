@@ -151,7 +151,35 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         int n, h, len;
         int64_t t0;
     };
+    // Fixed-length items it = (b W + c) H + h come in the order bid, bid + G, bid + 2G, ...
+    // (every one owns tokens): a cursor holds the decomposition of the next one and
+    // advances by G with carries, so the loop divides nothing.
+    int cb_ = 0, cc_ = 0, ch_ = 0, dB = 0, dC = 0, dH = 0;
+    if (!a.cu_seqlens && W > 0) {
+        dH = G % H;
+        dC = (G / H) % W;
+        dB = G / (W * H);
+        ch_ = bid % H;
+        cc_ = (bid / H) % W;
+        cb_ = bid / (W * H);
+    }
     auto find = [&](int from, Item &x) -> int {
+        if (!a.cu_seqlens) {  // `from` is the cursor's item
+            if (from >= nitems) return nitems;
+            const int c = c0 + cc_;
+            x.h = ch_;
+            x.n = cb_ * NC + c;
+            x.t0 = (int64_t)cb_ * a.T + (int64_t)c * C;
+            x.len = (int)min((int64_t)C, a.T - (int64_t)c * C);
+            ch_ += dH;
+            const int k1 = ch_ >= H ? 1 : 0;
+            ch_ -= k1 * H;
+            cc_ += dC + k1;
+            const int k2 = cc_ >= W ? 1 : 0;
+            cc_ -= k2 * W;
+            cb_ += dB + k2;
+            return from;
+        }
         for (int it = from; it < nitems; it += G) {
             if (a.cu_seqlens) {
                 x.n = it / H;
@@ -475,7 +503,31 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
 
         // ---- phase 4: T's off-diagonal blocks.  Block column qb depends only on itself
         // (T_pq = -T_pp sum_{r=q}^{p-1} A_pr T_rq), so wave qb fills column qb top down.
-        if (NP > 1 && wave < NP - 1) {
+        if constexpr (NP == 2) {
+            // one off-diagonal block: T_10 = -T_11 (A_10 T_00), every operand read first
+            if (wave == 0) {
+                const int l15 = lane & 15;
+                float av[4], tv[4], tt[4];
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    av[s4] = Akk[(16 + l15) * L::LCF + 4 * s4 + g];
+                    tv[s4] = Tf[(4 * s4 + g) * L::LCF + l15];
+                    tt[s4] = Tf[(16 + l15) * L::LCF + 16 + 4 * g + s4];
+                }
+                f4 m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) m = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s4], tv[s4], m, 0, 0, 0);
+                f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) t = __builtin_amdgcn_mfma_f32_16x16x4f32(tt[s4], m[s4], t, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 + 4 * g + e, j = l15;
+                    Tf[i * L::LCF + j] = -t[e];
+                    TmL[i * L::LCM + j] = from_f32<TM>(-t[e]);
+                }
+            }
+        } else if (NP > 1 && wave < NP - 1) {
             const int qb = wave;
             for (int p = qb + 1; p < NP; ++p) {
                 f4 m = {0.f, 0.f, 0.f, 0.f};
