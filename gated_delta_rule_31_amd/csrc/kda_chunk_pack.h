@@ -384,6 +384,10 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         // ---- phase 2: A-matrix operand staging and the package's Qt, -Bw, gamma_C; Kt is
         // kept in registers and goes out through LDS after phase 3 (16-byte stores)
         float2 ktk[CPT][4];
+        // (paired order, 16-bit: Qt and -Bw wait in registers as packed pairs and leave
+        // through LDS with the copy-out's 16-byte stores, a quarter of the store instructions)
+        constexpr bool STQ = PERM && !std::is_same<TM, float>::value;
+        uint32_t qtp[CPT][4], bwp[CPT][4];
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int cm = combo_of(u);
@@ -471,8 +475,14 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
                 }
                 constexpr uint32_t E = sizeof(TM);
                 const int cq = PERM ? paired_col(c0) : c0;  // (c0 even: c0, c0 + 1 stay adjacent)
-                st2_at<TM>(gp, (uint32_t)PL::gQt + E * (uint32_t)(r * K + cq), lq.x * eR.x * iq[i], lq.y * eR.y * iq[i]);
-                st2_at<TM>(gp, (uint32_t)PL::gBw + E * (uint32_t)(r * K + cq), -lk.x * eR.x * ik[i], -lk.y * eR.y * ik[i]);
+                if constexpr (STQ) {
+                    typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+                    qtp[u][i] = __builtin_bit_cast(uint32_t, h2{(_Float16)(lq.x * eR.x * iq[i]), (_Float16)(lq.y * eR.y * iq[i])});
+                    bwp[u][i] = __builtin_bit_cast(uint32_t, h2{(_Float16)(-lk.x * eR.x * ik[i]), (_Float16)(-lk.y * eR.y * ik[i])});
+                } else {
+                    st2_at<TM>(gp, (uint32_t)PL::gQt + E * (uint32_t)(r * K + cq), lq.x * eR.x * iq[i], lq.y * eR.y * iq[i]);
+                    st2_at<TM>(gp, (uint32_t)PL::gBw + E * (uint32_t)(r * K + cq), -lk.x * eR.x * ik[i], -lk.y * eR.y * ik[i]);
+                }
                 kro[i] = float2{ro.x * eCE.x * ik[i], ro.y * eCE.y * ik[i]};
                 ktk[u][i] = kro[i];
             }
@@ -488,6 +498,13 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         static_assert((size_t)K * LCT * sizeof(TM) <= (size_t)L::NST * sizeof(TA) * (P::kSplit ? 2 : 1),
                       "the Kt tile fits in the operand staging area");
         TM *KtL = reinterpret_cast<TM *>(St);
+        // Qt and -Bw [C][K] (paired columns) after Kt, row stride LQT
+        constexpr int LQT = K + 16 / (int)sizeof(TM);
+        constexpr size_t oQtL = ((size_t)K * LCT * sizeof(TM) + 15) & ~size_t(15);
+        constexpr size_t oBwL = oQtL + (size_t)C * LQT * sizeof(TM);
+        static_assert(!STQ || oBwL + (size_t)C * LQT * sizeof(TM) <= (size_t)L::NST * sizeof(TA) * (P::kSplit ? 2 : 1),
+                      "Kt, Qt and -Bw fit in the operand staging area");
+        unsigned char *StB = reinterpret_cast<unsigned char *>(St);
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int cm = combo_of(u);
@@ -498,6 +515,15 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
                 const int r = 16 * p + 4 * qd + i;
                 st2<TM>(KtL + c0 * LCT + r - 1, ktk[u][i - 1].x, ktk[u][i].x);
                 st2<TM>(KtL + (c0 + 1) * LCT + r - 1, ktk[u][i - 1].y, ktk[u][i].y);
+            }
+            if constexpr (STQ) {
+                const int cq = paired_col(c0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * p + 4 * qd + i;
+                    *reinterpret_cast<uint32_t *>(StB + oQtL + ((size_t)r * LQT + cq) * sizeof(TM)) = qtp[u][i];
+                    *reinterpret_cast<uint32_t *>(StB + oBwL + ((size_t)r * LQT + cq) * sizeof(TM)) = bwp[u][i];
+                }
             }
         }
 
@@ -557,6 +583,15 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         // (the next item's phase 1 touches neither these nor the staging area, and its
         // first barrier comes before anything here is written again)
         constexpr int RC = C * (int)sizeof(TM) / 16;  // 16-byte pieces per row
+        if constexpr (STQ) {  // Qt and -Bw rows, already in the paired order
+            constexpr int RQ = K * (int)sizeof(TM) / 16;
+            for (int e = tid; e < 2 * C * RQ; e += PPT) {
+                const int row = e / RQ, pc = e - row * RQ;  // rows: Qt's C, then -Bw's C
+                const size_t src = (row < C ? oQtL : oBwL) + ((size_t)(row % C) * LQT) * sizeof(TM) + 16 * pc;
+                const size_t dst = (row < C ? PL::gQt : PL::gBw) + (size_t)(row % C) * K * sizeof(TM) + 16 * pc;
+                *reinterpret_cast<uint4 *>(gp + dst) = *reinterpret_cast<const uint4 *>(StB + src);
+            }
+        }
         for (int e = tid; e < (K + (1 + P::kAqParts) * C) * RC; e += PPT) {
             const int row = e / RC, pc = e - row * RC;  // rows: Kt's K, then T's C, then A_qk's C (twice)
             const TM *src;
