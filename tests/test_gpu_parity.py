@@ -247,6 +247,23 @@ def test_varlen_matches_oracle_and_separate_calls():
         assert torch.equal(os_, o[:, a0:a1]) and torch.equal(fs[0], f[s])
 
 
+@pytest.mark.parametrize("n,seed", [(300, 61), (40, 62)])
+def test_many_packed_sequences(n, seed):
+    """Many short packed sequences with empty ones among them: 300 (more than the chain
+    kernel orders longest first, so the natural order) and 40 (ordered), against the oracle."""
+    _case("varlen %d sequences" % n)
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(0, 70, (n,), generator=g).tolist()
+    inp = synth.make_prefill(1, sum(lens), 2, 64, 64, seed=seed, seqlens=lens, state_std=0.2)
+    o, f = gpu_prefill(inp)
+    eo, ef = oracle_prefill(inp)
+    assert_close(o, eo, False, "out")
+    assert_close(f, ef, False, "final states")
+    for s_ in range(n):  # an empty sequence keeps its initial state
+        if lens[s_] == 0:
+            assert torch.equal(f[s_].cpu(), inp.initial_state[s_])
+
+
 def test_empty_sequence_contract():
     _case("empty sequence")
     B, H, K, V = 2, 3, 64, 32
