@@ -56,18 +56,31 @@ hipError_t launch_segment_any(const ChunkArgs &ca, const ChunkArgs &pa, bool fp3
 
 // The 16-bit chain kernel with direct global-to-LDS copies (kda_chunk_chain2.h), where its
 // layout fits; else hipErrorNotSupported.
-template <int K, int V, int C>
-hipError_t launch_chain2_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream) {
-    using L2 = Chain2Layout<K, V, C>;
+template <int K, int V, int C, int NW>
+hipError_t launch_chain2_kvcw(const ChunkArgs &a, int num_pairs, hipStream_t stream) {
+    using L2 = Chain2Layout<K, V, C, NW>;
     if constexpr (!L2::ok) {
         return hipErrorNotSupported;
     } else {
         if (!a.q) return hipSuccess;  // query only
-        // the kernel's LDS is static (its four chunk buffers)
-        auto kern = chunk_chain2_kernel<K, V, C>;
-        hipLaunchKernelGGL(kern, dim3(num_pairs * (V / L2::BV)), dim3(256), 0, stream, a);
+        // the kernel's LDS is static (its chunk buffers)
+        auto kern = chunk_chain2_kernel<K, V, C, NW>;
+        hipLaunchKernelGGL(kern, dim3(num_pairs * (V / L2::BV)), dim3(64 * NW), 0, stream, a);
         return hipGetLastError();
     }
+}
+
+// Four waves (64 value columns, one wave per SIMD) give the shortest step, so they serve
+// when the workgroups fit on the device at once; with at least two rounds of workgroups the
+// device is throughput-bound, and eight waves (128 value columns, two waves per SIMD, each
+// package copied once per head) do more per compute unit.
+template <int K, int V, int C>
+hipError_t launch_chain2_kvc(const ChunkArgs &a, int num_pairs, hipStream_t stream) {
+    if constexpr (Chain2Layout<K, V, C, 8>::ok) {
+        if (a.q && (int64_t)num_pairs * (V / 128) >= 2 * (int64_t)device_cu_count())
+            return launch_chain2_kvcw<K, V, C, 8>(a, num_pairs, stream);
+    }
+    return launch_chain2_kvcw<K, V, C, 4>(a, num_pairs, stream);
 }
 
 hipError_t launch_chain2(const ChunkArgs &a, int K, int V, int C, int num_pairs, hipStream_t stream) {

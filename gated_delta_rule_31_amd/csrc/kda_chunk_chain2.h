@@ -43,22 +43,25 @@ __device__ __forceinline__ int row_swz(int r) {
     return swz_of(R, r);
 }
 
-template <int K, int V, int C>
+template <int K, int V, int C, int NW>
 struct Chain2Layout {
     using PL = PackLayout<PrecMixed, K, C>;
-    static constexpr int BV = 64;
+    static constexpr int BV = 16 * NW;     // value columns of a workgroup: 16 per wave
     static constexpr int RK = K * 2 / 16;  // pieces per row of Qt / Bw
     static constexpr int RC = C * 2 / 16;  // pieces per row of Kt, T, A_qk
-    // A copy instruction moves 256 pieces of 16 bytes (4 waves x 64 lanes).  The package
+    // A copy instruction moves 64 NW pieces of 16 bytes (NW waves x 64 lanes).  The package
     // takes JV whole instructions (padded), the chunk's values [C][BV] bf16 exactly one more.
-    static constexpr int JV = (int)((PL::bytes + 4095) / 4096);
-    static constexpr size_t oV = (size_t)JV * 4096;
+    static constexpr size_t IB = 1024 * NW;
+    static constexpr int JV = (int)((PL::bytes + IB - 1) / IB);
+    static constexpr size_t oV = (size_t)JV * IB;
     static constexpr int J = JV + 1;                         // copy instructions per wave per chunk
-    static constexpr size_t buf = (size_t)J * 4096;          // one chunk buffer
-    static constexpr int NB = 4;                             // buffers: copies run three chunks ahead
+    static constexpr size_t buf = (size_t)J * IB;            // one chunk buffer
+    // buffers: with four waves four (copies run three chunks ahead), with eight three (two)
+    static constexpr int NB = NW == 4 ? 4 : 3;
     static constexpr size_t total = NB * buf;
-    // 32-token chunks: C * BV * 2 == 4096, and a 64-token chunk's fragments do not fit
-    static constexpr bool ok = K % 32 == 0 && C == 32 && V % BV == 0 && total <= 160 * 1024 && 2 * J <= 63 &&
+    // 32-token chunks: C * BV * 2 == IB, and a 64-token chunk's fragments do not fit
+    static constexpr bool ok = (NW == 4 || NW == 8) && K % 32 == 0 && C == 32 && V % BV == 0 &&
+                               total <= 160 * 1024 - 2048 && (NB - 2) * J <= 63 &&
                                (RK == 4 || RK == 8 || RK == 16) && (RC == 4 || RC == 8);
 };
 
@@ -154,18 +157,23 @@ __device__ __forceinline__ int wave_exp(float m) {
     return e > 141 ? e - 141 : 0;
 }
 
-template <int K, int V, int C>
-__global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
-    using L2 = Chain2Layout<K, V, C>;
+template <int K, int V, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void chunk_chain2_kernel(ChunkArgs a) {
+    using L2 = Chain2Layout<K, V, C, NW>;
     constexpr int NB = L2::NB;
     using PL = PackLayout<PrecMixed, K, C>;
     using F = Chain2Frags<K, V, C>;
+    static_assert(L2::ok, "layout");
+    // eight waves (two per SIMD): each part of a chunk's fragments is read from LDS right
+    // before its products, the other wave of the SIMD covering the latency; four waves: the
+    // next chunk's fragments are read into registers during the step
+    constexpr bool JIT = NW == 8;
     constexpr int NP = C / 16, NKT = K / 16, BV = L2::BV, J = L2::J;
     constexpr int RK = L2::RK, RC = L2::RC;
 
-    // Four separate arrays, not one: a copy into one buffer and the reads of another are then
+    // Separate arrays, not one: a copy into one buffer and the reads of another are then
     // distinct objects, so the compiler need not wait for the copies before every LDS read.
-    __shared__ __align__(16) unsigned char lds0[L2::buf], lds1[L2::buf], lds2[L2::buf], lds3[L2::buf];
+    __shared__ __align__(16) unsigned char lds0[L2::buf], lds1[L2::buf], lds2[L2::buf], lds3[NB > 3 ? L2::buf : 16];
     auto bufp = [&](auto I) -> unsigned char * {
         constexpr int i = decltype(I)::value % NB;
         if constexpr (i == 0) return lds0;
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
     uint32_t srcoff[L2::JV];  // byte offset in the package
 #pragma unroll
     for (int j = 0; j < L2::JV; ++j) {
-        const int x = 64 * (wave + 4 * j) + lane;
+        const int x = 64 * (wave + NW * j) + lane;
         const size_t b = (size_t)x * 16;
         uint32_t off = 0;
         if (b < PL::bytes) {
@@ -253,8 +261,9 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         }
         srcoff[j] = off;
     }
-    const int vrow = (64 * wave + lane) >> 3;                  // value piece: row and 16 bytes
-    const uint32_t vcol = (uint32_t)((64 * wave + lane) & 7) * 16;
+    constexpr int PV = BV * 2 / 16;                            // 16-byte pieces per value row
+    const int vrow = (64 * wave + lane) / PV;                  // value piece: row and 16 bytes
+    const uint32_t vcol = (uint32_t)((64 * wave + lane) % PV) * 16;
     const uint32_t vstride = (uint32_t)H * V * 2;              // bytes between token rows of v
     // The copies of one chunk go out in four groups spread over the serial step, so the
     // vector-memory path of the compute unit works beside the arithmetic instead of stalling
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = k * L2::JV / 4; j < (k + 1) * L2::JV / 4; ++j) {
             const unsigned char *src = cs.gp + srcoff[j];
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lb + 1024 * (wv + 4 * j)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lb + 1024 * (wv + NW * j)), 16, 0, 0);
         }
     };
     auto copy_chunk = [&](int ci, unsigned char *lb) {
@@ -407,8 +416,10 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
     // f is refilled from the next chunk's buffer nb as soon as its last product has issued, so
     // the LDS reads run under the rest of the step.  The power-of-two range scales are
     // wave-uniform and almost always 0: the unscaled forms skip their multiplies.
-    auto compute = [&](F &f, const unsigned char *nb, int cn, auto &&issue) __attribute__((always_inline)) {
+    auto compute = [&](F &f, const unsigned char *cb, const unsigned char *nb, int cn, auto &&issue)
+                       __attribute__((always_inline)) {
         issue(IC<0>{});
+        if constexpr (JIT) read_y(cb, f);
         f4 Y[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p)
@@ -425,7 +436,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
             for (int m = 0; m < NKT / 2; ++m)
                 Y[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.fb[p][m], Sh.pair[m], Y[p], 0, 0, 0);
         issue(IC<1>{});
-        read_y(nb, f);
+        if constexpr (!JIT) read_y(nb, f);
         const int sY = wave_exp(amax(Y));
         if (sY) {
             const float d = pow2f(-sY);
@@ -434,6 +445,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         }
         BFrag<_Float16, NP> Yh, Yl;
         split16(Yh, Yl, Y);
+        if constexpr (JIT) read_t(cb, f);
         f4 Vt[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -447,7 +459,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
             }
         }
         issue(IC<2>{});
-        read_t(nb, f);
+        if constexpr (!JIT) read_t(nb, f);
         const int sv = wave_exp(amax(Vt));
         if (sv) {
             const float d = pow2f(-sv);
@@ -456,6 +468,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         }
         BFrag<_Float16, NP> Vh, Vl;
         split16(Vh, Vl, Vt);
+        if constexpr (JIT) read_o(cb, f);
         const int sV = sY + sv;  // Vh (+ Vl) holds Vt 2^-(sS + sV)
         // O^T = S^T Qt^T + Vt^T A_qk^T: lane (g, r16) holds value columns 4g..4g+3 of token r16
         // (two accumulators: the state part is at scale 2^-sS, the intra-chunk part at
@@ -478,7 +491,8 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
             for (int e = 0; e < 4; ++e) opend[p][e] = __builtin_fmaf(o[e], uQ, oa[e] * uA);
         }
         issue(IC<3>{});
-        read_o(nb, f);
+        if constexpr (!JIT) read_o(nb, f);
+        if constexpr (JIT) read_s(cb, f);
         const int64_t t0 = bos + (int64_t)(cfirst + cn) * C;
         t_pend = t0;
         n_pend = (int)((eos - t0) < C ? (eos - t0) : C);
@@ -507,7 +521,7 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < NKT; ++t) S[t] = X[t];
-        read_s(nb, f);
+        if constexpr (!JIT) read_s(nb, f);
         state_operand();
     };
 
@@ -528,15 +542,17 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
     F f;
     if (nchunks > 0) copy_chunk(0, bufp(IC<0>{}));
     if (nchunks > 1) copy_chunk(1, bufp(IC<1>{}));
-    if (nchunks > 2) copy_chunk(2, bufp(IC<2>{}));
-    if (nchunks > 3) copy_chunk(3, bufp(IC<3>{}));
+    if (!JIT && nchunks > 2) copy_chunk(2, bufp(IC<2>{}));
+    if (!JIT && NB > 3 && nchunks > 3) copy_chunk(3, bufp(IC<3>{}));
     wait_barrier(IC<0>{});
-    read_y(bufp(IC<0>{}), f);
-    read_t(bufp(IC<0>{}), f);
-    read_o(bufp(IC<0>{}), f);
-    read_s(bufp(IC<0>{}), f);
-    // every wave's reads of buffer 0 are done before period 0 copies into it
-    wait_barrier(IC<0>{});
+    if constexpr (!JIT) {
+        read_y(bufp(IC<0>{}), f);
+        read_t(bufp(IC<0>{}), f);
+        read_o(bufp(IC<0>{}), f);
+        read_s(bufp(IC<0>{}), f);
+        // every wave's reads of buffer 0 are done before period 0 copies into it
+        wait_barrier(IC<0>{});
+    }
 
     // Period c (chunk c of the range in buffer c % 4): store chunk c-1's output; copy chunk
     // c+4 into chunk c's buffer (its fragments are in registers); compute chunk c while
@@ -546,21 +562,35 @@ __global__ __launch_bounds__(256) void chunk_chain2_kernel(ChunkArgs a) {
     // of chunks c+3 and c+4 (J each, issued after chunk c+2's) the last ones means chunk c+2
     // has landed.
     auto period = [&](auto I, int c) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
         store_pending();
-        const bool cp = c + NB < nchunks;
-        const CopySrc cs = copy_src(cp ? c + NB : c);
-        compute(f, bufp(IC<decltype(I)::value + 1>{}), c, [&](auto G) {
-            if (cp) copy_group(cs, bufp(I), G);
-        });
-        if (c + 4 < nchunks) wait_barrier(IC<2 * J>{});
-        else if (c + 3 < nchunks) wait_barrier(IC<J>{});
-        else wait_barrier(IC<0>{});
+        if constexpr (JIT) {
+            // chunk c is read from its own buffer during the step; chunk c+2 is copied into
+            // the buffer chunk c-1 left (read before the last barrier)
+            const bool cp = c + 2 < nchunks;
+            const CopySrc cs = copy_src(cp ? c + 2 : c);
+            compute(f, bufp(IC<i>{}), bufp(IC<i + 1>{}), c, [&](auto G) {
+                if (cp) copy_group(cs, bufp(IC<i + 2>{}), G);
+            });
+            if (cp) wait_barrier(IC<J>{});  // chunk c+1 has landed
+            else wait_barrier(IC<0>{});
+        } else {
+            const bool cp = c + NB < nchunks;
+            const CopySrc cs = copy_src(cp ? c + NB : c);
+            compute(f, bufp(IC<i>{}), bufp(IC<i + 1>{}), c, [&](auto G) {
+                if (cp) copy_group(cs, bufp(I), G);
+            });
+            if (NB > 3 && c + 4 < nchunks) wait_barrier(IC<(NB - 2) * J>{});
+            else if (c + 3 < nchunks) wait_barrier(IC<J>{});
+            else wait_barrier(IC<0>{});
+        }
     };
-    for (int c = 0; c < nchunks; c += 4) {  // workgroup-uniform
+    for (int c = 0; c < nchunks; c += NB) {  // workgroup-uniform
         period(IC<0>{}, c);
         if (c + 1 < nchunks) period(IC<1>{}, c + 1);
         if (c + 2 < nchunks) period(IC<2>{}, c + 2);
-        if (c + 3 < nchunks) period(IC<3>{}, c + 3);
+        if constexpr (NB > 3)
+            if (c + 3 < nchunks) period(IC<3>{}, c + 3);
     }
     store_pending();
 
