@@ -269,34 +269,48 @@ __global__ __launch_bounds__(64 * NW) void chunk_chain2_kernel(ChunkArgs a) {
     // vector-memory path of the compute unit works beside the arithmetic instead of stalling
     // the waves at the start of the period.  Group k takes package instructions
     // [k JV / 4, (k + 1) JV / 4); group 0 also the value instruction.
+    // The copies are buffer loads into LDS: the chunk's package and its value rows each get a
+    // raw buffer resource (a scalar base, no stride), and each lane's byte offset in it is a
+    // 32-bit vector operand (the package offsets are fixed for the whole kernel), so a copy
+    // instruction needs no per-lane address arithmetic.
+    // (the resources are made where they are used: a lambda returning one, or a struct
+    // holding one, fails in the host-side pass of hipcc, which then drops the launch stub)
     struct CopySrc {
-        const unsigned char *gp;    // the chunk's package
-        const unsigned char *vsrc;  // this lane's value piece
+        const unsigned char *pk;  // the chunk's package
+        const unsigned char *vr;  // the chunk's value rows
+        uint32_t voff;            // this lane's value piece
     };
-    auto copy_src = [&](int ci) {  // the range's chunk ci
-        const int cn = cfirst + ci;
-        const int64_t t0 = bos + (int64_t)cn * C;
-        const int last = (int)((eos - t0) < C ? (eos - t0) : C) - 1;
-        const unsigned char *vp = static_cast<const unsigned char *>(a.v) + ((t0 * H + h) * V + vb * BV) * 2;
-        return CopySrc{a.pack + ((size_t)(base + cn) * H + h) * PL::bytes,
-                       vp + ((uint32_t)(vrow < last ? vrow : last) * vstride + vcol)};
+    // The chunks are copied in order: the sources of the next one advance by fixed steps.
+    const unsigned char *pk_next = a.pack + ((size_t)(base + cfirst) * H + h) * PL::bytes;
+    const unsigned char *v_next =
+        static_cast<const unsigned char *>(a.v) + (((bos + (int64_t)cfirst * C) * H + h) * V + vb * BV) * 2;
+    int64_t t_next = bos + (int64_t)cfirst * C;
+    auto next_src = [&]() {  // the next chunk's sources (past the range: not used)
+        const int last = (int)((eos - t_next) < C ? (eos - t_next) : C) - 1;
+        const CopySrc cs{pk_next, v_next, (uint32_t)(vrow < last ? vrow : last) * vstride + vcol};
+        pk_next += (size_t)H * PL::bytes;
+        v_next += (size_t)C * vstride;
+        t_next += C;
+        return cs;
     };
-    // (the source pointers are named locals: given as expressions, the host-side pass of
-    // hipcc drops the kernel's launch stub)
     auto copy_group = [&](const CopySrc &cs, unsigned char *lb, auto G) {
         constexpr int k = decltype(G)::value;
         if constexpr (k == 0) {
-            const unsigned char *vsrc = cs.vsrc;
-            __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void *)(lb + L2::oV + 1024 * wv), 16, 0, 0);
+            __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(cs.vr), (short)0, (int)(C * vstride), 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void *)(lb + L2::oV + 1024 * wv),
+                                                     16, (int)cs.voff, 0, 0, 0);
         }
+        __amdgpu_buffer_rsrc_t rp =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(cs.pk), (short)0, (int)PL::bytes, 0x00020000);
 #pragma unroll
-        for (int j = k * L2::JV / 4; j < (k + 1) * L2::JV / 4; ++j) {
-            const unsigned char *src = cs.gp + srcoff[j];
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lb + 1024 * (wv + NW * j)), 16, 0, 0);
-        }
+        for (int j = k * L2::JV / 4; j < (k + 1) * L2::JV / 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (__attribute__((address_space(3))) void *)(lb + 1024 * (wv + NW * j)),
+                                                     16, (int)srcoff[j], 0, 0, 0);
     };
-    auto copy_chunk = [&](int ci, unsigned char *lb) {
-        const CopySrc cs = copy_src(ci);
+    auto copy_chunk = [&](bool go, unsigned char *lb) {
+        const CopySrc cs = next_src();
+        if (!go) return;
         copy_group(cs, lb, IC<0>{});
         copy_group(cs, lb, IC<1>{});
         copy_group(cs, lb, IC<2>{});
@@ -388,28 +402,35 @@ __global__ __launch_bounds__(64 * NW) void chunk_chain2_kernel(ChunkArgs a) {
     state_operand();
 
     // output of the previous chunk, stored at the start of the next period
+    // The stores go through a buffer resource over the chunk's output rows: a lane's row past
+    // the sequence's end lies past the resource's bound, and the hardware drops that store.
     f4 opend[NP];
-    int64_t t_pend = -1;
-    int n_pend = 0;
+    bool pend = false;
+    const unsigned char *o_pend = nullptr;
+    uint32_t nb_pend = 0;
+    const int esz = a.out_bf16 ? 2 : 4;
     const int j0 = vb * BV + wave * 16 + 4 * g;  // first of this lane's four output columns
+    unsigned char *o_run = static_cast<unsigned char *>(a.out) + ((bos + (int64_t)cfirst * C) * H + h) * V * esz;
+    int64_t t_run = bos + (int64_t)cfirst * C;   // first token of the chunk being computed
     auto store_pending = [&]() {
-        if (t_pend < 0) return;
-        unsigned char *ob = static_cast<unsigned char *>(a.out) + (t_pend * H + h) * V * (a.out_bf16 ? 2 : 4);
+        if (!pend) return;
+        __amdgpu_buffer_rsrc_t ro =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(o_pend), (short)0, (int)nb_pend, 0x00020000);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const int i = 16 * p + r16;
-            const uint32_t off = (uint32_t)(i * H * V + j0);
-            if (i < n_pend) {
-                if (a.out_bf16) {
-                    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-                    *reinterpret_cast<bf16x4 *>(ob + 2u * off) =
-                        bf16x4{(__bf16)opend[p][0], (__bf16)opend[p][1], (__bf16)opend[p][2], (__bf16)opend[p][3]};
-                } else {
-                    *reinterpret_cast<float4 *>(ob + 4u * off) = float4{opend[p][0], opend[p][1], opend[p][2], opend[p][3]};
-                }
+            const int off = ((16 * p + r16) * H * V + j0) * esz;
+            if (a.out_bf16) {
+                typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+                typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+                const u32x2 x = {__builtin_bit_cast(unsigned int, bf16x2{(__bf16)opend[p][0], (__bf16)opend[p][1]}),
+                                 __builtin_bit_cast(unsigned int, bf16x2{(__bf16)opend[p][2], (__bf16)opend[p][3]})};
+                __builtin_amdgcn_raw_buffer_store_b64(x, ro, off, 0, 0);
+            } else {
+                typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, opend[p]), ro, off, 0, 0);
             }
         }
-        t_pend = -1;
+        pend = false;
     };
 
     // One chunk's serial step from the fragments in f (the math of state_waves); each part of
@@ -493,9 +514,11 @@ __global__ __launch_bounds__(64 * NW) void chunk_chain2_kernel(ChunkArgs a) {
         issue(IC<3>{});
         if constexpr (!JIT) read_o(nb, f);
         if constexpr (JIT) read_s(cb, f);
-        const int64_t t0 = bos + (int64_t)(cfirst + cn) * C;
-        t_pend = t0;
-        n_pend = (int)((eos - t0) < C ? (eos - t0) : C);
+        pend = true;
+        o_pend = o_run;
+        nb_pend = (uint32_t)((eos - t_run) < C ? (eos - t_run) : C) * (uint32_t)(H * V * esz);
+        o_run += (size_t)C * H * V * esz;
+        t_run += C;
         // S = gamma_C S + Kt^T Vt, accumulated as S 2^-w with w the scale of Vh (the rare
         // rescales in place, so the state keeps its registers from chunk to chunk)
         const int w = sS + sV;
@@ -540,10 +563,12 @@ __global__ __launch_bounds__(64 * NW) void chunk_chain2_kernel(ChunkArgs a) {
 
     // ---- prologue: the range's first NB chunks copied, chunk 0's fragments read ----------------
     F f;
-    if (nchunks > 0) copy_chunk(0, bufp(IC<0>{}));
-    if (nchunks > 1) copy_chunk(1, bufp(IC<1>{}));
-    if (!JIT && nchunks > 2) copy_chunk(2, bufp(IC<2>{}));
-    if (!JIT && NB > 3 && nchunks > 3) copy_chunk(3, bufp(IC<3>{}));
+    copy_chunk(nchunks > 0, bufp(IC<0>{}));
+    copy_chunk(nchunks > 1, bufp(IC<1>{}));
+    if constexpr (!JIT) {
+        copy_chunk(nchunks > 2, bufp(IC<2>{}));
+        if constexpr (NB > 3) copy_chunk(nchunks > 3, bufp(IC<3>{}));
+    }
     wait_barrier(IC<0>{});
     if constexpr (!JIT) {
         read_y(bufp(IC<0>{}), f);
@@ -568,7 +593,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_chain2_kernel(ChunkArgs a) {
             // chunk c is read from its own buffer during the step; chunk c+2 is copied into
             // the buffer chunk c-1 left (read before the last barrier)
             const bool cp = c + 2 < nchunks;
-            const CopySrc cs = copy_src(cp ? c + 2 : c);
+            const CopySrc cs = next_src();  // chunk c+2
             compute(f, bufp(IC<i>{}), bufp(IC<i + 1>{}), c, [&](auto G) {
                 if (cp) copy_group(cs, bufp(IC<i + 2>{}), G);
             });
@@ -576,7 +601,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_chain2_kernel(ChunkArgs a) {
             else wait_barrier(IC<0>{});
         } else {
             const bool cp = c + NB < nchunks;
-            const CopySrc cs = copy_src(cp ? c + NB : c);
+            const CopySrc cs = next_src();  // chunk c+NB
             compute(f, bufp(IC<i>{}), bufp(IC<i + 1>{}), c, [&](auto G) {
                 if (cp) copy_group(cs, bufp(I), G);
             });
