@@ -105,7 +105,7 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, gat
     # the two-kernel form per call: the pre-pass over every (chunk, head) item (packages in
     # the paired column order), then the DMA-fed chain kernel
     two_pass = [(("chunk_pack_kernel<", "PrecMixed, 128, 32, %d, true>" % (1 if zg else 0)), 1),
-                (("chunk_chain2_kernel<128, 128, 32>",), 1)]
+                (("chunk_chain2_kernel<128, 128, 32, 4>",), 1)]
     entries = [("k3_prefill_chunk_fwd_" + gate, [("chunk_fwd_kernel<", chunk_pat)], "kda_chunk_kernel.h"),
                ("decode_recurrent_step_" + gate, [("recurrent_step_kernelIDF16bLi128ELi128E" + flag,)], "kda_step.hip"),
                ("short_recurrent_fwd_" + gate, [("recurrent_fwd_kernelIDF16bLi128ELi128E" + flag,)],

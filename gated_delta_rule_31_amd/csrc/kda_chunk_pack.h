@@ -67,28 +67,6 @@ struct ChainLds {
     static constexpr bool fits = total <= 160 * 1024;
 };
 
-// first token row and length of the chunk in slot n (length 0: no sequence owns it)
-template <int C>
-__device__ __forceinline__ void slot_span(int n, const int32_t *cu, int N, int64_t T, int64_t &t0, int &len) {
-    if (!cu) {
-        const int NC = (int)((T + C - 1) / C);
-        const int b = n / NC, j = n - b * NC;
-        t0 = (int64_t)b * T + (int64_t)j * C;
-        len = (int)min((int64_t)C, T - (int64_t)j * C);
-        return;
-    }
-    int lo = 0, hi = N - 1;  // last sequence whose first slot is <= n
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu[mid] / C + mid <= n) lo = mid;
-        else hi = mid - 1;
-    }
-    const int64_t a0 = cu[lo], l = (int64_t)cu[lo + 1] - a0;
-    const int64_t off = (int64_t)(n - (cu[lo] / C + lo)) * C;
-    t0 = a0 + off;
-    len = off < l ? (int)min((int64_t)C, l - off) : 0;
-}
-
 // Column k = 32m + 16h + 4g + e of a matrix stored in the paired order sits at
 // 32m + 8g + 4h + e: the eight k values one lane group takes in a 16x16x32 step over k tiles
 // 2m, 2m+1 (in the permuted order the accumulator tiles give) become one 16-byte piece.
@@ -155,6 +133,18 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
     // (every one owns tokens): a cursor holds the decomposition of the next one and
     // advances by G with carries, so the loop divides nothing.
     int cb_ = 0, cc_ = 0, ch_ = 0, dB = 0, dC = 0, dH = 0;
+    // Packed sequences: items it = n H + h (slot n) come in the same order; the cursor holds
+    // (n, h) of the next one and the sequence sq_ whose slots start at or before n (slots
+    // only grow, so it moves forward; fs_, fsn_: first slots of sq_ and sq_ + 1).
+    int sq_ = 0, fs_ = 0, fsn_ = 0;
+    if (a.cu_seqlens) {
+        dH = G % H;
+        dC = G / H;
+        ch_ = bid % H;
+        cc_ = bid / H;
+        fs_ = a.cu_seqlens[0] / C;
+        fsn_ = a.num_seqs > 1 ? a.cu_seqlens[1] / C + 1 : INT_MAX;
+    }
     if (!a.cu_seqlens && W > 0) {
         dH = G % H;
         dC = (G / H) % W;
@@ -180,17 +170,26 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
             cb_ += dB + k2;
             return from;
         }
-        for (int it = from; it < nitems; it += G) {
-            if (a.cu_seqlens) {
-                x.n = it / H;
-                x.h = it - x.n * H;
-            } else {
-                const int b = it / (W * H), rem = it - b * (W * H), c = rem / H;
-                x.h = rem - c * H;
-                x.n = b * NC + c0 + c;
+        for (int it = from; it < nitems; it += G) {  // `from` is the cursor's item
+            const int n = cc_, hh = ch_;
+            ch_ += dH;
+            const int k1 = ch_ >= H ? 1 : 0;
+            ch_ -= k1 * H;
+            cc_ += dC + k1;
+            while (n >= fsn_) {
+                ++sq_;
+                fs_ = fsn_;
+                fsn_ = sq_ + 1 < a.num_seqs ? a.cu_seqlens[sq_ + 1] / C + sq_ + 1 : INT_MAX;
             }
-            slot_span<C>(x.n, a.cu_seqlens, a.num_seqs, a.T, x.t0, x.len);
-            if (x.len > 0) return it;
+            const int64_t a0 = a.cu_seqlens[sq_], l = (int64_t)a.cu_seqlens[sq_ + 1] - a0;
+            const int64_t off = (int64_t)(n - fs_) * C;
+            if (off < l) {
+                x.n = n;
+                x.h = hh;
+                x.t0 = a0 + off;
+                x.len = (int)min((int64_t)C, l - off);
+                return it;
+            }
         }
         return nitems;
     };
