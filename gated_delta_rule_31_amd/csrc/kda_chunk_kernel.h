@@ -391,7 +391,13 @@ __device__ __forceinline__ void st2_stage(typename P::TA *p, int lo, float a, fl
         typedef __attribute__((ext_vector_type(2))) __bf16 v2;
         const v2 h = {(__bf16)a, (__bf16)b};
         *reinterpret_cast<v2 *>(p) = h;
-        if constexpr (P::kSplit) *reinterpret_cast<v2 *>(p + lo) = v2{(__bf16)(a - (float)h[0]), (__bf16)(b - (float)h[1])};
+        if constexpr (P::kSplit) {
+            // the hi parts back in float32 straight from the packed pair (no second rounding)
+            uint32_t hw = __builtin_bit_cast(uint32_t, h);
+            asm("" : "+v"(hw));  // keeps the compiler from converting each hi part once more
+            const float ha = __builtin_bit_cast(float, hw << 16), hb = __builtin_bit_cast(float, hw & 0xffff0000u);
+            *reinterpret_cast<v2 *>(p + lo) = v2{(__bf16)(a - ha), (__bf16)(b - hb)};
+        }
     }
 }
 

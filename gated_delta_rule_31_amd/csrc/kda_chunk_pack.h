@@ -266,7 +266,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         const bool glog = a.gate.mode == GATE_LOG;
         float gs2 = 0.f, gl2 = 0.f;
         if constexpr (ZG) {
-            gs2 = expf(rls) * 1.44269504088896341f;  // e^A log2(e)
+            gs2 = __builtin_amdgcn_exp2f(rls * 1.44269504088896341f) * 1.44269504088896341f;  // e^A log2(e)
             gl2 = a.gate.lower_bound * 1.44269504088896341f;
         }
         float2 ral[CPT][4], fq[CPT][4], fk[CPT][4];

@@ -104,14 +104,13 @@ __device__ __forceinline__ void mma_tile<float>(f4 &acc, const float *A, int lda
 
 // The bounded gate applied on the fly: alpha = exp(lower * sigmoid(scale * x)), with
 // s2 = scale * log2(e) and l2 = lower * log2(e), on the hardware base-2 exponential and
-// reciprocal (a few ulp).  The sigmoid takes exp only of a non-positive argument, so it
-// never overflows, and alpha stays in [e^lower, 1].
+// reciprocal (a few ulp).  sigmoid(u) = 1 / (1 + 2^(-u log2 e)) needs no sign split: for
+// very negative u the exponential overflows to +inf and its reciprocal is the exact limit
+// 0; otherwise 1 + 2^(...) >= 1 and the reciprocal keeps its relative accuracy.  alpha
+// stays in [e^lower, 1].
 __device__ __forceinline__ float fast_bounded_alpha(float x, float s2, float l2) {
-    const float u = s2 * x;
-    const float e = __builtin_amdgcn_exp2f(-fabsf(u));
-    const float r = __builtin_amdgcn_rcpf(1.f + e);
-    const float sg = u >= 0.f ? r : e * r;
-    return __builtin_amdgcn_exp2f(l2 * sg);
+    const float r = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(s2 * x)));
+    return __builtin_amdgcn_exp2f(l2 * r);
 }
 
 // Load one element of an input tensor as float.
