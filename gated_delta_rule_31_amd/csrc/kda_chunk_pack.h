@@ -261,6 +261,13 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         const int h = cur.h, last = cur.len - 1;
         unsigned char *gp = a.pack + ((size_t)cur.n * H + h) * PL::bytes;
         auto combo_of = [&](int u) { return CPR * u + 16 * wave + (lane & 15); };
+        // The 16-row tile of combo cm.  When NCP is a multiple of 16 the sixteen combos of a
+        // wave (and their validity) share one tile, so the tile index is wave-uniform: in a
+        // scalar register its comparisons select without vector instructions.
+        auto tile_of = [&](int cm) -> int {
+            if constexpr (NCP % 16 == 0) return __builtin_amdgcn_readfirstlane(cm / NCP);
+            else return cm / NCP;
+        };
 
         // ---- phase 1: retention factors (1 on padding rows), tile totals, beta --------
         const bool glog = a.gate.mode == GATE_LOG;
@@ -301,7 +308,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
 #pragma unroll
             for (int u = 0; u < CPT; ++u) {
                 const int cm = combo_of(u);
-                const int p = (cm < NCOMBO ? cm : 0) / NCP;
+                const int p = tile_of(cm < NCOMBO ? cm : 0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (16 * p + 4 * qd + i > last) {
@@ -317,7 +324,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
             const int cm = combo_of(u);
             const bool valid = cm < NCOMBO;
             const int cmc = valid ? cm : 0;
-            const int c0 = 2 * (cmc % NCP), p = cmc / NCP;
+            const int c0 = 2 * (cmc % NCP), p = tile_of(cmc);
             float2 run = {1.f, 1.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -391,7 +398,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         for (int u = 0; u < CPT; ++u) {
             const int cm = combo_of(u);
             if (cm >= NCOMBO) continue;
-            const int c0 = 2 * (cm % NCP), p = cm / NCP;
+            const int c0 = 2 * (cm % NCP), p = tile_of(cm);
             float2 tpr[NP];
 #pragma unroll
             for (int pp = 0; pp < NP; ++pp) tpr[pp] = *reinterpret_cast<const float2 *>(TPv + pp * K + c0);
@@ -508,7 +515,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         for (int u = 0; u < CPT; ++u) {
             const int cm = combo_of(u);
             if (cm >= NCOMBO) continue;
-            const int c0 = 2 * (cm % NCP), p = cm / NCP;
+            const int c0 = 2 * (cm % NCP), p = tile_of(cm);
 #pragma unroll
             for (int i = 1; i < 4; i += 2) {
                 const int r = 16 * p + 4 * qd + i;
@@ -578,47 +585,63 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         }
         lds_barrier();
 
-        // ---- Kt, T and A_qk to the package, 16 bytes per lane ---------------------------
+        // ---- Qt and -Bw (paired order), Kt, T and A_qk to the package, 16 bytes per lane ---
         // (the next item's phase 1 touches neither these nor the staging area, and its
-        // first barrier comes before anything here is written again)
-        constexpr int RC = C * (int)sizeof(TM) / 16;  // 16-byte pieces per row
-        if constexpr (STQ) {  // Qt and -Bw rows, already in the paired order
+        // first barrier comes before anything here is written again).  A lane reads all its
+        // pieces from LDS before it stores any, so it waits for LDS once; piece e of the lane
+        // is tid + j PPT, and with tid < PPT known the region of most pieces is fixed at
+        // compile time.
+        {
+            constexpr int RC = C * (int)sizeof(TM) / 16;            // 16-byte pieces per row
             constexpr int RQ = K * (int)sizeof(TM) / 16;
-            for (int e = tid; e < 2 * C * RQ; e += PPT) {
-                const int row = e / RQ, pc = e - row * RQ;  // rows: Qt's C, then -Bw's C
-                const size_t src = (row < C ? oQtL : oBwL) + ((size_t)(row % C) * LQT) * sizeof(TM) + 16 * pc;
-                const size_t dst = (row < C ? PL::gQt : PL::gBw) + (size_t)(row % C) * K * sizeof(TM) + 16 * pc;
-                *reinterpret_cast<uint4 *>(gp + dst) = *reinterpret_cast<const uint4 *>(StB + src);
+            constexpr int NQP = STQ ? 2 * C * RQ : 0;                // Qt's C rows, then -Bw's C
+            constexpr int NKP = (K + (1 + P::kAqParts) * C) * RC;   // Kt's K, T's C, A_qk's C per part
+            constexpr int NJ = (NQP + NKP + PPT - 1) / PPT;
+            __builtin_assume(tid >= 0 && tid < PPT);
+            uint4 x[NJ];
+            uint32_t dst[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int e = tid + j * PPT;
+                dst[j] = 0xffffffffu;  // no piece
+                if (e < NQP) {
+                    const int row = e / RQ, pc = e % RQ;
+                    const size_t src = (row < C ? oQtL : oBwL) + ((size_t)(row % C) * LQT) * sizeof(TM) + 16 * pc;
+                    dst[j] = (uint32_t)((row < C ? PL::gQt : PL::gBw) + (size_t)(row % C) * K * sizeof(TM) + 16 * pc);
+                    x[j] = *reinterpret_cast<const uint4 *>(StB + src);
+                } else if (e < NQP + NKP) {
+                    const int f = e - NQP;
+                    const int row = f / RC, pc = f % RC;
+                    const TM *src;
+                    size_t d;
+                    if (row < K) {
+                        src = KtL + row * LCT;
+                        d = PL::gKt + (size_t)row * C * sizeof(TM);
+                    } else if (row < K + C) {
+                        src = TmL + (row - K) * L::LCM;
+                        d = PL::gTm + (size_t)(row - K) * C * sizeof(TM);
+                    } else if (row < K + 2 * C) {
+                        src = AqL + (row - K - C) * L::LCM;
+                        d = PL::gAqk + (size_t)(row - K - C) * C * sizeof(TM);
+                    } else {
+                        src = AlL + (row - K - 2 * C) * L::LCM;
+                        d = PL::gAqk + (size_t)(row - K - C) * C * sizeof(TM);  // the lo part follows
+                    }
+                    dst[j] = (uint32_t)(d + 16 * pc);
+                    if constexpr (PERM && !std::is_same<TM, float>::value) {
+                        // piece pc of the paired row: tokens 32m + 4g + 0..3 and 32m + 16 + 4g + 0..3
+                        const int k0 = 32 * (pc >> 2) + 4 * (pc & 3);
+                        const uint2 lo = *reinterpret_cast<const uint2 *>(src + k0);
+                        const uint2 hi = *reinterpret_cast<const uint2 *>(src + k0 + 16);
+                        x[j] = uint4{lo.x, lo.y, hi.x, hi.y};
+                    } else {
+                        x[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(src) + 16 * pc);
+                    }
+                }
             }
-        }
-        for (int e = tid; e < (K + (1 + P::kAqParts) * C) * RC; e += PPT) {
-            const int row = e / RC, pc = e - row * RC;  // rows: Kt's K, then T's C, then A_qk's C (twice)
-            const TM *src;
-            size_t dst;
-            if (row < K) {
-                src = KtL + row * LCT;
-                dst = PL::gKt + (size_t)row * C * sizeof(TM);
-            } else if (row < K + C) {
-                src = TmL + (row - K) * L::LCM;
-                dst = PL::gTm + (size_t)(row - K) * C * sizeof(TM);
-            } else if (row < K + 2 * C) {
-                src = AqL + (row - K - C) * L::LCM;
-                dst = PL::gAqk + (size_t)(row - K - C) * C * sizeof(TM);
-            } else {
-                src = AlL + (row - K - 2 * C) * L::LCM;
-                dst = PL::gAqk + (size_t)(row - K - C) * C * sizeof(TM);  // the lo part follows
-            }
-            uint4 x;
-            if constexpr (PERM && !std::is_same<TM, float>::value) {
-                // piece pc of the paired row: tokens 32m + 4g + 0..3 and 32m + 16 + 4g + 0..3
-                const int k0 = 32 * (pc >> 2) + 4 * (pc & 3);
-                const uint2 lo = *reinterpret_cast<const uint2 *>(src + k0);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(src + k0 + 16);
-                x = uint4{lo.x, lo.y, hi.x, hi.y};
-            } else {
-                x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(src) + 16 * pc);
-            }
-            *reinterpret_cast<uint4 *>(gp + dst + 16 * pc) = x;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                if (dst[j] != 0xffffffffu) *reinterpret_cast<uint4 *>(gp + dst[j]) = x[j];
         }
         item = nxt;
         cur = nx;
