@@ -27,11 +27,21 @@ __device__ __forceinline__ float bounded_gate(float x, float scale, float lower,
     return out_log ? g : __expf(g);
 }
 
+// Heads whose per-head scale e^A the vectorised path keeps in LDS (one exponential per
+// head per workgroup instead of one per unit); more heads take it from memory per unit.
+constexpr int GATE_SC_HEADS = 1024;
+
 template <typename TIn>
 __global__ __launch_bounds__(256) void bounded_decay_kernel(GateArgs a) {
     const TIn *z = static_cast<const TIn *>(a.logits);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     if (a.vec4) {
+        __shared__ float s_sc[GATE_SC_HEADS];
+        const bool sc_lds = a.H <= GATE_SC_HEADS;  // workgroup-uniform
+        if (sc_lds) {
+            for (int i = threadIdx.x; i < a.H; i += 256) s_sc[i] = expf(a.log_scale[i]);
+            __syncthreads();
+        }
         // 4 consecutive channels of one (row, head) per thread: K / 4 threads per (row, head)
         // unit, 256 / (K / 4) units per workgroup (the host asks K / 4 to divide 256), so a
         // wave reads one contiguous run of logits and writes one contiguous 1 KB run of
@@ -48,7 +58,7 @@ __global__ __launch_bounds__(256) void bounded_decay_kernel(GateArgs a) {
         const bool bias16 = a.bias && ((uintptr_t)a.bias % 16 == 0);
         for (; u < units; u += ustride) {
             const int64_t e0 = u * a.K + c0;
-            const float sc = expf(a.log_scale[h]);
+            const float sc = sc_lds ? s_sc[h] : expf(a.log_scale[h]);
             float x[4];
             if constexpr (sizeof(TIn) == 2) {
                 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
@@ -71,7 +81,8 @@ __global__ __launch_bounds__(256) void bounded_decay_kernel(GateArgs a) {
             o.y = bounded_gate(x[1], sc, a.lower_bound, a.out_log);
             o.z = bounded_gate(x[2], sc, a.lower_bound, a.out_log);
             o.w = bounded_gate(x[3], sc, a.lower_bound, a.out_log);
-            *reinterpret_cast<float4 *>(a.out + e0) = o;
+            // streamed: written once, read by a later kernel
+            __builtin_nontemporal_store(f4{o.x, o.y, o.z, o.w}, reinterpret_cast<f4 *>(a.out + e0));
             h += dh;
             if (h >= a.H) h -= a.H;
         }
