@@ -15,8 +15,9 @@ starts.  Reported:
   average time (HIP events on the launch stream around the call's 2 launches), against
   8 TB/s and 2.5 PFLOP/s bf16; the single-kernel form is timed beside it;
 * decode: 256 successive single-token steps over a kept [64,96,128,128] fp32 state
-  (gate kernel + fused step kernel per step), with the step kernel's algorithmic
-  bytes (state read + write plus the token vectors) per launch over its launch time;
+  (one fused step kernel per step, the gate evaluated inside it; with --gate separate
+  the gate kernel before each step), with the step kernel's algorithmic bytes (state
+  read + write plus the token vectors) per launch over its launch time;
 * cpu_baseline: the fp64 oracle (gate + token scan) on half the heads of the same
   prefill workload, timed on the host cores and scaled to the whole workload.
 
@@ -307,7 +308,8 @@ def main():
                 kda.chunk_fwd_fused_gate(q, k, v, z, ls, bl, lower_bound=-5.0, chunk_size=args.chunk, out=out,
                                          final_state=fin_vk, qk_l2norm=True, beta_logits=True, state_vk=True,
                                          **(dict(workspace=wsp) if nws > 0 else dict(two_pass=False)))
-            pstep()
+            for _ in range(3):  # warm-up: the [V,K] final state and the variant's kernels
+                pstep()
             torch.cuda.synchronize()
             pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
             for a_, b_ in pev:
