@@ -58,12 +58,14 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
     }
     float4 *S = reinterpret_cast<float4 *>(a.state + (int64_t)pair * K * V);
 
-    // the state is streamed: read once and written once per step, so both use
-    // non-temporal accesses that do not displace other data from the caches
+    // the state is streamed: read once and written once per step.  The stores are
+    // non-temporal (nothing gains from allocating the state in the caches); the loads are
+    // ordinary ones, which on this GPU stream faster than non-temporal loads (measured:
+    // 123 against 143 us per B=64, H=96 step)
     float4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * CQ + cq]));
+        const f4 x = *reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * CQ + cq]);
         s[i] = float4{x[0], x[1], x[2], x[3]};
     }
 
@@ -161,7 +163,7 @@ __global__ __launch_bounds__((StepCfg<V, K>::NT)) void recurrent_step_vk_kernel(
     float4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * CQ + cq]));
+        const f4 x = *reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * CQ + cq]);
         s[i] = float4{x[0], x[1], x[2], x[3]};
     }
     float al[4], kv[4], qv[4];
