@@ -284,13 +284,19 @@ __global__ __launch_bounds__(64 * NW) void chunk_chain2_kernel(ChunkArgs a) {
     const unsigned char *pk_next = a.pack + ((size_t)(base + cfirst) * H + h) * PL::bytes;
     const unsigned char *v_next =
         static_cast<const unsigned char *>(a.v) + (((bos + (int64_t)cfirst * C) * H + h) * V + vb * BV) * 2;
-    int64_t t_next = bos + (int64_t)cfirst * C;
+    // This lane's value piece in a whole chunk, and in the sequence's partial last chunk (rows
+    // past its end read its last row): chosen per chunk by one scalar comparison.
+    const int64_t t_first = bos + (int64_t)cfirst * C;
+    const int nfull = (int)((eos - t_first) / C);                 // whole chunks from t_first on
+    const int tail_last = (int)((eos - t_first) - (int64_t)nfull * C) - 1;  // -1: no partial chunk
+    const uint32_t voff_full = (uint32_t)vrow * vstride + vcol;
+    const uint32_t voff_tail = (uint32_t)(vrow < tail_last ? vrow : (tail_last > 0 ? tail_last : 0)) * vstride + vcol;
+    int ci_next = 0;  // index of the next chunk in the range
     auto next_src = [&]() {  // the next chunk's sources (past the range: not used)
-        const int last = (int)((eos - t_next) < C ? (eos - t_next) : C) - 1;
-        const CopySrc cs{pk_next, v_next, (uint32_t)(vrow < last ? vrow : last) * vstride + vcol};
+        const CopySrc cs{pk_next, v_next, ci_next < nfull ? voff_full : voff_tail};
         pk_next += (size_t)H * PL::bytes;
         v_next += (size_t)C * vstride;
-        t_next += C;
+        ++ci_next;
         return cs;
     };
     auto copy_group = [&](const CopySrc &cs, unsigned char *lb, auto G) {
