@@ -136,7 +136,10 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
     // Packed sequences: items it = n H + h (slot n) come in the same order; the cursor holds
     // (n, h) of the next one and the sequence sq_ whose slots start at or before n (slots
     // only grow, so it moves forward; fs_, fsn_: first slots of sq_ and sq_ + 1).
+    // sa0_, slen_: start and length of sequence sq_, read when the cursor moves (not per item:
+    // a load per item would also make the item wait for every store still in flight)
     int sq_ = 0, fs_ = 0, fsn_ = 0;
+    int64_t sa0_ = 0, slen_ = 0;
     if (a.cu_seqlens) {
         dH = G % H;
         dC = G / H;
@@ -144,6 +147,10 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         cc_ = bid / H;
         fs_ = a.cu_seqlens[0] / C;
         fsn_ = a.num_seqs > 1 ? a.cu_seqlens[1] / C + 1 : INT_MAX;
+        if (a.num_seqs > 0) {
+            sa0_ = a.cu_seqlens[0];
+            slen_ = (int64_t)a.cu_seqlens[1] - sa0_;
+        }
     }
     if (!a.cu_seqlens && W > 0) {
         dH = G % H;
@@ -180,8 +187,10 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
                 ++sq_;
                 fs_ = fsn_;
                 fsn_ = sq_ + 1 < a.num_seqs ? a.cu_seqlens[sq_ + 1] / C + sq_ + 1 : INT_MAX;
+                sa0_ = a.cu_seqlens[sq_];
+                slen_ = (int64_t)a.cu_seqlens[sq_ + 1] - sa0_;
             }
-            const int64_t a0 = a.cu_seqlens[sq_], l = (int64_t)a.cu_seqlens[sq_ + 1] - a0;
+            const int64_t a0 = sa0_, l = slen_;
             const int64_t off = (int64_t)(n - fs_) * C;
             if (off < l) {
                 x.n = n;
@@ -254,6 +263,9 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
     Item cur;
     int item = find(bid, cur);
     if (item < nitems) fetch(cur);
+    // (the first item's raw inputs land before the loop; in the loop the wait at the end of
+    // each item covers the next item's, so no path enters the loop with loads in flight)
+    __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt(0), any LDS and export count
     while (item < nitems) {  // workgroup-uniform
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
@@ -642,6 +654,18 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
                 if (dst[j] != 0xffffffffu) *reinterpret_cast<uint4 *>(gp + dst[j]) = x[j];
+            // The next item's raw inputs were loaded before these stores, which every wave
+            // issues at least VMIN of (the last wave's first lane bounds them): waiting until at
+            // most VMIN vector-memory operations are in flight lands the loads without waiting
+            // for the stores to reach memory (a wait the compiler would otherwise place at the
+            // top of the loop, for every outstanding operation).
+            constexpr int VMIN = [] {
+                int n = 0;
+                for (int j = 0; j < NJ; ++j) n += (64 * (PPW - 1) + j * PPT < NQP + NKP) ? 1 : 0;
+                return n;
+            }();
+            static_assert(VMIN >= 0 && VMIN <= 15, "vmcnt's low field");
+            __builtin_amdgcn_s_waitcnt(0xf70 | VMIN);
         }
         item = nxt;
         cur = nx;

@@ -65,6 +65,20 @@ def test_bounded_decay_odd_width_scalar_path():
     np.testing.assert_allclose(f64(got), oracle.bounded_decay(f64(z), f64(ls)), rtol=2e-6)
 
 
+@pytest.mark.parametrize("H", [1024, 1031])
+def test_bounded_decay_many_heads(H):
+    """The vectorised gate keeps the per-head scales e^A in a table of 1024 heads: at the
+    table's size and past it (scales read per element group) it matches the oracle."""
+    _case("bounded_decay H=%d" % H)
+    g = torch.Generator().manual_seed(23)
+    z = (2.0 * torch.randn(3, H, 64, generator=g)).to(torch.bfloat16)
+    ls = 0.5 * torch.randn(H, generator=g)
+    bias = torch.randn(H, 64, generator=g)
+    got = f64(kda.bounded_decay(z.cuda(), ls.cuda(), -5.0, bias.cuda()))
+    ref = oracle.bounded_decay(f64(z), f64(ls), -5.0, f64(bias))
+    np.testing.assert_allclose(got, ref, rtol=2e-6)
+
+
 # ---- prefill: the small workloads ----------------------------------------------------
 
 @pytest.mark.parametrize("C", [16, 32, 64])
