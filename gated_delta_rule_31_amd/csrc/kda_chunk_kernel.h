@@ -498,7 +498,9 @@ __device__ __forceinline__ void halve_sums(float (&x)[N], int lane, int &base) {
 // With NORM the staged operands carry the raw q and k; the tiles are scaled by the
 // reciprocal row norms (A_kk[i,j] by 1/(|k_i||k_j|), A_qk[i,j] by 1/(|q_i||k_j|)),
 // which the prep waves left in LDS as per-wave partial sums of squares.
-template <class P, int K, int V, int C, int BV, bool NORM, int NW = 4>
+// INVN: the reciprocal row norms are already in the row-norm buffer after buffer nb, as
+// [q rows, k rows] (the pre-pass forms them once per item).
+template <class P, int K, int V, int C, int BV, bool NORM, int NW = 4, bool INVN = false>
 __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char *pk, int nb, int w, int lane) {
     using L = Layout<P, K, V, C, BV>;
     using TA = typename P::TA;
@@ -515,6 +517,7 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
     const float *Nrm = reinterpret_cast<const float *>(smem + L::oNrm) + nb * L::NNRM;
     // 1 / max(|x_r|, 1e-6) of chunk row r, for x = q (qk = 0) or k (qk = 1)
     auto inv_norm = [&](int qk, int r) -> float {
+        if constexpr (INVN) return Nrm[L::NNRM + qk * C + r];
         float n = 0.f;
 #pragma unroll
         for (int pt = 0; pt < L::NPART; ++pt) n += Nrm[(((r >> 4) * 2 + qk) * 16 + (r & 15)) * L::NPART + pt];

@@ -398,6 +398,23 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         const int nxt = find(item + G, nx);
         fetch(nxt < nitems ? nx : cur);
         lds_barrier();
+        // The item's 2 C reciprocal row norms, once (wave 0 sums each row's per-wave partials),
+        // into the second row-norm buffer, which the pre-pass does not otherwise use: the
+        // staging and the A-matrix tiles then read one value per row instead of summing the
+        // partials and taking the reciprocal square root per lane.
+        float *InvN = Nrm + L::NNRM;
+        if constexpr (NORM) {
+            if (wave == 0) {  // wave-uniform
+                for (int e = lane; e < 2 * C; e += 64) {
+                    const int qk = e / C, r = e % C;
+                    float n = 0.f;
+#pragma unroll
+                    for (int pt = 0; pt < L::NPART; ++pt) n += Nrm[(((r >> 4) * 2 + qk) * 16 + (r & 15)) * L::NPART + pt];
+                    InvN[e] = __builtin_amdgcn_rsqf(fmaxf(n, 1e-12f));
+                }
+            }
+            lds_barrier();
+        }
 
         // ---- phase 2: A-matrix operand staging and the package's Qt, -Bw, gamma_C; Kt is
         // kept in registers and goes out through LDS after phase 3 (16-byte stores)
@@ -455,14 +472,8 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
                 iq[i] = 1.f;
                 ik[i] = 1.f;
                 if constexpr (NORM) {
-                    float nq = 0.f, nk = 0.f;
-#pragma unroll
-                    for (int pt = 0; pt < L::NPART; ++pt) {
-                        nq += Nrm[((p * 2 + 0) * 16 + 4 * qd + i) * L::NPART + pt];
-                        nk += Nrm[((p * 2 + 1) * 16 + 4 * qd + i) * L::NPART + pt];
-                    }
-                    iq[i] = __builtin_amdgcn_rsqf(fmaxf(nq, 1e-12f));
-                    ik[i] = __builtin_amdgcn_rsqf(fmaxf(nk, 1e-12f));
+                    iq[i] = InvN[16 * p + 4 * qd + i];
+                    ik[i] = InvN[C + 16 * p + 4 * qd + i];
                 }
             }
             float2 pre = pin[u];  // gamma_i / R_p
@@ -508,7 +519,7 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         lds_barrier();
 
         // ---- phase 3: A-matrix tiles, T's diagonal blocks, A_qk ------------------------
-        a_matrix_work<P, K, 16, C, 16, NORM, PPW>(smem, smem + PXL::oTA - L::pTm, 0, wave, lane);
+        a_matrix_work<P, K, 16, C, 16, NORM, PPW, true>(smem, smem + PXL::oTA - L::pTm, 0, wave, lane);
         lds_barrier();
 
         // Kt [K][C] into the staging area, free now (row stride LCT), two tokens per store
