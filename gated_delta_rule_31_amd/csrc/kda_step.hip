@@ -141,54 +141,74 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
 }
 
 // The same step with the state stored [V, K] (K contiguous, the transposed layout some
-// model code keeps): thread (cq, rg) holds keys 4cq..4cq+3 of value rows rg + NRG*i, so
-// the reductions over K run across the CQ consecutive lanes of a row group and every lane
-// ends with the sums it needs; no LDS, no barrier.
+// model code keeps).  Thread (cq, rg) holds KPT keys of each of its value rows rg + NRG*i:
+// float4 piece g covers keys 4 (cq + CQ g) .. + 3, so the CQ lanes of a row read one
+// contiguous run per piece.  The reductions over K are in-thread sums over the KPT keys,
+// then log2(CQ) exchanges across the row's lanes; every lane ends with the sums it needs,
+// with no LDS and no barrier.  With 16 keys per thread (K >= 64) a row takes 8 lanes (3
+// exchange steps for each of its 4 rows at K = V = 128) instead of 32 (5 steps for each
+// of 16 rows at 4 keys per thread).
+template <int K, int V>
+struct StepVkCfg {
+    static constexpr int KPT = K >= 64 ? 16 : 4;              // keys per thread
+    static constexpr int G = KPT / 4;                         // float4 pieces per row
+    static constexpr int CQ = K / KPT;                        // lanes per value row
+    static constexpr int NT0 = V * CQ < 256 ? V * CQ : 256;
+    static constexpr int NRG = NT0 / CQ;                      // row groups
+    static constexpr int RPT = V / NRG;                       // rows per thread
+    static constexpr int NT = NRG * CQ;                       // threads
+    static_assert(64 % CQ == 0 && RPT * NRG == V && RPT >= 1, "vk step mapping");
+};
+
 template <typename TIn, int K, int V, bool ZG>
-__global__ __launch_bounds__((StepCfg<V, K>::NT)) void recurrent_step_vk_kernel(StepArgs a) {
-    using Cf = StepCfg<V, K>;  // rows = value rows, float4 groups along K
-    constexpr int CQ = Cf::CQ, RPT = Cf::RPT, NRG = Cf::NRG;
-    static_assert(64 % CQ == 0, "a row group's lanes sit in one wave");
+__global__ __launch_bounds__((StepVkCfg<K, V>::NT)) void recurrent_step_vk_kernel(StepArgs a) {
+    using Cf = StepVkCfg<K, V>;
+    constexpr int G = Cf::G, CQ = Cf::CQ, RPT = Cf::RPT, NRG = Cf::NRG;
     const int pair = blockIdx.x;  // b * H + h
     const int tid = threadIdx.x;
-    const int cq = tid % CQ;      // keys 4*cq .. 4*cq+3
+    const int cq = tid % CQ;      // keys 4 (cq + CQ g) .. + 3 of piece g
     const int rg = tid / CQ;      // value rows rg + NRG * i
     const int h = pair % a.H;
-    const int c0 = 4 * cq;
     const TIn *q = static_cast<const TIn *>(a.q) + (int64_t)pair * K;
     const TIn *k = static_cast<const TIn *>(a.k) + (int64_t)pair * K;
     const TIn *v = static_cast<const TIn *>(a.v) + (int64_t)pair * V;
     float4 *S = reinterpret_cast<float4 *>(a.state + (int64_t)pair * K * V);
+    constexpr int R4 = K / 4;     // float4 pieces per value row
 
-    float4 s[RPT];
+    float4 s[RPT][G];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const f4 x = *reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * CQ + cq]);
-        s[i] = float4{x[0], x[1], x[2], x[3]};
-    }
-    float al[4], kv[4], qv[4];
+    for (int i = 0; i < RPT; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        kv[e] = ld_f32(k, c0 + e);
-        qv[e] = ld_f32(q, c0 + e);
-        if constexpr (ZG) {
-            const float s2 = expf(a.gate.log_scale[h]) * 1.44269504088896341f;
-            const float l2 = a.gate.lower_bound * 1.44269504088896341f;
-            const float z = ld_f32(static_cast<const TIn *>(a.gate.logits) + (int64_t)pair * K, c0 + e) +
-                            (a.gate.bias ? a.gate.bias[h * K + c0 + e] : 0.f);
-            al[e] = fast_bounded_alpha(z, s2, l2);
-        } else {
-            const float g = a.gate.gate[(int64_t)pair * K + c0 + e];
-            al[e] = a.gate.mode == GATE_LOG ? expf(g) : g;
+        for (int g = 0; g < G; ++g) {
+            const f4 x = *reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * R4 + cq + CQ * g]);
+            s[i][g] = float4{x[0], x[1], x[2], x[3]};
         }
+    float s2 = 0.f, l2 = 0.f;
+    if constexpr (ZG) {
+        s2 = expf(a.gate.log_scale[h]) * 1.44269504088896341f;
+        l2 = a.gate.lower_bound * 1.44269504088896341f;
     }
+    float al[G][4], kv[G][4], qv[G][4];
     float kq = 0.f, nk = 0.f, nq = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        kq += kv[e] * qv[e];
-        nk += kv[e] * kv[e];
-        nq += qv[e] * qv[e];
-    }
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 4 * (cq + CQ * g) + e;
+            kv[g][e] = ld_f32(k, c);
+            qv[g][e] = ld_f32(q, c);
+            if constexpr (ZG) {
+                const float z = ld_f32(static_cast<const TIn *>(a.gate.logits) + (int64_t)pair * K, c) +
+                                (a.gate.bias ? a.gate.bias[h * K + c] : 0.f);
+                al[g][e] = fast_bounded_alpha(z, s2, l2);
+            } else {
+                const float gg = a.gate.gate[(int64_t)pair * K + c];
+                al[g][e] = a.gate.mode == GATE_LOG ? expf(gg) : gg;
+            }
+            kq += kv[g][e] * qv[g][e];
+            nk += kv[g][e] * kv[g][e];
+            nq += qv[g][e] * qv[g][e];
+        }
 #pragma unroll
     for (int m = 1; m < CQ; m <<= 1) {
         kq += __shfl_xor(kq, m);
@@ -203,9 +223,15 @@ __global__ __launch_bounds__((StepCfg<V, K>::NT)) void recurrent_step_vk_kernel(
     float p[RPT], r[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        s[i].x *= al[0]; s[i].y *= al[1]; s[i].z *= al[2]; s[i].w *= al[3];
-        p[i] = s[i].x * kv[0] + s[i].y * kv[1] + s[i].z * kv[2] + s[i].w * kv[3];
-        r[i] = s[i].x * qv[0] + s[i].y * qv[1] + s[i].z * qv[2] + s[i].w * qv[3];
+        p[i] = 0.f;
+        r[i] = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float4 &x = s[i][g];
+            x.x *= al[g][0]; x.y *= al[g][1]; x.z *= al[g][2]; x.w *= al[g][3];
+            p[i] += x.x * kv[g][0] + x.y * kv[g][1] + x.z * kv[g][2] + x.w * kv[g][3];
+            r[i] += x.x * qv[g][0] + x.y * qv[g][1] + x.z * qv[g][2] + x.w * qv[g][3];
+        }
     }
 #pragma unroll
     for (int m = 1; m < CQ; m <<= 1)
@@ -220,9 +246,12 @@ __global__ __launch_bounds__((StepCfg<V, K>::NT)) void recurrent_step_vk_kernel(
         const float d = bt * (ld_f32(v, row) - p[i] * ik);
         if (cq == 0) st_out(a.out, a.out_bf16, (int64_t)pair * V + row, a.scale * (r[i] * iq + kq * d));
         const float dk = d * ik;
-        float4 x = s[i];
-        x.x += kv[0] * dk; x.y += kv[1] * dk; x.z += kv[2] * dk; x.w += kv[3] * dk;
-        __builtin_nontemporal_store(f4{x.x, x.y, x.z, x.w}, reinterpret_cast<f4 *>(&S[row * CQ + cq]));
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float4 x = s[i][g];
+            x.x += kv[g][0] * dk; x.y += kv[g][1] * dk; x.z += kv[g][2] * dk; x.w += kv[g][3] * dk;
+            __builtin_nontemporal_store(f4{x.x, x.y, x.z, x.w}, reinterpret_cast<f4 *>(&S[row * R4 + cq + CQ * g]));
+        }
     }
 }
 
@@ -234,10 +263,10 @@ hipError_t launch_k(const StepArgs &a, int V, int pairs, hipStream_t stream) {
         if (a.state_vk) {                                                                         \
             if (a.gate.mode == GATE_LOGITS)                                                       \
                 hipLaunchKernelGGL((recurrent_step_vk_kernel<TIn, K, VV, true>), dim3(pairs),     \
-                                   dim3(StepCfg<VV, K>::NT), 0, stream, a);                       \
+                                   dim3(StepVkCfg<K, VV>::NT), 0, stream, a);                     \
             else                                                                                  \
                 hipLaunchKernelGGL((recurrent_step_vk_kernel<TIn, K, VV, false>), dim3(pairs),    \
-                                   dim3(StepCfg<VV, K>::NT), 0, stream, a);                       \
+                                   dim3(StepVkCfg<K, VV>::NT), 0, stream, a);                     \
         } else if (a.gate.mode == GATE_LOGITS) {                                                  \
             hipLaunchKernelGGL((recurrent_step_kernel<TIn, K, VV, true>), dim3(pairs),            \
                                dim3(StepCfg<K, VV>::NT), 0, stream, a);                           \
