@@ -263,9 +263,6 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
     Item cur;
     int item = find(bid, cur);
     if (item < nitems) fetch(cur);
-    // (the first item's raw inputs land before the loop; in the loop the wait at the end of
-    // each item covers the next item's, so no path enters the loop with loads in flight)
-    __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt(0), any LDS and export count
     while (item < nitems) {  // workgroup-uniform
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
@@ -665,18 +662,6 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
                 if (dst[j] != 0xffffffffu) *reinterpret_cast<uint4 *>(gp + dst[j]) = x[j];
-            // The next item's raw inputs were loaded before these stores, which every wave
-            // issues at least VMIN of (the last wave's first lane bounds them): waiting until at
-            // most VMIN vector-memory operations are in flight lands the loads without waiting
-            // for the stores to reach memory (a wait the compiler would otherwise place at the
-            // top of the loop, for every outstanding operation).
-            constexpr int VMIN = [] {
-                int n = 0;
-                for (int j = 0; j < NJ; ++j) n += (64 * (PPW - 1) + j * PPT < NQP + NKP) ? 1 : 0;
-                return n;
-            }();
-            static_assert(VMIN >= 0 && VMIN <= 15, "vmcnt's low field");
-            __builtin_amdgcn_s_waitcnt(0xf70 | VMIN);
         }
         item = nxt;
         cur = nx;
