@@ -326,6 +326,33 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": p_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg_bytes}}
             del bl, fin_vk
+        n64 = kda.chunk_fwd_workspace_size(q.dtype, B, T, H, K, V, 64)
+        if fused and full and n64 > 0 and args.chunk != 64:
+            # the same call at chunk size 64 (half the serial chunk steps, twice the A-matrix
+            # work per chunk), beside the default
+            w64 = torch.empty(n64, dtype=torch.uint8, device=dev)
+
+            def cstep():
+                kda.chunk_fwd_fused_gate(q, k, v, z, ls, beta, lower_bound=-5.0, initial_state=None, chunk_size=64,
+                                         out=out, final_state=fin, workspace=w64)
+            for _ in range(3):
+                cstep()
+            torch.cuda.synchronize()
+            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+            for a_, b_ in cev:
+                a_.record(stream)
+                cstep()
+                b_.record(stream)
+            torch.cuda.synchronize()
+            c_ms = sum(a_.elapsed_time(b_) for a_, b_ in cev) / len(cev)
+            c_gbs = alg_bytes / (c_ms * 1e-3) / 1e9
+            log("prefill at chunk size 64: %.3f ms" % c_ms)
+            result["prefill_chunk64"] = {
+                "workload": "k3_prefill_B1_T8192_H96_K128_V128", "chunk_size": 64, "launch_ms": c_ms,
+                "tokens_per_s": B * T / (c_ms * 1e-3),
+                "roofline": {"bound": "hbm", "achieved": c_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": c_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg_bytes}}
+            del w64
     else:
         result = {"metric": "KDA prefill tokens/s (H=96,D=128) + % MFMA peak; decode state HBM GB/s",
                   "only": args.only, "n_gpus": 1, "dtype": "bf16", "data": "synthetic"}

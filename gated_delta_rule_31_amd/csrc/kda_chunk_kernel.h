@@ -87,11 +87,17 @@ struct Layout {
     using TM = typename P::TM;
     static constexpr int NP = C / 16;                                  // 16-row tiles per chunk
     static constexpr int NX = NP >= 3 ? (NP - 1) * (NP - 2) / 2 : 0;  // tiles (p,q) with q <= p-2
-    static constexpr int LKA = K + 16 / (int)sizeof(TA);  // padded row strides (elements)
+    // 64-token chunks at K = 128 with 16-bit operands: the operand staging holds half of the
+    // key columns at a time (the A-matrix products accumulate over the two halves), and the
+    // package rows of token index (Kt, T, A_qk, v) go unpadded, so that the staging, and two
+    // packages, fit the 160 KB of LDS
+    static constexpr bool kWide = C >= 64 && K >= 128 && sizeof(TM) == 2;
+    static constexpr int KS = kWide ? K / 2 : K;                 // key columns staged at once
+    static constexpr int LKA = KS + 16 / (int)sizeof(TA);  // padded row strides (elements)
     static constexpr int LKM = K + 16 / (int)sizeof(TM);
-    static constexpr int LCM = C + 16 / (int)sizeof(TM);
+    static constexpr int LCM = C + (kWide ? 0 : 16 / (int)sizeof(TM));
     static constexpr int LCF = C + 4;
-    static constexpr int LKS = K + 16 / (int)sizeof(TA);        // staging rows
+    static constexpr int LKS = KS + 16 / (int)sizeof(TA);       // staging rows
     static constexpr int NJT = BV / 16;                         // value column tiles
     static constexpr int MJ = (NJT + NSW - 1) / NSW;            // column tiles per state wave
 
@@ -503,6 +509,7 @@ __device__ __forceinline__ void halve_sums(float (&x)[N], int lane, int &base) {
 template <class P, int K, int V, int C, int BV, bool NORM, int NW = 4, bool INVN = false>
 __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char *pk, int nb, int w, int lane) {
     using L = Layout<P, K, V, C, BV>;
+    static_assert(L::KS == K, "the whole key width is staged (else a_matrix_work_blocks)");
     using TA = typename P::TA;
     using TM = typename P::TM;
     constexpr int NP = L::NP;
@@ -591,6 +598,114 @@ __device__ __forceinline__ void a_matrix_work(unsigned char *smem, unsigned char
                 if constexpr (P::kAqParts == 2) Aql[(i0 + e) * L::LCM + j] = from_f32<TM>(x - to_f32(hi));
             }
         }
+}
+
+// a_matrix_work for a staging area that holds KS < K key columns at a time (the pre-pass of
+// 64-token chunks at K = 128).  Every tile's product is a sum over the key index, so each
+// tile accumulates over the K / KS column blocks in registers: block 0 is staged by the
+// caller before the call, restage(b) stages block b >= 1 (barriers included).  The tiles are
+// a_matrix_work's, in its order (diagonal A_kk tiles, lower A_kk tiles, lower A_qk tiles),
+// tile i on wave i % NW; the products are finished as there.  The reciprocal row norms
+// (NORM) are read from the table after the first row-norm buffer.
+template <class P, int K, int C, bool NORM, int NW, class Restage>
+__device__ __forceinline__ void a_matrix_work_blocks(unsigned char *smem, unsigned char *pk, int w, int lane,
+                                                     Restage &&restage) {
+    using L = Layout<P, K, 16, C, 16>;
+    using TA = typename P::TA;
+    using TM = typename P::TM;
+    constexpr int NP = L::NP;
+    constexpr int NOFF = NP * (NP - 1) / 2;
+    constexpr int NT = NP + NOFF + NP * (NP + 1) / 2;
+    constexpr int MS = (NT + NW - 1) / NW;  // tiles per wave, at most
+    constexpr int NB = K / L::KS;
+    static_assert(NB * L::KS == K, "the column blocks cover the key width");
+    const int g = lane >> 4;
+    const TA *Lk = reinterpret_cast<const TA *>(smem + L::oLk);
+    const TA *St = reinterpret_cast<const TA *>(smem + L::oSt);
+    float *Akk = reinterpret_cast<float *>(smem + L::oAkk);
+    float *Tf = reinterpret_cast<float *>(smem + L::oTf);
+    TM *Tm = reinterpret_cast<TM *>(pk + L::pTm);
+    TM *Aqk = reinterpret_cast<TM *>(pk + L::pAqk);
+    TM *Aql = reinterpret_cast<TM *>(pk + L::pAql);
+    const float *InvN = reinterpret_cast<const float *>(smem + L::oNrm) + L::NNRM;  // [q rows, k rows]
+    // tile i: kind 0 (diagonal A_kk tile p), 1 (A_kk tile (p, qt), qt < p), 2 (A_qk tile (p, qt), qt <= p)
+    auto decode = [&](int i, int &kind, int &p, int &qt) {
+        if (i < NP) {
+            kind = 0;
+            p = qt = i;
+        } else if (i < NP + NOFF) {
+            kind = 1;
+            int t = i - NP;
+            p = 1;
+            while (t >= p) { t -= p; ++p; }
+            qt = t;
+        } else {
+            kind = 2;
+            int t = i - NP - NOFF;
+            p = 0;
+            while (t > p) { t -= p + 1; ++p; }
+            qt = t;
+        }
+    };
+    auto right_of = [&](int p, int qt) -> const TA * {
+        if (qt == p) return St + L::sRd + qt * 16 * L::LKS;
+        if (qt == p - 1) return St + L::sRo + qt * 16 * L::LKS;
+        int xi = 0;
+        for (int pp = 2; pp < p; ++pp) xi += pp - 1;
+        return St + L::sX + (xi + qt) * 16 * L::LKS;
+    };
+    f4 acc[MS];
+#pragma unroll
+    for (int m = 0; m < MS; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b) {
+        if (b > 0) restage(b);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int i = w + NW * m;
+            if (i >= NT) continue;  // wave-uniform
+            int kind, p, qt;
+            decode(i, kind, p, qt);
+            if (kind == 2)
+                mma_stage<P, P::kSplit, L::KS>(acc[m], St + L::sLq + p * 16 * L::LKS, L::LKS, right_of(p, qt), L::LKS,
+                                               L::NST, lane);
+            else
+                mma_stage<P, false, L::KS>(acc[m], Lk + p * 16 * L::LKA, L::LKA, right_of(p, qt), L::LKS, 0, lane);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+        const int i = w + NW * m;
+        if (i >= NT) continue;
+        int kind, p, qt;
+        decode(i, kind, p, qt);
+        f4 x = acc[m];
+        const int i0 = p * 16 + 4 * g, j = qt * 16 + (lane & 15);
+        if constexpr (NORM) {
+            const float cj = InvN[C + j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= cj * InvN[(kind == 2 ? 0 : C) + i0 + e];
+        }
+        if (kind == 0) {
+            const f4 t = unit_lower_inverse16<TM>(x, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float y = (j <= i0 + e) ? t[e] : 0.f;
+                Tf[(i0 + e) * L::LCF + j] = y;
+                Tm[(i0 + e) * L::LCM + j] = from_f32<TM>(y);
+            }
+        } else if (kind == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Akk[(i0 + e) * L::LCF + j] = x[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float y = (j <= i0 + e) ? x[e] : 0.f;
+                const TM hi = from_f32<TM>(y);
+                Aqk[(i0 + e) * L::LCM + j] = hi;
+                if constexpr (P::kAqParts == 2) Aql[(i0 + e) * L::LCM + j] = from_f32<TM>(y - to_f32(hi));
+            }
+        }
+    }
 }
 
 // 2^e as a float (e clamped to the normal range)

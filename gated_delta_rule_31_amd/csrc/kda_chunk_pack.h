@@ -420,103 +420,127 @@ __device__ __forceinline__ void pack_body(const ChunkArgs &a, int bid, int G) {
         // through LDS with the copy-out's 16-byte stores, a quarter of the store instructions)
         constexpr bool STQ = PERM && !std::is_same<TM, float>::value;
         uint32_t qtp[CPT][4], bwp[CPT][4];
+        // Phase 2 for key-column block BLK of the staging (the only block unless the staging
+        // holds fewer than K columns); OUTS: also the package's Qt, -Bw, gamma_C and Kt
+        auto phase2 = [&](auto blk_c, auto outs_c) {
+            constexpr int BLK = decltype(blk_c)::value;
+            constexpr bool OUTS = decltype(outs_c)::value;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int cm = combo_of(u);
-            if (cm >= NCOMBO) continue;
-            const int c0 = 2 * (cm % NCP), p = tile_of(cm);
-            float2 tpr[NP];
+            for (int u = 0; u < CPT; ++u) {
+                const int cm = combo_of(u);
+                if (cm >= NCOMBO) continue;
+                const int c0 = 2 * (cm % NCP), p = tile_of(cm);
+                // this combo's columns in the staged block (c0, c0 + 1 stay in one block)
+                const bool stg = L::KS == K || c0 / L::KS == BLK;
+                if (!OUTS && !stg) continue;
+                const int cs = L::KS == K ? c0 : c0 - BLK * L::KS;
+                float2 tpr[NP];
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp) tpr[pp] = *reinterpret_cast<const float2 *>(TPv + pp * K + c0);
-            float2 eR = {1.f, 1.f}, eCE = {1.f, 1.f}, eAll = {1.f, 1.f}, own = {1.f, 1.f};
+                for (int pp = 0; pp < NP; ++pp) tpr[pp] = *reinterpret_cast<const float2 *>(TPv + pp * K + c0);
+                float2 eR = {1.f, 1.f}, eCE = {1.f, 1.f}, eAll = {1.f, 1.f}, own = {1.f, 1.f};
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp) {
-                if (pp < p) { eR.x *= tpr[pp].x; eR.y *= tpr[pp].y; }
-                if (pp > p) { eCE.x *= tpr[pp].x; eCE.y *= tpr[pp].y; }
-                if (pp == p) own = tpr[pp];
-                eAll.x *= tpr[pp].x;
-                eAll.y *= tpr[pp].y;
-            }
-            if (p == 0 && qd == 0) st2_at<float>(gp, (uint32_t)(PL::gGC + 4 * c0), eAll.x, eAll.y);
-            const float2 rT = {__builtin_amdgcn_rcpf(own.x), __builtin_amdgcn_rcpf(own.y)};
-            float2 xf[NP];  // extra right-operand factors for tiles (pp, p), pp >= p + 2
+                for (int pp = 0; pp < NP; ++pp) {
+                    if (pp < p) { eR.x *= tpr[pp].x; eR.y *= tpr[pp].y; }
+                    if (pp > p) { eCE.x *= tpr[pp].x; eCE.y *= tpr[pp].y; }
+                    if (pp == p) own = tpr[pp];
+                    eAll.x *= tpr[pp].x;
+                    eAll.y *= tpr[pp].y;
+                }
+                if (OUTS && p == 0 && qd == 0) st2_at<float>(gp, (uint32_t)(PL::gGC + 4 * c0), eAll.x, eAll.y);
+                const float2 rT = {__builtin_amdgcn_rcpf(own.x), __builtin_amdgcn_rcpf(own.y)};
+                float2 xf[NP];  // extra right-operand factors for tiles (pp, p), pp >= p + 2
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp) {
-                float2 f = {1.f, 1.f};
+                for (int pp = 0; pp < NP; ++pp) {
+                    float2 f = {1.f, 1.f};
 #pragma unroll
-                for (int r2 = 0; r2 < NP; ++r2)
-                    if (r2 > p && r2 < pp) { f.x *= tpr[r2].x; f.y *= tpr[r2].y; }
-                xf[pp] = f;
-            }
-            float bet[4];
-            {
-                const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + 4 * qd);
-                bet[0] = b4.x; bet[1] = b4.y; bet[2] = b4.z; bet[3] = b4.w;
-            }
-            float2 suf[4];  // E_p / gamma_i
-            {
-                float2 run = sin[u];
+                    for (int r2 = 0; r2 < NP; ++r2)
+                        if (r2 > p && r2 < pp) { f.x *= tpr[r2].x; f.y *= tpr[r2].y; }
+                    xf[pp] = f;
+                }
+                float bet[4];
+                {
+                    const float4 b4 = *reinterpret_cast<const float4 *>(Btv + 16 * p + 4 * qd);
+                    bet[0] = b4.x; bet[1] = b4.y; bet[2] = b4.z; bet[3] = b4.w;
+                }
+                float2 suf[4];  // E_p / gamma_i
+                {
+                    float2 run = sin[u];
 #pragma unroll
-                for (int i = 3; i >= 0; --i) {
-                    suf[i] = run;
-                    run.x *= ral[u][i].x;
-                    run.y *= ral[u][i].y;
+                    for (int i = 3; i >= 0; --i) {
+                        suf[i] = run;
+                        run.x *= ral[u][i].x;
+                        run.y *= ral[u][i].y;
+                    }
+                }
+                float iq[4], ik[4];  // reciprocal row norms (1 without normalisation)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    iq[i] = 1.f;
+                    ik[i] = 1.f;
+                    if constexpr (NORM) {
+                        iq[i] = InvN[16 * p + 4 * qd + i];
+                        ik[i] = InvN[C + 16 * p + 4 * qd + i];
+                    }
+                }
+                float2 pre = pin[u];  // gamma_i / R_p
+                float2 kro[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * p + 4 * qd + i;
+                    pre.x *= ral[u][i].x;
+                    pre.y *= ral[u][i].y;
+                    const float2 q2 = fq[u][i], k2 = fk[u][i];
+                    const float2 lq = {q2.x * pre.x, q2.y * pre.y};
+                    const float2 lk = {bet[i] * k2.x * pre.x, bet[i] * k2.y * pre.y};
+                    const float2 ro = {k2.x * suf[i].x, k2.y * suf[i].y};  // k E_p / gamma <= |k|
+                    const float2 rd = {ro.x * rT.x, ro.y * rT.y};        // k R_p / gamma <= e^80 |k|
+                    if (stg) {
+                        st2<TA>(Lk + r * L::LKA + cs, lk.x, lk.y);
+                        st2_stage<P>(St + L::sLq + r * L::LKS + cs, L::NST, lq.x, lq.y);
+                        st2_stage<P>(St + L::sRd + r * L::LKS + cs, L::NST, rd.x, rd.y);
+                        if (p < NP - 1) st2_stage<P>(St + L::sRo + r * L::LKS + cs, L::NST, ro.x, ro.y);
+                        if constexpr (L::NX > 0) {
+                            int xi = 0;
+#pragma unroll
+                            for (int pp = 2; pp < NP; ++pp)
+#pragma unroll
+                                for (int qq = 0; qq + 2 <= pp; ++qq, ++xi)
+                                    if (qq == p)
+                                        st2_stage<P>(St + L::sX + (xi * 16 + 4 * qd + i) * L::LKS + cs, L::NST,
+                                                     ro.x * xf[pp].x, ro.y * xf[pp].y);
+                        }
+                    }
+                    if constexpr (!OUTS) continue;
+                    constexpr uint32_t E = sizeof(TM);
+                    const int cq = PERM ? paired_col(c0) : c0;  // (c0 even: c0, c0 + 1 stay adjacent)
+                    if constexpr (STQ) {
+                        typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+                        qtp[u][i] = __builtin_bit_cast(uint32_t, h2{(_Float16)(lq.x * eR.x * iq[i]), (_Float16)(lq.y * eR.y * iq[i])});
+                        bwp[u][i] = __builtin_bit_cast(uint32_t, h2{(_Float16)(-lk.x * eR.x * ik[i]), (_Float16)(-lk.y * eR.y * ik[i])});
+                    } else {
+                        st2_at<TM>(gp, (uint32_t)PL::gQt + E * (uint32_t)(r * K + cq), lq.x * eR.x * iq[i], lq.y * eR.y * iq[i]);
+                        st2_at<TM>(gp, (uint32_t)PL::gBw + E * (uint32_t)(r * K + cq), -lk.x * eR.x * ik[i], -lk.y * eR.y * ik[i]);
+                    }
+                    kro[i] = float2{ro.x * eCE.x * ik[i], ro.y * eCE.y * ik[i]};
+                    ktk[u][i] = kro[i];
                 }
             }
-            float iq[4], ik[4];  // reciprocal row norms (1 without normalisation)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                iq[i] = 1.f;
-                ik[i] = 1.f;
-                if constexpr (NORM) {
-                    iq[i] = InvN[16 * p + 4 * qd + i];
-                    ik[i] = InvN[C + 16 * p + 4 * qd + i];
-                }
-            }
-            float2 pre = pin[u];  // gamma_i / R_p
-            float2 kro[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * p + 4 * qd + i;
-                pre.x *= ral[u][i].x;
-                pre.y *= ral[u][i].y;
-                const float2 q2 = fq[u][i], k2 = fk[u][i];
-                const float2 lq = {q2.x * pre.x, q2.y * pre.y};
-                const float2 lk = {bet[i] * k2.x * pre.x, bet[i] * k2.y * pre.y};
-                const float2 ro = {k2.x * suf[i].x, k2.y * suf[i].y};  // k E_p / gamma <= |k|
-                const float2 rd = {ro.x * rT.x, ro.y * rT.y};        // k R_p / gamma <= e^80 |k|
-                st2<TA>(Lk + r * L::LKA + c0, lk.x, lk.y);
-                st2_stage<P>(St + L::sLq + r * L::LKS + c0, L::NST, lq.x, lq.y);
-                st2_stage<P>(St + L::sRd + r * L::LKS + c0, L::NST, rd.x, rd.y);
-                if (p < NP - 1) st2_stage<P>(St + L::sRo + r * L::LKS + c0, L::NST, ro.x, ro.y);
-                if constexpr (L::NX > 0) {
-                    int xi = 0;
-#pragma unroll
-                    for (int pp = 2; pp < NP; ++pp)
-#pragma unroll
-                        for (int qq = 0; qq + 2 <= pp; ++qq, ++xi)
-                            if (qq == p)
-                                st2_stage<P>(St + L::sX + (xi * 16 + 4 * qd + i) * L::LKS + c0, L::NST,
-                                             ro.x * xf[pp].x, ro.y * xf[pp].y);
-                }
-                constexpr uint32_t E = sizeof(TM);
-                const int cq = PERM ? paired_col(c0) : c0;  // (c0 even: c0, c0 + 1 stay adjacent)
-                if constexpr (STQ) {
-                    typedef __attribute__((ext_vector_type(2))) _Float16 h2;
-                    qtp[u][i] = __builtin_bit_cast(uint32_t, h2{(_Float16)(lq.x * eR.x * iq[i]), (_Float16)(lq.y * eR.y * iq[i])});
-                    bwp[u][i] = __builtin_bit_cast(uint32_t, h2{(_Float16)(-lk.x * eR.x * ik[i]), (_Float16)(-lk.y * eR.y * ik[i])});
-                } else {
-                    st2_at<TM>(gp, (uint32_t)PL::gQt + E * (uint32_t)(r * K + cq), lq.x * eR.x * iq[i], lq.y * eR.y * iq[i]);
-                    st2_at<TM>(gp, (uint32_t)PL::gBw + E * (uint32_t)(r * K + cq), -lk.x * eR.x * ik[i], -lk.y * eR.y * ik[i]);
-                }
-                kro[i] = float2{ro.x * eCE.x * ik[i], ro.y * eCE.y * ik[i]};
-                ktk[u][i] = kro[i];
-            }
-        }
+        };
+        phase2(std::integral_constant<int, 0>{}, std::true_type{});
         lds_barrier();
 
         // ---- phase 3: A-matrix tiles, T's diagonal blocks, A_qk ------------------------
-        a_matrix_work<P, K, 16, C, 16, NORM, PPW, true>(smem, smem + PXL::oTA - L::pTm, 0, wave, lane);
+        if constexpr (L::KS == K) {
+            a_matrix_work<P, K, 16, C, 16, NORM, PPW, true>(smem, smem + PXL::oTA - L::pTm, 0, wave, lane);
+        } else {
+            // the second half of the key columns is staged once every wave is done with the first
+            static_assert(2 * L::KS == K, "two column blocks");
+            a_matrix_work_blocks<P, K, C, NORM, PPW>(smem, smem + PXL::oTA - L::pTm, wave, lane, [&](int) {
+                lds_barrier();
+                phase2(std::integral_constant<int, 1>{}, std::false_type{});
+                lds_barrier();
+            });
+        }
         lds_barrier();
 
         // Kt [K][C] into the staging area, free now (row stride LCT), two tokens per store

@@ -257,9 +257,11 @@ def test_python_prefill_form_selection():
     ws, n = kda._chunk_workspace(None, None, q, 1, 64, 32, False)
     assert n == kda.chunk_fwd_workspace_size(torch.bfloat16, 1, 100, 2, 64, 64, 32) > 0 and ws.numel() == n
     assert kda._chunk_workspace(False, None, q, 1, 64, 32, False) == (None, 0)
-    # bf16 K = V = 128 at chunk 64 has no two-kernel form (its pre-pass exceeds the LDS)
-    q128 = torch.zeros(1, 100, 2, 128, dtype=torch.bfloat16)
-    assert kda.chunk_fwd_workspace_size(torch.bfloat16, 1, 100, 2, 128, 128, 64) == 0
+    # float32 K = V = 128 at chunk 64 has no two-kernel form (two packages exceed the LDS);
+    # bf16 has one (the pre-pass stages the key columns in two halves)
+    assert kda.chunk_fwd_workspace_size(torch.bfloat16, 1, 100, 2, 128, 128, 64) > 0
+    q128 = torch.zeros(1, 100, 2, 128, dtype=torch.float32)
+    assert kda.chunk_fwd_workspace_size(torch.float32, 1, 100, 2, 128, 128, 64) == 0
     assert kda._chunk_workspace(None, None, q128, 1, 128, 64, False) == (None, 0)
     with pytest.raises(kda.KDAError):
         kda._chunk_workspace(True, None, q128, 1, 128, 64, False)

@@ -170,7 +170,7 @@ def test_fast_decay_chunk64(K, V):
     assert_close(f, ef, False, "final state")
 
 
-@pytest.mark.parametrize("K,V,C", [(128, 128, 32), (64, 64, 64), (64, 128, 32)])
+@pytest.mark.parametrize("K,V,C", [(128, 128, 32), (64, 64, 64), (64, 128, 32), (128, 128, 64)])
 @pytest.mark.parametrize("regime", ["slow", "k3"])
 def test_bf16_large_values_and_state(K, V, C, regime):
     """Values and an initial state near 1e5 on the bf16 path, beyond the fp16
@@ -259,6 +259,32 @@ def test_varlen_matches_oracle_and_separate_calls():
                                 initial_state=d(inp.initial_state[s:s + 1]), gate_is_log=True,
                                 out_dtype=torch.float32)
         assert torch.equal(os_, o[:, a0:a1]) and torch.equal(fs[0], f[s])
+
+
+def test_k128_chunk64_varlen_and_segments():
+    """Chunk size 64 at K = V = 128 (bf16; the pre-pass stages the key columns in two halves):
+    packed sequences with empty, single-token and ragged ones (whole pre-pass, then the
+    chain), and one sequence long enough for the segment schedule (65 chunks: the chain of
+    each segment beside the pre-pass of the next), with the gate tensor and inside the kernel."""
+    if not _form_supports(torch.bfloat16, 128, 128, 64):
+        pytest.skip("no chunk size 64 at K=V=128 in this form")
+    lens = [37, 0, 200, 64, 1, 130]
+    _case("K128 C64 varlen lens=%s" % lens)
+    inp = synth.make_prefill(1, sum(lens), 2, 128, 128, dtype=torch.bfloat16, seed=97, seqlens=lens,
+                             state_std=0.1, alog_std=0.5)
+    eo, ef = oracle_prefill(inp)
+    for run in (gpu_prefill, gpu_prefill_fused):
+        o, f = run(inp, chunk_size=64)
+        assert_close(o, eo, False, "out (varlen, %s)" % run.__name__)
+        assert_close(f, ef, False, "final states (varlen, %s)" % run.__name__)
+        assert torch.equal(f[1].cpu(), inp.initial_state[1].to(f.dtype))
+    _case("K128 C64 segments T=4160")
+    inp = synth.make_prefill(1, 4160, 2, 128, 128, dtype=torch.bfloat16, seed=98, state_std=0.1, alog_std=0.5)
+    eo, ef = oracle_prefill(inp)
+    for run in (gpu_prefill, gpu_prefill_fused):
+        o, f = run(inp, chunk_size=64)
+        assert_close(o, eo, False, "out (segments, %s)" % run.__name__)
+        assert_close(f, ef, False, "final state (segments, %s)" % run.__name__)
 
 
 @pytest.mark.parametrize("n,seed", [(300, 61), (40, 62)])
@@ -423,7 +449,8 @@ def _oracle_prefill_bias(inp, bias):
 
 
 @pytest.mark.parametrize("dtype,K,V,C", [(torch.float32, 16, 16, 16), (torch.float32, 64, 32, 32),
-                                         (torch.bfloat16, 128, 128, 32), (torch.bfloat16, 32, 64, 64)])
+                                         (torch.bfloat16, 128, 128, 32), (torch.bfloat16, 32, 64, 64),
+                                         (torch.bfloat16, 128, 128, 64)])
 def test_fused_gate_prefill_matches_oracle(dtype, K, V, C):
     if not _form_supports(dtype, K, V, C):
         pytest.skip("shape not compiled in this form")
@@ -651,7 +678,7 @@ def _oracle_prepared(r, qk_norm=True, beta_sig=True):
 
 
 @pytest.mark.parametrize("dtype,K,V,C", [(torch.float32, 64, 32, 32), (torch.bfloat16, 128, 128, 32),
-                                         (torch.bfloat16, 32, 64, 64)])
+                                         (torch.bfloat16, 32, 64, 64), (torch.bfloat16, 128, 128, 64)])
 def test_prepared_in_kernel_chunk(dtype, K, V, C):
     if not _form_supports(dtype, K, V, C):
         pytest.skip("shape not compiled in this form")
@@ -735,16 +762,20 @@ def _k3_oracle(inp):
     return _K3_ORACLE["r"]
 
 
+@pytest.mark.parametrize("C", [32, 64])
 @pytest.mark.parametrize("fused", [False, True])
-def test_k3_prefill_full_size_all_heads(fused):
+def test_k3_prefill_full_size_all_heads(fused, C):
     """Kimi K3 layer prefill at its full size (T=8192, H=96, K=V=128, bf16) in the launch
-    configuration the benchmark times, through the gate tensor and with the gate inside the
-    kernel; the oracle checks all 96 heads, output and final state."""
-    _case("k3 prefill full size, all heads, fused gate %s" % fused)
+    configuration the benchmark times (chunk size 32), and at chunk size 64, through the gate
+    tensor and with the gate inside the kernel; the oracle checks all 96 heads, output and
+    final state."""
+    if not _form_supports(torch.bfloat16, 128, 128, C):
+        pytest.skip("no chunk size %d at K=V=128 in this form" % C)
+    _case("k3 prefill full size, all heads, fused gate %s, C=%d" % (fused, C))
     inp = synth.k3_prefill(device="cuda")
     run = gpu_prefill_fused if fused else gpu_prefill
-    o, f = run(inp, chunk_size=32)
-    ob, fb = run(inp, chunk_size=32, out_dtype=torch.bfloat16)
+    o, f = run(inp, chunk_size=C)
+    ob, fb = run(inp, chunk_size=C, out_dtype=torch.bfloat16)
     assert torch.equal(ob, o.to(torch.bfloat16)) and torch.equal(fb, f)
     eo, ef = _k3_oracle(inp)
     for h0 in range(0, 96, 24):  # per block of heads (each block's own RMS)
