@@ -792,8 +792,9 @@ __device__ __forceinline__ void state_waves(const ChunkArgs &a, unsigned char *s
     using TIn = typename std::conditional<std::is_same<P, PrecF32>::value, float, __bf16>::type;
     constexpr bool P16 = !std::is_same<TM, float>::value;  // 16-bit matrix-core operands
     // Lean order (fewer fragments live at once): the single kernel, whose twelve waves have
-    // fewer registers each, and float32 fragments of 64-token chunks.
-    constexpr bool LEAN = FEW_REGS || !PK || (!P16 && C >= 64);
+    // fewer registers each, float32 fragments of 64-token chunks, and 16-bit fragments of
+    // 64-token chunks at K = 128.
+    constexpr bool LEAN = FEW_REGS || !PK || (!P16 && C >= 64) || L::kWide;
     constexpr int NP = L::NP;
     constexpr int NKT_K = K / 16;
     const int g = lane >> 4;
