@@ -122,8 +122,8 @@ kda_status kda_bounded_decay(const void *logits, kda_dtype logits_dtype, const f
  * which: chunk size 16 and 32 for every K, V on the bf16 path and up to K = 64 on the
  * float32 path, 64 only for small widths.  With a workspace (two kernels),
  * kda_chunk_fwd_workspace_size() > 0 tells which: chunk size 16 and 32 for every K, V on
- * the bf16 path and every V at K <= 64 on the float32 path, 64 for every K, V on the bf16
- * path and at K <= 32 on the float32 path.  Anything else returns
+ * both paths, 64 for every K, V on the bf16 path and at K <= 32 on the float32 path.
+ * Anything else returns
  * KDA_ERR_UNSUPPORTED.  in_dtype KDA_F32 computes in float32 (matrix cores in fp32);
  * KDA_BF16 uses bf16/fp16 matrix-core operands with float32 accumulation and a
  * float32 master state.
