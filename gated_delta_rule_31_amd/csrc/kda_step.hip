@@ -145,9 +145,10 @@ __global__ __launch_bounds__((StepCfg<K, V>::NT)) void recurrent_step_kernel(Ste
 // float4 piece g covers keys 4 (cq + CQ g) .. + 3, so the CQ lanes of a row read one
 // contiguous run per piece.  The reductions over K are in-thread sums over the KPT keys,
 // then log2(CQ) exchanges across the row's lanes; every lane ends with the sums it needs,
-// with no LDS and no barrier.  With 16 keys per thread (K >= 64) a row takes 8 lanes (3
+// with no LDS round trip.  With 16 keys per thread (K >= 64) a row takes 8 lanes (3
 // exchange steps for each of its 4 rows at K = V = 128) instead of 32 (5 steps for each
-// of 16 rows at 4 keys per thread).
+// of 16 rows at 4 keys per thread).  The token's k, q and retention are formed once per
+// key into a small LDS table (every row group needs all of them) behind one barrier.
 template <int K, int V>
 struct StepVkCfg {
     static constexpr int KPT = K >= 64 ? 16 : 4;              // keys per thread
@@ -183,32 +184,50 @@ __global__ __launch_bounds__((StepVkCfg<K, V>::NT)) void recurrent_step_vk_kerne
             const f4 x = *reinterpret_cast<const f4 *>(&S[(rg + NRG * i) * R4 + cq + CQ * g]);
             s[i][g] = float4{x[0], x[1], x[2], x[3]};
         }
-    float s2 = 0.f, l2 = 0.f;
-    if constexpr (ZG) {
-        s2 = expf(a.gate.log_scale[h]) * 1.44269504088896341f;
-        l2 = a.gate.lower_bound * 1.44269504088896341f;
+    // The token's k, q and retention, once per key for the whole workgroup (every row group
+    // needs the same keys): formed by the first K threads into LDS, behind an LDS-only
+    // barrier, so the state loads above stay in flight across it.
+    __shared__ __align__(16) float sh_k[K];
+    __shared__ __align__(16) float sh_q[K];
+    __shared__ __align__(16) float sh_al[K];
+    {
+        float s2 = 0.f, l2 = 0.f;
+        if constexpr (ZG) {
+            s2 = expf(a.gate.log_scale[h]) * 1.44269504088896341f;
+            l2 = a.gate.lower_bound * 1.44269504088896341f;
+        }
+        for (int c = tid; c < K; c += Cf::NT) {
+            sh_k[c] = ld_f32(k, c);
+            sh_q[c] = ld_f32(q, c);
+            if constexpr (ZG) {
+                const float z = ld_f32(static_cast<const TIn *>(a.gate.logits) + (int64_t)pair * K, c) +
+                                (a.gate.bias ? a.gate.bias[h * K + c] : 0.f);
+                sh_al[c] = fast_bounded_alpha(z, s2, l2);
+            } else {
+                const float gg = a.gate.gate[(int64_t)pair * K + c];
+                sh_al[c] = a.gate.mode == GATE_LOG ? expf(gg) : gg;
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     float al[G][4], kv[G][4], qv[G][4];
     float kq = 0.f, nk = 0.f, nq = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+        const int c = 4 * (cq + CQ * g);
+        const float4 k4 = *reinterpret_cast<const float4 *>(sh_k + c);
+        const float4 q4 = *reinterpret_cast<const float4 *>(sh_q + c);
+        const float4 a4 = *reinterpret_cast<const float4 *>(sh_al + c);
+        kv[g][0] = k4.x; kv[g][1] = k4.y; kv[g][2] = k4.z; kv[g][3] = k4.w;
+        qv[g][0] = q4.x; qv[g][1] = q4.y; qv[g][2] = q4.z; qv[g][3] = q4.w;
+        al[g][0] = a4.x; al[g][1] = a4.y; al[g][2] = a4.z; al[g][3] = a4.w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int c = 4 * (cq + CQ * g) + e;
-            kv[g][e] = ld_f32(k, c);
-            qv[g][e] = ld_f32(q, c);
-            if constexpr (ZG) {
-                const float z = ld_f32(static_cast<const TIn *>(a.gate.logits) + (int64_t)pair * K, c) +
-                                (a.gate.bias ? a.gate.bias[h * K + c] : 0.f);
-                al[g][e] = fast_bounded_alpha(z, s2, l2);
-            } else {
-                const float gg = a.gate.gate[(int64_t)pair * K + c];
-                al[g][e] = a.gate.mode == GATE_LOG ? expf(gg) : gg;
-            }
             kq += kv[g][e] * qv[g][e];
             nk += kv[g][e] * kv[g][e];
             nq += qv[g][e] * qv[g][e];
         }
+    }
 #pragma unroll
     for (int m = 1; m < CQ; m <<= 1) {
         kq += __shfl_xor(kq, m);
