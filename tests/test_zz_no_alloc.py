@@ -63,3 +63,12 @@ def test_noalloc_refuses_beyond_its_array():
     with pytest.raises(ValueError, match="unsupported"):
         kda.chunk_fwd_fused_gate_noalloc(x, x, x, x, torch.zeros(96, device="cuda"),
                                          torch.zeros(1, T, 96, device="cuda"), out)
+
+
+def test_noalloc_chunk64_k128():
+    """The same entry point at chunk size 64 with K = V = 128 (the pre-pass that stages the
+    key columns in two halves), on packed sequences with an empty one."""
+    _case("noalloc: chunk size 64, K=V=128, packed sequences")
+    inp = synth.make_prefill(1, 300, 4, 128, 128, seed=63, state_std=0.1, seqlens=[130, 0, 170], alog_std=0.5)
+    assert 0 < kda.chunk_fwd_workspace_size(torch.bfloat16, 1, 300, 4, 128, 128, 64) <= kda.noalloc_scratch_bytes()
+    _noalloc_vs_workspace(inp, 64)
